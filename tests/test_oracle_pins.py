@@ -1,0 +1,428 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test fixes one part of the oracle with a brute-force computation, a
+closed form, an invariant, a library routine, or a value the pages print.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gptinputs as gi
+import oracle as O
+from oracle.gpt import _Num
+from tests.brute_force import brute_losses
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def tiny_plus(**kw):
+    """Tiny fixture with every feature on: 2 layers, 'SL' windows (S=4),
+    value embeddings on layer 1 (gate over C=8 channels), G=2."""
+    cfg = gi.preset("tiny", n_layer=2, window_pattern="SL", window_short=4,
+                    window_long=16, ve_every_odd=1, ve_gate_channels=8)
+    return cfg
+
+
+def inputs(cfg, rows=None, sigma=None):
+    n = O.param_count(cfg)
+    if sigma is not None:
+        cfg = dict(cfg, sigma=sigma)
+    w, _ = gi.make_params(cfg, n)
+    return w.astype(np.float64), gi.make_tokens(cfg, rows)
+
+
+# ---------------------------------------------------------------- P13, golden
+def test_param_counts_closed_form():
+    assert O.param_count(gi.preset("tiny")) == 3680
+    # wte 432 + qkv 512 + o 256 + mlp 2048 + lm_head 432
+    assert O.param_count(gi.preset("d12")) == 286_262_400
+    assert O.param_count(gi.preset("d12gqa")) == 176_161_152
+    assert O.param_count(gi.preset("d24")) == 1_384_124_928
+    assert O.param_count(gi.preset("d4")) == 11_534_464
+
+
+def test_microgpt_param_count_golden():
+    """microgpt's printed ~4,192 parameters equal this layout (no biases, no
+    norm gains, 4x MLP) at its shape once a learned position table is added
+    and KV heads = query heads."""
+    g = json.load(open(os.path.join(GOLDEN, "microgpt.json")))
+    s = g["shape_reading"]
+    cfg = gi.preset("tiny", n_kv_head=s["n_head"], n_head=s["n_head"],
+                    head_dim=s["head_dim"], d_model=s["d_model"],
+                    vocab=g["vocab"])
+    assert O.param_count(cfg) + s["block_size"] * s["d_model"] == g["n_params"]
+
+
+def test_init_loss_matches_microgpt_start():
+    """P14: with N(0, sigma) lm_head on unit-RMS features, E[l] ~ ln V +
+    sigma^2 D / 2; for the tiny model that is ~3.35, and microgpt prints a
+    starting loss of ~3.3."""
+    g = json.load(open(os.path.join(GOLDEN, "microgpt.json")))
+    cfg = gi.preset("tiny", batch=64)
+    w, tok = inputs(cfg)
+    loss, _ = O.forward(cfg, w, tok, "fp64", keep=False)
+    approx = math.log(27) + cfg["sigma"] ** 2 * cfg["d_model"] / 2
+    assert abs(loss - approx) / approx < 0.03
+    assert abs(loss - g["init_loss_approx"]) / g["init_loss_approx"] < g["init_loss_rel_tol"]
+
+
+# ------------------------------------------------------------ brute force fwd
+@pytest.mark.parametrize("which", ["tiny", "tiny_plus"])
+def test_forward_equals_scalar_brute_force(which):
+    cfg = gi.preset("tiny") if which == "tiny" else tiny_plus()
+    w, tok = inputs(cfg, rows=3)
+    _, cache = O.forward(cfg, w, tok, "fp64", keep=False)
+    ref = np.array(brute_losses(cfg, w, tok)).reshape(-1)
+    np.testing.assert_allclose(cache["ell"], ref, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------- P1 finite differences
+def _fd_check(cfg, w, tok, coords):
+    _, g, _ = O.step(cfg, w, tok, "fp64")
+    eps = 1e-6
+    fd = np.empty(len(coords))
+    for n, i in enumerate(coords):
+        wp = w.copy(); wp[i] += eps
+        wm = w.copy(); wm[i] -= eps
+        lp, _ = O.forward(cfg, wp, tok, "fp64", keep=False)
+        lm, _ = O.forward(cfg, wm, tok, "fp64", keep=False)
+        fd[n] = (lp - lm) / (2 * eps)
+    an = g[coords]
+    return np.linalg.norm(fd - an) / np.linalg.norm(an)
+
+
+def test_finite_differences_tiny_all_params():
+    cfg = gi.preset("tiny")
+    w, tok = inputs(cfg)
+    err = _fd_check(cfg, w, tok, np.arange(O.param_count(cfg)))
+    assert err < 1e-6, err
+
+
+def test_finite_differences_tiny_plus_sampled():
+    cfg = tiny_plus()
+    w, tok = inputs(cfg, rows=4)
+    rng = np.random.default_rng(1)
+    # a sample from every tensor, so no block's gradient goes unchecked
+    coords, off = [], 0
+    for _, shape in O.param_layout(cfg):
+        n = int(np.prod(shape))
+        coords += list(off + rng.choice(n, size=min(n, 120), replace=False))
+        off += n
+    err = _fd_check(cfg, w, tok, np.array(coords))
+    assert err < 1e-6, err
+
+
+# ------------------------------------------------------- P2 uniform logits
+@pytest.mark.parametrize("name", ["tiny", "tiny_plus", "d4small"])
+def test_uniform_logits_closed_form(name):
+    if name == "tiny":
+        cfg = gi.preset("tiny")
+    elif name == "tiny_plus":
+        cfg = tiny_plus()
+    else:
+        cfg = gi.preset("d4", n_layer=2, seq_len=32, batch=2, d_model=64,
+                        n_head=2, n_kv_head=1, head_dim=32, vocab=300,
+                        window_short=8, window_long=32, ve_gate_channels=16)
+    w, tok = inputs(cfg)
+    lay = O.param_layout(cfg)
+    off = sum(int(np.prod(s)) for n, s in lay[:-1])
+    w[off:] = 0.0                                        # W_lm = 0
+    loss, g, cache = O.step(cfg, w, tok, "fp64")
+    V = cfg["vocab"]
+    assert loss == pytest.approx(math.log(V), abs=1e-12)
+    # every gradient except dW_lm is exactly zero
+    assert np.all(g[:off] == 0.0)
+    B, T = tok.shape[0], tok.shape[1] - 1
+    N = B * T
+    hf = cache["hf"].reshape(N, -1)
+    tgt = tok[:, 1:].reshape(-1)
+    onehot = np.zeros((N, V)); onehot[np.arange(N), tgt] = 1
+    ref = ((1.0 / V - onehot).T @ hf) / N
+    np.testing.assert_allclose(g[off:].reshape(V, -1), ref, atol=1e-15)
+    # bpb closed form
+    tb = gi.make_token_bytes(cfg)
+    nats, nbytes, bpb = O.eval_bpb(cfg, w, tok, tb, "fp64")
+    assert nats == pytest.approx(N * math.log(V), rel=1e-13)
+    assert bpb == pytest.approx(math.log(V) * N / (math.log(2) * tb[tgt].sum()), rel=1e-13)
+    if name == "tiny":
+        assert bpb == pytest.approx(math.log2(27), rel=1e-13)
+
+
+# ------------------------------------------------------- attention invariants
+def _rand_qkv(B=2, T=37, H=4, Hkv=2, hd=8, seed=0):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, T, H, hd)), rng.standard_normal((B, T, Hkv, hd)),
+            rng.standard_normal((B, T, Hkv, hd)))
+
+
+@pytest.mark.parametrize("W", [0, 1, 5, 36, 100])
+def test_attention_rows_stochastic_and_mask_exact(W):
+    """P3/P4: probabilities of each query sum to 1; masked ones are 0.0."""
+    q, k, v = _rand_qkv()
+    num = _Num("fp64")
+    _, lse = O.attention(q, k, v, W, num)
+    for b in range(2):
+        P, _, _ = O.gpt.attention_probs(q, k, lse, W, num, b)
+        np.testing.assert_allclose(P.sum(-1), 1.0, atol=1e-12)
+        mask = O.visible_mask(q.shape[1], W)
+        assert np.all(P[:, ~mask] == 0.0)
+        assert np.all(P[:, mask] > 0.0)
+
+
+def test_visible_mask_predicate():
+    m = O.visible_mask(6, 2)
+    for i in range(6):
+        for j in range(6):
+            assert m[i, j] == (j <= i and i - j <= 2)
+
+
+@pytest.mark.parametrize("W", [0, 3, 17, 64])
+def test_attention_matches_torch_sdpa(W):
+    """Dense attention equals torch's scaled_dot_product_attention (CPU,
+    float64) given the same boolean mask and KV heads repeated per group."""
+    q, k, v = _rand_qkv(T=40)
+    o, _ = O.attention(q, k, v, W, _Num("fp64"))
+    G = q.shape[2] // k.shape[2]
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(np.repeat(k, G, axis=2)).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(np.repeat(v, G, axis=2)).permute(0, 2, 1, 3)
+    mask = torch.from_numpy(O.visible_mask(40, W))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)
+    np.testing.assert_allclose(o, ref.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+
+
+def test_attention_bwd_matches_torch_autograd():
+    q, k, v = _rand_qkv(T=29)
+    W = 6
+    num = _Num("fp64")
+    o, lse = O.attention(q, k, v, W, num)
+    do = np.random.default_rng(5).standard_normal(o.shape)
+    dq, dk, dv = O.attention_bwd(q, k, v, o, lse, do, W, num)
+    G = q.shape[2] // k.shape[2]
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    mask = torch.from_numpy(O.visible_mask(29, W))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq.permute(0, 2, 1, 3), tk.repeat_interleave(G, 2).permute(0, 2, 1, 3),
+        tv.repeat_interleave(G, 2).permute(0, 2, 1, 3), attn_mask=mask)
+    out.permute(0, 2, 1, 3).backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("W", [0, 127, 128, 200, 1000])
+def test_dense_equals_tiled_online_softmax(W):
+    """P16: the 128-key tiled online softmax (what the GPU runs) equals the
+    dense definition."""
+    q, k, v = _rand_qkv(B=1, T=300, H=2, Hkv=1, hd=16, seed=3)
+    o, lse = O.attention(q, k, v, W, _Num("fp64"))
+    ot, lset = O.attention_tiled(q, k, v, W)
+    np.testing.assert_allclose(ot, o, atol=1e-12)
+    np.testing.assert_allclose(lset, lse, atol=1e-12)
+
+
+# ------------------------------------------------------- norm / rotary / CE
+def test_rmsnorm_matches_torch():
+    x = np.random.default_rng(0).standard_normal((5, 7, 24))
+    y, r = O.rmsnorm(x, 1e-5, _Num("fp64"))
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (24,), eps=1e-5)
+    np.testing.assert_allclose(y, ref.numpy(), atol=1e-14)
+    # P9: mean square after the norm is ms / (ms + eps)
+    ms = np.mean(x * x, axis=-1)
+    np.testing.assert_allclose(np.mean(y * y, axis=-1), ms / (ms + 1e-5), rtol=1e-13)
+
+
+def test_rmsnorm_bwd_matches_torch_autograd():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((6, 32)); dy = rng.standard_normal((6, 32))
+    num = _Num("fp64")
+    y, r = O.rmsnorm(x, 1e-5, num)
+    tx = torch.tensor(x, requires_grad=True)
+    torch.nn.functional.rms_norm(tx, (32,), eps=1e-5).backward(torch.from_numpy(dy))
+    np.testing.assert_allclose(O.rmsnorm_bwd(dy, y, r, num), tx.grad.numpy(), atol=1e-13)
+
+
+def test_rope_invariants():
+    """P8: rotation preserves each pair's norm; q.k after rotation depends on
+    positions only through their difference; rope then rms == rms then rope."""
+    rng = np.random.default_rng(2)
+    T, hd, s = 50, 16, 23
+    num = _Num("fp64")
+    x = rng.standard_normal((1, T, 3, hd))
+    cos, sin = O.rope_tables(T + s, hd, 10000.0)
+    y = O.rope(x, cos[:T], sin[:T], num)
+    h = hd // 2
+    np.testing.assert_allclose(x[..., :h] ** 2 + x[..., h:] ** 2,
+                               y[..., :h] ** 2 + y[..., h:] ** 2, atol=1e-12)
+    y2 = O.rope(x, cos[s:], sin[s:], num)            # every position + s
+    d1 = np.einsum("bihd,bjhd->bhij", y, y)
+    d2 = np.einsum("bihd,bjhd->bhij", y2, y2)
+    np.testing.assert_allclose(d1, d2, atol=1e-11)
+    a, _ = O.rmsnorm(O.rope(x, cos[:T], sin[:T], num), 1e-5, num)
+    b = O.rope(O.rmsnorm(x, 1e-5, num)[0], cos[:T], sin[:T], num)
+    np.testing.assert_allclose(a, b, atol=1e-12)
+    # rope_bwd is the inverse rotation
+    np.testing.assert_allclose(O.rope_bwd(y, cos[:T], sin[:T], num), x, atol=1e-12)
+    # half-split pairing and sign, written out for one pair (READING)
+    t, j = 7, 3
+    th = t * 10000.0 ** (-2 * j / hd)
+    assert y[0, t, 0, j] == pytest.approx(x[0, t, 0, j] * math.cos(th) - x[0, t, 0, j + h] * math.sin(th))
+    assert y[0, t, 0, j + h] == pytest.approx(x[0, t, 0, j] * math.sin(th) + x[0, t, 0, j + h] * math.cos(th))
+
+
+def test_cross_entropy_matches_torch():
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal((33, 50)) * 3
+    tgt = rng.integers(0, 50, 33)
+    ell, lse, dz = O.cross_entropy(z, tgt, _Num("fp64"))
+    tz = torch.tensor(z, requires_grad=True)
+    loss = torch.nn.functional.cross_entropy(tz, torch.from_numpy(tgt))
+    loss.backward()
+    assert ell.mean() == pytest.approx(loss.item(), abs=1e-13)
+    np.testing.assert_allclose(dz, tz.grad.numpy(), atol=1e-15)
+    np.testing.assert_allclose(lse, torch.logsumexp(torch.from_numpy(z), 1).numpy(), atol=1e-13)
+
+
+def test_round_bf16_matches_torch():
+    x = np.random.default_rng(6).standard_normal(100000).astype(np.float32) * 10
+    x[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 0.0]   # ties
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(O.round_bf16(x), ref)
+
+
+# ------------------------------------------------------- model-level invariants
+def test_causal_prefix_invariance():
+    """P6: changing tokens at positions >= t leaves losses at targets < t-1
+    unchanged, bit for bit."""
+    cfg = tiny_plus()
+    w, tok = inputs(cfg, rows=2)
+    t = 9
+    tok2 = tok.copy()
+    tok2[:, t:] = (tok2[:, t:] % 26) + 1
+    for prec in ("fp64", "bf16emu"):
+        _, c1 = O.forward(cfg, w, tok, prec, keep=False)
+        _, c2 = O.forward(cfg, w, tok2, prec, keep=False)
+        l1 = c1["ell"].reshape(2, -1)
+        l2 = c2["ell"].reshape(2, -1)
+        np.testing.assert_array_equal(l1[:, :t - 1], l2[:, :t - 1])
+        assert np.any(l1[:, t - 1:] != l2[:, t - 1:])
+
+
+def test_window_locality():
+    """P7: in a one-layer model with window W, the loss at query i does not
+    depend on the token at j < i - W."""
+    cfg = gi.preset("tiny", window_pattern="S", window_short=3, window_long=16)
+    w, tok = inputs(cfg, rows=1)
+    j = 2
+    tok2 = tok.copy(); tok2[0, j] = tok2[0, j] % 26 + 1
+    _, c1 = O.forward(cfg, w, tok, "fp64", keep=False)
+    _, c2 = O.forward(cfg, w, tok2, "fp64", keep=False)
+    W = 3
+    np.testing.assert_array_equal(c1["ell"][j + W + 1:], c2["ell"][j + W + 1:])
+    assert c1["ell"][j + W] != c2["ell"][j + W]
+
+
+def test_window_at_least_T_equals_full_causal():
+    """P11."""
+    cfg = gi.preset("tiny")
+    w, tok = inputs(cfg)
+    cfg_l = dict(cfg, window_pattern="L", window_long=cfg["seq_len"] + 5)
+    _, c1 = O.forward(cfg, w, tok, "fp64", keep=False)
+    _, c2 = O.forward(cfg_l, w, tok, "fp64", keep=False)
+    np.testing.assert_array_equal(c1["ell"], c2["ell"])
+
+
+def _to_mha(cfg, w):
+    """Replicate GQA K/V weights, value-embedding columns and gate rows per
+    group, giving an equivalent model with one KV head per query head."""
+    H, Hkv, hd = cfg["n_head"], cfg["n_kv_head"], cfg["head_dim"]
+    G = H // Hkv
+    P = O.unpack_params(cfg, w)
+    mcfg = dict(cfg, n_kv_head=H)
+    out = []
+    for name, shape in O.param_layout(mcfg):
+        t = P[name]
+        if name.endswith("wqkv"):
+            q = t[:H * hd]
+            k = t[H * hd:(H + Hkv) * hd].reshape(Hkv, hd, -1)
+            v = t[(H + Hkv) * hd:].reshape(Hkv, hd, -1)
+            t = np.concatenate([q, np.repeat(k, G, 0).reshape(H * hd, -1),
+                                np.repeat(v, G, 0).reshape(H * hd, -1)])
+        elif name.endswith(".ve"):
+            t = np.repeat(t.reshape(t.shape[0], Hkv, hd), G, 1).reshape(t.shape[0], -1)
+        elif name.endswith(".wg"):
+            t = np.repeat(t, G, 0)
+        assert t.shape == shape
+        out.append(t.reshape(-1))
+    return mcfg, np.concatenate(out)
+
+
+def test_gqa_equals_replicated_mha():
+    """P10."""
+    cfg = tiny_plus()
+    w, tok = inputs(cfg, rows=2)
+    mcfg, mw = _to_mha(cfg, w)
+    l1, g1, _ = O.step(cfg, w, tok, "fp64")
+    l2, g2, _ = O.step(mcfg, mw, tok, "fp64")
+    assert l1 == pytest.approx(l2, abs=1e-12)
+    # dW_k of the GQA model = sum over the group of the MHA model's dW_k
+    H, Hkv, hd, D = cfg["n_head"], cfg["n_kv_head"], cfg["head_dim"], cfg["d_model"]
+    G = H // Hkv
+    G1 = O.unpack_params(cfg, g1)["l0.wqkv"]
+    G2 = O.unpack_params(mcfg, g2)["l0.wqkv"]
+    dk1 = G1[H * hd:(H + Hkv) * hd].reshape(Hkv, hd, D)
+    dk2 = G2[H * hd:2 * H * hd].reshape(Hkv, G, hd, D).sum(1)
+    np.testing.assert_allclose(dk1, dk2, atol=1e-12)
+
+
+def test_value_embedding_special_cases():
+    """P12: W_g = 0 gives gate 1.5 exactly; E_l = 0 gives the plain layer."""
+    cfg = tiny_plus()
+    w, tok = inputs(cfg, rows=2)
+    P = O.unpack_params(cfg, w)
+    P["l1.wg"][:] = 0.0
+    _, c = O.forward(cfg, w, tok, "fp64")
+    assert np.all(c["layers"][1]["g"] == 1.5)
+    P["l1.ve"][:] = 0.0
+    l1, _ = O.forward(cfg, w, tok, "fp64", keep=False)
+    plain = dict(cfg, ve_every_odd=0)
+    pw = np.concatenate([P[n].reshape(-1) for n, _ in O.param_layout(plain)])
+    l2, _ = O.forward(plain, pw, tok, "fp64", keep=False)
+    assert l1 == l2
+
+
+def test_tiny_bpb_is_mean_loss_over_ln2():
+    """P15: with every byte length 1, bpb = mean loss / ln 2."""
+    cfg = gi.preset("tiny")
+    w, tok = inputs(cfg)
+    tb = gi.make_token_bytes(cfg)
+    nats, nbytes, bpb = O.eval_bpb(cfg, w, tok, tb, "fp64")
+    loss, _ = O.forward(cfg, w, tok, "fp64", keep=False)
+    assert nbytes == tok[:, 1:].size
+    assert bpb == pytest.approx(loss / math.log(2), rel=1e-14)
+
+
+def test_eval_batches_are_additive():
+    """Sums over a multi-batch set with a ragged last batch equal the sums
+    of the batches taken one by one."""
+    cfg = tiny_plus()
+    w, _ = inputs(cfg)
+    tok = gi.make_eval_tokens(cfg, 11)
+    tb = gi.make_token_bytes(cfg)
+    n1, b1, _ = O.eval_bpb(cfg, w, tok, tb, "fp64", rows_per_batch=4)
+    n2 = sum(O.eval_bpb(cfg, w, tok[i:i + 1], tb, "fp64")[0] for i in range(11))
+    assert n1 == pytest.approx(n2, rel=1e-13)
+
+
+def test_bf16emu_close_to_fp32():
+    """The rounding mode changes results only at bf16 level."""
+    cfg = tiny_plus()
+    w, tok = inputs(cfg, rows=4)
+    l32, g32, _ = O.step(cfg, w.astype(np.float32), tok, "fp32")
+    l16, g16, _ = O.step(cfg, w.astype(np.float32), tok, "bf16emu")
+    assert abs(l32 - l16) < 1e-2
+    assert np.abs(g32 - g16).max() / np.abs(g32).max() < 2e-2
