@@ -1,0 +1,275 @@
+"""Benchmark of the GPT training step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d12]
+
+Times K forward+backward steps of the d12 model (12 layers, width 768, 6
+heads of 128, vocab 32768, 16 rows of 2048 tokens, 'SSSL' windows 1024/2048,
+value embeddings on odd layers) on synthetic seeded inputs already resident
+in HBM, then prints one JSON line.  Besides the step it times, with HIP
+events on the library's stream, every kernel shape the step launches (each
+GEMM, attention forward/backward) through the kernel-level entry points, and
+reports the one with the largest share of the step against its roofline.
+The CPU oracle is timed on a bounded sample of the same workload as a
+reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
+PEAK_F32_MFMA = 157.3e12
+PEAK_HBM = 8.0e12         # bytes/s
+METRIC = "train tokens/s (fwd+bwd) d12 T=2048 on 1 GPU; % bf16 MFMA peak; eval tok/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def visible_pairs(T: int, W: int) -> int:
+    """Number of (query, key) pairs with 0 <= i - j <= W in one row."""
+    W = min(W, T - 1)
+    # query i sees min(i, W) + 1 keys
+    return sum(min(i, W) + 1 for i in range(T))
+
+
+def window_of(cfg, l):
+    pat = cfg["window_pattern"]
+    if not pat:
+        return cfg["seq_len"]
+    return cfg["window_short"] if pat[l % len(pat)] == "S" else cfg["window_long"]
+
+
+def model_flops(cfg):
+    """Algorithmic FLOPs per token: 6 x matmul parameters + 3 x attention
+    forward FLOPs over visible pairs; eval: 2 x matmul params + attention fwd."""
+    D, H, Hkv, hd, V, F = (cfg["d_model"], cfg["n_head"], cfg["n_kv_head"], cfg["head_dim"],
+                           cfg["vocab"], cfg["mlp_mult"] * cfg["d_model"])
+    T, L = cfg["seq_len"], cfg["n_layer"]
+    mm = L * ((H + 2 * Hkv) * hd * D + D * H * hd + 2 * F * D) + V * D
+    pairs = sum(visible_pairs(T, window_of(cfg, l)) for l in range(L))
+    attn_fwd_per_tok = 4 * hd * H * pairs / T
+    return 6 * mm + 3 * attn_fwd_per_tok, 2 * mm + attn_fwd_per_tok, mm
+
+
+def time_events(fn, iters, torch):
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    st.record()
+    for _ in range(iters):
+        fn()
+    en.record()
+    torch.cuda.synchronize()
+    return st.elapsed_time(en) / iters / 1e3
+
+
+def kernel_table(cfg, torch, G, iters=10):
+    """Average duration of every kernel shape the step launches, timed one
+    shape at a time through the kernel entry points."""
+    B, T, D, H, Hkv, hd, V = (cfg["batch"], cfg["seq_len"], cfg["d_model"], cfg["n_head"],
+                              cfg["n_kv_head"], cfg["head_dim"], cfg["vocab"])
+    F, N, L = cfg["mlp_mult"] * D, B * T, cfg["n_layer"]
+    QKV, HD = (H + 2 * Hkv) * hd, H * hd
+    dev = "cuda"
+    bf = torch.bfloat16
+    big = torch.randn(N * max(F, QKV), device=dev).to(bf) * 0.1
+    wbuf = torch.randn(V * D, device=dev).to(bf) * 0.02
+    out = torch.empty(N * max(F, V // 8 * 8, QKV), device=dev, dtype=torch.float32)
+    aux = torch.empty(N * F, device=dev, dtype=bf)
+    chunk = min(N, (512 << 20) // (V * 4) // 256 * 256)
+    rows = []
+    nS = sum(1 for l in range(L) if window_of(cfg, l) < T - 1)
+    gemms = [
+        # name, op, M, N, K, epi, launches per step
+        ("qkv_fwd NT", G.GEMM_NT, N, QKV, D, G.EPI_STORE, L),
+        ("o_fwd NT+res", G.GEMM_NT, N, D, HD, G.EPI_RESADD, L),
+        ("fc_fwd NT+relu2", G.GEMM_NT, N, F, D, G.EPI_RELU2, L),
+        ("proj_fwd NT+res", G.GEMM_NT, N, D, F, G.EPI_RESADD, L),
+        ("lm_fwd NT f32", G.GEMM_NT, chunk, V, D, G.EPI_F32, N // chunk),
+        ("lm_dx NN", G.GEMM_NN, N, D, V, G.EPI_STORE, 1),
+        ("lm_dw TN", G.GEMM_TN, V, D, N, G.EPI_F32, 1),
+        ("proj_dw TN", G.GEMM_TN, D, F, N, G.EPI_F32, L),
+        ("proj_dx NN+drelu2", G.GEMM_NN, N, F, D, G.EPI_DRELU2, L),
+        ("fc_dw TN", G.GEMM_TN, F, D, N, G.EPI_F32, L),
+        ("fc_dx NN", G.GEMM_NN, N, D, F, G.EPI_STORE, L),
+        ("o_dw TN", G.GEMM_TN, D, HD, N, G.EPI_F32, L),
+        ("o_dx NN", G.GEMM_NN, N, HD, D, G.EPI_STORE, L),
+        ("qkv_dw TN", G.GEMM_TN, QKV, D, N, G.EPI_F32, L),
+        ("qkv_dx NN", G.GEMM_NN, N, D, QKV, G.EPI_STORE, L),
+    ]
+    for name, op, M, Nn, K, epi, count in gemms:
+        lda = K if op != G.GEMM_TN else M
+        ldb = K if op == G.GEMM_NT else Nn
+        f32 = epi in (G.EPI_F32, G.EPI_F32_ACC)
+        Cb = out if f32 else aux
+        A = big if op != G.GEMM_TN or M * K <= big.numel() else wbuf
+        Bm = wbuf if op != G.GEMM_TN else big
+        fn = lambda: G.k_gemm(op, M, Nn, K, A, lda, Bm, ldb, Cb, Nn, epi,
+                              aux if epi in (G.EPI_RELU2, G.EPI_DRELU2) else None, G.BF16)
+        t = time_events(fn, iters, torch)
+        rows.append(dict(kernel="gemm " + name, avg_s=t, count=count, flops=2.0 * M * Nn * K,
+                         bound="mfma"))
+    # attention (one short-window and one long-window layer shape)
+    qkv = (torch.randn(N, QKV, device=dev) * 0.3).to(bf)
+    o = torch.empty(N, HD, device=dev, dtype=bf)
+    lse = torch.empty(B * H * T, device=dev, dtype=torch.float32)
+    do = (torch.randn(N, HD, device=dev) * 0.3).to(bf)
+    dqkv = torch.empty_like(qkv)
+    scr = torch.empty(G.k_attn_bwd_scratch_bytes(B, T, H, hd), device=dev, dtype=torch.uint8)
+    for W, count in ((cfg["window_short"], nS), (cfg["window_long"], L - nS)):
+        if count == 0:
+            continue
+        fl = 4.0 * hd * H * B * visible_pairs(T, W)
+        t = time_events(lambda: G.k_attn_fwd(qkv, o, lse, B, T, H, Hkv, hd, W, G.BF16), iters, torch)
+        rows.append(dict(kernel=f"attn_fwd W={W}", avg_s=t, count=count, flops=fl, bound="mfma"))
+        t = time_events(lambda: G.k_attn_bwd(qkv, o, lse, do, dqkv, scr, B, T, H, Hkv, hd, W,
+                                             G.BF16), max(2, iters // 2), torch)
+        rows.append(dict(kernel=f"attn_bwd W={W}", avg_s=t, count=count, flops=2 * fl,
+                         bound="mfma"))
+    del big, wbuf, out, aux, qkv, o, do, dqkv, scr
+    torch.cuda.empty_cache()
+    return rows
+
+
+def cpu_baseline(cfg, seconds_hint=20.0):
+    """The oracle (fp32 mode) on one row of the workload: tokens/s."""
+    import numpy as np
+    import gptinputs as gi
+    import oracle as O
+    c1 = dict(cfg, batch=1)
+    n = O.param_count(c1)
+    w, _ = gi.make_params(c1, n)
+    tok = gi.make_tokens(c1)
+    t0 = time.perf_counter()
+    O.step(c1, w, tok, "fp32")
+    dt = time.perf_counter() - t0
+    threads = os.environ.get("OMP_NUM_THREADS")
+    cores = int(threads) if threads else len(os.sched_getaffinity(0))
+    return {"value": round(cfg["seq_len"] / dt, 2), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"one {cfg['seq_len']}-token row of the {cfg['name']} workload "
+                      f"(fwd+bwd, numpy fp32, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="d12")
+    ap.add_argument("--eval-rows", type=int, default=64)
+    ap.add_argument("--no-kernels", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {a.gpus}); the step is built and "
+              "measured on one GPU's share, see the design notes for how it would shard",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import gptinputs as gi
+    import gpt_pretraining_step_amd as G
+    from gpt_pretraining_step_amd.session import Session
+
+    torch.cuda.set_device(0)
+    cfg = gi.preset(a.config)
+    train_fpt, eval_fpt, mm = model_flops(cfg)
+    B, T = cfg["batch"], cfg["seq_len"]
+    tokens_per_step = B * T
+
+    log("building inputs", a.config)
+    s = Session(cfg, eval_ws=True)
+    w, bits = gi.make_params(cfg, s.n_params)
+    s.set_params(w, bits)
+    s.set_tokens(gi.make_tokens(cfg))
+    del w, bits
+
+    def step():
+        s.fwd()
+        s.bwd()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    loss0 = s.loss.item()
+    assert math.isfinite(loss0), loss0
+    log(f"warmup done, loss {loss0:.4f}")
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    st.record()
+    for _ in range(a.steps):
+        step()
+    en.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = st.elapsed_time(en) / a.steps
+    tok_s = tokens_per_step / (ms / 1e3)
+    mfu = tok_s * train_fpt / PEAK_BF16
+    log(f"step {ms:.2f} ms  {tok_s:,.0f} tok/s  mfu {mfu:.3f}  (wall {wall:.2f} s)")
+
+    # evaluation throughput (forward + CE + bytes reduction)
+    ev_rows = a.eval_rows
+    ev_tok = s.upload(gi.make_eval_tokens(cfg, ev_rows))
+    tb = s.upload(gi.make_token_bytes(cfg))
+    s.evaluate(ev_tok, tb)
+    torch.cuda.synchronize()
+    t_ev = time_events(lambda: s.evaluate(ev_tok, tb), 2, torch)
+    eval_tok_s = ev_rows * T / t_ev
+    bpb = s.bpb.cpu().numpy().tolist()
+    log(f"eval {eval_tok_s:,.0f} tok/s, bpb {bpb[2]:.4f}")
+
+    roof = None
+    table = []
+    if not a.no_kernels:
+        del s
+        torch.cuda.empty_cache()
+        table = kernel_table(cfg, torch, G)
+        for r in table:
+            r["per_step_s"] = r["avg_s"] * r["count"]
+            r["tflops"] = r["flops"] / r["avg_s"] / 1e12
+            log(f"  {r['kernel']:<24} {r['avg_s'] * 1e3:8.3f} ms x{r['count']:<3} "
+                f"{r['tflops']:7.1f} TFLOP/s")
+        dom = max(table, key=lambda r: r["per_step_s"])
+        ach = dom["flops"] / dom["avg_s"]
+        roof = {"bound": dom["bound"], "kernel": dom["kernel"],
+                "achieved": round(ach / 1e12, 2), "peak": PEAK_BF16 / 1e12,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16, 4), "traffic": None,
+                "avg_launch_ms": round(dom["avg_s"] * 1e3, 4),
+                "share_of_step": round(dom["per_step_s"] / (ms / 1e3), 3)}
+
+    cpu = None if a.no_cpu else cpu_baseline(cfg)
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Zipf(1.1) tokens, N(0,0.02) random-init weights)",
+        "config": {"workload": f"{a.config} fwd+bwd step: {cfg['n_layer']} layers, "
+                               f"d_model {cfg['d_model']}, {cfg['n_head']}x{cfg['head_dim']} "
+                               f"heads ({cfg['n_kv_head']} KV), vocab {cfg['vocab']}, "
+                               f"{B} rows x T={T} ({tokens_per_step} tokens), windows "
+                               f"'{cfg['window_pattern']}' {cfg['window_short']}/"
+                               f"{cfg['window_long']}, value embeddings on odd layers",
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "mfu_bf16": round(mfu, 4), "train_flop_per_token": train_fpt,
+        "eval_tokens_per_s": round(eval_tok_s, 1), "eval_rows": ev_rows, "eval_bpb": bpb[2],
+        "roofline": roof, "cpu_baseline": cpu,
+        "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
+                    for r in table],
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

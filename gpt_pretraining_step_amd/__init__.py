@@ -1,0 +1,219 @@
+"""MI355X (gfx950) GPT training step: thin Python binding of libgptstep.so.
+
+Argument marshalling only.  Every step of the forward, backward and
+evaluation runs in the library's HIP kernels; torch provides device memory
+(tensors) and the current stream.  If the library is not built this module
+raises on first use: there is no CPU fallback.
+
+The C ABI and its conventions are documented in include/gpt_step.h.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgptstep.so")
+
+F32, BF16 = 0, 1
+MODE_TRAIN, MODE_EVAL = 0, 1
+GEMM_NT, GEMM_NN, GEMM_TN = 0, 1, 2
+EPI_STORE, EPI_RESADD, EPI_RELU2, EPI_DRELU2, EPI_F32, EPI_F32_ACC = range(6)
+P_WTE, P_WQKV, P_WO, P_WFC, P_WPROJ, P_VE, P_WG, P_WLM = range(8)
+(WS_ELL, WS_LOSS, WS_NONFINITE, WS_X_H, WS_X_QKV, WS_X_O, WS_X_LSE, WS_X_H2,
+ WS_X_A, WS_X_HF) = range(10)
+
+
+class GptError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"gpt_step status {status}: {msg}")
+        self.status = status
+
+
+class GptConfig(C.Structure):
+    _fields_ = [
+        ("n_layer", C.c_int32), ("d_model", C.c_int32), ("n_head", C.c_int32),
+        ("n_kv_head", C.c_int32), ("head_dim", C.c_int32), ("vocab", C.c_int32),
+        ("seq_len", C.c_int32), ("batch", C.c_int32), ("mlp_mult", C.c_int32),
+        ("ve_gate_channels", C.c_int32), ("window_pattern", C.c_char * 16),
+        ("window_short", C.c_int32), ("window_long", C.c_int32),
+        ("ve_every_odd", C.c_int32), ("rope_base", C.c_float),
+        ("norm_eps", C.c_float), ("dtype", C.c_int32),
+    ]
+
+
+def make_config(d: dict) -> GptConfig:
+    """A GptConfig from a dict with the struct's field names."""
+    c = GptConfig()
+    for name, _ in GptConfig._fields_:
+        v = d[name]
+        if name == "window_pattern":
+            v = (v or "").encode()
+        setattr(c, name, v)
+    return c
+
+
+_lib = None
+_vp, _i32, _i64, _f32, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+_cfgp = C.POINTER(GptConfig)
+
+_SIGS = {
+    "gpt_validate_config": (C.c_int, [_cfgp]),
+    "gpt_param_count": (_i64, [_cfgp]),
+    "gpt_param_offset": (_i64, [_cfgp, C.c_int, C.c_int]),
+    "gpt_workspace_bytes": (_sz, [_cfgp, C.c_int]),
+    "gpt_ws_offset": (_i64, [_cfgp, C.c_int, C.c_int]),
+    "gpt_step_fwd": (C.c_int, [_cfgp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "gpt_step_bwd": (C.c_int, [_cfgp, _vp, _vp, _vp, _sz, _vp, C.c_int, _vp]),
+    "gpt_eval_bpb": (C.c_int, [_cfgp, _vp, _vp, _i64, _vp, _vp, _sz, _vp, _vp]),
+    "gpt_status_string": (C.c_char_p, [C.c_int]),
+    "gpt_last_error": (C.c_char_p, []),
+    "gpt_k_rmsnorm_fwd": (C.c_int, [_vp, _vp, _vp, _i64, _i32, _f32, _i32, _vp]),
+    "gpt_k_rmsnorm_bwd": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp]),
+    "gpt_k_gemm": (C.c_int, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                             _i32, _vp, _i32, _vp]),
+    "gpt_k_rope_table": (C.c_int, [_vp, _i32, _i32, _f32, _vp]),
+    "gpt_k_rope_qknorm_fwd": (C.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                        _f32, _i32, _vp]),
+    "gpt_k_rope_qknorm_bwd": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                        _i32, _i32, _vp]),
+    "gpt_k_attn_fwd": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "gpt_k_attn_bwd_scratch_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "gpt_k_attn_bwd": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                 _i32, _i32, _vp]),
+    "gpt_k_ce": (C.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp]),
+}
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m gpt_pretraining_step_amd.build` (no CPU fallback exists)")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return sorted(_SIGS)
+
+
+def _check(status: int):
+    if status != 0:
+        raise GptError(status, lib().gpt_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+# ------------------------------------------------------------ model level
+def validate_config(cfg: GptConfig) -> int:
+    return lib().gpt_validate_config(C.byref(cfg))
+
+
+def param_count(cfg: GptConfig) -> int:
+    n = lib().gpt_param_count(C.byref(cfg))
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def param_offset(cfg: GptConfig, which: int, layer: int = 0) -> int:
+    n = lib().gpt_param_offset(C.byref(cfg), which, layer)
+    if n < -1:
+        _check(int(n))
+    return int(n)
+
+
+def workspace_bytes(cfg: GptConfig, mode: int = MODE_TRAIN) -> int:
+    n = lib().gpt_workspace_bytes(C.byref(cfg), mode)
+    if n == 0:
+        raise GptError(-1, lib().gpt_last_error().decode())
+    return int(n)
+
+
+def ws_offset(cfg: GptConfig, which: int, layer: int = 0) -> int:
+    n = lib().gpt_ws_offset(C.byref(cfg), which, layer)
+    if n < -1:
+        _check(int(n))
+    return int(n)
+
+
+def step_fwd(cfg, params, tokens, ws, loss, stream=None):
+    _check(lib().gpt_step_fwd(C.byref(cfg), _ptr(params), _ptr(tokens), _ptr(ws),
+                              ws.numel() * ws.element_size(), _ptr(loss), _stream(stream)))
+
+
+def step_bwd(cfg, params, tokens, ws, grads, accumulate=False, stream=None):
+    _check(lib().gpt_step_bwd(C.byref(cfg), _ptr(params), _ptr(tokens), _ptr(ws),
+                              ws.numel() * ws.element_size(), _ptr(grads),
+                              1 if accumulate else 0, _stream(stream)))
+
+
+def eval_bpb(cfg, params, tokens, token_bytes, ws, out, stream=None):
+    _check(lib().gpt_eval_bpb(C.byref(cfg), _ptr(params), _ptr(tokens), tokens.shape[0],
+                              _ptr(token_bytes), _ptr(ws), ws.numel() * ws.element_size(),
+                              _ptr(out), _stream(stream)))
+
+
+# ------------------------------------------------------------ kernel level
+def k_rmsnorm_fwd(x, y, r, rows, dim, eps, dtype, stream=None):
+    _check(lib().gpt_k_rmsnorm_fwd(_ptr(x), _ptr(y), _ptr(r), rows, dim, eps, dtype,
+                                   _stream(stream)))
+
+
+def k_rmsnorm_bwd(dy, y, r, dres, dx, rows, dim, dtype, stream=None):
+    _check(lib().gpt_k_rmsnorm_bwd(_ptr(dy), _ptr(y), _ptr(r), _ptr(dres), _ptr(dx), rows, dim,
+                                   dtype, _stream(stream)))
+
+
+def k_gemm(op, M, N, K, A, lda, B, ldb, Cm, ldc, epi, aux, dtype, stream=None):
+    _check(lib().gpt_k_gemm(op, M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(Cm), ldc, epi,
+                            _ptr(aux), dtype, _stream(stream)))
+
+
+def k_rope_table(cs, T, hd, base, stream=None):
+    _check(lib().gpt_k_rope_table(_ptr(cs), T, hd, base, _stream(stream)))
+
+
+def k_rope_qknorm_fwd(qkv, rq, rk, cs, B, T, H, Hkv, hd, eps, dtype, stream=None):
+    _check(lib().gpt_k_rope_qknorm_fwd(_ptr(qkv), _ptr(rq), _ptr(rk), _ptr(cs), B, T, H, Hkv,
+                                       hd, eps, dtype, _stream(stream)))
+
+
+def k_rope_qknorm_bwd(dqkv, qkv, rq, rk, cs, B, T, H, Hkv, hd, dtype, stream=None):
+    _check(lib().gpt_k_rope_qknorm_bwd(_ptr(dqkv), _ptr(qkv), _ptr(rq), _ptr(rk), _ptr(cs), B,
+                                       T, H, Hkv, hd, dtype, _stream(stream)))
+
+
+def k_attn_fwd(qkv, o, lse, B, T, H, Hkv, hd, window, dtype, stream=None):
+    _check(lib().gpt_k_attn_fwd(_ptr(qkv), _ptr(o), _ptr(lse), B, T, H, Hkv, hd, window, dtype,
+                                _stream(stream)))
+
+
+def k_attn_bwd_scratch_bytes(B, T, H, hd):
+    return int(lib().gpt_k_attn_bwd_scratch_bytes(B, T, H, hd))
+
+
+def k_attn_bwd(qkv, o, lse, dout, dqkv, scratch, B, T, H, Hkv, hd, window, dtype, stream=None):
+    _check(lib().gpt_k_attn_bwd(_ptr(qkv), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dqkv),
+                                _ptr(scratch), B, T, H, Hkv, hd, window, dtype, _stream(stream)))
+
+
+def k_ce(z, tgt, rows, V, ell, lse, dz, grad_scale, dtype, stream=None):
+    _check(lib().gpt_k_ce(_ptr(z), _ptr(tgt), rows, V, _ptr(ell), _ptr(lse), _ptr(dz),
+                          grad_scale, dtype, _stream(stream)))

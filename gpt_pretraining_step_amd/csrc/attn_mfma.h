@@ -1,0 +1,14 @@
+// MFMA flash attention for head_dim 128 on gfx950 (declarations).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gk {
+bool attn_mfma_supported(int T, int H, int Hkv, int hd);
+hipError_t attn_mfma_fwd(const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv,
+                         int hd, int W, hipStream_t s);
+size_t attn_mfma_bwd_scratch_bytes(int B, int T, int H, int hd);
+hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const void* dout,
+                         void* dqkv, float* delta, void* scratch, int B, int T, int H, int Hkv,
+                         int hd, int W, hipStream_t s);
+}  // namespace gk

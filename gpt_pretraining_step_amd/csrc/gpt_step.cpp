@@ -1,0 +1,631 @@
+// Host side of the GPT-step library: config validation, parameter layout,
+// workspace planning, the forward / backward / eval launch sequences and the
+// C ABI declared in include/gpt_step.h.
+#include "gpt_step.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+#define HIP_TRY(expr)                                                              \
+  do {                                                                             \
+    hipError_t e_ = (expr);                                                        \
+    if (e_ != hipSuccess)                                                          \
+      return fail(GPT_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));     \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t pad256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// ------------------------------------------------------------- the model
+struct Model {
+  int L, D, H, Hkv, hd, V, T, B, F, C, QKV;
+  int ve_odd;
+  float base, eps;
+  gk::DType dt;
+  int es;                     // element size of the storage dtype
+  std::string pattern;
+  int wS, wL;
+
+  bool is_ve(int l) const { return ve_odd && (l % 2 == 1); }
+  int window(int l) const {
+    if (pattern.empty()) return T;
+    char c = pattern[l % pattern.size()];
+    return c == 'S' ? wS : wL;
+  }
+};
+
+int validate(const gpt_config* c, Model* m) {
+  if (!c) return fail(GPT_ERR_INVALID_ARG, "config is null");
+  if (c->n_layer < 1 || c->d_model < 1 || c->n_head < 1 || c->n_kv_head < 1 ||
+      c->vocab < 2 || c->seq_len < 1 || c->batch < 1 || c->mlp_mult < 1)
+    return fail(GPT_ERR_INVALID_ARG, "sizes must be positive (vocab >= 2)");
+  if (c->n_head % c->n_kv_head)
+    return fail(GPT_ERR_UNSUPPORTED_CONFIG, "n_head (%d) must be a multiple of n_kv_head (%d)",
+                c->n_head, c->n_kv_head);
+  int hd = c->head_dim;
+  if (!(hd == 4 || hd == 8 || hd == 16 || hd == 32 || hd == 64 || hd == 128))
+    return fail(GPT_ERR_UNSUPPORTED_CONFIG, "head_dim %d not in {4,8,16,32,64,128}", hd);
+  if (c->dtype != GPT_F32 && c->dtype != GPT_BF16)
+    return fail(GPT_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
+  if (!(c->norm_eps > 0.f) || !(c->rope_base > 0.f))
+    return fail(GPT_ERR_INVALID_ARG, "norm_eps and rope_base must be positive");
+  size_t plen = strnlen(c->window_pattern, sizeof(c->window_pattern));
+  if (plen == sizeof(c->window_pattern))
+    return fail(GPT_ERR_INVALID_ARG, "window_pattern is not NUL-terminated");
+  for (size_t i = 0; i < plen; ++i)
+    if (c->window_pattern[i] != 'S' && c->window_pattern[i] != 'L')
+      return fail(GPT_ERR_INVALID_ARG, "window_pattern may hold only 'S' and 'L'");
+  if (plen && (c->window_short < 0 || c->window_long < 0))
+    return fail(GPT_ERR_INVALID_ARG, "windows must be >= 0");
+  if (c->ve_every_odd && c->n_layer > 1 &&
+      (c->ve_gate_channels < 1 || c->ve_gate_channels > c->d_model))
+    return fail(GPT_ERR_INVALID_ARG, "ve_gate_channels must be in [1, d_model]");
+  int64_t N = (int64_t)c->batch * c->seq_len;
+  int64_t qkv = (int64_t)(c->n_head + 2 * c->n_kv_head) * hd;
+  if (N > (1LL << 30) || (int64_t)c->mlp_mult * c->d_model > (1 << 30) || qkv > (1 << 30))
+    return fail(GPT_ERR_UNSUPPORTED_CONFIG, "sizes too large");
+  if (c->n_kv_head > 64) return fail(GPT_ERR_UNSUPPORTED_CONFIG, "n_kv_head > 64");
+  if (m) {
+    m->L = c->n_layer; m->D = c->d_model; m->H = c->n_head; m->Hkv = c->n_kv_head;
+    m->hd = hd; m->V = c->vocab; m->T = c->seq_len; m->B = c->batch;
+    m->F = c->mlp_mult * c->d_model; m->C = c->ve_gate_channels;
+    m->QKV = (int)qkv; m->ve_odd = c->ve_every_odd ? 1 : 0;
+    m->base = c->rope_base; m->eps = c->norm_eps;
+    m->dt = c->dtype == GPT_BF16 ? gk::BF16 : gk::F32;
+    m->es = c->dtype == GPT_BF16 ? 2 : 4;
+    m->pattern.assign(c->window_pattern, plen);
+    m->wS = c->window_short; m->wL = c->window_long;
+  }
+  return GPT_OK;
+}
+
+// element offsets of every tensor in the flat parameter buffer
+struct ParamLayout {
+  int64_t wte, wlm, total;
+  std::vector<int64_t> wqkv, wo, wfc, wproj, ve, wg;
+};
+
+ParamLayout param_layout(const Model& m) {
+  ParamLayout p;
+  int64_t off = 0;
+  p.wte = off; off += (int64_t)m.V * m.D;
+  for (int l = 0; l < m.L; ++l) {
+    p.wqkv.push_back(off); off += (int64_t)m.QKV * m.D;
+    p.wo.push_back(off);   off += (int64_t)m.D * m.H * m.hd;
+    p.wfc.push_back(off);  off += (int64_t)m.F * m.D;
+    p.wproj.push_back(off); off += (int64_t)m.D * m.F;
+    if (m.is_ve(l)) {
+      p.ve.push_back(off); off += (int64_t)m.V * m.Hkv * m.hd;
+      p.wg.push_back(off); off += (int64_t)m.Hkv * m.C;
+    } else {
+      p.ve.push_back(-1);
+      p.wg.push_back(-1);
+    }
+  }
+  p.wlm = off; off += (int64_t)m.V * m.D;
+  p.total = off;
+  return p;
+}
+
+// ------------------------------------------------------- workspace plan
+struct LayerBufs {
+  size_t h, r, qkv, rq, rk, g, o, lse, h2, r2, u, a;
+};
+
+struct Plan {
+  int64_t N, chunk;
+  size_t cs, x, hf, rf, ell, lse_z, loss, flag, logits, dz, evacc;
+  std::vector<LayerBufs> layers;     // train: one per layer; eval: one shared
+  // backward scratch
+  size_t dx, dh, du, dout, dqkv, attn_scr, vez;
+  size_t total;
+};
+
+Plan make_plan(const Model& m, int mode) {
+  Plan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += pad256(bytes); return o; };
+  const int64_t N = (int64_t)m.B * m.T;
+  p.N = N;
+  const size_t es = m.es;
+  p.chunk = N;
+  const int64_t max_logit_bytes = 512LL << 20;
+  if (N * (int64_t)m.V * 4 > max_logit_bytes) {
+    int64_t c = max_logit_bytes / ((int64_t)m.V * 4);
+    c = (c / 256) * 256;
+    if (c < 256) c = 256;
+    p.chunk = c < N ? c : N;
+  }
+  p.cs = take((size_t)m.T * (m.hd / 2) * 8);
+  p.x = take(N * m.D * es);
+  p.hf = take(N * m.D * es);
+  p.rf = take(N * 4);
+  p.ell = take(N * 4);
+  p.lse_z = take(N * 4);
+  p.loss = take(4);
+  p.flag = take(4);
+  p.evacc = take(3 * 8);
+  p.logits = take((size_t)p.chunk * m.V * 4);
+  p.dz = mode == GPT_MODE_TRAIN ? take((size_t)N * m.V * es) : 0;
+  const int nl = mode == GPT_MODE_TRAIN ? m.L : 1;
+  for (int l = 0; l < nl; ++l) {
+    LayerBufs b;
+    b.h = take(N * m.D * es);
+    b.r = take(N * 4);
+    b.qkv = take(N * (size_t)m.QKV * es);
+    b.rq = take(N * (size_t)m.H * 4);
+    b.rk = take(N * (size_t)m.Hkv * 4);
+    b.g = take(N * (size_t)m.Hkv * 4);
+    b.o = take(N * (size_t)m.H * m.hd * es);
+    b.lse = take(N * (size_t)m.H * 4);
+    b.h2 = take(N * m.D * es);
+    b.r2 = take(N * 4);
+    b.u = take(N * (size_t)m.F * es);
+    b.a = take(N * (size_t)m.F * es);
+    p.layers.push_back(b);
+  }
+  if (mode == GPT_MODE_TRAIN) {
+    p.dx = take(N * m.D * es);
+    p.dh = take(N * m.D * es);
+    p.du = take(N * (size_t)m.F * es);
+    p.dout = take(N * (size_t)m.H * m.hd * es);
+    p.dqkv = take(N * (size_t)m.QKV * es);
+    p.attn_scr = take(gk::attn_bwd_scratch_bytes(m.B, m.T, m.H, m.hd));
+    p.vez = take(N * (size_t)m.Hkv * 4);
+  } else {
+    p.dx = p.dh = p.du = p.dout = p.dqkv = p.attn_scr = p.vez = 0;
+  }
+  p.total = off;
+  return p;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return (T*)((char*)ws + off); }
+
+const void* elem(const void* base, int64_t idx, int es) {
+  return (const char*)base + idx * es;
+}
+
+// ------------------------------------------------------ launch sequences
+// Forward over one batch of `rows` rows (rows <= m.B).  In TRAIN mode every
+// layer's activations stay in ws for the backward; in EVAL mode one set of
+// layer buffers is reused and no softmax gradient is formed.
+int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const void* params,
+                const int32_t* tokens, int rows, void* ws, int mode, float* loss_dev,
+                hipStream_t s) {
+  Model m = m0;
+  m.B = rows;
+  const int64_t N = (int64_t)rows * m.T;
+  const int es = m.es;
+  const gk::DType dt = m.dt;
+  void* x = at<void>(ws, p.x);
+  float* cs = at<float>(ws, p.cs);
+  HIP_TRY(gk::rope_table(cs, m.T, m.hd, m.base, s));
+  HIP_TRY(gk::embed_fwd(tokens, rows, m.T, elem(params, pl.wte, es), x, m.D, dt, s));
+  for (int l = 0; l < m.L; ++l) {
+    const LayerBufs& b = p.layers[mode == GPT_MODE_TRAIN ? l : 0];
+    void* h = at<void>(ws, b.h);
+    void* qkv = at<void>(ws, b.qkv);
+    void* o = at<void>(ws, b.o);
+    void* h2 = at<void>(ws, b.h2);
+    void* u = at<void>(ws, b.u);
+    void* a = at<void>(ws, b.a);
+    HIP_TRY(gk::rmsnorm_fwd(x, h, at<float>(ws, b.r), N, m.D, m.eps, dt, s));
+    gk::GemmDesc g{gk::OP_NT, N, m.QKV, m.D, h, m.D, elem(params, pl.wqkv[l], es), m.D,
+                   qkv, m.QKV, gk::E_STORE, nullptr};
+    HIP_TRY(gk::gemm(g, dt, s));
+    if (m.is_ve(l))
+      HIP_TRY(gk::ve_fwd(tokens, rows, m.T, h, m.D, elem(params, pl.wg[l], es), m.C,
+                         elem(params, pl.ve[l], es), qkv, m.QKV, (m.H + m.Hkv) * m.hd,
+                         at<float>(ws, b.g), m.Hkv, m.hd, dt, s));
+    HIP_TRY(gk::rope_qknorm_fwd(qkv, at<float>(ws, b.rq), at<float>(ws, b.rk), cs, rows, m.T,
+                                m.H, m.Hkv, m.hd, m.eps, dt, s));
+    HIP_TRY(gk::attn_fwd(qkv, o, at<float>(ws, b.lse), rows, m.T, m.H, m.Hkv, m.hd, m.window(l),
+                         dt, s));
+    g = gk::GemmDesc{gk::OP_NT, N, m.D, (int64_t)m.H * m.hd, o, (int64_t)m.H * m.hd,
+                     elem(params, pl.wo[l], es), (int64_t)m.H * m.hd, x, m.D, gk::E_RESADD,
+                     nullptr};
+    HIP_TRY(gk::gemm(g, dt, s));
+    HIP_TRY(gk::rmsnorm_fwd(x, h2, at<float>(ws, b.r2), N, m.D, m.eps, dt, s));
+    g = gk::GemmDesc{gk::OP_NT, N, m.F, m.D, h2, m.D, elem(params, pl.wfc[l], es), m.D, u, m.F,
+                     gk::E_RELU2, a};
+    HIP_TRY(gk::gemm(g, dt, s));
+    g = gk::GemmDesc{gk::OP_NT, N, m.D, m.F, a, m.F, elem(params, pl.wproj[l], es), m.F, x, m.D,
+                     gk::E_RESADD, nullptr};
+    HIP_TRY(gk::gemm(g, dt, s));
+  }
+  void* hf = at<void>(ws, p.hf);
+  HIP_TRY(gk::rmsnorm_fwd(x, hf, at<float>(ws, p.rf), N, m.D, m.eps, dt, s));
+  float* logits = at<float>(ws, p.logits);
+  const float inv_n = 1.0f / (float)N;
+  for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
+    const int64_t nr = N - r0 < p.chunk ? N - r0 : p.chunk;
+    gk::GemmDesc g{gk::OP_NT, nr, m.V, m.D, elem(hf, r0 * m.D, es), m.D,
+                   elem(params, pl.wlm, es), m.D, logits, m.V, gk::E_F32, nullptr};
+    HIP_TRY(gk::gemm(g, dt, s));
+    // targets of rows r0.. : the ce kernel maps row -> token position itself
+    void* dz = mode == GPT_MODE_TRAIN ? (void*)((char*)ws + p.dz + (size_t)r0 * m.V * es) : nullptr;
+    HIP_TRY(gk::ce_rows(logits, nr, m.V, tokens, m.T, 0, at<float>(ws, p.ell) + r0,
+                        at<float>(ws, p.lse_z) + r0, dz, inv_n, dt, s, r0));
+  }
+  if (mode == GPT_MODE_TRAIN)
+    HIP_TRY(gk::loss_reduce(at<float>(ws, p.ell), N, at<float>(ws, p.loss), loss_dev,
+                            at<int>(ws, p.flag), s));
+  return GPT_OK;
+}
+
+int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const void* params,
+                 const int32_t* tokens, void* ws, float* grads, int accumulate, hipStream_t s) {
+  const int64_t N = p.N;
+  const int es = m.es;
+  const gk::DType dt = m.dt;
+  const gk::Epi wepi = accumulate ? gk::E_F32_ACC : gk::E_F32;
+  void* dx = at<void>(ws, p.dx);
+  void* dh = at<void>(ws, p.dh);
+  void* du = at<void>(ws, p.du);
+  void* dout = at<void>(ws, p.dout);
+  void* dqkv = at<void>(ws, p.dqkv);
+  float* vez = at<float>(ws, p.vez);
+  const float* cs = at<float>(ws, p.cs);
+  const void* dz = at<void>(ws, p.dz);
+  const void* hf = at<void>(ws, p.hf);
+
+  // embedding tables are scatter-added: clear them first unless accumulating
+  if (!accumulate) {
+    HIP_TRY(gk::fill_zero(grads + pl.wte, (int64_t)m.V * m.D * 4, s));
+    for (int l = 0; l < m.L; ++l)
+      if (m.is_ve(l)) HIP_TRY(gk::fill_zero(grads + pl.ve[l], (int64_t)m.V * m.Hkv * m.hd * 4, s));
+  }
+  // lm_head
+  gk::GemmDesc g{gk::OP_TN, m.V, m.D, N, dz, m.V, hf, m.D, grads + pl.wlm, m.D, wepi, nullptr};
+  HIP_TRY(gk::gemm(g, dt, s));
+  g = gk::GemmDesc{gk::OP_NN, N, m.D, m.V, dz, m.V, elem(params, pl.wlm, es), m.D, dh, m.D,
+                   gk::E_STORE, nullptr};
+  HIP_TRY(gk::gemm(g, dt, s));
+  HIP_TRY(gk::rmsnorm_bwd(dh, hf, at<float>(ws, p.rf), nullptr, dx, N, m.D, nullptr, nullptr, 0,
+                          0, dt, s));
+  for (int l = m.L - 1; l >= 0; --l) {
+    const LayerBufs& b = p.layers[l];
+    const void* h = at<void>(ws, b.h);
+    const void* qkv = at<void>(ws, b.qkv);
+    const void* o = at<void>(ws, b.o);
+    const void* h2 = at<void>(ws, b.h2);
+    void* u = at<void>(ws, b.u);
+    const void* a = at<void>(ws, b.a);
+    const int64_t HD = (int64_t)m.H * m.hd;
+    // MLP
+    g = gk::GemmDesc{gk::OP_TN, m.D, m.F, N, dx, m.D, a, m.F, grads + pl.wproj[l], m.F, wepi,
+                     nullptr};
+    HIP_TRY(gk::gemm(g, dt, s));
+    g = gk::GemmDesc{gk::OP_NN, N, m.F, m.D, dx, m.D, elem(params, pl.wproj[l], es), m.F, du,
+                     m.F, gk::E_DRELU2, u};
+    HIP_TRY(gk::gemm(g, dt, s));
+    g = gk::GemmDesc{gk::OP_TN, m.F, m.D, N, du, m.F, h2, m.D, grads + pl.wfc[l], m.D, wepi,
+                     nullptr};
+    HIP_TRY(gk::gemm(g, dt, s));
+    g = gk::GemmDesc{gk::OP_NN, N, m.D, m.F, du, m.F, elem(params, pl.wfc[l], es), m.D, dh, m.D,
+                     gk::E_STORE, nullptr};
+    HIP_TRY(gk::gemm(g, dt, s));
+    HIP_TRY(gk::rmsnorm_bwd(dh, h2, at<float>(ws, b.r2), dx, dx, N, m.D, nullptr, nullptr, 0, 0,
+                            dt, s));
+    // attention
+    g = gk::GemmDesc{gk::OP_TN, m.D, HD, N, dx, m.D, o, HD, grads + pl.wo[l], HD, wepi, nullptr};
+    HIP_TRY(gk::gemm(g, dt, s));
+    g = gk::GemmDesc{gk::OP_NN, N, HD, m.D, dx, m.D, elem(params, pl.wo[l], es), HD, dout, HD,
+                     gk::E_STORE, nullptr};
+    HIP_TRY(gk::gemm(g, dt, s));
+    HIP_TRY(gk::attn_bwd(qkv, o, at<float>(ws, b.lse), dout, dqkv, at<void>(ws, p.attn_scr),
+                         m.B, m.T, m.H, m.Hkv, m.hd, m.window(l), dt, s));
+    HIP_TRY(gk::rope_qknorm_bwd(dqkv, qkv, at<float>(ws, b.rq), at<float>(ws, b.rk), cs, m.B,
+                                m.T, m.H, m.Hkv, m.hd, dt, s));
+    const bool ve = m.is_ve(l);
+    if (ve) {
+      HIP_TRY(gk::ve_bwd(tokens, m.B, m.T, dqkv, m.QKV, (m.H + m.Hkv) * m.hd,
+                         elem(params, pl.ve[l], es), at<float>(ws, b.g), vez, grads + pl.ve[l],
+                         m.Hkv, m.hd, dt, s));
+      HIP_TRY(gk::ve_wgrad(vez, h, m.D, N, m.Hkv, m.C, grads + pl.wg[l], accumulate, dt, s));
+    }
+    g = gk::GemmDesc{gk::OP_TN, m.QKV, m.D, N, dqkv, m.QKV, h, m.D, grads + pl.wqkv[l], m.D,
+                     wepi, nullptr};
+    HIP_TRY(gk::gemm(g, dt, s));
+    g = gk::GemmDesc{gk::OP_NN, N, m.D, m.QKV, dqkv, m.QKV, elem(params, pl.wqkv[l], es), m.D,
+                     dh, m.D, gk::E_STORE, nullptr};
+    HIP_TRY(gk::gemm(g, dt, s));
+    HIP_TRY(gk::rmsnorm_bwd(dh, h, at<float>(ws, b.r), dx, dx, N, m.D, ve ? vez : nullptr,
+                            ve ? elem(params, pl.wg[l], es) : nullptr, m.Hkv, m.C, dt, s));
+  }
+  HIP_TRY(gk::embed_bwd(tokens, m.B, m.T, dx, m.D, grads + pl.wte, m.D, dt, s));
+  return GPT_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* q : ps) {
+    if (!q) return fail(GPT_ERR_INVALID_ARG, "a required pointer is null");
+    if (!aligned16(q)) return fail(GPT_ERR_MISALIGNED, "a pointer is not 16-byte aligned");
+  }
+  return GPT_OK;
+}
+
+}  // namespace
+
+// =============================================================== C ABI
+extern "C" {
+
+int gpt_validate_config(const gpt_config* cfg) { return validate(cfg, nullptr); }
+
+int64_t gpt_param_count(const gpt_config* cfg) {
+  Model m;
+  int st = validate(cfg, &m);
+  if (st) return st;
+  return param_layout(m).total;
+}
+
+int64_t gpt_param_offset(const gpt_config* cfg, int which, int layer) {
+  Model m;
+  int st = validate(cfg, &m);
+  if (st) return st;
+  ParamLayout p = param_layout(m);
+  if (which == GPT_P_WTE) return p.wte;
+  if (which == GPT_P_WLM) return p.wlm;
+  if (layer < 0 || layer >= m.L) return fail(GPT_ERR_INVALID_ARG, "layer out of range");
+  switch (which) {
+    case GPT_P_WQKV: return p.wqkv[layer];
+    case GPT_P_WO: return p.wo[layer];
+    case GPT_P_WFC: return p.wfc[layer];
+    case GPT_P_WPROJ: return p.wproj[layer];
+    case GPT_P_VE: return p.ve[layer];
+    case GPT_P_WG: return p.wg[layer];
+  }
+  return fail(GPT_ERR_INVALID_ARG, "unknown tensor id %d", which);
+}
+
+size_t gpt_workspace_bytes(const gpt_config* cfg, int mode) {
+  Model m;
+  if (validate(cfg, &m)) return 0;
+  if (mode != GPT_MODE_TRAIN && mode != GPT_MODE_EVAL) {
+    fail(GPT_ERR_INVALID_ARG, "unknown workspace mode %d", mode);
+    return 0;
+  }
+  return make_plan(m, mode).total;
+}
+
+int64_t gpt_ws_offset(const gpt_config* cfg, int which, int layer) {
+  Model m;
+  int st = validate(cfg, &m);
+  if (st) return st;
+  Plan p = make_plan(m, GPT_MODE_TRAIN);
+  switch (which) {
+    case GPT_WS_ELL: return (int64_t)p.ell;
+    case GPT_WS_LOSS: return (int64_t)p.loss;
+    case GPT_WS_NONFINITE: return (int64_t)p.flag;
+    case GPT_WS_X_HF: return (int64_t)p.hf;
+  }
+  if (layer < 0 || layer >= m.L) return fail(GPT_ERR_INVALID_ARG, "layer out of range");
+  const LayerBufs& b = p.layers[layer];
+  switch (which) {
+    case GPT_WS_X_H: return (int64_t)b.h;
+    case GPT_WS_X_QKV: return (int64_t)b.qkv;
+    case GPT_WS_X_O: return (int64_t)b.o;
+    case GPT_WS_X_LSE: return (int64_t)b.lse;
+    case GPT_WS_X_H2: return (int64_t)b.h2;
+    case GPT_WS_X_A: return (int64_t)b.a;
+  }
+  return fail(GPT_ERR_INVALID_ARG, "unknown workspace item %d", which);
+}
+
+int gpt_step_fwd(const gpt_config* cfg, const void* params, const int32_t* tokens, void* ws,
+                 size_t ws_bytes, float* loss_dev, hipStream_t stream) {
+  Model m;
+  int st = validate(cfg, &m);
+  if (st) return st;
+  if ((st = check_ptrs({params, tokens, ws, loss_dev}))) return st;
+  Plan p = make_plan(m, GPT_MODE_TRAIN);
+  if (ws_bytes < p.total)
+    return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, p.total);
+  return run_forward(m, p, param_layout(m), params, tokens, m.B, ws, GPT_MODE_TRAIN, loss_dev,
+                     stream);
+}
+
+int gpt_step_bwd(const gpt_config* cfg, const void* params, const int32_t* tokens, void* ws,
+                 size_t ws_bytes, float* grads, int accumulate, hipStream_t stream) {
+  Model m;
+  int st = validate(cfg, &m);
+  if (st) return st;
+  if ((st = check_ptrs({params, tokens, ws, grads}))) return st;
+  if (accumulate != 0 && accumulate != 1)
+    return fail(GPT_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  Plan p = make_plan(m, GPT_MODE_TRAIN);
+  if (ws_bytes < p.total)
+    return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, p.total);
+  return run_backward(m, p, param_layout(m), params, tokens, ws, grads, accumulate, stream);
+}
+
+int gpt_eval_bpb(const gpt_config* cfg, const void* params, const int32_t* tokens,
+                 int64_t n_rows, const int32_t* token_bytes, void* ws, size_t ws_bytes,
+                 double* out_dev, hipStream_t stream) {
+  Model m;
+  int st = validate(cfg, &m);
+  if (st) return st;
+  if ((st = check_ptrs({params, tokens, token_bytes, ws, out_dev}))) return st;
+  if (n_rows < 1) return fail(GPT_ERR_INVALID_ARG, "n_rows must be >= 1");
+  Plan p = make_plan(m, GPT_MODE_EVAL);
+  if (ws_bytes < p.total)
+    return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, p.total);
+  ParamLayout pl = param_layout(m);
+  double* acc = at<double>(ws, p.evacc);
+  for (int64_t r0 = 0; r0 < n_rows; r0 += m.B) {
+    int rows = (int)(n_rows - r0 < m.B ? n_rows - r0 : m.B);
+    const int32_t* tk = tokens + r0 * (m.T + 1);
+    st = run_forward(m, p, pl, params, tk, rows, ws, GPT_MODE_EVAL, nullptr, stream);
+    if (st) return st;
+    hipError_t e = gk::eval_accum(at<float>(ws, p.ell), tk, rows, m.T, token_bytes, acc, r0 == 0,
+                                  stream);
+    if (e != hipSuccess) return fail(GPT_ERR_HIP, "eval_accum: %s", hipGetErrorString(e));
+  }
+  hipError_t e = gk::eval_finish(acc, out_dev, stream);
+  if (e != hipSuccess) return fail(GPT_ERR_HIP, "eval_finish: %s", hipGetErrorString(e));
+  return GPT_OK;
+}
+
+const char* gpt_status_string(int status) {
+  switch (status) {
+    case GPT_OK: return "ok";
+    case GPT_ERR_INVALID_ARG: return "invalid argument";
+    case GPT_ERR_UNSUPPORTED_CONFIG: return "unsupported config";
+    case GPT_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case GPT_ERR_MISALIGNED: return "misaligned pointer";
+    case GPT_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* gpt_last_error(void) { return g_last_error.c_str(); }
+
+// ------------------------------------------------------- kernel entries
+static int dtype_ok(int32_t dtype) {
+  if (dtype != GPT_F32 && dtype != GPT_BF16) return fail(GPT_ERR_INVALID_ARG, "unknown dtype");
+  return GPT_OK;
+}
+#define KERNEL_TRY(expr)                                                           \
+  do {                                                                             \
+    hipError_t e_ = (expr);                                                        \
+    if (e_ != hipSuccess) return fail(GPT_ERR_HIP, "%s", hipGetErrorString(e_));   \
+  } while (0)
+
+int gpt_k_rmsnorm_fwd(const void* x, void* y, float* r, int64_t rows, int32_t dim, float eps,
+                      int32_t dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({x, y, r}))) return st;
+  if (rows < 0 || dim < 1) return fail(GPT_ERR_INVALID_ARG, "bad sizes");
+  KERNEL_TRY(gk::rmsnorm_fwd(x, y, r, rows, dim, eps, (gk::DType)dtype, s));
+  return GPT_OK;
+}
+
+int gpt_k_rmsnorm_bwd(const void* dy, const void* y, const float* r, const void* dres, void* dx,
+                      int64_t rows, int32_t dim, int32_t dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({dy, y, r, dx}))) return st;
+  if (dres && !aligned16(dres)) return fail(GPT_ERR_MISALIGNED, "dres misaligned");
+  if (rows < 0 || dim < 1) return fail(GPT_ERR_INVALID_ARG, "bad sizes");
+  KERNEL_TRY(gk::rmsnorm_bwd(dy, y, r, dres, dx, rows, dim, nullptr, nullptr, 0, 0,
+                             (gk::DType)dtype, s));
+  return GPT_OK;
+}
+
+int gpt_k_gemm(int32_t op, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+               const void* B, int64_t ldb, void* C, int64_t ldc, int32_t epilogue, void* aux,
+               int32_t dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({A, B, C}))) return st;
+  if (op < GPT_GEMM_NT || op > GPT_GEMM_TN) return fail(GPT_ERR_INVALID_ARG, "unknown op");
+  if (epilogue < GPT_EPI_STORE || epilogue > GPT_EPI_F32_ACC)
+    return fail(GPT_ERR_INVALID_ARG, "unknown epilogue");
+  if ((epilogue == GPT_EPI_RELU2 || epilogue == GPT_EPI_DRELU2) && (!aux || !aligned16(aux)))
+    return fail(GPT_ERR_INVALID_ARG, "epilogue needs an aligned aux buffer");
+  if (M < 0 || N < 0 || K < 1) return fail(GPT_ERR_INVALID_ARG, "bad sizes");
+  const int64_t rowA = op == GPT_GEMM_TN ? M : K, rowB = op == GPT_GEMM_NT ? K : N;
+  if (lda < rowA || ldb < rowB || ldc < N) return fail(GPT_ERR_INVALID_ARG, "leading dims too small");
+  gk::GemmDesc g{op, M, N, K, A, lda, B, ldb, C, ldc, epilogue, aux};
+  KERNEL_TRY(gk::gemm(g, (gk::DType)dtype, s));
+  return GPT_OK;
+}
+
+int gpt_k_rope_table(float* cs, int32_t T, int32_t hd, float base, hipStream_t s) {
+  int st;
+  if ((st = check_ptrs({cs}))) return st;
+  if (T < 1 || hd < 2 || hd % 2 || !(base > 0.f)) return fail(GPT_ERR_INVALID_ARG, "bad sizes");
+  KERNEL_TRY(gk::rope_table(cs, T, hd, base, s));
+  return GPT_OK;
+}
+
+static int attn_shape_ok(int32_t B, int32_t T, int32_t H, int32_t Hkv, int32_t hd) {
+  if (B < 1 || T < 1 || H < 1 || Hkv < 1 || H % Hkv) return fail(GPT_ERR_INVALID_ARG, "bad sizes");
+  if (!(hd == 4 || hd == 8 || hd == 16 || hd == 32 || hd == 64 || hd == 128))
+    return fail(GPT_ERR_UNSUPPORTED_CONFIG, "head_dim %d unsupported", hd);
+  return GPT_OK;
+}
+
+int gpt_k_rope_qknorm_fwd(void* qkv, float* rq, float* rk, const float* cs, int32_t B, int32_t T,
+                          int32_t H, int32_t Hkv, int32_t hd, float eps, int32_t dtype,
+                          hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({qkv, rq, rk, cs})) ||
+      (st = attn_shape_ok(B, T, H, Hkv, hd)))
+    return st;
+  KERNEL_TRY(gk::rope_qknorm_fwd(qkv, rq, rk, cs, B, T, H, Hkv, hd, eps, (gk::DType)dtype, s));
+  return GPT_OK;
+}
+
+int gpt_k_rope_qknorm_bwd(void* dqkv, const void* qkv, const float* rq, const float* rk,
+                          const float* cs, int32_t B, int32_t T, int32_t H, int32_t Hkv,
+                          int32_t hd, int32_t dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({dqkv, qkv, rq, rk, cs})) ||
+      (st = attn_shape_ok(B, T, H, Hkv, hd)))
+    return st;
+  KERNEL_TRY(gk::rope_qknorm_bwd(dqkv, qkv, rq, rk, cs, B, T, H, Hkv, hd, (gk::DType)dtype, s));
+  return GPT_OK;
+}
+
+int gpt_k_attn_fwd(const void* qkv, void* o, float* lse, int32_t B, int32_t T, int32_t H,
+                   int32_t Hkv, int32_t hd, int32_t window, int32_t dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({qkv, o, lse})) ||
+      (st = attn_shape_ok(B, T, H, Hkv, hd)))
+    return st;
+  if (window < 0) return fail(GPT_ERR_INVALID_ARG, "window < 0");
+  KERNEL_TRY(gk::attn_fwd(qkv, o, lse, B, T, H, Hkv, hd, window, (gk::DType)dtype, s));
+  return GPT_OK;
+}
+
+size_t gpt_k_attn_bwd_scratch_bytes(int32_t B, int32_t T, int32_t H, int32_t hd) {
+  if (B < 1 || T < 1 || H < 1 || hd < 1) return 0;
+  return gk::attn_bwd_scratch_bytes(B, T, H, hd);
+}
+
+int gpt_k_attn_bwd(const void* qkv, const void* o, const float* lse, const void* dout,
+                   void* dqkv, void* scratch, int32_t B, int32_t T, int32_t H, int32_t Hkv,
+                   int32_t hd, int32_t window, int32_t dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({qkv, o, lse, dout, dqkv, scratch})) ||
+      (st = attn_shape_ok(B, T, H, Hkv, hd)))
+    return st;
+  if (window < 0) return fail(GPT_ERR_INVALID_ARG, "window < 0");
+  KERNEL_TRY(gk::attn_bwd(qkv, o, lse, dout, dqkv, scratch, B, T, H, Hkv, hd, window,
+                          (gk::DType)dtype, s));
+  return GPT_OK;
+}
+
+int gpt_k_ce(const float* z, const int32_t* tgt, int64_t rows, int32_t V, float* ell, float* lse,
+             void* dz, float grad_scale, int32_t dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({z, tgt, ell, lse}))) return st;
+  if (dz && !aligned16(dz)) return fail(GPT_ERR_MISALIGNED, "dz misaligned");
+  if (rows < 0 || V < 1) return fail(GPT_ERR_INVALID_ARG, "bad sizes");
+  KERNEL_TRY(gk::ce_rows(z, rows, V, tgt, 1, 1, ell, lse, dz, grad_scale, (gk::DType)dtype, s, 0));
+  return GPT_OK;
+}
+
+}  // extern "C"

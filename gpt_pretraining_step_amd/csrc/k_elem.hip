@@ -1,0 +1,578 @@
+// HBM-bound kernels of the GPT step for gfx950: RMSNorm, rotary + QK-norm,
+// token / value embeddings, cross-entropy and the loss / bits-per-byte
+// reductions.  One 64-lane wavefront owns a row wherever a row reduction is
+// needed, so reductions are register shuffles with no LDS round trip.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace gk {
+
+static constexpr int kBlock = 256;   // 4 wavefronts
+
+// ------------------------------------------------------------------ utils
+__global__ void k_fill_zero(uint4* p, int64_t n16, uint8_t* tail, int ntail) {
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+// Zero-fill through a kernel (not a memset node), so a captured graph that
+// replays it stays correct.
+hipError_t fill_zero(void* p, int64_t bytes, hipStream_t s) {
+  if (bytes <= 0) return hipSuccess;
+  int64_t n16 = bytes / 16;
+  int ntail = (int)(bytes - n16 * 16);
+  int64_t blocks = n16 ? cdiv(n16, kBlock) : 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(kBlock), 0, s,
+                     (uint4*)p, n16, (uint8_t*)p + n16 * 16, ntail);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- rope table
+// (cos, sin) of theta_{t,j} = t * base^(-2j/hd), in double precision.
+__global__ void k_rope_table(float2* cs, int T, int hd, double base) {
+  int half = hd >> 1;
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= (int64_t)T * half) return;
+  int t = (int)(i / half), j = (int)(i % half);
+  double a = (double)t * pow(base, -2.0 * (double)j / (double)hd);
+  cs[i] = make_float2((float)cos(a), (float)sin(a));
+}
+
+hipError_t rope_table(float* cs, int T, int hd, float base, hipStream_t s) {
+  int64_t n = (int64_t)T * (hd / 2);
+  hipLaunchKernelGGL(k_rope_table, dim3((unsigned)cdiv(n, kBlock)), dim3(kBlock),
+                     0, s, (float2*)cs, T, hd, (double)base);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------- embedding
+// Row copy in 16-byte units (row bytes a multiple of 16) or elements.
+__global__ void k_embed_fwd16(const int32_t* tok, int T, const uint4* wte,
+                              uint4* x, int units, int64_t total) {
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  int64_t n = i / units;
+  int u = (int)(i % units);
+  int id = tok[(n / T) * (T + 1) + n % T];
+  x[i] = wte[(int64_t)id * units + u];
+}
+template <typename E>
+__global__ void k_embed_fwd_el(const int32_t* tok, int T, const E* wte, E* x,
+                               int D, int64_t total) {
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  int64_t n = i / D;
+  int d = (int)(i % D);
+  int id = tok[(n / T) * (T + 1) + n % T];
+  x[i] = wte[(int64_t)id * D + d];
+}
+
+hipError_t embed_fwd(const int32_t* tok, int B, int T, const void* wte,
+                     void* x, int D, DType dt, hipStream_t s) {
+  int es = dt == BF16 ? 2 : 4;
+  int64_t N = (int64_t)B * T;
+  if (((int64_t)D * es) % 16 == 0) {
+    int units = D * es / 16;
+    int64_t total = N * units;
+    hipLaunchKernelGGL(k_embed_fwd16, dim3((unsigned)cdiv(total, kBlock)), dim3(kBlock),
+                       0, s, tok, T, (const uint4*)wte, (uint4*)x, units, total);
+  } else if (dt == BF16) {
+    hipLaunchKernelGGL(k_embed_fwd_el<uint16_t>, dim3((unsigned)cdiv(N * D, kBlock)),
+                       dim3(kBlock), 0, s, tok, T, (const uint16_t*)wte, (uint16_t*)x, D, N * D);
+  } else {
+    hipLaunchKernelGGL(k_embed_fwd_el<float>, dim3((unsigned)cdiv(N * D, kBlock)),
+                       dim3(kBlock), 0, s, tok, T, (const float*)wte, (float*)x, D, N * D);
+  }
+  return hipGetLastError();
+}
+
+template <typename Tv>
+__global__ void k_embed_bwd(const int32_t* tok, int T, const Tv* dx, int ldx,
+                            float* dW, int D, int64_t total) {
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  int64_t n = i / D;
+  int d = (int)(i % D);
+  int id = tok[(n / T) * (T + 1) + n % T];
+  atomicAdd(dW + (int64_t)id * D + d, ld(dx, n * ldx + d));
+}
+
+hipError_t embed_bwd(const int32_t* tok, int B, int T, const void* dx, int ldx,
+                     float* dW, int D, DType dt, hipStream_t s) {
+  int64_t total = (int64_t)B * T * D;
+  if (dt == BF16)
+    hipLaunchKernelGGL(k_embed_bwd<bf16>, dim3((unsigned)cdiv(total, kBlock)), dim3(kBlock),
+                       0, s, tok, T, (const bf16*)dx, ldx, dW, D, total);
+  else
+    hipLaunchKernelGGL(k_embed_bwd<float>, dim3((unsigned)cdiv(total, kBlock)), dim3(kBlock),
+                       0, s, tok, T, (const float*)dx, ldx, dW, D, total);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// One wavefront per row.  r = 1/sqrt(mean(x^2) + eps), y = x r.
+template <typename Tv>
+__global__ __launch_bounds__(256) void k_rmsnorm_fwd(const Tv* x, Tv* y, float* r,
+                                                     int64_t rows, int D, float eps) {
+  int lane = threadIdx.x & 63;
+  int64_t row = blockIdx.x * (int64_t)(blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const Tv* xr = x + row * D;
+  float ss = 0.f;
+  for (int d = lane; d < D; d += 64) {
+    float v = ld(xr, d);
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  float rr = 1.0f / sqrtf(ss / (float)D + eps);
+  Tv* yr = y + row * D;
+  for (int d = lane; d < D; d += 64) st(yr, d, ld(xr, d) * rr);
+  if (lane == 0) r[row] = rr;
+}
+
+// bf16 rows with D % 8 == 0: 16-byte vectors, the row kept in registers.
+template <int VPL>
+__global__ __launch_bounds__(256) void k_rmsnorm_fwd_v(const bf16* x, bf16* y, float* r,
+                                                       int64_t rows, int D, float eps) {
+  int lane = threadIdx.x & 63;
+  int64_t row = blockIdx.x * (int64_t)(blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const uint4* xr = (const uint4*)(x + row * D);
+  int nv = D >> 3;
+  uint4 buf[VPL];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    int v = lane + 64 * k;
+    buf[k] = v < nv ? xr[v] : make_uint4(0, 0, 0, 0);
+    const uint32_t* w = (const uint32_t*)&buf[k];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float a = __uint_as_float(w[e] << 16), b = __uint_as_float(w[e] & 0xFFFF0000u);
+      ss += a * a + b * b;
+    }
+  }
+  ss = wave_sum(ss);
+  float rr = 1.0f / sqrtf(ss / (float)D + eps);
+  uint4* yr = (uint4*)(y + row * D);
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    int v = lane + 64 * k;
+    if (v < nv) {
+      const uint32_t* w = (const uint32_t*)&buf[k];
+      uint4 o;
+      uint32_t* ow = (uint32_t*)&o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        ow[e] = pack2bf(__uint_as_float(w[e] << 16) * rr,
+                        __uint_as_float(w[e] & 0xFFFF0000u) * rr);
+      yr[v] = o;
+    }
+  }
+  if (lane == 0) r[row] = rr;
+}
+
+hipError_t rmsnorm_fwd(const void* x, void* y, float* r, int64_t rows, int D,
+                       float eps, DType dt, hipStream_t s) {
+  dim3 grid((unsigned)cdiv(rows, 4)), block(256);
+  if (dt == BF16 && D % 8 == 0 && D <= 64 * 8 * 4) {
+    int vpl = (int)cdiv(D / 8, 64);
+    if (vpl == 1)
+      hipLaunchKernelGGL(k_rmsnorm_fwd_v<1>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
+    else if (vpl == 2)
+      hipLaunchKernelGGL(k_rmsnorm_fwd_v<2>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
+    else if (vpl == 3)
+      hipLaunchKernelGGL(k_rmsnorm_fwd_v<3>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
+    else
+      hipLaunchKernelGGL(k_rmsnorm_fwd_v<4>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
+  } else if (dt == BF16) {
+    hipLaunchKernelGGL(k_rmsnorm_fwd<bf16>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
+  } else {
+    hipLaunchKernelGGL(k_rmsnorm_fwd<float>, grid, block, 0, s, (const float*)x, (float*)y, r, rows, D, eps);
+  }
+  return hipGetLastError();
+}
+
+// dx = dres + r (g - y mean(g y)); g = dy plus, on the first C columns, the
+// value-embedding gate term sum_kv vez[row, kv] wg[kv, c].
+template <typename Tv>
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd(const Tv* dy, const Tv* y, const float* r,
+                                                     const Tv* dres, Tv* dx, int64_t rows, int D,
+                                                     const float* vez, const Tv* wg, int Hkv, int C) {
+  int lane = threadIdx.x & 63;
+  int64_t row = blockIdx.x * (int64_t)(blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const Tv* dyr = dy + row * D;
+  const Tv* yr = y + row * D;
+  const float* vz = vez ? vez + row * Hkv : nullptr;
+  float acc = 0.f;
+  for (int d = lane; d < D; d += 64) {
+    float g = ld(dyr, d);
+    if (vz && d < C)
+      for (int kv = 0; kv < Hkv; ++kv) g += vz[kv] * ld(wg, (int64_t)kv * C + d);
+    acc += g * ld(yr, d);
+  }
+  float m = wave_sum(acc) / (float)D;
+  float rr = r[row];
+  for (int d = lane; d < D; d += 64) {
+    float g = ld(dyr, d);
+    if (vz && d < C)
+      for (int kv = 0; kv < Hkv; ++kv) g += vz[kv] * ld(wg, (int64_t)kv * C + d);
+    float v = rr * (g - ld(yr, d) * m);
+    if (dres) v += ld(dres, row * D + d);
+    st(dx, row * D + d, v);
+  }
+}
+
+hipError_t rmsnorm_bwd(const void* dy, const void* y, const float* r,
+                       const void* dres, void* dx, int64_t rows, int D,
+                       const float* vez, const void* wg, int Hkv, int C,
+                       DType dt, hipStream_t s) {
+  dim3 grid((unsigned)cdiv(rows, 4)), block(256);
+  if (dt == BF16)
+    hipLaunchKernelGGL(k_rmsnorm_bwd<bf16>, grid, block, 0, s, (const bf16*)dy, (const bf16*)y, r,
+                       (const bf16*)dres, (bf16*)dx, rows, D, vez, (const bf16*)wg, Hkv, C);
+  else
+    hipLaunchKernelGGL(k_rmsnorm_bwd<float>, grid, block, 0, s, (const float*)dy, (const float*)y, r,
+                       (const float*)dres, (float*)dx, rows, D, vez, (const float*)wg, Hkv, C);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------ rotary + QK-norm
+// One thread per rotation pair (j, j + hd/2) of a q or k head; the hd/2
+// threads of a head are an aligned lane segment, so the norm's sum is a
+// segment shuffle.  Threads past the end still shuffle (whole segments are
+// out of range together) but neither load nor store.
+template <typename Tv>
+__global__ __launch_bounds__(256) void k_rope_qknorm_fwd(Tv* qkv, float* rq, float* rk,
+                                                         const float2* cs, int64_t N, int T,
+                                                         int H, int Hkv, int hd, float eps) {
+  int half = hd >> 1, heads = H + Hkv;
+  int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  bool valid = idx < N * heads * half;
+  int64_t id = valid ? idx : 0;
+  int j = (int)(id % half);
+  int64_t rest = id / half;
+  int hh = (int)(rest % heads);
+  int64_t n = rest / heads;
+  int t = (int)(n % T);
+  Tv* p = qkv + n * (int64_t)((H + 2 * Hkv) * hd) + (int64_t)hh * hd;
+  float x1 = valid ? ld(p, j) : 0.f, x2 = valid ? ld(p, j + half) : 0.f;
+  float2 c = cs[(int64_t)t * half + j];
+  float y1 = x1 * c.x - x2 * c.y;
+  float y2 = x1 * c.y + x2 * c.x;
+  float ss = seg_sum(y1 * y1 + y2 * y2, half);
+  float rr = 1.0f / sqrtf(ss / (float)hd + eps);
+  if (valid) {
+    st(p, j, y1 * rr);
+    st(p, j + half, y2 * rr);
+    if (j == 0) {
+      if (hh < H) rq[n * H + hh] = rr;
+      else rk[n * Hkv + (hh - H)] = rr;
+    }
+  }
+}
+
+template <typename Tv>
+__global__ __launch_bounds__(256) void k_rope_qknorm_bwd(Tv* dqkv, const Tv* qkv, const float* rq,
+                                                         const float* rk, const float2* cs,
+                                                         int64_t N, int T, int H, int Hkv, int hd) {
+  int half = hd >> 1, heads = H + Hkv;
+  int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  bool valid = idx < N * heads * half;
+  int64_t id = valid ? idx : 0;
+  int j = (int)(id % half);
+  int64_t rest = id / half;
+  int hh = (int)(rest % heads);
+  int64_t n = rest / heads;
+  int t = (int)(n % T);
+  int64_t off = n * (int64_t)((H + 2 * Hkv) * hd) + (int64_t)hh * hd;
+  Tv* dp = dqkv + off;
+  const Tv* yp = qkv + off;
+  float g1 = valid ? ld(dp, j) : 0.f, g2 = valid ? ld(dp, j + half) : 0.f;
+  float y1 = valid ? ld(yp, j) : 0.f, y2 = valid ? ld(yp, j + half) : 0.f;
+  float m = seg_sum(g1 * y1 + g2 * y2, half) / (float)hd;
+  float rr = valid ? (hh < H ? rq[n * H + hh] : rk[n * Hkv + (hh - H)]) : 0.f;
+  float a1 = rr * (g1 - y1 * m), a2 = rr * (g2 - y2 * m);
+  float2 c = cs[(int64_t)t * half + j];
+  if (valid) {   // inverse rotation (angle -theta)
+    st(dp, j, a1 * c.x + a2 * c.y);
+    st(dp, j + half, -a1 * c.y + a2 * c.x);
+  }
+}
+
+hipError_t rope_qknorm_fwd(void* qkv, float* rq, float* rk, const float* cs, int B, int T,
+                           int H, int Hkv, int hd, float eps, DType dt, hipStream_t s) {
+  int64_t N = (int64_t)B * T;
+  int64_t total = N * (H + Hkv) * (hd / 2);
+  dim3 grid((unsigned)cdiv(total, 256)), block(256);
+  if (dt == BF16)
+    hipLaunchKernelGGL(k_rope_qknorm_fwd<bf16>, grid, block, 0, s, (bf16*)qkv, rq, rk,
+                       (const float2*)cs, N, T, H, Hkv, hd, eps);
+  else
+    hipLaunchKernelGGL(k_rope_qknorm_fwd<float>, grid, block, 0, s, (float*)qkv, rq, rk,
+                       (const float2*)cs, N, T, H, Hkv, hd, eps);
+  return hipGetLastError();
+}
+
+hipError_t rope_qknorm_bwd(void* dqkv, const void* qkv, const float* rq, const float* rk,
+                           const float* cs, int B, int T, int H, int Hkv, int hd, DType dt,
+                           hipStream_t s) {
+  int64_t N = (int64_t)B * T;
+  int64_t total = N * (H + Hkv) * (hd / 2);
+  dim3 grid((unsigned)cdiv(total, 256)), block(256);
+  if (dt == BF16)
+    hipLaunchKernelGGL(k_rope_qknorm_bwd<bf16>, grid, block, 0, s, (bf16*)dqkv, (const bf16*)qkv,
+                       rq, rk, (const float2*)cs, N, T, H, Hkv, hd);
+  else
+    hipLaunchKernelGGL(k_rope_qknorm_bwd<float>, grid, block, 0, s, (float*)dqkv, (const float*)qkv,
+                       rq, rk, (const float2*)cs, N, T, H, Hkv, hd);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------- value embedding
+// One block per token.  Wave w computes the gates of KV heads w, w+4, ...
+template <typename Tv>
+__global__ __launch_bounds__(256) void k_ve_fwd(const int32_t* tok, int T, const Tv* h, int D,
+                                                const Tv* wg, int C, const Tv* E, Tv* qkv,
+                                                int ldqkv, int voff, float* g, int Hkv, int hd) {
+  __shared__ float gs[64];
+  int64_t n = blockIdx.x;
+  int id = tok[(n / T) * (T + 1) + n % T];
+  int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int kv = w; kv < Hkv; kv += 4) {
+    float acc = 0.f;
+    for (int c = lane; c < C; c += 64) acc += ld(h, n * D + c) * ld(wg, (int64_t)kv * C + c);
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      float gv = 3.0f / (1.0f + expf(-acc));
+      gs[kv] = gv;
+      g[n * Hkv + kv] = gv;
+    }
+  }
+  __syncthreads();
+  int tot = Hkv * hd;
+  for (int e = threadIdx.x; e < tot; e += blockDim.x) {
+    int64_t vi = n * ldqkv + voff + e;
+    st(qkv, vi, ld(qkv, vi) + gs[e / hd] * ld(E, (int64_t)id * tot + e));
+  }
+}
+
+hipError_t ve_fwd(const int32_t* tok, int B, int T, const void* h, int D, const void* wg, int C,
+                  const void* E, void* qkv, int ldqkv, int voff, float* g, int Hkv, int hd,
+                  DType dt, hipStream_t s) {
+  int64_t N = (int64_t)B * T;
+  if (dt == BF16)
+    hipLaunchKernelGGL(k_ve_fwd<bf16>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const bf16*)h, D,
+                       (const bf16*)wg, C, (const bf16*)E, (bf16*)qkv, ldqkv, voff, g, Hkv, hd);
+  else
+    hipLaunchKernelGGL(k_ve_fwd<float>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const float*)h, D,
+                       (const float*)wg, C, (const float*)E, (float*)qkv, ldqkv, voff, g, Hkv, hd);
+  return hipGetLastError();
+}
+
+template <typename Tv>
+__global__ __launch_bounds__(256) void k_ve_bwd(const int32_t* tok, int T, const Tv* dqkv,
+                                                int ldqkv, int voff, const Tv* E, const float* g,
+                                                float* vez, float* dE, int Hkv, int hd) {
+  int64_t n = blockIdx.x;
+  int id = tok[(n / T) * (T + 1) + n % T];
+  int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int tot = Hkv * hd;
+  for (int kv = w; kv < Hkv; kv += 4) {
+    float gv = g[n * Hkv + kv];
+    float acc = 0.f;
+    for (int d = lane; d < hd; d += 64) {
+      float dv = ld(dqkv, n * ldqkv + voff + kv * hd + d);
+      acc += dv * ld(E, (int64_t)id * tot + kv * hd + d);
+      atomicAdd(dE + (int64_t)id * tot + kv * hd + d, gv * dv);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) vez[n * Hkv + kv] = acc * gv * (1.0f - gv / 3.0f);
+  }
+}
+
+hipError_t ve_bwd(const int32_t* tok, int B, int T, const void* dqkv, int ldqkv, int voff,
+                  const void* E, const float* g, float* vez, float* dE, int Hkv, int hd,
+                  DType dt, hipStream_t s) {
+  int64_t N = (int64_t)B * T;
+  if (dt == BF16)
+    hipLaunchKernelGGL(k_ve_bwd<bf16>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const bf16*)dqkv,
+                       ldqkv, voff, (const bf16*)E, g, vez, dE, Hkv, hd);
+  else
+    hipLaunchKernelGGL(k_ve_bwd<float>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const float*)dqkv,
+                       ldqkv, voff, (const float*)E, g, vez, dE, Hkv, hd);
+  return hipGetLastError();
+}
+
+// dWg[kv, c] = sum_n vez[n, kv] h[n, c]: one block per (kv, c) output, a
+// fixed-order block reduction (deterministic).
+template <typename Tv>
+__global__ __launch_bounds__(256) void k_ve_wgrad(const float* vez, const Tv* h, int D, int64_t N,
+                                                  int Hkv, int C, float* dWg, int accumulate) {
+  __shared__ float red[4];
+  int o = blockIdx.x;
+  int kv = o / C, c = o % C;
+  float acc = 0.f;
+  for (int64_t n = threadIdx.x; n < N; n += blockDim.x) acc += vez[n * Hkv + kv] * ld(h, n * D + c);
+  acc = wave_sum(acc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v = (red[0] + red[1]) + (red[2] + red[3]);
+    dWg[o] = accumulate ? dWg[o] + v : v;
+  }
+}
+
+hipError_t ve_wgrad(const float* vez, const void* h, int D, int64_t N, int Hkv, int C, float* dWg,
+                    int accumulate, DType dt, hipStream_t s) {
+  if (dt == BF16)
+    hipLaunchKernelGGL(k_ve_wgrad<bf16>, dim3(Hkv * C), dim3(256), 0, s, vez, (const bf16*)h, D, N,
+                       Hkv, C, dWg, accumulate);
+  else
+    hipLaunchKernelGGL(k_ve_wgrad<float>, dim3(Hkv * C), dim3(256), 0, s, vez, (const float*)h, D, N,
+                       Hkv, C, dWg, accumulate);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------- cross-entropy
+// Combine two (max, sum-of-exp) pairs.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) { m = m2; s = s2; return; }
+  float M = fmaxf(m, m2);
+  s = s * expf(m - M) + s2 * expf(m2 - M);
+  m = M;
+}
+
+// One block per row: fp32 log-sum-exp over V (online max), the row loss,
+// and optionally the bf16/fp32 softmax gradient (softmax - onehot) * scale.
+template <typename TD>
+__global__ __launch_bounds__(256) void k_ce(const float* z, int64_t rows, int V,
+                                            const int32_t* tok, int tgtT, int direct, float* ell,
+                                            float* lse_out, TD* dz, float scale, int64_t row0) {
+  __shared__ float sm[4], ssum[4];
+  int64_t row = blockIdx.x;
+  const float* zr = z + row * (int64_t)V;
+  const int64_t n = row0 + row;
+  int tgt = direct ? tok[n] : tok[(n / tgtT) * (tgtT + 1) + n % tgtT + 1];
+  float m = -INFINITY, s = 0.f;
+  for (int v = threadIdx.x; v < V; v += blockDim.x) {
+    float x = zr[v];
+    if (x > m) {
+      s = s * expf(m - x) + 1.0f;
+      m = x;
+    } else {
+      s += expf(x - m);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    lse_merge(m, s, m2, s2);
+  }
+  int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sm[w] = m; ssum[w] = s; }
+  __syncthreads();
+  float M = sm[0], S = ssum[0];
+  for (int k = 1; k < 4; ++k) lse_merge(M, S, sm[k], ssum[k]);
+  float L = M + logf(S);
+  if (threadIdx.x == 0) {
+    ell[row] = L - zr[tgt];
+    lse_out[row] = L;
+  }
+  if (dz) {
+    TD* dr = dz + row * (int64_t)V;
+    for (int v = threadIdx.x; v < V; v += blockDim.x) {
+      float p = expf(zr[v] - L);
+      if (v == tgt) p -= 1.0f;
+      st(dr, v, p * scale);
+    }
+  }
+}
+
+hipError_t ce_rows(const float* z, int64_t rows, int V, const int32_t* tok, int tgt_T,
+                   int tgt_direct, float* ell, float* lse, void* dz, float grad_scale,
+                   DType dt, hipStream_t s, int64_t row0) {
+  if (rows <= 0) return hipSuccess;
+  if (dt == BF16)
+    hipLaunchKernelGGL(k_ce<bf16>, dim3((unsigned)rows), dim3(256), 0, s, z, rows, V, tok, tgt_T,
+                       tgt_direct, ell, lse, (bf16*)dz, grad_scale, row0);
+  else
+    hipLaunchKernelGGL(k_ce<float>, dim3((unsigned)rows), dim3(256), 0, s, z, rows, V, tok, tgt_T,
+                       tgt_direct, ell, lse, (float*)dz, grad_scale, row0);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- reductions
+__global__ __launch_bounds__(256) void k_loss_reduce(const float* ell, int64_t N, float* loss_ws,
+                                                     float* loss_out, int* flag) {
+  __shared__ double red[4];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < N; i += blockDim.x) acc += (double)ell[i];
+  acc = wave_sum_d(acc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = (red[0] + red[1]) + (red[2] + red[3]);
+    float loss = (float)(tot / (double)N);
+    *loss_ws = loss;
+    if (loss_out) *loss_out = loss;
+    *flag = isfinite(loss) ? 0 : 1;
+  }
+}
+
+hipError_t loss_reduce(const float* ell, int64_t N, float* loss_ws, float* loss_out, int* flag,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(k_loss_reduce, dim3(1), dim3(256), 0, s, ell, N, loss_ws, loss_out, flag);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_eval_accum(const float* ell, const int32_t* tok, int rows,
+                                                    int T, const int32_t* tb, double* acc,
+                                                    int first) {
+  __shared__ double rn[4], rb[4];
+  int64_t n_tok = (int64_t)rows * T;
+  double a = 0.0, b = 0.0;
+  for (int64_t i = threadIdx.x; i < n_tok; i += blockDim.x) {
+    a += (double)ell[i];
+    b += (double)tb[tok[(i / T) * (T + 1) + i % T + 1]];
+  }
+  a = wave_sum_d(a);
+  b = wave_sum_d(b);
+  if ((threadIdx.x & 63) == 0) { rn[threadIdx.x >> 6] = a; rb[threadIdx.x >> 6] = b; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double A = (rn[0] + rn[1]) + (rn[2] + rn[3]);
+    double Bb = (rb[0] + rb[1]) + (rb[2] + rb[3]);
+    if (first) { acc[0] = A; acc[1] = Bb; }
+    else { acc[0] += A; acc[1] += Bb; }
+  }
+}
+
+hipError_t eval_accum(const float* ell, const int32_t* tok, int rows, int T,
+                      const int32_t* token_bytes, double* acc, int first, hipStream_t s) {
+  hipLaunchKernelGGL(k_eval_accum, dim3(1), dim3(256), 0, s, ell, tok, rows, T, token_bytes, acc,
+                     first);
+  return hipGetLastError();
+}
+
+__global__ void k_eval_finish(const double* acc, double* out) {
+  if (threadIdx.x == 0) {
+    out[0] = acc[0];
+    out[1] = acc[1];
+    out[2] = acc[0] / (0.69314718055994530942 * acc[1]);
+  }
+}
+
+hipError_t eval_finish(const double* acc, double* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_eval_finish, dim3(1), dim3(64), 0, s, acc, out);
+  return hipGetLastError();
+}
+
+}  // namespace gk

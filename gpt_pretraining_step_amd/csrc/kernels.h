@@ -1,0 +1,89 @@
+// Host-side launchers of the gfx950 kernels (internal interface).
+// Every launcher enqueues on `s` and returns the hipError_t of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gk {
+
+enum DType { F32 = 0, BF16 = 1 };
+enum GemmOp { OP_NT = 0, OP_NN = 1, OP_TN = 2 };
+enum Epi { E_STORE = 0, E_RESADD, E_RELU2, E_DRELU2, E_F32, E_F32_ACC };
+
+// ---- elementwise / reductions -------------------------------------------
+hipError_t fill_zero(void* p, int64_t bytes, hipStream_t s);
+
+hipError_t rope_table(float* cs, int T, int hd, float base, hipStream_t s);
+
+// x[n, :] = wte[tok[b, t], :], n = b*T + t, tok rows of length T+1
+hipError_t embed_fwd(const int32_t* tok, int B, int T, const void* wte,
+                     void* x, int D, DType dt, hipStream_t s);
+// dW[tok[n], :] += dx[n, :] (fp32)
+hipError_t embed_bwd(const int32_t* tok, int B, int T, const void* dx,
+                     int ldx, float* dW, int D, DType dt, hipStream_t s);
+
+hipError_t rmsnorm_fwd(const void* x, void* y, float* r, int64_t rows, int D,
+                       float eps, DType dt, hipStream_t s);
+// dx = dres + r (g - y mean(g y)),  g = dy (+ VE term on the first C cols:
+// sum_kv vez[n, kv] * wg[kv, c])
+hipError_t rmsnorm_bwd(const void* dy, const void* y, const float* r,
+                       const void* dres, void* dx, int64_t rows, int D,
+                       const float* vez, const void* wg, int Hkv, int C,
+                       DType dt, hipStream_t s);
+
+struct GemmDesc {
+  int op;            // GemmOp
+  int64_t M, N, K;
+  const void* A; int64_t lda;
+  const void* B; int64_t ldb;
+  void* C; int64_t ldc;
+  int epi;           // Epi
+  void* aux;         // RELU2: output a; DRELU2: input u   (ldc, dtype)
+};
+hipError_t gemm(const GemmDesc& g, DType dt, hipStream_t s);
+
+hipError_t rope_qknorm_fwd(void* qkv, float* rq, float* rk, const float* cs,
+                           int B, int T, int H, int Hkv, int hd, float eps,
+                           DType dt, hipStream_t s);
+hipError_t rope_qknorm_bwd(void* dqkv, const void* qkv, const float* rq,
+                           const float* rk, const float* cs, int B, int T,
+                           int H, int Hkv, int hd, DType dt, hipStream_t s);
+
+// value embedding: g[n,kv] = 3 sigmoid(h[n,:C] . wg[kv,:]); v += g * E[tok]
+hipError_t ve_fwd(const int32_t* tok, int B, int T, const void* h, int D,
+                  const void* wg, int C, const void* E, void* qkv, int ldqkv,
+                  int voff, float* g, int Hkv, int hd, DType dt, hipStream_t s);
+// vez[n,kv] = (sum_d dv e) g (1 - g/3);  dE[tok] += g dv
+hipError_t ve_bwd(const int32_t* tok, int B, int T, const void* dqkv,
+                  int ldqkv, int voff, const void* E, const float* g,
+                  float* vez, float* dE, int Hkv, int hd, DType dt,
+                  hipStream_t s);
+// dWg[kv, c] (=/+=) sum_n vez[n, kv] h[n, c]
+hipError_t ve_wgrad(const float* vez, const void* h, int D, int64_t N,
+                    int Hkv, int C, float* dWg, int accumulate, DType dt,
+                    hipStream_t s);
+
+hipError_t attn_fwd(const void* qkv, void* o, float* lse, int B, int T,
+                    int H, int Hkv, int hd, int W, DType dt, hipStream_t s);
+size_t attn_bwd_scratch_bytes(int B, int T, int H, int hd);
+hipError_t attn_bwd(const void* qkv, const void* o, const float* lse,
+                    const void* dout, void* dqkv, void* scratch, int B, int T,
+                    int H, int Hkv, int hd, int W, DType dt, hipStream_t s);
+
+// cross-entropy over fp32 logits; tgt given by a token-row pointer:
+// target of row n = tok[(n / T) * (T+1) + n % T + 1]  (T = tgt_T)
+// (row0: token position of the first row, for chunked calls)
+hipError_t ce_rows(const float* z, int64_t rows, int V, const int32_t* tok,
+                   int tgt_T, int tgt_direct, float* ell, float* lse,
+                   void* dz, float grad_scale, DType dt, hipStream_t s,
+                   int64_t row0);
+// loss = mean(ell[0:N]) (fp64 sum); flag = !isfinite(loss)
+hipError_t loss_reduce(const float* ell, int64_t N, float* loss_ws,
+                       float* loss_out, int* flag, hipStream_t s);
+// acc[0] += sum ell, acc[1] += sum bytes[tgt]; if final, acc[2] = bpb
+hipError_t eval_accum(const float* ell, const int32_t* tok, int rows, int T,
+                      const int32_t* token_bytes, double* acc, int first,
+                      hipStream_t s);
+hipError_t eval_finish(const double* acc, double* out, hipStream_t s);
+
+}  // namespace gk

@@ -1,0 +1,260 @@
+/*
+ * gpt_step.h -- C ABI of the MI355X (gfx950) GPT training-step library.
+ *
+ * The library computes one forward + backward training step of the compact
+ * GPT decoder described by the nanochat walkthrough ("5만원으로 나만의 ChatGPT
+ * 훈련하는 방법", apidog.com, section "1. GPT model (nanochat/gpt.py)":
+ * rotary embeddings, QK normalisation, untied weights, ReLU^2 MLP, grouped-
+ * query attention, sliding-window pattern, value embeddings with a per-head
+ * gate) and scores it in bits per byte (tilnote.io autoresearch summary,
+ * "core mechanism": val_bpb).  Normalisation is RMSNorm with residual
+ * connections ("microgpt", news.hada.io, "model architecture"); the loss is
+ * the next-token cross-entropy ("microgpt", "training loop").
+ *
+ * Conventions for every entry point
+ *   - Pointers named *_dev or documented as "device" are device memory owned
+ *     by the caller and must stay valid until the enqueued work completes.
+ *     They must be 16-byte aligned (GPT_ERR_MISALIGNED otherwise).
+ *   - Work is enqueued on the caller's stream; no call synchronises the host.
+ *   - The library allocates no device memory: all scratch lives in the
+ *     caller's workspace `ws` (size from gpt_workspace_bytes).
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     negative return means nothing was enqueued; gpt_last_error() then holds
+ *     a message (thread-local).  Asynchronous device faults surface at the
+ *     caller's next stream synchronisation.
+ *   - Calls with distinct workspaces may run concurrently on distinct streams.
+ */
+#ifndef GPT_STEP_H
+#define GPT_STEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+enum {
+  GPT_OK = 0,
+  GPT_ERR_INVALID_ARG = -1,        /* null pointer, bad size or flag        */
+  GPT_ERR_UNSUPPORTED_CONFIG = -2, /* config outside what the kernels cover */
+  GPT_ERR_WORKSPACE_TOO_SMALL = -3,
+  GPT_ERR_MISALIGNED = -4,         /* a pointer is not 16-byte aligned      */
+  GPT_ERR_HIP = -5                 /* a HIP runtime call failed             */
+};
+
+/* storage dtype of parameters and activations */
+enum { GPT_F32 = 0, GPT_BF16 = 1 };
+
+/* workspace modes */
+enum { GPT_MODE_TRAIN = 0, GPT_MODE_EVAL = 1 };
+
+/*
+ * Model configuration.
+ *   n_layer, d_model (D), n_head (H), n_kv_head (Hkv, divides H), head_dim
+ *   (hd: 4, 8, 16, 32, 64 or 128), vocab (V), seq_len (T), batch (B rows),
+ *   mlp_mult (MLP width F = mlp_mult * D), ve_gate_channels (C: the value-
+ *   embedding gate reads the first C channels of the normalised attention
+ *   input, 1 <= C <= D).
+ *   window_pattern: "" = full causal in every layer; otherwise characters
+ *   'S'/'L', layer l uses pattern[l % len] -> window_short / window_long.
+ *   Key j is visible from query i iff 0 <= i - j <= window (the window counts
+ *   keys to the left of the query, as the window_size argument of the
+ *   nanochat walkthrough's flash-attention call, section "5").
+ *   ve_every_odd: 1 = value embeddings on layers 1, 3, 5, ... (0-based).
+ *   rope_base: rotary base; theta_{t,j} = t * base^(-2j/hd), pairs (j, j+hd/2).
+ *   norm_eps: added to the mean square inside every RMSNorm root.
+ *   dtype: GPT_BF16 (bf16 storage, fp32 accumulation, fp32 softmax/CE) or
+ *   GPT_F32 (fp32 storage).
+ */
+typedef struct gpt_config {
+  int32_t n_layer, d_model, n_head, n_kv_head, head_dim, vocab, seq_len, batch;
+  int32_t mlp_mult, ve_gate_channels;
+  char window_pattern[16];
+  int32_t window_short, window_long;
+  int32_t ve_every_odd;
+  float rope_base, norm_eps;
+  int32_t dtype;
+} gpt_config;
+
+/* ------------------------------------------------------- sizes and layout */
+/*
+ * Flat parameter buffer, in this order, every matrix [out, in] row-major
+ * (the weight of F.linear, nanochat walkthrough section "3. precision
+ * management"):
+ *   wte [V, D]
+ *   per layer l: Wqkv [(H + 2 Hkv) hd, D] (rows: q heads, k heads, v heads),
+ *                Wo [D, H hd], Wfc [F, D], Wproj [D, F],
+ *                and on value-embedding layers E_l [V, Hkv hd], Wg [Hkv, C]
+ *   Wlm [V, D]
+ * Gradients use the same layout in fp32.
+ */
+enum {
+  GPT_P_WTE = 0, GPT_P_WQKV, GPT_P_WO, GPT_P_WFC, GPT_P_WPROJ, GPT_P_VE,
+  GPT_P_WG, GPT_P_WLM
+};
+
+/* Number of parameters (elements), or a negative status for a bad config. */
+int64_t gpt_param_count(const gpt_config* cfg);
+
+/* Element offset of tensor `which` (GPT_P_*) of `layer` in the flat buffer;
+ * -1 if that layer has no such tensor; a status < -1 for a bad argument.
+ * `layer` is ignored for GPT_P_WTE and GPT_P_WLM. */
+int64_t gpt_param_offset(const gpt_config* cfg, int which, int layer);
+
+/* Workspace bytes needed by gpt_step_fwd/bwd (GPT_MODE_TRAIN) or by
+ * gpt_eval_bpb (GPT_MODE_EVAL); 0 for a bad config (see gpt_last_error). */
+size_t gpt_workspace_bytes(const gpt_config* cfg, int mode);
+
+/* Check a config without touching the GPU; returns a status. */
+int gpt_validate_config(const gpt_config* cfg);
+
+/* --------------------------------------------------------------- the step */
+/*
+ * Forward pass and mean next-token cross-entropy of one batch.
+ *   params : device, dtype per cfg->dtype, the flat layout above.
+ *   tokens : device int32 [B, T+1] row-major; inputs are the first T ids of a
+ *            row, targets the last T.  Ids outside [0, V) are a precondition
+ *            violation (not checked on the device).
+ *   ws     : device workspace of ws_bytes >= gpt_workspace_bytes(TRAIN).  The
+ *            forward saves what the backward needs in it; ws[] also holds the
+ *            per-token losses (gpt_ws_offset(GPT_WS_ELL)).
+ *   loss_dev : device float, receives mean loss over the B*T targets.
+ * Softmax and cross-entropy are fp32; logits are fp32.  The softmax gradient
+ * (softmax - onehot)/(B T) is formed here too and kept in ws for the
+ * backward.  A non-finite loss sets the int32 flag at GPT_WS_NONFINITE.
+ */
+int gpt_step_fwd(const gpt_config* cfg, const void* params,
+                 const int32_t* tokens, void* ws, size_t ws_bytes,
+                 float* loss_dev, hipStream_t stream);
+
+/*
+ * Backward pass of the preceding gpt_step_fwd on the same ws, params and
+ * tokens (upstream gradient of the mean loss = 1).
+ *   grads : device fp32, flat layout; overwritten (accumulate = 0) or added
+ *           to (accumulate = 1, for gradient accumulation over micro-batches).
+ */
+int gpt_step_bwd(const gpt_config* cfg, const void* params,
+                 const int32_t* tokens, void* ws, size_t ws_bytes,
+                 float* grads, int accumulate, hipStream_t stream);
+
+/*
+ * Bits per byte over an evaluation set (forward only).
+ *   tokens      : device int32 [n_rows, T+1]; rows are processed in batches
+ *                 of cfg->batch rows (the last one may be shorter).
+ *   token_bytes : device int32 [V], UTF-8 byte length of each vocabulary id,
+ *                 indexed by the target id.
+ *   ws          : ws_bytes >= gpt_workspace_bytes(EVAL).
+ *   out_dev     : device double[3] = { sum of nats, sum of bytes,
+ *                 bpb = nats / (ln 2 * bytes) }.
+ */
+int gpt_eval_bpb(const gpt_config* cfg, const void* params,
+                 const int32_t* tokens, int64_t n_rows,
+                 const int32_t* token_bytes, void* ws, size_t ws_bytes,
+                 double* out_dev, hipStream_t stream);
+
+/* ------------------------------------------------- workspace inspection */
+/* Byte offset into a TRAIN workspace of a saved tensor, for tests and
+ * debugging; -1 when absent.  Layer-wise items take `layer`. */
+enum {
+  GPT_WS_ELL = 0,       /* fp32 [B*T] per-token loss                         */
+  GPT_WS_LOSS,          /* fp32 scalar mean loss                             */
+  GPT_WS_NONFINITE,     /* int32 flag, 1 if the loss was not finite          */
+  GPT_WS_X_H,           /* dtype [N, D] normalised attention input  (layer)  */
+  GPT_WS_X_QKV,         /* dtype [N, (H+2Hkv) hd] q,k after rotary+norm,
+                           v after value embedding                  (layer)  */
+  GPT_WS_X_O,           /* dtype [N, H hd] attention output          (layer)  */
+  GPT_WS_X_LSE,         /* fp32 [B, H, T] attention log-sum-exp      (layer)  */
+  GPT_WS_X_H2,          /* dtype [N, D] normalised MLP input         (layer)  */
+  GPT_WS_X_A,           /* dtype [N, F] relu(u)^2                    (layer)  */
+  GPT_WS_X_HF           /* dtype [N, D] final normalised features            */
+};
+int64_t gpt_ws_offset(const gpt_config* cfg, int which, int layer);
+
+/* ------------------------------------------------------------- errors */
+const char* gpt_status_string(int status);
+const char* gpt_last_error(void);
+
+/* ------------------------------------------------ kernel-level entries */
+/*
+ * Single kernels of the step, for parity tests and profiling.  Same
+ * conventions; `dtype` (GPT_F32/GPT_BF16) is the storage type of the
+ * activation arguments.  Statistics (r, lse) are fp32.
+ */
+
+/* y = x / sqrt(mean(x^2) + eps) per row of x [rows, dim]; r[row] = 1/sqrt(.) */
+int gpt_k_rmsnorm_fwd(const void* x, void* y, float* r, int64_t rows,
+                      int32_t dim, float eps, int32_t dtype, hipStream_t s);
+
+/* dx = dres + r (dy - y mean(dy y)); dres may be null (= 0), dx may alias
+ * dres.  All [rows, dim]. */
+int gpt_k_rmsnorm_bwd(const void* dy, const void* y, const float* r,
+                      const void* dres, void* dx, int64_t rows, int32_t dim,
+                      int32_t dtype, hipStream_t s);
+
+/*
+ * C = op(A, B) over M x N x K with fp32 accumulation.
+ *   op GPT_GEMM_NT: A [M, K] (lda), B [N, K] (ldb):   C = A B^T   (y = x W^T)
+ *   op GPT_GEMM_NN: A [M, K] (lda), B [K, N] (ldb):   C = A B     (dx = dy W)
+ *   op GPT_GEMM_TN: A [K, M] (lda), B [K, N] (ldb):   C = A^T B   (dW = dy^T x)
+ *   epilogue GPT_EPI_STORE   : C (dtype) = acc
+ *            GPT_EPI_RESADD  : C (dtype) = C + acc, rounded once
+ *            GPT_EPI_RELU2   : C (dtype) = acc; aux (dtype, ldc) = relu(C)^2
+ *            GPT_EPI_DRELU2  : C (dtype) = acc * 2 relu(aux)  (aux: dtype, ldc)
+ *            GPT_EPI_F32     : C (fp32) = acc
+ *            GPT_EPI_F32_ACC : C (fp32) += acc
+ */
+enum { GPT_GEMM_NT = 0, GPT_GEMM_NN = 1, GPT_GEMM_TN = 2 };
+enum { GPT_EPI_STORE = 0, GPT_EPI_RESADD, GPT_EPI_RELU2, GPT_EPI_DRELU2,
+       GPT_EPI_F32, GPT_EPI_F32_ACC };
+int gpt_k_gemm(int32_t op, int64_t M, int64_t N, int64_t K, const void* A,
+               int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+               int32_t epilogue, void* aux, int32_t dtype, hipStream_t s);
+
+/* cos/sin table, float2 [T, hd/2]: (cos, sin) of t * base^(-2j/hd),
+ * evaluated in double precision. */
+int gpt_k_rope_table(float* cs, int32_t T, int32_t hd, float base,
+                     hipStream_t s);
+
+/* In place on qkv [B*T, (H+2Hkv) hd]: rotate every q and k head, then RMS-
+ * normalise it over hd; rq [B*T, H] and rk [B*T, Hkv] receive 1/rms. */
+int gpt_k_rope_qknorm_fwd(void* qkv, float* rq, float* rk, const float* cs,
+                          int32_t B, int32_t T, int32_t H, int32_t Hkv,
+                          int32_t hd, float eps, int32_t dtype, hipStream_t s);
+
+/* In place on the q and k parts of dqkv: norm backward (using the saved
+ * normalised q/k of qkv and rq/rk), then the inverse rotation. */
+int gpt_k_rope_qknorm_bwd(void* dqkv, const void* qkv, const float* rq,
+                          const float* rk, const float* cs, int32_t B,
+                          int32_t T, int32_t H, int32_t Hkv, int32_t hd,
+                          int32_t dtype, hipStream_t s);
+
+/* Attention over qkv [B*T, (H+2Hkv) hd] -> o [B*T, H hd], lse [B, H, T];
+ * causal, window `window` (keys i-window..i), query head h reads KV head
+ * h / (H / Hkv); scale 1/sqrt(hd). */
+int gpt_k_attn_fwd(const void* qkv, void* o, float* lse, int32_t B,
+                   int32_t T, int32_t H, int32_t Hkv, int32_t hd,
+                   int32_t window, int32_t dtype, hipStream_t s);
+
+/* Gradients of gpt_k_attn_fwd: dqkv (same layout as qkv) from do [B*T, H hd].
+ * scratch: device, >= gpt_k_attn_bwd_scratch_bytes(B, T, H, hd) bytes. */
+size_t gpt_k_attn_bwd_scratch_bytes(int32_t B, int32_t T, int32_t H,
+                                    int32_t hd);
+int gpt_k_attn_bwd(const void* qkv, const void* o, const float* lse,
+                   const void* dout, void* dqkv, void* scratch, int32_t B,
+                   int32_t T, int32_t H, int32_t Hkv, int32_t hd,
+                   int32_t window, int32_t dtype, hipStream_t s);
+
+/* Softmax cross-entropy on fp32 logits z [rows, V] with targets tgt[rows]:
+ * ell[row] = lse - z[tgt], lse[row]; if dz is non-null it receives
+ * (softmax - onehot) * grad_scale in `dtype` [rows, V]. */
+int gpt_k_ce(const float* z, const int32_t* tgt, int64_t rows, int32_t V,
+             float* ell, float* lse, void* dz, float grad_scale,
+             int32_t dtype, hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT_STEP_H */

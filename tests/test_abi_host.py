@@ -1,0 +1,134 @@
+"""Host-side tests of the C ABI (no GPU work is enqueued by any of them).
+
+The library must load, export every function include/gpt_step.h declares,
+agree with the oracle on parameter layout, and reject bad arguments with
+distinct status codes before anything reaches the GPU.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gptinputs as gi
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+G = pytest.importorskip("gpt_pretraining_step_amd")
+if not os.path.exists(G.LIB_PATH):
+    pytest.skip("libgptstep.so not built", allow_module_level=True)
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "gpt_step.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gpt_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = G.lib()
+    names = header_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(G.exported_symbols())
+
+
+@pytest.mark.parametrize("name", list(gi.PRESETS))
+def test_param_layout_matches_oracle(name):
+    d = gi.preset(name)
+    c = G.make_config(d)
+    assert G.param_count(c) == O.param_count(d)
+    off, layers = 0, {}
+    for tname, shape in O.param_layout(d):
+        layers[tname] = off
+        off += int(np.prod(shape))
+    assert G.param_offset(c, G.P_WTE) == layers["wte"]
+    assert G.param_offset(c, G.P_WLM) == layers["wlm"]
+    for l in range(d["n_layer"]):
+        assert G.param_offset(c, G.P_WQKV, l) == layers[f"l{l}.wqkv"]
+        assert G.param_offset(c, G.P_WO, l) == layers[f"l{l}.wo"]
+        assert G.param_offset(c, G.P_WFC, l) == layers[f"l{l}.wfc"]
+        assert G.param_offset(c, G.P_WPROJ, l) == layers[f"l{l}.wproj"]
+        assert G.param_offset(c, G.P_VE, l) == layers.get(f"l{l}.ve", -1)
+        assert G.param_offset(c, G.P_WG, l) == layers.get(f"l{l}.wg", -1)
+
+
+def test_workspace_sizes():
+    for name in gi.PRESETS:
+        c = G.make_config(gi.preset(name))
+        tr, ev = G.workspace_bytes(c, G.MODE_TRAIN), G.workspace_bytes(c, G.MODE_EVAL)
+        assert tr > ev > 0
+        assert tr % 256 == 0
+    # d24 training state fits one 288 GB device with room to spare
+    assert G.workspace_bytes(G.make_config(gi.preset("d24"))) < 64 << 30
+
+
+def _bad(**kw):
+    return G.make_config(dict(gi.preset("d4"), **kw))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_head=3, n_kv_head=2), -2),
+    (dict(head_dim=96), -2),
+    (dict(head_dim=0), -2),
+    (dict(window_pattern="SXL"), -1),
+    (dict(dtype=7), -1),
+    (dict(vocab=1), -1),
+    (dict(n_layer=0), -1),
+    (dict(norm_eps=0.0), -1),
+    (dict(ve_gate_channels=0), -1),
+    (dict(ve_gate_channels=4096), -1),
+    (dict(window_short=-1), -1),
+])
+def test_invalid_configs_rejected(kw, status):
+    c = _bad(**kw)
+    assert G.validate_config(c) == status
+    assert G.lib().gpt_param_count(C.byref(c)) == status
+    assert G.lib().gpt_workspace_bytes(C.byref(c), 0) == 0
+    assert len(G.lib().gpt_last_error()) > 0
+
+
+def _call_fwd(c, params, tokens, ws, ws_bytes, loss):
+    return G.lib().gpt_step_fwd(C.byref(c), params, tokens, ws, ws_bytes, loss, None)
+
+
+def test_entry_points_reject_bad_pointers_before_launch():
+    c = G.make_config(gi.preset("tiny"))
+    need = G.workspace_bytes(c)
+    A = C.c_void_p(0x1000)          # never dereferenced: validation fails first
+    assert _call_fwd(c, None, A, A, need, A) == -1
+    assert _call_fwd(c, C.c_void_p(0x1004), A, A, need, A) == -4
+    assert _call_fwd(c, A, A, A, need - 1, A) == -3
+    assert G.lib().gpt_step_bwd(C.byref(c), A, A, A, need, A, 2, None) == -1
+    assert G.lib().gpt_step_bwd(C.byref(c), A, A, A, need, None, 0, None) == -1
+    assert G.lib().gpt_eval_bpb(C.byref(c), A, A, 0, A, A, G.workspace_bytes(c, 1), A, None) == -1
+    assert G.lib().gpt_eval_bpb(C.byref(c), A, A, 3, A, A, 16, A, None) == -3
+    bad = _bad(n_head=3, n_kv_head=2)
+    assert _call_fwd(bad, A, A, A, need, A) == -2
+    # kernel entries
+    L = G.lib()
+    assert L.gpt_k_gemm(5, 4, 4, 4, A, 4, A, 4, A, 4, 0, None, 1, None) == -1
+    assert L.gpt_k_gemm(0, 4, 4, 4, A, 2, A, 4, A, 4, 0, None, 1, None) == -1
+    assert L.gpt_k_gemm(0, 4, 4, 4, A, 4, A, 4, A, 4, 2, None, 1, None) == -1
+    assert L.gpt_k_attn_fwd(A, A, A, 1, 8, 3, 2, 128, 4, 1, None) == -1
+    assert L.gpt_k_attn_fwd(A, A, A, 1, 8, 2, 2, 96, 4, 1, None) == -2
+    assert L.gpt_k_rmsnorm_fwd(A, C.c_void_p(0x1002), A, 4, 8, 1e-5, 1, None) == -4
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert G.lib().gpt_status_string(s)
+    assert G.lib().gpt_status_string(-99) == b"unknown status"
+
+
+def test_no_cpu_fallback_in_product_path():
+    """The binding and package never import the oracle."""
+    pkg = os.path.join(ROOT, "gpt_pretraining_step_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f

@@ -1,0 +1,283 @@
+"""Kernel-level parity of the HIP path against the CPU oracle (GPU only)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oracle.gpt import _Num
+from tests.gpu_util import rel_err, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():   # collected on CPU hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import gpt_pretraining_step_amd as G  # noqa: E402
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV, dtype)
+
+
+def rnd_in(shape, seed, scale=1.0, bf16=True):
+    x = np.random.default_rng(seed).standard_normal(shape).astype(np.float32) * scale
+    return O.round_bf16(x) if bf16 else x
+
+
+def tdtype(dt):
+    return torch.bfloat16 if dt == G.BF16 else torch.float32
+
+
+# ------------------------------------------------------------------ GEMM
+GEMM_SHAPES = [(130, 70, 50), (256, 256, 64), (300, 200, 96), (512, 384, 256),
+               (1000, 257, 160)]
+
+
+def _gemm_ref(op, A, B):
+    A64, B64 = A.astype(np.float64), B.astype(np.float64)
+    if op == G.GEMM_NT:
+        return A64 @ B64.T
+    if op == G.GEMM_NN:
+        return A64 @ B64
+    return A64.T @ B64
+
+
+@pytest.mark.parametrize("dt", [G.BF16, G.F32])
+@pytest.mark.parametrize("op", [G.GEMM_NT, G.GEMM_NN, G.GEMM_TN])
+@pytest.mark.parametrize("shape", GEMM_SHAPES)
+def test_gemm_store_and_f32(dt, op, shape):
+    M, N, K = shape
+    say("gemm", dt, op, shape)
+    bf = dt == G.BF16
+    Ash = (M, K) if op != G.GEMM_TN else (K, M)
+    Bsh = (N, K) if op == G.GEMM_NT else (K, N)
+    A, B = rnd_in(Ash, 1, bf16=bf), rnd_in(Bsh, 2, bf16=bf)
+    ref = _gemm_ref(op, A, B)
+    tA, tB = dev(A, tdtype(dt)), dev(B, tdtype(dt))
+    lda, ldb = Ash[1], Bsh[1]
+    C = torch.zeros(M, N, dtype=tdtype(dt), device=DEV)
+    G.k_gemm(op, M, N, K, tA, lda, tB, ldb, C, N, G.EPI_STORE, None, dt)
+    C32 = torch.full((M, N), 0.5, dtype=torch.float32, device=DEV)
+    G.k_gemm(op, M, N, K, tA, lda, tB, ldb, C32, N, G.EPI_F32_ACC, None, dt)
+    torch.cuda.synchronize()
+    tol = 8e-3 if bf else 1e-5
+    assert rel_err(to_np(C), ref) < tol
+    assert rel_err(to_np(C32), ref + 0.5) < 1e-5
+
+
+@pytest.mark.parametrize("dt", [G.BF16, G.F32])
+@pytest.mark.parametrize("shape", [(200, 130, 64), (512, 256, 128)])
+def test_gemm_epilogues(dt, shape):
+    M, N, K = shape
+    bf = dt == G.BF16
+    num = _Num("bf16emu" if bf else "fp32")
+    A, B = rnd_in((M, K), 3, bf16=bf), rnd_in((N, K), 4, bf16=bf)
+    acc = (A.astype(np.float64) @ B.astype(np.float64).T).astype(np.float32)
+    R = rnd_in((M, N), 5, bf16=bf)
+    U = rnd_in((M, N), 6, bf16=bf)
+    tA, tB = dev(A, tdtype(dt)), dev(B, tdtype(dt))
+    # residual add
+    C = dev(R, tdtype(dt))
+    G.k_gemm(G.GEMM_NT, M, N, K, tA, K, tB, K, C, N, G.EPI_RESADD, None, dt)
+    # relu^2 pair
+    Cu = torch.zeros(M, N, dtype=tdtype(dt), device=DEV)
+    Ca = torch.zeros(M, N, dtype=tdtype(dt), device=DEV)
+    G.k_gemm(G.GEMM_NT, M, N, K, tA, K, tB, K, Cu, N, G.EPI_RELU2, Ca, dt)
+    # relu^2 backward
+    Cd = torch.zeros(M, N, dtype=tdtype(dt), device=DEV)
+    tU = dev(U, tdtype(dt))
+    G.k_gemm(G.GEMM_NT, M, N, K, tA, K, tB, K, Cd, N, G.EPI_DRELU2, tU, dt)
+    torch.cuda.synchronize()
+    tol = 2e-2 if bf else 1e-5
+    assert rel_err(to_np(C), num.rnd(R + acc)) < tol
+    u = num.rnd(acc)
+    assert rel_err(to_np(Cu), u) < tol
+    assert rel_err(to_np(Ca), num.rnd(np.maximum(u, 0) ** 2)) < tol
+    assert rel_err(to_np(Cd), num.rnd(acc * 2 * np.maximum(U, 0))) < tol
+
+
+# --------------------------------------------------------------- RMSNorm
+@pytest.mark.parametrize("dt", [G.BF16, G.F32])
+@pytest.mark.parametrize("D", [16, 100, 256, 768, 1536])
+def test_rmsnorm(dt, D):
+    rows = 77
+    bf = dt == G.BF16
+    num = _Num("bf16emu" if bf else "fp32")
+    x = rnd_in((rows, D), 7, 3.0, bf)
+    dy = rnd_in((rows, D), 8, 1.0, bf)
+    dres = rnd_in((rows, D), 9, 1.0, bf)
+    y_ref, r_ref = O.rmsnorm(x, 1e-5, num)
+    tx = dev(x, tdtype(dt))
+    ty = torch.empty_like(tx)
+    tr = torch.empty(rows, dtype=torch.float32, device=DEV)
+    G.k_rmsnorm_fwd(tx, ty, tr, rows, D, 1e-5, dt)
+    tdx = dev(dres, tdtype(dt))
+    G.k_rmsnorm_bwd(dev(dy, tdtype(dt)), ty, tr, tdx, tdx, rows, D, dt)
+    torch.cuda.synchronize()
+    tol = 1e-2 if bf else 1e-5
+    assert rel_err(to_np(ty), y_ref) < tol
+    assert rel_err(to_np(tr), r_ref) < 1e-5
+    dx_ref = num.rnd(dres + O.rmsnorm_bwd(dy, y_ref, r_ref, num))
+    assert rel_err(to_np(tdx), dx_ref) < (2e-2 if bf else 1e-5)
+
+
+# ------------------------------------------------- rotary + QK-norm
+@pytest.mark.parametrize("dt,hd", [(G.F32, 4), (G.BF16, 64), (G.BF16, 128), (G.F32, 128)])
+def test_rope_qknorm(dt, hd):
+    B, T, H, Hkv = 2, 50, 4, 2
+    bf = dt == G.BF16
+    num = _Num("bf16emu" if bf else "fp32")
+    ld = (H + 2 * Hkv) * hd
+    qkv = rnd_in((B, T, ld), 10, 1.0, bf)
+    cs = torch.empty(T * hd, dtype=torch.float32, device=DEV)
+    G.k_rope_table(cs, T, hd, 10000.0)
+    tq = dev(qkv, tdtype(dt)).reshape(B * T, ld)
+    rq = torch.empty(B * T * H, dtype=torch.float32, device=DEV)
+    rk = torch.empty(B * T * Hkv, dtype=torch.float32, device=DEV)
+    G.k_rope_qknorm_fwd(tq, rq, rk, cs, B, T, H, Hkv, hd, 1e-5, dt)
+    cos, sin = O.rope_tables(T, hd, 10000.0)
+    q = qkv[..., :H * hd].reshape(B, T, H, hd)
+    k = qkv[..., H * hd:(H + Hkv) * hd].reshape(B, T, Hkv, hd)
+    qn, rq_ref = O.rmsnorm(O.rope(q, cos, sin, num), 1e-5, num)
+    kn, rk_ref = O.rmsnorm(O.rope(k, cos, sin, num), 1e-5, num)
+    dqkv = rnd_in((B, T, ld), 11, 1.0, bf)
+    td = dev(dqkv, tdtype(dt)).reshape(B * T, ld)
+    G.k_rope_qknorm_bwd(td, tq, rq, rk, cs, B, T, H, Hkv, hd, dt)
+    torch.cuda.synchronize()
+    got = to_np(tq).reshape(B, T, ld)
+    tol = 1e-2 if bf else 1e-5
+    assert rel_err(got[..., :H * hd], qn.reshape(B, T, -1)) < tol
+    assert rel_err(got[..., H * hd:(H + Hkv) * hd], kn.reshape(B, T, -1)) < tol
+    np.testing.assert_array_equal(got[..., (H + Hkv) * hd:], qkv[..., (H + Hkv) * hd:])
+    assert rel_err(to_np(rq), rq_ref.reshape(-1)) < 1e-5
+    assert rel_err(to_np(rk), rk_ref.reshape(-1)) < 1e-5
+    gq = dqkv[..., :H * hd].reshape(B, T, H, hd)
+    gk = dqkv[..., H * hd:(H + Hkv) * hd].reshape(B, T, Hkv, hd)
+    yq = to_np(tq).reshape(B, T, ld)[..., :H * hd].reshape(B, T, H, hd)
+    yk = to_np(tq).reshape(B, T, ld)[..., H * hd:(H + Hkv) * hd].reshape(B, T, Hkv, hd)
+    rq_g = to_np(rq).reshape(B, T, H)
+    rk_g = to_np(rk).reshape(B, T, Hkv)
+    dq_ref = num.rnd(O.rope_bwd(O.rmsnorm_bwd(gq, yq, rq_g, num), cos, sin, num))
+    dk_ref = num.rnd(O.rope_bwd(O.rmsnorm_bwd(gk, yk, rk_g, num), cos, sin, num))
+    gd = to_np(td).reshape(B, T, ld)
+    tolb = 2e-2 if bf else 1e-5
+    assert rel_err(gd[..., :H * hd], dq_ref.reshape(B, T, -1)) < tolb
+    assert rel_err(gd[..., H * hd:(H + Hkv) * hd], dk_ref.reshape(B, T, -1)) < tolb
+
+
+# -------------------------------------------------------------- attention
+ATTN_CASES = [
+    # dt, B, T, H, Hkv, hd, W
+    (G.F32, 2, 16, 4, 2, 4, 16),
+    (G.F32, 2, 37, 4, 2, 4, 5),
+    (G.F32, 1, 40, 2, 1, 32, 0),
+    (G.BF16, 2, 130, 2, 1, 64, 31),
+    (G.BF16, 2, 128, 2, 2, 128, 128),
+    (G.BF16, 1, 300, 6, 2, 128, 64),
+    (G.BF16, 2, 257, 2, 2, 128, 127),
+    (G.BF16, 1, 512, 4, 4, 128, 100),
+]
+
+
+def _attn_inputs(B, T, H, Hkv, hd, bf, seed=12):
+    num = _Num("bf16emu" if bf else "fp32")
+    q = rnd_in((B, T, H, hd), seed, 1.0, bf)
+    k = rnd_in((B, T, Hkv, hd), seed + 1, 1.0, bf)
+    v = rnd_in((B, T, Hkv, hd), seed + 2, 1.0, bf)
+    # q and k unit-RMS per head, as after QK-norm
+    q = O.rmsnorm(q, 1e-5, num)[0]
+    k = O.rmsnorm(k, 1e-5, num)[0]
+    qkv = np.concatenate([q.reshape(B, T, -1), k.reshape(B, T, -1), v.reshape(B, T, -1)], -1)
+    return q, k, v, qkv
+
+
+@pytest.mark.parametrize("case", ATTN_CASES)
+def test_attention_fwd_bwd(case):
+    dt, B, T, H, Hkv, hd, W = case
+    say("attn", case)
+    bf = dt == G.BF16
+    num = _Num("bf16emu" if bf else "fp32")
+    q, k, v, qkv = _attn_inputs(B, T, H, Hkv, hd, bf)
+    o_ref, lse_ref = O.attention(q, k, v, W, num)
+    do = rnd_in((B, T, H, hd), 20, 1.0, bf)
+    dq_ref, dk_ref, dv_ref = O.attention_bwd(q, k, v, o_ref, lse_ref, do, W, num)
+    tqkv = dev(qkv, tdtype(dt)).reshape(B * T, -1)
+    to = torch.empty(B * T, H * hd, dtype=tdtype(dt), device=DEV)
+    tl = torch.empty(B * H * T, dtype=torch.float32, device=DEV)
+    G.k_attn_fwd(tqkv, to, tl, B, T, H, Hkv, hd, W, dt)
+    # the backward consumes the kernel's own o and lse, as in the step
+    tdq = torch.zeros_like(tqkv)
+    scr = torch.empty(max(16, G.k_attn_bwd_scratch_bytes(B, T, H, hd)), dtype=torch.uint8,
+                      device=DEV)
+    G.k_attn_bwd(tqkv, to, tl, dev(do, tdtype(dt)).reshape(B * T, -1), tdq, scr, B, T, H, Hkv,
+                 hd, W, dt)
+    torch.cuda.synchronize()
+    tol = 2e-2 if bf else 1e-4
+    assert rel_err(to_np(to).reshape(B, T, H, hd), o_ref) < tol
+    assert rel_err(to_np(tl).reshape(B, H, T), lse_ref) < 1e-5
+    g = to_np(tdq).reshape(B, T, -1)
+    if W == 0:
+        # each query sees only itself: P = 1, dS = dP - Delta = 0, so dq and
+        # dk are exactly zero and the oracle's values are rounding noise
+        assert np.abs(g[..., :(H + Hkv) * hd]).max() < 1e-5
+        assert np.abs(dq_ref).max() < 1e-5 and np.abs(dk_ref).max() < 1e-5
+    else:
+        assert rel_err(g[..., :H * hd], dq_ref.reshape(B, T, -1)) < tol
+        assert rel_err(g[..., H * hd:(H + Hkv) * hd], dk_ref.reshape(B, T, -1)) < tol
+    assert rel_err(g[..., (H + Hkv) * hd:], dv_ref.reshape(B, T, -1)) < tol
+
+
+@pytest.mark.parametrize("W", [0, 1, 31, 32, 64, 127, 128])
+@pytest.mark.parametrize("hd", [128, 32])
+def test_attention_mask_exact_one_hot_values(W, hd):
+    """With v_j = e_j the output row i is the probability row P_i itself, so
+    its zero pattern must equal the window predicate exactly."""
+    T = hd
+    B, H, Hkv = 1, 2, 1
+    dt = G.BF16
+    q, k, _, _ = _attn_inputs(B, T, H, Hkv, hd, True, seed=30)
+    q = q * 0.25                                  # keep every visible p far from 0
+    v = np.zeros((B, T, Hkv, hd), np.float32)
+    v[0, np.arange(T), 0, np.arange(T)] = 1.0
+    qkv = np.concatenate([O.round_bf16(q).reshape(B, T, -1), k.reshape(B, T, -1),
+                          v.reshape(B, T, -1)], -1)
+    tqkv = dev(qkv, torch.bfloat16).reshape(B * T, -1)
+    to = torch.empty(B * T, H * hd, dtype=torch.bfloat16, device=DEV)
+    tl = torch.empty(B * H * T, dtype=torch.float32, device=DEV)
+    G.k_attn_fwd(tqkv, to, tl, B, T, H, Hkv, hd, W, dt)
+    torch.cuda.synchronize()
+    o = to_np(to).reshape(T, H, hd)
+    mask = O.visible_mask(T, W)
+    for h in range(H):
+        np.testing.assert_array_equal(o[:, h, :] != 0.0, mask)
+
+
+# ----------------------------------------------------------- cross-entropy
+@pytest.mark.parametrize("dt", [G.BF16, G.F32])
+@pytest.mark.parametrize("V", [27, 1000, 32768])
+def test_cross_entropy(dt, V):
+    rows = 37
+    rng = np.random.default_rng(40)
+    z = (rng.standard_normal((rows, V)) * 3).astype(np.float32)
+    tgt = rng.integers(0, V, rows).astype(np.int32)
+    num = _Num("bf16emu" if dt == G.BF16 else "fp32")
+    ell_ref, lse_ref, dz_ref = O.cross_entropy(z, tgt, num)
+    tz = dev(z, torch.float32)
+    ell = torch.empty(rows, dtype=torch.float32, device=DEV)
+    lse = torch.empty(rows, dtype=torch.float32, device=DEV)
+    dz = torch.empty(rows, V, dtype=tdtype(dt), device=DEV)
+    G.k_ce(tz, dev(tgt, torch.int32), rows, V, ell, lse, dz, 1.0 / rows, dt)
+    torch.cuda.synchronize()
+    assert rel_err(to_np(ell), ell_ref) < 1e-5
+    assert rel_err(to_np(lse), lse_ref) < 1e-6
+    assert rel_err(to_np(dz), num.rnd(dz_ref)) < (1e-2 if dt == G.BF16 else 1e-5)

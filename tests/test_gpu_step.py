@@ -1,0 +1,163 @@
+"""End-to-end parity of gpt_step_fwd / gpt_step_bwd / gpt_eval_bpb against
+the CPU oracle on identical seeded inputs (GPU only).
+
+Bars: floating-point tensors within normwise max relative error 2e-2
+(max|gpu - oracle| / max|oracle|) against the oracle's bf16-emulation mode
+(fp32 mode for fp32 configs); val_bpb within 1e-3 absolute.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import gptinputs as gi
+import oracle as O
+from tests.gpu_util import grads_by_tensor, rel_err, small_bf16, tiny_plus, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import gpt_pretraining_step_amd as G  # noqa: E402
+from gpt_pretraining_step_amd.session import Session  # noqa: E402
+
+TOL = 2e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _prec(cfg):
+    return "bf16emu" if cfg["dtype"] == G.BF16 else "fp32"
+
+
+def run_step(cfg, rows=None, accumulate_check=False):
+    n = O.param_count(cfg)
+    w, bits = gi.make_params(cfg, n)
+    tok = gi.make_tokens(cfg, rows)
+    if rows is not None:
+        cfg = dict(cfg, batch=rows)
+    s = Session(cfg)
+    assert s.n_params == n
+    s.set_params(w, bits)
+    s.set_tokens(tok)
+    s.fwd()
+    s.bwd()
+    torch.cuda.synchronize()
+    loss = float(s.loss.item())
+    N = tok.shape[0] * (tok.shape[1] - 1)
+    ell = to_np(s.ws_f32(G.WS_ELL, N))
+    grads = to_np(s.grads)
+    flag = int(s.ws[G.ws_offset(s.cfg, G.WS_NONFINITE):][:4].view(torch.int32).item())
+    if accumulate_check:
+        s.bwd(accumulate=True)
+        torch.cuda.synchronize()
+        g2 = to_np(s.grads)
+        assert rel_err(g2, 2 * grads) < 1e-6
+    return cfg, w, tok, loss, ell, grads, flag
+
+
+def compare(cfg, w, tok, loss, ell, grads, flag):
+    prec = _prec(cfg)
+    ref_loss, ref_g, cache = O.step(cfg, w, tok, prec)
+    assert flag == 0
+    assert abs(loss - ref_loss) / abs(ref_loss) < (1e-3 if prec == "bf16emu" else 1e-5), \
+        (loss, ref_loss)
+    assert rel_err(ell, cache["ell"]) < TOL
+    got = grads_by_tensor(cfg, grads)
+    ref = grads_by_tensor(cfg, ref_g)
+    errs = {k: rel_err(got[k], ref[k]) for k in ref}
+    say("grad errors", {k: f"{v:.2e}" for k, v in errs.items()})
+    bad = {k: v for k, v in errs.items() if not v < (TOL if prec == "bf16emu" else 1e-4)}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_plus", "small_bf16", "small_bf16_mha",
+                                  "d4"])
+def test_step_matches_oracle(name):
+    cfg = {"tiny": lambda: gi.preset("tiny"), "tiny_plus": tiny_plus,
+           "small_bf16": small_bf16,
+           "small_bf16_mha": lambda: small_bf16(n_kv_head=2, batch=2, seq_len=160,
+                                                window_short=40, window_long=160,
+                                                head_dim=128, n_head=2),
+           "d4": lambda: gi.preset("d4")}[name]()
+    say("step", name)
+    out = run_step(cfg, accumulate_check=(name == "tiny_plus"))
+    compare(*out)
+
+
+@pytest.mark.parametrize("name,n_rows", [("tiny", 11), ("small_bf16", 7), ("d4", 20)])
+def test_eval_bpb_matches_oracle(name, n_rows):
+    cfg = {"tiny": lambda: gi.preset("tiny"), "small_bf16": small_bf16,
+           "d4": lambda: gi.preset("d4")}[name]()
+    say("eval", name, n_rows)
+    n = O.param_count(cfg)
+    w, bits = gi.make_params(cfg, n)
+    tok = gi.make_eval_tokens(cfg, n_rows)          # ragged last batch
+    tb = gi.make_token_bytes(cfg)
+    s = Session(cfg, eval_ws=True, train_ws=False)
+    s.set_params(w, bits)
+    s.evaluate(s.upload(tok), s.upload(tb))
+    torch.cuda.synchronize()
+    got = s.bpb.cpu().numpy()
+    nats, nbytes, bpb = O.eval_bpb(cfg, w, tok, tb, _prec(cfg))
+    assert got[1] == nbytes
+    assert abs(got[2] - bpb) < 1e-3, (got, bpb)
+    assert abs(got[0] - nats) / nats < 1e-3
+
+
+def test_uniform_logits_on_gpu():
+    """With W_lm = 0 the loss is ln V exactly and every gradient but the
+    lm_head's is exactly zero (closed form)."""
+    cfg = small_bf16()
+    n = O.param_count(cfg)
+    w, bits = gi.make_params(cfg, n)
+    off = O.param_count(cfg) - cfg["vocab"] * cfg["d_model"]
+    w = w.copy(); bits = bits.copy()
+    w[off:] = 0; bits[off:] = 0
+    s = Session(cfg)
+    s.set_params(w, bits)
+    s.set_tokens(gi.make_tokens(cfg))
+    s.fwd(); s.bwd()
+    torch.cuda.synchronize()
+    assert abs(s.loss.item() - math.log(cfg["vocab"])) < 1e-6
+    g = to_np(s.grads)
+    assert np.all(g[:off] == 0.0)
+    assert np.abs(g[off:]).max() > 0
+
+
+def test_nonfinite_flag():
+    cfg = small_bf16()
+    n = O.param_count(cfg)
+    w, bits = gi.make_params(cfg, n)
+    bits = bits.copy()
+    bits[-5] = 0x7FC0                      # a NaN in W_lm
+    s = Session(cfg)
+    s.set_params(w, bits)
+    s.set_tokens(gi.make_tokens(cfg))
+    s.fwd()
+    torch.cuda.synchronize()
+    flag = int(s.ws[G.ws_offset(s.cfg, G.WS_NONFINITE):][:4].view(torch.int32).item())
+    assert flag == 1
+    assert not math.isfinite(s.loss.item())
+
+
+def test_deterministic_forward():
+    cfg = small_bf16()
+    n = O.param_count(cfg)
+    w, bits = gi.make_params(cfg, n)
+    s = Session(cfg)
+    s.set_params(w, bits)
+    s.set_tokens(gi.make_tokens(cfg))
+    s.fwd()
+    torch.cuda.synchronize()
+    N = cfg["batch"] * cfg["seq_len"]
+    a = s.ws_f32(G.WS_ELL, N).clone()
+    s.fwd()
+    torch.cuda.synchronize()
+    assert torch.equal(a, s.ws_f32(G.WS_ELL, N))
