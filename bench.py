@@ -81,43 +81,54 @@ def kernel_table(cfg, torch, G, iters=10):
     QKV, HD = (H + 2 * Hkv) * hd, H * hd
     dev = "cuda"
     bf = torch.bfloat16
-    big = torch.randn(N * max(F, QKV), device=dev).to(bf) * 0.1
-    wbuf = torch.randn(V * D, device=dev).to(bf) * 0.02
-    out = torch.empty(N * max(F, V // 8 * 8, QKV), device=dev, dtype=torch.float32)
-    aux = torch.empty(N * F, device=dev, dtype=bf)
     chunk = min(N, (512 << 20) // (V * 4) // 256 * 256)
+    # operand buffers sized for the largest use (checked before each launch)
+    act = (torch.randn(N * max(F, QKV), device=dev) * 0.1).to(bf)        # [N, <=F] activations
+    wts = (torch.randn(V * D, device=dev) * 0.02).to(bf)                 # any weight matrix
+    dz = (torch.randn(N * V, device=dev, dtype=torch.float32) * 1e-5).to(bf)  # [N, V]
+    out32 = torch.empty(max(chunk * V, V * D, F * D), device=dev, dtype=torch.float32)
+    out16 = torch.empty(N * max(F, QKV), device=dev, dtype=bf)
+    aux = torch.empty(N * F, device=dev, dtype=bf)
     rows = []
     nS = sum(1 for l in range(L) if window_of(cfg, l) < T - 1)
     gemms = [
-        # name, op, M, N, K, epi, launches per step
-        ("qkv_fwd NT", G.GEMM_NT, N, QKV, D, G.EPI_STORE, L),
-        ("o_fwd NT+res", G.GEMM_NT, N, D, HD, G.EPI_RESADD, L),
-        ("fc_fwd NT+relu2", G.GEMM_NT, N, F, D, G.EPI_RELU2, L),
-        ("proj_fwd NT+res", G.GEMM_NT, N, D, F, G.EPI_RESADD, L),
-        ("lm_fwd NT f32", G.GEMM_NT, chunk, V, D, G.EPI_F32, N // chunk),
-        ("lm_dx NN", G.GEMM_NN, N, D, V, G.EPI_STORE, 1),
-        ("lm_dw TN", G.GEMM_TN, V, D, N, G.EPI_F32, 1),
-        ("proj_dw TN", G.GEMM_TN, D, F, N, G.EPI_F32, L),
-        ("proj_dx NN+drelu2", G.GEMM_NN, N, F, D, G.EPI_DRELU2, L),
-        ("fc_dw TN", G.GEMM_TN, F, D, N, G.EPI_F32, L),
-        ("fc_dx NN", G.GEMM_NN, N, D, F, G.EPI_STORE, L),
-        ("o_dw TN", G.GEMM_TN, D, HD, N, G.EPI_F32, L),
-        ("o_dx NN", G.GEMM_NN, N, HD, D, G.EPI_STORE, L),
-        ("qkv_dw TN", G.GEMM_TN, QKV, D, N, G.EPI_F32, L),
-        ("qkv_dx NN", G.GEMM_NN, N, D, QKV, G.EPI_STORE, L),
+        # name, op, M, N, K, epi, launches per step, A, B
+        ("qkv_fwd NT", G.GEMM_NT, N, QKV, D, G.EPI_STORE, L, act, wts),
+        ("o_fwd NT+res", G.GEMM_NT, N, D, HD, G.EPI_RESADD, L, act, wts),
+        ("fc_fwd NT+relu2", G.GEMM_NT, N, F, D, G.EPI_RELU2, L, act, wts),
+        ("proj_fwd NT+res", G.GEMM_NT, N, D, F, G.EPI_RESADD, L, act, wts),
+        ("lm_fwd NT f32", G.GEMM_NT, chunk, V, D, G.EPI_F32, N // chunk, act, wts),
+        ("lm_dx NN", G.GEMM_NN, N, D, V, G.EPI_STORE, 1, dz, wts),
+        ("lm_dw TN", G.GEMM_TN, V, D, N, G.EPI_F32, 1, dz, act),
+        ("proj_dw TN", G.GEMM_TN, D, F, N, G.EPI_F32, L, act, act),
+        ("proj_dx NN+drelu2", G.GEMM_NN, N, F, D, G.EPI_DRELU2, L, act, wts),
+        ("fc_dw TN", G.GEMM_TN, F, D, N, G.EPI_F32, L, act, act),
+        ("fc_dx NN", G.GEMM_NN, N, D, F, G.EPI_STORE, L, act, wts),
+        ("o_dw TN", G.GEMM_TN, D, HD, N, G.EPI_F32, L, act, act),
+        ("o_dx NN", G.GEMM_NN, N, HD, D, G.EPI_STORE, L, act, wts),
+        ("qkv_dw TN", G.GEMM_TN, QKV, D, N, G.EPI_F32, L, act, act),
+        ("qkv_dx NN", G.GEMM_NN, N, D, QKV, G.EPI_STORE, L, act, wts),
     ]
-    for name, op, M, Nn, K, epi, count in gemms:
+    for name, op, M, Nn, K, epi, count, A, Bm in gemms:
         lda = K if op != G.GEMM_TN else M
         ldb = K if op == G.GEMM_NT else Nn
         f32 = epi in (G.EPI_F32, G.EPI_F32_ACC)
-        Cb = out if f32 else aux
-        A = big if op != G.GEMM_TN or M * K <= big.numel() else wbuf
-        Bm = wbuf if op != G.GEMM_TN else big
+        Cb = out32 if f32 else out16
+        need_a = (K if op == G.GEMM_TN else M) * lda
+        need_b = (Nn if op == G.GEMM_NT else K) * ldb
+        if A.numel() < need_a or Bm.numel() < need_b or Cb.numel() < M * Nn or \
+                (epi in (G.EPI_RELU2, G.EPI_DRELU2) and aux.numel() < M * Nn):
+            raise RuntimeError(f"bench buffer too small for {name}")
+        sb = G.k_gemm_scratch_bytes(M, Nn, K) if f32 else 0
+        scr = torch.empty(max(sb, 16), device=dev, dtype=torch.uint8) if sb else None
         fn = lambda: G.k_gemm(op, M, Nn, K, A, lda, Bm, ldb, Cb, Nn, epi,
-                              aux if epi in (G.EPI_RELU2, G.EPI_DRELU2) else None, G.BF16)
+                              aux if epi in (G.EPI_RELU2, G.EPI_DRELU2) else None, G.BF16,
+                              scratch=scr)
         t = time_events(fn, iters, torch)
         rows.append(dict(kernel="gemm " + name, avg_s=t, count=count, flops=2.0 * M * Nn * K,
                          bound="mfma"))
+    del act, wts, dz, out32, out16, aux
+    torch.cuda.empty_cache()
     # attention (one short-window and one long-window layer shape)
     qkv = (torch.randn(N, QKV, device=dev) * 0.3).to(bf)
     o = torch.empty(N, HD, device=dev, dtype=bf)
@@ -135,7 +146,7 @@ def kernel_table(cfg, torch, G, iters=10):
                                              G.BF16), max(2, iters // 2), torch)
         rows.append(dict(kernel=f"attn_bwd W={W}", avg_s=t, count=count, flops=2 * fl,
                          bound="mfma"))
-    del big, wbuf, out, aux, qkv, o, do, dqkv, scr
+    del qkv, o, do, dqkv, scr
     torch.cuda.empty_cache()
     return rows
 

@@ -70,8 +70,9 @@ _SIGS = {
     "gpt_last_error": (C.c_char_p, []),
     "gpt_k_rmsnorm_fwd": (C.c_int, [_vp, _vp, _vp, _i64, _i32, _f32, _i32, _vp]),
     "gpt_k_rmsnorm_bwd": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp]),
+    "gpt_k_gemm_scratch_bytes": (_sz, [_i64, _i64, _i64]),
     "gpt_k_gemm": (C.c_int, [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
-                             _i32, _vp, _i32, _vp]),
+                             _i32, _vp, _vp, _sz, _i32, _vp]),
     "gpt_k_rope_table": (C.c_int, [_vp, _i32, _i32, _f32, _vp]),
     "gpt_k_rope_qknorm_fwd": (C.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                         _f32, _i32, _vp]),
@@ -181,9 +182,14 @@ def k_rmsnorm_bwd(dy, y, r, dres, dx, rows, dim, dtype, stream=None):
                                    dtype, _stream(stream)))
 
 
-def k_gemm(op, M, N, K, A, lda, B, ldb, Cm, ldc, epi, aux, dtype, stream=None):
+def k_gemm_scratch_bytes(M, N, K):
+    return int(lib().gpt_k_gemm_scratch_bytes(M, N, K))
+
+
+def k_gemm(op, M, N, K, A, lda, B, ldb, Cm, ldc, epi, aux, dtype, stream=None, scratch=None):
+    nbytes = 0 if scratch is None else scratch.numel() * scratch.element_size()
     _check(lib().gpt_k_gemm(op, M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(Cm), ldc, epi,
-                            _ptr(aux), dtype, _stream(stream)))
+                            _ptr(aux), _ptr(scratch), nbytes, dtype, _stream(stream)))
 
 
 def k_rope_table(cs, T, hd, base, stream=None):

@@ -5,6 +5,7 @@
 
 namespace gk {
 bool attn_mfma_supported(int T, int H, int Hkv, int hd);
+bool attn_mfma_bwd_supported(int T, int H, int Hkv, int hd);
 hipError_t attn_mfma_fwd(const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv,
                          int hd, int W, hipStream_t s);
 size_t attn_mfma_bwd_scratch_bytes(int B, int T, int H, int hd);

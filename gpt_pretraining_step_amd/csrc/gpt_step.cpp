@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -139,7 +140,7 @@ struct Plan {
   size_t cs, x, hf, rf, ell, lse_z, loss, flag, logits, dz, evacc;
   std::vector<LayerBufs> layers;     // train: one per layer; eval: one shared
   // backward scratch
-  size_t dx, dh, du, dout, dqkv, attn_scr, vez;
+  size_t dx, dh, du, dout, dqkv, attn_scr, vez, gemm_scr, gemm_scr_bytes;
   size_t total;
 };
 
@@ -194,8 +195,17 @@ Plan make_plan(const Model& m, int mode) {
     p.dqkv = take(N * (size_t)m.QKV * es);
     p.attn_scr = take(gk::attn_bwd_scratch_bytes(m.B, m.T, m.H, m.hd));
     p.vez = take(N * (size_t)m.Hkv * 4);
+    // split-K partials of the weight-gradient products (largest of them)
+    size_t gs = 0;
+    const int64_t HD = (int64_t)m.H * m.hd;
+    const int64_t shapes[5][2] = {{m.V, m.D}, {m.D, m.F}, {m.F, m.D}, {m.D, HD}, {m.QKV, m.D}};
+    if (m.dt == gk::BF16)
+      for (auto& sh : shapes) gs = std::max(gs, gk::gemm_scratch_bytes(sh[0], sh[1], N));
+    p.gemm_scr_bytes = gs;
+    p.gemm_scr = take(gs);
   } else {
-    p.dx = p.dh = p.du = p.dout = p.dqkv = p.attn_scr = p.vez = 0;
+    p.dx = p.dh = p.du = p.dout = p.dqkv = p.attn_scr = p.vez = p.gemm_scr = 0;
+    p.gemm_scr_bytes = 0;
   }
   p.total = off;
   return p;
@@ -282,6 +292,8 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
   const int es = m.es;
   const gk::DType dt = m.dt;
   const gk::Epi wepi = accumulate ? gk::E_F32_ACC : gk::E_F32;
+  void* gscr = at<void>(ws, p.gemm_scr);
+  const size_t gscr_bytes = p.gemm_scr_bytes;
   void* dx = at<void>(ws, p.dx);
   void* dh = at<void>(ws, p.dh);
   void* du = at<void>(ws, p.du);
@@ -317,13 +329,13 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
     const int64_t HD = (int64_t)m.H * m.hd;
     // MLP
     g = gk::GemmDesc{gk::OP_TN, m.D, m.F, N, dx, m.D, a, m.F, grads + pl.wproj[l], m.F, wepi,
-                     nullptr};
+                     nullptr, gscr, gscr_bytes};
     HIP_TRY(gk::gemm(g, dt, s));
     g = gk::GemmDesc{gk::OP_NN, N, m.F, m.D, dx, m.D, elem(params, pl.wproj[l], es), m.F, du,
                      m.F, gk::E_DRELU2, u};
     HIP_TRY(gk::gemm(g, dt, s));
     g = gk::GemmDesc{gk::OP_TN, m.F, m.D, N, du, m.F, h2, m.D, grads + pl.wfc[l], m.D, wepi,
-                     nullptr};
+                     nullptr, gscr, gscr_bytes};
     HIP_TRY(gk::gemm(g, dt, s));
     g = gk::GemmDesc{gk::OP_NN, N, m.D, m.F, du, m.F, elem(params, pl.wfc[l], es), m.D, dh, m.D,
                      gk::E_STORE, nullptr};
@@ -331,7 +343,7 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
     HIP_TRY(gk::rmsnorm_bwd(dh, h2, at<float>(ws, b.r2), dx, dx, N, m.D, nullptr, nullptr, 0, 0,
                             dt, s));
     // attention
-    g = gk::GemmDesc{gk::OP_TN, m.D, HD, N, dx, m.D, o, HD, grads + pl.wo[l], HD, wepi, nullptr};
+    g = gk::GemmDesc{gk::OP_TN, m.D, HD, N, dx, m.D, o, HD, grads + pl.wo[l], HD, wepi, nullptr, gscr, gscr_bytes};
     HIP_TRY(gk::gemm(g, dt, s));
     g = gk::GemmDesc{gk::OP_NN, N, HD, m.D, dx, m.D, elem(params, pl.wo[l], es), HD, dout, HD,
                      gk::E_STORE, nullptr};
@@ -348,7 +360,7 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
       HIP_TRY(gk::ve_wgrad(vez, h, m.D, N, m.Hkv, m.C, grads + pl.wg[l], accumulate, dt, s));
     }
     g = gk::GemmDesc{gk::OP_TN, m.QKV, m.D, N, dqkv, m.QKV, h, m.D, grads + pl.wqkv[l], m.D,
-                     wepi, nullptr};
+                     wepi, nullptr, gscr, gscr_bytes};
     HIP_TRY(gk::gemm(g, dt, s));
     g = gk::GemmDesc{gk::OP_NN, N, m.D, m.QKV, dqkv, m.QKV, elem(params, pl.wqkv[l], es), m.D,
                      dh, m.D, gk::E_STORE, nullptr};
@@ -534,9 +546,14 @@ int gpt_k_rmsnorm_bwd(const void* dy, const void* y, const float* r, const void*
   return GPT_OK;
 }
 
+size_t gpt_k_gemm_scratch_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1) return 0;
+  return gk::gemm_scratch_bytes(M, N, K);
+}
+
 int gpt_k_gemm(int32_t op, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                const void* B, int64_t ldb, void* C, int64_t ldc, int32_t epilogue, void* aux,
-               int32_t dtype, hipStream_t s) {
+               void* scratch, size_t scratch_bytes, int32_t dtype, hipStream_t s) {
   int st;
   if ((st = dtype_ok(dtype)) || (st = check_ptrs({A, B, C}))) return st;
   if (op < GPT_GEMM_NT || op > GPT_GEMM_TN) return fail(GPT_ERR_INVALID_ARG, "unknown op");
@@ -547,7 +564,9 @@ int gpt_k_gemm(int32_t op, int64_t M, int64_t N, int64_t K, const void* A, int64
   if (M < 0 || N < 0 || K < 1) return fail(GPT_ERR_INVALID_ARG, "bad sizes");
   const int64_t rowA = op == GPT_GEMM_TN ? M : K, rowB = op == GPT_GEMM_NT ? K : N;
   if (lda < rowA || ldb < rowB || ldc < N) return fail(GPT_ERR_INVALID_ARG, "leading dims too small");
-  gk::GemmDesc g{op, M, N, K, A, lda, B, ldb, C, ldc, epilogue, aux};
+  if (scratch && !aligned16(scratch)) return fail(GPT_ERR_MISALIGNED, "scratch misaligned");
+  gk::GemmDesc g{op, M, N, K, A, lda, B, ldb, C, ldc, epilogue, aux,
+                 scratch, scratch ? scratch_bytes : 0};
   KERNEL_TRY(gk::gemm(g, (gk::DType)dtype, s));
   return GPT_OK;
 }

@@ -167,7 +167,7 @@ hipError_t attn_bwd(const void* qkv, const void* o, const float* lse, const void
                     void* dqkv, void* scratch, int B, int T, int H, int Hkv, int hd, int W,
                     DType dt, hipStream_t s) {
   float* delta = (float*)scratch;
-  if (dt == BF16 && attn_mfma_supported(T, H, Hkv, hd)) {
+  if (dt == BF16 && attn_mfma_bwd_supported(T, H, Hkv, hd)) {
     size_t dbytes = (((size_t)B * H * T * sizeof(float) + 255) / 256) * 256;
     return attn_mfma_bwd(qkv, o, lse, dout, dqkv, delta, (char*)scratch + dbytes, B, T, H, Hkv,
                          hd, W, s);

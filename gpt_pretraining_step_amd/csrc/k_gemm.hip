@@ -99,6 +99,10 @@ static hipError_t launch_simple(const GemmDesc& g, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K) {
+  return mfma_splitk_bytes(M, N, K);
+}
+
 hipError_t gemm(const GemmDesc& g, DType dt, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (g.K <= 0) return hipErrorInvalidValue;

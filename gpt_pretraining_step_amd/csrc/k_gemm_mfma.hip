@@ -1,7 +1,369 @@
-// bf16 MFMA GEMM for gfx950 (placeholder: the generic kernel serves all shapes).
+// bf16 MFMA GEMM for gfx950 (CDNA4), fp32 accumulation.
+//
+// Block tile BM x BN x 64 with four wavefronts in a 2 x 2 grid; every wave
+// owns a (BM/2) x (BN/2) sub-tile built from 16x16 v_mfma_f32_16x16x32_bf16
+// blocks.  Operands are staged through LDS in a K-contiguous layout
+// ([rows][64 + 8 pad]); the next K-slice is fetched into registers while the
+// current one is consumed (register double buffering, one LDS stage), so two
+// blocks fit per CU.
+//
+// Operands whose contraction index is the slow one in memory (A of TN, B of
+// NN and TN) are transposed on the way in: each thread loads a KB x 8 patch
+// (KB rows of 16 bytes), transposes it in registers with byte permutes and
+// writes one K-contiguous run per column.  No separate transpose kernel and
+// no extra HBM traffic.
+//
+// The MFMA is issued with B as the first source, so each lane ends up holding
+// four consecutive columns of one output row: the epilogue writes 8-byte
+// (bf16) or 16-byte (fp32) vectors.
+//
+// Blocks are numbered so that consecutive tiles land on the same XCD (the
+// dispatcher deals workgroups round-robin over the 8 XCDs, each with its own
+// L2), and tiles are visited in column-major groups of 8 tile rows.
+//
+// Weight-gradient products (TN) have few output tiles and a long reduction
+// (the tokens), so they split K; partial tiles go to fp32 scratch and a
+// second kernel adds them in a fixed order (deterministic).
+#include <algorithm>
+#include <type_traits>
+
+#include "common.h"
+#include "gemm_epi.h"
 #include "gemm_mfma.h"
 
 namespace gk {
-bool mfma_gemm_supported(const GemmDesc&) { return false; }
-hipError_t mfma_gemm(const GemmDesc&, hipStream_t) { return hipErrorNotSupported; }
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+static constexpr int BK = 64;
+static constexpr int LDK = BK + 8;     // LDS row stride (elements), 144 bytes
+
+// low / high 16-bit halves of two words packed into one word
+__device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t hi_pair(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x07060302u);
+}
+
+// ---------------------------------------------------------------- staging
+// K-contiguous operand: global [rows][ld], tile rows r0.., k0..k0+63.
+template <int R>
+struct KRowStage {
+  static constexpr int CH = R * 8 / 256;    // 16-byte chunks per thread
+  uint4 v[CH];
+  __device__ __forceinline__ void load(const bf16* g, int64_t ld, int64_t r0, int64_t rows,
+                                       int64_t k0, int64_t K) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int r = c >> 3, kc = c & 7;
+      const int64_t gr = r0 + r, gk = k0 + kc * 8;
+      v[i] = (gr < rows && gk < K) ? *(const uint4*)(g + gr * ld + gk) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(bf16* s) const {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int r = c >> 3, kc = c & 7;
+      *(uint4*)(s + r * LDK + kc * 8) = v[i];
+    }
+  }
+};
+
+// MN-contiguous operand: global [K][ld] (row index = k), tile columns r0..,
+// k0..k0+63.  Each thread owns a KB x 8 patch; R/8 patches per KB rows.
+template <int R>
+struct KColStage {
+  static constexpr int NCB = R / 8;                 // 8-wide column blocks
+  static constexpr int KB = 64 * NCB / 256;         // k rows per patch (8 or 4)
+  static_assert(KB == 8 || KB == 4, "tile width");
+  uint4 v[KB];
+  __device__ __forceinline__ void load(const bf16* g, int64_t ld, int64_t r0, int64_t rows,
+                                       int64_t k0, int64_t K) {
+    const int cb = threadIdx.x % NCB, kb = threadIdx.x / NCB;
+    const int64_t col = r0 + cb * 8;
+#pragma unroll
+    for (int r = 0; r < KB; ++r) {
+      const int64_t gk = k0 + kb * KB + r;
+      v[r] = (gk < K && col < rows) ? *(const uint4*)(g + gk * ld + col) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(bf16* s) const {
+    const int cb = threadIdx.x % NCB, kb = threadIdx.x / NCB;
+    const uint32_t* w[KB];
+#pragma unroll
+    for (int r = 0; r < KB; ++r) w[r] = (const uint32_t*)&v[r];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {          // column pair (2d, 2d+1)
+      if constexpr (KB == 8) {
+        uint4 lo, hi;
+        lo.x = lo_pair(w[0][d], w[1][d]); hi.x = hi_pair(w[0][d], w[1][d]);
+        lo.y = lo_pair(w[2][d], w[3][d]); hi.y = hi_pair(w[2][d], w[3][d]);
+        lo.z = lo_pair(w[4][d], w[5][d]); hi.z = hi_pair(w[4][d], w[5][d]);
+        lo.w = lo_pair(w[6][d], w[7][d]); hi.w = hi_pair(w[6][d], w[7][d]);
+        *(uint4*)(s + (cb * 8 + 2 * d) * LDK + kb * 8) = lo;
+        *(uint4*)(s + (cb * 8 + 2 * d + 1) * LDK + kb * 8) = hi;
+      } else {
+        uint2 lo, hi;
+        lo.x = lo_pair(w[0][d], w[1][d]); hi.x = hi_pair(w[0][d], w[1][d]);
+        lo.y = lo_pair(w[2][d], w[3][d]); hi.y = hi_pair(w[2][d], w[3][d]);
+        *(uint2*)(s + (cb * 8 + 2 * d) * LDK + kb * 4) = lo;
+        *(uint2*)(s + (cb * 8 + 2 * d + 1) * LDK + kb * 4) = hi;
+      }
+    }
+  }
+};
+
+template <bool TRANS, int R>
+using Stage = typename std::conditional<TRANS, KColStage<R>, KRowStage<R>>::type;
+
+// ------------------------------------------------------------ epilogue x4
+// Four consecutive columns n..n+3 of row m (n % 4 == 0, N % 4 == 0).
+template <int EPI>
+__device__ __forceinline__ void epi4(void* Cv, void* auxv, int64_t ldc, int64_t m, int64_t n,
+                                     f32x4_t a) {
+  const int64_t i = m * ldc + n;
+  if constexpr (EPI == E_F32) {
+    *(f32x4_t*)((float*)Cv + i) = a;
+  } else if constexpr (EPI == E_F32_ACC) {
+    f32x4_t* p = (f32x4_t*)((float*)Cv + i);
+    *p = *p + a;
+  } else {
+    bf16* C = (bf16*)Cv;
+    float v[4] = {a[0], a[1], a[2], a[3]};
+    if constexpr (EPI == E_RESADD) {
+      const uint2 r = *(const uint2*)(C + i);
+      v[0] += __uint_as_float(r.x << 16); v[1] += __uint_as_float(r.x & 0xFFFF0000u);
+      v[2] += __uint_as_float(r.y << 16); v[3] += __uint_as_float(r.y & 0xFFFF0000u);
+    } else if constexpr (EPI == E_DRELU2) {
+      const uint2 u = *(const uint2*)((const bf16*)auxv + i);
+      v[0] *= 2.0f * fmaxf(__uint_as_float(u.x << 16), 0.f);
+      v[1] *= 2.0f * fmaxf(__uint_as_float(u.x & 0xFFFF0000u), 0.f);
+      v[2] *= 2.0f * fmaxf(__uint_as_float(u.y << 16), 0.f);
+      v[3] *= 2.0f * fmaxf(__uint_as_float(u.y & 0xFFFF0000u), 0.f);
+    }
+    uint2 o;
+    o.x = pack2bf(v[0], v[1]);
+    o.y = pack2bf(v[2], v[3]);
+    *(uint2*)(C + i) = o;
+    if constexpr (EPI == E_RELU2) {      // a = relu(u)^2 of the stored (rounded) u
+      float r0 = fmaxf(__uint_as_float(o.x << 16), 0.f), r1 = fmaxf(__uint_as_float(o.x & 0xFFFF0000u), 0.f);
+      float r2 = fmaxf(__uint_as_float(o.y << 16), 0.f), r3 = fmaxf(__uint_as_float(o.y & 0xFFFF0000u), 0.f);
+      uint2 q;
+      q.x = pack2bf(r0 * r0, r1 * r1);
+      q.y = pack2bf(r2 * r2, r3 * r3);
+      *(uint2*)((bf16*)auxv + i) = q;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ kernel
+struct TileMap {
+  int tiles_m, tiles_n, splits;
+  int64_t k_per_split;     // multiple of BK
+};
+
+template <int BM, int BN, bool TA, bool TB, int EPI>
+__global__ __launch_bounds__(256, 2) void k_gemm_mfma(int64_t M, int64_t N, int64_t K,
+                                                      const bf16* __restrict__ A, int64_t lda,
+                                                      const bf16* __restrict__ B, int64_t ldb,
+                                                      void* C, int64_t ldc, void* aux,
+                                                      TileMap tm, float* partial) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TMI = WM / 16, TNJ = WN / 16;
+  __shared__ __attribute__((aligned(16))) bf16 As[BM * LDK];
+  __shared__ __attribute__((aligned(16))) bf16 Bs[BN * LDK];
+
+  // ---- which tile: XCD-contiguous numbering, then grouped column-major
+  const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
+  const int per_xcd = (nb + 7) / 8;
+  const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (logical >= nb) return;
+  const int ntile = tm.tiles_m * tm.tiles_n;
+  const int split = logical / ntile;
+  const int t = logical % ntile;
+  constexpr int GM = 8;
+  const int group = t / (GM * tm.tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tm.tiles_m - first_m, GM);
+  const int tile_m = first_m + (t % (GM * tm.tiles_n)) % gsize;
+  const int tile_n = (t % (GM * tm.tiles_n)) / gsize;
+  const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
+  const int64_t kbeg = (int64_t)split * tm.k_per_split;
+  const int64_t kend = min(K, kbeg + tm.k_per_split);
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
+
+  f32x4_t acc[TMI][TNJ];
+#pragma unroll
+  for (int i = 0; i < TMI; ++i)
+#pragma unroll
+    for (int j = 0; j < TNJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  Stage<TA, BM> sa;
+  Stage<TB, BN> sb;
+  sa.load(A, lda, m0, M, kbeg, kend);
+  sb.load(B, ldb, n0, N, kbeg, kend);
+  sa.store(As);
+  sb.store(Bs);
+  __syncthreads();
+
+  for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
+    const bool more = k0 + BK < kend;
+    if (more) {
+      sa.load(A, lda, m0, M, k0 + BK, kend);
+      sb.load(B, ldb, n0, N, k0 + BK, kend);
+    }
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      bf16x8_t a[TMI], b[TNJ];
+#pragma unroll
+      for (int i = 0; i < TMI; ++i)
+        a[i] = *(const bf16x8_t*)(As + (wm + 16 * i + lr) * LDK + kk + lk);
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j)
+        b[j] = *(const bf16x8_t*)(Bs + (wn + 16 * j + lr) * LDK + kk + lk);
+#pragma unroll
+      for (int i = 0; i < TMI; ++i)
+#pragma unroll
+        for (int j = 0; j < TNJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+    if (more) {
+      sa.store(As);
+      sb.store(Bs);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane holds rows m = .. + lr, columns n = .. + 4*(lane>>4) + 0..3
+  const int cq = (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < TMI; ++i) {
+    const int64_t m = m0 + wm + 16 * i + lr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < TNJ; ++j) {
+      const int64_t n = n0 + wn + 16 * j + cq;
+      if (n >= N) continue;
+      if (partial) {
+        *(f32x4_t*)(partial + ((int64_t)split * M + m) * N + n) = acc[i][j];
+      } else {
+        epi4<EPI>(C, aux, ldc, m, n, acc[i][j]);
+      }
+    }
+  }
+}
+
+// out[m, n] (=/+=) sum_s partial[s, m, n], fixed order over s
+__global__ void k_splitk_reduce(const float* __restrict__ partial, int splits, int64_t M,
+                                int64_t N, float* out, int64_t ldc, int accumulate) {
+  const int64_t i = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) * 4;
+  const int64_t MN = M * N;
+  if (i >= MN) return;
+  f32x4_t s = *(const f32x4_t*)(partial + i);
+  for (int k = 1; k < splits; ++k) s += *(const f32x4_t*)(partial + (int64_t)k * MN + i);
+  const int64_t m = i / N, n = i % N;
+  f32x4_t* o = (f32x4_t*)(out + m * ldc + n);
+  if (accumulate) s += *o;
+  *o = s;
+}
+
+// ------------------------------------------------------------------ host
+bool mfma_gemm_supported(const GemmDesc& g) {
+  if (g.K % 8 || g.lda % 8 || g.ldb % 8 || g.ldc % 4 || g.N % 4) return false;
+  const bool TA = g.op == OP_TN, TB = g.op != OP_NT;
+  if (TA && g.M % 8) return false;
+  if (TB && g.N % 8) return false;
+  const uintptr_t al = (uintptr_t)g.A | (uintptr_t)g.B | (uintptr_t)g.C |
+                       (uintptr_t)(g.aux ? g.aux : g.C);
+  if (al & 15) return false;
+  return true;
+}
+
+template <int BM, int BN, bool TA, bool TB, int EPI>
+static void launch(const GemmDesc& g, const TileMap& tm, float* partial, hipStream_t s) {
+  const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
+  const int grid = ((nb + 7) / 8) * 8;
+  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, TA, TB, EPI>), dim3(grid), dim3(256), 0, s, g.M, g.N,
+                     g.K, (const bf16*)g.A, g.lda, (const bf16*)g.B, g.ldb, g.C, g.ldc, g.aux, tm,
+                     partial);
+}
+
+template <int BM, int BN, bool TA, bool TB>
+static void launch_epi(const GemmDesc& g, const TileMap& tm, float* partial, hipStream_t s) {
+  switch (g.epi) {
+    case E_STORE:   launch<BM, BN, TA, TB, E_STORE>(g, tm, partial, s); break;
+    case E_RESADD:  launch<BM, BN, TA, TB, E_RESADD>(g, tm, partial, s); break;
+    case E_RELU2:   launch<BM, BN, TA, TB, E_RELU2>(g, tm, partial, s); break;
+    case E_DRELU2:  launch<BM, BN, TA, TB, E_DRELU2>(g, tm, partial, s); break;
+    case E_F32:     launch<BM, BN, TA, TB, E_F32>(g, tm, partial, s); break;
+    default:        launch<BM, BN, TA, TB, E_F32_ACC>(g, tm, partial, s); break;
+  }
+}
+
+template <int BM, int BN>
+static void launch_op(const GemmDesc& g, const TileMap& tm, float* partial, hipStream_t s) {
+  if (g.op == OP_NT) launch_epi<BM, BN, false, false>(g, tm, partial, s);
+  else if (g.op == OP_NN) launch_epi<BM, BN, false, true>(g, tm, partial, s);
+  else launch_epi<BM, BN, true, true>(g, tm, partial, s);
+}
+
+// Tile shape and K split of one product.  `scratch_bytes` bounds the split
+// (SIZE_MAX: as the shape asks).
+static TileMap plan(int64_t M, int64_t N, int64_t K, bool f32out, size_t scratch_bytes, int* bm) {
+  const int kCU = 256;
+  // the large tile unless it leaves the chip badly under-filled
+  int BM = 256, BN = 128;
+  int64_t tiles = cdiv(M, 256) * cdiv(N, 128);
+  if (tiles < 2 * kCU) { BM = 128; BN = 128; tiles = cdiv(M, 128) * cdiv(N, 128); }
+  TileMap tm;
+  tm.tiles_m = (int)cdiv(M, BM);
+  tm.tiles_n = (int)cdiv(N, BN);
+  tm.splits = 1;
+  tm.k_per_split = cdiv(K, BK) * BK;
+  if (f32out && tiles < kCU) {
+    // split the reduction so the grid reaches ~2 blocks per CU, keeping at
+    // least 8 K-slices per split
+    const int64_t ksl = cdiv(K, BK);
+    int sp = (int)cdiv(2 * kCU, tiles);
+    sp = (int)std::min<int64_t>(sp, ksl / 8);
+    sp = std::min(sp, 64);
+    while (sp > 1 && (size_t)sp * M * N * 4 > scratch_bytes) --sp;
+    if (sp > 1) {
+      tm.k_per_split = cdiv(ksl, sp) * BK;
+      tm.splits = (int)cdiv(K, tm.k_per_split);
+    }
+  }
+  *bm = BM;
+  return tm;
+}
+
+size_t mfma_splitk_bytes(int64_t M, int64_t N, int64_t K) {
+  int bm;
+  TileMap tm = plan(M, N, K, true, SIZE_MAX, &bm);
+  return tm.splits > 1 ? (size_t)tm.splits * M * N * sizeof(float) : 0;
+}
+
+hipError_t mfma_gemm(const GemmDesc& g, hipStream_t s) {
+  const bool f32out = g.epi == E_F32 || g.epi == E_F32_ACC;
+  int BM;
+  TileMap tm = plan(g.M, g.N, g.K, f32out, g.scratch ? g.scratch_bytes : 0, &BM);
+  float* partial = tm.splits > 1 ? (float*)g.scratch : nullptr;
+  if (BM == 256) launch_op<256, 128>(g, tm, partial, s);
+  else launch_op<128, 128>(g, tm, partial, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !partial) return e;
+  const int64_t MN = g.M * g.N;
+  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)cdiv(MN / 4, 256)), dim3(256), 0, s, partial,
+                     tm.splits, g.M, g.N, (float*)g.C, g.ldc, g.epi == E_F32_ACC ? 1 : 0);
+  return hipGetLastError();
+}
+
 }  // namespace gk

@@ -39,8 +39,12 @@ struct GemmDesc {
   void* C; int64_t ldc;
   int epi;           // Epi
   void* aux;         // RELU2: output a; DRELU2: input u   (ldc, dtype)
+  void* scratch;     // optional fp32 split-K partials (fp32 epilogues only)
+  size_t scratch_bytes;
 };
 hipError_t gemm(const GemmDesc& g, DType dt, hipStream_t s);
+// scratch bytes gemm() would use for this bf16 product with an fp32 epilogue
+size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K);
 
 hipError_t rope_qknorm_fwd(void* qkv, float* rq, float* rk, const float* cs,
                            int B, int T, int H, int Hkv, int hd, float eps,

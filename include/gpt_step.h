@@ -209,9 +209,16 @@ int gpt_k_rmsnorm_bwd(const void* dy, const void* y, const float* r,
 enum { GPT_GEMM_NT = 0, GPT_GEMM_NN = 1, GPT_GEMM_TN = 2 };
 enum { GPT_EPI_STORE = 0, GPT_EPI_RESADD, GPT_EPI_RELU2, GPT_EPI_DRELU2,
        GPT_EPI_F32, GPT_EPI_F32_ACC };
+/* scratch (may be null): device fp32 space for split-K partial tiles of
+ * fp32-epilogue bf16 products; gpt_k_gemm_scratch_bytes gives the size that
+ * lets the product split as far as it wants (less scratch, fewer splits).
+ * The result does not depend on whether or how the product is split, up to
+ * fp32 summation order. */
+size_t gpt_k_gemm_scratch_bytes(int64_t M, int64_t N, int64_t K);
 int gpt_k_gemm(int32_t op, int64_t M, int64_t N, int64_t K, const void* A,
                int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
-               int32_t epilogue, void* aux, int32_t dtype, hipStream_t s);
+               int32_t epilogue, void* aux, void* scratch, size_t scratch_bytes,
+               int32_t dtype, hipStream_t s);
 
 /* cos/sin table, float2 [T, hd/2]: (cos, sin) of t * base^(-2j/hd),
  * evaluated in double precision. */

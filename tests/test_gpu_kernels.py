@@ -73,6 +73,35 @@ def test_gemm_store_and_f32(dt, op, shape):
     tol = 8e-3 if bf else 1e-5
     assert rel_err(to_np(C), ref) < tol
     assert rel_err(to_np(C32), ref + 0.5) < 1e-5
+    if bf and op == G.GEMM_TN:
+        # the same products with split-K scratch: partial tiles summed in order
+        sb = G.k_gemm_scratch_bytes(M, N, K)
+        scr = torch.empty(max(sb, 16), dtype=torch.uint8, device=DEV)
+        S32 = torch.full((M, N), 0.5, dtype=torch.float32, device=DEV)
+        G.k_gemm(op, M, N, K, tA, lda, tB, ldb, S32, N, G.EPI_F32_ACC, None, dt, scratch=scr)
+        S0 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        G.k_gemm(op, M, N, K, tA, lda, tB, ldb, S0, N, G.EPI_F32, None, dt, scratch=scr)
+        torch.cuda.synchronize()
+        assert rel_err(to_np(S32), ref + 0.5) < 1e-5
+        assert rel_err(to_np(S0), ref) < 1e-5
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 512, 4096), (384, 128, 8192), (64, 96, 1024)])
+def test_gemm_tn_split_k(M, N, K):
+    """Weight-gradient shapes: few output tiles, long reduction."""
+    A, B = rnd_in((K, M), 13), rnd_in((K, N), 14)
+    ref = A.astype(np.float64).T @ B.astype(np.float64)
+    sb = G.k_gemm_scratch_bytes(M, N, K)
+    assert sb > 0
+    scr = torch.empty(sb, dtype=torch.uint8, device=DEV)
+    C32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    tA, tB = dev(A, torch.bfloat16), dev(B, torch.bfloat16)
+    G.k_gemm(G.GEMM_TN, M, N, K, tA, M, tB, N, C32, N, G.EPI_F32, None, G.BF16, scratch=scr)
+    first = C32.clone()
+    G.k_gemm(G.GEMM_TN, M, N, K, tA, M, tB, N, C32, N, G.EPI_F32, None, G.BF16, scratch=scr)
+    torch.cuda.synchronize()
+    assert rel_err(to_np(C32), ref) < 1e-5
+    assert torch.equal(first, C32)            # fixed-order reduction: bitwise repeatable
 
 
 @pytest.mark.parametrize("dt", [G.BF16, G.F32])
