@@ -30,6 +30,13 @@ constexpr int TR = 64;            // rows per staged tile
 constexpr int LDR = HD + 8;       // R-tile row stride (elements)
 constexpr int LDT = TR + 8;       // T-tile row stride (elements)
 
+// T-tile element offset of (head-dim row, position): 8-element chunks XOR-
+// swizzled by (row / 16) % 8 so the transposing writes (lanes 8 rows apart)
+// spread over the banks; reads of 16 consecutive rows stay conflict-free.
+__device__ __forceinline__ int toff(int row, int pos) {
+  return row * LDT + ((((pos >> 3) ^ (row >> 4)) & 7) << 3) + (pos & 7);
+}
+
 __device__ __forceinline__ f32x4_t mfma(bf16x8_t x, bf16x8_t y, f32x4_t acc) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc, 0, 0, 0);
 }
@@ -51,11 +58,16 @@ __device__ __forceinline__ bf16x8_t pack8(f32x4_t a, f32x4_t b) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-// Global rows [row0, row0 + 64) of a [T][ld] matrix (128 columns from col0),
-// fetched by NT threads into registers; rows >= T read as zero.
+// Global rows [row0, row0 + 64) of a [T][ld] matrix (128 columns), fetched
+// by NT threads into registers; rows >= T read as zero.  Either as 16-byte
+// row chunks (store_rows) or as PR x 8 patches (PR = 8 for 128 threads, 4
+// for 256), which can be written both as an R tile and, transposed, as a T
+// tile.
 template <int NT>
 struct TileRegs {
   static constexpr int NV = TR * HD / 8 / NT;      // uint4 per thread
+  static constexpr int PR = NV;                    // patch rows: one patch per thread
+  static_assert(PR == 8 || PR == 4, "128 or 256 threads");
   uint4 v[NV];
   __device__ __forceinline__ void load_rows(const bf16* g, int64_t ld, int row0, int T) {
     // chunk c: row c / 16, 8-column group c % 16
@@ -75,47 +87,47 @@ struct TileRegs {
       *(uint4*)(s + r * LDR + ch * 8) = v[i];
     }
   }
-  // patch p (8 rows x 8 columns): rows 8*(p / 16).., columns 8*(p % 16)..
+  // patch of this thread: rows PR*(tid / 16) + e, columns 8*(tid % 16)..
   __device__ __forceinline__ void load_patches(const bf16* g, int64_t ld, int row0, int T) {
-    constexpr int NP = TR * HD / 64 / NT;            // patches per thread
-    static_assert(NV == 8 * NP, "patch count");
+    const int rb = threadIdx.x >> 4, cb = threadIdx.x & 15;
 #pragma unroll
-    for (int pi = 0; pi < NP; ++pi) {
-      const int p = threadIdx.x + NT * pi;
-      const int rb = p >> 4, cb = p & 15;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = row0 + rb * 8 + e;
-        v[pi * 8 + e] = row < T ? *(const uint4*)(g + (int64_t)row * ld + cb * 8)
-                                : make_uint4(0, 0, 0, 0);
-      }
+    for (int e = 0; e < PR; ++e) {
+      const int row = row0 + rb * PR + e;
+      v[e] = row < T ? *(const uint4*)(g + (int64_t)row * ld + cb * 8) : make_uint4(0, 0, 0, 0);
     }
   }
+  __device__ __forceinline__ void store_patches_R(bf16* s) const {
+    const int rb = threadIdx.x >> 4, cb = threadIdx.x & 15;
+#pragma unroll
+    for (int e = 0; e < PR; ++e) *(uint4*)(s + (rb * PR + e) * LDR + cb * 8) = v[e];
+  }
   __device__ __forceinline__ void store_patches_T(bf16* s) const {
-    constexpr int NP = TR * HD / 64 / NT;
+    const int rb = threadIdx.x >> 4, cb = threadIdx.x & 15;
+    const uint32_t* w[PR];
 #pragma unroll
-    for (int pi = 0; pi < NP; ++pi) {
-      const int p = threadIdx.x + NT * pi;
-      const int rb = p >> 4, cb = p & 15;
-      // rows 8*rb + e of the tile: chunk rb/4, 8-row group q = rb%4 inside it
-      const int q = rb & 3;
-      const int base0 = 32 * (rb >> 2) + 16 * (q & 1) + 4 * (q >> 1);
-      const uint32_t* w[8];
+    for (int e = 0; e < PR; ++e) w[e] = (const uint32_t*)&v[e];
+    // position of tile row j (inside its 32-row chunk): 8 g + 4 blk + r for
+    // j = 16 blk + 4 g + r; the patch rows form runs of 4 consecutive positions
+    int base0;
+    if constexpr (PR == 8) {
+      const int q = rb & 3;                         // 8-row group inside the chunk
+      base0 = 32 * (rb >> 2) + 16 * (q & 1) + 4 * (q >> 1);
+    } else {
+      const int q = rb & 7;                         // 4-row group inside the chunk
+      base0 = 32 * (rb >> 3) + 8 * (q & 3) + 4 * (q >> 2);
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = (const uint32_t*)&v[pi * 8 + e];
+    for (int d = 0; d < 4; ++d) {
+      const int r0 = cb * 8 + 2 * d;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint2 lo0, hi0, lo1, hi1;
-        lo0.x = lo_pair(w[0][d], w[1][d]); hi0.x = hi_pair(w[0][d], w[1][d]);
-        lo0.y = lo_pair(w[2][d], w[3][d]); hi0.y = hi_pair(w[2][d], w[3][d]);
-        lo1.x = lo_pair(w[4][d], w[5][d]); hi1.x = hi_pair(w[4][d], w[5][d]);
-        lo1.y = lo_pair(w[6][d], w[7][d]); hi1.y = hi_pair(w[6][d], w[7][d]);
-        bf16* c0 = s + (cb * 8 + 2 * d) * LDT;
-        bf16* c1 = c0 + LDT;
-        *(uint2*)(c0 + base0) = lo0;
-        *(uint2*)(c0 + base0 + 8) = lo1;
-        *(uint2*)(c1 + base0) = hi0;
-        *(uint2*)(c1 + base0 + 8) = hi1;
+      for (int run = 0; run < PR / 4; ++run) {
+        uint2 lo, hi;
+        lo.x = lo_pair(w[4 * run][d], w[4 * run + 1][d]);
+        hi.x = hi_pair(w[4 * run][d], w[4 * run + 1][d]);
+        lo.y = lo_pair(w[4 * run + 2][d], w[4 * run + 3][d]);
+        hi.y = hi_pair(w[4 * run + 2][d], w[4 * run + 3][d]);
+        *(uint2*)(s + toff(r0, base0 + 8 * run)) = lo;
+        *(uint2*)(s + toff(r0 + 1, base0 + 8 * run)) = hi;
       }
     }
   }
@@ -127,7 +139,7 @@ __device__ __forceinline__ bf16x8_t rfrag(const bf16* s, int row, int ks, int g)
 }
 // 8 contraction values of a T tile: head-dim row `hrow`, 32-row chunk `ch`.
 __device__ __forceinline__ bf16x8_t tfrag(const bf16* s, int hrow, int ch, int g) {
-  return *(const bf16x8_t*)(s + hrow * LDT + 32 * ch + 8 * g);
+  return *(const bf16x8_t*)(s + toff(hrow, 32 * ch + 8 * g));
 }
 
 }  // namespace attn

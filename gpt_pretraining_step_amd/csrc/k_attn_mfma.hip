@@ -5,8 +5,8 @@
 // 1/sqrt(128).  Exact: an online softmax over 64-key tiles; tiles with no
 // visible pair are never loaded, tiles with every pair visible skip the mask.
 //
-// Forward: one workgroup = 2 waves = 128 queries of one (row, head); each
-// wave owns 64 queries and keeps them in registers.  Scores are formed
+// Forward: one workgroup = 4 waves = 128 queries of one (row, head); each
+// wave owns 32 queries and keeps them in registers (two waves per SIMD fit).  Scores are formed
 // transposed (keys x queries, X = K tile, Y = Q), so every lane owns one
 // query of each 16-query block and its running max / sum are lane-local
 // after a 4-lane reduction.  P goes from the score accumulators straight
@@ -22,7 +22,9 @@
 namespace gk {
 using namespace attn;
 
-static constexpr int FWD_BQ = 128;      // queries per workgroup (2 waves x 64)
+static constexpr int NW = 4;                   // waves per workgroup
+static constexpr int QW = 32;                  // queries per wave (2 blocks of 16)
+static constexpr int FWD_BQ = NW * QW;         // queries per workgroup
 static constexpr float kLog2e = 1.4426950408889634f;
 static constexpr float kLn2 = 0.6931471805599453f;
 
@@ -32,7 +34,7 @@ __device__ __forceinline__ void key_range(int q_lo, int q_hi, int W, int& lo, in
   hi = q_hi;
 }
 
-__global__ __launch_bounds__(128, 1) void k_attn_fwd_mfma(const bf16* __restrict__ qkv,
+__global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict__ qkv,
                                                           bf16* __restrict__ o,
                                                           float* __restrict__ lse, int T, int H,
                                                           int Hkv, int W) {
@@ -51,13 +53,13 @@ __global__ __launch_bounds__(128, 1) void k_attn_fwd_mfma(const bf16* __restrict
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, lr = lane & 15;
   const int q0 = qblk * FWD_BQ;
-  const int qw = q0 + wave * 64;                       // this wave's first query
+  const int qw = q0 + wave * QW;                       // this wave's first query
   const float sl2 = kLog2e / sqrtf((float)HD);        // scores in log2 units
 
-  // this wave's 64 queries, as MFMA Y operands: qf[qb][ks]
-  bf16x8_t qf[4][4];
+  // this wave's queries as MFMA Y operands: qf[qb][ks]
+  bf16x8_t qf[2][4];
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
+  for (int qb = 0; qb < 2; ++qb) {
     const int qi = qw + 16 * qb + lr;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -66,10 +68,10 @@ __global__ __launch_bounds__(128, 1) void k_attn_fwd_mfma(const bf16* __restrict
       qf[qb][ks] = __builtin_bit_cast(bf16x8_t, u);
     }
   }
-  float m[4], l[4];
-  f32x4_t oacc[8][4];
+  float m[2], l[2];
+  f32x4_t oacc[8][2];
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
+  for (int qb = 0; qb < 2; ++qb) {
     m[qb] = -INFINITY;
     l[qb] = 0.f;
 #pragma unroll
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(128, 1) void k_attn_fwd_mfma(const bf16* __restrict
   key_range(q0, min(q0 + FWD_BQ, T) - 1, W, klo, khi);
   const int kt0 = klo / TR, kt1 = khi / TR;
 
-  TileRegs<128> kr, vr;
+  TileRegs<256> kr, vr;
   kr.load_rows(kbase, ldq, kt0 * TR, T);
   vr.load_patches(vbase, ldq, kt0 * TR, T);
 
@@ -93,26 +95,26 @@ __global__ __launch_bounds__(128, 1) void k_attn_fwd_mfma(const bf16* __restrict
       kr.load_rows(kbase, ldq, k0 + TR, T);
       vr.load_patches(vbase, ldq, k0 + TR, T);
     }
-    // pairs of this wave: queries [qw, qw+63], keys [k0, k0+63]
-    const bool any = (qw + 63 >= k0) && (qw - (k0 + 63) <= W) && qw < T;
-    const bool full = (qw >= k0 + 63) && (qw + 63 - k0 <= W);
+    // pairs of this wave: queries [qw, qw+31], keys [k0, k0+63]
+    const bool any = (qw + QW - 1 >= k0) && (qw - (k0 + TR - 1) <= W) && qw < T;
+    const bool full = (qw >= k0 + TR - 1) && (qw + QW - 1 - k0 <= W);
     if (any) {
-      f32x4_t s[4][4];
+      f32x4_t s[4][2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) s[kb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           const bf16x8_t kf = rfrag(Ks, 16 * kb + lr, ks, g);
 #pragma unroll
-          for (int qb = 0; qb < 4; ++qb) s[kb][qb] = mfma(kf, qf[qb][ks], s[kb][qb]);
+          for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma(kf, qf[qb][ks], s[kb][qb]);
         }
       }
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
+      for (int qb = 0; qb < 2; ++qb) {
         const int qi = qw + 16 * qb + lr;
         float mx = -INFINITY;
 #pragma unroll
@@ -148,14 +150,14 @@ __global__ __launch_bounds__(128, 1) void k_attn_fwd_mfma(const bf16* __restrict
       }
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
-        bf16x8_t pf[4];
+        bf16x8_t pf[2];
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) pf[qb] = pack8(s[2 * ch][qb], s[2 * ch + 1][qb]);
+        for (int qb = 0; qb < 2; ++qb) pf[qb] = pack8(s[2 * ch][qb], s[2 * ch + 1][qb]);
 #pragma unroll
         for (int hb = 0; hb < 8; ++hb) {
           const bf16x8_t vf = tfrag(Vt, 16 * hb + lr, ch, g);
 #pragma unroll
-          for (int qb = 0; qb < 4; ++qb) oacc[hb][qb] = mfma(vf, pf[qb], oacc[hb][qb]);
+          for (int qb = 0; qb < 2; ++qb) oacc[hb][qb] = mfma(vf, pf[qb], oacc[hb][qb]);
         }
       }
     }
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(128, 1) void k_attn_fwd_mfma(const bf16* __restrict
 
   // normalise and store: lane holds O[query][16 hb + 4 g + r]
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
+  for (int qb = 0; qb < 2; ++qb) {
     float lt = l[qb];
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
@@ -191,19 +193,361 @@ hipError_t attn_mfma_fwd(const void* qkv, void* o, float* lse, int B, int T, int
                          int hd, int W, hipStream_t s) {
   (void)hd;
   dim3 grid((T + FWD_BQ - 1) / FWD_BQ, H, B);
-  hipLaunchKernelGGL(k_attn_fwd_mfma, grid, dim3(128), 0, s, (const bf16*)qkv, (bf16*)o, lse, T,
-                     H, Hkv, W);
+  hipLaunchKernelGGL(k_attn_fwd_mfma, grid, dim3(NW * 64), 0, s, (const bf16*)qkv, (bf16*)o, lse,
+                     T, H, Hkv, W);
   return hipGetLastError();
 }
 
-bool attn_mfma_bwd_supported(int, int, int, int) { return false; }
+// ---------------------------------------------------------------- backward
+//
+// Delta_i = sum_d dO[i, d] O[i, d] per (row, head): 16 lanes per head row.
+__global__ __launch_bounds__(256) void k_attn_delta(const bf16* __restrict__ o,
+                                                    const bf16* __restrict__ dout,
+                                                    float* __restrict__ delta, int T, int H,
+                                                    int64_t rows) {
+  const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t rh = gid >> 4;                        // (token, head) index
+  const int part = gid & 15;
+  const bool valid = rh < rows;
+  const int64_t r = valid ? rh : 0;
+  const uint4 a = *(const uint4*)(o + r * HD + part * 8);
+  const uint4 d = *(const uint4*)(dout + r * HD + part * 8);
+  const uint32_t* wa = (const uint32_t*)&a;
+  const uint32_t* wd = (const uint32_t*)&d;
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc += __uint_as_float(wa[e] << 16) * __uint_as_float(wd[e] << 16);
+    acc += __uint_as_float(wa[e] & 0xFFFF0000u) * __uint_as_float(wd[e] & 0xFFFF0000u);
+  }
+  acc = seg_sum(acc, 16);
+  if (valid && part == 0) {
+    const int64_t n = r / H;                          // token = b*T + t
+    const int hh = (int)(r % H);
+    const int64_t b = n / T, t = n % T;
+    delta[(b * H + hh) * T + t] = acc;
+  }
+}
+
+// dK, dV of 128 keys of one KV head (4 waves x 32 keys), summed over the G
+// query heads of the group and every 64-query tile that sees these keys.
+// Scores are formed queries x keys (X = Q tile, Y = K in registers), so each
+// lane owns one key; P and dS feed dV^T += dO^T P and dK^T += Q^T dS from
+// registers, with dO and Q staged transposed.
+static constexpr int KV_BK = NW * 32;          // keys per workgroup
+
+__global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict__ qkv,
+                                                         const bf16* __restrict__ dout,
+                                                         const float* __restrict__ lse,
+                                                         const float* __restrict__ delta,
+                                                         bf16* __restrict__ dqkv, int T, int H,
+                                                         int Hkv, int W) {
+  __shared__ __attribute__((aligned(16))) bf16 Qs[TR * LDR];
+  __shared__ __attribute__((aligned(16))) bf16 Qt[HD * LDT];
+  __shared__ __attribute__((aligned(16))) bf16 Ds[TR * LDR];
+  __shared__ __attribute__((aligned(16))) bf16 Dt[HD * LDT];
+  __shared__ float Ls[TR], Dl[TR];
+
+  const int nkb = (T + KV_BK - 1) / KV_BK;
+  const int kblk = nkb - 1 - (int)blockIdx.x;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int G = H / Hkv;
+  const int64_t ldq = (int64_t)(H + 2 * Hkv) * HD, ldo = (int64_t)H * HD;
+  const bf16* rowbase = qkv + (int64_t)b * T * ldq;
+  const bf16* obase = dout + (int64_t)b * T * ldo;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, lr = lane & 15;
+  const int k0 = kblk * KV_BK;
+  const int kw = k0 + 32 * wave;                      // this wave's first key
+  const float sl2 = kLog2e / sqrtf((float)HD);
+
+  bf16x8_t kf[2][4], vf[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = kw + 16 * kb + lr;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int64_t off = (int64_t)key * ldq + 32 * ks + 8 * g;
+      uint4 uk = key < T ? *(const uint4*)(rowbase + off + (int64_t)(H + kvh) * HD) : make_uint4(0, 0, 0, 0);
+      uint4 uv = key < T ? *(const uint4*)(rowbase + off + (int64_t)(H + Hkv + kvh) * HD) : make_uint4(0, 0, 0, 0);
+      kf[kb][ks] = __builtin_bit_cast(bf16x8_t, uk);
+      vf[kb][ks] = __builtin_bit_cast(bf16x8_t, uv);
+    }
+  }
+  f32x4_t dk[8][2], dv[8][2];
+#pragma unroll
+  for (int hb = 0; hb < 8; ++hb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      dk[hb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      dv[hb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+  // queries that see keys [k0, k0+127]: [k0, k0 + 127 + W]
+  const int qhi = (int)min((int64_t)T - 1, (int64_t)k0 + KV_BK - 1 + W);
+  const int qt0 = k0 / TR, nqt = qhi / TR - qt0 + 1;
+  const int iters = G * nqt;
+
+  TileRegs<256> qr, dr;
+  {
+    const int h = kvh * G;
+    qr.load_patches(rowbase + (int64_t)h * HD, ldq, qt0 * TR, T);
+    dr.load_patches(obase + (int64_t)h * HD, ldo, qt0 * TR, T);
+  }
+  for (int it = 0; it < iters; ++it) {
+    const int h = kvh * G + it / nqt;
+    const int q0 = (qt0 + it % nqt) * TR;
+    qr.store_patches_R(Qs);
+    qr.store_patches_T(Qt);
+    dr.store_patches_R(Ds);
+    dr.store_patches_T(Dt);
+    if (threadIdx.x < TR) {
+      const int q = q0 + threadIdx.x;
+      const int64_t li = ((int64_t)b * H + h) * T + q;
+      Ls[threadIdx.x] = q < T ? lse[li] * kLog2e : INFINITY;   // no probability mass
+      Dl[threadIdx.x] = q < T ? delta[li] : 0.f;
+    }
+    __syncthreads();
+    if (it + 1 < iters) {
+      const int hn = kvh * G + (it + 1) / nqt;
+      const int qn = (qt0 + (it + 1) % nqt) * TR;
+      qr.load_patches(rowbase + (int64_t)hn * HD, ldq, qn, T);
+      dr.load_patches(obase + (int64_t)hn * HD, ldo, qn, T);
+    }
+    // pairs of this wave: queries [q0, q0+63], keys [kw, kw+31]
+    const bool any = (q0 + TR - 1 >= kw) && (q0 - (kw + 31) <= W) && kw < T;
+    const bool full = (q0 >= kw + 31) && (q0 + TR - 1 - kw <= W);
+    if (any) {
+      f32x4_t s[4][2], dp[4][2];
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[qb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          dp[qb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+          const bf16x8_t qx = rfrag(Qs, 16 * qb + lr, ks, g);
+          const bf16x8_t dx = rfrag(Ds, 16 * qb + lr, ks, g);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            s[qb][kb] = mfma(qx, kf[kb][ks], s[qb][kb]);
+            dp[qb][kb] = mfma(dx, vf[kb][ks], dp[qb][kb]);
+          }
+        }
+      // P = exp(S - lse), dS = P (dP - Delta); lane: query 16qb+4g+r, key 16kb+lr
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int qi = 16 * qb + 4 * g + r;
+          const float L2 = Ls[qi], Dq = Dl[qi];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            float p = exp2f(s[qb][kb][r] * sl2 - L2);
+            if (!full) {
+              const int d = q0 + qi - (kw + 16 * kb + lr);
+              if (d < 0 || d > W) p = 0.f;
+            }
+            s[qb][kb][r] = p;
+            dp[qb][kb][r] = p * (dp[qb][kb][r] - Dq);
+          }
+        }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8_t pp = pack8(s[2 * c][kb], s[2 * c + 1][kb]);
+          const bf16x8_t ps = pack8(dp[2 * c][kb], dp[2 * c + 1][kb]);
+#pragma unroll
+          for (int hb = 0; hb < 8; ++hb) {
+            dv[hb][kb] = mfma(tfrag(Dt, 16 * hb + lr, c, g), pp, dv[hb][kb]);
+            dk[hb][kb] = mfma(tfrag(Qt, 16 * hb + lr, c, g), ps, dk[hb][kb]);
+          }
+        }
+    }
+    __syncthreads();
+  }
+  // lane holds dK^T / dV^T [16hb + 4g + r][key 16kb + lr]
+  const float scale = 1.0f / sqrtf((float)HD);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = kw + 16 * kb + lr;
+    if (key >= T) continue;
+    bf16* krow = dqkv + ((int64_t)b * T + key) * ldq + (int64_t)(H + kvh) * HD;
+    bf16* vrow = dqkv + ((int64_t)b * T + key) * ldq + (int64_t)(H + Hkv + kvh) * HD;
+#pragma unroll
+    for (int hb = 0; hb < 8; ++hb) {
+      uint2 uk, uv;
+      uk.x = pack2bf(dk[hb][kb][0] * scale, dk[hb][kb][1] * scale);
+      uk.y = pack2bf(dk[hb][kb][2] * scale, dk[hb][kb][3] * scale);
+      uv.x = pack2bf(dv[hb][kb][0], dv[hb][kb][1]);
+      uv.y = pack2bf(dv[hb][kb][2], dv[hb][kb][3]);
+      *(uint2*)(krow + 16 * hb + 4 * g) = uk;
+      *(uint2*)(vrow + 16 * hb + 4 * g) = uv;
+    }
+  }
+}
+
+// dQ of 128 queries of one head (4 waves x 32), over the key tiles they see.
+// Scores keys x queries as in the forward; dS feeds dQ^T += K^T dS with K
+// staged transposed.
+__global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(const bf16* __restrict__ qkv,
+                                                        const bf16* __restrict__ dout,
+                                                        const float* __restrict__ lse,
+                                                        const float* __restrict__ delta,
+                                                        bf16* __restrict__ dqkv, int T, int H,
+                                                        int Hkv, int W) {
+  __shared__ __attribute__((aligned(16))) bf16 Ks[TR * LDR];
+  __shared__ __attribute__((aligned(16))) bf16 Kt[HD * LDT];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[TR * LDR];
+
+  const int nqb = (T + FWD_BQ - 1) / FWD_BQ;
+  const int qblk = nqb - 1 - (int)blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int kvh = h / (H / Hkv);
+  const int64_t ldq = (int64_t)(H + 2 * Hkv) * HD, ldo = (int64_t)H * HD;
+  const bf16* rowbase = qkv + (int64_t)b * T * ldq;
+  const bf16* kbase = rowbase + (int64_t)(H + kvh) * HD;
+  const bf16* vbase = rowbase + (int64_t)(H + Hkv + kvh) * HD;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, lr = lane & 15;
+  const int q0 = qblk * FWD_BQ;
+  const int qw = q0 + wave * QW;
+  const float sl2 = kLog2e / sqrtf((float)HD);
+
+  bf16x8_t qf[2][4], df[2][4];
+  float L2[2], Dq[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = qw + 16 * qb + lr;
+    const bool ok = qi < T;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 uq = ok ? *(const uint4*)(rowbase + (int64_t)qi * ldq + (int64_t)h * HD + 32 * ks + 8 * g)
+                    : make_uint4(0, 0, 0, 0);
+      uint4 ud = ok ? *(const uint4*)(dout + ((int64_t)b * T + qi) * ldo + (int64_t)h * HD + 32 * ks + 8 * g)
+                    : make_uint4(0, 0, 0, 0);
+      qf[qb][ks] = __builtin_bit_cast(bf16x8_t, uq);
+      df[qb][ks] = __builtin_bit_cast(bf16x8_t, ud);
+    }
+    const int64_t li = ((int64_t)b * H + h) * T + qi;
+    L2[qb] = ok ? lse[li] * kLog2e : INFINITY;
+    Dq[qb] = ok ? delta[li] : 0.f;
+  }
+  f32x4_t dq[8][2];
+#pragma unroll
+  for (int hb = 0; hb < 8; ++hb)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) dq[hb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  int klo, khi;
+  key_range(q0, min(q0 + FWD_BQ, T) - 1, W, klo, khi);
+  const int kt0 = klo / TR, kt1 = khi / TR;
+  TileRegs<256> kr, vr;
+  kr.load_patches(kbase, ldq, kt0 * TR, T);
+  vr.load_rows(vbase, ldq, kt0 * TR, T);
+  for (int kt = kt0; kt <= kt1; ++kt) {
+    const int k0 = kt * TR;
+    kr.store_patches_R(Ks);
+    kr.store_patches_T(Kt);
+    vr.store_rows(Vs);
+    __syncthreads();
+    if (kt < kt1) {
+      kr.load_patches(kbase, ldq, k0 + TR, T);
+      vr.load_rows(vbase, ldq, k0 + TR, T);
+    }
+    const bool any = (qw + QW - 1 >= k0) && (qw - (k0 + TR - 1) <= W) && qw < T;
+    const bool full = (qw >= k0 + TR - 1) && (qw + QW - 1 - k0 <= W);
+    if (any) {
+      f32x4_t s[4][2];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8_t kx = rfrag(Ks, 16 * kb + lr, ks, g);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma(kx, qf[qb][ks], s[kb][qb]);
+        }
+      // lane: key 16kb + 4g + r, query 16qb + lr
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        f32x4_t dp[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) dp[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8_t vx = rfrag(Vs, 16 * kb + lr, ks, g);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma(vx, df[qb][ks], dp[qb]);
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float p = exp2f(s[kb][qb][r] * sl2 - L2[qb]);
+            if (!full) {
+              const int d = qw + 16 * qb + lr - (k0 + 16 * kb + 4 * g + r);
+              if (d < 0 || d > W) p = 0.f;
+            }
+            s[kb][qb][r] = p * (dp[qb][r] - Dq[qb]);
+          }
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const bf16x8_t ps = pack8(s[2 * c][qb], s[2 * c + 1][qb]);
+#pragma unroll
+          for (int hb = 0; hb < 8; ++hb)
+            dq[hb][qb] = mfma(tfrag(Kt, 16 * hb + lr, c, g), ps, dq[hb][qb]);
+        }
+    }
+    __syncthreads();
+  }
+  const float scale = 1.0f / sqrtf((float)HD);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = qw + 16 * qb + lr;
+    if (qi >= T) continue;
+    bf16* row = dqkv + ((int64_t)b * T + qi) * ldq + (int64_t)h * HD;
+#pragma unroll
+    for (int hb = 0; hb < 8; ++hb) {
+      uint2 u;
+      u.x = pack2bf(dq[hb][qb][0] * scale, dq[hb][qb][1] * scale);
+      u.y = pack2bf(dq[hb][qb][2] * scale, dq[hb][qb][3] * scale);
+      *(uint2*)(row + 16 * hb + 4 * g) = u;
+    }
+  }
+}
+
+bool attn_mfma_bwd_supported(int T, int H, int Hkv, int hd) {
+  return attn_mfma_supported(T, H, Hkv, hd);
+}
 
 size_t attn_mfma_bwd_scratch_bytes(int, int, int, int) { return 0; }
 
-// The backward still runs on the generic kernels (see k_attn.hip).
-hipError_t attn_mfma_bwd(const void*, const void*, const float*, const void*, void*, float*,
-                         void*, int, int, int, int, int, int, hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const void* dout,
+                         void* dqkv, float* delta, void*, int B, int T, int H, int Hkv, int hd,
+                         int W, hipStream_t s) {
+  (void)hd;
+  const int64_t rows = (int64_t)B * T * H;
+  hipLaunchKernelGGL(k_attn_delta, dim3((unsigned)cdiv(rows * 16, 256)), dim3(256), 0, s,
+                     (const bf16*)o, (const bf16*)dout, delta, T, H, rows);
+  hipLaunchKernelGGL(k_attn_bwd_dkv, dim3((T + KV_BK - 1) / KV_BK, Hkv, B), dim3(NW * 64), 0, s,
+                     (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T,
+                     H, Hkv, W);
+  hipLaunchKernelGGL(k_attn_bwd_dq, dim3((T + FWD_BQ - 1) / FWD_BQ, H, B), dim3(NW * 64), 0, s,
+                     (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T,
+                     H, Hkv, W);
+  return hipGetLastError();
 }
 
 }  // namespace gk

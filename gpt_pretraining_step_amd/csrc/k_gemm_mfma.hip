@@ -39,6 +39,14 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 static constexpr int BK = 64;
 static constexpr int LDK = BK + 8;     // LDS row stride (elements), 144 bytes
 
+// LDS element offset of (row, k): the 8-element chunks of a row are XOR-
+// swizzled by (row / 16) % 8, which spreads the transposed staging writes
+// (lanes 8 rows apart) over all banks while the fragment reads (16
+// consecutive rows, one chunk) stay conflict-free.
+__device__ __forceinline__ int lds_off(int row, int k) {
+  return row * LDK + ((((k >> 3) ^ (row >> 4)) & 7) << 3) + (k & 7);
+}
+
 // low / high 16-bit halves of two words packed into one word
 __device__ __forceinline__ uint32_t lo_pair(uint32_t x, uint32_t y) {
   return __builtin_amdgcn_perm(y, x, 0x05040100u);
@@ -68,7 +76,7 @@ struct KRowStage {
     for (int i = 0; i < CH; ++i) {
       const int c = threadIdx.x + 256 * i;
       const int r = c >> 3, kc = c & 7;
-      *(uint4*)(s + r * LDK + kc * 8) = v[i];
+      *(uint4*)(s + lds_off(r, kc * 8)) = v[i];
     }
   }
 };
@@ -104,14 +112,14 @@ struct KColStage {
         lo.y = lo_pair(w[2][d], w[3][d]); hi.y = hi_pair(w[2][d], w[3][d]);
         lo.z = lo_pair(w[4][d], w[5][d]); hi.z = hi_pair(w[4][d], w[5][d]);
         lo.w = lo_pair(w[6][d], w[7][d]); hi.w = hi_pair(w[6][d], w[7][d]);
-        *(uint4*)(s + (cb * 8 + 2 * d) * LDK + kb * 8) = lo;
-        *(uint4*)(s + (cb * 8 + 2 * d + 1) * LDK + kb * 8) = hi;
+        *(uint4*)(s + lds_off(cb * 8 + 2 * d, kb * 8)) = lo;
+        *(uint4*)(s + lds_off(cb * 8 + 2 * d + 1, kb * 8)) = hi;
       } else {
         uint2 lo, hi;
         lo.x = lo_pair(w[0][d], w[1][d]); hi.x = hi_pair(w[0][d], w[1][d]);
         lo.y = lo_pair(w[2][d], w[3][d]); hi.y = hi_pair(w[2][d], w[3][d]);
-        *(uint2*)(s + (cb * 8 + 2 * d) * LDK + kb * 4) = lo;
-        *(uint2*)(s + (cb * 8 + 2 * d + 1) * LDK + kb * 4) = hi;
+        *(uint2*)(s + lds_off(cb * 8 + 2 * d, kb * 4)) = lo;
+        *(uint2*)(s + lds_off(cb * 8 + 2 * d + 1, kb * 4)) = hi;
       }
     }
   }
@@ -224,10 +232,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(int64_t M, int64_t N, int6
       bf16x8_t a[TMI], b[TNJ];
 #pragma unroll
       for (int i = 0; i < TMI; ++i)
-        a[i] = *(const bf16x8_t*)(As + (wm + 16 * i + lr) * LDK + kk + lk);
+        a[i] = *(const bf16x8_t*)(As + lds_off(wm + 16 * i + lr, kk + lk));
 #pragma unroll
       for (int j = 0; j < TNJ; ++j)
-        b[j] = *(const bf16x8_t*)(Bs + (wn + 16 * j + lr) * LDK + kk + lk);
+        b[j] = *(const bf16x8_t*)(Bs + lds_off(wn + 16 * j + lr, kk + lk));
 #pragma unroll
       for (int i = 0; i < TMI; ++i)
 #pragma unroll
