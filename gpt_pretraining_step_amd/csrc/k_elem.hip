@@ -229,12 +229,93 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const Tv* dy, const Tv* y, 
   }
 }
 
+// bf16 rows with D % 8 == 0 (and C % 8 == 0): 16-byte vectors, the row's dy
+// and y kept in registers between the reduction and the update.
+__device__ __forceinline__ void unpack8(const uint4& u, float* f) {
+  const uint32_t* w = (const uint32_t*)&u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = __uint_as_float(w[e] << 16);
+    f[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ uint4 pack8f(const float* f) {
+  uint4 u;
+  u.x = pack2bf(f[0], f[1]);
+  u.y = pack2bf(f[2], f[3]);
+  u.z = pack2bf(f[4], f[5]);
+  u.w = pack2bf(f[6], f[7]);
+  return u;
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd_v(const bf16* dy, const bf16* y, const float* r,
+                                                       const bf16* dres, bf16* dx, int64_t rows,
+                                                       int D, const float* vez, const bf16* wg,
+                                                       int Hkv, int C) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = blockIdx.x * (int64_t)(blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int nv = D >> 3;
+  const uint4* dyr = (const uint4*)(dy + row * D);
+  const uint4* yr = (const uint4*)(y + row * D);
+  const float* vz = vez ? vez + row * Hkv : nullptr;
+  float g[VPL][8], yv[VPL][8];
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int v = lane + 64 * k;
+    if (v < nv) {
+      unpack8(dyr[v], g[k]);
+      unpack8(yr[v], yv[k]);
+      if (vz && 8 * v < C) {
+        for (int kv = 0; kv < Hkv; ++kv) {
+          float wgf[8];
+          unpack8(*(const uint4*)(wg + (int64_t)kv * C + 8 * v), wgf);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) g[k][e] += vz[kv] * wgf[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += g[k][e] * yv[k][e];
+    }
+  }
+  const float m = wave_sum(acc) / (float)D;
+  const float rr = r[row];
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int v = lane + 64 * k;
+    if (v < nv) {
+      float o[8];
+      if (dres) unpack8(((const uint4*)(dres + row * D))[v], o);
+      else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += rr * (g[k][e] - yv[k][e] * m);
+      ((uint4*)(dx + row * D))[v] = pack8f(o);
+    }
+  }
+}
+
 hipError_t rmsnorm_bwd(const void* dy, const void* y, const float* r,
                        const void* dres, void* dx, int64_t rows, int D,
                        const float* vez, const void* wg, int Hkv, int C,
                        DType dt, hipStream_t s) {
   dim3 grid((unsigned)cdiv(rows, 4)), block(256);
-  if (dt == BF16)
+  const bool vec = dt == BF16 && D % 8 == 0 && D <= 64 * 8 * 4 && (!vez || C % 8 == 0);
+  if (vec) {
+    const int vpl = (int)cdiv(D / 8, 64);
+#define RMSB(V)                                                                              \
+  hipLaunchKernelGGL(k_rmsnorm_bwd_v<V>, grid, block, 0, s, (const bf16*)dy, (const bf16*)y, r, \
+                     (const bf16*)dres, (bf16*)dx, rows, D, vez, (const bf16*)wg, Hkv, C)
+    if (vpl == 1) RMSB(1);
+    else if (vpl == 2) RMSB(2);
+    else if (vpl == 3) RMSB(3);
+    else RMSB(4);
+#undef RMSB
+  } else if (dt == BF16)
     hipLaunchKernelGGL(k_rmsnorm_bwd<bf16>, grid, block, 0, s, (const bf16*)dy, (const bf16*)y, r,
                        (const bf16*)dres, (bf16*)dx, rows, D, vez, (const bf16*)wg, Hkv, C);
   else
@@ -306,9 +387,110 @@ __global__ __launch_bounds__(256) void k_rope_qknorm_bwd(Tv* dqkv, const Tv* qkv
   }
 }
 
+// bf16, hd % 8 == 0: each thread rotates 4 consecutive pairs (8-byte loads of
+// x[4j..4j+3] and x[hd/2 + 4j..]); hd/8 threads per head form the segment.
+__device__ __forceinline__ void unpack4(uint2 u, float* f) {
+  f[0] = __uint_as_float(u.x << 16); f[1] = __uint_as_float(u.x & 0xFFFF0000u);
+  f[2] = __uint_as_float(u.y << 16); f[3] = __uint_as_float(u.y & 0xFFFF0000u);
+}
+__device__ __forceinline__ uint2 pack4f(const float* f) {
+  uint2 u;
+  u.x = pack2bf(f[0], f[1]);
+  u.y = pack2bf(f[2], f[3]);
+  return u;
+}
+
+__global__ __launch_bounds__(256) void k_rope_qknorm_fwd_v(bf16* qkv, float* rq, float* rk,
+                                                           const float2* cs, int64_t N, int T,
+                                                           int H, int Hkv, int hd, float eps) {
+  const int half = hd >> 1, lph = hd >> 3, heads = H + Hkv;
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const bool valid = idx < N * heads * lph;
+  const int64_t id = valid ? idx : 0;
+  const int j4 = (int)(id % lph);
+  const int64_t rest = id / lph;
+  const int hh = (int)(rest % heads);
+  const int64_t n = rest / heads;
+  const int t = (int)(n % T);
+  bf16* p = qkv + n * (int64_t)((H + 2 * Hkv) * hd) + (int64_t)hh * hd;
+  float x1[4], x2[4];
+  unpack4(*(const uint2*)(p + 4 * j4), x1);
+  unpack4(*(const uint2*)(p + half + 4 * j4), x2);
+  const float4* c4 = (const float4*)(cs + (int64_t)t * half + 4 * j4);
+  const float4 ca = c4[0], cb = c4[1];                // (cos, sin) x 4
+  const float c[4] = {ca.x, ca.z, cb.x, cb.z}, sn[4] = {ca.y, ca.w, cb.y, cb.w};
+  float y1[4], y2[4], ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y1[e] = x1[e] * c[e] - x2[e] * sn[e];
+    y2[e] = x1[e] * sn[e] + x2[e] * c[e];
+    ss += y1[e] * y1[e] + y2[e] * y2[e];
+  }
+  ss = seg_sum(ss, lph);
+  const float rr = 1.0f / sqrtf(ss / (float)hd + eps);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { y1[e] *= rr; y2[e] *= rr; }
+  if (valid) {
+    *(uint2*)(p + 4 * j4) = pack4f(y1);
+    *(uint2*)(p + half + 4 * j4) = pack4f(y2);
+    if (j4 == 0) {
+      if (hh < H) rq[n * H + hh] = rr;
+      else rk[n * Hkv + (hh - H)] = rr;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_rope_qknorm_bwd_v(bf16* dqkv, const bf16* qkv,
+                                                           const float* rq, const float* rk,
+                                                           const float2* cs, int64_t N, int T,
+                                                           int H, int Hkv, int hd) {
+  const int half = hd >> 1, lph = hd >> 3, heads = H + Hkv;
+  const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const bool valid = idx < N * heads * lph;
+  const int64_t id = valid ? idx : 0;
+  const int j4 = (int)(id % lph);
+  const int64_t rest = id / lph;
+  const int hh = (int)(rest % heads);
+  const int64_t n = rest / heads;
+  const int t = (int)(n % T);
+  const int64_t off = n * (int64_t)((H + 2 * Hkv) * hd) + (int64_t)hh * hd;
+  bf16* dp = dqkv + off;
+  const bf16* yp = qkv + off;
+  float g1[4], g2[4], y1[4], y2[4];
+  unpack4(*(const uint2*)(dp + 4 * j4), g1);
+  unpack4(*(const uint2*)(dp + half + 4 * j4), g2);
+  unpack4(*(const uint2*)(yp + 4 * j4), y1);
+  unpack4(*(const uint2*)(yp + half + 4 * j4), y2);
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc += g1[e] * y1[e] + g2[e] * y2[e];
+  const float m = seg_sum(acc, lph) / (float)hd;
+  const float rr = hh < H ? rq[n * H + hh] : rk[n * Hkv + (hh - H)];
+  const float4* c4 = (const float4*)(cs + (int64_t)t * half + 4 * j4);
+  const float4 ca = c4[0], cb = c4[1];
+  const float c[4] = {ca.x, ca.z, cb.x, cb.z}, sn[4] = {ca.y, ca.w, cb.y, cb.w};
+  float o1[4], o2[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {           // norm backward, then the inverse rotation
+    const float a1 = rr * (g1[e] - y1[e] * m), a2 = rr * (g2[e] - y2[e] * m);
+    o1[e] = a1 * c[e] + a2 * sn[e];
+    o2[e] = -a1 * sn[e] + a2 * c[e];
+  }
+  if (valid) {
+    *(uint2*)(dp + 4 * j4) = pack4f(o1);
+    *(uint2*)(dp + half + 4 * j4) = pack4f(o2);
+  }
+}
+
 hipError_t rope_qknorm_fwd(void* qkv, float* rq, float* rk, const float* cs, int B, int T,
                            int H, int Hkv, int hd, float eps, DType dt, hipStream_t s) {
   int64_t N = (int64_t)B * T;
+  if (dt == BF16 && hd % 8 == 0) {
+    const int64_t total = N * (H + Hkv) * (hd / 8);
+    hipLaunchKernelGGL(k_rope_qknorm_fwd_v, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s,
+                       (bf16*)qkv, rq, rk, (const float2*)cs, N, T, H, Hkv, hd, eps);
+    return hipGetLastError();
+  }
   int64_t total = N * (H + Hkv) * (hd / 2);
   dim3 grid((unsigned)cdiv(total, 256)), block(256);
   if (dt == BF16)
@@ -324,6 +506,12 @@ hipError_t rope_qknorm_bwd(void* dqkv, const void* qkv, const float* rq, const f
                            const float* cs, int B, int T, int H, int Hkv, int hd, DType dt,
                            hipStream_t s) {
   int64_t N = (int64_t)B * T;
+  if (dt == BF16 && hd % 8 == 0) {
+    const int64_t total = N * (H + Hkv) * (hd / 8);
+    hipLaunchKernelGGL(k_rope_qknorm_bwd_v, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s,
+                       (bf16*)dqkv, (const bf16*)qkv, rq, rk, (const float2*)cs, N, T, H, Hkv, hd);
+    return hipGetLastError();
+  }
   int64_t total = N * (H + Hkv) * (hd / 2);
   dim3 grid((unsigned)cdiv(total, 256)), block(256);
   if (dt == BF16)
@@ -496,10 +684,84 @@ __global__ __launch_bounds__(256) void k_ce(const float* z, int64_t rows, int V,
   }
 }
 
+// Single pass over a logit row: 512 threads hold the row in registers (NV4
+// float4 each, V = 2048 NV4), so the logits are read from HBM once; max and
+// sum are exact two-step block reductions.
+template <int NV4>
+__global__ __launch_bounds__(512) void k_ce_reg(const float* z, int V, const int32_t* tok,
+                                                int tgtT, int direct, float* ell, float* lse_out,
+                                                bf16* dz, float scale, int64_t row0) {
+  __shared__ float red[8];
+  const int64_t row = blockIdx.x;
+  const float4* zr = (const float4*)(z + row * (int64_t)V);
+  const int64_t n = row0 + row;
+  const int tgt = direct ? tok[n] : tok[(n / tgtT) * (tgtT + 1) + n % tgtT + 1];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float4 v[NV4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NV4; ++k) {
+    v[k] = zr[k * 512 + threadIdx.x];
+    m = fmaxf(m, fmaxf(fmaxf(v[k].x, v[k].y), fmaxf(v[k].z, v[k].w)));
+  }
+  m = wave_max(m);
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) M = fmaxf(M, red[k]);
+  __syncthreads();
+  float sacc = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV4; ++k)
+    sacc += (expf(v[k].x - M) + expf(v[k].y - M)) + (expf(v[k].z - M) + expf(v[k].w - M));
+  sacc = wave_sum(sacc);
+  if (lane == 0) red[w] = sacc;
+  __syncthreads();
+  float S = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) S += red[k];
+  const float L = M + logf(S);
+  if (threadIdx.x == 0) {
+    ell[row] = L - z[row * (int64_t)V + tgt];
+    lse_out[row] = L;
+  }
+  if (dz) {
+    uint2* dr = (uint2*)(dz + row * (int64_t)V);
+#pragma unroll
+    for (int k = 0; k < NV4; ++k) {
+      const int c = k * 512 + threadIdx.x;
+      float p[4] = {expf(v[k].x - L), expf(v[k].y - L), expf(v[k].z - L), expf(v[k].w - L)};
+      if ((tgt >> 2) == c) p[tgt & 3] -= 1.0f;
+      uint2 u;
+      u.x = pack2bf(p[0] * scale, p[1] * scale);
+      u.y = pack2bf(p[2] * scale, p[3] * scale);
+      dr[c] = u;
+    }
+  }
+}
+
 hipError_t ce_rows(const float* z, int64_t rows, int V, const int32_t* tok, int tgt_T,
                    int tgt_direct, float* ell, float* lse, void* dz, float grad_scale,
                    DType dt, hipStream_t s, int64_t row0) {
   if (rows <= 0) return hipSuccess;
+  if (dt == BF16 && V % 2048 == 0 && V <= 32768 && ((uintptr_t)z & 15) == 0) {
+    const int nv4 = V / 2048;
+#define CEREG(K)                                                                             \
+  hipLaunchKernelGGL(k_ce_reg<K>, dim3((unsigned)rows), dim3(512), 0, s, z, V, tok, tgt_T,      \
+                     tgt_direct, ell, lse, (bf16*)dz, grad_scale, row0)
+    switch (nv4) {
+      case 1: CEREG(1); break;
+      case 2: CEREG(2); break;
+      case 4: CEREG(4); break;
+      case 8: CEREG(8); break;
+      case 16: CEREG(16); break;
+      default: goto generic;
+    }
+#undef CEREG
+    return hipGetLastError();
+  }
+generic:
   if (dt == BF16)
     hipLaunchKernelGGL(k_ce<bf16>, dim3((unsigned)rows), dim3(256), 0, s, z, rows, V, tok, tgt_T,
                        tgt_direct, ell, lse, (bf16*)dz, grad_scale, row0);

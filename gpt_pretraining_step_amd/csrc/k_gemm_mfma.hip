@@ -11,7 +11,8 @@
 // NN and TN) are transposed on the way in: each thread loads a KB x 8 patch
 // (KB rows of 16 bytes), transposes it in registers with byte permutes and
 // writes one K-contiguous run per column.  No separate transpose kernel and
-// no extra HBM traffic.
+// no extra HBM traffic.  The patch-to-lane assignment keeps those stores free
+// of LDS bank conflicts.
 //
 // The MFMA is issued with B as the first source, so each lane ends up holding
 // four consecutive columns of one output row: the epilogue writes 8-byte
@@ -39,12 +40,21 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 static constexpr int BK = 64;
 static constexpr int LDK = BK + 8;     // LDS row stride (elements), 144 bytes
 
-// LDS element offset of (row, k): the 8-element chunks of a row are XOR-
-// swizzled by (row / 16) % 8, which spreads the transposed staging writes
-// (lanes 8 rows apart) over all banks while the fragment reads (16
-// consecutive rows, one chunk) stay conflict-free.
-__device__ __forceinline__ int lds_off(int row, int k) {
-  return row * LDK + ((((k >> 3) ^ (row >> 4)) & 7) << 3) + (k & 7);
+// LDS element offset of (row, k).  With the 144-byte row stride, fragment
+// reads (16 consecutive rows, one 16-byte chunk) hit 16 distinct bank groups,
+// and the transposing stores below are arranged so that 16 lanes fill one
+// 128-byte row segment; the address stays affine in the row, so fragment
+// reads use one base register plus immediate offsets.
+__device__ __forceinline__ int lds_off(int row, int k) { return row * LDK + k; }
+
+// Layout used when both operands are transposed on the way in (TN): the
+// column-fastest lane order there gives fully coalesced 256-byte global
+// reads, and an XOR swizzle of the 16-byte chunks by (row / 16) % 8 keeps
+// its stores (lanes 8 rows apart) free of bank conflicts.
+template <bool XS>
+__device__ __forceinline__ int lds_at(int row, int k) {
+  if constexpr (XS) return row * LDK + ((((k >> 3) ^ (row >> 4)) & 7) << 3) + (k & 7);
+  else return lds_off(row, k);
 }
 
 // low / high 16-bit halves of two words packed into one word
@@ -57,50 +67,62 @@ __device__ __forceinline__ uint32_t hi_pair(uint32_t x, uint32_t y) {
 
 // ---------------------------------------------------------------- staging
 // K-contiguous operand: global [rows][ld], tile rows r0.., k0..k0+63.
-template <int R>
+template <int R, int NT = 256, bool XS = false>
 struct KRowStage {
-  static constexpr int CH = R * 8 / 256;    // 16-byte chunks per thread
+  static constexpr int CH = R * 8 / NT;     // 16-byte chunks per thread
   uint4 v[CH];
   __device__ __forceinline__ void load(const bf16* g, int64_t ld, int64_t r0, int64_t rows,
                                        int64_t k0, int64_t K) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + NT * i;
       const int r = c >> 3, kc = c & 7;
       const int64_t gr = r0 + r, gk = k0 + kc * 8;
-      v[i] = (gr < rows && gk < K) ? *(const uint4*)(g + gr * ld + gk) : make_uint4(0, 0, 0, 0);
+      // clamped (always valid) address, then zero the lanes out of range:
+      // no branch around the load
+      const bool ok = gr < rows && gk < K;
+      const uint4 x = *(const uint4*)(g + (ok ? gr : 0) * ld + (ok ? gk : 0));
+      v[i] = ok ? x : make_uint4(0, 0, 0, 0);
     }
   }
   __device__ __forceinline__ void store(bf16* s) const {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + NT * i;
       const int r = c >> 3, kc = c & 7;
-      *(uint4*)(s + lds_off(r, kc * 8)) = v[i];
+      *(uint4*)(s + lds_at<XS>(r, kc * 8)) = v[i];
     }
   }
 };
 
 // MN-contiguous operand: global [K][ld] (row index = k), tile columns r0..,
-// k0..k0+63.  Each thread owns a KB x 8 patch; R/8 patches per KB rows.
-template <int R>
+// k0..k0+63.  Each thread owns a KB x 8 patch.  Consecutive threads take
+// consecutive k-blocks of the same 8 columns, so a load instruction reads
+// 128-byte row segments and a store instruction fills 128-byte runs of one
+// LDS row.
+template <int R, int NT = 256, bool XS = false>
 struct KColStage {
   static constexpr int NCB = R / 8;                 // 8-wide column blocks
-  static constexpr int KB = 64 * NCB / 256;         // k rows per patch (8 or 4)
+  static constexpr int KB = 64 * NCB / NT;          // k rows per patch (8 or 4)
+  static constexpr int NKB = 64 / KB;               // k-blocks per K-slice
   static_assert(KB == 8 || KB == 4, "tile width");
   uint4 v[KB];
   __device__ __forceinline__ void load(const bf16* g, int64_t ld, int64_t r0, int64_t rows,
                                        int64_t k0, int64_t K) {
-    const int cb = threadIdx.x % NCB, kb = threadIdx.x / NCB;
+    const int kb = XS ? threadIdx.x / NCB : threadIdx.x % NKB;
+    const int cb = XS ? threadIdx.x % NCB : threadIdx.x / NKB;
     const int64_t col = r0 + cb * 8;
 #pragma unroll
     for (int r = 0; r < KB; ++r) {
       const int64_t gk = k0 + kb * KB + r;
-      v[r] = (gk < K && col < rows) ? *(const uint4*)(g + gk * ld + col) : make_uint4(0, 0, 0, 0);
+      const bool ok = gk < K && col < rows;
+      const uint4 x = *(const uint4*)(g + (ok ? gk : 0) * ld + (ok ? col : 0));
+      v[r] = ok ? x : make_uint4(0, 0, 0, 0);
     }
   }
   __device__ __forceinline__ void store(bf16* s) const {
-    const int cb = threadIdx.x % NCB, kb = threadIdx.x / NCB;
+    const int kb = XS ? threadIdx.x / NCB : threadIdx.x % NKB;
+    const int cb = XS ? threadIdx.x % NCB : threadIdx.x / NKB;
     const uint32_t* w[KB];
 #pragma unroll
     for (int r = 0; r < KB; ++r) w[r] = (const uint32_t*)&v[r];
@@ -112,21 +134,21 @@ struct KColStage {
         lo.y = lo_pair(w[2][d], w[3][d]); hi.y = hi_pair(w[2][d], w[3][d]);
         lo.z = lo_pair(w[4][d], w[5][d]); hi.z = hi_pair(w[4][d], w[5][d]);
         lo.w = lo_pair(w[6][d], w[7][d]); hi.w = hi_pair(w[6][d], w[7][d]);
-        *(uint4*)(s + lds_off(cb * 8 + 2 * d, kb * 8)) = lo;
-        *(uint4*)(s + lds_off(cb * 8 + 2 * d + 1, kb * 8)) = hi;
+        *(uint4*)(s + lds_at<XS>(cb * 8 + 2 * d, kb * 8)) = lo;
+        *(uint4*)(s + lds_at<XS>(cb * 8 + 2 * d + 1, kb * 8)) = hi;
       } else {
         uint2 lo, hi;
         lo.x = lo_pair(w[0][d], w[1][d]); hi.x = hi_pair(w[0][d], w[1][d]);
         lo.y = lo_pair(w[2][d], w[3][d]); hi.y = hi_pair(w[2][d], w[3][d]);
-        *(uint2*)(s + lds_off(cb * 8 + 2 * d, kb * 4)) = lo;
-        *(uint2*)(s + lds_off(cb * 8 + 2 * d + 1, kb * 4)) = hi;
+        *(uint2*)(s + lds_at<XS>(cb * 8 + 2 * d, kb * 4)) = lo;
+        *(uint2*)(s + lds_at<XS>(cb * 8 + 2 * d + 1, kb * 4)) = hi;
       }
     }
   }
 };
 
-template <bool TRANS, int R>
-using Stage = typename std::conditional<TRANS, KColStage<R>, KRowStage<R>>::type;
+template <bool TRANS, int R, int NT = 256, bool XS = false>
+using Stage = typename std::conditional<TRANS, KColStage<R, NT, XS>, KRowStage<R, NT, XS>>::type;
 
 // ------------------------------------------------------------ epilogue x4
 // Four consecutive columns n..n+3 of row m (n % 4 == 0, N % 4 == 0).
@@ -213,8 +235,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(int64_t M, int64_t N, int6
 #pragma unroll
     for (int j = 0; j < TNJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  Stage<TA, BM> sa;
-  Stage<TB, BN> sb;
+  constexpr bool XS = TA && TB;
+  Stage<TA, BM, 256, XS> sa;
+  Stage<TB, BN, 256, XS> sb;
   sa.load(A, lda, m0, M, kbeg, kend);
   sb.load(B, ldb, n0, N, kbeg, kend);
   sa.store(As);
@@ -232,10 +255,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(int64_t M, int64_t N, int6
       bf16x8_t a[TMI], b[TNJ];
 #pragma unroll
       for (int i = 0; i < TMI; ++i)
-        a[i] = *(const bf16x8_t*)(As + lds_off(wm + 16 * i + lr, kk + lk));
+        a[i] = *(const bf16x8_t*)(As + lds_at<XS>(wm + 16 * i + lr, kk + lk));
 #pragma unroll
       for (int j = 0; j < TNJ; ++j)
-        b[j] = *(const bf16x8_t*)(Bs + lds_off(wn + 16 * j + lr, kk + lk));
+        b[j] = *(const bf16x8_t*)(Bs + lds_at<XS>(wn + 16 * j + lr, kk + lk));
 #pragma unroll
       for (int i = 0; i < TMI; ++i)
 #pragma unroll
@@ -268,6 +291,247 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(int64_t M, int64_t N, int6
     }
   }
 }
+
+// Large-tile variant: 256 x 256 block tile, 8 waves (2 x 4, each 128 x 64),
+// two LDS stages.  The next K-slice is fetched into registers while the
+// current stage is consumed and written into the other stage afterwards, so
+// one barrier per K-slice suffices (the barrier that publishes stage s+1 also
+// retires every read of stage s before it is overwritten).  One block per CU
+// (144 KB of LDS), two waves per SIMD.
+template <bool TA, bool TB, int EPI>
+__global__ __launch_bounds__(512, 1) void k_gemm_mfma_db(int64_t M, int64_t N, int64_t K,
+                                                         const bf16* __restrict__ A, int64_t lda,
+                                                         const bf16* __restrict__ B, int64_t ldb,
+                                                         void* C, int64_t ldc, void* aux,
+                                                         TileMap tm, float* partial) {
+  constexpr int BM = 256, BN = 256, NT = 512;
+  constexpr int WM = 128, WN = 64;
+  constexpr int TMI = WM / 16, TNJ = WN / 16;
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * (BM + BN) * LDK];
+  bf16* As0 = lds;
+  bf16* Bs0 = lds + BM * LDK;
+  bf16* As1 = lds + (BM + BN) * LDK;
+  bf16* Bs1 = lds + (2 * BM + BN) * LDK;
+
+  const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
+  const int per_xcd = (nb + 7) / 8;
+  const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (logical >= nb) return;
+  const int ntile = tm.tiles_m * tm.tiles_n;
+  const int split = logical / ntile;
+  const int t = logical % ntile;
+  constexpr int GM = 8;
+  const int group = t / (GM * tm.tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tm.tiles_m - first_m, GM);
+  const int tile_m = first_m + (t % (GM * tm.tiles_n)) % gsize;
+  const int tile_n = (t % (GM * tm.tiles_n)) / gsize;
+  const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
+  const int64_t kbeg = (int64_t)split * tm.k_per_split;
+  const int64_t kend = min(K, kbeg + tm.k_per_split);
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = (wave >> 2) * WM, wn = (wave & 3) * WN;
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
+
+  f32x4_t acc[TMI][TNJ];
+#pragma unroll
+  for (int i = 0; i < TMI; ++i)
+#pragma unroll
+    for (int j = 0; j < TNJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  Stage<TA, BM, NT> sa;
+  Stage<TB, BN, NT> sb;
+  sa.load(A, lda, m0, M, kbeg, kend);
+  sb.load(B, ldb, n0, N, kbeg, kend);
+  sa.store(As0);
+  sb.store(Bs0);
+  __syncthreads();
+
+  int stage = 0;
+  for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
+    const bool more = k0 + BK < kend;
+    if (more) {
+      sa.load(A, lda, m0, M, k0 + BK, kend);
+      sb.load(B, ldb, n0, N, k0 + BK, kend);
+    }
+    const bf16* As = stage ? As1 : As0;
+    const bf16* Bs = stage ? Bs1 : Bs0;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      bf16x8_t a[TMI], b[TNJ];
+#pragma unroll
+      for (int i = 0; i < TMI; ++i)
+        a[i] = *(const bf16x8_t*)(As + lds_off(wm + 16 * i + lr, kk + lk));
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j)
+        b[j] = *(const bf16x8_t*)(Bs + lds_off(wn + 16 * j + lr, kk + lk));
+#pragma unroll
+      for (int i = 0; i < TMI; ++i)
+#pragma unroll
+        for (int j = 0; j < TNJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      sa.store(stage ? As0 : As1);
+      sb.store(stage ? Bs0 : Bs1);
+    }
+    __syncthreads();
+    stage ^= 1;
+  }
+
+  const int cq = (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < TMI; ++i) {
+    const int64_t m = m0 + wm + 16 * i + lr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < TNJ; ++j) {
+      const int64_t n = n0 + wn + 16 * j + cq;
+      if (n >= N) continue;
+      if (partial) {
+        *(f32x4_t*)(partial + ((int64_t)split * M + m) * N + n) = acc[i][j];
+      } else {
+        epi4<EPI>(C, aux, ldc, m, n, acc[i][j]);
+      }
+    }
+  }
+}
+
+// Big-register-tile variant: 256 x 256 block tile, 4 waves (2 x 2) each
+// owning a 128 x 128 sub-tile (64 accumulator quads, held in AGPRs), one
+// wave per SIMD.  Two LDS stages; inside a K-slice the fragments of the
+// second 32-deep half are read while the MFMAs of the first half run, so the
+// matrix pipe is fed from a single wave.
+template <bool TA, bool TB, int EPI>
+__global__ __launch_bounds__(256, 1) void k_gemm_mfma_big(int64_t M, int64_t N, int64_t K,
+                                                          const bf16* __restrict__ A, int64_t lda,
+                                                          const bf16* __restrict__ B, int64_t ldb,
+                                                          void* C, int64_t ldc, void* aux,
+                                                          TileMap tm, float* partial) {
+  constexpr int BM = 256, BN = 256, NT = 256;
+  constexpr int WM = 128, WN = 128;
+  constexpr int TMI = WM / 16, TNJ = WN / 16;
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * (BM + BN) * LDK];
+  bf16* As0 = lds;
+  bf16* Bs0 = lds + BM * LDK;
+  bf16* As1 = lds + (BM + BN) * LDK;
+  bf16* Bs1 = lds + (2 * BM + BN) * LDK;
+
+  const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
+  const int per_xcd = (nb + 7) / 8;
+  const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (logical >= nb) return;
+  const int ntile = tm.tiles_m * tm.tiles_n;
+  const int split = logical / ntile;
+  const int t = logical % ntile;
+  constexpr int GM = 8;
+  const int group = t / (GM * tm.tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tm.tiles_m - first_m, GM);
+  const int tile_m = first_m + (t % (GM * tm.tiles_n)) % gsize;
+  const int tile_n = (t % (GM * tm.tiles_n)) / gsize;
+  const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
+  const int64_t kbeg = (int64_t)split * tm.k_per_split;
+  const int64_t kend = min(K, kbeg + tm.k_per_split);
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
+
+  f32x4_t acc[TMI][TNJ];
+#pragma unroll
+  for (int i = 0; i < TMI; ++i)
+#pragma unroll
+    for (int j = 0; j < TNJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  Stage<TA, BM, NT> sa;
+  Stage<TB, BN, NT> sb;
+  sa.load(A, lda, m0, M, kbeg, kend);
+  sb.load(B, ldb, n0, N, kbeg, kend);
+  sa.store(As0);
+  sb.store(Bs0);
+  __syncthreads();
+
+  // Software pipeline (per K-slice, stage s current):
+  //   global loads of the next slice | fragments of half 1 (stage s)
+  //   MFMAs of half 0
+  //   store the next slice into stage 1-s | barrier | fragments of half 0
+  //   of stage 1-s
+  //   MFMAs of half 1
+  // so each 64-MFMA block runs while LDS reads for the next block are in
+  // flight.  sched_barrier(0) keeps the compiler from sinking the reads next
+  // to their uses.
+  bf16x8_t a0[TMI], b0[TNJ], a1[TMI], b1[TNJ];
+#pragma unroll
+  for (int i = 0; i < TMI; ++i) a0[i] = *(const bf16x8_t*)(As0 + lds_off(wm + 16 * i + lr, lk));
+#pragma unroll
+  for (int j = 0; j < TNJ; ++j) b0[j] = *(const bf16x8_t*)(Bs0 + lds_off(wn + 16 * j + lr, lk));
+  int stage = 0;
+  for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
+    const bool more = k0 + BK < kend;
+    if (more) {
+      sa.load(A, lda, m0, M, k0 + BK, kend);
+      sb.load(B, ldb, n0, N, k0 + BK, kend);
+    }
+    const bf16* As = stage ? As1 : As0;
+    const bf16* Bs = stage ? Bs1 : Bs0;
+#pragma unroll
+    for (int i = 0; i < TMI; ++i)
+      a1[i] = *(const bf16x8_t*)(As + lds_off(wm + 16 * i + lr, 32 + lk));
+#pragma unroll
+    for (int j = 0; j < TNJ; ++j)
+      b1[j] = *(const bf16x8_t*)(Bs + lds_off(wn + 16 * j + lr, 32 + lk));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TMI; ++i)
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[j], a0[i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
+      sa.store(stage ? As0 : As1);
+      sb.store(stage ? Bs0 : Bs1);
+    }
+    __syncthreads();
+    if (more) {
+      const bf16* An = stage ? As0 : As1;
+      const bf16* Bn = stage ? Bs0 : Bs1;
+#pragma unroll
+      for (int i = 0; i < TMI; ++i) a0[i] = *(const bf16x8_t*)(An + lds_off(wm + 16 * i + lr, lk));
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j) b0[j] = *(const bf16x8_t*)(Bn + lds_off(wn + 16 * j + lr, lk));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < TMI; ++i)
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[j], a1[i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    stage ^= 1;
+  }
+
+  const int cq = (lane >> 4) * 4;
+#pragma unroll
+  for (int i = 0; i < TMI; ++i) {
+    const int64_t m = m0 + wm + 16 * i + lr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < TNJ; ++j) {
+      const int64_t n = n0 + wn + 16 * j + cq;
+      if (n >= N) continue;
+      if (partial) {
+        *(f32x4_t*)(partial + ((int64_t)split * M + m) * N + n) = acc[i][j];
+      } else {
+        epi4<EPI>(C, aux, ldc, m, n, acc[i][j]);
+      }
+    }
+  }
+}
+
+// which 256x256 kernel serves the large products
+static constexpr bool kBigRegisterTile = false;
 
 // out[m, n] (=/+=) sum_s partial[s, m, n], fixed order over s
 __global__ void k_splitk_reduce(const float* __restrict__ partial, int splits, int64_t M,
@@ -327,12 +591,19 @@ static void launch_op(const GemmDesc& g, const TileMap& tm, float* partial, hipS
 // (SIZE_MAX: as the shape asks).
 static TileMap plan(int64_t M, int64_t N, int64_t K, bool f32out, size_t scratch_bytes, int* bm) {
   const int kCU = 256;
-  // the large tile unless it leaves the chip badly under-filled
+  // 256x256 (one block per CU) when that still gives two full waves of
+  // blocks; else 256x128 (two blocks per CU) unless that under-fills the chip
   int BM = 256, BN = 128;
   int64_t tiles = cdiv(M, 256) * cdiv(N, 128);
-  if (tiles < 2 * kCU) { BM = 128; BN = 128; tiles = cdiv(M, 128) * cdiv(N, 128); }
+  if (cdiv(M, 256) * cdiv(N, 256) >= 2 * kCU) {
+    BM = 512;            // code for the 256x256 kernel
+    BN = 256;
+    tiles = cdiv(M, 256) * cdiv(N, 256);
+  } else if (tiles < 2 * kCU) {
+    BM = 128; BN = 128; tiles = cdiv(M, 128) * cdiv(N, 128);
+  }
   TileMap tm;
-  tm.tiles_m = (int)cdiv(M, BM);
+  tm.tiles_m = (int)cdiv(M, BM == 512 ? 256 : BM);
   tm.tiles_n = (int)cdiv(N, BN);
   tm.splits = 1;
   tm.k_per_split = cdiv(K, BK) * BK;
@@ -353,6 +624,38 @@ static TileMap plan(int64_t M, int64_t N, int64_t K, bool f32out, size_t scratch
   return tm;
 }
 
+template <bool TA, bool TB, int EPI>
+static void launch_db_t(const GemmDesc& g, const TileMap& tm, float* partial, hipStream_t s) {
+  const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
+  const int grid = ((nb + 7) / 8) * 8;
+  if (kBigRegisterTile)
+    hipLaunchKernelGGL((k_gemm_mfma_big<TA, TB, EPI>), dim3(grid), dim3(256), 0, s, g.M, g.N,
+                       g.K, (const bf16*)g.A, g.lda, (const bf16*)g.B, g.ldb, g.C, g.ldc, g.aux,
+                       tm, partial);
+  else
+    hipLaunchKernelGGL((k_gemm_mfma_db<TA, TB, EPI>), dim3(grid), dim3(512), 0, s, g.M, g.N,
+                       g.K, (const bf16*)g.A, g.lda, (const bf16*)g.B, g.ldb, g.C, g.ldc, g.aux,
+                       tm, partial);
+}
+
+template <bool TA, bool TB>
+static void launch_db_e(const GemmDesc& g, const TileMap& tm, float* partial, hipStream_t s) {
+  switch (g.epi) {
+    case E_STORE:   launch_db_t<TA, TB, E_STORE>(g, tm, partial, s); break;
+    case E_RESADD:  launch_db_t<TA, TB, E_RESADD>(g, tm, partial, s); break;
+    case E_RELU2:   launch_db_t<TA, TB, E_RELU2>(g, tm, partial, s); break;
+    case E_DRELU2:  launch_db_t<TA, TB, E_DRELU2>(g, tm, partial, s); break;
+    case E_F32:     launch_db_t<TA, TB, E_F32>(g, tm, partial, s); break;
+    default:        launch_db_t<TA, TB, E_F32_ACC>(g, tm, partial, s); break;
+  }
+}
+
+static void launch_db(const GemmDesc& g, const TileMap& tm, float* partial, hipStream_t s) {
+  if (g.op == OP_NT) launch_db_e<false, false>(g, tm, partial, s);
+  else if (g.op == OP_NN) launch_db_e<false, true>(g, tm, partial, s);
+  else launch_db_e<true, true>(g, tm, partial, s);
+}
+
 size_t mfma_splitk_bytes(int64_t M, int64_t N, int64_t K) {
   int bm;
   TileMap tm = plan(M, N, K, true, SIZE_MAX, &bm);
@@ -364,7 +667,8 @@ hipError_t mfma_gemm(const GemmDesc& g, hipStream_t s) {
   int BM;
   TileMap tm = plan(g.M, g.N, g.K, f32out, g.scratch ? g.scratch_bytes : 0, &BM);
   float* partial = tm.splits > 1 ? (float*)g.scratch : nullptr;
-  if (BM == 256) launch_op<256, 128>(g, tm, partial, s);
+  if (BM == 512) launch_db(g, tm, partial, s);
+  else if (BM == 256) launch_op<256, 128>(g, tm, partial, s);
   else launch_op<128, 128>(g, tm, partial, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !partial) return e;

@@ -86,6 +86,26 @@ def test_gemm_store_and_f32(dt, op, shape):
         assert rel_err(to_np(S0), ref) < 1e-5
 
 
+@pytest.mark.parametrize("op", [G.GEMM_NT, G.GEMM_NN, G.GEMM_TN])
+@pytest.mark.parametrize("M,N,K", [(4096, 8192, 128), (4136, 8192, 192)])
+def test_gemm_large_tiles(op, M, N, K):
+    """Products big enough for the 256x256 double-buffered kernel (ragged M)."""
+    say("gemm large", op, M, N, K)
+    Ash = (M, K) if op != G.GEMM_TN else (K, M)
+    Bsh = (N, K) if op == G.GEMM_NT else (K, N)
+    A, B = rnd_in(Ash, 21), rnd_in(Bsh, 22)
+    tA, tB = dev(A, torch.bfloat16), dev(B, torch.bfloat16)
+    C = torch.empty(M, N, dtype=torch.float32, device=DEV)
+    G.k_gemm(op, M, N, K, tA, Ash[1], tB, Bsh[1], C, N, G.EPI_F32, None, G.BF16)
+    R = dev(rnd_in((M, N), 23), torch.bfloat16)
+    R0 = R.clone()
+    G.k_gemm(op, M, N, K, tA, Ash[1], tB, Bsh[1], R, N, G.EPI_RESADD, None, G.BF16)
+    torch.cuda.synchronize()
+    ref = torch.from_numpy(_gemm_ref(op, A, B)).to(DEV)
+    assert rel_err(to_np(C), to_np(ref)) < 1e-5
+    assert rel_err(to_np(R), to_np(R0.double() + ref)) < 2e-2
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 512, 4096), (384, 128, 8192), (64, 96, 1024)])
 def test_gemm_tn_split_k(M, N, K):
     """Weight-gradient shapes: few output tiles, long reduction."""
