@@ -190,6 +190,64 @@ __device__ __forceinline__ void epi4(void* Cv, void* auxv, int64_t ldc, int64_t 
   }
 }
 
+// --------------------------------------------------------- one K-slice
+// MFMAs of one 64-deep K-slice for a wave's (16 TMI) x (16 TNJ) sub-tile,
+// software-pipelined: the B fragments of both 32-deep halves are read first,
+// then the A fragments stream D ahead of the 4..8-MFMA group that consumes
+// each one.  sched_barrier(0) pins that order: left alone, the scheduler
+// sinks every LDS read next to its first use and the wave then waits out the
+// full LDS latency before each group.
+//
+// D = 0 leaves the order to the compiler (better where the tile leaves no
+// spare registers for the streamed fragments, as in the 4-wave kernels).
+template <int TMI, int TNJ, bool XS, int D>
+__device__ __forceinline__ void mma_slice(const bf16* As, const bf16* Bs, int wm, int wn, int lr,
+                                          int lk, f32x4_t (&acc)[TMI][TNJ]) {
+  if constexpr (D == 0) {
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      bf16x8_t a[TMI], b[TNJ];
+#pragma unroll
+      for (int i = 0; i < TMI; ++i)
+        a[i] = *(const bf16x8_t*)(As + lds_at<XS>(wm + 16 * i + lr, kk + lk));
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j)
+        b[j] = *(const bf16x8_t*)(Bs + lds_at<XS>(wn + 16 * j + lr, kk + lk));
+#pragma unroll
+      for (int i = 0; i < TMI; ++i)
+#pragma unroll
+        for (int j = 0; j < TNJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    }
+    return;
+  }
+  bf16x8_t b[2][TNJ];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < TNJ; ++j)
+      b[h][j] = *(const bf16x8_t*)(Bs + lds_at<XS>(wn + 16 * j + lr, 32 * h + lk));
+  constexpr int NA = 2 * TMI;
+  constexpr int DD = D > 0 ? D : 1;
+  bf16x8_t a[NA];
+#pragma unroll
+  for (int x = 0; x < DD; ++x)
+    a[x] = *(const bf16x8_t*)(As + lds_at<XS>(wm + 16 * (x % TMI) + lr, 32 * (x / TMI) + lk));
+#pragma unroll
+  for (int x = 0; x < NA; ++x) {
+    if (x + DD < NA) {
+      const int y = x + DD;
+      a[y] = *(const bf16x8_t*)(As + lds_at<XS>(wm + 16 * (y % TMI) + lr, 32 * (y / TMI) + lk));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int i = x % TMI, h = x / TMI;
+#pragma unroll
+    for (int j = 0; j < TNJ; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[h][j], a[x], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // ------------------------------------------------------------------ kernel
 struct TileMap {
   int tiles_m, tiles_n, splits;
@@ -250,21 +308,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(int64_t M, int64_t N, int6
       sa.load(A, lda, m0, M, k0 + BK, kend);
       sb.load(B, ldb, n0, N, k0 + BK, kend);
     }
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      bf16x8_t a[TMI], b[TNJ];
-#pragma unroll
-      for (int i = 0; i < TMI; ++i)
-        a[i] = *(const bf16x8_t*)(As + lds_at<XS>(wm + 16 * i + lr, kk + lk));
-#pragma unroll
-      for (int j = 0; j < TNJ; ++j)
-        b[j] = *(const bf16x8_t*)(Bs + lds_at<XS>(wn + 16 * j + lr, kk + lk));
-#pragma unroll
-      for (int i = 0; i < TMI; ++i)
-#pragma unroll
-        for (int j = 0; j < TNJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-    }
+    mma_slice<TMI, TNJ, XS, 0>(As, Bs, wm, wn, lr, lk, acc);
     __syncthreads();
     if (more) {
       sa.store(As);
@@ -357,21 +401,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mfma_db(int64_t M, int64_t N, i
     }
     const bf16* As = stage ? As1 : As0;
     const bf16* Bs = stage ? Bs1 : Bs0;
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      bf16x8_t a[TMI], b[TNJ];
-#pragma unroll
-      for (int i = 0; i < TMI; ++i)
-        a[i] = *(const bf16x8_t*)(As + lds_off(wm + 16 * i + lr, kk + lk));
-#pragma unroll
-      for (int j = 0; j < TNJ; ++j)
-        b[j] = *(const bf16x8_t*)(Bs + lds_off(wn + 16 * j + lr, kk + lk));
-#pragma unroll
-      for (int i = 0; i < TMI; ++i)
-#pragma unroll
-        for (int j = 0; j < TNJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-    }
+    mma_slice<TMI, TNJ, false, 2>(As, Bs, wm, wn, lr, lk, acc);
     if (more) {
       sa.store(stage ? As0 : As1);
       sb.store(stage ? Bs0 : Bs1);
@@ -397,141 +427,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mfma_db(int64_t M, int64_t N, i
     }
   }
 }
-
-// Big-register-tile variant: 256 x 256 block tile, 4 waves (2 x 2) each
-// owning a 128 x 128 sub-tile (64 accumulator quads, held in AGPRs), one
-// wave per SIMD.  Two LDS stages; inside a K-slice the fragments of the
-// second 32-deep half are read while the MFMAs of the first half run, so the
-// matrix pipe is fed from a single wave.
-template <bool TA, bool TB, int EPI>
-__global__ __launch_bounds__(256, 1) void k_gemm_mfma_big(int64_t M, int64_t N, int64_t K,
-                                                          const bf16* __restrict__ A, int64_t lda,
-                                                          const bf16* __restrict__ B, int64_t ldb,
-                                                          void* C, int64_t ldc, void* aux,
-                                                          TileMap tm, float* partial) {
-  constexpr int BM = 256, BN = 256, NT = 256;
-  constexpr int WM = 128, WN = 128;
-  constexpr int TMI = WM / 16, TNJ = WN / 16;
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * (BM + BN) * LDK];
-  bf16* As0 = lds;
-  bf16* Bs0 = lds + BM * LDK;
-  bf16* As1 = lds + (BM + BN) * LDK;
-  bf16* Bs1 = lds + (2 * BM + BN) * LDK;
-
-  const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
-  const int per_xcd = (nb + 7) / 8;
-  const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (logical >= nb) return;
-  const int ntile = tm.tiles_m * tm.tiles_n;
-  const int split = logical / ntile;
-  const int t = logical % ntile;
-  constexpr int GM = 8;
-  const int group = t / (GM * tm.tiles_n);
-  const int first_m = group * GM;
-  const int gsize = min(tm.tiles_m - first_m, GM);
-  const int tile_m = first_m + (t % (GM * tm.tiles_n)) % gsize;
-  const int tile_n = (t % (GM * tm.tiles_n)) / gsize;
-  const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
-  const int64_t kbeg = (int64_t)split * tm.k_per_split;
-  const int64_t kend = min(K, kbeg + tm.k_per_split);
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
-  const int lr = lane & 15, lk = (lane >> 4) * 8;
-
-  f32x4_t acc[TMI][TNJ];
-#pragma unroll
-  for (int i = 0; i < TMI; ++i)
-#pragma unroll
-    for (int j = 0; j < TNJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  Stage<TA, BM, NT> sa;
-  Stage<TB, BN, NT> sb;
-  sa.load(A, lda, m0, M, kbeg, kend);
-  sb.load(B, ldb, n0, N, kbeg, kend);
-  sa.store(As0);
-  sb.store(Bs0);
-  __syncthreads();
-
-  // Software pipeline (per K-slice, stage s current):
-  //   global loads of the next slice | fragments of half 1 (stage s)
-  //   MFMAs of half 0
-  //   store the next slice into stage 1-s | barrier | fragments of half 0
-  //   of stage 1-s
-  //   MFMAs of half 1
-  // so each 64-MFMA block runs while LDS reads for the next block are in
-  // flight.  sched_barrier(0) keeps the compiler from sinking the reads next
-  // to their uses.
-  bf16x8_t a0[TMI], b0[TNJ], a1[TMI], b1[TNJ];
-#pragma unroll
-  for (int i = 0; i < TMI; ++i) a0[i] = *(const bf16x8_t*)(As0 + lds_off(wm + 16 * i + lr, lk));
-#pragma unroll
-  for (int j = 0; j < TNJ; ++j) b0[j] = *(const bf16x8_t*)(Bs0 + lds_off(wn + 16 * j + lr, lk));
-  int stage = 0;
-  for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
-    const bool more = k0 + BK < kend;
-    if (more) {
-      sa.load(A, lda, m0, M, k0 + BK, kend);
-      sb.load(B, ldb, n0, N, k0 + BK, kend);
-    }
-    const bf16* As = stage ? As1 : As0;
-    const bf16* Bs = stage ? Bs1 : Bs0;
-#pragma unroll
-    for (int i = 0; i < TMI; ++i)
-      a1[i] = *(const bf16x8_t*)(As + lds_off(wm + 16 * i + lr, 32 + lk));
-#pragma unroll
-    for (int j = 0; j < TNJ; ++j)
-      b1[j] = *(const bf16x8_t*)(Bs + lds_off(wn + 16 * j + lr, 32 + lk));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < TMI; ++i)
-#pragma unroll
-      for (int j = 0; j < TNJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[j], a0[i], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) {
-      sa.store(stage ? As0 : As1);
-      sb.store(stage ? Bs0 : Bs1);
-    }
-    __syncthreads();
-    if (more) {
-      const bf16* An = stage ? As0 : As1;
-      const bf16* Bn = stage ? Bs0 : Bs1;
-#pragma unroll
-      for (int i = 0; i < TMI; ++i) a0[i] = *(const bf16x8_t*)(An + lds_off(wm + 16 * i + lr, lk));
-#pragma unroll
-      for (int j = 0; j < TNJ; ++j) b0[j] = *(const bf16x8_t*)(Bn + lds_off(wn + 16 * j + lr, lk));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < TMI; ++i)
-#pragma unroll
-      for (int j = 0; j < TNJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[j], a1[i], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    stage ^= 1;
-  }
-
-  const int cq = (lane >> 4) * 4;
-#pragma unroll
-  for (int i = 0; i < TMI; ++i) {
-    const int64_t m = m0 + wm + 16 * i + lr;
-    if (m >= M) continue;
-#pragma unroll
-    for (int j = 0; j < TNJ; ++j) {
-      const int64_t n = n0 + wn + 16 * j + cq;
-      if (n >= N) continue;
-      if (partial) {
-        *(f32x4_t*)(partial + ((int64_t)split * M + m) * N + n) = acc[i][j];
-      } else {
-        epi4<EPI>(C, aux, ldc, m, n, acc[i][j]);
-      }
-    }
-  }
-}
-
-// which 256x256 kernel serves the large products
-static constexpr bool kBigRegisterTile = false;
 
 // out[m, n] (=/+=) sum_s partial[s, m, n], fixed order over s
 __global__ void k_splitk_reduce(const float* __restrict__ partial, int splits, int64_t M,
@@ -628,14 +523,9 @@ template <bool TA, bool TB, int EPI>
 static void launch_db_t(const GemmDesc& g, const TileMap& tm, float* partial, hipStream_t s) {
   const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
   const int grid = ((nb + 7) / 8) * 8;
-  if (kBigRegisterTile)
-    hipLaunchKernelGGL((k_gemm_mfma_big<TA, TB, EPI>), dim3(grid), dim3(256), 0, s, g.M, g.N,
-                       g.K, (const bf16*)g.A, g.lda, (const bf16*)g.B, g.ldb, g.C, g.ldc, g.aux,
-                       tm, partial);
-  else
-    hipLaunchKernelGGL((k_gemm_mfma_db<TA, TB, EPI>), dim3(grid), dim3(512), 0, s, g.M, g.N,
-                       g.K, (const bf16*)g.A, g.lda, (const bf16*)g.B, g.ldb, g.C, g.ldc, g.aux,
-                       tm, partial);
+  hipLaunchKernelGGL((k_gemm_mfma_db<TA, TB, EPI>), dim3(grid), dim3(512), 0, s, g.M, g.N, g.K,
+                     (const bf16*)g.A, g.lda, (const bf16*)g.B, g.ldb, g.C, g.ldc, g.aux, tm,
+                     partial);
 }
 
 template <bool TA, bool TB>
