@@ -5,12 +5,15 @@
 Times K forward+backward steps of the d12 model (12 layers, width 768, 6
 heads of 128, vocab 32768, 16 rows of 2048 tokens, 'SSSL' windows 1024/2048,
 value embeddings on odd layers) on synthetic seeded inputs already resident
-in HBM, then prints one JSON line.  Besides the step it times, with HIP
-events on the library's stream, every kernel shape the step launches (each
-GEMM, attention forward/backward) through the kernel-level entry points, and
-reports the one with the largest share of the step against its roofline.
-The CPU oracle is timed on a bounded sample of the same workload as a
-reported baseline.
+in HBM, then prints one JSON line.  After the timed steps it runs a few more
+steps with the library's launch recording on (two HIP events per kernel
+launch, on the stream the kernel runs on) and reports, per kernel, the
+average launch duration and the algorithmic work the library attributes to
+it; the kernel with the largest share of the step is set against its
+roofline.  HBM traffic of that kernel comes from the rocprofv3 counter
+summary in profiles/ when the kernel's sources still hash to the value
+recorded there (else null).  The CPU oracle is timed on a bounded sample of
+the same workload as a reported baseline.
 """
 from __future__ import annotations
 
@@ -151,6 +154,73 @@ def kernel_table(cfg, torch, G, iters=10):
     return rows
 
 
+def kernel_profile(step, n_steps, torch, G):
+    """Per-kernel time and work over n_steps steps run with the library's
+    launch recording on: {name: dict(...)} per step."""
+    from rocprof_summary import short_name
+    torch.cuda.synchronize()
+    G.prof_start(65536)
+    for _ in range(n_steps):
+        step()
+    overflow = G.prof_stop()
+    torch.cuda.synchronize()
+    recs = G.prof_records()
+    G.prof_clear()
+    if overflow:
+        raise RuntimeError("launch recording overflowed")
+    agg = {}
+    for name, ms, fl, by in recs:
+        k = short_name(name)
+        a = agg.setdefault(k, dict(kernel=k, launches=0, ms=0.0, flops=0.0, bytes=0.0))
+        a["launches"] += 1
+        a["ms"] += ms
+        a["flops"] += fl
+        a["bytes"] += by
+    rows = []
+    for a in agg.values():
+        n = a["launches"]
+        sec = a["ms"] / 1e3
+        rows.append(dict(kernel=a["kernel"], launches_per_step=n / n_steps,
+                         ms_per_step=a["ms"] / n_steps, avg_launch_ms=a["ms"] / n,
+                         flops_per_launch=a["flops"] / n, bytes_per_launch=a["bytes"] / n,
+                         tflops=a["flops"] / sec / 1e12 if a["flops"] else None,
+                         gbps=a["bytes"] / sec / 1e9 if a["bytes"] else None))
+    rows.sort(key=lambda r: -r["ms_per_step"])
+    return rows
+
+
+def roofline_of(row, step_ms):
+    """Roofline object of one kernel row of kernel_profile."""
+    from rocprof_summary import load_traffic
+    sec = row["avg_launch_ms"] / 1e3
+    if row["flops_per_launch"] > 0:
+        ach, peak, unit, bound = row["flops_per_launch"] / sec / 1e12, PEAK_BF16 / 1e12, "TFLOP/s", "mfma"
+    else:
+        ach, peak, unit, bound = row["bytes_per_launch"] / sec / 1e9, PEAK_HBM / 1e9, "GB/s", "hbm"
+    tr = load_traffic(row["kernel"])
+    return {"bound": bound, "kernel": row["kernel"], "achieved": round(ach, 2), "peak": peak,
+            "unit": unit, "frac": round(ach / peak, 4),
+            "traffic": tr["traffic_bytes"] if tr else None,
+            "traffic_source": tr["summary"] if tr else None,
+            "algorithmic_flops_per_launch": row["flops_per_launch"],
+            "algorithmic_bytes_per_launch": row["bytes_per_launch"],
+            "avg_launch_ms": round(row["avg_launch_ms"], 4),
+            "launches_per_step": row["launches_per_step"],
+            "share_of_step": round(row["ms_per_step"] / step_ms, 3)}
+
+
+def copy_calibration(torch):
+    """A device copy of exactly 1 GiB (1 GiB read, 1 GiB written), three
+    times, for calibrating the FETCH_SIZE / WRITE_SIZE counters."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copied 1 GiB x3")
+
+
 def cpu_baseline(cfg, seconds_hint=20.0):
     """The oracle (fp32 mode) on one row of the workload: tokens/s."""
     import numpy as np
@@ -178,8 +248,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="d12")
     ap.add_argument("--eval-rows", type=int, default=64)
-    ap.add_argument("--no-kernels", action="store_true")
+    ap.add_argument("--prof-steps", type=int, default=2,
+                    help="steps run with launch recording for the per-kernel split (0: none)")
+    ap.add_argument("--shapes", action="store_true",
+                    help="also time every product / attention shape alone")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the 1 GiB device copy used to calibrate HBM counters")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {a.gpus}); the step is built and "
@@ -194,6 +269,9 @@ def main():
     from gpt_pretraining_step_amd.session import Session
 
     torch.cuda.set_device(0)
+    if a.copy_calibration:
+        copy_calibration(torch)
+        return
     cfg = gi.preset(a.config)
     train_fpt, eval_fpt, mm = model_flops(cfg)
     B, T = cfg["batch"], cfg["seq_len"]
@@ -241,24 +319,27 @@ def main():
     bpb = s.bpb.cpu().numpy().tolist()
     log(f"eval {eval_tok_s:,.0f} tok/s, bpb {bpb[2]:.4f}")
 
-    roof = None
+    # per-kernel split of the step with the library's launch recording
+    prof = kernel_profile(step, a.prof_steps, torch, G) if a.prof_steps > 0 else []
+    roof = roofline_of(prof[0], ms) if prof else None
+    for r in prof[:14]:
+        rate = (f"{r['tflops']:7.1f} TFLOP/s" if r["tflops"] else
+                f"{r['gbps']:7.0f} GB/s" if r["gbps"] else "")
+        log(f"  {r['ms_per_step']:7.3f} ms/step {r['launches_per_step']:5.0f} x "
+            f"{r['avg_launch_ms'] * 1e3:8.1f} us  {rate:>16}  {r['kernel']}")
+    if roof:
+        log(f"roofline: {roof['kernel']} {roof['achieved']} {roof['unit']} "
+            f"frac {roof['frac']} traffic {roof['traffic']}")
+
     table = []
-    if not a.no_kernels:
+    if a.shapes:
         del s
         torch.cuda.empty_cache()
         table = kernel_table(cfg, torch, G)
         for r in table:
-            r["per_step_s"] = r["avg_s"] * r["count"]
             r["tflops"] = r["flops"] / r["avg_s"] / 1e12
             log(f"  {r['kernel']:<24} {r['avg_s'] * 1e3:8.3f} ms x{r['count']:<3} "
                 f"{r['tflops']:7.1f} TFLOP/s")
-        dom = max(table, key=lambda r: r["per_step_s"])
-        ach = dom["flops"] / dom["avg_s"]
-        roof = {"bound": dom["bound"], "kernel": dom["kernel"],
-                "achieved": round(ach / 1e12, 2), "peak": PEAK_BF16 / 1e12,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16, 4), "traffic": None,
-                "avg_launch_ms": round(dom["avg_s"] * 1e3, 4),
-                "share_of_step": round(dom["per_step_s"] / (ms / 1e3), 3)}
 
     cpu = None if a.no_cpu else cpu_baseline(cfg)
     out = {
@@ -277,7 +358,9 @@ def main():
         "eval_tokens_per_s": round(eval_tok_s, 1), "eval_rows": ev_rows, "eval_bpb": bpb[2],
         "roofline": roof, "cpu_baseline": cpu,
         "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
-                    for r in table],
+                    for r in prof],
+        "shapes": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
+                   for r in table],
     }
     print(json.dumps(out), flush=True)
 

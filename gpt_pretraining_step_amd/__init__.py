@@ -83,6 +83,12 @@ _SIGS = {
     "gpt_k_attn_bwd": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _vp]),
     "gpt_k_ce": (C.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp]),
+    "gpt_prof_start": (C.c_int, [_i32]),
+    "gpt_prof_stop": (C.c_int, []),
+    "gpt_prof_count": (_i32, []),
+    "gpt_prof_record": (C.c_int, [_i32, C.c_char_p, _sz, C.POINTER(C.c_float),
+                                  C.POINTER(C.c_double), C.POINTER(C.c_double)]),
+    "gpt_prof_clear": (None, []),
 }
 
 
@@ -223,3 +229,32 @@ def k_attn_bwd(qkv, o, lse, dout, dqkv, scratch, B, T, H, Hkv, hd, window, dtype
 def k_ce(z, tgt, rows, V, ell, lse, dz, grad_scale, dtype, stream=None):
     _check(lib().gpt_k_ce(_ptr(z), _ptr(tgt), rows, V, _ptr(ell), _ptr(lse), _ptr(dz),
                           grad_scale, dtype, _stream(stream)))
+
+
+# ------------------------------------------------------- launch recording
+def prof_start(capacity: int = 65536):
+    """Record every kernel launch (two HIP events each on its own stream)."""
+    _check(lib().gpt_prof_start(capacity))
+
+
+def prof_stop() -> bool:
+    """Stop recording; True if launches beyond the capacity went unrecorded."""
+    return bool(lib().gpt_prof_stop())
+
+
+def prof_records():
+    """[(kernel name, ms, flops, bytes)] of the recorded launches, in order
+    (waits for them to finish)."""
+    L = lib()
+    buf = C.create_string_buffer(1024)
+    ms, fl, by = C.c_float(), C.c_double(), C.c_double()
+    out = []
+    for i in range(int(L.gpt_prof_count())):
+        _check(L.gpt_prof_record(i, buf, len(buf), C.byref(ms), C.byref(fl), C.byref(by)))
+        out.append((buf.value.decode(), float(ms.value), float(fl.value), float(by.value)))
+    return out
+
+
+def prof_clear():
+    lib().gpt_prof_clear()
+

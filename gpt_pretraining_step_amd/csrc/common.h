@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 namespace gk {
 
 typedef uint16_t bf16;   // raw bf16 bits; arithmetic is always done in fp32

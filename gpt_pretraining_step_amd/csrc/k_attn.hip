@@ -150,10 +150,10 @@ hipError_t attn_fwd(const void* qkv, void* o, float* lse, int B, int T, int H, i
   const int64_t rows = (int64_t)B * H * T;
   dim3 grid((unsigned)cdiv(rows, 4)), block(256);
   if (dt == BF16)
-    hipLaunchKernelGGL(k_attn_fwd_row<bf16>, grid, block, 0, s, (const bf16*)qkv, (bf16*)o, lse, B,
+    GK_LAUNCH(Work(), k_attn_fwd_row<bf16>, grid, block, 0, s, (const bf16*)qkv, (bf16*)o, lse, B,
                        T, H, Hkv, hd, W);
   else
-    hipLaunchKernelGGL(k_attn_fwd_row<float>, grid, block, 0, s, (const float*)qkv, (float*)o, lse,
+    GK_LAUNCH(Work(), k_attn_fwd_row<float>, grid, block, 0, s, (const float*)qkv, (float*)o, lse,
                        B, T, H, Hkv, hd, W);
   return hipGetLastError();
 }
@@ -175,17 +175,17 @@ hipError_t attn_bwd(const void* qkv, const void* o, const float* lse, const void
   const int64_t rows = (int64_t)B * H * T;
   const int64_t krows = (int64_t)B * Hkv * T;
   if (dt == BF16) {
-    hipLaunchKernelGGL(k_attn_bwd_dq_row<bf16>, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, s,
+    GK_LAUNCH(Work(), k_attn_bwd_dq_row<bf16>, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, s,
                        (const bf16*)qkv, (const bf16*)o, lse, (const bf16*)dout, (bf16*)dqkv, delta,
                        B, T, H, Hkv, hd, W);
-    hipLaunchKernelGGL(k_attn_bwd_dkv_row<bf16>, dim3((unsigned)cdiv(krows, 4)), dim3(256), 0, s,
+    GK_LAUNCH(Work(), k_attn_bwd_dkv_row<bf16>, dim3((unsigned)cdiv(krows, 4)), dim3(256), 0, s,
                        (const bf16*)qkv, lse, (const bf16*)dout, delta, (bf16*)dqkv, B, T, H, Hkv,
                        hd, W);
   } else {
-    hipLaunchKernelGGL(k_attn_bwd_dq_row<float>, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, s,
+    GK_LAUNCH(Work(), k_attn_bwd_dq_row<float>, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, s,
                        (const float*)qkv, (const float*)o, lse, (const float*)dout, (float*)dqkv,
                        delta, B, T, H, Hkv, hd, W);
-    hipLaunchKernelGGL(k_attn_bwd_dkv_row<float>, dim3((unsigned)cdiv(krows, 4)), dim3(256), 0, s,
+    GK_LAUNCH(Work(), k_attn_bwd_dkv_row<float>, dim3((unsigned)cdiv(krows, 4)), dim3(256), 0, s,
                        (const float*)qkv, lse, (const float*)dout, delta, (float*)dqkv, B, T, H,
                        Hkv, hd, W);
   }

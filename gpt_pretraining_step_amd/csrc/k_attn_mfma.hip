@@ -193,7 +193,11 @@ hipError_t attn_mfma_fwd(const void* qkv, void* o, float* lse, int B, int T, int
                          int hd, int W, hipStream_t s) {
   (void)hd;
   dim3 grid((T + FWD_BQ - 1) / FWD_BQ, H, B);
-  hipLaunchKernelGGL(k_attn_fwd_mfma, grid, dim3(NW * 64), 0, s, (const bf16*)qkv, (bf16*)o, lse,
+  // 2 hd flops per visible pair for each of S = Q K^T and O = P V; q, k, v
+  // read once, o and lse written once
+  const double pairs = (double)B * H * visible_pairs(T, W), tok = (double)B * T;
+  const Work w(4.0 * HD * pairs, tok * HD * 2 * (2.0 * H + 2 * Hkv) + tok * H * 4);
+  GK_LAUNCH(w, k_attn_fwd_mfma, grid, dim3(NW * 64), 0, s, (const bf16*)qkv, (bf16*)o, lse,
                      T, H, Hkv, W);
   return hipGetLastError();
 }
@@ -539,12 +543,20 @@ hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const
                          int W, hipStream_t s) {
   (void)hd;
   const int64_t rows = (int64_t)B * T * H;
-  hipLaunchKernelGGL(k_attn_delta, dim3((unsigned)cdiv(rows * 16, 256)), dim3(256), 0, s,
+  // per kernel: 2 hd flops per visible pair and matrix product formed
+  // (dK/dV pass: S, dP, dV, dK; dQ pass: S, dP, dQ); operands read once,
+  // results written once
+  const double pairs = (double)B * H * visible_pairs(T, W), tok = (double)B * T;
+  const double qkvo = tok * HD * 2 * (2.0 * H + 2 * Hkv), stats = (double)rows * 8;
+  const Work wd(0.0, tok * H * HD * 2 * 2 + rows * 4.0);
+  const Work wkv(8.0 * HD * pairs, qkvo + stats + tok * 2 * Hkv * HD * 2);
+  const Work wq(6.0 * HD * pairs, qkvo + stats + tok * H * HD * 2);
+  GK_LAUNCH(wd, k_attn_delta, dim3((unsigned)cdiv(rows * 16, 256)), dim3(256), 0, s,
                      (const bf16*)o, (const bf16*)dout, delta, T, H, rows);
-  hipLaunchKernelGGL(k_attn_bwd_dkv, dim3((T + KV_BK - 1) / KV_BK, Hkv, B), dim3(NW * 64), 0, s,
+  GK_LAUNCH(wkv, k_attn_bwd_dkv, dim3((T + KV_BK - 1) / KV_BK, Hkv, B), dim3(NW * 64), 0, s,
                      (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T,
                      H, Hkv, W);
-  hipLaunchKernelGGL(k_attn_bwd_dq, dim3((T + FWD_BQ - 1) / FWD_BQ, H, B), dim3(NW * 64), 0, s,
+  GK_LAUNCH(wq, k_attn_bwd_dq, dim3((T + FWD_BQ - 1) / FWD_BQ, H, B), dim3(NW * 64), 0, s,
                      (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T,
                      H, Hkv, W);
   return hipGetLastError();

@@ -27,7 +27,7 @@ hipError_t fill_zero(void* p, int64_t bytes, hipStream_t s) {
   int ntail = (int)(bytes - n16 * 16);
   int64_t blocks = n16 ? cdiv(n16, kBlock) : 1;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(kBlock), 0, s,
+  GK_LAUNCH(Work(), k_fill_zero, dim3((unsigned)blocks), dim3(kBlock), 0, s,
                      (uint4*)p, n16, (uint8_t*)p + n16 * 16, ntail);
   return hipGetLastError();
 }
@@ -45,7 +45,7 @@ __global__ void k_rope_table(float2* cs, int T, int hd, double base) {
 
 hipError_t rope_table(float* cs, int T, int hd, float base, hipStream_t s) {
   int64_t n = (int64_t)T * (hd / 2);
-  hipLaunchKernelGGL(k_rope_table, dim3((unsigned)cdiv(n, kBlock)), dim3(kBlock),
+  GK_LAUNCH(Work(), k_rope_table, dim3((unsigned)cdiv(n, kBlock)), dim3(kBlock),
                      0, s, (float2*)cs, T, hd, (double)base);
   return hipGetLastError();
 }
@@ -79,13 +79,13 @@ hipError_t embed_fwd(const int32_t* tok, int B, int T, const void* wte,
   if (((int64_t)D * es) % 16 == 0) {
     int units = D * es / 16;
     int64_t total = N * units;
-    hipLaunchKernelGGL(k_embed_fwd16, dim3((unsigned)cdiv(total, kBlock)), dim3(kBlock),
+    GK_LAUNCH(Work(), k_embed_fwd16, dim3((unsigned)cdiv(total, kBlock)), dim3(kBlock),
                        0, s, tok, T, (const uint4*)wte, (uint4*)x, units, total);
   } else if (dt == BF16) {
-    hipLaunchKernelGGL(k_embed_fwd_el<uint16_t>, dim3((unsigned)cdiv(N * D, kBlock)),
+    GK_LAUNCH(Work(), k_embed_fwd_el<uint16_t>, dim3((unsigned)cdiv(N * D, kBlock)),
                        dim3(kBlock), 0, s, tok, T, (const uint16_t*)wte, (uint16_t*)x, D, N * D);
   } else {
-    hipLaunchKernelGGL(k_embed_fwd_el<float>, dim3((unsigned)cdiv(N * D, kBlock)),
+    GK_LAUNCH(Work(), k_embed_fwd_el<float>, dim3((unsigned)cdiv(N * D, kBlock)),
                        dim3(kBlock), 0, s, tok, T, (const float*)wte, (float*)x, D, N * D);
   }
   return hipGetLastError();
@@ -106,10 +106,10 @@ hipError_t embed_bwd(const int32_t* tok, int B, int T, const void* dx, int ldx,
                      float* dW, int D, DType dt, hipStream_t s) {
   int64_t total = (int64_t)B * T * D;
   if (dt == BF16)
-    hipLaunchKernelGGL(k_embed_bwd<bf16>, dim3((unsigned)cdiv(total, kBlock)), dim3(kBlock),
+    GK_LAUNCH(Work(), k_embed_bwd<bf16>, dim3((unsigned)cdiv(total, kBlock)), dim3(kBlock),
                        0, s, tok, T, (const bf16*)dx, ldx, dW, D, total);
   else
-    hipLaunchKernelGGL(k_embed_bwd<float>, dim3((unsigned)cdiv(total, kBlock)), dim3(kBlock),
+    GK_LAUNCH(Work(), k_embed_bwd<float>, dim3((unsigned)cdiv(total, kBlock)), dim3(kBlock),
                        0, s, tok, T, (const float*)dx, ldx, dW, D, total);
   return hipGetLastError();
 }
@@ -180,20 +180,21 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd_v(const bf16* x, bf16* y, f
 hipError_t rmsnorm_fwd(const void* x, void* y, float* r, int64_t rows, int D,
                        float eps, DType dt, hipStream_t s) {
   dim3 grid((unsigned)cdiv(rows, 4)), block(256);
+  const Work w(0.0, (double)rows * D * 2 * (dt == BF16 ? 2 : 4) + rows * 4.0);  // x in, y out, r
   if (dt == BF16 && D % 8 == 0 && D <= 64 * 8 * 4) {
     int vpl = (int)cdiv(D / 8, 64);
     if (vpl == 1)
-      hipLaunchKernelGGL(k_rmsnorm_fwd_v<1>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
+      GK_LAUNCH(w, k_rmsnorm_fwd_v<1>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
     else if (vpl == 2)
-      hipLaunchKernelGGL(k_rmsnorm_fwd_v<2>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
+      GK_LAUNCH(w, k_rmsnorm_fwd_v<2>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
     else if (vpl == 3)
-      hipLaunchKernelGGL(k_rmsnorm_fwd_v<3>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
+      GK_LAUNCH(w, k_rmsnorm_fwd_v<3>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
     else
-      hipLaunchKernelGGL(k_rmsnorm_fwd_v<4>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
+      GK_LAUNCH(w, k_rmsnorm_fwd_v<4>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
   } else if (dt == BF16) {
-    hipLaunchKernelGGL(k_rmsnorm_fwd<bf16>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
+    GK_LAUNCH(w, k_rmsnorm_fwd<bf16>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
   } else {
-    hipLaunchKernelGGL(k_rmsnorm_fwd<float>, grid, block, 0, s, (const float*)x, (float*)y, r, rows, D, eps);
+    GK_LAUNCH(w, k_rmsnorm_fwd<float>, grid, block, 0, s, (const float*)x, (float*)y, r, rows, D, eps);
   }
   return hipGetLastError();
 }
@@ -304,11 +305,13 @@ hipError_t rmsnorm_bwd(const void* dy, const void* y, const float* r,
                        const float* vez, const void* wg, int Hkv, int C,
                        DType dt, hipStream_t s) {
   dim3 grid((unsigned)cdiv(rows, 4)), block(256);
+  // dy, y (and dres) in, dx out, r in
+  const Work w(0.0, (double)rows * D * (dres ? 4 : 3) * (dt == BF16 ? 2 : 4) + rows * 4.0);
   const bool vec = dt == BF16 && D % 8 == 0 && D <= 64 * 8 * 4 && (!vez || C % 8 == 0);
   if (vec) {
     const int vpl = (int)cdiv(D / 8, 64);
 #define RMSB(V)                                                                              \
-  hipLaunchKernelGGL(k_rmsnorm_bwd_v<V>, grid, block, 0, s, (const bf16*)dy, (const bf16*)y, r, \
+  GK_LAUNCH(w, k_rmsnorm_bwd_v<V>, grid, block, 0, s, (const bf16*)dy, (const bf16*)y, r, \
                      (const bf16*)dres, (bf16*)dx, rows, D, vez, (const bf16*)wg, Hkv, C)
     if (vpl == 1) RMSB(1);
     else if (vpl == 2) RMSB(2);
@@ -316,10 +319,10 @@ hipError_t rmsnorm_bwd(const void* dy, const void* y, const float* r,
     else RMSB(4);
 #undef RMSB
   } else if (dt == BF16)
-    hipLaunchKernelGGL(k_rmsnorm_bwd<bf16>, grid, block, 0, s, (const bf16*)dy, (const bf16*)y, r,
+    GK_LAUNCH(w, k_rmsnorm_bwd<bf16>, grid, block, 0, s, (const bf16*)dy, (const bf16*)y, r,
                        (const bf16*)dres, (bf16*)dx, rows, D, vez, (const bf16*)wg, Hkv, C);
   else
-    hipLaunchKernelGGL(k_rmsnorm_bwd<float>, grid, block, 0, s, (const float*)dy, (const float*)y, r,
+    GK_LAUNCH(w, k_rmsnorm_bwd<float>, grid, block, 0, s, (const float*)dy, (const float*)y, r,
                        (const float*)dres, (float*)dx, rows, D, vez, (const float*)wg, Hkv, C);
   return hipGetLastError();
 }
@@ -485,19 +488,20 @@ __global__ __launch_bounds__(256) void k_rope_qknorm_bwd_v(bf16* dqkv, const bf1
 hipError_t rope_qknorm_fwd(void* qkv, float* rq, float* rk, const float* cs, int B, int T,
                            int H, int Hkv, int hd, float eps, DType dt, hipStream_t s) {
   int64_t N = (int64_t)B * T;
+  const Work w(0.0, (double)N * (H + Hkv) * (hd * 2.0 * (dt == BF16 ? 2 : 4) + 4));
   if (dt == BF16 && hd % 8 == 0) {
     const int64_t total = N * (H + Hkv) * (hd / 8);
-    hipLaunchKernelGGL(k_rope_qknorm_fwd_v, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s,
+    GK_LAUNCH(w, k_rope_qknorm_fwd_v, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s,
                        (bf16*)qkv, rq, rk, (const float2*)cs, N, T, H, Hkv, hd, eps);
     return hipGetLastError();
   }
   int64_t total = N * (H + Hkv) * (hd / 2);
   dim3 grid((unsigned)cdiv(total, 256)), block(256);
   if (dt == BF16)
-    hipLaunchKernelGGL(k_rope_qknorm_fwd<bf16>, grid, block, 0, s, (bf16*)qkv, rq, rk,
+    GK_LAUNCH(w, k_rope_qknorm_fwd<bf16>, grid, block, 0, s, (bf16*)qkv, rq, rk,
                        (const float2*)cs, N, T, H, Hkv, hd, eps);
   else
-    hipLaunchKernelGGL(k_rope_qknorm_fwd<float>, grid, block, 0, s, (float*)qkv, rq, rk,
+    GK_LAUNCH(w, k_rope_qknorm_fwd<float>, grid, block, 0, s, (float*)qkv, rq, rk,
                        (const float2*)cs, N, T, H, Hkv, hd, eps);
   return hipGetLastError();
 }
@@ -506,19 +510,20 @@ hipError_t rope_qknorm_bwd(void* dqkv, const void* qkv, const float* rq, const f
                            const float* cs, int B, int T, int H, int Hkv, int hd, DType dt,
                            hipStream_t s) {
   int64_t N = (int64_t)B * T;
+  const Work w(0.0, (double)N * (H + Hkv) * (hd * 3.0 * (dt == BF16 ? 2 : 4) + 4));
   if (dt == BF16 && hd % 8 == 0) {
     const int64_t total = N * (H + Hkv) * (hd / 8);
-    hipLaunchKernelGGL(k_rope_qknorm_bwd_v, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s,
+    GK_LAUNCH(w, k_rope_qknorm_bwd_v, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s,
                        (bf16*)dqkv, (const bf16*)qkv, rq, rk, (const float2*)cs, N, T, H, Hkv, hd);
     return hipGetLastError();
   }
   int64_t total = N * (H + Hkv) * (hd / 2);
   dim3 grid((unsigned)cdiv(total, 256)), block(256);
   if (dt == BF16)
-    hipLaunchKernelGGL(k_rope_qknorm_bwd<bf16>, grid, block, 0, s, (bf16*)dqkv, (const bf16*)qkv,
+    GK_LAUNCH(w, k_rope_qknorm_bwd<bf16>, grid, block, 0, s, (bf16*)dqkv, (const bf16*)qkv,
                        rq, rk, (const float2*)cs, N, T, H, Hkv, hd);
   else
-    hipLaunchKernelGGL(k_rope_qknorm_bwd<float>, grid, block, 0, s, (float*)dqkv, (const float*)qkv,
+    GK_LAUNCH(w, k_rope_qknorm_bwd<float>, grid, block, 0, s, (float*)dqkv, (const float*)qkv,
                        rq, rk, (const float2*)cs, N, T, H, Hkv, hd);
   return hipGetLastError();
 }
@@ -556,10 +561,10 @@ hipError_t ve_fwd(const int32_t* tok, int B, int T, const void* h, int D, const 
                   DType dt, hipStream_t s) {
   int64_t N = (int64_t)B * T;
   if (dt == BF16)
-    hipLaunchKernelGGL(k_ve_fwd<bf16>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const bf16*)h, D,
+    GK_LAUNCH(Work(), k_ve_fwd<bf16>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const bf16*)h, D,
                        (const bf16*)wg, C, (const bf16*)E, (bf16*)qkv, ldqkv, voff, g, Hkv, hd);
   else
-    hipLaunchKernelGGL(k_ve_fwd<float>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const float*)h, D,
+    GK_LAUNCH(Work(), k_ve_fwd<float>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const float*)h, D,
                        (const float*)wg, C, (const float*)E, (float*)qkv, ldqkv, voff, g, Hkv, hd);
   return hipGetLastError();
 }
@@ -590,10 +595,10 @@ hipError_t ve_bwd(const int32_t* tok, int B, int T, const void* dqkv, int ldqkv,
                   DType dt, hipStream_t s) {
   int64_t N = (int64_t)B * T;
   if (dt == BF16)
-    hipLaunchKernelGGL(k_ve_bwd<bf16>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const bf16*)dqkv,
+    GK_LAUNCH(Work(), k_ve_bwd<bf16>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const bf16*)dqkv,
                        ldqkv, voff, (const bf16*)E, g, vez, dE, Hkv, hd);
   else
-    hipLaunchKernelGGL(k_ve_bwd<float>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const float*)dqkv,
+    GK_LAUNCH(Work(), k_ve_bwd<float>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const float*)dqkv,
                        ldqkv, voff, (const float*)E, g, vez, dE, Hkv, hd);
   return hipGetLastError();
 }
@@ -620,10 +625,10 @@ __global__ __launch_bounds__(256) void k_ve_wgrad(const float* vez, const Tv* h,
 hipError_t ve_wgrad(const float* vez, const void* h, int D, int64_t N, int Hkv, int C, float* dWg,
                     int accumulate, DType dt, hipStream_t s) {
   if (dt == BF16)
-    hipLaunchKernelGGL(k_ve_wgrad<bf16>, dim3(Hkv * C), dim3(256), 0, s, vez, (const bf16*)h, D, N,
+    GK_LAUNCH(Work(), k_ve_wgrad<bf16>, dim3(Hkv * C), dim3(256), 0, s, vez, (const bf16*)h, D, N,
                        Hkv, C, dWg, accumulate);
   else
-    hipLaunchKernelGGL(k_ve_wgrad<float>, dim3(Hkv * C), dim3(256), 0, s, vez, (const float*)h, D, N,
+    GK_LAUNCH(Work(), k_ve_wgrad<float>, dim3(Hkv * C), dim3(256), 0, s, vez, (const float*)h, D, N,
                        Hkv, C, dWg, accumulate);
   return hipGetLastError();
 }
@@ -745,10 +750,12 @@ hipError_t ce_rows(const float* z, int64_t rows, int V, const int32_t* tok, int 
                    int tgt_direct, float* ell, float* lse, void* dz, float grad_scale,
                    DType dt, hipStream_t s, int64_t row0) {
   if (rows <= 0) return hipSuccess;
+  // logits read once, the gradient written once, per-row results
+  const Work w(0.0, (double)rows * V * (4.0 + (dz ? (dt == BF16 ? 2 : 4) : 0)) + rows * 12.0);
   if (dt == BF16 && V % 2048 == 0 && V <= 32768 && ((uintptr_t)z & 15) == 0) {
     const int nv4 = V / 2048;
 #define CEREG(K)                                                                             \
-  hipLaunchKernelGGL(k_ce_reg<K>, dim3((unsigned)rows), dim3(512), 0, s, z, V, tok, tgt_T,      \
+  GK_LAUNCH(w, k_ce_reg<K>, dim3((unsigned)rows), dim3(512), 0, s, z, V, tok, tgt_T,      \
                      tgt_direct, ell, lse, (bf16*)dz, grad_scale, row0)
     switch (nv4) {
       case 1: CEREG(1); break;
@@ -763,10 +770,10 @@ hipError_t ce_rows(const float* z, int64_t rows, int V, const int32_t* tok, int 
   }
 generic:
   if (dt == BF16)
-    hipLaunchKernelGGL(k_ce<bf16>, dim3((unsigned)rows), dim3(256), 0, s, z, rows, V, tok, tgt_T,
+    GK_LAUNCH(w, k_ce<bf16>, dim3((unsigned)rows), dim3(256), 0, s, z, rows, V, tok, tgt_T,
                        tgt_direct, ell, lse, (bf16*)dz, grad_scale, row0);
   else
-    hipLaunchKernelGGL(k_ce<float>, dim3((unsigned)rows), dim3(256), 0, s, z, rows, V, tok, tgt_T,
+    GK_LAUNCH(w, k_ce<float>, dim3((unsigned)rows), dim3(256), 0, s, z, rows, V, tok, tgt_T,
                        tgt_direct, ell, lse, (float*)dz, grad_scale, row0);
   return hipGetLastError();
 }
@@ -791,7 +798,7 @@ __global__ __launch_bounds__(256) void k_loss_reduce(const float* ell, int64_t N
 
 hipError_t loss_reduce(const float* ell, int64_t N, float* loss_ws, float* loss_out, int* flag,
                        hipStream_t s) {
-  hipLaunchKernelGGL(k_loss_reduce, dim3(1), dim3(256), 0, s, ell, N, loss_ws, loss_out, flag);
+  GK_LAUNCH(Work(), k_loss_reduce, dim3(1), dim3(256), 0, s, ell, N, loss_ws, loss_out, flag);
   return hipGetLastError();
 }
 
@@ -819,7 +826,7 @@ __global__ __launch_bounds__(256) void k_eval_accum(const float* ell, const int3
 
 hipError_t eval_accum(const float* ell, const int32_t* tok, int rows, int T,
                       const int32_t* token_bytes, double* acc, int first, hipStream_t s) {
-  hipLaunchKernelGGL(k_eval_accum, dim3(1), dim3(256), 0, s, ell, tok, rows, T, token_bytes, acc,
+  GK_LAUNCH(Work(), k_eval_accum, dim3(1), dim3(256), 0, s, ell, tok, rows, T, token_bytes, acc,
                      first);
   return hipGetLastError();
 }
@@ -833,7 +840,7 @@ __global__ void k_eval_finish(const double* acc, double* out) {
 }
 
 hipError_t eval_finish(const double* acc, double* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_eval_finish, dim3(1), dim3(64), 0, s, acc, out);
+  GK_LAUNCH(Work(), k_eval_finish, dim3(1), dim3(64), 0, s, acc, out);
   return hipGetLastError();
 }
 

@@ -78,12 +78,12 @@ static hipError_t launch_simple_op(const GemmDesc& g, hipStream_t s) {
   const Tv* A = (const Tv*)g.A;
   const Tv* B = (const Tv*)g.B;
   switch (g.epi) {
-    case E_STORE:   hipLaunchKernelGGL((k_gemm_simple<Tv, OP, E_STORE>), grid, block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, g.aux); break;
-    case E_RESADD:  hipLaunchKernelGGL((k_gemm_simple<Tv, OP, E_RESADD>), grid, block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, g.aux); break;
-    case E_RELU2:   hipLaunchKernelGGL((k_gemm_simple<Tv, OP, E_RELU2>), grid, block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, g.aux); break;
-    case E_DRELU2:  hipLaunchKernelGGL((k_gemm_simple<Tv, OP, E_DRELU2>), grid, block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, g.aux); break;
-    case E_F32:     hipLaunchKernelGGL((k_gemm_simple<Tv, OP, E_F32>), grid, block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, g.aux); break;
-    case E_F32_ACC: hipLaunchKernelGGL((k_gemm_simple<Tv, OP, E_F32_ACC>), grid, block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, g.aux); break;
+    case E_STORE:   GK_LAUNCH(Work(), (k_gemm_simple<Tv, OP, E_STORE>), grid, block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, g.aux); break;
+    case E_RESADD:  GK_LAUNCH(Work(), (k_gemm_simple<Tv, OP, E_RESADD>), grid, block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, g.aux); break;
+    case E_RELU2:   GK_LAUNCH(Work(), (k_gemm_simple<Tv, OP, E_RELU2>), grid, block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, g.aux); break;
+    case E_DRELU2:  GK_LAUNCH(Work(), (k_gemm_simple<Tv, OP, E_DRELU2>), grid, block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, g.aux); break;
+    case E_F32:     GK_LAUNCH(Work(), (k_gemm_simple<Tv, OP, E_F32>), grid, block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, g.aux); break;
+    case E_F32_ACC: GK_LAUNCH(Work(), (k_gemm_simple<Tv, OP, E_F32_ACC>), grid, block, 0, s, g.M, g.N, g.K, A, g.lda, B, g.ldb, g.C, g.ldc, g.aux); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -454,11 +454,23 @@ bool mfma_gemm_supported(const GemmDesc& g) {
   return true;
 }
 
+// Algorithmic work of one product: 2 M N K flops; A and B read once, C
+// written once (read too for RESADD / F32_ACC), aux written (RELU2) or read
+// (DRELU2) once.  Split-K partials are the reduce kernel's traffic.
+static Work gemm_work(const GemmDesc& g) {
+  const double mn = (double)g.M * g.N;
+  const bool f32out = g.epi == E_F32 || g.epi == E_F32_ACC;
+  double bytes = 2.0 * ((double)g.M * g.K + (double)g.N * g.K) + mn * (f32out ? 4 : 2);
+  if (g.epi == E_RESADD || g.epi == E_RELU2 || g.epi == E_DRELU2) bytes += 2.0 * mn;
+  if (g.epi == E_F32_ACC) bytes += 4.0 * mn;
+  return Work(2.0 * mn * g.K, bytes);
+}
+
 template <int BM, int BN, bool TA, bool TB, int EPI>
 static void launch(const GemmDesc& g, const TileMap& tm, float* partial, hipStream_t s) {
   const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
   const int grid = ((nb + 7) / 8) * 8;
-  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, TA, TB, EPI>), dim3(grid), dim3(256), 0, s, g.M, g.N,
+  GK_LAUNCH(gemm_work(g), (k_gemm_mfma<BM, BN, TA, TB, EPI>), dim3(grid), dim3(256), 0, s, g.M, g.N,
                      g.K, (const bf16*)g.A, g.lda, (const bf16*)g.B, g.ldb, g.C, g.ldc, g.aux, tm,
                      partial);
 }
@@ -523,7 +535,7 @@ template <bool TA, bool TB, int EPI>
 static void launch_db_t(const GemmDesc& g, const TileMap& tm, float* partial, hipStream_t s) {
   const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
   const int grid = ((nb + 7) / 8) * 8;
-  hipLaunchKernelGGL((k_gemm_mfma_db<TA, TB, EPI>), dim3(grid), dim3(512), 0, s, g.M, g.N, g.K,
+  GK_LAUNCH(gemm_work(g), (k_gemm_mfma_db<TA, TB, EPI>), dim3(grid), dim3(512), 0, s, g.M, g.N, g.K,
                      (const bf16*)g.A, g.lda, (const bf16*)g.B, g.ldb, g.C, g.ldc, g.aux, tm,
                      partial);
 }
@@ -563,7 +575,8 @@ hipError_t mfma_gemm(const GemmDesc& g, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !partial) return e;
   const int64_t MN = g.M * g.N;
-  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)cdiv(MN / 4, 256)), dim3(256), 0, s, partial,
+  const Work rw(0.0, 4.0 * MN * (tm.splits + 1 + (g.epi == E_F32_ACC ? 1 : 0)));
+  GK_LAUNCH(rw, k_splitk_reduce, dim3((unsigned)cdiv(MN / 4, 256)), dim3(256), 0, s, partial,
                      tm.splits, g.M, g.N, (float*)g.C, g.ldc, g.epi == E_F32_ACC ? 1 : 0);
   return hipGetLastError();
 }

@@ -261,6 +261,39 @@ int gpt_k_ce(const float* z, const int32_t* tgt, int64_t rows, int32_t V,
              float* ell, float* lse, void* dz, float grad_scale,
              int32_t dtype, hipStream_t s);
 
+/* ------------------------------------------------- launch recording */
+/*
+ * Per-launch timing of the library's own kernels, for measurement without a
+ * profiler.  Between gpt_prof_start and gpt_prof_stop every kernel the
+ * library enqueues (from any entry point above) is bracketed by two HIP
+ * events recorded on the stream it is launched on, and its algorithmic work
+ * is kept beside them: matmul flops (2 M N K for a product; for attention,
+ * 2 hd per visible (query, key) pair and per matrix product the kernel
+ * forms) and compulsory HBM bytes (operands read once, results written
+ * once), 0 where not stated.  Recording adds two event records per launch,
+ * so time steps with recording off and use it for the per-kernel split.
+ * Not for concurrent use from several host threads; events are owned by the
+ * library until gpt_prof_clear or the next gpt_prof_start.
+ */
+/* Allocates 2*capacity events (host call, not enqueued), drops earlier
+ * records and turns recording on.  GPT_ERR_INVALID_ARG unless
+ * 1 <= capacity <= 2^20; GPT_ERR_HIP if event creation fails. */
+int gpt_prof_start(int32_t capacity);
+/* Turns recording off.  Returns 1 if launches beyond `capacity` went
+ * unrecorded, else 0. */
+int gpt_prof_stop(void);
+/* Number of launches recorded. */
+int32_t gpt_prof_count(void);
+/* Record i (0-based, launch order): kernel name as the HIP runtime reports
+ * it, demangled, truncated to name_len - 1 characters (host buffer);
+ * duration in ms (waits for the launch to finish); flops and bytes as
+ * above.  Only after gpt_prof_stop; GPT_ERR_INVALID_ARG for a bad index or
+ * null output. */
+int gpt_prof_record(int32_t i, char* name, size_t name_len, float* ms,
+                    double* flops, double* bytes);
+/* Turns recording off and frees the events and records. */
+void gpt_prof_clear(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,199 @@
+"""rocprofv3 summaries for profiles/, and the HBM traffic bench.py reports.
+
+    python rocprof_summary.py --kernel NAME --stats DIR [--fetch DIR --write DIR
+        --cal-fetch DIR --cal-write DIR] [--bench-json FILE] [--cmd TEXT ...]
+        --out profiles/<file>.md
+
+--stats is the output folder of a `rocprofv3 --kernel-trace --stats -f csv`
+run; --fetch / --write are `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE`
+runs (with --kernel-trace, -f csv) of the workload; --cal-fetch / --cal-write
+the same counters over `bench.py --copy-calibration`, a device copy of
+exactly 1 GiB (1 GiB read, 1 GiB written), which fixes the bytes each counter
+unit stands for on this part.  The summary gives the per-kernel time table,
+the kernel's counters per dispatch and, on a line starting `traffic-json:`,
+its calibrated HBM bytes per launch with a hash of the kernel's sources;
+bench.py reports that traffic only while the sources still hash the same.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "gpt_pretraining_step_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 1 << 30
+
+
+def short_name(name: str) -> str:
+    """'void gk::k_x<1, 2>(int, ...)' -> 'k_x<1, 2>'."""
+    n = name.strip()
+    if n.startswith("void "):
+        n = n[5:]
+    depth, cut = 0, len(n)
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    n = n[:cut]
+    return n.replace("gk::", "").strip()
+
+
+def kernel_sources_sha256(kernel: str) -> str:
+    """sha256 over the source file(s) defining the kernel and every header
+    of the library's source folder."""
+    base = re.sub(r"<.*", "", kernel)
+    files = []
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if f.endswith(".h"):
+            files.append(f)
+        elif f.endswith((".hip", ".cpp")):
+            with open(f, encoding="utf-8") as fh:
+                if re.search(r"\bvoid\s+" + re.escape(base) + r"\s*\(", fh.read()):
+                    files.append(f)
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def load_traffic(kernel: str):
+    """Calibrated HBM bytes per launch of `kernel` from profiles/, or None
+    when no summary covers it or its sources changed since."""
+    want = kernel_sources_sha256(kernel)
+    for f in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        with open(f, encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("traffic-json:"):
+                    d = json.loads(line[len("traffic-json:"):])
+                    if d.get("kernel") == kernel and d.get("sources_sha256") == want:
+                        d["summary"] = os.path.relpath(f, ROOT)
+                        return d
+    return None
+
+
+def _one(path: str, pattern: str) -> str:
+    hits = glob.glob(os.path.join(path, "**", pattern), recursive=True)
+    if len(hits) != 1:
+        raise SystemExit(f"expected one {pattern} under {path}, found {hits}")
+    return hits[0]
+
+
+def read_stats(d: str):
+    rows = []
+    with open(_one(d, "*kernel_stats.csv")) as fh:
+        for r in csv.DictReader(fh):
+            rows.append(dict(name=short_name(r["Name"]), calls=int(r["Calls"]),
+                             total_ns=float(r["TotalDurationNs"]), avg_ns=float(r["AverageNs"]),
+                             pct=float(r["Percentage"])))
+    return rows
+
+
+def read_counter(d: str, counter: str):
+    """{short kernel name: [value per dispatch]} (KiB for *_SIZE counters)."""
+    out = {}
+    with open(_one(d, "*counter_collection.csv")) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            out.setdefault(short_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return out
+
+
+def copy_factor(d: str, counter: str):
+    """Bytes per counter KiB unit, from the 1 GiB copy: the largest dispatch
+    of the calibration run is the copy."""
+    vals = read_counter(d, counter)
+    name, best = max(((k, max(v)) for k, v in vals.items()), key=lambda kv: kv[1])
+    return COPY_BYTES / (best * 1024.0), name, best
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--kernel", required=True)
+    ap.add_argument("--stats", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--cal-fetch")
+    ap.add_argument("--cal-write")
+    ap.add_argument("--bench-json")
+    ap.add_argument("--cmd", action="append", default=[])
+    ap.add_argument("--title", default="")
+    ap.add_argument("--top", type=int, default=25)
+    ap.add_argument("--out", required=True)
+    a = ap.parse_args()
+
+    stats = read_stats(a.stats)
+    tot = sum(r["total_ns"] for r in stats)
+    L = [f"# {a.title or a.kernel}", ""]
+    if a.cmd:
+        L += ["Commands (run from the repository root; rocprofv3 after "
+              "`cd /tmp && export TMPDIR=/tmp`, paths shortened):", ""]
+        L += [f"    {c}" for c in a.cmd] + [""]
+    bench = None
+    if a.bench_json:
+        with open(a.bench_json) as fh:
+            lines = [l for l in fh if l.startswith("{")]
+        bench = json.loads(lines[-1])
+        rf = bench.get("roofline") or {}
+        L += [f"bench.py line of the profiled run: {bench['value']:,.0f} {bench['unit']}, "
+              f"{bench['ms_per_step']} ms/step; roofline kernel `{rf.get('kernel')}`, "
+              f"avg launch {rf.get('avg_launch_ms')} ms (HIP events), achieved "
+              f"{rf.get('achieved')} {rf.get('unit')}, frac {rf.get('frac')}", ""]
+    L += [f"Kernel time over the whole run: {tot / 1e6:.2f} ms", "",
+          "| share | total ms | calls | avg us | kernel |", "|---:|---:|---:|---:|---|"]
+    for r in sorted(stats, key=lambda r: -r["total_ns"])[:a.top]:
+        L.append(f"| {r['pct']:.2f}% | {r['total_ns'] / 1e6:.3f} | {r['calls']} | "
+                 f"{r['avg_ns'] / 1e3:.1f} | `{r['name']}` |")
+    L.append("")
+    mine = [r for r in stats if r["name"] == a.kernel]
+    if not mine:
+        raise SystemExit(f"{a.kernel} not in {a.stats}")
+    L += [f"`{a.kernel}`: {mine[0]['calls']} calls, average {mine[0]['avg_ns'] / 1e3:.1f} us "
+          "(rocprofv3 kernel trace).", ""]
+    if a.fetch and a.write and a.cal_fetch and a.cal_write:
+        ff, fname, fval = copy_factor(a.cal_fetch, "FETCH_SIZE")
+        wf, wname, wval = copy_factor(a.cal_write, "WRITE_SIZE")
+        fv = read_counter(a.fetch, "FETCH_SIZE")[a.kernel]
+        wv = read_counter(a.write, "WRITE_SIZE")[a.kernel]
+        f_kib, w_kib = sum(fv) / len(fv), sum(wv) / len(wv)
+        fetch_b, write_b = f_kib * 1024 * ff, w_kib * 1024 * wf
+        L += ["Calibration (device copy of exactly 1 GiB):", "",
+              f"- FETCH_SIZE read {fval:.0f} KiB for `{fname}`: factor {ff:.4f} bytes per counted byte",
+              f"- WRITE_SIZE read {wval:.0f} KiB for `{wname}`: factor {wf:.4f}", "",
+              f"`{a.kernel}` per dispatch ({len(fv)} / {len(wv)} dispatches): FETCH_SIZE "
+              f"{f_kib:.0f} KiB -> {fetch_b / 1e6:.1f} MB, WRITE_SIZE {w_kib:.0f} KiB -> "
+              f"{write_b / 1e6:.1f} MB; HBM traffic {(fetch_b + write_b) / 1e6:.1f} MB per launch.",
+              ""]
+        if bench and (bench.get("kernels")):
+            k = [r for r in bench["kernels"] if r.get("kernel") == a.kernel]
+            if k and k[0].get("bytes_per_launch"):
+                alg = k[0]["bytes_per_launch"]
+                L += [f"Algorithmic bytes per launch (library's count): {alg / 1e6:.1f} MB; "
+                      f"measured / algorithmic = {(fetch_b + write_b) / alg:.2f}.", ""]
+        rec = dict(kernel=a.kernel, fetch_bytes=round(fetch_b), write_bytes=round(write_b),
+                   traffic_bytes=round(fetch_b + write_b), fetch_factor=round(ff, 5),
+                   write_factor=round(wf, 5), dispatches=len(fv),
+                   sources_sha256=kernel_sources_sha256(a.kernel))
+        L.append("traffic-json: " + json.dumps(rec))
+        L.append("")
+    os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(L))
+    print(a.out)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
