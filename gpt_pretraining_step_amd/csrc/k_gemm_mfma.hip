@@ -428,6 +428,239 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mfma_db(int64_t M, int64_t N, i
   }
 }
 
+// ------------------------------------------------- direct-to-LDS variant
+// 8 waves (4 x 2, each (BM/4) x (BN/2)), two LDS stages filled straight from
+// global memory by global_load_lds_dwordx4: every load instruction moves one
+// contiguous 1 KB LDS block (lane i -> bytes 16i..16i+15), so the layout is
+// chosen through which global 16-byte chunk each lane fetches.  No staging
+// registers, no LDS store instructions, and the loads of slice s+1 stay in
+// flight while slice s is multiplied.
+//
+// K-contiguous operand: LDS rows of 64 k (128 B, no padding), 16-byte chunk c
+// of row r stored at position c ^ ((r >> 1) & 7); a fragment read (16 rows,
+// one chunk) then touches 16 distinct 16-byte bank slots.
+// MN-contiguous operand: LDS rows are k (R elements each, as in memory), and
+// a fragment is gathered with two ds_read_b64_tr_b16: in each 16-lane group,
+// lane s points at 4 elements (row k0 + s/4, columns 4(s%4)..) and receives
+// the 4 k-values of column s (its MFMA operand layout).  Chunks are XOR-
+// swizzled per k row so the 8 rows one read instruction touches per 32 lanes
+// fall in distinct 32-byte bank slots.
+//
+// K must be a multiple of 64 (no zero fill: rows past M or N are clamped to
+// valid memory and their results dropped).
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
+
+// chunk swizzle of k-row `k` in an MN-contiguous stage of R columns
+template <int R>
+__device__ __forceinline__ int swz_mn(int k) {
+  if constexpr (R == 192) return 2 * (((k >> 1) & 1) | (((k >> 3) & 1) << 1));
+  else return 2 * ((k & 3) | (((k >> 3) & 1) << 2));
+}
+
+// Buffer loads straight into LDS.  The descriptor of an operand starts at
+// the tile's first row (K-contiguous) or column (MN-contiguous) and ends at
+// the end of the matrix, so lanes past the last row or k read zeros; columns
+// past N alias into the next row and only feed results that are dropped.
+// One per-lane byte offset per operand: the NB load instructions of a wave
+// differ by a uniform step (64 rows, or 2048 / R k-rows, with the same
+// swizzle), which goes into the scalar offset.
+static constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, gfx9 family
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4_t make_rsrc(const bf16* base, int64_t bytes) {
+  const int64_t lim = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  const uint64_t a = (uint64_t)base;
+  i32x4_t r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);   // stride 0
+  r[2] = (int)(uint32_t)lim;
+  r[3] = kRsrcWord3;
+  return r;
+}
+
+// One 16-byte-per-lane buffer load into the 1 KB LDS block at `lds` (a wave-
+// uniform LDS byte address).  Written as asm so the compiler does not track
+// it: the waits for these loads are the explicit vmcnt(0) before each
+// barrier of the main loop, and reads of the other stage never wait for them.
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+template <int R, bool TRANS>
+struct DmaPlan {
+  static constexpr int NB = R / 64;                        // load instructions per wave
+  static constexpr int STEP_ROWS = TRANS ? 4096 / R : 64;  // rows (k or MN) between them
+  static_assert(!TRANS || R == 128 || R == 256, "MN-contiguous stage width");
+  i32x4_t rsrc;
+  uint32_t voff;
+  int64_t ld;
+  // g: operand base; r0: first MN index of the tile; rows: M or N; K rows
+  __device__ __forceinline__ void init(const bf16* g, int64_t ld_, int64_t r0, int64_t rows,
+                                       int64_t K, int wave, int lane) {
+    ld = ld_;
+    const int o = 1024 * wave + 16 * lane;      // byte offset of this lane in block `wave`
+    if constexpr (!TRANS) {
+      const int row = o >> 7, p = (o >> 4) & 7;
+      rsrc = make_rsrc(g + r0 * ld, (rows - r0) * ld * 2);
+      voff = (uint32_t)(row * ld * 2 + 16 * (p ^ swz_k(row)));
+    } else {
+      const int krow = o / (2 * R), p = (o % (2 * R)) >> 4;
+      rsrc = make_rsrc(g + r0, (K * ld - r0) * 2);
+      voff = (uint32_t)(krow * ld * 2 + 16 * (p ^ swz_mn<R>(krow)));
+    }
+  }
+  __device__ __forceinline__ void issue(int64_t k0, bf16* stage, int wave) const {
+    const uint32_t kofs = (uint32_t)(TRANS ? k0 * ld * 2 : k0 * 2);
+    const uint32_t step = (uint32_t)(STEP_ROWS * ld * 2);
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_void_t*)stage + 1024u * (uint32_t)wave);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) dma16(rsrc, base + 8192u * i, voff, kofs + i * step);
+  }
+};
+
+// fragment (16 rows of the MN index from `base`, k = kk + 8g .. +7) of a
+// stage operand
+template <int R, bool TRANS>
+__device__ __forceinline__ bf16x8_t frag(const bf16* st, int base, int kk, int lane) {
+  const int g = lane >> 4, l16 = lane & 15;
+  if constexpr (!TRANS) {
+    const int row = base + l16, c = (kk >> 3) + g;
+    return *(const bf16x8_t*)(st + row * 64 + 8 * (c ^ swz_k(row)));
+  } else {
+    const int n = base + 4 * (l16 & 3), c = n >> 3;
+    v4s_t h[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int k = kk + 8 * g + 4 * hh + (l16 >> 2);
+      const bf16* p = st + k * R + 8 * (c ^ swz_mn<R>(k)) + (n & 7);
+      h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)p);
+    }
+    typedef short v8s_t __attribute__((ext_vector_type(8)));
+    v8s_t v = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+}
+
+template <int BM, int BN, bool TA, bool TB, int EPI>
+__global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64_t K,
+                                                     const bf16* __restrict__ A, int64_t lda,
+                                                     const bf16* __restrict__ B, int64_t ldb,
+                                                     void* C, int64_t ldc, void* aux,
+                                                     TileMap tm, float* partial) {
+  constexpr int WM = BM / 4, WN = BN / 2;
+  constexpr int TMI = WM / 16, TNJ = WN / 16;
+  __shared__ __attribute__((aligned(1024))) bf16 st0[(BM + BN) * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 st1[(BM + BN) * 64];
+
+  const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
+  const int per_xcd = (nb + 7) / 8;
+  const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (logical >= nb) return;
+  const int ntile = tm.tiles_m * tm.tiles_n;
+  const int split = logical / ntile;
+  const int t = logical % ntile;
+  constexpr int GM = 8;
+  const int group = t / (GM * tm.tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tm.tiles_m - first_m, GM);
+  const int tile_m = first_m + (t % (GM * tm.tiles_n)) % gsize;
+  const int tile_n = (t % (GM * tm.tiles_n)) / gsize;
+  const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
+  const int64_t kbeg = (int64_t)split * tm.k_per_split;
+  const int64_t kend = min(K, kbeg + tm.k_per_split);
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
+
+  DmaPlan<BM, TA> pa;
+  DmaPlan<BN, TB> pb;
+  pa.init(A, lda, m0, M, K, wave, lane);
+  pb.init(B, ldb, n0, N, K, wave, lane);
+
+  f32x4_t acc[TMI][TNJ];
+#pragma unroll
+  for (int i = 0; i < TMI; ++i)
+#pragma unroll
+    for (int j = 0; j < TNJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const bf16* st) {
+    const bf16* As = st;
+    const bf16* Bs = st + BM * 64;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      bf16x8_t a[TMI], b[TNJ];
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j) b[j] = frag<BN, TB>(Bs, wn + 16 * j, kk, lane);
+#pragma unroll
+      for (int i = 0; i < TMI; ++i) a[i] = frag<BM, TA>(As, wm + 16 * i, kk, lane);
+#pragma unroll
+      for (int i = 0; i < TMI; ++i)
+#pragma unroll
+        for (int j = 0; j < TNJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // two stages in two arrays, visited in a loop unrolled by two so that
+  // every LDS access names its stage statically (the loads in flight into
+  // one stage then never hold up reads of the other)
+  const int nsl = (int)((kend - kbeg) / BK);
+  pa.issue(kbeg, st0, wave);
+  pb.issue(kbeg, st0 + BM * 64, wave);
+  int it = 0;
+  for (; it + 2 <= nsl; it += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    pa.issue(kbeg + (int64_t)(it + 1) * BK, st1, wave);
+    pb.issue(kbeg + (int64_t)(it + 1) * BK, st1 + BM * 64, wave);
+    compute(st0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + 2 < nsl) {
+      pa.issue(kbeg + (int64_t)(it + 2) * BK, st0, wave);
+      pb.issue(kbeg + (int64_t)(it + 2) * BK, st0 + BM * 64, wave);
+    }
+    compute(st1);
+  }
+  if (it < nsl) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    compute(st0);
+  }
+
+  const int cq = (lane >> 4) * 4, lr = lane & 15;
+  if (partial) {
+    float* P = partial + (int64_t)split * M * N;
+#pragma unroll
+    for (int i = 0; i < TMI; ++i) {
+      const int64_t m = m0 + wm + 16 * i + lr;
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j) {
+        const int64_t n = n0 + wn + 16 * j + cq;
+        if (m < M && n < N) *(f32x4_t*)(P + m * N + n) = acc[i][j];
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < TMI; ++i) {
+    const int64_t m = m0 + wm + 16 * i + lr;
+#pragma unroll
+    for (int j = 0; j < TNJ; ++j) {
+      const int64_t n = n0 + wn + 16 * j + cq;
+      if (m < M && n < N) epi4<EPI>(C, aux, ldc, m, n, acc[i][j]);
+    }
+  }
+}
+
 // out[m, n] (=/+=) sum_s partial[s, m, n], fixed order over s
 __global__ void k_splitk_reduce(const float* __restrict__ partial, int splits, int64_t M,
                                 int64_t N, float* out, int64_t ldc, int accumulate) {
@@ -558,26 +791,116 @@ static void launch_db(const GemmDesc& g, const TileMap& tm, float* partial, hipS
   else launch_db_e<true, true>(g, tm, partial, s);
 }
 
+template <int BM, int BN, bool TA, bool TB, int EPI>
+static void launch_dma_t(const GemmDesc& g, const TileMap& tm, float* partial, hipStream_t s) {
+  const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
+  const int grid = ((nb + 7) / 8) * 8;
+  GK_LAUNCH(gemm_work(g), (k_gemm_dma<BM, BN, TA, TB, EPI>), dim3(grid), dim3(512), 0, s, g.M,
+            g.N, g.K, (const bf16*)g.A, g.lda, (const bf16*)g.B, g.ldb, g.C, g.ldc, g.aux, tm,
+            partial);
+}
+
+template <int BM, int BN, bool TA, bool TB>
+static void launch_dma_e(const GemmDesc& g, const TileMap& tm, float* partial, hipStream_t s) {
+  switch (g.epi) {
+    case E_STORE:   launch_dma_t<BM, BN, TA, TB, E_STORE>(g, tm, partial, s); break;
+    case E_RESADD:  launch_dma_t<BM, BN, TA, TB, E_RESADD>(g, tm, partial, s); break;
+    case E_RELU2:   launch_dma_t<BM, BN, TA, TB, E_RELU2>(g, tm, partial, s); break;
+    case E_DRELU2:  launch_dma_t<BM, BN, TA, TB, E_DRELU2>(g, tm, partial, s); break;
+    case E_F32:     launch_dma_t<BM, BN, TA, TB, E_F32>(g, tm, partial, s); break;
+    default:        launch_dma_t<BM, BN, TA, TB, E_F32_ACC>(g, tm, partial, s); break;
+  }
+}
+
+template <int BM, int BN>
+static void launch_dma(const GemmDesc& g, const TileMap& tm, float* partial, hipStream_t s) {
+  if (g.op == OP_NT) launch_dma_e<BM, BN, false, false>(g, tm, partial, s);
+  else if (g.op == OP_NN) launch_dma_e<BM, BN, false, true>(g, tm, partial, s);
+  else launch_dma_e<BM, BN, true, true>(g, tm, partial, s);
+}
+
+// The direct-to-LDS kernel takes every product it can: K a multiple of 64,
+// at least 2^31 multiply-adds (smaller ones keep the 4-wave kernels), and
+// operands addressable with 32-bit buffer offsets.
+static bool dma_shape_ok(int64_t M, int64_t N, int64_t K) {
+  return K % BK == 0 && (double)M * N * K >= 2147483648.0;
+}
+
+static bool dma_ok(const GemmDesc& g) {
+  if (!dma_shape_ok(g.M, g.N, g.K)) return false;
+  const bool TA = g.op == OP_TN, TB = g.op != OP_NT;
+  const double a_bytes = 2.0 * (TA ? g.K * g.lda : g.M * g.lda);
+  const double b_bytes = 2.0 * (TB ? g.K * g.ldb : g.N * g.ldb);
+  return a_bytes < 4294967295.0 && b_bytes < 4294967295.0;
+}
+
+// 256x256 tiles, one block per CU.  fp32 outputs may split K: the split
+// minimises a time estimate, rounds of 256 blocks x K-slices per block x
+// ~2.1 us per 256x256x64 slice, plus the partial tiles' HBM traffic (written
+// and read once, ~5 TB/s) and the reduce launch; at least 8 K-slices per
+// split.
+static TileMap plan_dma(int64_t M, int64_t N, int64_t K, bool f32out, size_t scratch_bytes) {
+  const int kCU = 256;
+  TileMap tm;
+  tm.tiles_m = (int)cdiv(M, 256);
+  tm.tiles_n = (int)cdiv(N, 256);
+  tm.splits = 1;
+  tm.k_per_split = K;
+  if (!f32out) return tm;
+  const int64_t tiles = (int64_t)tm.tiles_m * tm.tiles_n, ksl = K / BK;
+  auto cost = [&](int sp) {
+    const double rounds = (double)cdiv(tiles * sp, kCU);
+    const double slices = (double)cdiv(ksl, sp);
+    return rounds * slices * 2.1 + (sp > 1 ? sp * (double)M * N * 8.0 / 5e6 + 10.0 : 0.0);
+  };
+  int best = 1;
+  double best_cost = cost(1);
+  for (int sp = 2; sp <= 64 && ksl / sp >= 8; ++sp) {
+    if ((size_t)sp * M * N * 4 > scratch_bytes) break;
+    const double c = cost(sp);
+    if (c < best_cost) { best = sp; best_cost = c; }
+  }
+  if (best > 1) {
+    tm.k_per_split = cdiv(ksl, best) * BK;
+    tm.splits = (int)cdiv(K, tm.k_per_split);
+  }
+  return tm;
+}
+
 size_t mfma_splitk_bytes(int64_t M, int64_t N, int64_t K) {
   int bm;
   TileMap tm = plan(M, N, K, true, SIZE_MAX, &bm);
-  return tm.splits > 1 ? (size_t)tm.splits * M * N * sizeof(float) : 0;
+  size_t b = tm.splits > 1 ? (size_t)tm.splits * M * N * sizeof(float) : 0;
+  if (dma_shape_ok(M, N, K)) {
+    TileMap td = plan_dma(M, N, K, true, SIZE_MAX);
+    if (td.splits > 1) b = std::max(b, (size_t)td.splits * M * N * sizeof(float));
+  }
+  return b;
 }
 
 hipError_t mfma_gemm(const GemmDesc& g, hipStream_t s) {
   const bool f32out = g.epi == E_F32 || g.epi == E_F32_ACC;
-  int BM;
-  TileMap tm = plan(g.M, g.N, g.K, f32out, g.scratch ? g.scratch_bytes : 0, &BM);
-  float* partial = tm.splits > 1 ? (float*)g.scratch : nullptr;
-  if (BM == 512) launch_db(g, tm, partial, s);
-  else if (BM == 256) launch_op<256, 128>(g, tm, partial, s);
-  else launch_op<128, 128>(g, tm, partial, s);
+  const size_t scr = g.scratch ? g.scratch_bytes : 0;
+  TileMap tm;
+  float* partial = nullptr;
+  if (dma_ok(g)) {
+    tm = plan_dma(g.M, g.N, g.K, f32out, scr);
+    partial = tm.splits > 1 ? (float*)g.scratch : nullptr;
+    launch_dma<256, 256>(g, tm, partial, s);
+  } else {
+    int BM;
+    tm = plan(g.M, g.N, g.K, f32out, scr, &BM);
+    partial = tm.splits > 1 ? (float*)g.scratch : nullptr;
+    if (BM == 512) launch_db(g, tm, partial, s);
+    else if (BM == 256) launch_op<256, 128>(g, tm, partial, s);
+    else launch_op<128, 128>(g, tm, partial, s);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !partial) return e;
   const int64_t MN = g.M * g.N;
   const Work rw(0.0, 4.0 * MN * (tm.splits + 1 + (g.epi == E_F32_ACC ? 1 : 0)));
   GK_LAUNCH(rw, k_splitk_reduce, dim3((unsigned)cdiv(MN / 4, 256)), dim3(256), 0, s, partial,
-                     tm.splits, g.M, g.N, (float*)g.C, g.ldc, g.epi == E_F32_ACC ? 1 : 0);
+            tm.splits, g.M, g.N, (float*)g.C, g.ldc, g.epi == E_F32_ACC ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -106,7 +106,8 @@ def test_gemm_large_tiles(op, M, N, K):
     assert rel_err(to_np(R), to_np(R0.double() + ref)) < 2e-2
 
 
-@pytest.mark.parametrize("M,N,K", [(256, 512, 4096), (384, 128, 8192), (64, 96, 1024)])
+@pytest.mark.parametrize("M,N,K", [(256, 512, 4096), (384, 128, 8192), (64, 96, 1024),
+                                   (512, 512, 8192), (520, 776, 8192)])
 def test_gemm_tn_split_k(M, N, K):
     """Weight-gradient shapes: few output tiles, long reduction."""
     A, B = rnd_in((K, M), 13), rnd_in((K, N), 14)
@@ -153,6 +154,45 @@ def test_gemm_epilogues(dt, shape):
     assert rel_err(to_np(Cu), u) < tol
     assert rel_err(to_np(Ca), num.rnd(np.maximum(u, 0) ** 2)) < tol
     assert rel_err(to_np(Cd), num.rnd(acc * 2 * np.maximum(U, 0))) < tol
+
+
+@pytest.mark.parametrize("op", [G.GEMM_NT, G.GEMM_NN, G.GEMM_TN])
+def test_gemm_direct_to_lds_epilogues(op):
+    """A product large enough for the direct-to-LDS kernel (>= 2^31 multiply-
+    adds, K % 64 == 0), ragged in M and N, through every epilogue."""
+    M, N, K = 1288, 1032, 2048
+    say("gemm dma", op, M, N, K)
+    num = _Num("bf16emu")
+    Ash = (M, K) if op != G.GEMM_TN else (K, M)
+    Bsh = (N, K) if op == G.GEMM_NT else (K, N)
+    A, B = rnd_in(Ash, 31), rnd_in(Bsh, 32)
+    acc = _gemm_ref(op, A, B)
+    R, U = rnd_in((M, N), 33, 4.0), rnd_in((M, N), 34)
+    tA, tB = dev(A, torch.bfloat16), dev(B, torch.bfloat16)
+    lda, ldb = Ash[1], Bsh[1]
+    bf = torch.bfloat16
+
+    def run(epi, C, aux=None):
+        G.k_gemm(op, M, N, K, tA, lda, tB, ldb, C, N, epi, aux, G.BF16)
+        return C
+
+    Cs = run(G.EPI_STORE, torch.zeros(M, N, dtype=bf, device=DEV))
+    Cf = run(G.EPI_F32, torch.zeros(M, N, dtype=torch.float32, device=DEV))
+    Ca = run(G.EPI_F32_ACC, torch.full((M, N), 0.25, dtype=torch.float32, device=DEV))
+    Cr = run(G.EPI_RESADD, dev(R, bf))
+    Ca2 = torch.zeros(M, N, dtype=bf, device=DEV)
+    Cu = run(G.EPI_RELU2, torch.zeros(M, N, dtype=bf, device=DEV), Ca2)
+    Cd = run(G.EPI_DRELU2, torch.zeros(M, N, dtype=bf, device=DEV), dev(U, bf))
+    torch.cuda.synchronize()
+    acc32 = acc.astype(np.float32)
+    assert rel_err(to_np(Cf), acc) < 1e-5
+    assert rel_err(to_np(Ca), acc + 0.25) < 1e-5
+    assert rel_err(to_np(Cs), acc) < 8e-3
+    assert rel_err(to_np(Cr), num.rnd(R + acc32)) < 2e-2
+    u = num.rnd(acc32)
+    assert rel_err(to_np(Cu), u) < 2e-2
+    assert rel_err(to_np(Ca2), num.rnd(np.maximum(u, 0) ** 2)) < 2e-2
+    assert rel_err(to_np(Cd), num.rnd(acc32 * 2 * np.maximum(U, 0))) < 2e-2
 
 
 # --------------------------------------------------------------- RMSNorm
