@@ -13,18 +13,18 @@ __device__ __forceinline__ float bf2f(bf16 v) {
   return __uint_as_float(((uint32_t)v) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even (finite inputs; a NaN stays a
-// NaN because the quiet bit survives the shift).
-__device__ __forceinline__ bf16 f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16)(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16x2 (low half = a), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack2bf(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// Two fp32 -> packed bf16x2 (low half = a).
-__device__ __forceinline__ uint32_t pack2bf(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
-}
+// fp32 -> bf16, round to nearest even.
+__device__ __forceinline__ bf16 f2bf(float f) { return (bf16)(pack2bf(f, 0.f) & 0xFFFFu); }
 
 // Storage-type load/store (float or bf16 bits).
 __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }

@@ -133,14 +133,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float mn = fmaxf(m[qb], mx);
         const float ms = mn == -INFINITY ? 0.f : mn;   // row with nothing visible yet
-        const float alpha = exp2f(m[qb] - ms);
+        const float alpha = __builtin_amdgcn_exp2f(m[qb] - ms);
         m[qb] = mn;
         float ls = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float p = exp2f(s[kb][qb][r] - ms);
+            const float p = __builtin_amdgcn_exp2f(s[kb][qb][r] - ms);
             s[kb][qb][r] = p;
             ls += p;
           }
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
           const float L2 = Ls[qi], Dq = Dl[qi];
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
-            float p = exp2f(s[qb][kb][r] * sl2 - L2);
+            float p = __builtin_amdgcn_exp2f(s[qb][kb][r] * sl2 - L2);
             if (!full) {
               const int d = q0 + qi - (kw + 16 * kb + lr);
               if (d < 0 || d > W) p = 0.f;
@@ -496,7 +496,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(const bf16* __restrict__
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float p = exp2f(s[kb][qb][r] * sl2 - L2[qb]);
+            float p = __builtin_amdgcn_exp2f(s[kb][qb][r] * sl2 - L2[qb]);
             if (!full) {
               const int d = qw + 16 * qb + lr - (k0 + 16 * kb + 4 * g + r);
               if (d < 0 || d > W) p = 0.f;
