@@ -18,6 +18,7 @@
 //   accumulators to the next MFMA without an LDS round trip.
 #pragma once
 #include "common.h"
+#include "dma.h"
 
 namespace gk {
 namespace attn {
@@ -140,6 +141,55 @@ __device__ __forceinline__ bf16x8_t rfrag(const bf16* s, int row, int ks, int g)
 // 8 contraction values of a T tile: head-dim row `hrow`, 32-row chunk `ch`.
 __device__ __forceinline__ bf16x8_t tfrag(const bf16* s, int hrow, int ch, int g) {
   return *(const bf16x8_t*)(s + toff(hrow, 32 * ch + 8 * g));
+}
+
+
+// ------------------------------------------------ buffer-to-LDS staged tiles
+// A [64 rows][128] tile as it sits in memory (256-byte rows, no padding),
+// filled by buffer loads straight into LDS.  The 16-byte chunk c of row r
+// is stored at chunk position c ^ dsw(r): 16-row fragment reads (one chunk
+// per row) and transposing reads (8 consecutive rows, 32 bytes each, per 32
+// lanes) both land in distinct bank slots.
+__device__ __forceinline__ int dsw(int r) { return (2 * (r & 7)) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int doff(int r, int col) {
+  return r * HD + 8 * ((col >> 3) ^ dsw(r)) + (col & 7);
+}
+
+// Loads rows [row0, row0 + 64) of a [T][ld] bf16 matrix (128 columns from
+// `base`) into a tile with the 4 waves of a workgroup: 4 x 1 KB per wave.
+// Rows at or past T read as zeros.
+struct TileDma {
+  i32x4_t rsrc;
+  uint32_t voff, ldb;
+  __device__ __forceinline__ void init(const bf16* base, int64_t ld, int T, int wave, int lane) {
+    rsrc = make_rsrc(base, ((int64_t)(T - 1) * ld + HD) * 2);
+    ldb = (uint32_t)(ld * 2);
+    const int row = 4 * wave + (lane >> 4), p = lane & 15;
+    voff = (uint32_t)row * ldb + 16u * (uint32_t)(p ^ dsw(row));
+  }
+  __device__ __forceinline__ void issue(int row0, bf16* tile, int wave) const {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_void_t*)tile + 1024u * (uint32_t)wave);
+    const uint32_t s0 = (uint32_t)row0 * ldb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(rsrc, lds + 4096u * i, voff + s0 + 16u * ldb * i);
+  }
+};
+
+// 8 contraction values along the columns: row `row`, columns 32 ks + 8 g ..
+__device__ __forceinline__ bf16x8_t dfrag_row(const bf16* t, int row, int ks, int g) {
+  return *(const bf16x8_t*)(t + doff(row, 32 * ks + 8 * g));
+}
+
+// 8 contraction values along the rows for column c0 + (lane % 16): rows
+// ka .. ka+3 then kb .. kb+3 (two transposing reads).
+__device__ __forceinline__ bf16x8_t dfrag_col(const bf16* t, int c0, int ka, int kb, int l16) {
+  const int r = l16 >> 2, c = c0 + 4 * (l16 & 3);
+  const v4s_t x = tr16(t + doff(ka + r, c));
+  const v4s_t y = tr16(t + doff(kb + r, c));
+  typedef short v8s_t __attribute__((ext_vector_type(8)));
+  const v8s_t v = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 
 }  // namespace attn

@@ -38,8 +38,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
                                                           bf16* __restrict__ o,
                                                           float* __restrict__ lse, int T, int H,
                                                           int Hkv, int W) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[TR * LDR];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[HD * LDT];
+  // two stages of (K tile, V tile), filled by buffer loads straight into LDS
+  __shared__ __attribute__((aligned(16))) bf16 kv[2][2][TR * HD];
 
   const int nqb = (T + FWD_BQ - 1) / FWD_BQ;
   const int qblk = nqb - 1 - (int)blockIdx.x;          // long rows first
@@ -47,14 +47,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
   const int kvh = h / (H / Hkv);
   const int64_t ldq = (int64_t)(H + 2 * Hkv) * HD;
   const bf16* rowbase = qkv + (int64_t)b * T * ldq;
-  const bf16* kbase = rowbase + (int64_t)(H + kvh) * HD;
-  const bf16* vbase = rowbase + (int64_t)(H + Hkv + kvh) * HD;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, lr = lane & 15;
   const int q0 = qblk * FWD_BQ;
   const int qw = q0 + wave * QW;                       // this wave's first query
   const float sl2 = kLog2e / sqrtf((float)HD);        // scores in log2 units
+
+  TileDma kd, vd;
+  kd.init(rowbase + (int64_t)(H + kvh) * HD, ldq, T, wave, lane);
+  vd.init(rowbase + (int64_t)(H + Hkv + kvh) * HD, ldq, T, wave, lane);
+
+  int klo, khi;
+  key_range(q0, min(q0 + FWD_BQ, T) - 1, W, klo, khi);
+  const int kt0 = klo / TR, kt1 = khi / TR;
+  kd.issue(kt0 * TR, kv[0][0], wave);
+  vd.issue(kt0 * TR, kv[0][1], wave);
 
   // this wave's queries as MFMA Y operands: qf[qb][ks]
   bf16x8_t qf[2][4];
@@ -68,6 +76,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
       qf[qb][ks] = __builtin_bit_cast(bf16x8_t, u);
     }
   }
+  // running max (raw score units) and sum per query
   float m[2], l[2];
   f32x4_t oacc[8][2];
 #pragma unroll
@@ -78,90 +87,88 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
     for (int hb = 0; hb < 8; ++hb) oacc[hb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  int klo, khi;
-  key_range(q0, min(q0 + FWD_BQ, T) - 1, W, klo, khi);
-  const int kt0 = klo / TR, kt1 = khi / TR;
-
-  TileRegs<256> kr, vr;
-  kr.load_rows(kbase, ldq, kt0 * TR, T);
-  vr.load_patches(vbase, ldq, kt0 * TR, T);
-
   for (int kt = kt0; kt <= kt1; ++kt) {
-    const int k0 = kt * TR;
-    kr.store_rows(Ks);
-    vr.store_patches_T(Vt);
-    __syncthreads();
-    if (kt < kt1) {                                    // prefetch the next tile
-      kr.load_rows(kbase, ldq, k0 + TR, T);
-      vr.load_patches(vbase, ldq, k0 + TR, T);
+    const int k0 = kt * TR, st = (kt - kt0) & 1;
+    dma_wait();
+    __syncthreads();                                   // stage st filled, stage st^1 free
+    if (kt < kt1) {
+      kd.issue(k0 + TR, kv[st ^ 1][0], wave);
+      vd.issue(k0 + TR, kv[st ^ 1][1], wave);
     }
+    const bf16* Ks = kv[st][0];
+    const bf16* Vs = kv[st][1];
     // pairs of this wave: queries [qw, qw+31], keys [k0, k0+63]
     const bool any = (qw + QW - 1 >= k0) && (qw - (k0 + TR - 1) <= W) && qw < T;
     const bool full = (qw >= k0 + TR - 1) && (qw + QW - 1 - k0 <= W);
-    if (any) {
-      f32x4_t s[4][2];
+    if (!any) continue;
+    f32x4_t s[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const bf16x8_t kf0 = dfrag_row(Ks, 16 * kb + lr, 0, g);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma(kf0, qf[qb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int ks = 1; ks < 4; ++ks) {
+        const bf16x8_t kf = dfrag_row(Ks, 16 * kb + lr, ks, g);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma(kf, qf[qb][ks], s[kb][qb]);
+      }
+    }
+    bool grew = false;
+    float alpha[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qi = qw + 16 * qb + lr;
+      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const bf16x8_t kf = rfrag(Ks, 16 * kb + lr, ks, g);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma(kf, qf[qb][ks], s[kb][qb]);
-        }
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int qi = qw + 16 * qb + lr;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float v = s[kb][qb][r] * sl2;
-            if (!full) {
-              const int d = qi - (k0 + 16 * kb + 4 * g + r);
-              if (d < 0 || d > W) v = -INFINITY;
-            }
-            s[kb][qb][r] = v;
-            mx = fmaxf(mx, v);
+        for (int r = 0; r < 4; ++r) {
+          if (!full) {
+            const int d = qi - (k0 + 16 * kb + 4 * g + r);
+            if (d < 0 || d > W) s[kb][qb][r] = -INFINITY;
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mn = fmaxf(m[qb], mx);
-        const float ms = mn == -INFINITY ? 0.f : mn;   // row with nothing visible yet
-        const float alpha = __builtin_amdgcn_exp2f(m[qb] - ms);
-        m[qb] = mn;
-        float ls = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = __builtin_amdgcn_exp2f(s[kb][qb][r] - ms);
-            s[kb][qb][r] = p;
-            ls += p;
-          }
-        l[qb] = l[qb] * alpha + ls;
-#pragma unroll
-        for (int hb = 0; hb < 8; ++hb) oacc[hb][qb] *= alpha;
-      }
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        bf16x8_t pf[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) pf[qb] = pack8(s[2 * ch][qb], s[2 * ch + 1][qb]);
-#pragma unroll
-        for (int hb = 0; hb < 8; ++hb) {
-          const bf16x8_t vf = tfrag(Vt, 16 * hb + lr, ch, g);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) oacc[hb][qb] = mfma(vf, pf[qb], oacc[hb][qb]);
+          mx = fmaxf(mx, s[kb][qb][r]);
         }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m[qb], mx);
+      const bool up = mn > m[qb];
+      grew |= up;
+      // exponent offset; a query with nothing visible yet keeps offset 0
+      const float off = mn == -INFINITY ? 0.f : mn * sl2;
+      alpha[qb] = up ? __builtin_amdgcn_exp2f(fmaf(m[qb], sl2, -off)) : 1.f;
+      m[qb] = mn;
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], sl2, -off));
+          s[kb][qb][r] = p;
+          ls += p;
+        }
+      l[qb] = fmaf(l[qb], alpha[qb], ls);
+    }
+    // rescale the output only when some running max of the wave moved
+    if (__builtin_amdgcn_ballot_w64(grew)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int hb = 0; hb < 8; ++hb) oacc[hb][qb] *= alpha[qb];
+    }
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      bf16x8_t pf[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) pf[qb] = pack8(s[2 * ch][qb], s[2 * ch + 1][qb]);
+#pragma unroll
+      for (int hb = 0; hb < 8; ++hb) {
+        const bf16x8_t vf = dfrag_col(Vs, 16 * hb, 32 * ch + 4 * g, 32 * ch + 16 + 4 * g, lr);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) oacc[hb][qb] = mfma(vf, pf[qb], oacc[hb][qb]);
       }
     }
-    __syncthreads();
   }
 
   // normalise and store: lane holds O[query][16 hb + 4 g + r]
@@ -181,7 +188,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
       u.y = pack2bf(oacc[hb][qb][2] * inv, oacc[hb][qb][3] * inv);
       *(uint2*)(orow + 16 * hb + 4 * g) = u;
     }
-    if (g == 0) lse[((int64_t)b * H + h) * T + qi] = (m[qb] + log2f(lt)) * kLn2;
+    if (g == 0) lse[((int64_t)b * H + h) * T + qi] = (m[qb] * sl2 + log2f(lt)) * kLn2;
   }
 }
 

@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "dma.h"
 #include "gemm_epi.h"
 #include "gemm_mfma.h"
 
@@ -448,9 +449,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mfma_db(int64_t M, int64_t N, i
 //
 // K must be a multiple of 64 (no zero fill: rows past M or N are clamped to
 // valid memory and their results dropped).
-typedef short v4s_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
 
@@ -466,33 +464,9 @@ __device__ __forceinline__ int swz_mn(int k) {
 // the end of the matrix, so lanes past the last row or k read zeros; columns
 // past N alias into the next row and only feed results that are dropped.
 // One per-lane byte offset per operand: the NB load instructions of a wave
-// differ by a uniform step (64 rows, or 2048 / R k-rows, with the same
-// swizzle), which goes into the scalar offset.
-static constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, gfx9 family
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ i32x4_t make_rsrc(const bf16* base, int64_t bytes) {
-  const int64_t lim = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
-  const uint64_t a = (uint64_t)base;
-  i32x4_t r;
-  r[0] = (int)(uint32_t)a;
-  r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);   // stride 0
-  r[2] = (int)(uint32_t)lim;
-  r[3] = kRsrcWord3;
-  return r;
-}
-
-// One 16-byte-per-lane buffer load into the 1 KB LDS block at `lds` (a wave-
-// uniform LDS byte address).  Written as asm so the compiler does not track
-// it: the waits for these loads are the explicit vmcnt(0) before each
-// barrier of the main loop, and reads of the other stage never wait for them.
-__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory", "m0");
-}
-
+// differ by a uniform step (64 rows, or 4096 / R k-rows, with the same
+// swizzle), added to it per instruction (the whole offset stays in the
+// vector operand, which is what the range check sees).
 template <int R, bool TRANS>
 struct DmaPlan {
   static constexpr int NB = R / 64;                        // load instructions per wave
@@ -522,7 +496,7 @@ struct DmaPlan {
     const uint32_t base = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(lds_void_t*)stage + 1024u * (uint32_t)wave);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) dma16(rsrc, base + 8192u * i, voff, kofs + i * step);
+    for (int i = 0; i < NB; ++i) dma16(rsrc, base + 8192u * i, voff + kofs + i * step);
   }
 };
 
@@ -541,7 +515,7 @@ __device__ __forceinline__ bf16x8_t frag(const bf16* st, int base, int kk, int l
     for (int hh = 0; hh < 2; ++hh) {
       const int k = kk + 8 * g + 4 * hh + (l16 >> 2);
       const bf16* p = st + k * R + 8 * (c ^ swz_mn<R>(k)) + (n & 7);
-      h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)p);
+      h[hh] = tr16(p);
     }
     typedef short v8s_t __attribute__((ext_vector_type(8)));
     v8s_t v = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
