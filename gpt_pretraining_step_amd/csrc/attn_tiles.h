@@ -159,15 +159,15 @@ __device__ __forceinline__ int doff(int r, int col) {
 // `base`) into a tile with the 4 waves of a workgroup: 4 x 1 KB per wave.
 // Rows at or past T read as zeros.
 struct TileDma {
-  i32x4_t rsrc;
   uint32_t voff, ldb;
-  __device__ __forceinline__ void init(const bf16* base, int64_t ld, int T, int wave, int lane) {
-    rsrc = make_rsrc(base, ((int64_t)(T - 1) * ld + HD) * 2);
+  __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
     ldb = (uint32_t)(ld * 2);
     const int row = 4 * wave + (lane >> 4), p = lane & 15;
     voff = (uint32_t)row * ldb + 16u * (uint32_t)(p ^ dsw(row));
   }
-  __device__ __forceinline__ void issue(int row0, bf16* tile, int wave) const {
+  __device__ __forceinline__ void issue(const bf16* base, int T, int row0, bf16* tile,
+                                        int wave) const {
+    const i32x4_t rsrc = make_rsrc(base, ((int64_t)(T - 1) * (ldb / 2) + HD) * 2);
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(lds_void_t*)tile + 1024u * (uint32_t)wave);
     const uint32_t s0 = (uint32_t)row0 * ldb;
@@ -175,6 +175,16 @@ struct TileDma {
     for (int i = 0; i < 4; ++i) dma16(rsrc, lds + 4096u * i, voff + s0 + 16u * ldb * i);
   }
 };
+
+// 64 consecutive floats v[row0 ..] of a length-T vector into LDS (one wave,
+// one 1 KB block: lanes 0..15 carry the data, the rest write zeros after
+// it).  Entries at or past T read as zeros.
+__device__ __forceinline__ void dma_vec64(const float* v, int T, int row0, float* dst, int lane) {
+  const i32x4_t rsrc = make_rsrc(v, (int64_t)T * 4);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)dst);
+  const uint32_t off = lane < 16 ? (uint32_t)row0 * 4u + 16u * (uint32_t)lane : 0xFFFFFFF0u;
+  dma16(rsrc, lds, off);
+}
 
 // 8 contraction values along the columns: row `row`, columns 32 ks + 8 g ..
 __device__ __forceinline__ bf16x8_t dfrag_row(const bf16* t, int row, int ks, int g) {

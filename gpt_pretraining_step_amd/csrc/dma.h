@@ -25,7 +25,7 @@ __device__ __forceinline__ v4s_t tr16(const bf16* p) {
 static constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, gfx9 family
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ i32x4_t make_rsrc(const bf16* base, int64_t bytes) {
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, int64_t bytes) {
   const int64_t lim = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
   const uint64_t a = (uint64_t)base;
   i32x4_t r;

@@ -54,15 +54,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
   const int qw = q0 + wave * QW;                       // this wave's first query
   const float sl2 = kLog2e / sqrtf((float)HD);        // scores in log2 units
 
-  TileDma kd, vd;
-  kd.init(rowbase + (int64_t)(H + kvh) * HD, ldq, T, wave, lane);
-  vd.init(rowbase + (int64_t)(H + Hkv + kvh) * HD, ldq, T, wave, lane);
+  const bf16* kbase = rowbase + (int64_t)(H + kvh) * HD;
+  const bf16* vbase = rowbase + (int64_t)(H + Hkv + kvh) * HD;
+  TileDma td;
+  td.init(ldq, wave, lane);
 
   int klo, khi;
   key_range(q0, min(q0 + FWD_BQ, T) - 1, W, klo, khi);
   const int kt0 = klo / TR, kt1 = khi / TR;
-  kd.issue(kt0 * TR, kv[0][0], wave);
-  vd.issue(kt0 * TR, kv[0][1], wave);
+  td.issue(kbase, T, kt0 * TR, kv[0][0], wave);
+  td.issue(vbase, T, kt0 * TR, kv[0][1], wave);
 
   // this wave's queries as MFMA Y operands: qf[qb][ks]
   bf16x8_t qf[2][4];
@@ -92,8 +93,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
     dma_wait();
     __syncthreads();                                   // stage st filled, stage st^1 free
     if (kt < kt1) {
-      kd.issue(k0 + TR, kv[st ^ 1][0], wave);
-      vd.issue(k0 + TR, kv[st ^ 1][1], wave);
+      td.issue(kbase, T, k0 + TR, kv[st ^ 1][0], wave);
+      td.issue(vbase, T, k0 + TR, kv[st ^ 1][1], wave);
     }
     const bf16* Ks = kv[st][0];
     const bf16* Vs = kv[st][1];
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
         for (int r = 0; r < 4; ++r) {
           if (!full) {
             const int d = qi - (k0 + 16 * kb + 4 * g + r);
-            if (d < 0 || d > W) s[kb][qb][r] = -INFINITY;
+            s[kb][qb][r] = (unsigned)d > (unsigned)W ? -INFINITY : s[kb][qb][r];
           }
           mx = fmaxf(mx, s[kb][qb][r]);
         }
@@ -242,9 +243,11 @@ __global__ __launch_bounds__(256) void k_attn_delta(const bf16* __restrict__ o,
 
 // dK, dV of 128 keys of one KV head (4 waves x 32 keys), summed over the G
 // query heads of the group and every 64-query tile that sees these keys.
-// Scores are formed queries x keys (X = Q tile, Y = K in registers), so each
-// lane owns one key; P and dS feed dV^T += dO^T P and dK^T += Q^T dS from
-// registers, with dO and Q staged transposed.
+// Scores are formed queries x keys (X = Q tile rows, Y = K in registers), so
+// each lane owns one key; a 64-query tile is taken in two 32-query halves
+// (fewer live score registers: two waves per SIMD), and P and dS of a half
+// feed dV^T += dO^T P and dK^T += Q^T dS from registers, with the dO^T and
+// Q^T fragments gathered by transposing LDS reads.
 static constexpr int KV_BK = NW * 32;          // keys per workgroup
 
 __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict__ qkv,
@@ -253,11 +256,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
                                                          const float* __restrict__ delta,
                                                          bf16* __restrict__ dqkv, int T, int H,
                                                          int Hkv, int W) {
-  __shared__ __attribute__((aligned(16))) bf16 Qs[TR * LDR];
-  __shared__ __attribute__((aligned(16))) bf16 Qt[HD * LDT];
-  __shared__ __attribute__((aligned(16))) bf16 Ds[TR * LDR];
-  __shared__ __attribute__((aligned(16))) bf16 Dt[HD * LDT];
-  __shared__ float Ls[TR], Dl[TR];
+  __shared__ __attribute__((aligned(16))) bf16 qd[2][2][TR * HD];   // stages of (Q, dO)
+  __shared__ __attribute__((aligned(16))) float ldl[2][2][256];      // stages of (lse, delta)
 
   const int nkb = (T + KV_BK - 1) / KV_BK;
   const int kblk = nkb - 1 - (int)blockIdx.x;
@@ -271,6 +271,27 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
   const int k0 = kblk * KV_BK;
   const int kw = k0 + 32 * wave;                      // this wave's first key
   const float sl2 = kLog2e / sqrtf((float)HD);
+
+  // queries that see keys [k0, k0+127]: [k0, k0 + 127 + W]
+  const int qhi = (int)min((int64_t)T - 1, (int64_t)k0 + KV_BK - 1 + W);
+  const int qt0 = k0 / TR, nqt = qhi / TR - qt0 + 1;
+  const int iters = G * nqt;
+
+  TileDma tq, to;
+  tq.init(ldq, wave, lane);
+  to.init(ldo, wave, lane);
+  auto issue = [&](int it, int st) {
+    const int hh = kvh * G + it / nqt;
+    const int qq = (qt0 + it % nqt) * TR;
+    tq.issue(rowbase + (int64_t)hh * HD, T, qq, qd[st][0], wave);
+    to.issue(obase + (int64_t)hh * HD, T, qq, qd[st][1], wave);
+    if (wave == 0) {
+      const int64_t li = ((int64_t)b * H + hh) * T;
+      dma_vec64(lse + li, T, qq, ldl[st][0], lane);
+      dma_vec64(delta + li, T, qq, ldl[st][1], lane);
+    }
+  };
+  issue(0, 0);
 
   bf16x8_t kf[2][4], vf[2][4];
 #pragma unroll
@@ -294,93 +315,75 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
       dv[hb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-  // queries that see keys [k0, k0+127]: [k0, k0 + 127 + W]
-  const int qhi = (int)min((int64_t)T - 1, (int64_t)k0 + KV_BK - 1 + W);
-  const int qt0 = k0 / TR, nqt = qhi / TR - qt0 + 1;
-  const int iters = G * nqt;
-
-  TileRegs<256> qr, dr;
-  {
-    const int h = kvh * G;
-    qr.load_patches(rowbase + (int64_t)h * HD, ldq, qt0 * TR, T);
-    dr.load_patches(obase + (int64_t)h * HD, ldo, qt0 * TR, T);
-  }
   for (int it = 0; it < iters; ++it) {
-    const int h = kvh * G + it / nqt;
-    const int q0 = (qt0 + it % nqt) * TR;
-    qr.store_patches_R(Qs);
-    qr.store_patches_T(Qt);
-    dr.store_patches_R(Ds);
-    dr.store_patches_T(Dt);
-    if (threadIdx.x < TR) {
-      const int q = q0 + threadIdx.x;
-      const int64_t li = ((int64_t)b * H + h) * T + q;
-      Ls[threadIdx.x] = q < T ? lse[li] * kLog2e : INFINITY;   // no probability mass
-      Dl[threadIdx.x] = q < T ? delta[li] : 0.f;
-    }
+    const int q0 = (qt0 + it % nqt) * TR, st = it & 1;
+    dma_wait();
     __syncthreads();
-    if (it + 1 < iters) {
-      const int hn = kvh * G + (it + 1) / nqt;
-      const int qn = (qt0 + (it + 1) % nqt) * TR;
-      qr.load_patches(rowbase + (int64_t)hn * HD, ldq, qn, T);
-      dr.load_patches(obase + (int64_t)hn * HD, ldo, qn, T);
-    }
-    // pairs of this wave: queries [q0, q0+63], keys [kw, kw+31]
-    const bool any = (q0 + TR - 1 >= kw) && (q0 - (kw + 31) <= W) && kw < T;
-    const bool full = (q0 >= kw + 31) && (q0 + TR - 1 - kw <= W);
-    if (any) {
-      f32x4_t s[4][2], dp[4][2];
+    if (it + 1 < iters) issue(it + 1, st ^ 1);
+    const bf16* Qs = qd[st][0];
+    const bf16* Ds = qd[st][1];
+    const float* Ls = ldl[st][0];
+    const float* Dl = ldl[st][1];
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb)
+    for (int hq = 0; hq < 2; ++hq) {
+      // pairs of this wave: queries [qa, qa+31], keys [kw, kw+31]
+      const int qa = q0 + 32 * hq;
+      const bool any = (qa + 31 >= kw) && (qa - (kw + 31) <= W) && kw < T && qa < T;
+      const bool full = (qa >= kw + 31) && (qa + 31 - kw <= W);
+      if (!any) continue;
+      f32x4_t s[2][2], dp[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int row = 32 * hq + 16 * qb + lr;
+        const bf16x8_t qx0 = dfrag_row(Qs, row, 0, g);
+        const bf16x8_t dx0 = dfrag_row(Ds, row, 0, g);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          s[qb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          dp[qb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          s[qb][kb] = mfma(qx0, kf[kb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+          dp[qb][kb] = mfma(dx0, vf[kb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
         }
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-          const bf16x8_t qx = rfrag(Qs, 16 * qb + lr, ks, g);
-          const bf16x8_t dx = rfrag(Ds, 16 * qb + lr, ks, g);
+        for (int ks = 1; ks < 4; ++ks) {
+          const bf16x8_t qx = dfrag_row(Qs, row, ks, g);
+          const bf16x8_t dx = dfrag_row(Ds, row, ks, g);
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
             s[qb][kb] = mfma(qx, kf[kb][ks], s[qb][kb]);
             dp[qb][kb] = mfma(dx, vf[kb][ks], dp[qb][kb]);
           }
         }
-      // P = exp(S - lse), dS = P (dP - Delta); lane: query 16qb+4g+r, key 16kb+lr
+      }
+      // P = exp(S - lse), dS = P (dP - Delta); lane: query 32hq+16qb+4g+r, key 16kb+lr
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb)
+      for (int qb = 0; qb < 2; ++qb) {
+        const f32x4_t L2 = *(const f32x4_t*)(Ls + 32 * hq + 16 * qb + 4 * g) * kLog2e;
+        const f32x4_t Dq = *(const f32x4_t*)(Dl + 32 * hq + 16 * qb + 4 * g);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int qi = 16 * qb + 4 * g + r;
-          const float L2 = Ls[qi], Dq = Dl[qi];
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
-            float p = __builtin_amdgcn_exp2f(s[qb][kb][r] * sl2 - L2);
+            float p = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], sl2, -L2[r]));
             if (!full) {
-              const int d = q0 + qi - (kw + 16 * kb + lr);
-              if (d < 0 || d > W) p = 0.f;
+              const int d = qa + 16 * qb + 4 * g + r - (kw + 16 * kb + lr);
+              p = (unsigned)d > (unsigned)W ? 0.f : p;
             }
             s[qb][kb][r] = p;
-            dp[qb][kb][r] = p * (dp[qb][kb][r] - Dq);
+            dp[qb][kb][r] = p * (dp[qb][kb][r] - Dq[r]);
           }
         }
+      }
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t pp = pack8(s[0][kb], s[1][kb]);
+        const bf16x8_t ps = pack8(dp[0][kb], dp[1][kb]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8_t pp = pack8(s[2 * c][kb], s[2 * c + 1][kb]);
-          const bf16x8_t ps = pack8(dp[2 * c][kb], dp[2 * c + 1][kb]);
-#pragma unroll
-          for (int hb = 0; hb < 8; ++hb) {
-            dv[hb][kb] = mfma(tfrag(Dt, 16 * hb + lr, c, g), pp, dv[hb][kb]);
-            dk[hb][kb] = mfma(tfrag(Qt, 16 * hb + lr, c, g), ps, dk[hb][kb]);
-          }
+        for (int hb = 0; hb < 8; ++hb) {
+          const int ka = 32 * hq + 4 * g, kb2 = 32 * hq + 16 + 4 * g;
+          dv[hb][kb] = mfma(dfrag_col(Ds, 16 * hb, ka, kb2, lr), pp, dv[hb][kb]);
+          dk[hb][kb] = mfma(dfrag_col(Qs, 16 * hb, ka, kb2, lr), ps, dk[hb][kb]);
         }
+      }
     }
-    __syncthreads();
   }
   // lane holds dK^T / dV^T [16hb + 4g + r][key 16kb + lr]
   const float scale = 1.0f / sqrtf((float)HD);
@@ -404,17 +407,15 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
 }
 
 // dQ of 128 queries of one head (4 waves x 32), over the key tiles they see.
-// Scores keys x queries as in the forward; dS feeds dQ^T += K^T dS with K
-// staged transposed.
+// Scores keys x queries as in the forward; dS feeds dQ^T += K^T dS with the
+// K^T fragments gathered from the K tile by transposing LDS reads.
 __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(const bf16* __restrict__ qkv,
                                                         const bf16* __restrict__ dout,
                                                         const float* __restrict__ lse,
                                                         const float* __restrict__ delta,
                                                         bf16* __restrict__ dqkv, int T, int H,
                                                         int Hkv, int W) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[TR * LDR];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[HD * LDT];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[TR * LDR];
+  __shared__ __attribute__((aligned(16))) bf16 kv[2][2][TR * HD];   // stages of (K, V)
 
   const int nqb = (T + FWD_BQ - 1) / FWD_BQ;
   const int qblk = nqb - 1 - (int)blockIdx.x;
@@ -429,6 +430,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(const bf16* __restrict__
   const int q0 = qblk * FWD_BQ;
   const int qw = q0 + wave * QW;
   const float sl2 = kLog2e / sqrtf((float)HD);
+
+  TileDma td;
+  td.init(ldq, wave, lane);
+  int klo, khi;
+  key_range(q0, min(q0 + FWD_BQ, T) - 1, W, klo, khi);
+  const int kt0 = klo / TR, kt1 = khi / TR;
+  td.issue(kbase, T, kt0 * TR, kv[0][0], wave);
+  td.issue(vbase, T, kt0 * TR, kv[0][1], wave);
 
   bf16x8_t qf[2][4], df[2][4];
   float L2[2], Dq[2];
@@ -455,73 +464,69 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(const bf16* __restrict__
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) dq[hb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  int klo, khi;
-  key_range(q0, min(q0 + FWD_BQ, T) - 1, W, klo, khi);
-  const int kt0 = klo / TR, kt1 = khi / TR;
-  TileRegs<256> kr, vr;
-  kr.load_patches(kbase, ldq, kt0 * TR, T);
-  vr.load_rows(vbase, ldq, kt0 * TR, T);
   for (int kt = kt0; kt <= kt1; ++kt) {
-    const int k0 = kt * TR;
-    kr.store_patches_R(Ks);
-    kr.store_patches_T(Kt);
-    vr.store_rows(Vs);
+    const int k0 = kt * TR, st = (kt - kt0) & 1;
+    dma_wait();
     __syncthreads();
     if (kt < kt1) {
-      kr.load_patches(kbase, ldq, k0 + TR, T);
-      vr.load_rows(vbase, ldq, k0 + TR, T);
+      td.issue(kbase, T, k0 + TR, kv[st ^ 1][0], wave);
+      td.issue(vbase, T, k0 + TR, kv[st ^ 1][1], wave);
     }
+    const bf16* Ks = kv[st][0];
+    const bf16* Vs = kv[st][1];
     const bool any = (qw + QW - 1 >= k0) && (qw - (k0 + TR - 1) <= W) && qw < T;
     const bool full = (qw >= k0 + TR - 1) && (qw + QW - 1 - k0 <= W);
-    if (any) {
-      f32x4_t s[4][2];
+    if (!any) continue;
+    f32x4_t s[4][2];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+      const bf16x8_t kx0 = dfrag_row(Ks, 16 * kb + lr, 0, g);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma(kx0, qf[qb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 1; ks < 4; ++ks) {
+        const bf16x8_t kx = dfrag_row(Ks, 16 * kb + lr, ks, g);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const bf16x8_t kx = rfrag(Ks, 16 * kb + lr, ks, g);
+        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma(kx, qf[qb][ks], s[kb][qb]);
+      }
+    }
+    // lane: key 16kb + 4g + r, query 16qb + lr
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma(kx, qf[qb][ks], s[kb][qb]);
-        }
-      // lane: key 16kb + 4g + r, query 16qb + lr
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x4_t dp[2];
+      const bf16x8_t vx0 = dfrag_row(Vs, 16 * kb + lr, 0, g);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        f32x4_t dp[2];
+      for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma(vx0, df[qb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) dp[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 1; ks < 4; ++ks) {
+        const bf16x8_t vx = dfrag_row(Vs, 16 * kb + lr, ks, g);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8_t vx = rfrag(Vs, 16 * kb + lr, ks, g);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma(vx, df[qb][ks], dp[qb]);
-        }
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float p = __builtin_amdgcn_exp2f(s[kb][qb][r] * sl2 - L2[qb]);
-            if (!full) {
-              const int d = qw + 16 * qb + lr - (k0 + 16 * kb + 4 * g + r);
-              if (d < 0 || d > W) p = 0.f;
-            }
-            s[kb][qb][r] = p * (dp[qb][r] - Dq[qb]);
-          }
+        for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma(vx, df[qb][ks], dp[qb]);
       }
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const bf16x8_t ps = pack8(s[2 * c][qb], s[2 * c + 1][qb]);
-#pragma unroll
-          for (int hb = 0; hb < 8; ++hb)
-            dq[hb][qb] = mfma(tfrag(Kt, 16 * hb + lr, c, g), ps, dq[hb][qb]);
+        for (int r = 0; r < 4; ++r) {
+          float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], sl2, -L2[qb]));
+          if (!full) {
+            const int d = qw + 16 * qb + lr - (k0 + 16 * kb + 4 * g + r);
+            p = (unsigned)d > (unsigned)W ? 0.f : p;
+          }
+          s[kb][qb][r] = p * (dp[qb][r] - Dq[qb]);
         }
     }
-    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bf16x8_t ps[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) ps[qb] = pack8(s[2 * c][qb], s[2 * c + 1][qb]);
+#pragma unroll
+      for (int hb = 0; hb < 8; ++hb) {
+        const bf16x8_t kt_ = dfrag_col(Ks, 16 * hb, 32 * c + 4 * g, 32 * c + 16 + 4 * g, lr);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) dq[hb][qb] = mfma(kt_, ps[qb], dq[hb][qb]);
+      }
+    }
   }
   const float scale = 1.0f / sqrtf((float)HD);
 #pragma unroll
