@@ -471,23 +471,31 @@ template <int R, bool TRANS>
 struct DmaPlan {
   static constexpr int NB = R / 64;                        // load instructions per wave
   static constexpr int STEP_ROWS = TRANS ? 4096 / R : 64;  // rows (k or MN) between them
-  static_assert(!TRANS || R == 128 || R == 256, "MN-contiguous stage width");
+  // an MN-contiguous stage of 192 columns has 384-byte rows, which 1 KB load
+  // blocks do not tile evenly: one offset per load instruction there
+  static constexpr bool PER_LOAD = TRANS && R == 192;
+  static constexpr int NV = PER_LOAD ? NB : 1;
+  static_assert(!TRANS || R == 128 || R == 192 || R == 256, "MN-contiguous stage width");
   i32x4_t rsrc;
-  uint32_t voff;
+  uint32_t voff[NV];
   int64_t ld;
   // g: operand base; r0: first MN index of the tile; rows: M or N; K rows
   __device__ __forceinline__ void init(const bf16* g, int64_t ld_, int64_t r0, int64_t rows,
                                        int64_t K, int wave, int lane) {
     ld = ld_;
-    const int o = 1024 * wave + 16 * lane;      // byte offset of this lane in block `wave`
     if constexpr (!TRANS) {
+      const int o = 1024 * wave + 16 * lane;    // byte offset of this lane in block `wave`
       const int row = o >> 7, p = (o >> 4) & 7;
       rsrc = make_rsrc(g + r0 * ld, (rows - r0) * ld * 2);
-      voff = (uint32_t)(row * ld * 2 + 16 * (p ^ swz_k(row)));
+      voff[0] = (uint32_t)(row * ld * 2 + 16 * (p ^ swz_k(row)));
     } else {
-      const int krow = o / (2 * R), p = (o % (2 * R)) >> 4;
       rsrc = make_rsrc(g + r0, (K * ld - r0) * 2);
-      voff = (uint32_t)(krow * ld * 2 + 16 * (p ^ swz_mn<R>(krow)));
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int o = 1024 * (wave + 8 * i) + 16 * lane;
+        const int krow = o / (2 * R), p = (o % (2 * R)) >> 4;
+        voff[i] = (uint32_t)(krow * ld * 2 + 16 * (p ^ swz_mn<R>(krow)));
+      }
     }
   }
   __device__ __forceinline__ void issue(int64_t k0, bf16* stage, int wave) const {
@@ -496,7 +504,8 @@ struct DmaPlan {
     const uint32_t base = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(lds_void_t*)stage + 1024u * (uint32_t)wave);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) dma16(rsrc, base + 8192u * i, voff + kofs + i * step);
+    for (int i = 0; i < NB; ++i)
+      dma16(rsrc, base + 8192u * i, (PER_LOAD ? voff[i] : voff[0] + i * step) + kofs);
   }
 };
 
@@ -813,14 +822,28 @@ static bool dma_ok(const GemmDesc& g) {
 // ~2.1 us per 256x256x64 slice, plus the partial tiles' HBM traffic (written
 // and read once, ~5 TB/s) and the reduce launch; at least 8 K-slices per
 // split.
-static TileMap plan_dma(int64_t M, int64_t N, int64_t K, bool f32out, size_t scratch_bytes) {
+static TileMap plan_dma(int64_t M, int64_t N, int64_t K, bool f32out, size_t scratch_bytes,
+                        int* bn) {
   const int kCU = 256;
   TileMap tm;
   tm.tiles_m = (int)cdiv(M, 256);
   tm.tiles_n = (int)cdiv(N, 256);
   tm.splits = 1;
   tm.k_per_split = K;
-  if (!f32out) return tm;
+  *bn = 256;
+  if (!f32out) {
+    // 256 x 192 tiles when they fill the rounds of 256 blocks better (N a
+    // multiple of 192, e.g. 768 or 2304): fewer idle CUs in the last round
+    if (N % 192 == 0) {
+      const int64_t r256 = cdiv((int64_t)tm.tiles_m * tm.tiles_n, kCU) * 256;
+      const int64_t r192 = cdiv((int64_t)tm.tiles_m * (N / 192), kCU) * 192;
+      if (r192 < r256) {
+        tm.tiles_n = (int)(N / 192);
+        *bn = 192;
+      }
+    }
+    return tm;
+  }
   const int64_t tiles = (int64_t)tm.tiles_m * tm.tiles_n, ksl = K / BK;
   auto cost = [&](int sp) {
     const double rounds = (double)cdiv(tiles * sp, kCU);
@@ -846,7 +869,8 @@ size_t mfma_splitk_bytes(int64_t M, int64_t N, int64_t K) {
   TileMap tm = plan(M, N, K, true, SIZE_MAX, &bm);
   size_t b = tm.splits > 1 ? (size_t)tm.splits * M * N * sizeof(float) : 0;
   if (dma_shape_ok(M, N, K)) {
-    TileMap td = plan_dma(M, N, K, true, SIZE_MAX);
+    int bn;
+    TileMap td = plan_dma(M, N, K, true, SIZE_MAX, &bn);
     if (td.splits > 1) b = std::max(b, (size_t)td.splits * M * N * sizeof(float));
   }
   return b;
@@ -858,9 +882,11 @@ hipError_t mfma_gemm(const GemmDesc& g, hipStream_t s) {
   TileMap tm;
   float* partial = nullptr;
   if (dma_ok(g)) {
-    tm = plan_dma(g.M, g.N, g.K, f32out, scr);
+    int bn;
+    tm = plan_dma(g.M, g.N, g.K, f32out, scr, &bn);
     partial = tm.splits > 1 ? (float*)g.scratch : nullptr;
-    launch_dma<256, 256>(g, tm, partial, s);
+    if (bn == 192) launch_dma<256, 192>(g, tm, partial, s);
+    else launch_dma<256, 256>(g, tm, partial, s);
   } else {
     int BM;
     tm = plan(g.M, g.N, g.K, f32out, scr, &BM);
