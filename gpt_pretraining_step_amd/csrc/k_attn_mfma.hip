@@ -27,6 +27,7 @@ static constexpr int QW = 32;                  // queries per wave (2 blocks of 
 static constexpr int FWD_BQ = NW * QW;         // queries per workgroup
 static constexpr float kLog2e = 1.4426950408889634f;
 static constexpr float kLn2 = 0.6931471805599453f;
+static constexpr float kLazy = 8.0f;           // forward: offset lag allowed (log2 units)
 
 // Inclusive key range [lo, hi] seen by queries [q_lo, q_hi] under window W.
 __device__ __forceinline__ void key_range(int q_lo, int q_hi, int W, int& lo, int& hi) {
@@ -115,29 +116,37 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
         for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma(kf, qf[qb][ks], s[kb][qb]);
       }
     }
+    // mask (tiles on the diagonal or the window edge only: a wave-uniform
+    // branch between two copies of the loop)
+    if (!full) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int d = qw + 16 * qb + lr - (k0 + 16 * kb + 4 * g + r);
+            s[kb][qb][r] = (unsigned)d > (unsigned)W ? -INFINITY : s[kb][qb][r];
+          }
+    }
     bool grew = false;
     float alpha[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int qi = qw + 16 * qb + lr;
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (!full) {
-            const int d = qi - (k0 + 16 * kb + 4 * g + r);
-            s[kb][qb][r] = (unsigned)d > (unsigned)W ? -INFINITY : s[kb][qb][r];
-          }
-          mx = fmaxf(mx, s[kb][qb][r]);
-        }
+        mx = fmaxf(mx, fmaxf(fmaxf(s[kb][qb][0], s[kb][qb][1]), fmaxf(s[kb][qb][2], s[kb][qb][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m[qb], mx);
-      const bool up = mn > m[qb];
+      // The exponent offset m moves only when the tile's maximum exceeds it
+      // by more than kLazy (log2 units), or on the first visible tile: the
+      // probabilities then stay below 2^kLazy, exact in fp32 and in bf16's
+      // relative precision, and the output is rescaled rarely.
+      const bool up = m[qb] == -INFINITY ? mx > -INFINITY : (mx - m[qb]) * sl2 > kLazy;
+      const float mn = up ? mx : m[qb];
       grew |= up;
-      // exponent offset; a query with nothing visible yet keeps offset 0
-      const float off = mn == -INFINITY ? 0.f : mn * sl2;
+      const float off = mn == -INFINITY ? 0.f : mn * sl2;   // nothing visible yet: 0
       alpha[qb] = up ? __builtin_amdgcn_exp2f(fmaf(m[qb], sl2, -off)) : 1.f;
       m[qb] = mn;
       float ls = 0.f;
@@ -354,6 +363,17 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
         }
       }
       // P = exp(S - lse), dS = P (dP - Delta); lane: query 32hq+16qb+4g+r, key 16kb+lr
+      if (!full) {                       // masked scores -> P = 0 (wave-uniform branch)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int d = qa + 16 * qb + 4 * g + r - (kw + 16 * kb + lr);
+              s[qb][kb][r] = (unsigned)d > (unsigned)W ? -INFINITY : s[qb][kb][r];
+            }
+      }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const f32x4_t L2 = *(const f32x4_t*)(Ls + 32 * hq + 16 * qb + 4 * g) * kLog2e;
@@ -362,11 +382,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
         for (int r = 0; r < 4; ++r) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
-            float p = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], sl2, -L2[r]));
-            if (!full) {
-              const int d = qa + 16 * qb + 4 * g + r - (kw + 16 * kb + lr);
-              p = (unsigned)d > (unsigned)W ? 0.f : p;
-            }
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], sl2, -L2[r]));
             s[qb][kb][r] = p;
             dp[qb][kb][r] = p * (dp[qb][kb][r] - Dq[r]);
           }
@@ -490,6 +506,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(const bf16* __restrict__
         for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma(kx, qf[qb][ks], s[kb][qb]);
       }
     }
+    if (!full) {                         // masked scores -> P = 0 (wave-uniform branch)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int d = qw + 16 * qb + lr - (k0 + 16 * kb + 4 * g + r);
+            s[kb][qb][r] = (unsigned)d > (unsigned)W ? -INFINITY : s[kb][qb][r];
+          }
+    }
     // lane: key 16kb + 4g + r, query 16qb + lr
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -507,11 +534,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(const bf16* __restrict__
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], sl2, -L2[qb]));
-          if (!full) {
-            const int d = qw + 16 * qb + lr - (k0 + 16 * kb + 4 * g + r);
-            p = (unsigned)d > (unsigned)W ? 0.f : p;
-          }
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], sl2, -L2[qb]));
           s[kb][qb][r] = p * (dp[qb][r] - Dq[qb]);
         }
     }
