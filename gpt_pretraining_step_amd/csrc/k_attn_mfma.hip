@@ -253,12 +253,14 @@ __global__ __launch_bounds__(256) void k_attn_delta(const bf16* __restrict__ o,
 // dK, dV of 128 keys of one KV head (4 waves x 32 keys), summed over the G
 // query heads of the group and every 64-query tile that sees these keys.
 // Scores are formed queries x keys (X = Q tile rows, Y = K in registers), so
-// each lane owns one key; a 64-query tile is taken in two 32-query halves
-// (fewer live score registers: two waves per SIMD), and P and dS of a half
-// feed dV^T += dO^T P and dK^T += Q^T dS from registers, with the dO^T and
-// Q^T fragments gathered by transposing LDS reads.
+// each lane owns one key; a 64-query tile is taken in halves of 16 NQB
+// queries (NQB = 2 measured faster than whole tiles: fewer live scores),
+// and P and dS of a half feed dV^T += dO^T P and dK^T += Q^T dS from
+// registers, with the dO^T and Q^T fragments gathered by transposing LDS
+// reads.
 static constexpr int KV_BK = NW * 32;          // keys per workgroup
 
+template <int NQB>
 __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict__ qkv,
                                                          const bf16* __restrict__ dout,
                                                          const float* __restrict__ lse,
@@ -334,16 +336,16 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
     const float* Ls = ldl[st][0];
     const float* Dl = ldl[st][1];
 #pragma unroll
-    for (int hq = 0; hq < 2; ++hq) {
-      // pairs of this wave: queries [qa, qa+31], keys [kw, kw+31]
-      const int qa = q0 + 32 * hq;
-      const bool any = (qa + 31 >= kw) && (qa - (kw + 31) <= W) && kw < T && qa < T;
-      const bool full = (qa >= kw + 31) && (qa + 31 - kw <= W);
+    for (int hq = 0; hq < 4 / NQB; ++hq) {
+      // pairs of this wave: queries [qa, qa + 16 NQB), keys [kw, kw+31]
+      const int qa = q0 + 16 * NQB * hq;
+      const bool any = (qa + 16 * NQB - 1 >= kw) && (qa - (kw + 31) <= W) && kw < T && qa < T;
+      const bool full = (qa >= kw + 31) && (qa + 16 * NQB - 1 - kw <= W);
       if (!any) continue;
-      f32x4_t s[2][2], dp[2][2];
+      f32x4_t s[NQB][2], dp[NQB][2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int row = 32 * hq + 16 * qb + lr;
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int row = 16 * NQB * hq + 16 * qb + lr;
         const bf16x8_t qx0 = dfrag_row(Qs, row, 0, g);
         const bf16x8_t dx0 = dfrag_row(Ds, row, 0, g);
 #pragma unroll
@@ -362,10 +364,10 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
           }
         }
       }
-      // P = exp(S - lse), dS = P (dP - Delta); lane: query 32hq+16qb+4g+r, key 16kb+lr
+      // P = exp(S - lse), dS = P (dP - Delta); lane: query qa+16qb+4g+r, key 16kb+lr
       if (!full) {                       // masked scores -> P = 0 (wave-uniform branch)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -375,9 +377,10 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
             }
       }
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const f32x4_t L2 = *(const f32x4_t*)(Ls + 32 * hq + 16 * qb + 4 * g) * kLog2e;
-        const f32x4_t Dq = *(const f32x4_t*)(Dl + 32 * hq + 16 * qb + 4 * g);
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int qo = 16 * NQB * hq + 16 * qb + 4 * g;
+        const f32x4_t L2 = *(const f32x4_t*)(Ls + qo) * kLog2e;
+        const f32x4_t Dq = *(const f32x4_t*)(Dl + qo);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
 #pragma unroll
@@ -389,14 +392,18 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
         }
       }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8_t pp = pack8(s[0][kb], s[1][kb]);
-        const bf16x8_t ps = pack8(dp[0][kb], dp[1][kb]);
+      for (int c = 0; c < NQB / 2; ++c) {
+        const int ch = (NQB / 2) * hq + c;                 // 32-query chunk of the tile
+        const int ka = 32 * ch + 4 * g, kb2 = 32 * ch + 16 + 4 * g;
 #pragma unroll
-        for (int hb = 0; hb < 8; ++hb) {
-          const int ka = 32 * hq + 4 * g, kb2 = 32 * hq + 16 + 4 * g;
-          dv[hb][kb] = mfma(dfrag_col(Ds, 16 * hb, ka, kb2, lr), pp, dv[hb][kb]);
-          dk[hb][kb] = mfma(dfrag_col(Qs, 16 * hb, ka, kb2, lr), ps, dk[hb][kb]);
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8_t pp = pack8(s[2 * c][kb], s[2 * c + 1][kb]);
+          const bf16x8_t ps = pack8(dp[2 * c][kb], dp[2 * c + 1][kb]);
+#pragma unroll
+          for (int hb = 0; hb < 8; ++hb) {
+            dv[hb][kb] = mfma(dfrag_col(Ds, 16 * hb, ka, kb2, lr), pp, dv[hb][kb]);
+            dk[hb][kb] = mfma(dfrag_col(Qs, 16 * hb, ka, kb2, lr), ps, dk[hb][kb]);
+          }
         }
       }
     }
@@ -588,9 +595,9 @@ hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const
   const Work wq(6.0 * HD * pairs, qkvo + stats + tok * H * HD * 2);
   GK_LAUNCH(wd, k_attn_delta, dim3((unsigned)cdiv(rows * 16, 256)), dim3(256), 0, s,
                      (const bf16*)o, (const bf16*)dout, delta, T, H, rows);
-  GK_LAUNCH(wkv, k_attn_bwd_dkv, dim3((T + KV_BK - 1) / KV_BK, Hkv, B), dim3(NW * 64), 0, s,
-                     (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T,
-                     H, Hkv, W);
+  GK_LAUNCH(wkv, k_attn_bwd_dkv<2>, dim3((T + KV_BK - 1) / KV_BK, Hkv, B), dim3(NW * 64), 0, s,
+            (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T, H,
+            Hkv, W);
   GK_LAUNCH(wq, k_attn_bwd_dq, dim3((T + FWD_BQ - 1) / FWD_BQ, H, B), dim3(NW * 64), 0, s,
                      (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T,
                      H, Hkv, W);
