@@ -1,12 +1,15 @@
 // Kernel launch with optional per-launch timing.
 //
 // Every kernel of the library is launched through GK_LAUNCH.  While launch
-// recording is on (gpt_prof_start), each launch is bracketed by two HIP
-// events recorded on the launch's own stream, and the launch's algorithmic
-// work (matmul flops, compulsory HBM bytes) is kept beside them, so a caller
-// can read per-kernel durations of a real step without a profiler.  When
-// recording is off the cost is one load and branch per launch.
+// recording is on (gpt_prof_start), each launch goes through
+// hipExtLaunchKernel with a start and a stop HIP event that the runtime ties
+// to the kernel's own dispatch on its stream (the kernel's execution
+// interval), and the launch's algorithmic work (matmul flops, compulsory HBM
+// bytes) is kept beside them, so a caller can read per-kernel durations of a
+// real step without a profiler.  When recording is off the cost is one load
+// and branch per launch.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -21,8 +24,9 @@ struct Work {
 };
 
 extern volatile int g_prof_on;
-void prof_begin(hipStream_t s, const void* kernel, Work w);
-void prof_end(hipStream_t s);
+// Reserves the next record for a launch of `kernel` on `s`: its two events,
+// or false when the capacity is exhausted (the launch then goes unrecorded).
+bool prof_slot(hipStream_t s, const void* kernel, Work w, hipEvent_t* start, hipEvent_t* stop);
 
 // Visible (query, key) pairs of one head row of length T with window W:
 // query i sees keys j with 0 <= i - j <= W.
@@ -34,10 +38,12 @@ inline double visible_pairs(int64_t T, int64_t W) {
 
 }  // namespace gk
 
-#define GK_LAUNCH(WORK, K, GRID, BLOCK, SHMEM, STREAM, ...)                       \
-  do {                                                                             \
-    const bool gk_rec_ = ::gk::g_prof_on != 0;                                     \
-    if (gk_rec_) ::gk::prof_begin((STREAM), reinterpret_cast<const void*>(&K), (WORK)); \
-    hipLaunchKernelGGL(K, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);                \
-    if (gk_rec_) ::gk::prof_end((STREAM));                                         \
+#define GK_LAUNCH(WORK, K, GRID, BLOCK, SHMEM, STREAM, ...)                                  \
+  do {                                                                                        \
+    hipEvent_t gk_ev0_, gk_ev1_;                                                              \
+    if (::gk::g_prof_on != 0 &&                                                               \
+        ::gk::prof_slot((STREAM), reinterpret_cast<const void*>(&K), (WORK), &gk_ev0_, &gk_ev1_)) \
+      hipExtLaunchKernelGGL(K, GRID, BLOCK, SHMEM, STREAM, gk_ev0_, gk_ev1_, 0u, __VA_ARGS__); \
+    else                                                                                      \
+      hipLaunchKernelGGL(K, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);                         \
   } while (0)

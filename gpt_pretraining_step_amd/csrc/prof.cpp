@@ -31,7 +31,6 @@ struct Recorder {
   std::vector<Rec> recs;
   int capacity = 0;
   bool overflow = false;
-  bool open = false;  // a begin without its end
 };
 
 Recorder& rec() {
@@ -45,29 +44,22 @@ void free_events(Recorder& r) {
   r.recs.clear();
   r.capacity = 0;
   r.overflow = false;
-  r.open = false;
 }
 
 }  // namespace
 
-void prof_begin(hipStream_t s, const void* kernel, Work w) {
+bool prof_slot(hipStream_t s, const void* kernel, Work w, hipEvent_t* start, hipEvent_t* stop) {
   Recorder& r = rec();
   std::lock_guard<std::mutex> lk(r.mu);
   if ((int)r.recs.size() >= r.capacity) {
     r.overflow = true;
-    return;
+    return false;
   }
-  hipEventRecord(r.ev[2 * r.recs.size()], s);
+  const size_t i = r.recs.size();
+  *start = r.ev[2 * i];
+  *stop = r.ev[2 * i + 1];
   r.recs.push_back(Rec{kernel, s, w});
-  r.open = true;
-}
-
-void prof_end(hipStream_t s) {
-  Recorder& r = rec();
-  std::lock_guard<std::mutex> lk(r.mu);
-  if (!r.open) return;
-  hipEventRecord(r.ev[2 * (r.recs.size() - 1) + 1], s);
-  r.open = false;
+  return true;
 }
 
 }  // namespace gk

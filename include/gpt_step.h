@@ -265,13 +265,14 @@ int gpt_k_ce(const float* z, const int32_t* tgt, int64_t rows, int32_t V,
 /*
  * Per-launch timing of the library's own kernels, for measurement without a
  * profiler.  Between gpt_prof_start and gpt_prof_stop every kernel the
- * library enqueues (from any entry point above) is bracketed by two HIP
- * events recorded on the stream it is launched on, and its algorithmic work
- * is kept beside them: matmul flops (2 M N K for a product; for attention,
+ * library enqueues (from any entry point above) is launched with
+ * hipExtLaunchKernel and a start / stop HIP event pair that the runtime
+ * ties to that kernel's dispatch on its stream, and its algorithmic work is
+ * kept beside them: matmul flops (2 M N K for a product; for attention,
  * 2 hd per visible (query, key) pair and per matrix product the kernel
  * forms) and compulsory HBM bytes (operands read once, results written
- * once), 0 where not stated.  Recording adds two event records per launch,
- * so time steps with recording off and use it for the per-kernel split.
+ * once), 0 where not stated.  Recording adds event traffic per launch, so
+ * time steps with recording off and use it for the per-kernel split.
  * Not for concurrent use from several host threads; events are owned by the
  * library until gpt_prof_clear or the next gpt_prof_start.
  */
