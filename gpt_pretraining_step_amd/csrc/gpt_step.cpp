@@ -140,7 +140,7 @@ struct Plan {
   size_t cs, x, hf, rf, ell, lse_z, loss, flag, logits, dz, evacc;
   std::vector<LayerBufs> layers;     // train: one per layer; eval: one shared
   // backward scratch
-  size_t dx, dh, du, dout, dqkv, attn_scr, vez, gemm_scr, gemm_scr_bytes;
+  size_t dx, dh, du, dout, dqkv, attn_scr, vez, vwg, gemm_scr, gemm_scr_bytes;
   size_t total;
 };
 
@@ -195,6 +195,7 @@ Plan make_plan(const Model& m, int mode) {
     p.dqkv = take(N * (size_t)m.QKV * es);
     p.attn_scr = take(gk::attn_bwd_scratch_bytes(m.B, m.T, m.H, m.hd));
     p.vez = take(N * (size_t)m.Hkv * 4);
+    p.vwg = take(gk::ve_wgrad_scratch_bytes(m.Hkv, m.C));
     // split-K partials of the weight-gradient products (largest of them)
     size_t gs = 0;
     const int64_t HD = (int64_t)m.H * m.hd;
@@ -204,7 +205,7 @@ Plan make_plan(const Model& m, int mode) {
     p.gemm_scr_bytes = gs;
     p.gemm_scr = take(gs);
   } else {
-    p.dx = p.dh = p.du = p.dout = p.dqkv = p.attn_scr = p.vez = p.gemm_scr = 0;
+    p.dx = p.dh = p.du = p.dout = p.dqkv = p.attn_scr = p.vez = p.vwg = p.gemm_scr = 0;
     p.gemm_scr_bytes = 0;
   }
   p.total = off;
@@ -357,7 +358,8 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
       HIP_TRY(gk::ve_bwd(tokens, m.B, m.T, dqkv, m.QKV, (m.H + m.Hkv) * m.hd,
                          elem(params, pl.ve[l], es), at<float>(ws, b.g), vez, grads + pl.ve[l],
                          m.Hkv, m.hd, dt, s));
-      HIP_TRY(gk::ve_wgrad(vez, h, m.D, N, m.Hkv, m.C, grads + pl.wg[l], accumulate, dt, s));
+      HIP_TRY(gk::ve_wgrad(vez, h, m.D, N, m.Hkv, m.C, grads + pl.wg[l], accumulate,
+                           at<float>(ws, p.vwg), dt, s));
     }
     g = gk::GemmDesc{gk::OP_TN, m.QKV, m.D, N, dqkv, m.QKV, h, m.D, grads + pl.wqkv[l], m.D,
                      wepi, nullptr, gscr, gscr_bytes};

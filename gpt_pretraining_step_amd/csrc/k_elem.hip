@@ -4,6 +4,8 @@
 // needed, so reductions are register shuffles with no LDS round trip.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -603,33 +605,50 @@ hipError_t ve_bwd(const int32_t* tok, int B, int T, const void* dqkv, int ldqkv,
   return hipGetLastError();
 }
 
-// dWg[kv, c] = sum_n vez[n, kv] h[n, c]: one block per (kv, c) output, a
-// fixed-order block reduction (deterministic).
+// dWg[kv, c] = sum_n vez[n, kv] h[n, c], in two deterministic stages: each
+// block sums a fixed run of rows for every (kv, c) (the C channels of a row
+// are one coalesced read), then one thread per output adds the blocks'
+// partials in block order.
 template <typename Tv>
-__global__ __launch_bounds__(256) void k_ve_wgrad(const float* vez, const Tv* h, int D, int64_t N,
-                                                  int Hkv, int C, float* dWg, int accumulate) {
-  __shared__ float red[4];
-  int o = blockIdx.x;
-  int kv = o / C, c = o % C;
-  float acc = 0.f;
-  for (int64_t n = threadIdx.x; n < N; n += blockDim.x) acc += vez[n * Hkv + kv] * ld(h, n * D + c);
-  acc = wave_sum(acc);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float v = (red[0] + red[1]) + (red[2] + red[3]);
-    dWg[o] = accumulate ? dWg[o] + v : v;
+__global__ __launch_bounds__(256) void k_ve_wgrad_part(const float* vez, const Tv* h, int D,
+                                                       int64_t N, int Hkv, int C, int64_t rows,
+                                                       float* part) {
+  const int64_t n0 = blockIdx.x * rows, n1 = min(N, n0 + rows);
+  const int HC = Hkv * C;
+  for (int t = threadIdx.x; t < HC; t += blockDim.x) {
+    const int kv = t / C, c = t % C;
+    float acc = 0.f;
+    for (int64_t n = n0; n < n1; ++n) acc = fmaf(vez[n * Hkv + kv], ld(h, n * D + c), acc);
+    part[(int64_t)blockIdx.x * HC + t] = acc;
   }
 }
 
+__global__ __launch_bounds__(256) void k_ve_wgrad_sum(const float* part, int nb, int HC,
+                                                      float* dWg, int accumulate) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= HC) return;
+  float v = 0.f;
+  for (int b = 0; b < nb; ++b) v += part[(int64_t)b * HC + t];
+  dWg[t] = accumulate ? dWg[t] + v : v;
+}
+
+size_t ve_wgrad_scratch_bytes(int Hkv, int C) { return (size_t)kVeWgradBlocks * Hkv * C * 4; }
+
 hipError_t ve_wgrad(const float* vez, const void* h, int D, int64_t N, int Hkv, int C, float* dWg,
-                    int accumulate, DType dt, hipStream_t s) {
+                    int accumulate, float* part, DType dt, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  const int nb = (int)std::min<int64_t>(kVeWgradBlocks, N);
+  const int64_t rows = cdiv(N, nb);
+  const int HC = Hkv * C;
+  const Work w(0.0, (double)N * (C * (dt == BF16 ? 2 : 4) + Hkv * 4));
   if (dt == BF16)
-    GK_LAUNCH(Work(), k_ve_wgrad<bf16>, dim3(Hkv * C), dim3(256), 0, s, vez, (const bf16*)h, D, N,
-                       Hkv, C, dWg, accumulate);
+    GK_LAUNCH(w, k_ve_wgrad_part<bf16>, dim3((unsigned)nb), dim3(256), 0, s, vez, (const bf16*)h,
+              D, N, Hkv, C, rows, part);
   else
-    GK_LAUNCH(Work(), k_ve_wgrad<float>, dim3(Hkv * C), dim3(256), 0, s, vez, (const float*)h, D, N,
-                       Hkv, C, dWg, accumulate);
+    GK_LAUNCH(w, k_ve_wgrad_part<float>, dim3((unsigned)nb), dim3(256), 0, s, vez,
+              (const float*)h, D, N, Hkv, C, rows, part);
+  GK_LAUNCH(Work(), k_ve_wgrad_sum, dim3((unsigned)cdiv(HC, 256)), dim3(256), 0, s, part, nb, HC,
+            dWg, accumulate);
   return hipGetLastError();
 }
 

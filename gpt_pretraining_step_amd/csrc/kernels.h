@@ -62,10 +62,13 @@ hipError_t ve_bwd(const int32_t* tok, int B, int T, const void* dqkv,
                   int ldqkv, int voff, const void* E, const float* g,
                   float* vez, float* dE, int Hkv, int hd, DType dt,
                   hipStream_t s);
-// dWg[kv, c] (=/+=) sum_n vez[n, kv] h[n, c]
+// dWg[kv, c] (=/+=) sum_n vez[n, kv] h[n, c]; part: ve_wgrad_scratch_bytes
+// of fp32 scratch (deterministic two-stage sum)
+constexpr int kVeWgradBlocks = 256;
+size_t ve_wgrad_scratch_bytes(int Hkv, int C);
 hipError_t ve_wgrad(const float* vez, const void* h, int D, int64_t N,
-                    int Hkv, int C, float* dWg, int accumulate, DType dt,
-                    hipStream_t s);
+                    int Hkv, int C, float* dWg, int accumulate, float* part,
+                    DType dt, hipStream_t s);
 
 hipError_t attn_fwd(const void* qkv, void* o, float* lse, int B, int T,
                     int H, int Hkv, int hd, int W, DType dt, hipStream_t s);
