@@ -260,8 +260,11 @@ __global__ __launch_bounds__(256) void k_attn_delta(const bf16* __restrict__ o,
 // reads.
 static constexpr int KV_BK = NW * 32;          // keys per workgroup
 
-template <int NQB>
-__global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict__ qkv,
+// MODE: 0 = dK and dV together (one wave per SIMD: both accumulators and the
+// K and V fragments do not fit two), 1 = dK only, 2 = dV only (each fits two
+// waves per SIMD; dV needs no dP, Delta or Q^T, dK no dO^T).
+template <int NQB, int MODE>
+__global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const bf16* __restrict__ qkv,
                                                          const bf16* __restrict__ dout,
                                                          const float* __restrict__ lse,
                                                          const float* __restrict__ delta,
@@ -282,6 +285,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
   const int k0 = kblk * KV_BK;
   const int kw = k0 + 32 * wave;                      // this wave's first key
   const float sl2 = kLog2e / sqrtf((float)HD);
+  constexpr bool DO_K = MODE != 2, DO_V = MODE != 1;
 
   // queries that see keys [k0, k0+127]: [k0, k0 + 127 + W]
   const int qhi = (int)min((int64_t)T - 1, (int64_t)k0 + KV_BK - 1 + W);
@@ -299,7 +303,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
     if (wave == 0) {
       const int64_t li = ((int64_t)b * H + hh) * T;
       dma_vec64(lse + li, T, qq, ldl[st][0], lane);
-      dma_vec64(delta + li, T, qq, ldl[st][1], lane);
+      if constexpr (DO_K) dma_vec64(delta + li, T, qq, ldl[st][1], lane);
     }
   };
   issue(0, 0);
@@ -312,9 +316,11 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
     for (int ks = 0; ks < 4; ++ks) {
       const int64_t off = (int64_t)key * ldq + 32 * ks + 8 * g;
       uint4 uk = key < T ? *(const uint4*)(rowbase + off + (int64_t)(H + kvh) * HD) : make_uint4(0, 0, 0, 0);
-      uint4 uv = key < T ? *(const uint4*)(rowbase + off + (int64_t)(H + Hkv + kvh) * HD) : make_uint4(0, 0, 0, 0);
       kf[kb][ks] = __builtin_bit_cast(bf16x8_t, uk);
-      vf[kb][ks] = __builtin_bit_cast(bf16x8_t, uv);
+      if constexpr (DO_K) {
+        uint4 uv = key < T ? *(const uint4*)(rowbase + off + (int64_t)(H + Hkv + kvh) * HD) : make_uint4(0, 0, 0, 0);
+        vf[kb][ks] = __builtin_bit_cast(bf16x8_t, uv);
+      }
     }
   }
   f32x4_t dk[8][2], dv[8][2];
@@ -347,20 +353,21 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
       for (int qb = 0; qb < NQB; ++qb) {
         const int row = 16 * NQB * hq + 16 * qb + lr;
         const bf16x8_t qx0 = dfrag_row(Qs, row, 0, g);
-        const bf16x8_t dx0 = dfrag_row(Ds, row, 0, g);
+        const bf16x8_t dx0 = DO_K ? dfrag_row(Ds, row, 0, g) : qx0;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           s[qb][kb] = mfma(qx0, kf[kb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
-          dp[qb][kb] = mfma(dx0, vf[kb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+          if constexpr (DO_K) dp[qb][kb] = mfma(dx0, vf[kb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
         }
 #pragma unroll
         for (int ks = 1; ks < 4; ++ks) {
           const bf16x8_t qx = dfrag_row(Qs, row, ks, g);
-          const bf16x8_t dx = dfrag_row(Ds, row, ks, g);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            s[qb][kb] = mfma(qx, kf[kb][ks], s[qb][kb]);
-            dp[qb][kb] = mfma(dx, vf[kb][ks], dp[qb][kb]);
+          for (int kb = 0; kb < 2; ++kb) s[qb][kb] = mfma(qx, kf[kb][ks], s[qb][kb]);
+          if constexpr (DO_K) {
+            const bf16x8_t dx = dfrag_row(Ds, row, ks, g);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) dp[qb][kb] = mfma(dx, vf[kb][ks], dp[qb][kb]);
           }
         }
       }
@@ -380,14 +387,14 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
       for (int qb = 0; qb < NQB; ++qb) {
         const int qo = 16 * NQB * hq + 16 * qb + 4 * g;
         const f32x4_t L2 = *(const f32x4_t*)(Ls + qo) * kLog2e;
-        const f32x4_t Dq = *(const f32x4_t*)(Dl + qo);
+        const f32x4_t Dq = DO_K ? *(const f32x4_t*)(Dl + qo) : L2;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
             const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], sl2, -L2[r]));
             s[qb][kb][r] = p;
-            dp[qb][kb][r] = p * (dp[qb][kb][r] - Dq[r]);
+            if constexpr (DO_K) dp[qb][kb][r] = p * (dp[qb][kb][r] - Dq[r]);
           }
         }
       }
@@ -397,12 +404,17 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
         const int ka = 32 * ch + 4 * g, kb2 = 32 * ch + 16 + 4 * g;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8_t pp = pack8(s[2 * c][kb], s[2 * c + 1][kb]);
-          const bf16x8_t ps = pack8(dp[2 * c][kb], dp[2 * c + 1][kb]);
+          if constexpr (DO_V) {
+            const bf16x8_t pp = pack8(s[2 * c][kb], s[2 * c + 1][kb]);
 #pragma unroll
-          for (int hb = 0; hb < 8; ++hb) {
-            dv[hb][kb] = mfma(dfrag_col(Ds, 16 * hb, ka, kb2, lr), pp, dv[hb][kb]);
-            dk[hb][kb] = mfma(dfrag_col(Qs, 16 * hb, ka, kb2, lr), ps, dk[hb][kb]);
+            for (int hb = 0; hb < 8; ++hb)
+              dv[hb][kb] = mfma(dfrag_col(Ds, 16 * hb, ka, kb2, lr), pp, dv[hb][kb]);
+          }
+          if constexpr (DO_K) {
+            const bf16x8_t ps = pack8(dp[2 * c][kb], dp[2 * c + 1][kb]);
+#pragma unroll
+            for (int hb = 0; hb < 8; ++hb)
+              dk[hb][kb] = mfma(dfrag_col(Qs, 16 * hb, ka, kb2, lr), ps, dk[hb][kb]);
           }
         }
       }
@@ -418,13 +430,18 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(const bf16* __restrict_
     bf16* vrow = dqkv + ((int64_t)b * T + key) * ldq + (int64_t)(H + Hkv + kvh) * HD;
 #pragma unroll
     for (int hb = 0; hb < 8; ++hb) {
-      uint2 uk, uv;
-      uk.x = pack2bf(dk[hb][kb][0] * scale, dk[hb][kb][1] * scale);
-      uk.y = pack2bf(dk[hb][kb][2] * scale, dk[hb][kb][3] * scale);
-      uv.x = pack2bf(dv[hb][kb][0], dv[hb][kb][1]);
-      uv.y = pack2bf(dv[hb][kb][2], dv[hb][kb][3]);
-      *(uint2*)(krow + 16 * hb + 4 * g) = uk;
-      *(uint2*)(vrow + 16 * hb + 4 * g) = uv;
+      if constexpr (DO_K) {
+        uint2 uk;
+        uk.x = pack2bf(dk[hb][kb][0] * scale, dk[hb][kb][1] * scale);
+        uk.y = pack2bf(dk[hb][kb][2] * scale, dk[hb][kb][3] * scale);
+        *(uint2*)(krow + 16 * hb + 4 * g) = uk;
+      }
+      if constexpr (DO_V) {
+        uint2 uv;
+        uv.x = pack2bf(dv[hb][kb][0], dv[hb][kb][1]);
+        uv.y = pack2bf(dv[hb][kb][2], dv[hb][kb][3]);
+        *(uint2*)(vrow + 16 * hb + 4 * g) = uv;
+      }
     }
   }
 }
@@ -586,18 +603,23 @@ hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const
   (void)hd;
   const int64_t rows = (int64_t)B * T * H;
   // per kernel: 2 hd flops per visible pair and matrix product formed
-  // (dK/dV pass: S, dP, dV, dK; dQ pass: S, dP, dQ); operands read once,
-  // results written once
+  // (dK pass: S, dP, dK; dV pass: S, dV; dQ pass: S, dP, dQ); operands read
+  // once, results written once
   const double pairs = (double)B * H * visible_pairs(T, W), tok = (double)B * T;
   const double qkvo = tok * HD * 2 * (2.0 * H + 2 * Hkv), stats = (double)rows * 8;
   const Work wd(0.0, tok * H * HD * 2 * 2 + rows * 4.0);
-  const Work wkv(8.0 * HD * pairs, qkvo + stats + tok * 2 * Hkv * HD * 2);
   const Work wq(6.0 * HD * pairs, qkvo + stats + tok * H * HD * 2);
   GK_LAUNCH(wd, k_attn_delta, dim3((unsigned)cdiv(rows * 16, 256)), dim3(256), 0, s,
                      (const bf16*)o, (const bf16*)dout, delta, T, H, rows);
-  GK_LAUNCH(wkv, k_attn_bwd_dkv<2>, dim3((T + KV_BK - 1) / KV_BK, Hkv, B), dim3(NW * 64), 0, s,
-            (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T, H,
-            Hkv, W);
+  // dK and dV in two passes (two waves per SIMD each; measured faster than
+  // the one-wave-per-SIMD combined pass despite recomputing S)
+  const dim3 gkv((T + KV_BK - 1) / KV_BK, Hkv, B);
+  const Work wk(6.0 * HD * pairs, qkvo + stats + tok * Hkv * HD * 2);
+  const Work wv(4.0 * HD * pairs, qkvo + stats / 2 + tok * Hkv * HD * 2);
+  GK_LAUNCH(wk, (k_attn_bwd_dkv<2, 1>), gkv, dim3(NW * 64), 0, s, (const bf16*)qkv,
+            (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T, H, Hkv, W);
+  GK_LAUNCH(wv, (k_attn_bwd_dkv<2, 2>), gkv, dim3(NW * 64), 0, s, (const bf16*)qkv,
+            (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T, H, Hkv, W);
   GK_LAUNCH(wq, k_attn_bwd_dq, dim3((T + FWD_BQ - 1) / FWD_BQ, H, B), dim3(NW * 64), 0, s,
                      (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T,
                      H, Hkv, W);
