@@ -605,31 +605,81 @@ hipError_t ve_bwd(const int32_t* tok, int B, int T, const void* dqkv, int ldqkv,
   return hipGetLastError();
 }
 
-// dWg[kv, c] = sum_n vez[n, kv] h[n, c], in two deterministic stages: each
-// block sums a fixed run of rows for every (kv, c) (the C channels of a row
-// are one coalesced read), then one thread per output adds the blocks'
-// partials in block order.
+// dWg[kv, c] = sum_n vez[n, kv] h[n, c], in two deterministic stages.  Stage
+// one: each block takes a fixed run of rows; its 256 threads are 8 row
+// groups x 32 channels (the channels of a row are one coalesced read) and
+// keep all Hkv gate gradients of their channel; the 8 row groups are added in
+// order through LDS.  Stage two: one wavefront per output adds the blocks'
+// partials with a fixed lane assignment and butterfly.
+constexpr int kVeMaxKv = 16, kVeMaxCb = 2;     // Hkv <= 16, C <= 64 in this path
 template <typename Tv>
 __global__ __launch_bounds__(256) void k_ve_wgrad_part(const float* vez, const Tv* h, int D,
                                                        int64_t N, int Hkv, int C, int64_t rows,
                                                        float* part) {
+  __shared__ float red[8][kVeMaxKv * kVeMaxCb * 32];
+  const int rg = threadIdx.x >> 5, cc = threadIdx.x & 31;
   const int64_t n0 = blockIdx.x * rows, n1 = min(N, n0 + rows);
+  float acc[kVeMaxKv][kVeMaxCb];
+#pragma unroll
+  for (int kv = 0; kv < kVeMaxKv; ++kv)
+#pragma unroll
+    for (int cb = 0; cb < kVeMaxCb; ++cb) acc[kv][cb] = 0.f;
+  for (int64_t n = n0 + rg; n < n1; n += 8) {
+    float hv[kVeMaxCb];
+#pragma unroll
+    for (int cb = 0; cb < kVeMaxCb; ++cb) {
+      const int c = cc + 32 * cb;
+      hv[cb] = c < C ? ld(h, n * D + c) : 0.f;
+    }
+#pragma unroll
+    for (int kv = 0; kv < kVeMaxKv; ++kv) {
+      if (kv >= Hkv) break;
+      const float z = vez[n * Hkv + kv];
+#pragma unroll
+      for (int cb = 0; cb < kVeMaxCb; ++cb) acc[kv][cb] = fmaf(z, hv[cb], acc[kv][cb]);
+    }
+  }
+#pragma unroll
+  for (int kv = 0; kv < kVeMaxKv; ++kv)
+#pragma unroll
+    for (int cb = 0; cb < kVeMaxCb; ++cb) red[rg][(kv * kVeMaxCb + cb) * 32 + cc] = acc[kv][cb];
+  __syncthreads();
   const int HC = Hkv * C;
   for (int t = threadIdx.x; t < HC; t += blockDim.x) {
     const int kv = t / C, c = t % C;
-    float acc = 0.f;
-    for (int64_t n = n0; n < n1; ++n) acc = fmaf(vez[n * Hkv + kv], ld(h, n * D + c), acc);
-    part[(int64_t)blockIdx.x * HC + t] = acc;
+    const int slot = (kv * kVeMaxCb + c / 32) * 32 + c % 32;
+    float v = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) v += red[r][slot];
+    part[(int64_t)blockIdx.x * HC + t] = v;
   }
 }
 
-__global__ __launch_bounds__(256) void k_ve_wgrad_sum(const float* part, int nb, int HC,
-                                                      float* dWg, int accumulate) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= HC) return;
+// any Hkv, C: one block per output, a fixed-order block reduction
+template <typename Tv>
+__global__ __launch_bounds__(256) void k_ve_wgrad_any(const float* vez, const Tv* h, int D,
+                                                      int64_t N, int Hkv, int C, float* dWg,
+                                                      int accumulate) {
+  __shared__ float red[4];
+  const int o = blockIdx.x, kv = o / C, c = o % C;
+  float acc = 0.f;
+  for (int64_t n = threadIdx.x; n < N; n += blockDim.x) acc += vez[n * Hkv + kv] * ld(h, n * D + c);
+  acc = wave_sum(acc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float v = (red[0] + red[1]) + (red[2] + red[3]);
+    dWg[o] = accumulate ? dWg[o] + v : v;
+  }
+}
+
+__global__ __launch_bounds__(64) void k_ve_wgrad_sum(const float* part, int nb, int HC,
+                                                     float* dWg, int accumulate) {
+  const int t = blockIdx.x, lane = threadIdx.x;
   float v = 0.f;
-  for (int b = 0; b < nb; ++b) v += part[(int64_t)b * HC + t];
-  dWg[t] = accumulate ? dWg[t] + v : v;
+  for (int b = lane; b < nb; b += 64) v += part[(int64_t)b * HC + t];
+  v = wave_sum(v);
+  if (lane == 0) dWg[t] = accumulate ? dWg[t] + v : v;
 }
 
 size_t ve_wgrad_scratch_bytes(int Hkv, int C) { return (size_t)kVeWgradBlocks * Hkv * C * 4; }
@@ -637,7 +687,16 @@ size_t ve_wgrad_scratch_bytes(int Hkv, int C) { return (size_t)kVeWgradBlocks * 
 hipError_t ve_wgrad(const float* vez, const void* h, int D, int64_t N, int Hkv, int C, float* dWg,
                     int accumulate, float* part, DType dt, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  const int nb = (int)std::min<int64_t>(kVeWgradBlocks, N);
+  if (Hkv > kVeMaxKv || C > 32 * kVeMaxCb) {
+    if (dt == BF16)
+      GK_LAUNCH(Work(), k_ve_wgrad_any<bf16>, dim3(Hkv * C), dim3(256), 0, s, vez,
+                (const bf16*)h, D, N, Hkv, C, dWg, accumulate);
+    else
+      GK_LAUNCH(Work(), k_ve_wgrad_any<float>, dim3(Hkv * C), dim3(256), 0, s, vez,
+                (const float*)h, D, N, Hkv, C, dWg, accumulate);
+    return hipGetLastError();
+  }
+  const int nb = (int)std::min<int64_t>(kVeWgradBlocks, cdiv(N, 8));
   const int64_t rows = cdiv(N, nb);
   const int HC = Hkv * C;
   const Work w(0.0, (double)N * (C * (dt == BF16 ? 2 : 4) + Hkv * 4));
@@ -647,8 +706,8 @@ hipError_t ve_wgrad(const float* vez, const void* h, int D, int64_t N, int Hkv, 
   else
     GK_LAUNCH(w, k_ve_wgrad_part<float>, dim3((unsigned)nb), dim3(256), 0, s, vez,
               (const float*)h, D, N, Hkv, C, rows, part);
-  GK_LAUNCH(Work(), k_ve_wgrad_sum, dim3((unsigned)cdiv(HC, 256)), dim3(256), 0, s, part, nb, HC,
-            dWg, accumulate);
+  GK_LAUNCH(Work(), k_ve_wgrad_sum, dim3((unsigned)HC), dim3(64), 0, s, part, nb, HC, dWg,
+            accumulate);
   return hipGetLastError();
 }
 

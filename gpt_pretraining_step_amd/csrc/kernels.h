@@ -64,7 +64,7 @@ hipError_t ve_bwd(const int32_t* tok, int B, int T, const void* dqkv,
                   hipStream_t s);
 // dWg[kv, c] (=/+=) sum_n vez[n, kv] h[n, c]; part: ve_wgrad_scratch_bytes
 // of fp32 scratch (deterministic two-stage sum)
-constexpr int kVeWgradBlocks = 256;
+constexpr int kVeWgradBlocks = 512;
 size_t ve_wgrad_scratch_bytes(int Hkv, int C);
 hipError_t ve_wgrad(const float* vez, const void* h, int D, int64_t N,
                     int Hkv, int C, float* dWg, int accumulate, float* part,

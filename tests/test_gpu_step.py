@@ -78,13 +78,15 @@ def compare(cfg, w, tok, loss, ell, grads, flag):
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_plus", "small_bf16", "small_bf16_mha",
-                                  "d4"])
+                                  "small_bf16_wide_gate", "d4"])
 def test_step_matches_oracle(name):
     cfg = {"tiny": lambda: gi.preset("tiny"), "tiny_plus": tiny_plus,
            "small_bf16": small_bf16,
            "small_bf16_mha": lambda: small_bf16(n_kv_head=2, batch=2, seq_len=160,
                                                 window_short=40, window_long=160,
                                                 head_dim=128, n_head=2),
+           # gate reading more channels than the fast gate-gradient path covers
+           "small_bf16_wide_gate": lambda: small_bf16(ve_gate_channels=100),
            "d4": lambda: gi.preset("d4")}[name]()
     say("step", name)
     out = run_step(cfg, accumulate_check=(name == "tiny_plus"))
