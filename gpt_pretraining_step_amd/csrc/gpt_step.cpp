@@ -140,7 +140,8 @@ struct Plan {
   size_t cs, x, hf, rf, ell, lse_z, loss, flag, logits, dz, evacc;
   std::vector<LayerBufs> layers;     // train: one per layer; eval: one shared
   // backward scratch
-  size_t dx, dh, du, dout, dqkv, attn_scr, vez, vwg, gemm_scr, gemm_scr_bytes;
+  size_t dx, dh, du, dout, dqkv, attn_scr, vez, vwg, sort, gemm_scr, gemm_scr_bytes;
+  bool sorted_scatter;   // embedding-table gradients by the token sort (no atomics)
   size_t total;
 };
 
@@ -196,6 +197,9 @@ Plan make_plan(const Model& m, int mode) {
     p.attn_scr = take(gk::attn_bwd_scratch_bytes(m.B, m.T, m.H, m.hd));
     p.vez = take(N * (size_t)m.Hkv * 4);
     p.vwg = take(gk::ve_wgrad_scratch_bytes(m.Hkv, m.C));
+    const int maxW = std::max(m.D, m.Hkv * m.hd);
+    p.sorted_scatter = m.D % 4 == 0 && maxW <= 2048 && (m.Hkv * m.hd) % 4 == 0 && m.QKV % 4 == 0;
+    p.sort = p.sorted_scatter ? take(gk::tok_sort_bytes(N, m.V, maxW)) : 0;
     // split-K partials of the weight-gradient products (largest of them)
     size_t gs = 0;
     const int64_t HD = (int64_t)m.H * m.hd;
@@ -205,7 +209,8 @@ Plan make_plan(const Model& m, int mode) {
     p.gemm_scr_bytes = gs;
     p.gemm_scr = take(gs);
   } else {
-    p.dx = p.dh = p.du = p.dout = p.dqkv = p.attn_scr = p.vez = p.vwg = p.gemm_scr = 0;
+    p.dx = p.dh = p.du = p.dout = p.dqkv = p.attn_scr = p.vez = p.vwg = p.sort = p.gemm_scr = 0;
+    p.sorted_scatter = false;
     p.gemm_scr_bytes = 0;
   }
   p.total = off;
@@ -305,8 +310,18 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
   const void* dz = at<void>(ws, p.dz);
   const void* hf = at<void>(ws, p.hf);
 
-  // embedding tables are scatter-added: clear them first unless accumulating
-  if (!accumulate) {
+  // embedding tables: the batch's token ids are sorted once and every table
+  // row is summed in a fixed order (rows of absent ids cleared unless
+  // accumulating); otherwise they are scatter-added with atomics into
+  // cleared tables
+  const int maxW = std::max(m.D, m.Hkv * m.hd);
+  void* sortws = at<void>(ws, p.sort);
+  bool sorted = p.sorted_scatter && pl.wte % 4 == 0;      // 16-byte row stores
+  for (int l = 0; l < m.L; ++l)
+    if (m.is_ve(l)) sorted = sorted && pl.ve[l] % 4 == 0;
+  if (sorted) {
+    HIP_TRY(gk::tok_sort(tokens, m.B, m.T, m.V, maxW, sortws, s));
+  } else if (!accumulate) {
     HIP_TRY(gk::fill_zero(grads + pl.wte, (int64_t)m.V * m.D * 4, s));
     for (int l = 0; l < m.L; ++l)
       if (m.is_ve(l)) HIP_TRY(gk::fill_zero(grads + pl.ve[l], (int64_t)m.V * m.Hkv * m.hd * 4, s));
@@ -355,9 +370,17 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
                                 m.T, m.H, m.Hkv, m.hd, dt, s));
     const bool ve = m.is_ve(l);
     if (ve) {
-      HIP_TRY(gk::ve_bwd(tokens, m.B, m.T, dqkv, m.QKV, (m.H + m.Hkv) * m.hd,
-                         elem(params, pl.ve[l], es), at<float>(ws, b.g), vez, grads + pl.ve[l],
-                         m.Hkv, m.hd, dt, s));
+      const int voff = (m.H + m.Hkv) * m.hd;
+      if (sorted) {
+        HIP_TRY(gk::ve_vez(tokens, m.B, m.T, dqkv, m.QKV, voff, elem(params, pl.ve[l], es),
+                           at<float>(ws, b.g), vez, m.Hkv, m.hd, dt, s));
+        HIP_TRY(gk::seg_scatter(sortws, N, m.V, maxW, elem(dqkv, voff, es), m.QKV,
+                                m.Hkv * m.hd, at<float>(ws, b.g), m.Hkv, m.hd, grads + pl.ve[l],
+                                accumulate, dt, s));
+      } else {
+        HIP_TRY(gk::ve_bwd(tokens, m.B, m.T, dqkv, m.QKV, voff, elem(params, pl.ve[l], es),
+                           at<float>(ws, b.g), vez, grads + pl.ve[l], m.Hkv, m.hd, dt, s));
+      }
       HIP_TRY(gk::ve_wgrad(vez, h, m.D, N, m.Hkv, m.C, grads + pl.wg[l], accumulate,
                            at<float>(ws, p.vwg), dt, s));
     }
@@ -370,7 +393,11 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
     HIP_TRY(gk::rmsnorm_bwd(dh, h, at<float>(ws, b.r), dx, dx, N, m.D, ve ? vez : nullptr,
                             ve ? elem(params, pl.wg[l], es) : nullptr, m.Hkv, m.C, dt, s));
   }
-  HIP_TRY(gk::embed_bwd(tokens, m.B, m.T, dx, m.D, grads + pl.wte, m.D, dt, s));
+  if (sorted)
+    HIP_TRY(gk::seg_scatter(sortws, N, m.V, maxW, dx, m.D, m.D, nullptr, 1, m.D, grads + pl.wte,
+                            accumulate, dt, s));
+  else
+    HIP_TRY(gk::embed_bwd(tokens, m.B, m.T, dx, m.D, grads + pl.wte, m.D, dt, s));
   return GPT_OK;
 }
 

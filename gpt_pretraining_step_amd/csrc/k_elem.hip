@@ -571,7 +571,7 @@ hipError_t ve_fwd(const int32_t* tok, int B, int T, const void* h, int D, const 
   return hipGetLastError();
 }
 
-template <typename Tv>
+template <typename Tv, bool SCATTER>
 __global__ __launch_bounds__(256) void k_ve_bwd(const int32_t* tok, int T, const Tv* dqkv,
                                                 int ldqkv, int voff, const Tv* E, const float* g,
                                                 float* vez, float* dE, int Hkv, int hd) {
@@ -585,11 +585,24 @@ __global__ __launch_bounds__(256) void k_ve_bwd(const int32_t* tok, int T, const
     for (int d = lane; d < hd; d += 64) {
       float dv = ld(dqkv, n * ldqkv + voff + kv * hd + d);
       acc += dv * ld(E, (int64_t)id * tot + kv * hd + d);
-      atomicAdd(dE + (int64_t)id * tot + kv * hd + d, gv * dv);
+      if constexpr (SCATTER) atomicAdd(dE + (int64_t)id * tot + kv * hd + d, gv * dv);
     }
     acc = wave_sum(acc);
     if (lane == 0) vez[n * Hkv + kv] = acc * gv * (1.0f - gv / 3.0f);
   }
+}
+
+hipError_t ve_vez(const int32_t* tok, int B, int T, const void* dqkv, int ldqkv, int voff,
+                  const void* E, const float* g, float* vez, int Hkv, int hd, DType dt,
+                  hipStream_t s) {
+  int64_t N = (int64_t)B * T;
+  if (dt == BF16)
+    GK_LAUNCH(Work(), (k_ve_bwd<bf16, false>), dim3((unsigned)N), dim3(256), 0, s, tok, T,
+              (const bf16*)dqkv, ldqkv, voff, (const bf16*)E, g, vez, nullptr, Hkv, hd);
+  else
+    GK_LAUNCH(Work(), (k_ve_bwd<float, false>), dim3((unsigned)N), dim3(256), 0, s, tok, T,
+              (const float*)dqkv, ldqkv, voff, (const float*)E, g, vez, nullptr, Hkv, hd);
+  return hipGetLastError();
 }
 
 hipError_t ve_bwd(const int32_t* tok, int B, int T, const void* dqkv, int ldqkv, int voff,
@@ -597,10 +610,10 @@ hipError_t ve_bwd(const int32_t* tok, int B, int T, const void* dqkv, int ldqkv,
                   DType dt, hipStream_t s) {
   int64_t N = (int64_t)B * T;
   if (dt == BF16)
-    GK_LAUNCH(Work(), k_ve_bwd<bf16>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const bf16*)dqkv,
+    GK_LAUNCH(Work(), (k_ve_bwd<bf16, true>), dim3((unsigned)N), dim3(256), 0, s, tok, T, (const bf16*)dqkv,
                        ldqkv, voff, (const bf16*)E, g, vez, dE, Hkv, hd);
   else
-    GK_LAUNCH(Work(), k_ve_bwd<float>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const float*)dqkv,
+    GK_LAUNCH(Work(), (k_ve_bwd<float, true>), dim3((unsigned)N), dim3(256), 0, s, tok, T, (const float*)dqkv,
                        ldqkv, voff, (const float*)E, g, vez, dE, Hkv, hd);
   return hipGetLastError();
 }

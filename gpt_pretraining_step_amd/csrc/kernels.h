@@ -70,6 +70,22 @@ hipError_t ve_wgrad(const float* vez, const void* h, int D, int64_t N,
                     int Hkv, int C, float* dWg, int accumulate, float* part,
                     DType dt, hipStream_t s);
 
+// Token-sorted scatter into embedding-table gradients (deterministic):
+// tok_sort orders the batch's ids once (scratch of tok_sort_bytes; maxW =
+// the widest row later scattered), then seg_scatter sets (or adds to) dst[v,
+// 0:W] the sum over positions n with token v of f(n, col) src[n*ld + col],
+// f = gate[n*Hkv + col/hd] or 1.  W % 4 == 0, W <= 2048, ld % 4 == 0.
+size_t tok_sort_bytes(int64_t N, int V, int maxW);
+hipError_t tok_sort(const int32_t* tok, int B, int T, int V, int maxW, void* scratch,
+                    hipStream_t s);
+hipError_t seg_scatter(const void* scratch, int64_t N, int V, int maxW, const void* src,
+                       int64_t ld, int W, const float* gate, int Hkv, int hd, float* dst,
+                       int accumulate, DType dt, hipStream_t s);
+// vez only (the value-embedding gate gradient), no table scatter
+hipError_t ve_vez(const int32_t* tok, int B, int T, const void* dqkv, int ldqkv, int voff,
+                  const void* E, const float* g, float* vez, int Hkv, int hd, DType dt,
+                  hipStream_t s);
+
 hipError_t attn_fwd(const void* qkv, void* o, float* lse, int B, int T,
                     int H, int Hkv, int hd, int W, DType dt, hipStream_t s);
 size_t attn_bwd_scratch_bytes(int B, int T, int H, int hd);

@@ -78,7 +78,7 @@ def compare(cfg, w, tok, loss, ell, grads, flag):
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_plus", "small_bf16", "small_bf16_mha",
-                                  "small_bf16_wide_gate", "d4"])
+                                  "small_bf16_wide_gate", "tiny_odd_gate", "d4"])
 def test_step_matches_oracle(name):
     cfg = {"tiny": lambda: gi.preset("tiny"), "tiny_plus": tiny_plus,
            "small_bf16": small_bf16,
@@ -87,6 +87,11 @@ def test_step_matches_oracle(name):
                                                 head_dim=128, n_head=2),
            # gate reading more channels than the fast gate-gradient path covers
            "small_bf16_wide_gate": lambda: small_bf16(ve_gate_channels=100),
+           # a gate of 7 channels leaves later value-embedding tables off 16-byte
+           # alignment: their gradients take the atomic scatter path
+           "tiny_odd_gate": lambda: gi.preset("tiny", n_layer=4, window_pattern="SL",
+                                              window_short=4, window_long=16, ve_every_odd=1,
+                                              ve_gate_channels=7),
            "d4": lambda: gi.preset("d4")}[name]()
     say("step", name)
     out = run_step(cfg, accumulate_check=(name == "tiny_plus"))
@@ -163,3 +168,22 @@ def test_deterministic_forward():
     s.fwd()
     torch.cuda.synchronize()
     assert torch.equal(a, s.ws_f32(G.WS_ELL, N))
+
+
+def test_deterministic_backward():
+    """Every gradient, the embedding tables' sorted scatter included, is a
+    fixed-order sum: two backward passes agree bit for bit."""
+    cfg = small_bf16(batch=4, seq_len=256)
+    n = O.param_count(cfg)
+    w, bits = gi.make_params(cfg, n)
+    s = Session(cfg)
+    s.set_params(w, bits)
+    s.set_tokens(gi.make_tokens(cfg))
+    s.fwd()
+    s.bwd()
+    torch.cuda.synchronize()
+    a = s.grads.clone()
+    s.fwd()
+    s.bwd()
+    torch.cuda.synchronize()
+    assert torch.equal(a, s.grads)
