@@ -592,16 +592,46 @@ __global__ __launch_bounds__(256) void k_ve_bwd(const int32_t* tok, int T, const
   }
 }
 
+// vez[n, kv] = (dv . E[tok[n]])_kv g (1 - g/3): one wavefront per token, the
+// Hkv*hd values in passes of 256 (lane: 4 consecutive columns), each head's
+// dot product a reduction over its hd/4 lanes.
+template <typename Tv>
+__global__ __launch_bounds__(256) void k_ve_vez(const int32_t* tok, int T, int64_t N,
+                                                const Tv* dqkv, int ldqkv, int voff, const Tv* E,
+                                                const float* g, float* vez, int Hkv, int hd) {
+  const int64_t n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (n >= N) return;
+  const int id = tok[(n / T) * (T + 1) + n % T];
+  const int W = Hkv * hd, seg = hd / 4;
+  for (int c0 = 0; c0 < W; c0 += 256) {
+    const int col = c0 + 4 * lane;
+    float acc = 0.f;
+    if (col < W) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc = fmaf(ld(dqkv, n * ldqkv + voff + col + e), ld(E, (int64_t)id * W + col + e), acc);
+    }
+    acc = seg_sum(acc, seg);
+    if (col < W && (lane % seg) == 0) {
+      const int kv = col / hd;
+      const float gv = g[n * Hkv + kv];
+      vez[n * Hkv + kv] = acc * gv * (1.0f - gv / 3.0f);
+    }
+  }
+}
+
 hipError_t ve_vez(const int32_t* tok, int B, int T, const void* dqkv, int ldqkv, int voff,
                   const void* E, const float* g, float* vez, int Hkv, int hd, DType dt,
                   hipStream_t s) {
-  int64_t N = (int64_t)B * T;
+  const int64_t N = (int64_t)B * T;
+  if (hd % 4 || hd / 4 > 64) return hipErrorInvalidValue;
   if (dt == BF16)
-    GK_LAUNCH(Work(), (k_ve_bwd<bf16, false>), dim3((unsigned)N), dim3(256), 0, s, tok, T,
-              (const bf16*)dqkv, ldqkv, voff, (const bf16*)E, g, vez, nullptr, Hkv, hd);
+    GK_LAUNCH(Work(), k_ve_vez<bf16>, dim3((unsigned)cdiv(N, 4)), dim3(256), 0, s, tok, T, N,
+              (const bf16*)dqkv, ldqkv, voff, (const bf16*)E, g, vez, Hkv, hd);
   else
-    GK_LAUNCH(Work(), (k_ve_bwd<float, false>), dim3((unsigned)N), dim3(256), 0, s, tok, T,
-              (const float*)dqkv, ldqkv, voff, (const float*)E, g, vez, nullptr, Hkv, hd);
+    GK_LAUNCH(Work(), k_ve_vez<float>, dim3((unsigned)cdiv(N, 4)), dim3(256), 0, s, tok, T, N,
+              (const float*)dqkv, ldqkv, voff, (const float*)E, g, vez, Hkv, hd);
   return hipGetLastError();
 }
 

@@ -166,9 +166,67 @@ __device__ __forceinline__ void load4<float>(const float* p, float (&v)[4]) {
   v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
 }
 
-// One block (4 waves) per chunk of 64 sorted positions; the chunk's runs of
-// equal ids go to the waves round-robin and each run is summed by one wave in
-// sorted order (no block-wide steps per run).
+// Sum of rows [i0, i1) of the chunk (sorted order) into acc, loads issued in
+// groups of 4 rows.
+template <typename Tv, int NP>
+__device__ __forceinline__ void rows_sum(const uint64_t* ck, int i0, int i1, const Tv* src,
+                                         int64_t ld, int W, const float* gate, int Hkv, int hd,
+                                         int lane, float (&acc)[NP][4]) {
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[p][e] = 0.f;
+  for (int b = i0; b < i1; b += 4) {
+    float v[4][NP][4], f[4][NP];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = b + u < i1 ? b + u : b;
+      const int64_t n = (int64_t)(uint32_t)ck[i];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int col = 256 * p + 4 * lane;
+        if (col < W) {
+          load4<Tv>(src + n * ld + col, v[u][p]);
+          f[u][p] = gate ? gate[n * Hkv + col / hd] : 1.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (b + u >= i1) break;
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[p][e] = fmaf(f[u][p], v[u][p][e], acc[p][e]);
+    }
+  }
+}
+
+// One block (4 waves) per chunk of 64 sorted positions.  Runs of equal ids
+// shorter than kLongRun go to the waves round-robin, each summed by one wave
+// in sorted order; longer runs are split into 4 consecutive quarters, one per
+// wave, added in quarter order through LDS.  A run that is its id's whole
+// segment is written as the final row; a run cut by the chunk's edge leaves a
+// partial row (slot 0 if it starts the chunk, 1 if it ends it).
+static constexpr int kLongRun = 16;
+
+template <int NP>
+__device__ __forceinline__ void put_row(float* out, int W, int lane, bool add,
+                                        const float (&acc)[NP][4]) {
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int col = 256 * p + 4 * lane;
+    if (col < W) {
+      float4 v = make_float4(acc[p][0], acc[p][1], acc[p][2], acc[p][3]);
+      if (add) {
+        const float4 q = *(const float4*)(out + col);
+        v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+      }
+      *(float4*)(out + col) = v;
+    }
+  }
+}
+
 template <typename Tv, int NP>
 __global__ __launch_bounds__(256) void k_seg_rows(const uint64_t* keys, int64_t N,
                                                   const int32_t* first1, const int32_t* last1,
@@ -177,82 +235,110 @@ __global__ __launch_bounds__(256) void k_seg_rows(const uint64_t* keys, int64_t 
                                                   float* dst, float* part, int accumulate) {
   static_assert(kChunk == 64, "one lane per chunk position");
   __shared__ uint64_t ck[kChunk];
+  __shared__ float red[4][NP * 256];
   const int64_t c0 = (int64_t)blockIdx.x * kChunk, c1 = std::min(N, c0 + kChunk);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int len = (int)(c1 - c0);
   if (threadIdx.x < kChunk) ck[threadIdx.x] = c0 + threadIdx.x < N ? keys[c0 + threadIdx.x] : kPad;
   __syncthreads();
-  // run starts of the chunk, one bit per position
   const bool start = lane < len && (lane == 0 || (ck[lane] >> 32) != (ck[lane - 1] >> 32));
-  uint64_t starts = __builtin_amdgcn_ballot_w64(start);
-  for (int r = 0; starts; ++r) {
-    const int rs = __builtin_ctzll(starts);
-    starts &= starts - 1;
-    const int re = starts ? __builtin_ctzll(starts) : len;
-    if ((r & 3) != w) continue;
+  const uint64_t starts = __builtin_amdgcn_ballot_w64(start);
+  // whole-segment flags of the runs, looked up once for the chunk
+  __shared__ int wh[kChunk];
+  if (w == 0 && start) {
+    const uint32_t id = (uint32_t)(ck[lane] >> 32);
+    const int64_t sf = first1[id] - 1, sl = last1[id];
+    wh[lane] = sf >= c0 && sl <= c1;
+  }
+  __syncthreads();
+  auto target = [&](int rs, int re, uint32_t id, bool* whole) {
+    *whole = wh[rs] != 0;
+    return *whole ? dst + (int64_t)id * W
+                  : part + ((int64_t)blockIdx.x * 2 + (rs == 0 ? 0 : 1)) * W;
+  };
+  float acc[NP][4];
+  // short runs: one wave each
+  uint64_t m = starts;
+  for (int r = 0; m; ++r) {
+    const int rs = __builtin_ctzll(m);
+    m &= m - 1;
+    const int re = m ? __builtin_ctzll(m) : len;
+    if (re - rs >= kLongRun || (r & 3) != w) continue;
     const uint32_t id = (uint32_t)(ck[rs] >> 32);
-    float acc[NP][4];
+    rows_sum<Tv, NP>(ck, rs, re, src, ld, W, gate, Hkv, hd, lane, acc);
+    bool whole;
+    float* out = target(rs, re, id, &whole);
+    put_row<NP>(out, W, lane, whole && accumulate, acc);
+  }
+  // long runs: a quarter per wave
+  m = starts;
+  while (m) {
+    const int rs = __builtin_ctzll(m);
+    m &= m - 1;
+    const int re = m ? __builtin_ctzll(m) : len;
+    if (re - rs < kLongRun) continue;
+    const int q = (re - rs + 3) / 4;
+    const int a = std::min(re, rs + w * q), b = std::min(re, a + q);
+    rows_sum<Tv, NP>(ck, a, b, src, ld, W, gate, Hkv, hd, lane, acc);
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[p][e] = 0.f;
-    for (int i = rs; i < re; ++i) {
-      const int64_t n = (int64_t)(uint32_t)ck[i];
+      for (int e = 0; e < 4; ++e) red[w][256 * p + 4 * lane + e] = acc[p][e];
+    __syncthreads();
+    if (w == 0) {
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int col = 256 * p + 4 * lane;
-        if (col < W) {
-          float v[4];
-          load4<Tv>(src + n * ld + col, v);
-          const float f = gate ? gate[n * Hkv + col / hd] : 1.f;
+      for (int p = 0; p < NP; ++p)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[p][e] = fmaf(f, v[e], acc[p][e]);
+        for (int e = 0; e < 4; ++e) {
+          const int c = 256 * p + 4 * lane + e;
+          acc[p][e] = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
         }
-      }
+      const uint32_t id = (uint32_t)(ck[rs] >> 32);
+      bool whole;
+      float* out = target(rs, re, id, &whole);
+      put_row<NP>(out, W, lane, whole && accumulate, acc);
     }
-    // whole segment inside this chunk: final row; else a partial (slot 0 if
-    // the run starts the chunk, 1 if it ends it)
-    const int64_t sf = first1[id] - 1, sl = last1[id];
-    const bool whole = sf >= c0 && sl <= c1;
-    float* out = whole ? dst + (int64_t)id * W
-                       : part + ((int64_t)blockIdx.x * 2 + (rs == 0 ? 0 : 1)) * W;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int col = 256 * p + 4 * lane;
-      if (col < W) {
-        float4* o = (float4*)(out + col);
-        float4 v = make_float4(acc[p][0], acc[p][1], acc[p][2], acc[p][3]);
-        if (whole && accumulate) {
-          const float4 q = *o;
-          v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
-        }
-        *o = v;
-      }
-    }
+    __syncthreads();
   }
 }
 
-// One block per id: rows of absent ids are cleared (unless accumulating),
-// ids cut by chunk boundaries get their partials added in chunk order.
+// One wavefront per id (4 ids per block): rows of absent ids are cleared
+// (unless accumulating), ids cut by chunk boundaries get their partials added
+// in chunk order.
 __global__ __launch_bounds__(256) void k_seg_fix(const int32_t* first1, const int32_t* last1,
-                                                 const float* part, int W, float* dst,
+                                                 const float* part, int V, int W, float* dst,
                                                  int accumulate) {
-  const int id = blockIdx.x;
+  const int id = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (id >= V) return;
   const int32_t f1 = first1[id];
   float* out = dst + (int64_t)id * W;
   if (f1 == 0) {
     if (!accumulate)
-      for (int col = threadIdx.x; col < W; col += blockDim.x) out[col] = 0.f;
+      for (int col = 4 * lane; col < W; col += 256) *(float4*)(out + col) = make_float4(0, 0, 0, 0);
     return;
   }
   const int64_t sf = f1 - 1, se = last1[id];
   const int64_t ca = sf / kChunk, cb = (se - 1) / kChunk;
   if (ca == cb) return;                                 // written whole by k_seg_rows
   const int sa = sf == ca * kChunk ? 0 : 1;
-  for (int col = threadIdx.x; col < W; col += blockDim.x) {
-    float v = part[(ca * 2 + sa) * W + col];
-    for (int64_t c = ca + 1; c <= cb; ++c) v += part[(c * 2) * W + col];
-    out[col] = accumulate ? out[col] + v : v;
+  for (int col = 4 * lane; col < W; col += 256) {
+    float4 v = *(const float4*)(part + (ca * 2 + sa) * W + col);
+    for (int64_t c = ca + 1; c <= cb; c += 8) {         // 8 loads in flight, added in order
+      float4 q[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        q[u] = c + u <= cb ? *(const float4*)(part + ((c + u) * 2) * W + col)
+                           : make_float4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        v.x += q[u].x; v.y += q[u].y; v.z += q[u].z; v.w += q[u].w;
+      }
+    }
+    if (accumulate) {
+      const float4 q = *(const float4*)(out + col);
+      v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+    }
+    *(float4*)(out + col) = v;
   }
 }
 
@@ -290,8 +376,8 @@ hipError_t seg_scatter(const void* scratch, int64_t N, int V, int maxW, const vo
   }
 #undef SEG_NP
 #undef SEG_ROWS
-  GK_LAUNCH(Work(), k_seg_fix, dim3((unsigned)V), dim3(256), 0, s, first1, last1,
-            (const float*)part, W, dst, accumulate);
+  GK_LAUNCH(Work(), k_seg_fix, dim3((unsigned)cdiv(V, 4)), dim3(256), 0, s, first1, last1,
+            (const float*)part, V, W, dst, accumulate);
   return hipGetLastError();
 }
 
