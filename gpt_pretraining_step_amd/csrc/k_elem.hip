@@ -532,42 +532,56 @@ hipError_t rope_qknorm_bwd(void* dqkv, const void* qkv, const float* rq, const f
 
 // -------------------------------------------------------- value embedding
 // One block per token.  Wave w computes the gates of KV heads w, w+4, ...
+// One wavefront per token (4 per block): the Hkv gates (3 sigmoid of a C-long
+// dot product, wave reductions), then v += g E[tok] over the Hkv hd values in
+// passes of 256 (lane: 4 consecutive values of one head).
 template <typename Tv>
-__global__ __launch_bounds__(256) void k_ve_fwd(const int32_t* tok, int T, const Tv* h, int D,
-                                                const Tv* wg, int C, const Tv* E, Tv* qkv,
+__global__ __launch_bounds__(256) void k_ve_fwd(const int32_t* tok, int T, int64_t N, const Tv* h,
+                                                int D, const Tv* wg, int C, const Tv* E, Tv* qkv,
                                                 int ldqkv, int voff, float* g, int Hkv, int hd) {
-  __shared__ float gs[64];
-  int64_t n = blockIdx.x;
-  int id = tok[(n / T) * (T + 1) + n % T];
-  int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int kv = w; kv < Hkv; kv += 4) {
+  __shared__ float gs[4][64];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t n = blockIdx.x * 4 + w;
+  if (n >= N) return;
+  const int id = tok[(n / T) * (T + 1) + n % T];
+  for (int kv = 0; kv < Hkv; ++kv) {
     float acc = 0.f;
-    for (int c = lane; c < C; c += 64) acc += ld(h, n * D + c) * ld(wg, (int64_t)kv * C + c);
+    for (int c = lane; c < C; c += 64) acc = fmaf(ld(h, n * D + c), ld(wg, (int64_t)kv * C + c), acc);
     acc = wave_sum(acc);
     if (lane == 0) {
-      float gv = 3.0f / (1.0f + expf(-acc));
-      gs[kv] = gv;
+      const float gv = 3.0f / (1.0f + expf(-acc));
+      gs[w][kv] = gv;
       g[n * Hkv + kv] = gv;
     }
   }
-  __syncthreads();
-  int tot = Hkv * hd;
-  for (int e = threadIdx.x; e < tot; e += blockDim.x) {
-    int64_t vi = n * ldqkv + voff + e;
-    st(qkv, vi, ld(qkv, vi) + gs[e / hd] * ld(E, (int64_t)id * tot + e));
+  // the gates written by lane 0 are read by the whole wave: LDS is coherent
+  // within the wave once the writes are issued (s_waitcnt before the reads)
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  const int W = Hkv * hd;
+  for (int c0 = 0; c0 < W; c0 += 256) {
+    const int col = c0 + 4 * lane;
+    if (col >= W) continue;
+    const float gv = gs[w][col / hd];
+    const int64_t vi = n * ldqkv + voff + col, ei = (int64_t)id * W + col;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st(qkv, vi + e, fmaf(gv, ld(E, ei + e), ld(qkv, vi + e)));
   }
 }
 
 hipError_t ve_fwd(const int32_t* tok, int B, int T, const void* h, int D, const void* wg, int C,
                   const void* E, void* qkv, int ldqkv, int voff, float* g, int Hkv, int hd,
                   DType dt, hipStream_t s) {
-  int64_t N = (int64_t)B * T;
+  const int64_t N = (int64_t)B * T;
+  if (Hkv > 64 || hd % 4) return hipErrorInvalidValue;
   if (dt == BF16)
-    GK_LAUNCH(Work(), k_ve_fwd<bf16>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const bf16*)h, D,
-                       (const bf16*)wg, C, (const bf16*)E, (bf16*)qkv, ldqkv, voff, g, Hkv, hd);
+    GK_LAUNCH(Work(), k_ve_fwd<bf16>, dim3((unsigned)cdiv(N, 4)), dim3(256), 0, s, tok, T, N,
+              (const bf16*)h, D, (const bf16*)wg, C, (const bf16*)E, (bf16*)qkv, ldqkv, voff, g,
+              Hkv, hd);
   else
-    GK_LAUNCH(Work(), k_ve_fwd<float>, dim3((unsigned)N), dim3(256), 0, s, tok, T, (const float*)h, D,
-                       (const float*)wg, C, (const float*)E, (float*)qkv, ldqkv, voff, g, Hkv, hd);
+    GK_LAUNCH(Work(), k_ve_fwd<float>, dim3((unsigned)cdiv(N, 4)), dim3(256), 0, s, tok, T, N,
+              (const float*)h, D, (const float*)wg, C, (const float*)E, (float*)qkv, ldqkv, voff,
+              g, Hkv, hd);
   return hipGetLastError();
 }
 
