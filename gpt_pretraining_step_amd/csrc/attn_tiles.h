@@ -147,10 +147,13 @@ __device__ __forceinline__ bf16x8_t tfrag(const bf16* s, int hrow, int ch, int g
 // ------------------------------------------------ buffer-to-LDS staged tiles
 // A [64 rows][128] tile as it sits in memory (256-byte rows, no padding),
 // filled by buffer loads straight into LDS.  The 16-byte chunk c of row r
-// is stored at chunk position c ^ dsw(r): 16-row fragment reads (one chunk
-// per row) and transposing reads (8 consecutive rows, 32 bytes each, per 32
-// lanes) both land in distinct bank slots.
-__device__ __forceinline__ int dsw(int r) { return (2 * (r & 7)) ^ ((r >> 3) & 1); }
+// is stored at chunk position c ^ dsw(r).  A 16-byte fragment read is served
+// 32 lanes (512 bytes) at a time: 16 rows x 2 adjacent chunks, so the rows of
+// each parity need distinct dsw(r) / 2; a transposing read covers 8
+// consecutive rows x 32 bytes, which needs dsw(r) / 2 distinct over aligned
+// groups of 8 rows.  dsw(r) = 2 ((r & 7) ^ ((r >> 3) & 1)) meets both (the
+// hardware's bank-conflict counter reads 0 for both reads of this layout).
+__device__ __forceinline__ int dsw(int r) { return 2 * ((r & 7) ^ ((r >> 3) & 1)); }
 __device__ __forceinline__ int doff(int r, int col) {
   return r * HD + 8 * ((col >> 3) ^ dsw(r)) + (col & 7);
 }
