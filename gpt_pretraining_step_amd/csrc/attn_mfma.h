@@ -9,7 +9,11 @@ bool attn_mfma_bwd_supported(int T, int H, int Hkv, int hd);
 hipError_t attn_mfma_fwd(const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv,
                          int hd, int W, hipStream_t s);
 size_t attn_mfma_bwd_scratch_bytes(int B, int T, int H, int hd);
+// nrq / nrk / ncs (all or none): 1/rms of the rotated q and k heads and the
+// (cos, sin) table; given, the dq and dk written are the gradients w.r.t.
+// the raw q and k (RoPE-then-QK-norm backward fused into the epilogues)
 hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const void* dout,
                          void* dqkv, float* delta, void* scratch, int B, int T, int H, int Hkv,
-                         int hd, int W, hipStream_t s);
+                         int hd, int W, hipStream_t s, const float* nrq, const float* nrk,
+                         const float* ncs);
 }  // namespace gk

@@ -364,10 +364,18 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
     g = gk::GemmDesc{gk::OP_NN, N, HD, m.D, dx, m.D, elem(params, pl.wo[l], es), HD, dout, HD,
                      gk::E_STORE, nullptr};
     HIP_TRY(gk::gemm(g, dt, s));
-    HIP_TRY(gk::attn_bwd(qkv, o, at<float>(ws, b.lse), dout, dqkv, at<void>(ws, p.attn_scr),
-                         m.B, m.T, m.H, m.Hkv, m.hd, m.window(l), dt, s));
-    HIP_TRY(gk::rope_qknorm_bwd(dqkv, qkv, at<float>(ws, b.rq), at<float>(ws, b.rk), cs, m.B,
-                                m.T, m.H, m.Hkv, m.hd, dt, s));
+    // attention backward; where the kernels can, they also apply the
+    // backward of RoPE-then-QK-norm in their epilogues
+    if (gk::attn_bwd_fuses_norm(m.T, m.H, m.Hkv, m.hd, dt)) {
+      HIP_TRY(gk::attn_bwd(qkv, o, at<float>(ws, b.lse), dout, dqkv, at<void>(ws, p.attn_scr),
+                           m.B, m.T, m.H, m.Hkv, m.hd, m.window(l), dt, s, at<float>(ws, b.rq),
+                           at<float>(ws, b.rk), cs));
+    } else {
+      HIP_TRY(gk::attn_bwd(qkv, o, at<float>(ws, b.lse), dout, dqkv, at<void>(ws, p.attn_scr),
+                           m.B, m.T, m.H, m.Hkv, m.hd, m.window(l), dt, s));
+      HIP_TRY(gk::rope_qknorm_bwd(dqkv, qkv, at<float>(ws, b.rq), at<float>(ws, b.rk), cs, m.B,
+                                  m.T, m.H, m.Hkv, m.hd, dt, s));
+    }
     const bool ve = m.is_ve(l);
     if (ve) {
       const int voff = (m.H + m.Hkv) * m.hd;

@@ -163,14 +163,19 @@ size_t attn_bwd_scratch_bytes(int B, int T, int H, int hd) {
   return ((delta + 255) / 256) * 256 + attn_mfma_bwd_scratch_bytes(B, T, H, hd);
 }
 
+bool attn_bwd_fuses_norm(int T, int H, int Hkv, int hd, DType dt) {
+  return dt == BF16 && attn_mfma_bwd_supported(T, H, Hkv, hd);
+}
+
 hipError_t attn_bwd(const void* qkv, const void* o, const float* lse, const void* dout,
                     void* dqkv, void* scratch, int B, int T, int H, int Hkv, int hd, int W,
-                    DType dt, hipStream_t s) {
+                    DType dt, hipStream_t s, const float* nrq, const float* nrk,
+                    const float* ncs) {
   float* delta = (float*)scratch;
   if (dt == BF16 && attn_mfma_bwd_supported(T, H, Hkv, hd)) {
     size_t dbytes = (((size_t)B * H * T * sizeof(float) + 255) / 256) * 256;
     return attn_mfma_bwd(qkv, o, lse, dout, dqkv, delta, (char*)scratch + dbytes, B, T, H, Hkv,
-                         hd, W, s);
+                         hd, W, s, nrq, nrk, ncs);
   }
   const int64_t rows = (int64_t)B * H * T;
   const int64_t krows = (int64_t)B * Hkv * T;

@@ -250,6 +250,53 @@ __global__ __launch_bounds__(256) void k_attn_delta(const bf16* __restrict__ o,
   }
 }
 
+// Backward of "RoPE then QK-norm" fused into the dQ / dK epilogues (used by
+// the step; the kernel-level entry leaves it out).  One head row (hd = 128)
+// sits in the MFMA output layout: lane (g, l16) holds x[16 hb + 4 g + r],
+// hb < 8, r < 4 (the gradient w.r.t. the normalised q or k, already
+// scaled).  It is rounded to bf16 as the unfused path stores it, then
+// dx = rr (x - y mean(x y)) with y the saved normalised row and rr its
+// 1/rms, then the rotation is undone: pairs (d, d + 64) are (hb, hb + 4) of
+// the same lane.  The four lanes of a row (g = 0..3) finish the dot product
+// with two shuffles.
+struct NormBwdArgs {
+  const float* rq;      // [B*T, H] 1/rms of the rotated q heads
+  const float* rk;      // [B*T, Hkv]
+  const float2* cs;     // [T, 64] (cos, sin)
+};
+
+__device__ __forceinline__ void norm_rope_bwd_row(float (&x)[8][4], const bf16* yrow, float rr,
+                                                  const float2* csrow, int g, bool ok) {
+  float y[8][4];
+  float acc = 0.f;
+#pragma unroll
+  for (int hb = 0; hb < 8; ++hb) {
+    const uint2 u = ok ? *(const uint2*)(yrow + 16 * hb + 4 * g) : make_uint2(0, 0);
+    y[hb][0] = __uint_as_float(u.x << 16);
+    y[hb][1] = __uint_as_float(u.x & 0xFFFF0000u);
+    y[hb][2] = __uint_as_float(u.y << 16);
+    y[hb][3] = __uint_as_float(u.y & 0xFFFF0000u);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[hb][r] = bf2f(f2bf(x[hb][r]));
+      acc = fmaf(x[hb][r], y[hb][r], acc);
+    }
+  }
+  acc += __shfl_xor(acc, 16, 64);
+  acc += __shfl_xor(acc, 32, 64);
+  const float m = acc / (float)HD;
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float2 c = ok ? csrow[16 * hb + 4 * g + r] : make_float2(1.f, 0.f);
+      const float a1 = rr * (x[hb][r] - y[hb][r] * m), a2 = rr * (x[hb + 4][r] - y[hb + 4][r] * m);
+      x[hb][r] = a1 * c.x + a2 * c.y;
+      x[hb + 4][r] = -a1 * c.y + a2 * c.x;
+    }
+  }
+}
+
 // dK, dV of 128 keys of one KV head (4 waves x 32 keys), summed over the G
 // query heads of the group and every 64-query tile that sees these keys.
 // Scores are formed queries x keys (X = Q tile rows, Y = K in registers), so
@@ -263,13 +310,13 @@ static constexpr int KV_BK = NW * 32;          // keys per workgroup
 // MODE: 0 = dK and dV together (one wave per SIMD: both accumulators and the
 // K and V fragments do not fit two), 1 = dK only, 2 = dV only (each fits two
 // waves per SIMD; dV needs no dP, Delta or Q^T, dK no dO^T).
-template <int NQB, int MODE>
+template <int NQB, int MODE, bool FUSE>
 __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const bf16* __restrict__ qkv,
                                                          const bf16* __restrict__ dout,
                                                          const float* __restrict__ lse,
                                                          const float* __restrict__ delta,
                                                          bf16* __restrict__ dqkv, int T, int H,
-                                                         int Hkv, int W) {
+                                                         int Hkv, int W, NormBwdArgs nb) {
   __shared__ __attribute__((aligned(16))) bf16 qd[2][2][TR * HD];   // stages of (Q, dO)
   __shared__ __attribute__((aligned(16))) float ldl[2][2][256];      // stages of (lse, delta)
 
@@ -425,15 +472,32 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = kw + 16 * kb + lr;
-    if (key >= T) continue;
+    const bool ok = key < T;
+    if constexpr (DO_K && FUSE) {          // every lane of the row takes part
+      float x[8][4];
+#pragma unroll
+      for (int hb = 0; hb < 8; ++hb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[hb][r] = dk[hb][kb][r] * scale;
+      const int64_t n = (int64_t)b * T + (ok ? key : 0);
+      norm_rope_bwd_row(x, qkv + n * ldq + (int64_t)(H + kvh) * HD,
+                        ok ? nb.rk[n * Hkv + kvh] : 0.f, nb.cs + (int64_t)(ok ? key : 0) * (HD / 2),
+                        g, ok);
+#pragma unroll
+      for (int hb = 0; hb < 8; ++hb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dk[hb][kb][r] = x[hb][r];
+    }
+    if (!ok) continue;
     bf16* krow = dqkv + ((int64_t)b * T + key) * ldq + (int64_t)(H + kvh) * HD;
     bf16* vrow = dqkv + ((int64_t)b * T + key) * ldq + (int64_t)(H + Hkv + kvh) * HD;
+    const float ks = FUSE ? 1.f : scale;
 #pragma unroll
     for (int hb = 0; hb < 8; ++hb) {
       if constexpr (DO_K) {
         uint2 uk;
-        uk.x = pack2bf(dk[hb][kb][0] * scale, dk[hb][kb][1] * scale);
-        uk.y = pack2bf(dk[hb][kb][2] * scale, dk[hb][kb][3] * scale);
+        uk.x = pack2bf(dk[hb][kb][0] * ks, dk[hb][kb][1] * ks);
+        uk.y = pack2bf(dk[hb][kb][2] * ks, dk[hb][kb][3] * ks);
         *(uint2*)(krow + 16 * hb + 4 * g) = uk;
       }
       if constexpr (DO_V) {
@@ -449,12 +513,13 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
 // dQ of 128 queries of one head (4 waves x 32), over the key tiles they see.
 // Scores keys x queries as in the forward; dS feeds dQ^T += K^T dS with the
 // K^T fragments gathered from the K tile by transposing LDS reads.
+template <bool FUSE>
 __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(const bf16* __restrict__ qkv,
                                                         const bf16* __restrict__ dout,
                                                         const float* __restrict__ lse,
                                                         const float* __restrict__ delta,
                                                         bf16* __restrict__ dqkv, int T, int H,
-                                                        int Hkv, int W) {
+                                                        int Hkv, int W, NormBwdArgs nb) {
   __shared__ __attribute__((aligned(16))) bf16 kv[2][2][TR * HD];   // stages of (K, V)
 
   const int nqb = (T + FWD_BQ - 1) / FWD_BQ;
@@ -579,13 +644,24 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(const bf16* __restrict__
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qi = qw + 16 * qb + lr;
-    if (qi >= T) continue;
+    const bool ok = qi < T;
+    float x[8][4];
+#pragma unroll
+    for (int hb = 0; hb < 8; ++hb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[hb][r] = dq[hb][qb][r] * scale;
+    if constexpr (FUSE) {                  // every lane of the row takes part
+      const int64_t n = (int64_t)b * T + (ok ? qi : 0);
+      norm_rope_bwd_row(x, qkv + n * ldq + (int64_t)h * HD, ok ? nb.rq[n * H + h] : 0.f,
+                        nb.cs + (int64_t)(ok ? qi : 0) * (HD / 2), g, ok);
+    }
+    if (!ok) continue;
     bf16* row = dqkv + ((int64_t)b * T + qi) * ldq + (int64_t)h * HD;
 #pragma unroll
     for (int hb = 0; hb < 8; ++hb) {
       uint2 u;
-      u.x = pack2bf(dq[hb][qb][0] * scale, dq[hb][qb][1] * scale);
-      u.y = pack2bf(dq[hb][qb][2] * scale, dq[hb][qb][3] * scale);
+      u.x = pack2bf(x[hb][0], x[hb][1]);
+      u.y = pack2bf(x[hb][2], x[hb][3]);
       *(uint2*)(row + 16 * hb + 4 * g) = u;
     }
   }
@@ -599,8 +675,11 @@ size_t attn_mfma_bwd_scratch_bytes(int, int, int, int) { return 0; }
 
 hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const void* dout,
                          void* dqkv, float* delta, void*, int B, int T, int H, int Hkv, int hd,
-                         int W, hipStream_t s) {
+                         int W, hipStream_t s, const float* nrq, const float* nrk,
+                         const float* ncs) {
   (void)hd;
+  const bool fuse = nrq && nrk && ncs;
+  const NormBwdArgs nb{nrq, nrk, (const float2*)ncs};
   const int64_t rows = (int64_t)B * T * H;
   // per kernel: 2 hd flops per visible pair and matrix product formed
   // (dK pass: S, dP, dK; dV pass: S, dV; dQ pass: S, dP, dQ); operands read
@@ -610,19 +689,24 @@ hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const
   const Work wd(0.0, tok * H * HD * 2 * 2 + rows * 4.0);
   const Work wq(6.0 * HD * pairs, qkvo + stats + tok * H * HD * 2);
   GK_LAUNCH(wd, k_attn_delta, dim3((unsigned)cdiv(rows * 16, 256)), dim3(256), 0, s,
-                     (const bf16*)o, (const bf16*)dout, delta, T, H, rows);
+            (const bf16*)o, (const bf16*)dout, delta, T, H, rows);
   // dK and dV in two passes (two waves per SIMD each; measured faster than
   // the one-wave-per-SIMD combined pass despite recomputing S)
   const dim3 gkv((T + KV_BK - 1) / KV_BK, Hkv, B);
   const Work wk(6.0 * HD * pairs, qkvo + stats + tok * Hkv * HD * 2);
   const Work wv(4.0 * HD * pairs, qkvo + stats / 2 + tok * Hkv * HD * 2);
-  GK_LAUNCH(wk, (k_attn_bwd_dkv<2, 1>), gkv, dim3(NW * 64), 0, s, (const bf16*)qkv,
-            (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T, H, Hkv, W);
-  GK_LAUNCH(wv, (k_attn_bwd_dkv<2, 2>), gkv, dim3(NW * 64), 0, s, (const bf16*)qkv,
-            (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T, H, Hkv, W);
-  GK_LAUNCH(wq, k_attn_bwd_dq, dim3((T + FWD_BQ - 1) / FWD_BQ, H, B), dim3(NW * 64), 0, s,
-                     (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T,
-                     H, Hkv, W);
+  const dim3 gq((T + FWD_BQ - 1) / FWD_BQ, H, B);
+#define DKV_ARGS (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T, H, Hkv, W, nb
+  if (fuse) {
+    GK_LAUNCH(wk, (k_attn_bwd_dkv<2, 1, true>), gkv, dim3(NW * 64), 0, s, DKV_ARGS);
+    GK_LAUNCH(wv, (k_attn_bwd_dkv<2, 2, false>), gkv, dim3(NW * 64), 0, s, DKV_ARGS);
+    GK_LAUNCH(wq, k_attn_bwd_dq<true>, gq, dim3(NW * 64), 0, s, DKV_ARGS);
+  } else {
+    GK_LAUNCH(wk, (k_attn_bwd_dkv<2, 1, false>), gkv, dim3(NW * 64), 0, s, DKV_ARGS);
+    GK_LAUNCH(wv, (k_attn_bwd_dkv<2, 2, false>), gkv, dim3(NW * 64), 0, s, DKV_ARGS);
+    GK_LAUNCH(wq, k_attn_bwd_dq<false>, gq, dim3(NW * 64), 0, s, DKV_ARGS);
+  }
+#undef DKV_ARGS
   return hipGetLastError();
 }
 

@@ -89,9 +89,15 @@ hipError_t ve_vez(const int32_t* tok, int B, int T, const void* dqkv, int ldqkv,
 hipError_t attn_fwd(const void* qkv, void* o, float* lse, int B, int T,
                     int H, int Hkv, int hd, int W, DType dt, hipStream_t s);
 size_t attn_bwd_scratch_bytes(int B, int T, int H, int hd);
+// With nrq / nrk / ncs (1/rms of the rotated q, k heads and the rope table)
+// and attn_bwd_fuses_norm() true, the backward of RoPE-then-QK-norm is
+// applied too (dq, dk w.r.t. the raw q, k); otherwise they are ignored.
+bool attn_bwd_fuses_norm(int T, int H, int Hkv, int hd, DType dt);
 hipError_t attn_bwd(const void* qkv, const void* o, const float* lse,
                     const void* dout, void* dqkv, void* scratch, int B, int T,
-                    int H, int Hkv, int hd, int W, DType dt, hipStream_t s);
+                    int H, int Hkv, int hd, int W, DType dt, hipStream_t s,
+                    const float* nrq = nullptr, const float* nrk = nullptr,
+                    const float* ncs = nullptr);
 
 // cross-entropy over fp32 logits; tgt given by a token-row pointer:
 // target of row n = tok[(n / T) * (T+1) + n % T + 1]  (T = tgt_T)
