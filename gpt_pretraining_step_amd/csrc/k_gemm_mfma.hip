@@ -153,28 +153,49 @@ using Stage = typename std::conditional<TRANS, KColStage<R, NT, XS>, KRowStage<R
 
 // ------------------------------------------------------------ epilogue x4
 // Four consecutive columns n..n+3 of row m (n % 4 == 0, N % 4 == 0).
+// Epilogues that read memory (residual add: C; ReLU² backward: u; fp32
+// accumulate: C) take what they read as `in`, loaded by epi_load, so a
+// kernel can issue the loads of many fragments before the first one is used.
 template <int EPI>
-__device__ __forceinline__ void epi4(void* Cv, void* auxv, int64_t ldc, int64_t m, int64_t n,
-                                     f32x4_t a) {
-  const int64_t i = m * ldc + n;
+struct EpiIn {
+  typedef uint2 type;       // 4 bf16
+};
+template <>
+struct EpiIn<E_F32_ACC> {
+  typedef f32x4_t type;
+};
+template <int EPI>
+constexpr bool epi_reads() {
+  return EPI == E_RESADD || EPI == E_DRELU2 || EPI == E_F32_ACC;
+}
+
+template <int EPI>
+__device__ __forceinline__ typename EpiIn<EPI>::type epi_load(const void* Cv, const void* auxv,
+                                                              int64_t i) {
+  if constexpr (EPI == E_F32_ACC) return *(const f32x4_t*)((const float*)Cv + i);
+  else if constexpr (EPI == E_DRELU2) return *(const uint2*)((const bf16*)auxv + i);
+  else if constexpr (EPI == E_RESADD) return *(const uint2*)((const bf16*)Cv + i);
+  else return uint2{0u, 0u};
+}
+
+template <int EPI>
+__device__ __forceinline__ void epi4_in(void* Cv, void* auxv, int64_t i, f32x4_t a,
+                                        typename EpiIn<EPI>::type in) {
   if constexpr (EPI == E_F32) {
     *(f32x4_t*)((float*)Cv + i) = a;
   } else if constexpr (EPI == E_F32_ACC) {
-    f32x4_t* p = (f32x4_t*)((float*)Cv + i);
-    *p = *p + a;
+    *(f32x4_t*)((float*)Cv + i) = in + a;
   } else {
     bf16* C = (bf16*)Cv;
     float v[4] = {a[0], a[1], a[2], a[3]};
     if constexpr (EPI == E_RESADD) {
-      const uint2 r = *(const uint2*)(C + i);
-      v[0] += __uint_as_float(r.x << 16); v[1] += __uint_as_float(r.x & 0xFFFF0000u);
-      v[2] += __uint_as_float(r.y << 16); v[3] += __uint_as_float(r.y & 0xFFFF0000u);
+      v[0] += __uint_as_float(in.x << 16); v[1] += __uint_as_float(in.x & 0xFFFF0000u);
+      v[2] += __uint_as_float(in.y << 16); v[3] += __uint_as_float(in.y & 0xFFFF0000u);
     } else if constexpr (EPI == E_DRELU2) {
-      const uint2 u = *(const uint2*)((const bf16*)auxv + i);
-      v[0] *= 2.0f * fmaxf(__uint_as_float(u.x << 16), 0.f);
-      v[1] *= 2.0f * fmaxf(__uint_as_float(u.x & 0xFFFF0000u), 0.f);
-      v[2] *= 2.0f * fmaxf(__uint_as_float(u.y << 16), 0.f);
-      v[3] *= 2.0f * fmaxf(__uint_as_float(u.y & 0xFFFF0000u), 0.f);
+      v[0] *= 2.0f * fmaxf(__uint_as_float(in.x << 16), 0.f);
+      v[1] *= 2.0f * fmaxf(__uint_as_float(in.x & 0xFFFF0000u), 0.f);
+      v[2] *= 2.0f * fmaxf(__uint_as_float(in.y << 16), 0.f);
+      v[3] *= 2.0f * fmaxf(__uint_as_float(in.y & 0xFFFF0000u), 0.f);
     }
     uint2 o;
     o.x = pack2bf(v[0], v[1]);
@@ -189,6 +210,13 @@ __device__ __forceinline__ void epi4(void* Cv, void* auxv, int64_t ldc, int64_t 
       *(uint2*)((bf16*)auxv + i) = q;
     }
   }
+}
+
+template <int EPI>
+__device__ __forceinline__ void epi4(void* Cv, void* auxv, int64_t ldc, int64_t m, int64_t n,
+                                     f32x4_t a) {
+  const int64_t i = m * ldc + n;
+  epi4_in<EPI>(Cv, auxv, i, a, epi_load<EPI>(Cv, auxv, i));
 }
 
 // --------------------------------------------------------- one K-slice
@@ -600,12 +628,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
   pb.issue(kbeg, st0 + BM * 64, wave);
   int it = 0;
   for (; it + 2 <= nsl; it += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    dma_wait();
     __syncthreads();
     pa.issue(kbeg + (int64_t)(it + 1) * BK, st1, wave);
     pb.issue(kbeg + (int64_t)(it + 1) * BK, st1 + BM * 64, wave);
     compute(st0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    dma_wait();
     __syncthreads();
     if (it + 2 < nsl) {
       pa.issue(kbeg + (int64_t)(it + 2) * BK, st0, wave);
@@ -614,7 +642,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
     compute(st1);
   }
   if (it < nsl) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    dma_wait();
     __syncthreads();
     compute(st0);
   }
@@ -633,13 +661,23 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
     }
     return;
   }
+  // per 16-row group: every load of the group first, then the stores (one
+  // memory latency per group instead of one per fragment)
 #pragma unroll
   for (int i = 0; i < TMI; ++i) {
     const int64_t m = m0 + wm + 16 * i + lr;
+    typename EpiIn<EPI>::type in[TNJ];
+    if constexpr (epi_reads<EPI>()) {
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j) {
+        const int64_t n = n0 + wn + 16 * j + cq;
+        if (m < M && n < N) in[j] = epi_load<EPI>(C, aux, m * ldc + n);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TNJ; ++j) {
       const int64_t n = n0 + wn + 16 * j + cq;
-      if (m < M && n < N) epi4<EPI>(C, aux, ldc, m, n, acc[i][j]);
+      if (m < M && n < N) epi4_in<EPI>(C, aux, m * ldc + n, acc[i][j], in[j]);
     }
   }
 }
