@@ -78,7 +78,8 @@ _SIGS = {
                                         _f32, _i32, _vp]),
     "gpt_k_rope_qknorm_bwd": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                         _i32, _i32, _vp]),
-    "gpt_k_attn_fwd": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "gpt_k_attn_fwd": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                 _vp]),
     "gpt_k_attn_bwd_scratch_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "gpt_k_attn_bwd": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _vp]),
@@ -212,9 +213,9 @@ def k_rope_qknorm_bwd(dqkv, qkv, rq, rk, cs, B, T, H, Hkv, hd, dtype, stream=Non
                                        T, H, Hkv, hd, dtype, _stream(stream)))
 
 
-def k_attn_fwd(qkv, o, lse, B, T, H, Hkv, hd, window, dtype, stream=None):
+def k_attn_fwd(qkv, o, lse, B, T, H, Hkv, hd, window, dtype, stream=None, score_bound=0.0):
     _check(lib().gpt_k_attn_fwd(_ptr(qkv), _ptr(o), _ptr(lse), B, T, H, Hkv, hd, window, dtype,
-                                _stream(stream)))
+                                score_bound, _stream(stream)))
 
 
 def k_attn_bwd_scratch_bytes(B, T, H, hd):

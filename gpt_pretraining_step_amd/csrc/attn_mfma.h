@@ -6,8 +6,10 @@
 namespace gk {
 bool attn_mfma_supported(int T, int H, int Hkv, int hd);
 bool attn_mfma_bwd_supported(int T, int H, int Hkv, int hd);
+// score_bound > 0: every |q . k| / sqrt(hd) is at most score_bound (the
+// caller's guarantee; 0 = unknown)
 hipError_t attn_mfma_fwd(const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv,
-                         int hd, int W, hipStream_t s);
+                         int hd, int W, hipStream_t s, float score_bound);
 size_t attn_mfma_bwd_scratch_bytes(int B, int T, int H, int hd);
 // nrq / nrk / ncs (all or none): 1/rms of the rotated q and k heads and the
 // (cos, sin) table; given, the dq and dk written are the gradients w.r.t.

@@ -258,8 +258,10 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
                          at<float>(ws, b.g), m.Hkv, m.hd, dt, s));
     HIP_TRY(gk::rope_qknorm_fwd(qkv, at<float>(ws, b.rq), at<float>(ws, b.rk), cs, rows, m.T,
                                 m.H, m.Hkv, m.hd, m.eps, dt, s));
+    // q and k rows are RMS-normalised (norm <= sqrt(hd), times 1 + 2^-8 per
+    // factor after bf16 rounding), so |q . k| / sqrt(hd) <= 1.01 sqrt(hd)
     HIP_TRY(gk::attn_fwd(qkv, o, at<float>(ws, b.lse), rows, m.T, m.H, m.Hkv, m.hd, m.window(l),
-                         dt, s));
+                         dt, s, 1.01f * sqrtf((float)m.hd)));
     g = gk::GemmDesc{gk::OP_NT, N, m.D, (int64_t)m.H * m.hd, o, (int64_t)m.H * m.hd,
                      elem(params, pl.wo[l], es), (int64_t)m.H * m.hd, x, m.D, gk::E_RESADD,
                      nullptr};
@@ -646,13 +648,17 @@ int gpt_k_rope_qknorm_bwd(void* dqkv, const void* qkv, const float* rq, const fl
 }
 
 int gpt_k_attn_fwd(const void* qkv, void* o, float* lse, int32_t B, int32_t T, int32_t H,
-                   int32_t Hkv, int32_t hd, int32_t window, int32_t dtype, hipStream_t s) {
+                   int32_t Hkv, int32_t hd, int32_t window, int32_t dtype, float score_bound,
+                   hipStream_t s) {
   int st;
   if ((st = dtype_ok(dtype)) || (st = check_ptrs({qkv, o, lse})) ||
       (st = attn_shape_ok(B, T, H, Hkv, hd)))
     return st;
   if (window < 0) return fail(GPT_ERR_INVALID_ARG, "window < 0");
-  KERNEL_TRY(gk::attn_fwd(qkv, o, lse, B, T, H, Hkv, hd, window, (gk::DType)dtype, s));
+  if (!(score_bound >= 0.f) || !(score_bound < 64.f))
+    return fail(GPT_ERR_INVALID_ARG, "score_bound outside [0, 64)");
+  KERNEL_TRY(gk::attn_fwd(qkv, o, lse, B, T, H, Hkv, hd, window, (gk::DType)dtype, s,
+                          score_bound));
   return GPT_OK;
 }
 

@@ -144,9 +144,9 @@ __global__ __launch_bounds__(256) void k_attn_bwd_dkv_row(const Tv* qkv, const f
 }
 
 hipError_t attn_fwd(const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv, int hd,
-                    int W, DType dt, hipStream_t s) {
+                    int W, DType dt, hipStream_t s, float score_bound) {
   if (dt == BF16 && attn_mfma_supported(T, H, Hkv, hd))
-    return attn_mfma_fwd(qkv, o, lse, B, T, H, Hkv, hd, W, s);
+    return attn_mfma_fwd(qkv, o, lse, B, T, H, Hkv, hd, W, s, score_bound);
   const int64_t rows = (int64_t)B * H * T;
   dim3 grid((unsigned)cdiv(rows, 4)), block(256);
   if (dt == BF16)

@@ -35,10 +35,18 @@ __device__ __forceinline__ void key_range(int q_lo, int q_hi, int W, int& lo, in
   hi = q_hi;
 }
 
+// BOUNDED: the caller guarantees |q . k| / sqrt(hd) <= bound for every pair
+// (true after QK-norm: RMS-normalised rows have norm <= sqrt(hd)), passed as
+// off2 = bound * log2(e).  Then p = 2^(s log2(e) / sqrt(hd) - off2) <= 1 for
+// every score with one fixed offset, so the online max, the rescaling of the
+// output and the lazy-offset logic all drop out (the row sums stay fp32 sums
+// of the unrounded P).  Without a bound the offset follows the running
+// maximum.
+template <bool BOUNDED>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict__ qkv,
                                                           bf16* __restrict__ o,
                                                           float* __restrict__ lse, int T, int H,
-                                                          int Hkv, int W) {
+                                                          int Hkv, int W, float off2) {
   // two stages of (K tile, V tile), filled by buffer loads straight into LDS
   __shared__ __attribute__((aligned(16))) bf16 kv[2][2][TR * HD];
 
@@ -129,6 +137,21 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
             s[kb][qb][r] = (unsigned)d > (unsigned)W ? -INFINITY : s[kb][qb][r];
           }
     }
+    if constexpr (BOUNDED) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float ls = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], sl2, -off2));
+            s[kb][qb][r] = p;
+            ls += p;
+          }
+        l[qb] += ls;
+      }
+    } else {
     bool grew = false;
     float alpha[2];
 #pragma unroll
@@ -167,6 +190,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
 #pragma unroll
         for (int hb = 0; hb < 8; ++hb) oacc[hb][qb] *= alpha[qb];
     }
+    }
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
       bf16x8_t pf[2];
@@ -198,7 +222,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
       u.y = pack2bf(oacc[hb][qb][2] * inv, oacc[hb][qb][3] * inv);
       *(uint2*)(orow + 16 * hb + 4 * g) = u;
     }
-    if (g == 0) lse[((int64_t)b * H + h) * T + qi] = (m[qb] * sl2 + log2f(lt)) * kLn2;
+    const float off = BOUNDED ? off2 : m[qb] * sl2;
+    if (g == 0) lse[((int64_t)b * H + h) * T + qi] = (off + log2f(lt)) * kLn2;
   }
 }
 
@@ -207,15 +232,19 @@ bool attn_mfma_supported(int T, int H, int Hkv, int hd) {
 }
 
 hipError_t attn_mfma_fwd(const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv,
-                         int hd, int W, hipStream_t s) {
+                         int hd, int W, hipStream_t s, float score_bound) {
   (void)hd;
   dim3 grid((T + FWD_BQ - 1) / FWD_BQ, H, B);
   // 2 hd flops per visible pair for each of S = Q K^T and O = P V; q, k, v
   // read once, o and lse written once
   const double pairs = (double)B * H * visible_pairs(T, W), tok = (double)B * T;
   const Work w(4.0 * HD * pairs, tok * HD * 2 * (2.0 * H + 2 * Hkv) + tok * H * 4);
-  GK_LAUNCH(w, k_attn_fwd_mfma, grid, dim3(NW * 64), 0, s, (const bf16*)qkv, (bf16*)o, lse,
-                     T, H, Hkv, W);
+  if (score_bound > 0.f)
+    GK_LAUNCH(w, k_attn_fwd_mfma<true>, grid, dim3(NW * 64), 0, s, (const bf16*)qkv, (bf16*)o,
+              lse, T, H, Hkv, W, score_bound * kLog2e);
+  else
+    GK_LAUNCH(w, k_attn_fwd_mfma<false>, grid, dim3(NW * 64), 0, s, (const bf16*)qkv, (bf16*)o,
+              lse, T, H, Hkv, W, 0.f);
   return hipGetLastError();
 }
 

@@ -86,8 +86,12 @@ hipError_t ve_vez(const int32_t* tok, int B, int T, const void* dqkv, int ldqkv,
                   const void* E, const float* g, float* vez, int Hkv, int hd, DType dt,
                   hipStream_t s);
 
+// score_bound > 0: the caller guarantees |q . k| / sqrt(hd) <= score_bound
+// for every pair (QK-normed rows: sqrt(hd)); lets the kernel use one fixed
+// softmax offset.  0: no bound known.
 hipError_t attn_fwd(const void* qkv, void* o, float* lse, int B, int T,
-                    int H, int Hkv, int hd, int W, DType dt, hipStream_t s);
+                    int H, int Hkv, int hd, int W, DType dt, hipStream_t s,
+                    float score_bound = 0.f);
 size_t attn_bwd_scratch_bytes(int B, int T, int H, int hd);
 // With nrq / nrk / ncs (1/rms of the rotated q, k heads and the rope table)
 // and attn_bwd_fuses_norm() true, the backward of RoPE-then-QK-norm is

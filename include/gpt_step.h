@@ -240,10 +240,15 @@ int gpt_k_rope_qknorm_bwd(void* dqkv, const void* qkv, const float* rq,
 
 /* Attention over qkv [B*T, (H+2Hkv) hd] -> o [B*T, H hd], lse [B, H, T];
  * causal, window `window` (keys i-window..i), query head h reads KV head
- * h / (H / Hkv); scale 1/sqrt(hd). */
+ * h / (H / Hkv); scale 1/sqrt(hd).  score_bound: 0, or a bound the caller
+ * guarantees on every |q . k| / sqrt(hd) (rows after QK-norm: a little over
+ * sqrt(hd)); with a bound the bf16 hd-128 kernel uses one fixed softmax
+ * offset instead of a running maximum (scores above the bound by more than
+ * ~80 would overflow).  Must lie in [0, 64), else GPT_ERR_INVALID_ARG. */
 int gpt_k_attn_fwd(const void* qkv, void* o, float* lse, int32_t B,
                    int32_t T, int32_t H, int32_t Hkv, int32_t hd,
-                   int32_t window, int32_t dtype, hipStream_t s);
+                   int32_t window, int32_t dtype, float score_bound,
+                   hipStream_t s);
 
 /* Gradients of gpt_k_attn_fwd: dqkv (same layout as qkv) from do [B*T, H hd].
  * scratch: device, >= gpt_k_attn_bwd_scratch_bytes(B, T, H, hd) bytes. */

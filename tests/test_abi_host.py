@@ -114,8 +114,10 @@ def test_entry_points_reject_bad_pointers_before_launch():
     assert L.gpt_k_gemm(0, 4, 4, 4, A, 2, A, 4, A, 4, 0, None, None, 0, 1, None) == -1
     assert L.gpt_k_gemm(0, 4, 4, 4, A, 4, A, 4, A, 4, 2, None, None, 0, 1, None) == -1
     assert L.gpt_k_gemm(0, 4, 4, 4, A, 4, A, 4, A, 4, 0, None, C.c_void_p(0x1008), 64, 1, None) == -4
-    assert L.gpt_k_attn_fwd(A, A, A, 1, 8, 3, 2, 128, 4, 1, None) == -1
-    assert L.gpt_k_attn_fwd(A, A, A, 1, 8, 2, 2, 96, 4, 1, None) == -2
+    assert L.gpt_k_attn_fwd(A, A, A, 1, 8, 3, 2, 128, 4, 1, 0.0, None) == -1
+    assert L.gpt_k_attn_fwd(A, A, A, 1, 8, 2, 2, 96, 4, 1, 0.0, None) == -2
+    assert L.gpt_k_attn_fwd(A, A, A, 1, 8, 2, 2, 128, 4, 1, -1.0, None) == -1
+    assert L.gpt_k_attn_fwd(A, A, A, 1, 8, 2, 2, 128, 4, 1, float("nan"), None) == -1
     assert L.gpt_k_rmsnorm_fwd(A, C.c_void_p(0x1002), A, 4, 8, 1e-5, 1, None) == -4
 
 

@@ -290,10 +290,13 @@ def _attn_inputs(B, T, H, Hkv, hd, bf, seed=12):
     return q, k, v, qkv
 
 
+@pytest.mark.parametrize("bounded", [False, True])
 @pytest.mark.parametrize("case", ATTN_CASES)
-def test_attention_fwd_bwd(case):
+def test_attention_fwd_bwd(case, bounded):
+    """bounded: the forward is told that |q . k| / sqrt(hd) <= 1.01 sqrt(hd),
+    which holds for these unit-RMS rows (the step's QK-normed q and k)."""
     dt, B, T, H, Hkv, hd, W = case
-    say("attn", case)
+    say("attn", case, "bounded" if bounded else "")
     bf = dt == G.BF16
     num = _Num("bf16emu" if bf else "fp32")
     q, k, v, qkv = _attn_inputs(B, T, H, Hkv, hd, bf)
@@ -303,7 +306,8 @@ def test_attention_fwd_bwd(case):
     tqkv = dev(qkv, tdtype(dt)).reshape(B * T, -1)
     to = torch.empty(B * T, H * hd, dtype=tdtype(dt), device=DEV)
     tl = torch.empty(B * H * T, dtype=torch.float32, device=DEV)
-    G.k_attn_fwd(tqkv, to, tl, B, T, H, Hkv, hd, W, dt)
+    G.k_attn_fwd(tqkv, to, tl, B, T, H, Hkv, hd, W, dt,
+                 score_bound=1.01 * np.sqrt(hd) if bounded else 0.0)
     # the backward consumes the kernel's own o and lse, as in the step
     tdq = torch.zeros_like(tqkv)
     scr = torch.empty(max(16, G.k_attn_bwd_scratch_bytes(B, T, H, hd)), dtype=torch.uint8,
@@ -326,9 +330,10 @@ def test_attention_fwd_bwd(case):
     assert rel_err(g[..., (H + Hkv) * hd:], dv_ref.reshape(B, T, -1)) < tol
 
 
+@pytest.mark.parametrize("bounded", [False, True])
 @pytest.mark.parametrize("W", [0, 1, 31, 32, 64, 127, 128])
 @pytest.mark.parametrize("hd", [128, 32])
-def test_attention_mask_exact_one_hot_values(W, hd):
+def test_attention_mask_exact_one_hot_values(W, hd, bounded):
     """With v_j = e_j the output row i is the probability row P_i itself, so
     its zero pattern must equal the window predicate exactly."""
     T = hd
@@ -343,12 +348,44 @@ def test_attention_mask_exact_one_hot_values(W, hd):
     tqkv = dev(qkv, torch.bfloat16).reshape(B * T, -1)
     to = torch.empty(B * T, H * hd, dtype=torch.bfloat16, device=DEV)
     tl = torch.empty(B * H * T, dtype=torch.float32, device=DEV)
-    G.k_attn_fwd(tqkv, to, tl, B, T, H, Hkv, hd, W, dt)
+    G.k_attn_fwd(tqkv, to, tl, B, T, H, Hkv, hd, W, dt,
+                 score_bound=1.01 * np.sqrt(hd) if bounded else 0.0)
     torch.cuda.synchronize()
     o = to_np(to).reshape(T, H, hd)
     mask = O.visible_mask(T, W)
     for h in range(H):
         np.testing.assert_array_equal(o[:, h, :] != 0.0, mask)
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_attention_bounded_extreme_scores(sign):
+    """Every key equal to +-q (one shared unit-RMS vector): every score is
+    +-sqrt(hd), the two ends of the bound.  Attention is then uniform over
+    the visible keys, so o_i is the mean of the visible v_j and
+    lse_i = ln(count) +- sqrt(hd), whatever the fixed offset."""
+    B, T, H, Hkv, hd, W = 1, 200, 2, 1, 128, 70
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(hd).astype(np.float32)
+    x = O.round_bf16(x / np.sqrt(np.mean(x.astype(np.float64) ** 2)))
+    q = np.broadcast_to(x, (B, T, H, hd)).astype(np.float32)
+    k = np.broadcast_to(sign * x, (B, T, Hkv, hd)).astype(np.float32)
+    v = O.round_bf16(rng.standard_normal((B, T, Hkv, hd)).astype(np.float32))
+    qkv = np.concatenate([q.reshape(B, T, -1), k.reshape(B, T, -1), v.reshape(B, T, -1)], -1)
+    tqkv = dev(qkv, torch.bfloat16).reshape(B * T, -1)
+    to = torch.empty(B * T, H * hd, dtype=torch.bfloat16, device=DEV)
+    tl = torch.empty(B * H * T, dtype=torch.float32, device=DEV)
+    G.k_attn_fwd(tqkv, to, tl, B, T, H, Hkv, hd, W, G.BF16, score_bound=1.01 * np.sqrt(hd))
+    torch.cuda.synchronize()
+    s = float(np.dot(x.astype(np.float64), sign * x.astype(np.float64))) / np.sqrt(hd)
+    lo = np.maximum(np.arange(T) - W, 0)
+    cnt = np.arange(T) - lo + 1
+    csum = np.concatenate([np.zeros((1, hd)), np.cumsum(v[0, :, 0].astype(np.float64), 0)])
+    mean = (csum[np.arange(T) + 1] - csum[lo]) / cnt[:, None]
+    o = to_np(to).reshape(T, H, hd)
+    for h in range(H):
+        assert rel_err(o[:, h], mean) < 1e-2
+    np.testing.assert_allclose(to_np(tl).reshape(H, T), np.broadcast_to(np.log(cnt) + s, (H, T)),
+                               rtol=0, atol=1e-4)
 
 
 # ----------------------------------------------------------- cross-entropy
