@@ -15,6 +15,8 @@
 // head-dim values.
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn_mfma.h"
 #include "attn_tiles.h"
 #include "common.h"
@@ -97,8 +99,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
     for (int hb = 0; hb < 8; ++hb) oacc[hb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    const int k0 = kt * TR, st = (kt - kt0) & 1;
+  // one key tile; the loop below is unrolled by two so every LDS address
+  // names its stage statically (fragment addresses become per-lane bases
+  // plus immediate offsets, no per-tile address arithmetic)
+  auto tile = [&](int kt, auto stc) {
+    const int k0 = kt * TR;
+    constexpr int st = decltype(stc)::value;
     dma_wait();
     __syncthreads();                                   // stage st filled, stage st^1 free
     if (kt < kt1) {
@@ -110,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
     // pairs of this wave: queries [qw, qw+31], keys [k0, k0+63]
     const bool any = (qw + QW - 1 >= k0) && (qw - (k0 + TR - 1) <= W) && qw < T;
     const bool full = (qw >= k0 + TR - 1) && (qw + QW - 1 - k0 <= W);
-    if (!any) continue;
+    if (!any) return;
     f32x4_t s[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -203,7 +209,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
         for (int qb = 0; qb < 2; ++qb) oacc[hb][qb] = mfma(vf, pf[qb], oacc[hb][qb]);
       }
     }
+    };
+  int kt = kt0;
+  for (; kt + 1 <= kt1; kt += 2) {
+    tile(kt, std::integral_constant<int, 0>());
+    tile(kt + 1, std::integral_constant<int, 1>());
   }
+  if (kt <= kt1) tile(kt, std::integral_constant<int, 0>());
 
   // normalise and store: lane holds O[query][16 hb + 4 g + r]
 #pragma unroll
@@ -408,8 +420,11 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
       dv[hb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-  for (int it = 0; it < iters; ++it) {
-    const int q0 = (qt0 + it % nqt) * TR, st = it & 1;
+  // one query tile; unrolled by two below so LDS addresses name their stage
+  // statically
+  auto step = [&](int it, auto stc) {
+    constexpr int st = decltype(stc)::value;
+    const int q0 = (qt0 + it % nqt) * TR;
     dma_wait();
     __syncthreads();
     if (it + 1 < iters) issue(it + 1, st ^ 1);
@@ -495,7 +510,13 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
         }
       }
     }
+    };
+  int it = 0;
+  for (; it + 2 <= iters; it += 2) {
+    step(it, std::integral_constant<int, 0>());
+    step(it + 1, std::integral_constant<int, 1>());
   }
+  if (it < iters) step(it, std::integral_constant<int, 0>());
   // lane holds dK^T / dV^T [16hb + 4g + r][key 16kb + lr]
   const float scale = 1.0f / sqrtf((float)HD);
 #pragma unroll
@@ -598,8 +619,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(const bf16* __restrict__
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) dq[hb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    const int k0 = kt * TR, st = (kt - kt0) & 1;
+  // one key tile; unrolled by two below so LDS addresses name their stage
+  // statically
+  auto tile = [&](int kt, auto stc) {
+    const int k0 = kt * TR;
+    constexpr int st = decltype(stc)::value;
     dma_wait();
     __syncthreads();
     if (kt < kt1) {
@@ -610,7 +634,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(const bf16* __restrict__
     const bf16* Vs = kv[st][1];
     const bool any = (qw + QW - 1 >= k0) && (qw - (k0 + TR - 1) <= W) && qw < T;
     const bool full = (qw >= k0 + TR - 1) && (qw + QW - 1 - k0 <= W);
-    if (!any) continue;
+    if (!any) return;
     f32x4_t s[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -668,7 +692,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(const bf16* __restrict__
         for (int qb = 0; qb < 2; ++qb) dq[hb][qb] = mfma(kt_, ps[qb], dq[hb][qb]);
       }
     }
+    };
+  int kt = kt0;
+  for (; kt + 1 <= kt1; kt += 2) {
+    tile(kt, std::integral_constant<int, 0>());
+    tile(kt + 1, std::integral_constant<int, 1>());
   }
+  if (kt <= kt1) tile(kt, std::integral_constant<int, 0>());
   const float scale = 1.0f / sqrtf((float)HD);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
