@@ -138,6 +138,8 @@ struct LayerBufs {
 struct Plan {
   int64_t N, chunk;
   size_t cs, x, hf, rf, ell, lse_z, loss, flag, logits, dz, evacc;
+  bool fused_ce;         // lm_head + cross-entropy fused (no fp32 logits)
+  size_t ce_stats, ce_zt;
   std::vector<LayerBufs> layers;     // train: one per layer; eval: one shared
   // backward scratch
   size_t dx, dh, du, dout, dqkv, attn_scr, vez, vwg, sort, gemm_scr, gemm_scr_bytes;
@@ -169,7 +171,10 @@ Plan make_plan(const Model& m, int mode) {
   p.loss = take(4);
   p.flag = take(4);
   p.evacc = take(3 * 8);
-  p.logits = take((size_t)p.chunk * m.V * 4);
+  p.fused_ce = m.dt == gk::BF16 && gk::lm_ce_fused_ok(N, m.V, m.D);
+  p.logits = p.fused_ce ? 0 : take((size_t)p.chunk * m.V * 4);
+  p.ce_stats = p.fused_ce ? take(gk::lm_ce_stats_bytes(N, m.V)) : 0;
+  p.ce_zt = p.fused_ce ? take(N * 4) : 0;
   p.dz = mode == GPT_MODE_TRAIN ? take((size_t)N * m.V * es) : 0;
   const int nl = mode == GPT_MODE_TRAIN ? m.L : 1;
   for (int l = 0; l < nl; ++l) {
@@ -278,6 +283,17 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
   HIP_TRY(gk::rmsnorm_fwd(x, hf, at<float>(ws, p.rf), N, m.D, m.eps, dt, s));
   float* logits = at<float>(ws, p.logits);
   const float inv_n = 1.0f / (float)N;
+  if (p.fused_ce) {
+    // e = exp(logit - tile max) lands where the softmax gradient goes and
+    // is rescaled there in place; EVAL keeps only the per-tile statistics
+    void* dz = mode == GPT_MODE_TRAIN ? at<void>(ws, p.dz) : nullptr;
+    float* stats = at<float>(ws, p.ce_stats);
+    float* zt = at<float>(ws, p.ce_zt);
+    HIP_TRY(gk::lm_ce_gemm(hf, N, m.D, elem(params, pl.wlm, es), m.V, dz, stats, zt, tokens, m.T,
+                           s));
+    HIP_TRY(gk::ce_fix(stats, zt, N, m.V, tokens, m.T, at<float>(ws, p.ell),
+                       at<float>(ws, p.lse_z), dz, inv_n, s));
+  } else {
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t nr = N - r0 < p.chunk ? N - r0 : p.chunk;
     gk::GemmDesc g{gk::OP_NT, nr, m.V, m.D, elem(hf, r0 * m.D, es), m.D,
@@ -287,6 +303,7 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
     void* dz = mode == GPT_MODE_TRAIN ? (void*)((char*)ws + p.dz + (size_t)r0 * m.V * es) : nullptr;
     HIP_TRY(gk::ce_rows(logits, nr, m.V, tokens, m.T, 0, at<float>(ws, p.ell) + r0,
                         at<float>(ws, p.lse_z) + r0, dz, inv_n, dt, s, r0));
+  }
   }
   if (mode == GPT_MODE_TRAIN)
     HIP_TRY(gk::loss_reduce(at<float>(ws, p.ell), N, at<float>(ws, p.loss), loss_dev,

@@ -913,6 +913,84 @@ generic:
   return hipGetLastError();
 }
 
+// Fused lm_head + cross-entropy, second half: one 512-thread block per row.
+// lse from the row's per-tile (m_t, s_t) in a fixed order, the loss, then
+// the softmax gradient from the stored fp16 e = exp(logit - m_t), rescaled
+// by exp(m_t - lse) and written back as bf16 over the same bytes.
+__global__ __launch_bounds__(512) void k_ce_fix(const float2* __restrict__ stats, int ntn,
+                                                const float* __restrict__ zt, int V,
+                                                const int32_t* __restrict__ tok, int T,
+                                                float* __restrict__ ell, float* __restrict__ lse,
+                                                uint16_t* dz, float scale) {
+  __shared__ float ct[1024];
+  __shared__ float red[8];
+  const int64_t row = blockIdx.x;
+  const float2* st = stats + row * ntn;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float m = -INFINITY;
+  for (int t = threadIdx.x; t < ntn; t += 512) m = fmaxf(m, st[t].x);
+  m = wave_max(m);
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) M = fmaxf(M, red[k]);
+  __syncthreads();
+  float sacc = 0.f;
+  for (int t = threadIdx.x; t < ntn; t += 512) {
+    const float2 v = st[t];
+    sacc += v.y * expf(v.x - M);
+  }
+  sacc = wave_sum(sacc);
+  if (lane == 0) red[w] = sacc;
+  __syncthreads();
+  float S = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) S += red[k];
+  const float L = M + logf(S);
+  if (threadIdx.x == 0) {
+    ell[row] = L - zt[row];
+    lse[row] = L;
+  }
+  if (!dz) return;
+  for (int t = threadIdx.x; t < ntn; t += 512) ct[t] = expf(st[t].x - L) * scale;
+  __syncthreads();
+  const int tgt = tok[(row / T) * (T + 1) + row % T + 1];
+  uint4* p = (uint4*)(dz + row * (int64_t)V);
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  for (int k = threadIdx.x; k < V / 8; k += 512) {
+    const uint4 u = p[k];
+    const float c = ct[(8 * k) >> 8];
+    const uint32_t* wu = (const uint32_t*)&u;
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const h2_t h = __builtin_bit_cast(h2_t, wu[e]);
+      f[2 * e] = (float)h[0] * c;
+      f[2 * e + 1] = (float)h[1] * c;
+    }
+    if ((tgt >> 3) == k) f[tgt & 7] -= scale;
+    uint4 o;
+    o.x = pack2bf(f[0], f[1]);
+    o.y = pack2bf(f[2], f[3]);
+    o.z = pack2bf(f[4], f[5]);
+    o.w = pack2bf(f[6], f[7]);
+    p[k] = o;
+  }
+}
+
+hipError_t ce_fix(const float* stats, const float* zt, int64_t rows, int V, const int32_t* tok,
+                  int tgt_T, float* ell, float* lse, void* dz, float grad_scale, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (V % 256 || V / 256 > 1024) return hipErrorInvalidValue;
+  const int ntn = V / 256;
+  // stats and target logits read once; e read and the gradient written once
+  const Work w(0.0, (double)rows * (8.0 * ntn + 12.0) + (dz ? 4.0 * (double)rows * V : 0.0));
+  GK_LAUNCH(w, k_ce_fix, dim3((unsigned)rows), dim3(512), 0, s, (const float2*)stats, ntn, zt, V,
+            tok, tgt_T, ell, lse, (uint16_t*)dz, grad_scale);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------- reductions
 __global__ __launch_bounds__(256) void k_loss_reduce(const float* ell, int64_t N, float* loss_ws,
                                                      float* loss_out, int* flag) {

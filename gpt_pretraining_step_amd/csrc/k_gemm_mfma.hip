@@ -281,7 +281,19 @@ __device__ __forceinline__ void mma_slice(const bf16* As, const bf16* Bs, int wm
 struct TileMap {
   int tiles_m, tiles_n, splits;
   int64_t k_per_split;     // multiple of BK
+  // E_CE only: per-(row, column tile) stats, target logits, token rows
+  float* ce_stats = nullptr;
+  float* ce_zt = nullptr;
+  const int32_t* ce_tok = nullptr;
+  int ce_T = 1;
 };
+
+// two floats as packed fp16 (round to nearest even)
+__device__ __forceinline__ uint32_t pack2h(float a, float b) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, h2_t));
+}
 
 template <int BM, int BN, bool TA, bool TB, int EPI>
 __global__ __launch_bounds__(256, 2) void k_gemm_mfma(int64_t M, int64_t N, int64_t K,
@@ -648,6 +660,91 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
   }
 
   const int cq = (lane >> 4) * 4, lr = lane & 15;
+  if constexpr (EPI == E_CE) {
+    // Fused lm_head + cross-entropy, first half (the tile is 256 x 256 and
+    // every column is a valid vocabulary entry): per row of the tile, the
+    // max m of its 256 logits and s = sum exp(logit - m) in fp32, e = exp(
+    // logit - m) as fp16 (when C is given), and the target's logit.  The
+    // two waves sharing a row combine through LDS (the stages are free).
+    const int ntn = tm.tiles_n;
+    int tg[TMI];
+#pragma unroll
+    for (int i = 0; i < TMI; ++i) {
+      const int64_t m = m0 + wm + 16 * i + lr;
+      tg[i] = m < M ? tm.ce_tok[(m / tm.ce_T) * (tm.ce_T + 1) + m % tm.ce_T + 1] : -1;
+    }
+    __syncthreads();
+    float* red = (float*)st0;              // [0, 512): maxima, [512, 1024): sums
+    float mx[TMI];
+#pragma unroll
+    for (int i = 0; i < TMI; ++i) {
+      // the one lane holding the row's target column stores its logit
+      const int lc = tg[i] - (int)n0 - wn;           // column within this wave's 128
+      if (lc >= 0 && lc < WN && ((lc >> 2) & 3) == (lane >> 4)) {
+        const int jj = lc >> 4, rr = lc & 3;
+        float v = 0.f;
+#pragma unroll
+        for (int j = 0; j < TNJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v = (j == jj && r == rr) ? acc[i][j][r] : v;
+        tm.ce_zt[m0 + wm + 16 * i + lr] = v;
+      }
+      float v = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v = fmaxf(v, acc[i][j][r]);
+      v = fmaxf(v, __shfl_xor(v, 16, 64));
+      v = fmaxf(v, __shfl_xor(v, 32, 64));
+      if (lane < 16) red[(wave & 1) * 256 + wm + 16 * i + lr] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TMI; ++i) {
+      const int rr = wm + 16 * i + lr;
+      mx[i] = fmaxf(red[rr], red[256 + rr]);
+      const float mxl = mx[i] * 1.4426950408889634f;
+      float sacc = 0.f;
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], 1.4426950408889634f, -mxl));
+          acc[i][j][r] = e;
+          sacc += e;
+        }
+      sacc += __shfl_xor(sacc, 16, 64);
+      sacc += __shfl_xor(sacc, 32, 64);
+      if (lane < 16) red[512 + (wave & 1) * 256 + rr] = sacc;
+    }
+    __syncthreads();
+    if ((wave & 1) == 0 && lane < 16) {
+#pragma unroll
+      for (int i = 0; i < TMI; ++i) {
+        const int rr = wm + 16 * i + lr;
+        const int64_t m = m0 + rr;
+        if (m < M)
+          *(float2*)(tm.ce_stats + 2 * (m * ntn + tile_n)) =
+              make_float2(mx[i], red[512 + rr] + red[768 + rr]);
+      }
+    }
+    if (C) {
+#pragma unroll
+      for (int i = 0; i < TMI; ++i) {
+        const int64_t m = m0 + wm + 16 * i + lr;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < TNJ; ++j) {
+          const int64_t n = n0 + wn + 16 * j + cq;
+          uint2 u;
+          u.x = pack2h(acc[i][j][0], acc[i][j][1]);
+          u.y = pack2h(acc[i][j][2], acc[i][j][3]);
+          *(uint2*)((uint16_t*)C + m * ldc + n) = u;
+        }
+      }
+    }
+    return;
+  }
   if (partial) {
     float* P = partial + (int64_t)split * M * N;
 #pragma unroll
@@ -900,6 +997,39 @@ static TileMap plan_dma(int64_t M, int64_t N, int64_t K, bool f32out, size_t scr
     tm.splits = (int)cdiv(K, tm.k_per_split);
   }
   return tm;
+}
+
+// any row count (partial row tiles read zeros past the last row)
+bool lm_ce_fused_ok(int64_t rows, int V, int D) {
+  return rows >= 1 && V % 256 == 0 && V / 256 <= 1024 && D % BK == 0 &&
+         2.0 * rows * D < 4294967295.0 && 2.0 * V * D < 4294967295.0;
+}
+
+size_t lm_ce_stats_bytes(int64_t rows, int V) { return (size_t)rows * (V / 256) * 8; }
+
+hipError_t lm_ce_gemm(const void* hf, int64_t rows, int D, const void* wlm, int V, void* e16,
+                      float* stats, float* zt, const int32_t* tok, int tgt_T, hipStream_t s) {
+  if (!lm_ce_fused_ok(rows, V, D)) return hipErrorInvalidValue;
+  TileMap tm;
+  tm.tiles_m = (int)cdiv(rows, 256);
+  tm.tiles_n = V / 256;
+  tm.splits = 1;
+  tm.k_per_split = D;
+  tm.ce_stats = stats;
+  tm.ce_zt = zt;
+  tm.ce_tok = tok;
+  tm.ce_T = tgt_T;
+  const int nb = tm.tiles_m * tm.tiles_n;
+  const int grid = ((nb + 7) / 8) * 8;
+  // 2 rows V D flops; hf and Wlm read once, e written (2 bytes), stats and
+  // target logits written
+  const double mn = (double)rows * V;
+  const Work w(2.0 * mn * D, 2.0 * ((double)rows * D + (double)V * D) + (e16 ? 2.0 * mn : 0.0) +
+                                 8.0 * rows * (V / 256) + 4.0 * rows);
+  GK_LAUNCH(w, (k_gemm_dma<256, 256, false, false, E_CE>), dim3(grid), dim3(512), 0, s, rows,
+            (int64_t)V, (int64_t)D, (const bf16*)hf, (int64_t)D, (const bf16*)wlm, (int64_t)D,
+            e16, (int64_t)V, nullptr, tm, nullptr);
+  return hipGetLastError();
 }
 
 size_t mfma_splitk_bytes(int64_t M, int64_t N, int64_t K) {

@@ -8,7 +8,8 @@ namespace gk {
 
 enum DType { F32 = 0, BF16 = 1 };
 enum GemmOp { OP_NT = 0, OP_NN = 1, OP_TN = 2 };
-enum Epi { E_STORE = 0, E_RESADD, E_RELU2, E_DRELU2, E_F32, E_F32_ACC };
+enum Epi { E_STORE = 0, E_RESADD, E_RELU2, E_DRELU2, E_F32, E_F32_ACC,
+           E_CE };   // E_CE: lm_ce_gemm only
 
 // ---- elementwise / reductions -------------------------------------------
 hipError_t fill_zero(void* p, int64_t bytes, hipStream_t s);
@@ -111,6 +112,20 @@ hipError_t ce_rows(const float* z, int64_t rows, int V, const int32_t* tok,
                    void* dz, float grad_scale, DType dt, hipStream_t s,
                    int64_t row0);
 // loss = mean(ell[0:N]) (fp64 sum); flag = !isfinite(loss)
+// Fused lm_head + cross-entropy for bf16 (V a multiple of 256, products the
+// direct-to-LDS GEMM takes).  lm_ce_gemm: logits = hf[rows, D] Wlm[V, D]^T,
+// never stored as such; per row and 256-column tile t the max m_t of the
+// logits and s_t = sum exp(logit - m_t) go to stats[row * (V / 256) + t],
+// the target's logit to zt[row], and (if e16) e = exp(logit - m_t) as fp16
+// to e16[row * V + col].  ce_fix: lse = max_t m_t + log(sum_t s_t
+// exp(m_t - max)), ell = lse - zt, and (if dz) dz = (e exp(m_t - lse) -
+// onehot) * grad_scale as bf16, in place over e16.  Targets as in ce_rows.
+bool lm_ce_fused_ok(int64_t rows, int V, int D);
+size_t lm_ce_stats_bytes(int64_t rows, int V);
+hipError_t lm_ce_gemm(const void* hf, int64_t rows, int D, const void* wlm, int V, void* e16,
+                      float* stats, float* zt, const int32_t* tok, int tgt_T, hipStream_t s);
+hipError_t ce_fix(const float* stats, const float* zt, int64_t rows, int V, const int32_t* tok,
+                  int tgt_T, float* ell, float* lse, void* dz, float grad_scale, hipStream_t s);
 hipError_t loss_reduce(const float* ell, int64_t N, float* loss_ws,
                        float* loss_out, int* flag, hipStream_t s);
 // acc[0] += sum ell, acc[1] += sum bytes[tgt]; if final, acc[2] = bpb
