@@ -125,7 +125,7 @@ def kernel_table(cfg, torch, G, iters=10):
         sb = G.k_gemm_scratch_bytes(M, Nn, K) if f32 else 0
         scr = torch.empty(max(sb, 16), device=dev, dtype=torch.uint8) if sb else None
         fn = lambda: G.k_gemm(op, M, Nn, K, A, lda, Bm, ldb, Cb, Nn, epi,
-                              aux if epi in (G.EPI_RELU2, G.EPI_DRELU2) else None, G.BF16,
+                              aux if epi == G.EPI_DRELU2 else None, G.BF16,
                               scratch=scr)
         t = time_events(fn, iters, torch)
         rows.append(dict(kernel="gemm " + name, avg_s=t, count=count, flops=2.0 * M * Nn * K,

@@ -132,7 +132,7 @@ ParamLayout param_layout(const Model& m) {
 
 // ------------------------------------------------------- workspace plan
 struct LayerBufs {
-  size_t h, r, qkv, rq, rk, g, o, lse, h2, r2, u, a;
+  size_t h, r, qkv, rq, rk, g, o, lse, h2, r2, a;
 };
 
 struct Plan {
@@ -189,7 +189,6 @@ Plan make_plan(const Model& m, int mode) {
     b.lse = take(N * (size_t)m.H * 4);
     b.h2 = take(N * m.D * es);
     b.r2 = take(N * 4);
-    b.u = take(N * (size_t)m.F * es);
     b.a = take(N * (size_t)m.F * es);
     p.layers.push_back(b);
   }
@@ -251,7 +250,6 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
     void* qkv = at<void>(ws, b.qkv);
     void* o = at<void>(ws, b.o);
     void* h2 = at<void>(ws, b.h2);
-    void* u = at<void>(ws, b.u);
     void* a = at<void>(ws, b.a);
     HIP_TRY(gk::rmsnorm_fwd(x, h, at<float>(ws, b.r), N, m.D, m.eps, dt, s));
     gk::GemmDesc g{gk::OP_NT, N, m.QKV, m.D, h, m.D, elem(params, pl.wqkv[l], es), m.D,
@@ -272,8 +270,10 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
                      nullptr};
     HIP_TRY(gk::gemm(g, dt, s));
     HIP_TRY(gk::rmsnorm_fwd(x, h2, at<float>(ws, b.r2), N, m.D, m.eps, dt, s));
-    g = gk::GemmDesc{gk::OP_NT, N, m.F, m.D, h2, m.D, elem(params, pl.wfc[l], es), m.D, u, m.F,
-                     gk::E_RELU2, a};
+    // only a = relu(u)^2 is kept (u rounded first); the backward takes
+    // relu(u) as sqrt(a)
+    g = gk::GemmDesc{gk::OP_NT, N, m.F, m.D, h2, m.D, elem(params, pl.wfc[l], es), m.D, a, m.F,
+                     gk::E_RELU2, nullptr};
     HIP_TRY(gk::gemm(g, dt, s));
     g = gk::GemmDesc{gk::OP_NT, N, m.D, m.F, a, m.F, elem(params, pl.wproj[l], es), m.F, x, m.D,
                      gk::E_RESADD, nullptr};
@@ -359,7 +359,6 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
     const void* qkv = at<void>(ws, b.qkv);
     const void* o = at<void>(ws, b.o);
     const void* h2 = at<void>(ws, b.h2);
-    void* u = at<void>(ws, b.u);
     const void* a = at<void>(ws, b.a);
     const int64_t HD = (int64_t)m.H * m.hd;
     // MLP
@@ -367,7 +366,7 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
                      nullptr, gscr, gscr_bytes};
     HIP_TRY(gk::gemm(g, dt, s));
     g = gk::GemmDesc{gk::OP_NN, N, m.F, m.D, dx, m.D, elem(params, pl.wproj[l], es), m.F, du,
-                     m.F, gk::E_DRELU2, u};
+                     m.F, gk::E_DRELU2, const_cast<void*>(a)};
     HIP_TRY(gk::gemm(g, dt, s));
     g = gk::GemmDesc{gk::OP_TN, m.F, m.D, N, du, m.F, h2, m.D, grads + pl.wfc[l], m.D, wepi,
                      nullptr, gscr, gscr_bytes};
@@ -615,8 +614,9 @@ int gpt_k_gemm(int32_t op, int64_t M, int64_t N, int64_t K, const void* A, int64
   if (op < GPT_GEMM_NT || op > GPT_GEMM_TN) return fail(GPT_ERR_INVALID_ARG, "unknown op");
   if (epilogue < GPT_EPI_STORE || epilogue > GPT_EPI_F32_ACC)
     return fail(GPT_ERR_INVALID_ARG, "unknown epilogue");
-  if ((epilogue == GPT_EPI_RELU2 || epilogue == GPT_EPI_DRELU2) && (!aux || !aligned16(aux)))
+  if (epilogue == GPT_EPI_DRELU2 && (!aux || !aligned16(aux)))
     return fail(GPT_ERR_INVALID_ARG, "epilogue needs an aligned aux buffer");
+  if (epilogue != GPT_EPI_DRELU2) aux = nullptr;
   if (M < 0 || N < 0 || K < 1) return fail(GPT_ERR_INVALID_ARG, "bad sizes");
   const int64_t rowA = op == GPT_GEMM_TN ? M : K, rowB = op == GPT_GEMM_NT ? K : N;
   if (lda < rowA || ldb < rowB || ldc < N) return fail(GPT_ERR_INVALID_ARG, "leading dims too small");

@@ -191,24 +191,22 @@ __device__ __forceinline__ void epi4_in(void* Cv, void* auxv, int64_t i, f32x4_t
     if constexpr (EPI == E_RESADD) {
       v[0] += __uint_as_float(in.x << 16); v[1] += __uint_as_float(in.x & 0xFFFF0000u);
       v[2] += __uint_as_float(in.y << 16); v[3] += __uint_as_float(in.y & 0xFFFF0000u);
-    } else if constexpr (EPI == E_DRELU2) {
-      v[0] *= 2.0f * fmaxf(__uint_as_float(in.x << 16), 0.f);
-      v[1] *= 2.0f * fmaxf(__uint_as_float(in.x & 0xFFFF0000u), 0.f);
-      v[2] *= 2.0f * fmaxf(__uint_as_float(in.y << 16), 0.f);
-      v[3] *= 2.0f * fmaxf(__uint_as_float(in.y & 0xFFFF0000u), 0.f);
+    } else if constexpr (EPI == E_DRELU2) {    // in: a = relu(u)^2, relu(u) = sqrt(a)
+      v[0] *= 2.0f * __builtin_sqrtf(__uint_as_float(in.x << 16));
+      v[1] *= 2.0f * __builtin_sqrtf(__uint_as_float(in.x & 0xFFFF0000u));
+      v[2] *= 2.0f * __builtin_sqrtf(__uint_as_float(in.y << 16));
+      v[3] *= 2.0f * __builtin_sqrtf(__uint_as_float(in.y & 0xFFFF0000u));
     }
     uint2 o;
     o.x = pack2bf(v[0], v[1]);
     o.y = pack2bf(v[2], v[3]);
-    *(uint2*)(C + i) = o;
-    if constexpr (EPI == E_RELU2) {      // a = relu(u)^2 of the stored (rounded) u
+    if constexpr (EPI == E_RELU2) {      // a = relu(u)^2 of u rounded to bf16
       float r0 = fmaxf(__uint_as_float(o.x << 16), 0.f), r1 = fmaxf(__uint_as_float(o.x & 0xFFFF0000u), 0.f);
       float r2 = fmaxf(__uint_as_float(o.y << 16), 0.f), r3 = fmaxf(__uint_as_float(o.y & 0xFFFF0000u), 0.f);
-      uint2 q;
-      q.x = pack2bf(r0 * r0, r1 * r1);
-      q.y = pack2bf(r2 * r2, r3 * r3);
-      *(uint2*)((bf16*)auxv + i) = q;
+      o.x = pack2bf(r0 * r0, r1 * r1);
+      o.y = pack2bf(r2 * r2, r3 * r3);
     }
+    *(uint2*)(C + i) = o;
   }
 }
 
@@ -806,13 +804,12 @@ bool mfma_gemm_supported(const GemmDesc& g) {
 }
 
 // Algorithmic work of one product: 2 M N K flops; A and B read once, C
-// written once (read too for RESADD / F32_ACC), aux written (RELU2) or read
-// (DRELU2) once.  Split-K partials are the reduce kernel's traffic.
+// written once (read too for RESADD / F32_ACC), aux read (DRELU2) once.  Split-K partials are the reduce kernel's traffic.
 static Work gemm_work(const GemmDesc& g) {
   const double mn = (double)g.M * g.N;
   const bool f32out = g.epi == E_F32 || g.epi == E_F32_ACC;
   double bytes = 2.0 * ((double)g.M * g.K + (double)g.N * g.K) + mn * (f32out ? 4 : 2);
-  if (g.epi == E_RESADD || g.epi == E_RELU2 || g.epi == E_DRELU2) bytes += 2.0 * mn;
+  if (g.epi == E_RESADD || g.epi == E_DRELU2) bytes += 2.0 * mn;
   if (g.epi == E_F32_ACC) bytes += 4.0 * mn;
   return Work(2.0 * mn * g.K, bytes);
 }

@@ -201,8 +201,11 @@ int gpt_k_rmsnorm_bwd(const void* dy, const void* y, const float* r,
  *   op GPT_GEMM_TN: A [K, M] (lda), B [K, N] (ldb):   C = A^T B   (dW = dy^T x)
  *   epilogue GPT_EPI_STORE   : C (dtype) = acc
  *            GPT_EPI_RESADD  : C (dtype) = C + acc, rounded once
- *            GPT_EPI_RELU2   : C (dtype) = acc; aux (dtype, ldc) = relu(C)^2
- *            GPT_EPI_DRELU2  : C (dtype) = acc * 2 relu(aux)  (aux: dtype, ldc)
+ *            GPT_EPI_RELU2   : C (dtype) = relu(u)^2, u = acc rounded to dtype
+ *                              (aux ignored for every epilogue but DRELU2)
+ *            GPT_EPI_DRELU2  : C (dtype) = acc * 2 sqrt(aux), aux (dtype, ldc)
+ *                              holding a = relu(u)^2 as RELU2 wrote it, so
+ *                              sqrt(aux) stands for relu(u)
  *            GPT_EPI_F32     : C (fp32) = acc
  *            GPT_EPI_F32_ACC : C (fp32) += acc
  */

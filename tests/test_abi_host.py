@@ -112,7 +112,7 @@ def test_entry_points_reject_bad_pointers_before_launch():
     L = G.lib()
     assert L.gpt_k_gemm(5, 4, 4, 4, A, 4, A, 4, A, 4, 0, None, None, 0, 1, None) == -1
     assert L.gpt_k_gemm(0, 4, 4, 4, A, 2, A, 4, A, 4, 0, None, None, 0, 1, None) == -1
-    assert L.gpt_k_gemm(0, 4, 4, 4, A, 4, A, 4, A, 4, 2, None, None, 0, 1, None) == -1
+    assert L.gpt_k_gemm(0, 4, 4, 4, A, 4, A, 4, A, 4, 3, None, None, 0, 1, None) == -1
     assert L.gpt_k_gemm(0, 4, 4, 4, A, 4, A, 4, A, 4, 0, None, C.c_void_p(0x1008), 64, 1, None) == -4
     assert L.gpt_k_attn_fwd(A, A, A, 1, 8, 3, 2, 128, 4, 1, 0.0, None) == -1
     assert L.gpt_k_attn_fwd(A, A, A, 1, 8, 2, 2, 96, 4, 1, 0.0, None) == -2
