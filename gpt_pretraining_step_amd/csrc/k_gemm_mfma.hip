@@ -756,23 +756,32 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
     }
     return;
   }
-  // per 16-row group: every load of the group first, then the stores (one
-  // memory latency per group instead of one per fragment)
+  // per pair of 16-row groups (one group for fp32 inputs): every load of
+  // the groups first, then the stores (one memory latency per batch instead
+  // of one per fragment; the MFMA operand registers are free by now)
+  constexpr int GB = (EPI == E_F32_ACC || TMI % 2) ? 1 : 2;
 #pragma unroll
-  for (int i = 0; i < TMI; ++i) {
-    const int64_t m = m0 + wm + 16 * i + lr;
-    typename EpiIn<EPI>::type in[TNJ];
+  for (int i0 = 0; i0 < TMI; i0 += GB) {
+    typename EpiIn<EPI>::type in[GB][TNJ];
     if constexpr (epi_reads<EPI>()) {
 #pragma unroll
-      for (int j = 0; j < TNJ; ++j) {
-        const int64_t n = n0 + wn + 16 * j + cq;
-        if (m < M && n < N) in[j] = epi_load<EPI>(C, aux, m * ldc + n);
+      for (int gi = 0; gi < GB; ++gi) {
+        const int64_t m = m0 + wm + 16 * (i0 + gi) + lr;
+#pragma unroll
+        for (int j = 0; j < TNJ; ++j) {
+          const int64_t n = n0 + wn + 16 * j + cq;
+          if (m < M && n < N) in[gi][j] = epi_load<EPI>(C, aux, m * ldc + n);
+        }
       }
     }
 #pragma unroll
-    for (int j = 0; j < TNJ; ++j) {
-      const int64_t n = n0 + wn + 16 * j + cq;
-      if (m < M && n < N) epi4_in<EPI>(C, aux, m * ldc + n, acc[i][j], in[j]);
+    for (int gi = 0; gi < GB; ++gi) {
+      const int64_t m = m0 + wm + 16 * (i0 + gi) + lr;
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j) {
+        const int64_t n = n0 + wn + 16 * j + cq;
+        if (m < M && n < N) epi4_in<EPI>(C, aux, m * ldc + n, acc[i0 + gi][j], in[gi][j]);
+      }
     }
   }
 }
