@@ -84,6 +84,8 @@ _SIGS = {
     "gpt_k_attn_bwd": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _vp]),
     "gpt_k_ce": (C.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp]),
+    "gpt_k_lm_ce_scratch_bytes": (_sz, [_i64, _i32]),
+    "gpt_k_lm_ce": (C.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _f32, _vp, _vp]),
     "gpt_prof_start": (C.c_int, [_i32]),
     "gpt_prof_stop": (C.c_int, []),
     "gpt_prof_count": (_i32, []),
@@ -225,6 +227,15 @@ def k_attn_bwd_scratch_bytes(B, T, H, hd):
 def k_attn_bwd(qkv, o, lse, dout, dqkv, scratch, B, T, H, Hkv, hd, window, dtype, stream=None):
     _check(lib().gpt_k_attn_bwd(_ptr(qkv), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dqkv),
                                 _ptr(scratch), B, T, H, Hkv, hd, window, dtype, _stream(stream)))
+
+
+def k_lm_ce_scratch_bytes(rows, V):
+    return int(lib().gpt_k_lm_ce_scratch_bytes(rows, V))
+
+
+def k_lm_ce(h, w, tgt, rows, D, V, ell, lse, dz, grad_scale, scratch, stream=None):
+    _check(lib().gpt_k_lm_ce(_ptr(h), _ptr(w), _ptr(tgt), rows, D, V, _ptr(ell), _ptr(lse),
+                             _ptr(dz), grad_scale, _ptr(scratch), _stream(stream)))
 
 
 def k_ce(z, tgt, rows, V, ell, lse, dz, grad_scale, dtype, stream=None):

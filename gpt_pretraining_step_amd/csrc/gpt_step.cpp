@@ -290,8 +290,8 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
     float* stats = at<float>(ws, p.ce_stats);
     float* zt = at<float>(ws, p.ce_zt);
     HIP_TRY(gk::lm_ce_gemm(hf, N, m.D, elem(params, pl.wlm, es), m.V, dz, stats, zt, tokens, m.T,
-                           s));
-    HIP_TRY(gk::ce_fix(stats, zt, N, m.V, tokens, m.T, at<float>(ws, p.ell),
+                           0, s));
+    HIP_TRY(gk::ce_fix(stats, zt, N, m.V, tokens, m.T, 0, at<float>(ws, p.ell),
                        at<float>(ws, p.lse_z), dz, inv_n, s));
   } else {
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
@@ -704,6 +704,28 @@ int gpt_k_ce(const float* z, const int32_t* tgt, int64_t rows, int32_t V, float*
   if (dz && !aligned16(dz)) return fail(GPT_ERR_MISALIGNED, "dz misaligned");
   if (rows < 0 || V < 1) return fail(GPT_ERR_INVALID_ARG, "bad sizes");
   KERNEL_TRY(gk::ce_rows(z, rows, V, tgt, 1, 1, ell, lse, dz, grad_scale, (gk::DType)dtype, s, 0));
+  return GPT_OK;
+}
+
+size_t gpt_k_lm_ce_scratch_bytes(int64_t rows, int32_t V) {
+  if (rows < 1 || V < 256 || V % 256) return 0;
+  return pad256(gk::lm_ce_stats_bytes(rows, V)) + pad256((size_t)rows * 4);
+}
+
+int gpt_k_lm_ce(const void* h, const void* w, const int32_t* tgt, int64_t rows, int32_t D,
+                int32_t V, float* ell, float* lse, void* dz, float grad_scale, void* scratch,
+                hipStream_t s) {
+  int st;
+  if ((st = check_ptrs({h, w, tgt, ell, lse, scratch}))) return st;
+  if (dz && !aligned16(dz)) return fail(GPT_ERR_MISALIGNED, "dz not 16-byte aligned");
+  if (!gk::lm_ce_fused_ok(rows, V, D))
+    return fail(GPT_ERR_INVALID_ARG,
+                "fused lm_head/CE needs rows >= 1, V a multiple of 256 (<= 262144), D a "
+                "multiple of 64 and operands under 4 GiB");
+  float* stats = (float*)scratch;
+  float* zt = (float*)((char*)scratch + pad256(gk::lm_ce_stats_bytes(rows, V)));
+  KERNEL_TRY(gk::lm_ce_gemm(h, rows, D, w, V, dz, stats, zt, tgt, 1, 1, s));
+  KERNEL_TRY(gk::ce_fix(stats, zt, rows, V, tgt, 1, 1, ell, lse, dz, grad_scale, s));
   return GPT_OK;
 }
 

@@ -920,8 +920,9 @@ generic:
 __global__ __launch_bounds__(512) void k_ce_fix(const float2* __restrict__ stats, int ntn,
                                                 const float* __restrict__ zt, int V,
                                                 const int32_t* __restrict__ tok, int T,
-                                                float* __restrict__ ell, float* __restrict__ lse,
-                                                uint16_t* dz, float scale) {
+                                                int direct, float* __restrict__ ell,
+                                                float* __restrict__ lse, uint16_t* dz,
+                                                float scale) {
   __shared__ float ct[1024];
   __shared__ float red[8];
   const int64_t row = blockIdx.x;
@@ -955,7 +956,7 @@ __global__ __launch_bounds__(512) void k_ce_fix(const float2* __restrict__ stats
   if (!dz) return;
   for (int t = threadIdx.x; t < ntn; t += 512) ct[t] = expf(st[t].x - L) * scale;
   __syncthreads();
-  const int tgt = tok[(row / T) * (T + 1) + row % T + 1];
+  const int tgt = direct ? tok[row] : tok[(row / T) * (T + 1) + row % T + 1];
   uint4* p = (uint4*)(dz + row * (int64_t)V);
   typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
   for (int k = threadIdx.x; k < V / 8; k += 512) {
@@ -980,14 +981,15 @@ __global__ __launch_bounds__(512) void k_ce_fix(const float2* __restrict__ stats
 }
 
 hipError_t ce_fix(const float* stats, const float* zt, int64_t rows, int V, const int32_t* tok,
-                  int tgt_T, float* ell, float* lse, void* dz, float grad_scale, hipStream_t s) {
+                  int tgt_T, int tgt_direct, float* ell, float* lse, void* dz, float grad_scale,
+                  hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (V % 256 || V / 256 > 1024) return hipErrorInvalidValue;
   const int ntn = V / 256;
   // stats and target logits read once; e read and the gradient written once
   const Work w(0.0, (double)rows * (8.0 * ntn + 12.0) + (dz ? 4.0 * (double)rows * V : 0.0));
   GK_LAUNCH(w, k_ce_fix, dim3((unsigned)rows), dim3(512), 0, s, (const float2*)stats, ntn, zt, V,
-            tok, tgt_T, ell, lse, (uint16_t*)dz, grad_scale);
+            tok, tgt_T, tgt_direct, ell, lse, (uint16_t*)dz, grad_scale);
   return hipGetLastError();
 }
 

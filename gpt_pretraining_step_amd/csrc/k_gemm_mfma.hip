@@ -284,6 +284,7 @@ struct TileMap {
   float* ce_zt = nullptr;
   const int32_t* ce_tok = nullptr;
   int ce_T = 1;
+  int ce_direct = 0;
 };
 
 // two floats as packed fp16 (round to nearest even)
@@ -669,7 +670,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
 #pragma unroll
     for (int i = 0; i < TMI; ++i) {
       const int64_t m = m0 + wm + 16 * i + lr;
-      tg[i] = m < M ? tm.ce_tok[(m / tm.ce_T) * (tm.ce_T + 1) + m % tm.ce_T + 1] : -1;
+      tg[i] = m >= M ? -1
+              : tm.ce_direct ? tm.ce_tok[m]
+                             : tm.ce_tok[(m / tm.ce_T) * (tm.ce_T + 1) + m % tm.ce_T + 1];
     }
     __syncthreads();
     float* red = (float*)st0;              // [0, 512): maxima, [512, 1024): sums
@@ -1014,7 +1017,8 @@ bool lm_ce_fused_ok(int64_t rows, int V, int D) {
 size_t lm_ce_stats_bytes(int64_t rows, int V) { return (size_t)rows * (V / 256) * 8; }
 
 hipError_t lm_ce_gemm(const void* hf, int64_t rows, int D, const void* wlm, int V, void* e16,
-                      float* stats, float* zt, const int32_t* tok, int tgt_T, hipStream_t s) {
+                      float* stats, float* zt, const int32_t* tok, int tgt_T, int tgt_direct,
+                      hipStream_t s) {
   if (!lm_ce_fused_ok(rows, V, D)) return hipErrorInvalidValue;
   TileMap tm;
   tm.tiles_m = (int)cdiv(rows, 256);
@@ -1025,6 +1029,7 @@ hipError_t lm_ce_gemm(const void* hf, int64_t rows, int D, const void* wlm, int 
   tm.ce_zt = zt;
   tm.ce_tok = tok;
   tm.ce_T = tgt_T;
+  tm.ce_direct = tgt_direct;
   const int nb = tm.tiles_m * tm.tiles_n;
   const int grid = ((nb + 7) / 8) * 8;
   // 2 rows V D flops; hf and Wlm read once, e written (2 bytes), stats and

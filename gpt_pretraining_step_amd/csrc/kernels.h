@@ -122,10 +122,13 @@ hipError_t ce_rows(const float* z, int64_t rows, int V, const int32_t* tok,
 // onehot) * grad_scale as bf16, in place over e16.  Targets as in ce_rows.
 bool lm_ce_fused_ok(int64_t rows, int V, int D);
 size_t lm_ce_stats_bytes(int64_t rows, int V);
+// (tgt_direct: the target of row n is tok[n] instead)
 hipError_t lm_ce_gemm(const void* hf, int64_t rows, int D, const void* wlm, int V, void* e16,
-                      float* stats, float* zt, const int32_t* tok, int tgt_T, hipStream_t s);
+                      float* stats, float* zt, const int32_t* tok, int tgt_T, int tgt_direct,
+                      hipStream_t s);
 hipError_t ce_fix(const float* stats, const float* zt, int64_t rows, int V, const int32_t* tok,
-                  int tgt_T, float* ell, float* lse, void* dz, float grad_scale, hipStream_t s);
+                  int tgt_T, int tgt_direct, float* ell, float* lse, void* dz, float grad_scale,
+                  hipStream_t s);
 hipError_t loss_reduce(const float* ell, int64_t N, float* loss_ws,
                        float* loss_out, int* flag, hipStream_t s);
 // acc[0] += sum ell, acc[1] += sum bytes[tgt]; if final, acc[2] = bpb

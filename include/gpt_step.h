@@ -262,6 +262,22 @@ int gpt_k_attn_bwd(const void* qkv, const void* o, const float* lse,
                    int32_t T, int32_t H, int32_t Hkv, int32_t hd,
                    int32_t window, int32_t dtype, hipStream_t s);
 
+/* Fused lm_head + softmax cross-entropy (bf16): logits = h [rows, D] times
+ * w [V, D]^T are formed in fp32 inside the product and never stored; per
+ * row and 256-column tile the product keeps the max and sum of exp(logit -
+ * max) and writes exp(logit - max) as fp16 into dz, which a second pass
+ * rescales in place (the same steps as the training step's loss).
+ *   tgt[rows]: target ids in [0, V).  ell[row] = lse - logit[tgt[row]],
+ *   lse[row] (fp32).  dz (may be null): [rows, V] bf16, receives
+ *   (softmax - onehot) * grad_scale.  scratch: device, at least
+ *   gpt_k_lm_ce_scratch_bytes(rows, V) bytes (per-tile statistics and target
+ *   logits).  Needs V a multiple of 256, D a multiple of 64, h and w
+ *   16-byte aligned (else GPT_ERR_INVALID_ARG / GPT_ERR_MISALIGNED). */
+size_t gpt_k_lm_ce_scratch_bytes(int64_t rows, int32_t V);
+int gpt_k_lm_ce(const void* h, const void* w, const int32_t* tgt, int64_t rows,
+                int32_t D, int32_t V, float* ell, float* lse, void* dz,
+                float grad_scale, void* scratch, hipStream_t s);
+
 /* Softmax cross-entropy on fp32 logits z [rows, V] with targets tgt[rows]:
  * ell[row] = lse - z[tgt], lse[row]; if dz is non-null it receives
  * (softmax - onehot) * grad_scale in `dtype` [rows, V]. */

@@ -389,6 +389,36 @@ def test_attention_bounded_extreme_scores(sign):
 
 
 # ----------------------------------------------------------- cross-entropy
+@pytest.mark.parametrize("rows,D,V,scale", [(300, 128, 1024, 1.0), (513, 64, 32768, 0.3),
+                                            (37, 256, 512, 4.0)])
+def test_fused_lm_head_cross_entropy(rows, D, V, scale):
+    """The step's fused lm_head + CE path against the oracle's CE on the
+    exact logits of the same bf16 inputs: ragged row tiles, targets on tile
+    edges, and (scale 4) logits spread over +-100, where exp(logit - tile
+    max) falls far below fp16's range for most columns."""
+    say("lm_ce", rows, D, V, scale)
+    rng = np.random.default_rng(50 + rows)
+    h = O.round_bf16(rng.standard_normal((rows, D)).astype(np.float32))
+    w = O.round_bf16((rng.standard_normal((V, D)) * scale / np.sqrt(D) * 8).astype(np.float32))
+    tgt = rng.integers(0, V, rows).astype(np.int32)
+    edges = [0, 255, 256, V - 1, V - 256, 511 % V]
+    tgt[:len(edges)] = edges
+    z = (h.astype(np.float64) @ w.astype(np.float64).T)
+    num = _Num("bf16emu")
+    ell_ref, lse_ref, dz_ref = O.cross_entropy(z, tgt, num)
+    ell = torch.empty(rows, dtype=torch.float32, device=DEV)
+    lse = torch.empty(rows, dtype=torch.float32, device=DEV)
+    dz = torch.empty(rows, V, dtype=torch.bfloat16, device=DEV)
+    scr = torch.empty(G.k_lm_ce_scratch_bytes(rows, V), dtype=torch.uint8, device=DEV)
+    G.k_lm_ce(dev(h, torch.bfloat16), dev(w, torch.bfloat16), dev(tgt, torch.int32), rows, D, V,
+              ell, lse, dz, 1.0 / rows, scr)
+    torch.cuda.synchronize()
+    # fp32 accumulation of the logits: lse and the loss to ~1e-6 relative
+    assert np.abs(to_np(lse) - lse_ref).max() < 1e-5 * max(1.0, np.abs(lse_ref).max())
+    assert np.abs(to_np(ell) - ell_ref).max() < 1e-5 * max(1.0, np.abs(lse_ref).max())
+    assert rel_err(to_np(dz), num.rnd(dz_ref)) < 1e-2
+
+
 @pytest.mark.parametrize("dt", [G.BF16, G.F32])
 @pytest.mark.parametrize("V", [27, 1000, 32768])
 def test_cross_entropy(dt, V):
