@@ -252,15 +252,25 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
     void* h2 = at<void>(ws, b.h2);
     void* a = at<void>(ws, b.a);
     HIP_TRY(gk::rmsnorm_fwd(x, h, at<float>(ws, b.r), N, m.D, m.eps, dt, s));
+    // RoPE then QK-norm touch only q and k, the value embedding only v: with
+    // head_dim 128 the rotation and norm run in the QKV product's epilogue
+    const bool qk_fused =
+        dt == gk::BF16 && gk::qkv_rope_fused_ok(N, m.D, m.H, m.Hkv, m.hd);
     gk::GemmDesc g{gk::OP_NT, N, m.QKV, m.D, h, m.D, elem(params, pl.wqkv[l], es), m.D,
                    qkv, m.QKV, gk::E_STORE, nullptr};
-    HIP_TRY(gk::gemm(g, dt, s));
+    if (qk_fused)
+      HIP_TRY(gk::qkv_gemm_rope_norm(h, N, m.D, elem(params, pl.wqkv[l], es), m.H, m.Hkv, qkv,
+                                     cs, at<float>(ws, b.rq), at<float>(ws, b.rk), m.T, m.eps,
+                                     s));
+    else
+      HIP_TRY(gk::gemm(g, dt, s));
     if (m.is_ve(l))
       HIP_TRY(gk::ve_fwd(tokens, rows, m.T, h, m.D, elem(params, pl.wg[l], es), m.C,
                          elem(params, pl.ve[l], es), qkv, m.QKV, (m.H + m.Hkv) * m.hd,
                          at<float>(ws, b.g), m.Hkv, m.hd, dt, s));
-    HIP_TRY(gk::rope_qknorm_fwd(qkv, at<float>(ws, b.rq), at<float>(ws, b.rk), cs, rows, m.T,
-                                m.H, m.Hkv, m.hd, m.eps, dt, s));
+    if (!qk_fused)
+      HIP_TRY(gk::rope_qknorm_fwd(qkv, at<float>(ws, b.rq), at<float>(ws, b.rk), cs, rows, m.T,
+                                  m.H, m.Hkv, m.hd, m.eps, dt, s));
     // q and k rows are RMS-normalised (norm <= sqrt(hd), times 1 + 2^-8 per
     // factor after bf16 rounding), so |q . k| / sqrt(hd) <= 1.01 sqrt(hd)
     HIP_TRY(gk::attn_fwd(qkv, o, at<float>(ws, b.lse), rows, m.T, m.H, m.Hkv, m.hd, m.window(l),

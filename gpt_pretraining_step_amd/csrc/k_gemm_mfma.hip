@@ -285,6 +285,12 @@ struct TileMap {
   const int32_t* ce_tok = nullptr;
   int ce_T = 1;
   int ce_direct = 0;
+  // E_QKNORM only
+  const float2* qk_cs = nullptr;
+  float* qk_rq = nullptr;
+  float* qk_rk = nullptr;
+  int qk_T = 1, qk_H = 0, qk_Hkv = 0;
+  float qk_eps = 0.f;
 };
 
 // two floats as packed fp16 (round to nearest even)
@@ -746,6 +752,68 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
     }
     return;
   }
+  if constexpr (EPI == E_QKNORM) {
+    // RoPE then RMS-norm per q / k head: the wave's 128 columns are one head
+    // (256-wide tiles, head_dim 128); lane (g, lr) holds dims 16 j + 4 g + r,
+    // so the rotation pairs (d, d + 64) are fragments j and j + 4 of one lane
+    // and a row's sum of squares needs two shuffles.  u rounded to bf16
+    // first, as the stored product would be.
+    static_assert(WN == 128, "one head per wave");
+    const int head = (int)((n0 + wn) >> 7);
+    const int H = tm.qk_H, Hkv = tm.qk_Hkv;
+#pragma unroll
+    for (int i = 0; i < TMI; ++i) {
+      const int64_t m = m0 + wm + 16 * i + lr;
+      float x[TNJ][4];
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[j][r] = bf2f(f2bf(acc[i][j][r]));
+      if (head < H + Hkv) {
+        const int t = (int)((m < M ? m : 0) % tm.qk_T);
+        const float2* cst = tm.qk_cs + (int64_t)t * 64;
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < TNJ / 2; ++j) {
+          const float4* c4 = (const float4*)(cst + 16 * j + cq);
+          const float4 ca = c4[0], cb = c4[1];
+          const float c[4] = {ca.x, ca.z, cb.x, cb.z}, sn[4] = {ca.y, ca.w, cb.y, cb.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float x1 = x[j][r], x2 = x[j + 4][r];
+            const float y1 = x1 * c[r] - x2 * sn[r], y2 = x1 * sn[r] + x2 * c[r];
+            x[j][r] = y1;
+            x[j + 4][r] = y2;
+            ss += y1 * y1 + y2 * y2;
+          }
+        }
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        const float rr = 1.0f / sqrtf(ss / 128.0f + tm.qk_eps);
+#pragma unroll
+        for (int j = 0; j < TNJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[j][r] *= rr;
+        if ((lane >> 4) == 0 && m < M) {
+          if (head < H) tm.qk_rq[m * H + head] = rr;
+          else tm.qk_rk[m * Hkv + (head - H)] = rr;
+        }
+      }
+      if (m < M) {
+#pragma unroll
+        for (int j = 0; j < TNJ; ++j) {
+          const int64_t n = n0 + wn + 16 * j + cq;
+          if (n < N) {
+            uint2 o;
+            o.x = pack2bf(x[j][0], x[j][1]);
+            o.y = pack2bf(x[j][2], x[j][3]);
+            *(uint2*)((bf16*)C + m * ldc + n) = o;
+          }
+        }
+      }
+    }
+    return;
+  }
   if (partial) {
     float* P = partial + (int64_t)split * M * N;
 #pragma unroll
@@ -1006,6 +1074,40 @@ static TileMap plan_dma(int64_t M, int64_t N, int64_t K, bool f32out, size_t scr
     tm.splits = (int)cdiv(K, tm.k_per_split);
   }
   return tm;
+}
+
+bool qkv_rope_fused_ok(int64_t rows, int D, int H, int Hkv, int hd) {
+  const int64_t n = (int64_t)(H + 2 * Hkv) * hd;
+  return hd == 128 && rows >= 1 && D % BK == 0 && dma_shape_ok(rows, n, D) &&
+         2.0 * rows * D < 4294967295.0 && 2.0 * n * D < 4294967295.0;
+}
+
+hipError_t qkv_gemm_rope_norm(const void* h, int64_t rows, int D, const void* wqkv, int H,
+                              int Hkv, void* qkv, const float* cs, float* rq, float* rk, int T,
+                              float eps, hipStream_t s) {
+  if (!qkv_rope_fused_ok(rows, D, H, Hkv, 128)) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)(H + 2 * Hkv) * 128;
+  TileMap tm;
+  tm.tiles_m = (int)cdiv(rows, 256);
+  tm.tiles_n = (int)cdiv(n, 256);
+  tm.splits = 1;
+  tm.k_per_split = D;
+  tm.qk_cs = (const float2*)cs;
+  tm.qk_rq = rq;
+  tm.qk_rk = rk;
+  tm.qk_T = T;
+  tm.qk_H = H;
+  tm.qk_Hkv = Hkv;
+  tm.qk_eps = eps;
+  const int nb = tm.tiles_m * tm.tiles_n;
+  const int grid = ((nb + 7) / 8) * 8;
+  // 2 rows n D flops; h and Wqkv read once, qkv written once, 1/rms written
+  const Work w(2.0 * rows * n * D, 2.0 * ((double)rows * D + (double)n * D + (double)rows * n) +
+                                       4.0 * rows * (H + Hkv));
+  GK_LAUNCH(w, (k_gemm_dma<256, 256, false, false, E_QKNORM>), dim3(grid), dim3(512), 0, s, rows,
+            n, (int64_t)D, (const bf16*)h, (int64_t)D, (const bf16*)wqkv, (int64_t)D, qkv, n,
+            nullptr, tm, nullptr);
+  return hipGetLastError();
 }
 
 // any row count (partial row tiles read zeros past the last row)

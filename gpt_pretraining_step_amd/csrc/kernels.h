@@ -9,7 +9,8 @@ namespace gk {
 enum DType { F32 = 0, BF16 = 1 };
 enum GemmOp { OP_NT = 0, OP_NN = 1, OP_TN = 2 };
 enum Epi { E_STORE = 0, E_RESADD, E_RELU2, E_DRELU2, E_F32, E_F32_ACC,
-           E_CE };   // E_CE: lm_ce_gemm only
+           E_CE,       // lm_ce_gemm only
+           E_QKNORM }; // qkv_gemm_rope_norm only
 
 // ---- elementwise / reductions -------------------------------------------
 hipError_t fill_zero(void* p, int64_t bytes, hipStream_t s);
@@ -112,6 +113,15 @@ hipError_t ce_rows(const float* z, int64_t rows, int V, const int32_t* tok,
                    void* dz, float grad_scale, DType dt, hipStream_t s,
                    int64_t row0);
 // loss = mean(ell[0:N]) (fp64 sum); flag = !isfinite(loss)
+// QKV projection with RoPE then QK-norm fused into the product's epilogue
+// (bf16, head_dim 128): qkv[rows, (H + 2 Hkv) 128] = h Wqkv^T, every q and k
+// head rotated (position = row % T, table cs [T][64] (cos, sin)) and RMS-
+// normalised, its 1/rms to rq [rows, H] / rk [rows, Hkv]; v heads stored as
+// they are.  Same rounding points as gemm + rope_qknorm_fwd.
+bool qkv_rope_fused_ok(int64_t rows, int D, int H, int Hkv, int hd);
+hipError_t qkv_gemm_rope_norm(const void* h, int64_t rows, int D, const void* wqkv, int H,
+                              int Hkv, void* qkv, const float* cs, float* rq, float* rk, int T,
+                              float eps, hipStream_t s);
 // Fused lm_head + cross-entropy for bf16 (V a multiple of 256, products the
 // direct-to-LDS GEMM takes).  lm_ce_gemm: logits = hf[rows, D] Wlm[V, D]^T,
 // never stored as such; per row and 256-column tile t the max m_t of the
