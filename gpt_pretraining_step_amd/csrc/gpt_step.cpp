@@ -255,16 +255,21 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
     // RoPE then QK-norm touch only q and k, the value embedding only v: with
     // head_dim 128 the rotation and norm run in the QKV product's epilogue
     const bool qk_fused =
-        dt == gk::BF16 && gk::qkv_rope_fused_ok(N, m.D, m.H, m.Hkv, m.hd);
+        dt == gk::BF16 && gk::qkv_rope_fused_ok(N, m.D, m.H, m.Hkv, m.hd) &&
+        (!m.is_ve(l) || ((uintptr_t)elem(params, pl.ve[l], es) & 7) == 0);
     gk::GemmDesc g{gk::OP_NT, N, m.QKV, m.D, h, m.D, elem(params, pl.wqkv[l], es), m.D,
                    qkv, m.QKV, gk::E_STORE, nullptr};
-    if (qk_fused)
+    if (qk_fused) {
+      // a value-embedding layer's v += g E[token] joins the same epilogue
+      gk::VeArgs ve{tokens, m.is_ve(l) ? elem(params, pl.wg[l], es) : nullptr, m.C,
+                    m.is_ve(l) ? elem(params, pl.ve[l], es) : nullptr, at<float>(ws, b.g)};
       HIP_TRY(gk::qkv_gemm_rope_norm(h, N, m.D, elem(params, pl.wqkv[l], es), m.H, m.Hkv, qkv,
                                      cs, at<float>(ws, b.rq), at<float>(ws, b.rk), m.T, m.eps,
-                                     s));
-    else
+                                     m.is_ve(l) ? &ve : nullptr, s));
+    } else {
       HIP_TRY(gk::gemm(g, dt, s));
-    if (m.is_ve(l))
+    }
+    if (m.is_ve(l) && !qk_fused)
       HIP_TRY(gk::ve_fwd(tokens, rows, m.T, h, m.D, elem(params, pl.wg[l], es), m.C,
                          elem(params, pl.ve[l], es), qkv, m.QKV, (m.H + m.Hkv) * m.hd,
                          at<float>(ws, b.g), m.Hkv, m.hd, dt, s));

@@ -291,6 +291,13 @@ struct TileMap {
   float* qk_rk = nullptr;
   int qk_T = 1, qk_H = 0, qk_Hkv = 0;
   float qk_eps = 0.f;
+  // E_QKNORM, value-embedding layers: v += g E[token], g = 3 sigmoid(h[:, :C] wg^T)
+  const int32_t* ve_tok = nullptr;
+  const bf16* ve_h = nullptr;
+  const bf16* ve_wg = nullptr;
+  const bf16* ve_E = nullptr;
+  float* ve_g = nullptr;
+  int ve_D = 0, ve_C = 0;
 };
 
 // two floats as packed fp16 (round to nearest even)
@@ -798,6 +805,45 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
           if (head < H) tm.qk_rq[m * H + head] = rr;
           else tm.qk_rk[m * Hkv + (head - H)] = rr;
         }
+      } else if (tm.ve_E && head < H + 2 * Hkv) {
+        // value embedding of KV head hv: the gate is a C-long dot product
+        // of the row's normalised input with wg[hv] (the row's four lanes
+        // take every fourth channel), then v = v + g E[token] in fp32, one
+        // rounding
+        const int hv = head - H - Hkv;
+        const int64_t mm = m < M ? m : 0;
+        float ga = 0.f;
+        if (tm.ve_C % 8 == 0) {
+          // 8 consecutive channels per lane and step (16-byte loads)
+          for (int c = 8 * (lane >> 4); c < tm.ve_C; c += 32) {
+            const uint4 hv8 = *(const uint4*)(tm.ve_h + mm * tm.ve_D + c);
+            const uint4 wv8 = *(const uint4*)(tm.ve_wg + (int64_t)hv * tm.ve_C + c);
+            const uint32_t* hw = (const uint32_t*)&hv8;
+            const uint32_t* ww = (const uint32_t*)&wv8;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              ga = fmaf(__uint_as_float(hw[e] << 16), __uint_as_float(ww[e] << 16), ga);
+              ga = fmaf(__uint_as_float(hw[e] & 0xFFFF0000u), __uint_as_float(ww[e] & 0xFFFF0000u), ga);
+            }
+          }
+        } else {
+          for (int c = lane >> 4; c < tm.ve_C; c += 4)
+            ga = fmaf(bf2f(tm.ve_h[mm * tm.ve_D + c]), bf2f(tm.ve_wg[(int64_t)hv * tm.ve_C + c]), ga);
+        }
+        ga += __shfl_xor(ga, 16, 64);
+        ga += __shfl_xor(ga, 32, 64);
+        const float gv = 3.0f / (1.0f + expf(-ga));
+        if ((lane >> 4) == 0 && m < M) tm.ve_g[m * Hkv + hv] = gv;
+        const int id = tm.ve_tok[(mm / tm.qk_T) * (tm.qk_T + 1) + mm % tm.qk_T];
+        const bf16* er = tm.ve_E + (int64_t)id * (Hkv * 128) + hv * 128 + cq;
+#pragma unroll
+        for (int j = 0; j < TNJ; ++j) {
+          const uint2 e = *(const uint2*)(er + 16 * j);
+          x[j][0] = fmaf(gv, __uint_as_float(e.x << 16), x[j][0]);
+          x[j][1] = fmaf(gv, __uint_as_float(e.x & 0xFFFF0000u), x[j][1]);
+          x[j][2] = fmaf(gv, __uint_as_float(e.y << 16), x[j][2]);
+          x[j][3] = fmaf(gv, __uint_as_float(e.y & 0xFFFF0000u), x[j][3]);
+        }
       }
       if (m < M) {
 #pragma unroll
@@ -1084,7 +1130,7 @@ bool qkv_rope_fused_ok(int64_t rows, int D, int H, int Hkv, int hd) {
 
 hipError_t qkv_gemm_rope_norm(const void* h, int64_t rows, int D, const void* wqkv, int H,
                               int Hkv, void* qkv, const float* cs, float* rq, float* rk, int T,
-                              float eps, hipStream_t s) {
+                              float eps, const VeArgs* ve, hipStream_t s) {
   if (!qkv_rope_fused_ok(rows, D, H, Hkv, 128)) return hipErrorInvalidValue;
   const int64_t n = (int64_t)(H + 2 * Hkv) * 128;
   TileMap tm;
@@ -1099,6 +1145,15 @@ hipError_t qkv_gemm_rope_norm(const void* h, int64_t rows, int D, const void* wq
   tm.qk_H = H;
   tm.qk_Hkv = Hkv;
   tm.qk_eps = eps;
+  if (ve) {
+    tm.ve_tok = ve->tok;
+    tm.ve_h = (const bf16*)h;
+    tm.ve_D = D;
+    tm.ve_wg = (const bf16*)ve->wg;
+    tm.ve_C = ve->C;
+    tm.ve_E = (const bf16*)ve->E;
+    tm.ve_g = ve->g;
+  }
   const int nb = tm.tiles_m * tm.tiles_n;
   const int grid = ((nb + 7) / 8) * 8;
   // 2 rows n D flops; h and Wqkv read once, qkv written once, 1/rms written

@@ -118,10 +118,20 @@ hipError_t ce_rows(const float* z, int64_t rows, int V, const int32_t* tok,
 // head rotated (position = row % T, table cs [T][64] (cos, sin)) and RMS-
 // normalised, its 1/rms to rq [rows, H] / rk [rows, Hkv]; v heads stored as
 // they are.  Same rounding points as gemm + rope_qknorm_fwd.
+// With ve, the value embedding of a VE layer is applied to the v heads in the
+// same epilogue: g = 3 sigmoid(h[:, :C] wg^T) per KV head (to ve->g [rows,
+// Hkv]), v = v + g E[token] (token of row n: tok[(n / T)(T + 1) + n % T]).
+struct VeArgs {
+  const int32_t* tok;
+  const void* wg;     // [Hkv, C]
+  int C;
+  const void* E;      // [V, Hkv hd]
+  float* g;
+};
 bool qkv_rope_fused_ok(int64_t rows, int D, int H, int Hkv, int hd);
 hipError_t qkv_gemm_rope_norm(const void* h, int64_t rows, int D, const void* wqkv, int H,
                               int Hkv, void* qkv, const float* cs, float* rq, float* rk, int T,
-                              float eps, hipStream_t s);
+                              float eps, const VeArgs* ve, hipStream_t s);
 // Fused lm_head + cross-entropy for bf16 (V a multiple of 256, products the
 // direct-to-LDS GEMM takes).  lm_ce_gemm: logits = hf[rows, D] Wlm[V, D]^T,
 // never stored as such; per row and 256-column tile t the max m_t of the
