@@ -994,16 +994,28 @@ hipError_t ce_fix(const float* stats, const float* zt, int64_t rows, int V, cons
 }
 
 // ------------------------------------------------------------- reductions
-__global__ __launch_bounds__(256) void k_loss_reduce(const float* ell, int64_t N, float* loss_ws,
-                                                     float* loss_out, int* flag) {
-  __shared__ double red[4];
+// loss = mean(ell): one 1024-thread block, 16-byte loads, fp64 sums in a
+// fixed order (per thread, then per wave, then the 16 wave sums in order)
+__global__ __launch_bounds__(1024) void k_loss_reduce(const float* ell, int64_t N, float* loss_ws,
+                                                      float* loss_out, int* flag) {
+  __shared__ double red[16];
   double acc = 0.0;
-  for (int64_t i = threadIdx.x; i < N; i += blockDim.x) acc += (double)ell[i];
+  if (((uintptr_t)ell & 15) == 0) {
+    const int64_t n4 = N / 4;
+    for (int64_t i = threadIdx.x; i < n4; i += blockDim.x) {
+      const float4 v = ((const float4*)ell)[i];
+      acc += ((double)v.x + (double)v.y) + ((double)v.z + (double)v.w);
+    }
+    for (int64_t i = 4 * n4 + threadIdx.x; i < N; i += blockDim.x) acc += (double)ell[i];
+  } else {
+    for (int64_t i = threadIdx.x; i < N; i += blockDim.x) acc += (double)ell[i];
+  }
   acc = wave_sum_d(acc);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
   __syncthreads();
   if (threadIdx.x == 0) {
-    double tot = (red[0] + red[1]) + (red[2] + red[3]);
+    double tot = 0.0;
+    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) tot += red[k];
     float loss = (float)(tot / (double)N);
     *loss_ws = loss;
     if (loss_out) *loss_out = loss;
@@ -1013,7 +1025,8 @@ __global__ __launch_bounds__(256) void k_loss_reduce(const float* ell, int64_t N
 
 hipError_t loss_reduce(const float* ell, int64_t N, float* loss_ws, float* loss_out, int* flag,
                        hipStream_t s) {
-  GK_LAUNCH(Work(), k_loss_reduce, dim3(1), dim3(256), 0, s, ell, N, loss_ws, loss_out, flag);
+  GK_LAUNCH(Work(0.0, 4.0 * N), k_loss_reduce, dim3(1), dim3(1024), 0, s, ell, N, loss_ws,
+            loss_out, flag);
   return hipGetLastError();
 }
 
