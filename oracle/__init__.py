@@ -26,5 +26,6 @@ from .gpt import (  # noqa: F401
     PRECISIONS, param_layout, param_count, unpack_params, window_for_layer,
     is_ve_layer, visible_mask, rope_tables, rope, rope_bwd, rmsnorm,
     rmsnorm_bwd, attention, attention_bwd, attention_tiled, cross_entropy,
+    embedding, embedding_bwd, value_embedding, value_embedding_bwd,
     forward, backward, step, eval_bpb, round_bf16,
 )

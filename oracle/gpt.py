@@ -347,6 +347,47 @@ def _sigmoid(x):
     return 1.0 / (1.0 + np.exp(-x))
 
 
+def embedding(wte, inp, num: _Num):
+    """x0 = wte[inp]: row lookup of the input ids ([microgpt] "model
+    architecture": token embedding; [nanochat] "1. GPT model")."""
+    return num.rnd(wte[inp])
+
+
+def embedding_bwd(dx, inp, V: int):
+    """dwte[v] = sum of dx over the positions whose input id is v (the
+    transpose of the lookup)."""
+    D = dx.shape[-1]
+    dW = np.zeros((V, D), dtype=dx.dtype)
+    np.add.at(dW, np.asarray(inp).reshape(-1), dx.reshape(-1, D))
+    return dW
+
+
+def value_embedding(v, h, wg, E, inp, C: int, num: _Num):
+    """[nanochat] value-embedding snippet: per KV head, e = E[inp] and the
+    gate g = 3 sigmoid(h[..., :C] wg^T) (READING: the first C channels of the
+    normalised attention input); v + g e, rounded once.  Returns (v, g, e)."""
+    B, T, Hkv, hd = v.shape
+    e = E[inp].reshape(B, T, Hkv, hd)
+    g = (3.0 * _sigmoid(h[..., :C] @ wg.T)).astype(num.dt)     # [B,T,Hkv]
+    return num.rnd(v + g[..., None] * e), g, e
+
+
+def value_embedding_bwd(dv, g, e, h, wg, inp, V: int):
+    """Gradients of value_embedding from dv [B,T,Hkv,hd]: with s the sigmoid,
+    dg = sum_d dv e, dzg = dg 3 s (1 - s) = dg g (1 - g/3); dwg = dzg^T h[:,
+    :C]; dE[inp] += g dv; and the gate's share of dh[..., :C] is dzg wg.
+    Returns (dzg, dwg, dE, dh_c)."""
+    B, T, Hkv, hd = dv.shape
+    C = wg.shape[1]
+    dt = dv.dtype
+    dgate = np.sum(dv * e, axis=-1)                             # [B,T,Hkv]
+    dzg = dgate * g * (1.0 - g / 3.0)                           # 3s(1-s)
+    dwg = (dzg.reshape(-1, Hkv).T @ h[..., :C].reshape(-1, C)).astype(dt)
+    dE = np.zeros((V, Hkv * hd), dtype=dt)
+    np.add.at(dE, np.asarray(inp).reshape(-1), (g[..., None] * dv).reshape(B * T, Hkv * hd))
+    return dzg, dwg, dE, dzg @ wg
+
+
 def forward(cfg: dict, flat_params, tokens, precision: str = "fp32",
             keep: bool = True):
     """One forward pass.  tokens [B, T+1] int; inputs are the first T ids,
@@ -365,7 +406,7 @@ def forward(cfg: dict, flat_params, tokens, precision: str = "fp32",
     C, eps = cfg["ve_gate_channels"], cfg["norm_eps"]
     cos, sin = rope_tables(T, hd, cfg["rope_base"])
 
-    x = num.rnd(P["wte"][inp])                                   # [B,T,D]
+    x = embedding(P["wte"], inp, num)                            # [B,T,D]
     layers = []
     for l in range(cfg["n_layer"]):
         c = {}
@@ -373,9 +414,7 @@ def forward(cfg: dict, flat_params, tokens, precision: str = "fp32",
         qkv = num.rnd(h @ P[f"l{l}.wqkv"].T)
         q, k, v = _split_qkv(qkv, cfg)
         if is_ve_layer(cfg, l):
-            e = P[f"l{l}.ve"][inp].reshape(B, T, Hkv, hd)
-            g = (3.0 * _sigmoid(h[..., :C] @ P[f"l{l}.wg"].T)).astype(dt)  # [B,T,Hkv]
-            v = num.rnd(v + g[..., None] * e)
+            v, g, e = value_embedding(v, h, P[f"l{l}.wg"], P[f"l{l}.ve"], inp, C, num)
             c.update(e=e, g=g)
         q, rq = rmsnorm(rope(q, cos, sin, num), eps, num)
         k, rk = rmsnorm(rope(k, cos, sin, num), eps, num)
@@ -449,22 +488,15 @@ def backward(cfg: dict, cache: dict) -> dict:
                                @ c["h"].reshape(B * T, D)).astype(dt)
         if is_ve_layer(cfg, l):
             # v = v_lin + g * e,  g = 3 sigmoid(zg),  zg = h[:, :C] Wg^T
-            g, e = c["g"], c["e"]
-            dgate = np.sum(dv * e, axis=-1)                      # [B,T,Hkv]
-            dzg = dgate * g * (1.0 - g / 3.0)                    # 3s(1-s)
-            grads[f"l{l}.wg"] = (dzg.reshape(-1, Hkv).T
-                                 @ c["h"][..., :C].reshape(-1, C)).astype(dt)
-            dE = np.zeros_like(P[f"l{l}.ve"])
-            np.add.at(dE, inp.reshape(-1),
-                      (g[..., None] * dv).reshape(B * T, Hkv * hd))
+            _, dwg, dE, dh_c = value_embedding_bwd(dv.astype(dt), c["g"], c["e"], c["h"],
+                                                   P[f"l{l}.wg"], inp, P[f"l{l}.ve"].shape[0])
+            grads[f"l{l}.wg"] = dwg
             grads[f"l{l}.ve"] = dE
             dh = dh.astype(dt).copy()
-            dh[..., :C] += dzg @ P[f"l{l}.wg"]
+            dh[..., :C] += dh_c
         dx = num.rnd(dx + rmsnorm_bwd(dh, c["h"], c["r"], num))
 
-    dwte = np.zeros_like(P["wte"])
-    np.add.at(dwte, inp.reshape(-1), dx.reshape(B * T, D))
-    grads["wte"] = dwte
+    grads["wte"] = embedding_bwd(dx, inp, P["wte"].shape[0])
     return grads
 
 
