@@ -85,6 +85,15 @@ _SIGS = {
                                  _i32, _i32, _vp]),
     "gpt_k_ce": (C.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp]),
     "gpt_k_lm_ce_scratch_bytes": (_sz, [_i64, _i32]),
+    "gpt_k_embed_fwd": (C.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp]),
+    "gpt_k_embed_bwd_scratch_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "gpt_k_embed_bwd": (C.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _sz, _i32,
+                                  _vp]),
+    "gpt_k_ve_fwd": (C.c_int, [_vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _vp,
+                               _i32, _i32, _i32, _vp]),
+    "gpt_k_ve_bwd_scratch_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "gpt_k_ve_bwd": (C.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
+                               _i32, _i32, _vp, _vp, _vp, _i32, _vp, _sz, _i32, _vp]),
     "gpt_k_lm_ce": (C.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _f32, _vp, _vp]),
     "gpt_prof_start": (C.c_int, [_i32]),
     "gpt_prof_stop": (C.c_int, []),
@@ -227,6 +236,38 @@ def k_attn_bwd_scratch_bytes(B, T, H, hd):
 def k_attn_bwd(qkv, o, lse, dout, dqkv, scratch, B, T, H, Hkv, hd, window, dtype, stream=None):
     _check(lib().gpt_k_attn_bwd(_ptr(qkv), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dqkv),
                                 _ptr(scratch), B, T, H, Hkv, hd, window, dtype, _stream(stream)))
+
+
+def k_embed_fwd(tokens, B, T, wte, V, D, x, dtype, stream=None):
+    _check(lib().gpt_k_embed_fwd(_ptr(tokens), B, T, _ptr(wte), V, D, _ptr(x), dtype,
+                                 _stream(stream)))
+
+
+def k_embed_bwd_scratch_bytes(B, T, V, D):
+    return int(lib().gpt_k_embed_bwd_scratch_bytes(B, T, V, D))
+
+
+def k_embed_bwd(tokens, B, T, dx, V, D, dwte, accumulate, scratch, dtype, stream=None):
+    nb = scratch.numel() * scratch.element_size() if scratch is not None else 0
+    _check(lib().gpt_k_embed_bwd(_ptr(tokens), B, T, _ptr(dx), V, D, _ptr(dwte), accumulate,
+                                 _ptr(scratch), nb, dtype, _stream(stream)))
+
+
+def k_ve_fwd(tokens, B, T, h, D, wg, C_, E, qkv, ldqkv, voff, g, Hkv, hd, dtype, stream=None):
+    _check(lib().gpt_k_ve_fwd(_ptr(tokens), B, T, _ptr(h), D, _ptr(wg), C_, _ptr(E), _ptr(qkv),
+                              ldqkv, voff, _ptr(g), Hkv, hd, dtype, _stream(stream)))
+
+
+def k_ve_bwd_scratch_bytes(B, T, V, Hkv, hd, C_):
+    return int(lib().gpt_k_ve_bwd_scratch_bytes(B, T, V, Hkv, hd, C_))
+
+
+def k_ve_bwd(tokens, B, T, dqkv, ldqkv, voff, E, g, h, D, C_, V, Hkv, hd, vez, dE, dwg,
+             accumulate, scratch, dtype, stream=None):
+    nb = scratch.numel() * scratch.element_size()
+    _check(lib().gpt_k_ve_bwd(_ptr(tokens), B, T, _ptr(dqkv), ldqkv, voff, _ptr(E), _ptr(g),
+                              _ptr(h), D, C_, V, Hkv, hd, _ptr(vez), _ptr(dE), _ptr(dwg),
+                              accumulate, _ptr(scratch), nb, dtype, _stream(stream)))
 
 
 def k_lm_ce_scratch_bytes(rows, V):

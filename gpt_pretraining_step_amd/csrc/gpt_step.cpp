@@ -722,6 +722,101 @@ int gpt_k_ce(const float* z, const int32_t* tgt, int64_t rows, int32_t V, float*
   return GPT_OK;
 }
 
+// ---- token embedding and value embedding (kernel-level entries)
+int gpt_k_embed_fwd(const int32_t* tokens, int32_t B, int32_t T, const void* wte, int32_t V,
+                    int32_t D, void* x, int32_t dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({tokens, wte, x}))) return st;
+  if (B < 1 || T < 1 || V < 1 || D < 1) return fail(GPT_ERR_INVALID_ARG, "bad sizes");
+  KERNEL_TRY(gk::embed_fwd(tokens, B, T, wte, x, D, (gk::DType)dtype, s));
+  return GPT_OK;
+}
+
+static bool embed_sorted_ok(int32_t D, const void* dx, const float* dW) {
+  return D % 4 == 0 && D <= 2048 && aligned16(dx) && aligned16(dW);
+}
+
+size_t gpt_k_embed_bwd_scratch_bytes(int32_t B, int32_t T, int32_t V, int32_t D) {
+  if (B < 1 || T < 1 || V < 1 || D < 1) return 0;
+  return gk::tok_sort_bytes((int64_t)B * T, V, D);
+}
+
+int gpt_k_embed_bwd(const int32_t* tokens, int32_t B, int32_t T, const void* dx, int32_t V,
+                    int32_t D, float* dwte, int32_t accumulate, void* scratch,
+                    size_t scratch_bytes, int32_t dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({tokens, dx, dwte}))) return st;
+  if (B < 1 || T < 1 || V < 1 || D < 1) return fail(GPT_ERR_INVALID_ARG, "bad sizes");
+  if (accumulate != 0 && accumulate != 1)
+    return fail(GPT_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  const int64_t N = (int64_t)B * T;
+  if (scratch && scratch_bytes >= gk::tok_sort_bytes(N, V, D) && embed_sorted_ok(D, dx, dwte)) {
+    KERNEL_TRY(gk::tok_sort(tokens, B, T, V, D, scratch, s));
+    KERNEL_TRY(gk::seg_scatter(scratch, N, V, D, dx, D, D, nullptr, 1, D, dwte, accumulate,
+                               (gk::DType)dtype, s));
+  } else {
+    if (!accumulate) KERNEL_TRY(gk::fill_zero(dwte, (int64_t)V * D * 4, s));
+    KERNEL_TRY(gk::embed_bwd(tokens, B, T, dx, D, dwte, D, (gk::DType)dtype, s));
+  }
+  return GPT_OK;
+}
+
+int gpt_k_ve_fwd(const int32_t* tokens, int32_t B, int32_t T, const void* h, int32_t D,
+                 const void* wg, int32_t C, const void* E, void* qkv, int32_t ldqkv,
+                 int32_t voff, float* g, int32_t Hkv, int32_t hd, int32_t dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({tokens, h, wg, E, qkv, g}))) return st;
+  if (B < 1 || T < 1 || D < 1 || C < 1 || C > D || Hkv < 1 || Hkv > 64 || hd < 4 || hd % 4 ||
+      voff < 0 || voff + Hkv * hd > ldqkv)
+    return fail(GPT_ERR_INVALID_ARG, "bad sizes");
+  KERNEL_TRY(gk::ve_fwd(tokens, B, T, h, D, wg, C, E, qkv, ldqkv, voff, g, Hkv, hd,
+                        (gk::DType)dtype, s));
+  return GPT_OK;
+}
+
+size_t gpt_k_ve_bwd_scratch_bytes(int32_t B, int32_t T, int32_t V, int32_t Hkv, int32_t hd,
+                                  int32_t C) {
+  if (B < 1 || T < 1 || V < 1 || Hkv < 1 || hd < 1 || C < 1) return 0;
+  return pad256(gk::ve_wgrad_scratch_bytes(Hkv, C)) +
+         gk::tok_sort_bytes((int64_t)B * T, V, Hkv * hd);
+}
+
+int gpt_k_ve_bwd(const int32_t* tokens, int32_t B, int32_t T, const void* dqkv, int32_t ldqkv,
+                 int32_t voff, const void* E, const float* g, const void* h, int32_t D,
+                 int32_t C, int32_t V, int32_t Hkv, int32_t hd, float* vez, float* dE,
+                 float* dwg, int32_t accumulate, void* scratch, size_t scratch_bytes,
+                 int32_t dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) ||
+      (st = check_ptrs({tokens, dqkv, E, g, h, vez, dE, dwg, scratch})))
+    return st;
+  if (B < 1 || T < 1 || D < 1 || C < 1 || C > D || V < 1 || Hkv < 1 || Hkv > 64 || hd < 4 ||
+      hd % 4 || voff < 0 || voff + Hkv * hd > ldqkv)
+    return fail(GPT_ERR_INVALID_ARG, "bad sizes");
+  if (accumulate != 0 && accumulate != 1)
+    return fail(GPT_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  const int64_t N = (int64_t)B * T;
+  const int W = Hkv * hd;
+  const size_t part = pad256(gk::ve_wgrad_scratch_bytes(Hkv, C));
+  if (scratch_bytes < part) return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "scratch too small");
+  const gk::DType dt = (gk::DType)dtype;
+  const size_t es = dt == gk::BF16 ? 2 : 4;
+  const bool sorted = scratch_bytes >= part + gk::tok_sort_bytes(N, V, W) && W % 4 == 0 &&
+                      W <= 2048 && ldqkv % 4 == 0 && ((size_t)voff * es) % 16 == 0;
+  if (sorted) {
+    void* sortws = (char*)scratch + part;
+    KERNEL_TRY(gk::tok_sort(tokens, B, T, V, W, sortws, s));
+    KERNEL_TRY(gk::ve_vez(tokens, B, T, dqkv, ldqkv, voff, E, g, vez, Hkv, hd, dt, s));
+    KERNEL_TRY(gk::seg_scatter(sortws, N, V, W, (const char*)dqkv + voff * es, ldqkv, W, g, Hkv,
+                               hd, dE, accumulate, dt, s));
+  } else {
+    if (!accumulate) KERNEL_TRY(gk::fill_zero(dE, (int64_t)V * W * 4, s));
+    KERNEL_TRY(gk::ve_bwd(tokens, B, T, dqkv, ldqkv, voff, E, g, vez, dE, Hkv, hd, dt, s));
+  }
+  KERNEL_TRY(gk::ve_wgrad(vez, h, D, N, Hkv, C, dwg, accumulate, (float*)scratch, dt, s));
+  return GPT_OK;
+}
+
 size_t gpt_k_lm_ce_scratch_bytes(int64_t rows, int32_t V) {
   if (rows < 1 || V < 256 || V % 256) return 0;
   return pad256(gk::lm_ce_stats_bytes(rows, V)) + pad256((size_t)rows * 4);

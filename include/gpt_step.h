@@ -262,6 +262,48 @@ int gpt_k_attn_bwd(const void* qkv, const void* o, const float* lse,
                    int32_t T, int32_t H, int32_t Hkv, int32_t hd,
                    int32_t window, int32_t dtype, hipStream_t s);
 
+/* Token embedding (a1).  tokens [B, T+1] int32 (inputs are the first T of
+ * each row), wte [V, D] dtype -> x [B*T, D] dtype: x[b*T + t] =
+ * wte[tokens[b][t]] (bitwise copies of the rows). */
+int gpt_k_embed_fwd(const int32_t* tokens, int32_t B, int32_t T,
+                    const void* wte, int32_t V, int32_t D, void* x,
+                    int32_t dtype, hipStream_t s);
+/* Its gradient: dwte [V, D] fp32 (=, or += with accumulate = 1) the sum of
+ * dx [B*T, D] (dtype) over the positions holding each id.  With scratch of
+ * at least gpt_k_embed_bwd_scratch_bytes bytes (and D % 4 == 0, D <= 2048)
+ * the ids are sorted once and every row summed in a fixed order
+ * (deterministic); otherwise fp32 atomics. */
+size_t gpt_k_embed_bwd_scratch_bytes(int32_t B, int32_t T, int32_t V,
+                                     int32_t D);
+int gpt_k_embed_bwd(const int32_t* tokens, int32_t B, int32_t T,
+                    const void* dx, int32_t V, int32_t D, float* dwte,
+                    int32_t accumulate, void* scratch, size_t scratch_bytes,
+                    int32_t dtype, hipStream_t s);
+
+/* Value embedding (a4), [nanochat] value-embedding snippet.  For every token
+ * n (input id e = tokens[b][t]) and KV head kv: g[n, kv] = 3 sigmoid(
+ * h[n, :C] . wg[kv, :]) (fp32 out, [B*T, Hkv]), and in place
+ * qkv[n, voff + kv*hd + d] += g[n, kv] * E[e, kv*hd + d], rounded once.
+ * h [B*T, D], wg [Hkv, C], E [V, Hkv*hd], qkv [B*T, ldqkv]; all dtype. */
+int gpt_k_ve_fwd(const int32_t* tokens, int32_t B, int32_t T, const void* h,
+                 int32_t D, const void* wg, int32_t C, const void* E,
+                 void* qkv, int32_t ldqkv, int32_t voff, float* g,
+                 int32_t Hkv, int32_t hd, int32_t dtype, hipStream_t s);
+/* Its gradients from dv = dqkv[:, voff : voff + Hkv*hd]: vez [B*T, Hkv]
+ * fp32 = (sum_d dv e) g (1 - g/3) (the gate pre-activation's gradient; its
+ * share of dh[:, :C] is vez wg), dE [V, Hkv*hd] fp32 (=, or +=) the sum of
+ * g dv over the positions holding each id, dwg [Hkv, C] fp32 (=, or +=)
+ * vez^T h[:, :C].  scratch: at least gpt_k_ve_bwd_scratch_bytes bytes (the
+ * sorted, deterministic table sum when the widths allow, else atomics). */
+size_t gpt_k_ve_bwd_scratch_bytes(int32_t B, int32_t T, int32_t V, int32_t Hkv,
+                                  int32_t hd, int32_t C);
+int gpt_k_ve_bwd(const int32_t* tokens, int32_t B, int32_t T,
+                 const void* dqkv, int32_t ldqkv, int32_t voff, const void* E,
+                 const float* g, const void* h, int32_t D, int32_t C, int32_t V,
+                 int32_t Hkv, int32_t hd, float* vez, float* dE, float* dwg,
+                 int32_t accumulate, void* scratch, size_t scratch_bytes,
+                 int32_t dtype, hipStream_t s);
+
 /* Fused lm_head + softmax cross-entropy (bf16): logits = h [rows, D] times
  * w [V, D]^T are formed in fp32 inside the product and never stored; per
  * row and 256-column tile the product keeps the max and sum of exp(logit -

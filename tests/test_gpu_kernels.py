@@ -389,6 +389,92 @@ def test_attention_bounded_extreme_scores(sign):
 
 
 # ----------------------------------------------------------- cross-entropy
+# ------------------------------------------------ token / value embedding
+def _tokens(B, T, V, seed, spread):
+    """Rows of T+1 ids; ids drawn from the first `spread` entries so most
+    repeat, and every id >= spread is absent from the batch."""
+    return np.random.default_rng(seed).integers(0, spread, (B, T + 1)).astype(np.int32)
+
+
+@pytest.mark.parametrize("dt", [G.BF16, G.F32])
+@pytest.mark.parametrize("D,sorted_path", [(96, True), (96, False), (30, False)])
+def test_token_embedding(dt, D, sorted_path):
+    B, T, V = 3, 70, 300
+    say("embed", dt, D, sorted_path)
+    bf = dt == G.BF16
+    tok = _tokens(B, T, V, 60, 40)
+    inp = tok[:, :T]
+    wte = rnd_in((V, D), 61, bf16=bf)
+    dx = rnd_in((B * T, D), 62, bf16=bf)
+    ttok = dev(tok, torch.int32)
+    x = torch.empty(B * T, D, dtype=tdtype(dt), device=DEV)
+    G.k_embed_fwd(ttok, B, T, dev(wte, tdtype(dt)), V, D, x, dt)
+    scr = (torch.empty(G.k_embed_bwd_scratch_bytes(B, T, V, D), dtype=torch.uint8, device=DEV)
+           if sorted_path else None)
+    tdx = dev(dx, tdtype(dt))
+    dW = torch.full((V, D), 7.0, dtype=torch.float32, device=DEV)   # overwritten
+    G.k_embed_bwd(ttok, B, T, tdx, V, D, dW, 0, scr, dt)
+    first = dW.clone()
+    G.k_embed_bwd(ttok, B, T, tdx, V, D, dW, 1, scr, dt)            # += the same
+    torch.cuda.synchronize()
+    # the lookup copies rows exactly
+    np.testing.assert_array_equal(to_np(x).reshape(B, T, D), wte[inp])
+    ref = O.embedding_bwd(dx.astype(np.float64), inp, V)
+    assert rel_err(to_np(first), ref) < 1e-6
+    assert rel_err(to_np(dW), 2 * ref) < 1e-6
+    assert np.all(to_np(first)[40:] == 0.0)          # absent ids: exact zeros
+    if sorted_path:                                   # fixed summation order
+        G.k_embed_bwd(ttok, B, T, tdx, V, D, dW, 0, scr, dt)
+        torch.cuda.synchronize()
+        assert torch.equal(first, dW)
+
+
+@pytest.mark.parametrize("dt", [G.BF16, G.F32])
+@pytest.mark.parametrize("C,hd", [(32, 16), (7, 32), (64, 128)])
+def test_value_embedding(dt, C, hd):
+    B, T, V, D, H, Hkv = 2, 50, 60, 64, 2, 2
+    say("ve", dt, C, hd)
+    bf = dt == G.BF16
+    num = _Num("bf16emu" if bf else "fp32")
+    tok = _tokens(B, T, V, 70, 25)
+    inp = tok[:, :T]
+    ld = (H + 2 * Hkv) * hd
+    voff = (H + Hkv) * hd
+    h = rnd_in((B, T, D), 71, bf16=bf)
+    wg = rnd_in((Hkv, C), 72, 0.3, bf16=bf)
+    E = rnd_in((V, Hkv * hd), 73, bf16=bf)
+    qkv = rnd_in((B * T, ld), 74, bf16=bf)
+    v = qkv[:, voff:].reshape(B, T, Hkv, hd)
+    v_ref, g_ref, e = O.value_embedding(v, h, wg, E, inp, C, num)
+    ttok = dev(tok, torch.int32)
+    th, twg, tE = dev(h, tdtype(dt)).reshape(B * T, D), dev(wg, tdtype(dt)), dev(E, tdtype(dt))
+    tqkv = dev(qkv, tdtype(dt))
+    g = torch.empty(B * T, Hkv, dtype=torch.float32, device=DEV)
+    G.k_ve_fwd(ttok, B, T, th, D, twg, C, tE, tqkv, ld, voff, g, Hkv, hd, dt)
+    # backward from a random dv (in the v slot of a dqkv buffer)
+    dqkv = rnd_in((B * T, ld), 75, bf16=bf)
+    dv = dqkv[:, voff:].reshape(B, T, Hkv, hd)
+    dzg, dwg_ref, dE_ref, _ = O.value_embedding_bwd(dv.astype(np.float64), g_ref.astype(np.float64),
+                                                    e.astype(np.float64), h.astype(np.float64),
+                                                    wg.astype(np.float64), inp, V)
+    vez = torch.empty(B * T, Hkv, dtype=torch.float32, device=DEV)
+    dE = torch.empty(V, Hkv * hd, dtype=torch.float32, device=DEV)
+    dwg = torch.empty(Hkv, C, dtype=torch.float32, device=DEV)
+    scr = torch.empty(G.k_ve_bwd_scratch_bytes(B, T, V, Hkv, hd, C), dtype=torch.uint8,
+                      device=DEV)
+    G.k_ve_bwd(ttok, B, T, dev(dqkv, tdtype(dt)), ld, voff, tE, g, th, D, C, V, Hkv, hd, vez, dE,
+               dwg, 0, scr, dt)
+    torch.cuda.synchronize()
+    out = to_np(tqkv)
+    tol = 2e-2 if bf else 1e-5
+    assert rel_err(out[:, voff:].reshape(B, T, Hkv, hd), v_ref) < tol
+    np.testing.assert_array_equal(out[:, :voff], qkv[:, :voff])      # q, k untouched
+    assert rel_err(to_np(g).reshape(B, T, Hkv), g_ref) < 1e-5
+    assert rel_err(to_np(vez).reshape(B, T, Hkv), dzg) < 1e-5
+    assert rel_err(to_np(dE), dE_ref) < 1e-5
+    assert rel_err(to_np(dwg), dwg_ref) < 1e-5
+
+
 @pytest.mark.parametrize("rows,D,V,scale", [(300, 128, 1024, 1.0), (513, 64, 32768, 0.3),
                                             (37, 256, 512, 4.0)])
 def test_fused_lm_head_cross_entropy(rows, D, V, scale):
