@@ -12,7 +12,8 @@ Sources (pages, cited by title and section):
   [nanochat]  "5만원으로 나만의 ChatGPT 훈련하는 방법" (apidog.com blog, nanochat
               walkthrough): "1. GPT model (nanochat/gpt.py)" architecture list,
               value-embedding snippet; "3. precision management"; "5. flash
-              attention integration" (causal + window_size call).
+              attention integration" (causal + window_size call); "6.
+              inference engine" (KV-cache attention of new tokens).
   [microgpt]  "microgpt" (news.hada.io): "model architecture" (RMSNorm, ReLU,
               residual, multi-head attention), "training loop" (cross-entropy
               on the next token), "parameter initialisation" (~4,192 params).
@@ -25,7 +26,8 @@ differences, closed forms, invariants, brute force); see the test suite.
 from .gpt import (  # noqa: F401
     PRECISIONS, param_layout, param_count, unpack_params, window_for_layer,
     is_ve_layer, visible_mask, rope_tables, rope, rope_bwd, rmsnorm,
-    rmsnorm_bwd, attention, attention_bwd, attention_tiled, cross_entropy,
+    rmsnorm_bwd, attention, attention_bwd, attention_tiled, decode_attention,
+    cross_entropy,
     embedding, embedding_bwd, value_embedding, value_embedding_bwd,
     forward, backward, step, eval_bpb, round_bf16,
 )

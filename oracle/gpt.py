@@ -312,6 +312,43 @@ def attention_tiled(q, k, v, W: int, tile: int = 128):
     return o, lse
 
 
+def decode_attention(q, k_cache, v_cache, lens, W: int, num: _Num):
+    """Attention of the newest tokens over a KV cache ([nanochat] "6.
+    inference engine": prefilled caches, flash_attn_with_kvcache).
+
+    q [B,Tq,H,hd]; k_cache/v_cache [B,Tmax,Hkv,hd]; lens[b] = L_b cached
+    positions (clamped to [0, Tmax]).  READING: the Tq queries are the last
+    Tq positions, p = L_b - Tq + t, and see key j < L_b iff 0 <= p - j <= W
+    (the training mask); query head h reads KV head h // G; scale
+    1/sqrt(hd).  Returns o [B,Tq,H,hd] (rounded) and lse [B,H,Tq]; a query
+    that sees no key gets o = 0, lse = -inf.
+    """
+    q = np.asarray(q, dtype=num.dt)
+    B, Tq, H, hd = q.shape
+    Tmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    G = H // Hkv
+    scale = num.dt(1.0 / math.sqrt(hd))
+    o = np.zeros_like(q)
+    lse = np.full((B, H, Tq), -np.inf, dtype=num.dt)
+    for b in range(B):
+        L = min(max(int(lens[b]), 0), Tmax)
+        for t in range(Tq):
+            p = L - Tq + t
+            j = np.arange(L)
+            keys = j[(p - j >= 0) & (p - j <= W)]
+            if len(keys) == 0:
+                continue
+            for h in range(H):
+                kk = np.asarray(k_cache[b, keys, h // G], num.dt)
+                vv = np.asarray(v_cache[b, keys, h // G], num.dt)
+                sc = (kk @ q[b, t, h]) * scale
+                m = sc.max()
+                e = np.exp(sc - m)
+                o[b, t, h] = (e / e.sum()) @ vv
+                lse[b, h, t] = m + np.log(e.sum())
+    return num.rnd(o), lse
+
+
 def cross_entropy(z, tgt, num: _Num):
     """Per-token softmax cross-entropy on logits z [N, V].
 

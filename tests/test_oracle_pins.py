@@ -225,6 +225,96 @@ def test_dense_equals_tiled_online_softmax(W):
     np.testing.assert_allclose(lset, lse, atol=1e-12)
 
 
+# ------------------------------------------------------- KV-cache decode
+def _rand_cache(B=3, Tq=2, Tmax=23, H=4, Hkv=2, hd=8, seed=11):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, Tq, H, hd)), rng.standard_normal((B, Tmax, Hkv, hd)),
+            rng.standard_normal((B, Tmax, Hkv, hd)))
+
+
+@pytest.mark.parametrize("W", [0, 2, 9, 100])
+def test_decode_attention_matches_torch_sdpa(W):
+    """Decode attention equals torch's scaled_dot_product_attention (CPU,
+    float64) of each sequence's queries over its first L_b cache rows, with
+    the boolean mask 0 <= p - j <= W written from the positions p = L_b - Tq
+    + t; sequences of different lengths."""
+    q, kc, vc = _rand_cache()
+    lens = np.array([23, 9, 2])
+    o, lse = O.decode_attention(q, kc, vc, lens, W, _Num("fp64"))
+    B, Tq, H, hd = q.shape
+    G = H // kc.shape[2]
+    for b in range(B):
+        L = int(lens[b])
+        pos = np.arange(L - Tq, L)[:, None]
+        j = np.arange(L)[None, :]
+        mask = torch.from_numpy((pos - j >= 0) & (pos - j <= W))
+        tq = torch.from_numpy(q[b]).permute(1, 0, 2)
+        tk = torch.from_numpy(np.repeat(kc[b, :L], G, axis=1)).permute(1, 0, 2)
+        tv = torch.from_numpy(np.repeat(vc[b, :L], G, axis=1)).permute(1, 0, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)
+        np.testing.assert_allclose(o[b], ref.permute(1, 0, 2).numpy(), atol=1e-12)
+        s = np.einsum("thd,jhd->htj", q[b], np.repeat(kc[b, :L], G, axis=1)) / math.sqrt(hd)
+        s = np.where(mask.numpy()[None], s, -np.inf)
+        np.testing.assert_allclose(lse[b], np.log(np.exp(s).sum(-1)), atol=1e-12)
+
+
+def test_decode_attention_is_the_last_rows_of_training_attention():
+    """With the new tokens' keys in the cache, decode attention of the last Tq
+    positions equals those rows of the dense causal attention over the whole
+    sequence (the two masks are the same predicate)."""
+    q_all, k, v = _rand_qkv(B=2, T=31, seed=7)
+    for W in (0, 4, 30):
+        o, lse = O.attention(q_all, k, v, W, _Num("fp64"))
+        for Tq in (1, 3):
+            od, lsed = O.decode_attention(q_all[:, -Tq:], k, v, np.array([31, 31]), W,
+                                          _Num("fp64"))
+            np.testing.assert_allclose(od, o[:, -Tq:], atol=1e-12)
+            np.testing.assert_allclose(lsed, lse[:, :, -Tq:], atol=1e-12)
+
+
+def test_decode_attention_closed_forms():
+    """W = 0: the query sees only its own key, so o = v[p] and lse = q.k[p] /
+    sqrt(hd).  Equal keys: o is the mean of the visible values and lse =
+    score + log(count).  No visible key (L < Tq): o = 0, lse = -inf.  Rows at
+    or past L never matter (NaN there changes nothing); lengths outside [0,
+    Tmax] act as the nearest end."""
+    q, kc, vc = _rand_cache(B=2, Tq=2, Tmax=12, H=2, Hkv=1, hd=4)
+    num = _Num("fp64")
+    lens = np.array([12, 5])
+    o, lse = O.decode_attention(q, kc, vc, lens, 0, num)
+    for b, L in enumerate(lens):
+        for t in range(2):
+            p = L - 2 + t
+            for h in range(2):
+                np.testing.assert_allclose(o[b, t, h], vc[b, p, 0], atol=1e-14)
+                assert lse[b, h, t] == pytest.approx(q[b, t, h] @ kc[b, p, 0] / 2.0, abs=1e-14)
+    kc_eq = np.broadcast_to(kc[:, :1], kc.shape).copy()
+    o, lse = O.decode_attention(q, kc_eq, vc, lens, 3, num)
+    for b, L in enumerate(lens):
+        for t in range(2):
+            p = L - 2 + t
+            keys = [j for j in range(L) if 0 <= p - j <= 3]
+            for h in range(2):
+                np.testing.assert_allclose(o[b, t, h], vc[b, keys, 0].mean(0), atol=1e-14)
+                sc = q[b, t, h] @ kc[b, 0, 0] / 2.0
+                assert lse[b, h, t] == pytest.approx(sc + math.log(len(keys)), abs=1e-13)
+    o, lse = O.decode_attention(q, kc, vc, np.array([1, 0]), 5, num)
+    assert np.all(o[1] == 0.0) and np.all(np.isneginf(lse[1]))
+    assert np.all(o[0, 0] == 0.0) and np.all(np.isneginf(lse[0, :, 0]))
+    np.testing.assert_allclose(o[0, 1, 0], vc[0, 0, 0], atol=1e-14)
+    kn, vn = kc.copy(), vc.copy()
+    kn[1, 5:], vn[1, 5:] = np.nan, np.nan
+    a = O.decode_attention(q, kc, vc, lens, 7, num)
+    bb = O.decode_attention(q, kn, vn, lens, 7, num)
+    np.testing.assert_array_equal(a[0], bb[0])
+    np.testing.assert_array_equal(a[1], bb[1])
+    # lengths are clamped to [0, Tmax]
+    hi = O.decode_attention(q, kc, vc, np.array([40, -3]), 7, num)
+    ref = O.decode_attention(q, kc, vc, np.array([12, 0]), 7, num)
+    np.testing.assert_array_equal(hi[0], ref[0])
+    np.testing.assert_array_equal(hi[1], ref[1])
+
+
 # ------------------------------------------------------- norm / rotary / CE
 def test_rmsnorm_matches_torch():
     x = np.random.default_rng(0).standard_normal((5, 7, 24))
