@@ -1,6 +1,7 @@
 """Benchmark of the GPT training step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d12]
+    python bench.py --workload decode [--config d12gqa] [--decode-batch 64]
 
 Times K forward+backward steps of the d12 model (12 layers, width 768, 6
 heads of 128, vocab 32768, 16 rows of 2048 tokens, 'SSSL' windows 1024/2048,
@@ -14,6 +15,11 @@ roofline.  HBM traffic of that kernel comes from the rocprofv3 counter
 summary in profiles/ when the kernel's sources still hash to the value
 recorded there (else null).  The CPU oracle is timed on a bounded sample of
 the same workload as a reported baseline.
+
+With --workload decode it instead times the attention of one generation
+step: one new token for each of --decode-batch sequences whose caches hold
+seq_len positions, every layer over its own cache with that layer's window;
+the line reports new tokens/s and the KV-cache bytes read per second.
 """
 from __future__ import annotations
 
@@ -241,18 +247,126 @@ def cpu_baseline(cfg, seconds_hint=20.0):
                       f"(fwd+bwd, numpy fp32, {dt:.1f} s)"}
 
 
+DECODE_METRIC = "decode attention: new tokens/s over KV caches (all layers), HBM GB/s"
+
+
+def decode_inputs_gpu(torch, B, T, H, Hkv, n_layer, seed):
+    """Per layer: q [B, 1, H, 128] and cached k [B, T, Hkv, 128] with unit-RMS
+    rows (as after QK-norm), v N(0, 1), bf16, drawn on the device from a
+    seeded generator; every cache full (length T)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+
+    def unit_rms(shape):
+        x = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+        return (x * torch.rsqrt(x.square().mean(-1, keepdim=True) + 1e-5)).bfloat16()
+
+    layers = []
+    for _ in range(n_layer):
+        q = unit_rms((B, 1, H, 128))
+        k = unit_rms((B, T, Hkv, 128))
+        v = torch.randn((B, T, Hkv, 128), generator=g, device="cuda").bfloat16()
+        layers.append((q, k, v))
+    return layers
+
+
+def cpu_decode_baseline(cfg, T, n_seq=32):
+    """The oracle's decode attention over every layer's window for n_seq
+    sequences of the workload (numpy fp32): new tokens/s."""
+    import numpy as np
+    import oracle as O
+    from oracle.gpt import _Num
+    rng = np.random.default_rng(7)
+    H, Hkv = cfg["n_head"], cfg["n_kv_head"]
+    dt = 0.0
+    for l in range(cfg["n_layer"]):
+        q = rng.standard_normal((n_seq, 1, H, 128), dtype=np.float32)
+        k = rng.standard_normal((n_seq, T, Hkv, 128), dtype=np.float32)
+        v = rng.standard_normal((n_seq, T, Hkv, 128), dtype=np.float32)
+        t0 = time.perf_counter()
+        O.decode_attention(q, k, v, np.full(n_seq, T), window_of(cfg, l), _Num("fp32"))
+        dt += time.perf_counter() - t0
+    threads = os.environ.get("OMP_NUM_THREADS")
+    cores = int(threads) if threads else len(os.sched_getaffinity(0))
+    return {"value": round(n_seq / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_seq} sequences x {T} cached positions, all {cfg['n_layer']} layers "
+                      f"(numpy fp32, {dt:.1f} s)"}
+
+
+def bench_decode(a, torch, G):
+    """One decode step's attention (one new token per sequence, every layer
+    over its own full cache with the layer's window) timed over a.steps
+    steps; roofline of the dominant launch in HBM bytes."""
+    import gptinputs as gi
+    cfg = gi.preset(a.config)
+    T, H, Hkv, n_layer = cfg["seq_len"], cfg["n_head"], cfg["n_kv_head"], cfg["n_layer"]
+    B = a.decode_batch
+    log(f"decode inputs: {n_layer} layers x {B} seq x {T} positions")
+    layers = decode_inputs_gpu(torch, B, T, H, Hkv, n_layer, seed=cfg["seed"])
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    outs = [(torch.empty(B, 1, H, 128, dtype=torch.bfloat16, device="cuda"),
+             torch.empty(B, H, 1, dtype=torch.float32, device="cuda")) for _ in range(n_layer)]
+    nbs = [G.k_attn_decode_scratch_bytes(B, 1, H, Hkv, T, window_of(cfg, l))
+           for l in range(n_layer)]
+    scr = torch.empty(max(16, max(nbs)), dtype=torch.uint8, device="cuda")
+    bound = 1.01 * math.sqrt(128)
+
+    def step():
+        for l, (q, k, v) in enumerate(layers):
+            o, lse = outs[l]
+            G.k_attn_decode(q, k, v, lens, o, lse, B, 1, T, H, Hkv, 128, window_of(cfg, l),
+                            bound, scr, G.BF16)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    for o, _ in outs:
+        assert torch.isfinite(o.float()).all()
+    ms = time_events(step, a.steps, torch) * 1e3
+    tok_s = B / (ms / 1e3)
+    kv_bytes = sum(2.0 * B * min(T, window_of(cfg, l) + 1) * Hkv * 128 * 2
+                   for l in range(n_layer))
+    log(f"decode step {ms * 1e3:.1f} us  {tok_s:,.0f} tok/s  {kv_bytes / ms / 1e6:,.0f} GB/s")
+    prof = kernel_profile(step, a.prof_steps, torch, G) if a.prof_steps > 0 else []
+    for r in prof:
+        log(f"  {r['ms_per_step'] * 1e3:8.1f} us/step {r['launches_per_step']:5.0f} x "
+            f"{r['avg_launch_ms'] * 1e3:8.1f} us  {r['gbps'] or 0:7.0f} GB/s  {r['kernel']}")
+    roof = roofline_of(prof[0], ms) if prof else None
+    cpu = None if a.no_cpu else cpu_decode_baseline(cfg, T)
+    out = {
+        "metric": DECODE_METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded unit-RMS q, k and N(0,1) v, full caches)",
+        "config": {"workload": f"{a.config} decode attention: {B} sequences x {T} cached "
+                               f"positions, 1 new token each, {n_layer} layers "
+                               f"'{cfg['window_pattern']}' {cfg['window_short']}/"
+                               f"{cfg['window_long']}, {H} heads on {Hkv} KV heads x 128",
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "kv_bytes_per_step": kv_bytes, "kv_gbps": round(kv_bytes / ms / 1e6, 1),
+        "roofline": roof, "cpu_baseline": cpu,
+        "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
+                    for r in prof],
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="d12")
+    ap.add_argument("--config", default=None, help="preset (train: d12, decode: d12gqa)")
     ap.add_argument("--eval-rows", type=int, default=64)
     ap.add_argument("--prof-steps", type=int, default=2,
                     help="steps run with launch recording for the per-kernel split (0: none)")
     ap.add_argument("--shapes", action="store_true",
                     help="also time every product / attention shape alone")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--workload", choices=("train", "decode"), default="train",
+                    help="train: the fwd+bwd step; decode: KV-cache decode attention")
+    ap.add_argument("--decode-batch", type=int, default=64,
+                    help="sequences sampled in parallel (decode workload)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB device copy used to calibrate HBM counters")
     a = ap.parse_args()
@@ -272,6 +386,11 @@ def main():
     if a.copy_calibration:
         copy_calibration(torch)
         return
+    if a.workload == "decode":
+        a.config = a.config or "d12gqa"
+        bench_decode(a, torch, G)
+        return
+    a.config = a.config or "d12"
     cfg = gi.preset(a.config)
     train_fpt, eval_fpt, mm = model_flops(cfg)
     B, T = cfg["batch"], cfg["seq_len"]

@@ -83,6 +83,9 @@ _SIGS = {
     "gpt_k_attn_bwd_scratch_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "gpt_k_attn_bwd": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _vp]),
+    "gpt_k_attn_decode_scratch_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "gpt_k_attn_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                    _i32, _i32, _f32, _vp, _sz, _i32, _vp]),
     "gpt_k_ce": (C.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp]),
     "gpt_k_lm_ce_scratch_bytes": (_sz, [_i64, _i32]),
     "gpt_k_embed_fwd": (C.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp]),
@@ -236,6 +239,18 @@ def k_attn_bwd_scratch_bytes(B, T, H, hd):
 def k_attn_bwd(qkv, o, lse, dout, dqkv, scratch, B, T, H, Hkv, hd, window, dtype, stream=None):
     _check(lib().gpt_k_attn_bwd(_ptr(qkv), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dqkv),
                                 _ptr(scratch), B, T, H, Hkv, hd, window, dtype, _stream(stream)))
+
+
+def k_attn_decode_scratch_bytes(B, Tq, H, Hkv, Tmax, window):
+    return int(lib().gpt_k_attn_decode_scratch_bytes(B, Tq, H, Hkv, Tmax, window))
+
+
+def k_attn_decode(q, k_cache, v_cache, cache_lens, o, lse, B, Tq, Tmax, H, Hkv, hd, window,
+                  score_bound, scratch, dtype, stream=None):
+    nb = scratch.numel() * scratch.element_size() if scratch is not None else 0
+    _check(lib().gpt_k_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens),
+                                   _ptr(o), _ptr(lse), B, Tq, Tmax, H, Hkv, hd, window,
+                                   score_bound, _ptr(scratch), nb, dtype, _stream(stream)))
 
 
 def k_embed_fwd(tokens, B, T, wte, V, D, x, dtype, stream=None):

@@ -712,6 +712,46 @@ int gpt_k_attn_bwd(const void* qkv, const void* o, const float* lse, const void*
   return GPT_OK;
 }
 
+size_t gpt_k_attn_decode_scratch_bytes(int32_t B, int32_t Tq, int32_t H, int32_t Hkv,
+                                       int32_t Tmax, int32_t window) {
+  if (B < 1 || Tq < 1 || H < 1 || Hkv < 1 || H % Hkv || Tmax < 1 || window < 0) return 0;
+  return gk::attn_decode_scratch_bytes(B, Tq, H, Hkv, Tmax, window);
+}
+
+int gpt_k_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* cache_lens, void* o, float* lse, int32_t B, int32_t Tq,
+                      int32_t Tmax, int32_t H, int32_t Hkv, int32_t hd, int32_t window,
+                      float score_bound, void* scratch, size_t scratch_bytes, int32_t dtype,
+                      hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype))) return st;
+  if (dtype != GPT_BF16 || hd != 128)
+    return fail(GPT_ERR_UNSUPPORTED_CONFIG, "decode attention covers bf16, head_dim 128");
+  if (B < 1 || Tq < 1 || Tmax < 1 || H < 1 || Hkv < 1 || H % Hkv)
+    return fail(GPT_ERR_INVALID_ARG, "bad sizes");
+  if ((int64_t)(H / Hkv) * Tq > 1024) return fail(GPT_ERR_INVALID_ARG, "H / Hkv * Tq > 1024");
+  if (((int64_t)Tmax + 64) * Hkv > (1ll << 24))
+    return fail(GPT_ERR_INVALID_ARG, "(Tmax + 64) * Hkv > 2^24");
+  if (B > 65535 || (int64_t)Hkv * ((H / Hkv * Tq + 15) / 16) > 65535)
+    return fail(GPT_ERR_INVALID_ARG, "B or Hkv * ceil(H / Hkv * Tq / 16) above 65535");
+  if (window < 0) return fail(GPT_ERR_INVALID_ARG, "window < 0");
+  if (!(score_bound >= 0.f) || !(score_bound < 64.f))
+    return fail(GPT_ERR_INVALID_ARG, "score_bound outside [0, 64)");
+  if (!cache_lens || ((uintptr_t)cache_lens & 3u))
+    return fail(GPT_ERR_INVALID_ARG, "cache_lens null or misaligned");
+  if ((st = check_ptrs({q, k_cache, v_cache, o, lse}))) return st;
+  const size_t need = gk::attn_decode_scratch_bytes(B, Tq, H, Hkv, Tmax, window);
+  if (need) {
+    if (!scratch) return fail(GPT_ERR_INVALID_ARG, "scratch is null");
+    if (!aligned16(scratch)) return fail(GPT_ERR_MISALIGNED, "scratch misaligned");
+    if (scratch_bytes < need)
+      return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "scratch needs %zu bytes", need);
+  }
+  KERNEL_TRY(gk::attn_decode(q, k_cache, v_cache, cache_lens, o, lse, B, Tq, Tmax, H, Hkv,
+                             window, score_bound, scratch, s));
+  return GPT_OK;
+}
+
 int gpt_k_ce(const float* z, const int32_t* tgt, int64_t rows, int32_t V, float* ell, float* lse,
              void* dz, float grad_scale, int32_t dtype, hipStream_t s) {
   int st;

@@ -95,6 +95,14 @@ hipError_t attn_fwd(const void* qkv, void* o, float* lse, int B, int T,
                     int H, int Hkv, int hd, int W, DType dt, hipStream_t s,
                     float score_bound = 0.f);
 size_t attn_bwd_scratch_bytes(int B, int T, int H, int hd);
+// KV-cache decode attention (bf16, hd 128): q [B, Tq, H, 128], caches [B,
+// Tmax, Hkv, 128], lens [B] (device, clamped to [0, Tmax]) -> o [B, Tq, H,
+// 128], lse [B, H, Tq].  Query t of sequence b at position lens[b] - Tq + t.
+// scratch: attn_decode_scratch_bytes (0: none needed).
+size_t attn_decode_scratch_bytes(int B, int Tq, int H, int Hkv, int Tmax, int W);
+hipError_t attn_decode(const void* q, const void* kc, const void* vc, const int32_t* lens,
+                       void* o, float* lse, int B, int Tq, int Tmax, int H, int Hkv, int W,
+                       float score_bound, void* scratch, hipStream_t s);
 // With nrq / nrk / ncs (1/rms of the rotated q, k heads and the rope table)
 // and attn_bwd_fuses_norm() true, the backward of RoPE-then-QK-norm is
 // applied too (dq, dk w.r.t. the raw q, k); otherwise they are ignored.

@@ -262,6 +262,37 @@ int gpt_k_attn_bwd(const void* qkv, const void* o, const float* lse,
                    int32_t T, int32_t H, int32_t Hkv, int32_t hd,
                    int32_t window, int32_t dtype, hipStream_t s);
 
+/* Attention of new tokens over a KV cache (generation: the nanochat
+ * walkthrough, section "6. inference engine", prefilled caches read by
+ * flash_attn_with_kvcache), bf16, head_dim 128.
+ *   q [B, Tq, H, 128]: the Tq newest tokens of each sequence.
+ *   k_cache, v_cache [B, Tmax, Hkv, 128]: sequence b holds positions
+ *     0 .. L_b - 1, the new tokens' own keys and values included at
+ *     L_b - Tq .. L_b - 1; rows at or past L_b are never read.
+ *   cache_lens [B] int32 on the device: L_b, clamped to [0, Tmax].
+ *   Query t of sequence b sits at position p = L_b - Tq + t and sees key j
+ *   iff 0 <= p - j <= window; query head h reads KV head h / (H / Hkv);
+ *   scale 1/sqrt(128).
+ *   o [B, Tq, H, 128] bf16, lse [B, H, Tq] fp32 (natural log; a query with
+ *   no visible key gets o = 0, lse = -inf).
+ *   score_bound: as for gpt_k_attn_fwd, [0, 64).
+ *   scratch: device, at least gpt_k_attn_decode_scratch_bytes(B, Tq, H, Hkv,
+ *   Tmax, window) bytes (per-chunk partial results; 0 means none is needed),
+ *   16-byte aligned.  Needs H % Hkv == 0, H / Hkv * Tq <= 1024, (Tmax + 64)
+ *   * Hkv <= 2^24, B <= 65535 and Hkv * ceil(H / Hkv * Tq / 16) <= 65535.
+ *   GPT_ERR_UNSUPPORTED_CONFIG for another dtype or head_dim, else
+ *   GPT_ERR_INVALID_ARG / GPT_ERR_MISALIGNED / GPT_ERR_WORKSPACE_TOO_SMALL.
+ *   Deterministic: fixed reduction order for given sizes. */
+size_t gpt_k_attn_decode_scratch_bytes(int32_t B, int32_t Tq, int32_t H,
+                                       int32_t Hkv, int32_t Tmax,
+                                       int32_t window);
+int gpt_k_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* cache_lens, void* o, float* lse,
+                      int32_t B, int32_t Tq, int32_t Tmax, int32_t H,
+                      int32_t Hkv, int32_t hd, int32_t window,
+                      float score_bound, void* scratch, size_t scratch_bytes,
+                      int32_t dtype, hipStream_t s);
+
 /* Token embedding (a1).  tokens [B, T+1] int32 (inputs are the first T of
  * each row), wte [V, D] dtype -> x [B*T, D] dtype: x[b*T + t] =
  * wte[tokens[b][t]] (bitwise copies of the rows). */

@@ -119,6 +119,23 @@ def test_entry_points_reject_bad_pointers_before_launch():
     assert L.gpt_k_attn_fwd(A, A, A, 1, 8, 2, 2, 128, 4, 1, -1.0, None) == -1
     assert L.gpt_k_attn_fwd(A, A, A, 1, 8, 2, 2, 128, 4, 1, float("nan"), None) == -1
     assert L.gpt_k_rmsnorm_fwd(A, C.c_void_p(0x1002), A, 4, 8, 1e-5, 1, None) == -4
+    # decode attention: q, kc, vc, lens, o, lse, B, Tq, Tmax, H, Hkv, hd, W, bound,
+    # scratch, scratch_bytes, dtype
+    dec = L.gpt_k_attn_decode
+    nb = L.gpt_k_attn_decode_scratch_bytes(4, 1, 6, 2, 4096, 4096)
+    assert nb > 0 and L.gpt_k_attn_decode_scratch_bytes(1, 1, 6, 4, 64, 64) == 0
+    assert dec(A, A, A, A, A, A, 4, 1, 4096, 6, 2, 128, 4096, 0.0, A, nb, 0, None) == -2
+    assert dec(A, A, A, A, A, A, 4, 1, 4096, 6, 2, 64, 4096, 0.0, A, nb, 1, None) == -2
+    assert dec(A, A, A, A, A, A, 4, 1, 4096, 6, 4, 128, 4096, 0.0, A, nb, 1, None) == -1
+    assert dec(A, A, A, A, A, A, 4, 100, 4096, 12, 1, 128, 4096, 0.0, A, nb, 1, None) == -1
+    assert dec(A, A, A, A, A, A, 4, 1, 1 << 22, 6, 6, 128, 4096, 0.0, A, nb, 1, None) == -1
+    assert dec(A, A, A, A, A, A, 4, 1, 4096, 6, 2, 128, -1, 0.0, A, nb, 1, None) == -1
+    assert dec(A, A, A, A, A, A, 4, 1, 4096, 6, 2, 128, 4096, 64.0, A, nb, 1, None) == -1
+    assert dec(A, A, A, None, A, A, 4, 1, 4096, 6, 2, 128, 4096, 0.0, A, nb, 1, None) == -1
+    assert dec(A, A, A, A, A, A, 4, 1, 4096, 6, 2, 128, 4096, 0.0, None, nb, 1, None) == -1
+    assert dec(A, A, A, A, A, A, 4, 1, 4096, 6, 2, 128, 4096, 0.0, A, nb - 1, 1, None) == -3
+    assert dec(A, A, A, A, C.c_void_p(0x1008), A, 4, 1, 4096, 6, 2, 128, 4096, 0.0, A, nb, 1,
+               None) == -4
 
 
 def test_status_strings():

@@ -167,3 +167,32 @@ def test_eval_bpb_full_set(name):
     say(name, "bpb gpu", got[2], "oracle", ref[2], "full set", full[2])
     assert abs(got[2] - ref[2]) < 1e-3
     assert got[1] == ref[1]
+
+
+def test_decode_attention_bench_workload():
+    """KV-cache decode attention at the benchmark's decode workload and launch
+    configuration (d12-GQA: 64 sequences x 4096 cached positions, one new
+    token, 6 heads on 2 KV heads, score bound on): the first four layers'
+    inputs ('SSSL': windows 1024 and 4096), every sequence and head against
+    the oracle."""
+    import math
+    import bench
+    from oracle.gpt import _Num
+    cfg = gi.preset("d12gqa")
+    B, T, H, Hkv = 64, cfg["seq_len"], cfg["n_head"], cfg["n_kv_head"]
+    layers = bench.decode_inputs_gpu(torch, B, T, H, Hkv, 4, seed=cfg["seed"])
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    for l, (q, k, v) in enumerate(layers):
+        W = bench.window_of(cfg, l)
+        say("decode layer", l, "window", W)
+        o = torch.empty(B, 1, H, 128, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(B, H, 1, dtype=torch.float32, device="cuda")
+        nb = G.k_attn_decode_scratch_bytes(B, 1, H, Hkv, T, W)
+        scr = torch.empty(max(16, nb), dtype=torch.uint8, device="cuda")
+        G.k_attn_decode(q, k, v, lens, o, lse, B, 1, T, H, Hkv, 128, W, 1.01 * math.sqrt(128),
+                        scr, G.BF16)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = O.decode_attention(to_np(q), to_np(k), to_np(v), np.full(B, T), W,
+                                            _Num("bf16emu"))
+        assert rel_err(to_np(o), o_ref) < TOL
+        assert rel_err(to_np(lse), lse_ref) < 1e-5

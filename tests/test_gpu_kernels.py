@@ -523,3 +523,91 @@ def test_cross_entropy(dt, V):
     assert rel_err(to_np(ell), ell_ref) < 1e-5
     assert rel_err(to_np(lse), lse_ref) < 1e-6
     assert rel_err(to_np(dz), num.rnd(dz_ref)) < (1e-2 if dt == G.BF16 else 1e-5)
+
+
+# ------------------------------------------------------ KV-cache decode
+# B, Tq, Tmax, H, Hkv, window, cache lengths
+DECODE_CASES = [
+    (3, 1, 300, 6, 6, 300, [300, 1, 157]),
+    (2, 4, 1000, 8, 2, 100, [1000, 517]),
+    (1, 1, 64, 2, 1, 64, [64]),
+    (4, 3, 2048, 12, 2, 1023, [2048, 2000, 5, 0]),
+    (2, 2, 700, 4, 4, 5000, [9000, -4]),
+    (5, 1, 4096, 6, 2, 4096, [4096, 4000, 3333, 64, 65]),
+    (2, 16, 513, 2, 1, 40, [513, 200]),
+]
+
+
+def decode_inputs(B, Tq, Tmax, H, Hkv, lens, seed=40, nan_tail=True):
+    """q and cached k unit-RMS per head (rows after QK-norm), v N(0, 1), all
+    bf16; cache rows at or past a sequence's length hold NaN, which must never
+    reach the output."""
+    num = _Num("bf16emu")
+    q = O.rmsnorm(rnd_in((B, Tq, H, 128), seed), 1e-5, num)[0]
+    kc = O.rmsnorm(rnd_in((B, Tmax, Hkv, 128), seed + 1), 1e-5, num)[0]
+    vc = rnd_in((B, Tmax, Hkv, 128), seed + 2)
+    if nan_tail:
+        for b, L in enumerate(lens):
+            L = min(max(L, 0), Tmax)
+            kc[b, L:] = np.nan
+            vc[b, L:] = np.nan
+    return q, kc, vc
+
+
+def run_decode(q, kc, vc, lens, W, bounded):
+    B, Tq, H, _ = q.shape
+    Tmax, Hkv = kc.shape[1], kc.shape[2]
+    tq, tk, tv = (dev(a, torch.bfloat16) for a in (q, kc, vc))
+    tlen = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    to = torch.empty(B, Tq, H, 128, dtype=torch.bfloat16, device=DEV)
+    tl = torch.empty(B, H, Tq, dtype=torch.float32, device=DEV)
+    nb = G.k_attn_decode_scratch_bytes(B, Tq, H, Hkv, Tmax, W)
+    scr = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
+    G.k_attn_decode(tq, tk, tv, tlen, to, tl, B, Tq, Tmax, H, Hkv, 128, W,
+                    1.01 * math.sqrt(128) if bounded else 0.0, scr, G.BF16)
+    torch.cuda.synchronize()
+    return to_np(to), to_np(tl), nb
+
+
+@pytest.mark.parametrize("bounded", [False, True])
+@pytest.mark.parametrize("case", DECODE_CASES)
+def test_attention_decode(case, bounded):
+    """Decode attention of the newest Tq tokens over per-sequence cache
+    lengths (ragged, empty, shorter than Tq, clamped) against the oracle;
+    split-key chunks and their merge included (scratch > 0)."""
+    B, Tq, Tmax, H, Hkv, W, lens = case
+    say("decode", case, "bounded" if bounded else "")
+    q, kc, vc = decode_inputs(B, Tq, Tmax, H, Hkv, lens)
+    o_ref, lse_ref = O.decode_attention(q, kc, vc, np.array(lens), W, _Num("bf16emu"))
+    o, lse, nb = run_decode(q, kc, vc, lens, W, bounded)
+    say("  scratch bytes", nb)
+    assert np.isfinite(o).all()
+    assert rel_err(o, o_ref) < 2e-2
+    dead = np.isneginf(lse_ref)
+    np.testing.assert_array_equal(np.isneginf(lse), dead)
+    assert np.all(o.transpose(0, 2, 1, 3)[dead] == 0.0)
+    if (~dead).any():
+        assert rel_err(lse[~dead], lse_ref[~dead]) < 1e-5
+
+
+def test_attention_decode_one_hot_values_and_determinism():
+    """v_j = e_(j mod 128) turns each output row into sums of probabilities
+    over keys j = c (mod 128): with a window below 128 every visible key has
+    its own column, so the zero pattern of the output must equal the window
+    predicate exactly.  Two calls give identical bits."""
+    B, Tq, Tmax, H, Hkv, W = 2, 3, 900, 4, 2, 100
+    lens = [900, 333]
+    q, kc, _ = decode_inputs(B, Tq, Tmax, H, Hkv, lens, seed=50, nan_tail=False)
+    vc = np.zeros((B, Tmax, Hkv, 128), np.float32)
+    vc[:, np.arange(Tmax), :, np.arange(Tmax) % 128] = 1.0
+    o, lse, _ = run_decode(q, kc, vc, lens, W, False)
+    for b, L in enumerate(lens):
+        for t in range(Tq):
+            p = L - Tq + t
+            vis = np.zeros(128, bool)
+            for j in range(max(0, p - W), p + 1):
+                vis[j % 128] = True
+            for h in range(H):
+                assert np.array_equal(o[b, t, h] > 0, vis), (b, t, h)
+    o2, lse2, _ = run_decode(q, kc, vc, lens, W, False)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
