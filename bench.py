@@ -308,7 +308,7 @@ def bench_decode(a, torch, G):
              torch.empty(B, H, 1, dtype=torch.float32, device="cuda")) for _ in range(n_layer)]
     nbs = [G.k_attn_decode_scratch_bytes(B, 1, H, Hkv, T, window_of(cfg, l))
            for l in range(n_layer)]
-    scr = torch.empty(max(16, max(nbs)), dtype=torch.uint8, device="cuda")
+    scr = torch.zeros(max(16, max(nbs)), dtype=torch.uint8, device="cuda")
     bound = 1.01 * math.sqrt(128)
 
     def step():

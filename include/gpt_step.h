@@ -277,8 +277,11 @@ int gpt_k_attn_bwd(const void* qkv, const void* o, const float* lse,
  *   no visible key gets o = 0, lse = -inf).
  *   score_bound: as for gpt_k_attn_fwd, [0, 64).
  *   scratch: device, at least gpt_k_attn_decode_scratch_bytes(B, Tq, H, Hkv,
- *   Tmax, window) bytes (per-chunk partial results; 0 means none is needed),
- *   16-byte aligned.  Needs H % Hkv == 0, H / Hkv * Tq <= 1024, (Tmax + 64)
+ *   Tmax, window) bytes (0 means none is needed), 16-byte aligned: arrival
+ *   counters, then per-chunk partial results.  Zero-fill it once before its
+ *   first use; every call leaves the counters at zero again, so the same
+ *   buffer serves later calls without clearing.  Calls sharing a scratch
+ *   buffer must not run concurrently.  Needs H % Hkv == 0, H / Hkv * Tq <= 1024, (Tmax + 64)
  *   * Hkv <= 2^24, B <= 65535 and Hkv * ceil(H / Hkv * Tq / 16) <= 65535.
  *   GPT_ERR_UNSUPPORTED_CONFIG for another dtype or head_dim, else
  *   GPT_ERR_INVALID_ARG / GPT_ERR_MISALIGNED / GPT_ERR_WORKSPACE_TOO_SMALL.

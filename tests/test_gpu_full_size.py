@@ -188,7 +188,7 @@ def test_decode_attention_bench_workload():
         o = torch.empty(B, 1, H, 128, dtype=torch.bfloat16, device="cuda")
         lse = torch.empty(B, H, 1, dtype=torch.float32, device="cuda")
         nb = G.k_attn_decode_scratch_bytes(B, 1, H, Hkv, T, W)
-        scr = torch.empty(max(16, nb), dtype=torch.uint8, device="cuda")
+        scr = torch.zeros(max(16, nb), dtype=torch.uint8, device="cuda")
         G.k_attn_decode(q, k, v, lens, o, lse, B, 1, T, H, Hkv, 128, W, 1.01 * math.sqrt(128),
                         scr, G.BF16)
         torch.cuda.synchronize()

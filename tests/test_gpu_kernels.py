@@ -554,7 +554,7 @@ def decode_inputs(B, Tq, Tmax, H, Hkv, lens, seed=40, nan_tail=True):
     return q, kc, vc
 
 
-def run_decode(q, kc, vc, lens, W, bounded):
+def run_decode(q, kc, vc, lens, W, bounded, scr=None):
     B, Tq, H, _ = q.shape
     Tmax, Hkv = kc.shape[1], kc.shape[2]
     tq, tk, tv = (dev(a, torch.bfloat16) for a in (q, kc, vc))
@@ -562,7 +562,9 @@ def run_decode(q, kc, vc, lens, W, bounded):
     to = torch.empty(B, Tq, H, 128, dtype=torch.bfloat16, device=DEV)
     tl = torch.empty(B, H, Tq, dtype=torch.float32, device=DEV)
     nb = G.k_attn_decode_scratch_bytes(B, Tq, H, Hkv, Tmax, W)
-    scr = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
+    if scr is None:
+        scr = torch.zeros(max(nb, 16), dtype=torch.uint8, device=DEV)
+    assert scr.numel() >= nb
     G.k_attn_decode(tq, tk, tv, tlen, to, tl, B, Tq, Tmax, H, Hkv, 128, W,
                     1.01 * math.sqrt(128) if bounded else 0.0, scr, G.BF16)
     torch.cuda.synchronize()
@@ -611,3 +613,18 @@ def test_attention_decode_one_hot_values_and_determinism():
                 assert np.array_equal(o[b, t, h] > 0, vis), (b, t, h)
     o2, lse2, _ = run_decode(q, kc, vc, lens, W, False)
     assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+def test_attention_decode_scratch_reuse():
+    """One zero-filled scratch buffer serves consecutive calls of different
+    shapes and chunk counts (each call leaves its arrival counters at zero):
+    every call equals the same call on a fresh buffer."""
+    cases = [DECODE_CASES[5], DECODE_CASES[1], DECODE_CASES[0], DECODE_CASES[5],
+             DECODE_CASES[3]]
+    shared = torch.zeros(1 << 24, dtype=torch.uint8, device=DEV)
+    for B, Tq, Tmax, H, Hkv, W, lens in cases:
+        say("decode reuse", B, Tq, Tmax, H, Hkv, W)
+        q, kc, vc = decode_inputs(B, Tq, Tmax, H, Hkv, lens, seed=60)
+        fresh = run_decode(q, kc, vc, lens, W, True)
+        again = run_decode(q, kc, vc, lens, W, True, scr=shared)
+        assert np.array_equal(fresh[0], again[0]) and np.array_equal(fresh[1], again[1])
