@@ -16,9 +16,10 @@
 // from memory into the registers that feed the score product, the value rows
 // into the wave's LDS slot (buffer loads to LDS) for the transposing reads of
 // the P V product.  The 8 states are merged through LDS; with several chunks
-// each workgroup leaves its partial (max, sum, O) in scratch and a second
-// kernel merges them in chunk order.  HBM-bound: the roofline is the cache
-// bytes read once.
+// each workgroup leaves its partial (max, sum, O) in scratch, and the last
+// one to finish for a (sequence, KV head, query group) -- an arrival counter
+// tells -- merges all of them in chunk order.  HBM-bound: the roofline is
+// the cache bytes read once.
 #include <math.h>
 
 #include "attn_tiles.h"
@@ -31,12 +32,7 @@ using namespace attn;
 namespace {
 
 constexpr int DW = 8;                     // waves per workgroup
-#ifndef GK_DECODE_BLOCKS
-#define GK_DECODE_BLOCKS 256
-#endif
-#ifndef GK_DECODE_LASTBLOCK
-#define GK_DECODE_LASTBLOCK 1
-#endif
+constexpr int kTargetBlocks = 256;        // about one workgroup per CU
 constexpr int QS = 16;                    // query slots per workgroup
 constexpr int PSTRIDE = 2 + HD;           // partial record: m, l, O[128]
 constexpr float kLog2eD = 1.4426950408889634f;
@@ -124,8 +120,9 @@ __device__ __forceinline__ void store_final(const Merged& r, bf16* orow, float* 
 
 }  // namespace
 
-// grid: (chunks, Hkv * qgroups, B); 512 threads.  part: per (sequence, KV
-// head, query group) and chunk, 16 records (with more than one chunk).
+// grid: (chunks, Hkv * qgroups, B); 512 threads.  With more than one chunk:
+// cnt, one arrival counter per (sequence, KV head, query group), zero on
+// entry and left zero; part, per such triple and chunk 16 records.
 __global__ __launch_bounds__(DW * 64, 1) void k_attn_decode(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ lens, bf16* __restrict__ o, float* __restrict__ lse,
@@ -291,7 +288,6 @@ __global__ __launch_bounds__(DW * 64, 1) void k_attn_decode(
   }
   const int64_t pair = ((int64_t)b * Hkv + kvh) * qgroups + qgrp;
   float* pbase = part + pair * nchunks * QS * PSTRIDE + tslot * PSTRIDE;
-#if GK_DECODE_LASTBLOCK
   // Publish this chunk's record with agent-scope stores, wait until they
   // have completed, then count the chunk; the last chunk to arrive merges
   // all records (agent-scope loads) and sets the counter back to zero.
@@ -300,7 +296,8 @@ __global__ __launch_bounds__(DW * 64, 1) void k_attn_decode(
     float* rec = pbase + (int64_t)chunk * QS * PSTRIDE;
     if (tpart == 0) coherent_store2(rec, r.M, r.L);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) coherent_store2(rec + 2 + 8 * tpart + 2 * e, r.acc[2 * e], r.acc[2 * e + 1]);
+    for (int e = 0; e < 4; ++e)
+      coherent_store2(rec + 2 + 8 * tpart + 2 * e, r.acc[2 * e], r.acc[2 * e + 1]);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -314,39 +311,6 @@ __global__ __launch_bounds__(DW * 64, 1) void k_attn_decode(
                 tpart, sl2);
   if (threadIdx.x == 0)
     __hip_atomic_store(cnt + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#else
-  if (!active) return;
-  float* rec = pbase + (int64_t)chunk * QS * PSTRIDE;
-  const Merged r = merge_records<false>(red + tslot * PSTRIDE, QS * PSTRIDE, DW, tpart, sl2);
-  if (tpart == 0) {
-    rec[0] = r.M;
-    rec[1] = r.L;
-  }
-  *(float4*)(rec + 2 + 8 * tpart) = make_float4(r.acc[0], r.acc[1], r.acc[2], r.acc[3]);
-  *(float4*)(rec + 6 + 8 * tpart) = make_float4(r.acc[4], r.acc[5], r.acc[6], r.acc[7]);
-#endif
-}
-
-// merge the chunks' partials of one (sequence, KV head, query group) in
-// chunk order: 16 threads per query slot
-__global__ __launch_bounds__(256) void k_attn_decode_merge(const float* __restrict__ part,
-                                                           bf16* __restrict__ o,
-                                                           float* __restrict__ lse, int Tq, int H,
-                                                           int Hkv, int nchunks) {
-  const int qgroups = (int)gridDim.y / Hkv;
-  const int kvh = (int)blockIdx.y / qgroups, qgrp = (int)blockIdx.y % qgroups;
-  const int b = blockIdx.z;
-  const int G = H / Hkv, nq = G * Tq;
-  const int tslot = threadIdx.x >> 4, tpart = threadIdx.x & 15;
-  const int tsl = qgrp * QS + tslot;
-  if (tsl >= nq) return;
-  const float sl2 = kLog2eD / sqrtf((float)HD);
-  const int64_t pair = ((int64_t)b * Hkv + kvh) * qgroups + qgrp;
-  const float* base = part + pair * nchunks * QS * PSTRIDE + tslot * PSTRIDE;
-  const int thq = kvh * G + tsl / Tq, ttq = tsl % Tq;
-  store_final(merge_records<false>(base, QS * PSTRIDE, nchunks, tpart, sl2),
-              o + (((int64_t)b * Tq + ttq) * H + thq) * HD,
-              lse + ((int64_t)b * H + thq) * Tq + ttq, tpart, sl2);
 }
 
 namespace {
@@ -361,10 +325,9 @@ DecodePlan decode_plan(int B, int Tq, int H, int Hkv, int Tmax, int W) {
   d.kvrows = std::min<int64_t>(Tmax, (int64_t)W + Tq);
   // live tiles of a sequence, at most (the window's start need not be aligned)
   const int64_t tiles = std::min<int64_t>((Tmax + TR - 1) / TR, (d.kvrows + TR - 1) / TR + 1);
-  // about GK_DECODE_BLOCKS workgroups, each with at least 4 tiles
+  // about kTargetBlocks workgroups, each with at least 4 tiles
   d.pairs = (int64_t)B * Hkv * d.qgroups;
-  const int64_t nc =
-      std::min<int64_t>((GK_DECODE_BLOCKS + d.pairs - 1) / d.pairs, (tiles + 3) / 4);
+  const int64_t nc = std::min<int64_t>((kTargetBlocks + d.pairs - 1) / d.pairs, (tiles + 3) / 4);
   d.nchunks = (int)std::max<int64_t>(1, nc);
   return d;
 }
@@ -372,9 +335,7 @@ DecodePlan decode_plan(int B, int Tq, int H, int Hkv, int Tmax, int W) {
 
 // with several chunks: arrival counters (one int per (sequence, KV head,
 // query group), padded to 256 bytes), then the partial records
-size_t counter_bytes(const DecodePlan& d) {
-  return GK_DECODE_LASTBLOCK ? (d.pairs * 4 + 255) / 256 * 256 : 0;
-}
+size_t counter_bytes(const DecodePlan& d) { return (d.pairs * 4 + 255) / 256 * 256; }
 
 size_t attn_decode_scratch_bytes(int B, int Tq, int H, int Hkv, int Tmax, int W) {
   const DecodePlan d = decode_plan(B, Tq, H, Hkv, Tmax, W);
@@ -398,12 +359,6 @@ hipError_t attn_decode(const void* q, const void* kc, const void* vc, const int3
   GK_LAUNCH(Work(0.0, kvbytes + qo), k_attn_decode, grid, dim3(DW * 64), 0, s, (const bf16*)q,
             (const bf16*)kc, (const bf16*)vc, lens, (bf16*)o, lse, cnt, part, Tq, Tmax, H, Hkv,
             W, d.nchunks, score_bound > 0.f ? score_bound * kLog2eD : 0.f);
-  hipError_t e = hipGetLastError();
-  if (GK_DECODE_LASTBLOCK || e != hipSuccess || d.nchunks == 1) return e;
-  // partials of the valid query slots read once, outputs written once
-  const double pbytes = (double)B * H * Tq * d.nchunks * PSTRIDE * 4;
-  GK_LAUNCH(Work(0.0, pbytes + qo / 2), k_attn_decode_merge, dim3(1, Hkv * d.qgroups, B),
-            dim3(256), 0, s, (const float*)part, (bf16*)o, lse, Tq, H, Hkv, d.nchunks);
   return hipGetLastError();
 }
 
