@@ -516,3 +516,100 @@ def test_bf16emu_close_to_fp32():
     l16, g16, _ = O.step(cfg, w.astype(np.float32), tok, "bf16emu")
     assert abs(l32 - l16) < 1e-2
     assert np.abs(g32 - g16).max() / np.abs(g32).max() < 2e-2
+
+
+# ------------------------------------------------------- FP8 (tensor-wise)
+FP8 = ["e4m3", "e5m2"]
+_TORCH_F8 = {"e4m3": "float8_e4m3fn", "e5m2": "float8_e5m2"}
+
+
+@pytest.mark.parametrize("fmt", FP8)
+def test_fp8_decode_matches_torch_and_encode_inverts_it(fmt):
+    """All 256 codes: the field-definition decoder equals torch's view of the
+    same bytes as its float8 dtype; encoding every finite value gives its
+    code back."""
+    from oracle import fp8
+    codes = np.arange(256, dtype=np.uint8)
+    v = fp8.fp8_decode(codes, fmt)
+    ref = torch.from_numpy(codes.copy()).view(getattr(torch, _TORCH_F8[fmt])).double().numpy()
+    np.testing.assert_array_equal(np.isnan(v), np.isnan(ref))
+    fin = np.isfinite(ref)
+    np.testing.assert_array_equal(v[fin], ref[fin])
+    np.testing.assert_array_equal(np.signbit(v[fin]), np.signbit(ref[fin]))
+    np.testing.assert_array_equal(fp8.fp8_encode(v[fin], fmt), codes[fin])
+    assert np.nanmax(v[np.isfinite(v)]) == fp8.FORMATS[fmt][3]
+
+
+@pytest.mark.parametrize("fmt", FP8)
+def test_fp8_round_is_nearest_even_by_brute_force(fmt):
+    """Rounding equals a search over the sorted table of every finite value
+    (nearest; a tie goes to the even code), on random values, every
+    representable value and every midpoint; and equals torch's cast for the
+    same in-range values."""
+    from oracle import fp8
+    codes = np.arange(256, dtype=np.uint8)
+    vals = fp8.fp8_decode(codes, fmt)
+    ok = np.isfinite(vals) & ~((vals == 0) & np.signbit(vals))
+    table, tcodes = vals[ok], codes[ok]
+    order = np.argsort(table)
+    table, tcodes = table[order], tcodes[order]
+    fmax = fp8.FORMATS[fmt][3]
+    rng = np.random.default_rng(3)
+    y = np.concatenate([rng.uniform(-fmax, fmax, 4000),
+                        rng.standard_normal(4000) * np.exp2(rng.integers(-20, 8, 4000)),
+                        table, (table[1:] + table[:-1]) / 2])
+    y = y[np.abs(y) <= fmax].astype(np.float32).astype(np.float64)
+    got = fp8.fp8_round(y, fmt)
+    d = np.abs(y[:, None] - table[None, :])
+    best = d.min(1, keepdims=True)
+    cand = d == best
+    # among equally near values (a tie) take the even code
+    even = (tcodes[None, :] & 1) == 0
+    pick = np.where(cand.sum(1) > 1, np.argmax(cand & even, 1), np.argmax(cand, 1))
+    np.testing.assert_array_equal(np.abs(got), np.abs(table[pick]))
+    tt = torch.from_numpy(y).to(getattr(torch, _TORCH_F8[fmt])).double().numpy()
+    np.testing.assert_array_equal(np.abs(got), np.abs(tt))
+
+
+@pytest.mark.parametrize("fmt", FP8)
+def test_fp8_quantize_scale(fmt):
+    """The largest magnitude maps to +-fmax exactly; s = fmax / amax in fp32;
+    an all-zero tensor gives zeros and s = fmax / 1e-12."""
+    from oracle import fp8
+    x = np.random.default_rng(5).standard_normal((7, 33)).astype(np.float32)
+    x[3, 4] = -7.25
+    codes, v, s, inv = fp8.quantize(x, fmt)
+    fmax = fp8.FORMATS[fmt][3]
+    assert s == np.float32(np.float32(fmax) / np.float32(7.25))
+    assert v[3, 4] == -fmax and np.abs(v).max() == fmax
+    assert inv == np.float32(1) / s
+    np.testing.assert_array_equal(fp8.fp8_decode(codes, fmt), v)
+    z = fp8.quantize(np.zeros((2, 16), np.float32), fmt)
+    assert np.all(z[1] == 0) and z[2] == np.float32(np.float32(fmax) / np.float32(1e-12))
+    # amax values where fp32(amax * s) lands above fmax: the clamp keeps the
+    # largest element at fmax instead of overflowing the format
+    amax = {"e4m3": np.float32(12.5159), "e5m2": np.float32(27.432611)}[fmt]
+    s = np.float32(np.float32(fmax) / amax)
+    assert np.float32(amax * s) > fmax
+    _, v, _, _ = fp8.quantize(np.array([[amax, -amax / 3]], np.float32), fmt)
+    assert v[0, 0] == fmax
+
+
+def test_fp8_linear_exact_when_operands_are_representable():
+    """x = k / 4 with |k| <= 14 and amax 3.5: s = 128 (a power of two), so
+    every x s = 32 k is an e4m3 value and the FP8 product must equal the
+    plain product exactly (rounded to bf16); the weight likewise with a
+    different power of two.  A transposed operand or a wrong scale breaks
+    this."""
+    from oracle import fp8
+    rng = np.random.default_rng(9)
+    x = rng.integers(-14, 15, (37, 64)).astype(np.float32) / 4
+    x[0, 0] = 3.5
+    w = rng.integers(-12, 13, (21, 64)).astype(np.float32) / 32
+    w[5, 7] = -448.0 / 1024           # amax 0.4375: s = 1024
+    y = fp8.fp8_linear(x, w)
+    ref = O.round_bf16((x.astype(np.float64) @ w.astype(np.float64).T).astype(np.float32))
+    np.testing.assert_array_equal(y, ref)
+    _, qx, sx, ix = fp8.quantize(x, "e4m3")
+    assert sx == 128 and ix == np.float32(1 / 128)
+    np.testing.assert_array_equal(qx, x * 128)
