@@ -86,6 +86,11 @@ _SIGS = {
     "gpt_k_attn_decode_scratch_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "gpt_k_attn_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _f32, _vp, _sz, _i32, _vp]),
+    "gpt_k_fp8_cast_scratch_bytes": (_sz, []),
+    "gpt_k_fp8_cast": (C.c_int, [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "gpt_k_gemm_fp8_scratch_bytes": (_sz, [_i64, _i64, _i64]),
+    "gpt_k_gemm_fp8": (C.c_int, [_i64, _i64, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _vp, _vp,
+                                 _vp, _i64, _i32, _vp, _sz, _vp]),
     "gpt_k_ce": (C.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp]),
     "gpt_k_lm_ce_scratch_bytes": (_sz, [_i64, _i32]),
     "gpt_k_embed_fwd": (C.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp]),
@@ -251,6 +256,31 @@ def k_attn_decode(q, k_cache, v_cache, cache_lens, o, lse, B, Tq, Tmax, H, Hkv, 
     _check(lib().gpt_k_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens),
                                    _ptr(o), _ptr(lse), B, Tq, Tmax, H, Hkv, hd, window,
                                    score_bound, _ptr(scratch), nb, dtype, _stream(stream)))
+
+
+FP8_E4M3, FP8_E5M2 = 0, 1
+
+
+def k_fp8_cast_scratch_bytes():
+    return int(lib().gpt_k_fp8_cast_scratch_bytes())
+
+
+def k_fp8_cast(x, rows, cols, dtype, fmt, q, q_t, scales, scratch, stream=None):
+    nb = scratch.numel() * scratch.element_size()
+    _check(lib().gpt_k_fp8_cast(_ptr(x), rows, cols, dtype, fmt, _ptr(q), _ptr(q_t),
+                                _ptr(scales), _ptr(scratch), nb, _stream(stream)))
+
+
+def k_gemm_fp8_scratch_bytes(M, N, K):
+    return int(lib().gpt_k_gemm_fp8_scratch_bytes(M, N, K))
+
+
+def k_gemm_fp8(M, N, K, A, lda, fmt_a, B, ldb, fmt_b, a_inv, b_inv, C, ldc, epilogue,
+               scratch=None, stream=None):
+    nb = scratch.numel() * scratch.element_size() if scratch is not None else 0
+    _check(lib().gpt_k_gemm_fp8(M, N, K, _ptr(A), lda, fmt_a, _ptr(B), ldb, fmt_b, _ptr(a_inv),
+                                _ptr(b_inv), _ptr(C), ldc, epilogue, _ptr(scratch), nb,
+                                _stream(stream)))
 
 
 def k_embed_fwd(tokens, B, T, wte, V, D, x, dtype, stream=None):

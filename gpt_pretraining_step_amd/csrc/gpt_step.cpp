@@ -642,6 +642,55 @@ int gpt_k_gemm(int32_t op, int64_t M, int64_t N, int64_t K, const void* A, int64
   return GPT_OK;
 }
 
+size_t gpt_k_fp8_cast_scratch_bytes(void) { return gk::fp8_cast_scratch_bytes(); }
+
+int gpt_k_fp8_cast(const void* x, int64_t rows, int64_t cols, int32_t dtype, int32_t fp8_format,
+                   void* q, void* q_t, float* scales, void* scratch, size_t scratch_bytes,
+                   hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({x, scales, scratch}))) return st;
+  if (fp8_format != GPT_FP8_E4M3 && fp8_format != GPT_FP8_E5M2)
+    return fail(GPT_ERR_INVALID_ARG, "unknown fp8 format");
+  if (!q && !q_t) return fail(GPT_ERR_INVALID_ARG, "no output requested");
+  if ((q && !aligned16(q)) || (q_t && !aligned16(q_t)))
+    return fail(GPT_ERR_MISALIGNED, "an output is not 16-byte aligned");
+  if (rows < 1 || cols < 16 || cols % 16 || (q_t && rows % 16))
+    return fail(GPT_ERR_INVALID_ARG, "bad sizes (cols, and rows for q_t, multiples of 16)");
+  if (cols > 65535ll * 64 || rows > (1ll << 31) * 64)
+    return fail(GPT_ERR_INVALID_ARG, "tensor too large (cols <= 65535 * 64)");
+  if (scratch_bytes < gk::fp8_cast_scratch_bytes())
+    return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "scratch needs %zu bytes", gk::fp8_cast_scratch_bytes());
+  KERNEL_TRY(gk::fp8_cast(x, rows, cols, (gk::DType)dtype, fp8_format, q, q_t, scales, scratch, s));
+  return GPT_OK;
+}
+
+size_t gpt_k_gemm_fp8_scratch_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 128 || K % 128) return 0;
+  return gk::gemm_fp8_scratch_bytes(M, N, K);
+}
+
+int gpt_k_gemm_fp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int32_t fmt_a,
+                   const void* B, int64_t ldb, int32_t fmt_b, const float* a_inv_scale,
+                   const float* b_inv_scale, void* C, int64_t ldc, int32_t epilogue,
+                   void* scratch, size_t scratch_bytes, hipStream_t s) {
+  int st;
+  if ((st = check_ptrs({A, B, C}))) return st;
+  if (!a_inv_scale || !b_inv_scale) return fail(GPT_ERR_INVALID_ARG, "a scale pointer is null");
+  if ((fmt_a != GPT_FP8_E4M3 && fmt_a != GPT_FP8_E5M2) ||
+      (fmt_b != GPT_FP8_E4M3 && fmt_b != GPT_FP8_E5M2))
+    return fail(GPT_ERR_INVALID_ARG, "unknown fp8 format");
+  if (epilogue != GPT_EPI_STORE && epilogue != GPT_EPI_F32 && epilogue != GPT_EPI_F32_ACC)
+    return fail(GPT_ERR_INVALID_ARG, "epilogue must be STORE, F32 or F32_ACC");
+  if (!gk::gemm_fp8_ok(M, N, K, lda, ldb, ldc))
+    return fail(GPT_ERR_INVALID_ARG,
+                "bad sizes (K a multiple of 128, lda/ldb multiples of 16 and >= K, N and ldc "
+                "multiples of 4, operands under 4 GiB)");
+  if (scratch && !aligned16(scratch)) return fail(GPT_ERR_MISALIGNED, "scratch misaligned");
+  KERNEL_TRY(gk::gemm_fp8(M, N, K, A, lda, fmt_a, B, ldb, fmt_b, a_inv_scale, b_inv_scale, C, ldc,
+                          epilogue, scratch, scratch ? scratch_bytes : 0, s));
+  return GPT_OK;
+}
+
 int gpt_k_rope_table(float* cs, int32_t T, int32_t hd, float base, hipStream_t s) {
   int st;
   if ((st = check_ptrs({cs}))) return st;

@@ -584,6 +584,75 @@ __device__ __forceinline__ bf16x8_t frag(const bf16* st, int base, int kk, int l
   }
 }
 
+// Epilogue of one wave's TMI x TNJ accumulator fragments: lane (g, lr)
+// holds rows r0 + 16 i + lr, columns c0 + 16 j + 4 g .. + 3.  With P (split
+// K) the fp32 partial tile goes there; otherwise EPI applies.
+template <int EPI, int TMI, int TNJ>
+__device__ __forceinline__ void store_tiles(const f32x4_t (&acc)[TMI][TNJ], int64_t M, int64_t N,
+                                            int64_t r0, int64_t c0, int lane, void* C,
+                                            int64_t ldc, void* aux, float* P) {
+  const int cq = (lane >> 4) * 4, lr = lane & 15;
+  if (P) {
+#pragma unroll
+    for (int i = 0; i < TMI; ++i) {
+      const int64_t m = r0 + 16 * i + lr;
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j) {
+        const int64_t n = c0 + 16 * j + cq;
+        if (m < M && n < N) *(f32x4_t*)(P + m * N + n) = acc[i][j];
+      }
+    }
+    return;
+  }
+  // per pair of 16-row groups (one group for fp32 inputs): every load of
+  // the groups first, then the stores (one memory latency per batch instead
+  // of one per fragment; the MFMA operand registers are free by now)
+  constexpr int GB = (EPI == E_F32_ACC || TMI % 2) ? 1 : 2;
+  if constexpr (EPI == E_F32_ACC) {
+    // read-add-write one fragment at a time (hoisting these loads above the
+    // main loop costs the accumulators their registers)
+#pragma unroll
+    for (int i = 0; i < TMI; ++i) {
+      const int64_t m = r0 + 16 * i + lr;
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j) {
+        const int64_t n = c0 + 16 * j + cq;
+        if (m < M && n < N) {
+          f32x4_t* p = (f32x4_t*)((float*)C + m * ldc + n);
+          f32x4_t v = __builtin_nontemporal_load(p);
+          asm volatile("" : "+v"(v));
+          *p = v + acc[i][j];
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i0 = 0; i0 < TMI; i0 += GB) {
+    typename EpiIn<EPI>::type in[GB][TNJ];
+    if constexpr (epi_reads<EPI>()) {
+#pragma unroll
+      for (int gi = 0; gi < GB; ++gi) {
+        const int64_t m = r0 + 16 * (i0 + gi) + lr;
+#pragma unroll
+        for (int j = 0; j < TNJ; ++j) {
+          const int64_t n = c0 + 16 * j + cq;
+          if (m < M && n < N) in[gi][j] = epi_load<EPI>(C, aux, m * ldc + n);
+        }
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < GB; ++gi) {
+      const int64_t m = r0 + 16 * (i0 + gi) + lr;
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j) {
+        const int64_t n = c0 + 16 * j + cq;
+        if (m < M && n < N) epi4_in<EPI>(C, aux, m * ldc + n, acc[i0 + gi][j], in[gi][j]);
+      }
+    }
+  }
+}
+
 template <int BM, int BN, bool TA, bool TB, int EPI>
 __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64_t K,
                                                      const bf16* __restrict__ A, int64_t lda,
@@ -860,47 +929,128 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
     }
     return;
   }
-  if (partial) {
-    float* P = partial + (int64_t)split * M * N;
+  store_tiles<EPI>(acc, M, N, m0 + wm, n0 + wn, lane, C, ldc, aux,
+                   partial ? partial + (int64_t)split * M * N : nullptr);
+}
+
+// --------------------------------------------------------------- FP8
+// C = (A B^T) * a_inv[0] * b_inv[0] for 8-bit float operands, both K-
+// contiguous (A [M, K], B [N, K]; the transposed products of a layer's
+// backward take transposed copies, which the cast kernel writes).  Same
+// structure as k_gemm_dma: 256 x BN tiles, buffer loads straight into LDS,
+// two stages.  A stage holds 128 k per row -- 128 bytes, the bf16 stages'
+// row length -- so the bf16 operand plans and fragment reads serve
+// unchanged, with the byte matrices viewed as 2-byte units.  Each stage is
+// one v_mfma_f32_16x16x128_f8f6f4 per fragment pair: a lane brings 32 bytes
+// of its row (the 16-byte chunks g and g + 4, the same k positions for
+// both operands, so their products pair up whatever order the instruction
+// sums them in).  FA / FB: 0 = e4m3, 1 = e5m2.  Twice the bf16 rate per
+// instruction and half the bytes per k.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+template <int R>
+__device__ __forceinline__ i32x8_t frag_f8(const bf16* st, int base, int lane) {
+  const bf16x8_t lo = frag<R, false>(st, base, 0, lane);
+  const bf16x8_t hi = frag<R, false>(st, base, 32, lane);
+  typedef short v8s_t __attribute__((ext_vector_type(8)));
+  typedef short v16s_t __attribute__((ext_vector_type(16)));
+  const v16s_t v = __builtin_shufflevector(__builtin_bit_cast(v8s_t, lo),
+                                           __builtin_bit_cast(v8s_t, hi), 0, 1, 2, 3, 4, 5, 6,
+                                           7, 8, 9, 10, 11, 12, 13, 14, 15);
+  return __builtin_bit_cast(i32x8_t, v);
+}
+
+template <int BN, int FA, int FB, int EPI>
+__global__ __launch_bounds__(512, 1) void k_gemm_fp8(int64_t M, int64_t N, int64_t Ku,
+                                                     const bf16* __restrict__ A, int64_t ldau,
+                                                     const bf16* __restrict__ B, int64_t ldbu,
+                                                     const float* __restrict__ a_inv,
+                                                     const float* __restrict__ b_inv, void* C,
+                                                     int64_t ldc, TileMap tm, float* partial) {
+  // Ku, ldau, ldbu, tm.k_per_split: in 2-byte units (2 fp8 values each)
+  constexpr int BM = 256;
+  constexpr int WM = BM / 4, WN = BN / 2;
+  constexpr int TMI = WM / 16, TNJ = WN / 16;
+  __shared__ __attribute__((aligned(1024))) bf16 st0[(BM + BN) * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 st1[(BM + BN) * 64];
+
+  const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
+  const int per_xcd = (nb + 7) / 8;
+  const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (logical >= nb) return;
+  const int ntile = tm.tiles_m * tm.tiles_n;
+  const int split = logical / ntile;
+  const int t = logical % ntile;
+  constexpr int GM = 8;
+  const int group = t / (GM * tm.tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tm.tiles_m - first_m, GM);
+  const int tile_m = first_m + (t % (GM * tm.tiles_n)) % gsize;
+  const int tile_n = (t % (GM * tm.tiles_n)) / gsize;
+  const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
+  const int64_t kbeg = (int64_t)split * tm.k_per_split;
+  const int64_t kend = min(Ku, kbeg + tm.k_per_split);
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
+
+  DmaPlan<BM, false> pa;
+  DmaPlan<BN, false> pb;
+  pa.init(A, ldau, m0, M, Ku, wave, lane);
+  pb.init(B, ldbu, n0, N, Ku, wave, lane);
+
+  f32x4_t acc[TMI][TNJ];
 #pragma unroll
-    for (int i = 0; i < TMI; ++i) {
-      const int64_t m = m0 + wm + 16 * i + lr;
+  for (int i = 0; i < TMI; ++i)
 #pragma unroll
-      for (int j = 0; j < TNJ; ++j) {
-        const int64_t n = n0 + wn + 16 * j + cq;
-        if (m < M && n < N) *(f32x4_t*)(P + m * N + n) = acc[i][j];
-      }
+    for (int j = 0; j < TNJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const bf16* st) {
+    const bf16* As = st;
+    const bf16* Bs = st + BM * 64;
+    i32x8_t a[TMI], b[TNJ];
+#pragma unroll
+    for (int j = 0; j < TNJ; ++j) b[j] = frag_f8<BN>(Bs, wn + 16 * j, lane);
+#pragma unroll
+    for (int i = 0; i < TMI; ++i) a[i] = frag_f8<BM>(As, wm + 16 * i, lane);
+#pragma unroll
+    for (int i = 0; i < TMI; ++i)
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b[j], a[i], acc[i][j], FB, FA,
+                                                                     0, 0, 0, 0);
+  };
+
+  const int nsl = (int)((kend - kbeg) / BK);
+  pa.issue(kbeg, st0, wave);
+  pb.issue(kbeg, st0 + BM * 64, wave);
+  int it = 0;
+  for (; it + 2 <= nsl; it += 2) {
+    dma_wait();
+    __syncthreads();
+    pa.issue(kbeg + (int64_t)(it + 1) * BK, st1, wave);
+    pb.issue(kbeg + (int64_t)(it + 1) * BK, st1 + BM * 64, wave);
+    compute(st0);
+    dma_wait();
+    __syncthreads();
+    if (it + 2 < nsl) {
+      pa.issue(kbeg + (int64_t)(it + 2) * BK, st0, wave);
+      pb.issue(kbeg + (int64_t)(it + 2) * BK, st0 + BM * 64, wave);
     }
-    return;
+    compute(st1);
   }
-  // per pair of 16-row groups (one group for fp32 inputs): every load of
-  // the groups first, then the stores (one memory latency per batch instead
-  // of one per fragment; the MFMA operand registers are free by now)
-  constexpr int GB = (EPI == E_F32_ACC || TMI % 2) ? 1 : 2;
-#pragma unroll
-  for (int i0 = 0; i0 < TMI; i0 += GB) {
-    typename EpiIn<EPI>::type in[GB][TNJ];
-    if constexpr (epi_reads<EPI>()) {
-#pragma unroll
-      for (int gi = 0; gi < GB; ++gi) {
-        const int64_t m = m0 + wm + 16 * (i0 + gi) + lr;
-#pragma unroll
-        for (int j = 0; j < TNJ; ++j) {
-          const int64_t n = n0 + wn + 16 * j + cq;
-          if (m < M && n < N) in[gi][j] = epi_load<EPI>(C, aux, m * ldc + n);
-        }
-      }
-    }
-#pragma unroll
-    for (int gi = 0; gi < GB; ++gi) {
-      const int64_t m = m0 + wm + 16 * (i0 + gi) + lr;
-#pragma unroll
-      for (int j = 0; j < TNJ; ++j) {
-        const int64_t n = n0 + wn + 16 * j + cq;
-        if (m < M && n < N) epi4_in<EPI>(C, aux, m * ldc + n, acc[i0 + gi][j], in[gi][j]);
-      }
-    }
+  if (it < nsl) {
+    dma_wait();
+    __syncthreads();
+    compute(st0);
   }
+  const float sc = a_inv[0] * b_inv[0];
+#pragma unroll
+  for (int i = 0; i < TMI; ++i)
+#pragma unroll
+    for (int j = 0; j < TNJ; ++j) acc[i][j] *= sc;
+  store_tiles<EPI>(acc, M, N, m0 + wm, n0 + wn, lane, C, ldc, nullptr,
+                   partial ? partial + (int64_t)split * M * N : nullptr);
 }
 
 // out[m, n] (=/+=) sum_s partial[s, m, n], fixed order over s
@@ -1237,6 +1387,84 @@ hipError_t mfma_gemm(const GemmDesc& g, hipStream_t s) {
   const Work rw(0.0, 4.0 * MN * (tm.splits + 1 + (g.epi == E_F32_ACC ? 1 : 0)));
   GK_LAUNCH(rw, k_splitk_reduce, dim3((unsigned)cdiv(MN / 4, 256)), dim3(256), 0, s, partial,
             tm.splits, g.M, g.N, (float*)g.C, g.ldc, g.epi == E_F32_ACC ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace gk
+
+namespace gk {
+
+template <int BN, int FA, int FB, int EPI>
+static void launch_fp8_t(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                         const void* B, int64_t ldb, const float* ai, const float* bi, void* C,
+                         int64_t ldc, const TileMap& tm, float* partial, hipStream_t s) {
+  const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
+  const int grid = ((nb + 7) / 8) * 8;
+  const double mn = (double)M * N;
+  const Work w(2.0 * mn * K, (double)M * K + (double)N * K +
+                                 mn * (EPI == E_STORE ? 2 : EPI == E_F32 ? 4 : 8));
+  GK_LAUNCH(w, (k_gemm_fp8<BN, FA, FB, EPI>), dim3(grid), dim3(512), 0, s, M, N, K / 2,
+            (const bf16*)A, lda / 2, (const bf16*)B, ldb / 2, ai, bi, C, ldc, tm, partial);
+}
+
+template <int BN, int FA, int FB>
+static void launch_fp8_e(int epi, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                         const void* B, int64_t ldb, const float* ai, const float* bi, void* C,
+                         int64_t ldc, const TileMap& tm, float* partial, hipStream_t s) {
+  if (partial || epi == E_F32)
+    launch_fp8_t<BN, FA, FB, E_F32>(M, N, K, A, lda, B, ldb, ai, bi, C, ldc, tm, partial, s);
+  else if (epi == E_F32_ACC)
+    launch_fp8_t<BN, FA, FB, E_F32_ACC>(M, N, K, A, lda, B, ldb, ai, bi, C, ldc, tm, partial, s);
+  else
+    launch_fp8_t<BN, FA, FB, E_STORE>(M, N, K, A, lda, B, ldb, ai, bi, C, ldc, tm, partial, s);
+}
+
+template <int BN>
+static void launch_fp8_f(int fa, int fb, int epi, int64_t M, int64_t N, int64_t K,
+                         const void* A, int64_t lda, const void* B, int64_t ldb, const float* ai,
+                         const float* bi, void* C, int64_t ldc, const TileMap& tm, float* partial,
+                         hipStream_t s) {
+  if (fa == 0 && fb == 0)
+    launch_fp8_e<BN, 0, 0>(epi, M, N, K, A, lda, B, ldb, ai, bi, C, ldc, tm, partial, s);
+  else if (fa == 1 && fb == 0)
+    launch_fp8_e<BN, 1, 0>(epi, M, N, K, A, lda, B, ldb, ai, bi, C, ldc, tm, partial, s);
+  else if (fa == 0 && fb == 1)
+    launch_fp8_e<BN, 0, 1>(epi, M, N, K, A, lda, B, ldb, ai, bi, C, ldc, tm, partial, s);
+  else
+    launch_fp8_e<BN, 1, 1>(epi, M, N, K, A, lda, B, ldb, ai, bi, C, ldc, tm, partial, s);
+}
+
+bool gemm_fp8_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc) {
+  return M >= 1 && N >= 1 && K >= 128 && K % 128 == 0 && lda >= K && ldb >= K && lda % 16 == 0 &&
+         ldb % 16 == 0 && ldc >= N && ldc % 4 == 0 && N % 4 == 0 &&
+         (double)M * lda < 4294967295.0 && (double)N * ldb < 4294967295.0;
+}
+
+size_t gemm_fp8_scratch_bytes(int64_t M, int64_t N, int64_t K) {
+  int bn;
+  const TileMap tm = plan_dma(M, N, K / 2, true, SIZE_MAX, &bn);
+  return tm.splits > 1 ? (size_t)tm.splits * M * N * sizeof(float) : 0;
+}
+
+hipError_t gemm_fp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int fa,
+                    const void* B, int64_t ldb, int fb, const float* a_inv, const float* b_inv,
+                    void* C, int64_t ldc, int epi, void* scratch, size_t scratch_bytes,
+                    hipStream_t s) {
+  if (!gemm_fp8_ok(M, N, K, lda, ldb, ldc)) return hipErrorInvalidValue;
+  const bool f32out = epi == E_F32 || epi == E_F32_ACC;
+  int bn;
+  const TileMap tm = plan_dma(M, N, K / 2, f32out, scratch ? scratch_bytes : 0, &bn);
+  float* partial = tm.splits > 1 ? (float*)scratch : nullptr;
+  if (bn == 192)
+    launch_fp8_f<192>(fa, fb, epi, M, N, K, A, lda, B, ldb, a_inv, b_inv, C, ldc, tm, partial, s);
+  else
+    launch_fp8_f<256>(fa, fb, epi, M, N, K, A, lda, B, ldb, a_inv, b_inv, C, ldc, tm, partial, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !partial) return e;
+  const int64_t MN = M * N;
+  const Work rw(0.0, 4.0 * MN * (tm.splits + 1 + (epi == E_F32_ACC ? 1 : 0)));
+  GK_LAUNCH(rw, k_splitk_reduce, dim3((unsigned)cdiv(MN / 4, 256)), dim3(256), 0, s, partial,
+            tm.splits, M, N, (float*)C, ldc, epi == E_F32_ACC ? 1 : 0);
   return hipGetLastError();
 }
 

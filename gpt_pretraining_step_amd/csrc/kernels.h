@@ -157,6 +157,23 @@ hipError_t lm_ce_gemm(const void* hf, int64_t rows, int D, const void* wlm, int 
 hipError_t ce_fix(const float* stats, const float* zt, int64_t rows, int V, const int32_t* tok,
                   int tgt_T, int tgt_direct, float* ell, float* lse, void* dz, float grad_scale,
                   hipStream_t s);
+// FP8 linear layers with tensor-wise scaling.  fp8_cast: q = fp8(clamp(x s,
+// +-fmax)), s = fmax / max(max|x|, 1e-12), x [rows, cols] (cols % 16 == 0;
+// rows % 16 == 0 when qt is given), row-major into q and/or transposed into
+// qt ([cols, rows]); scales[0] = s, scales[1] = 1/s.  fmt 0: e4m3, 1: e5m2.
+// scratch: fp8_cast_scratch_bytes.
+size_t fp8_cast_scratch_bytes();
+hipError_t fp8_cast(const void* x, int64_t rows, int64_t cols, DType dt, int fmt, void* q,
+                    void* qt, float* scales, void* scratch, hipStream_t s);
+// gemm_fp8: C[M, N] = (A[M, K] B[N, K]^T) a_inv[0] b_inv[0], K-contiguous
+// fp8 operands (formats fa, fb), epi E_STORE (bf16), E_F32 or E_F32_ACC;
+// scratch: split-K partials (gemm_fp8_scratch_bytes for the full split).
+bool gemm_fp8_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc);
+size_t gemm_fp8_scratch_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t gemm_fp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int fa,
+                    const void* B, int64_t ldb, int fb, const float* a_inv, const float* b_inv,
+                    void* C, int64_t ldc, int epi, void* scratch, size_t scratch_bytes,
+                    hipStream_t s);
 hipError_t loss_reduce(const float* ell, int64_t N, float* loss_ws,
                        float* loss_out, int* flag, hipStream_t s);
 // acc[0] += sum ell, acc[1] += sum bytes[tgt]; if final, acc[2] = bpb

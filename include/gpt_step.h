@@ -223,6 +223,44 @@ int gpt_k_gemm(int32_t op, int64_t M, int64_t N, int64_t K, const void* A,
                int32_t epilogue, void* aux, void* scratch, size_t scratch_bytes,
                int32_t dtype, hipStream_t s);
 
+/* FP8 linear layers with tensor-wise scaling (the nanochat walkthrough,
+ * section "3. precision management": with --fp8 most linear layers become
+ * Float8Linear with tensor-wise scales).  Formats are the OCP 8-bit floats:
+ * GPT_FP8_E4M3 (max 448; activations and weights) and GPT_FP8_E5M2 (max
+ * 57344; gradients). */
+enum { GPT_FP8_E4M3 = 0, GPT_FP8_E5M2 = 1 };
+
+/* Cast x [rows, cols] (dtype, device) with its tensor-wise scale:
+ * s = fmax / max(max |x|, 1e-12) (fp32), q = fp8(clamp(x * s, -fmax, fmax))
+ * rounded to nearest even (NaN stays NaN).  Outputs (device, 16-byte
+ * aligned, either may be null but not both): q [rows, cols] row-major and
+ * q_t [cols, rows] (its transpose, for the products that contract over
+ * rows); scales[0] = s, scales[1] = 1/s (device fp32).  Needs cols a
+ * multiple of 16, and rows too when q_t is given.  scratch: device, >=
+ * gpt_k_fp8_cast_scratch_bytes() bytes (per-block maxima). */
+size_t gpt_k_fp8_cast_scratch_bytes(void);
+int gpt_k_fp8_cast(const void* x, int64_t rows, int64_t cols, int32_t dtype,
+                   int32_t fp8_format, void* q, void* q_t, float* scales,
+                   void* scratch, size_t scratch_bytes, hipStream_t s);
+
+/* FP8 product: C [M, N] = (A [M, K] . B [N, K]^T) * a_inv_scale[0] *
+ * b_inv_scale[0], both operands K-contiguous 8-bit floats of the given
+ * formats (leading dimensions lda, ldb in bytes), fp32 accumulation.
+ * epilogue GPT_EPI_STORE (C bf16), GPT_EPI_F32 (C fp32) or GPT_EPI_F32_ACC
+ * (C fp32 +=).  For y = x W^T pass A = q(x), B = q(W); for dX = dY W pass
+ * A = q(dY), B = q_t(W); for dW = dY^T X pass A = q_t(dY), B = q_t(X).
+ * Needs K a multiple of 128, lda and ldb multiples of 16 and >= K, N and
+ * ldc multiples of 4, each operand under 4 GiB.  scratch (optional, fp32
+ * outputs): split-K partials, up to gpt_k_gemm_fp8_scratch_bytes(M, N, K)
+ * bytes; the product splits K only as far as the scratch allows. */
+size_t gpt_k_gemm_fp8_scratch_bytes(int64_t M, int64_t N, int64_t K);
+int gpt_k_gemm_fp8(int64_t M, int64_t N, int64_t K, const void* A,
+                   int64_t lda, int32_t fmt_a, const void* B, int64_t ldb,
+                   int32_t fmt_b, const float* a_inv_scale,
+                   const float* b_inv_scale, void* C, int64_t ldc,
+                   int32_t epilogue, void* scratch, size_t scratch_bytes,
+                   hipStream_t s);
+
 /* cos/sin table, float2 [T, hd/2]: (cos, sin) of t * base^(-2j/hd),
  * evaluated in double precision. */
 int gpt_k_rope_table(float* cs, int32_t T, int32_t hd, float base,

@@ -119,6 +119,25 @@ def test_entry_points_reject_bad_pointers_before_launch():
     assert L.gpt_k_attn_fwd(A, A, A, 1, 8, 2, 2, 128, 4, 1, -1.0, None) == -1
     assert L.gpt_k_attn_fwd(A, A, A, 1, 8, 2, 2, 128, 4, 1, float("nan"), None) == -1
     assert L.gpt_k_rmsnorm_fwd(A, C.c_void_p(0x1002), A, 4, 8, 1e-5, 1, None) == -4
+    # fp8 cast: x, rows, cols, dtype, fmt, q, q_t, scales, scratch, bytes
+    cs = L.gpt_k_fp8_cast_scratch_bytes()
+    assert cs >= 4096
+    assert L.gpt_k_fp8_cast(A, 64, 64, 1, 2, A, None, A, A, cs, None) == -1
+    assert L.gpt_k_fp8_cast(A, 64, 64, 1, 0, None, None, A, A, cs, None) == -1
+    assert L.gpt_k_fp8_cast(A, 64, 40, 1, 0, A, None, A, A, cs, None) == -1
+    assert L.gpt_k_fp8_cast(A, 70, 64, 1, 0, None, A, A, A, cs, None) == -1
+    assert L.gpt_k_fp8_cast(A, 64, 64, 1, 0, A, None, A, A, cs - 1, None) == -3
+    assert L.gpt_k_fp8_cast(A, 64, 64, 1, 0, C.c_void_p(0x1001), None, A, A, cs, None) == -4
+    # fp8 gemm: M, N, K, A, lda, fa, B, ldb, fb, ai, bi, C, ldc, epi, scratch, bytes
+    g8 = L.gpt_k_gemm_fp8
+    assert g8(64, 64, 100, A, 128, 0, A, 128, 0, A, A, A, 64, 0, None, 0, None) == -1
+    assert g8(64, 64, 128, A, 136, 0, A, 128, 0, A, A, A, 64, 0, None, 0, None) == -1
+    assert g8(64, 64, 128, A, 128, 0, A, 128, 0, A, A, A, 64, 1, None, 0, None) == -1
+    assert g8(64, 64, 128, A, 128, 3, A, 128, 0, A, A, A, 64, 0, None, 0, None) == -1
+    assert g8(64, 64, 128, A, 128, 0, A, 128, 0, None, A, A, 64, 0, None, 0, None) == -1
+    assert g8(64, 62, 128, A, 128, 0, A, 128, 0, A, A, A, 64, 0, None, 0, None) == -1
+    assert L.gpt_k_gemm_fp8_scratch_bytes(256, 256, 8192) > 0
+    assert L.gpt_k_gemm_fp8_scratch_bytes(256, 256, 100) == 0
     # decode attention: q, kc, vc, lens, o, lse, B, Tq, Tmax, H, Hkv, hd, W, bound,
     # scratch, scratch_bytes, dtype
     dec = L.gpt_k_attn_decode

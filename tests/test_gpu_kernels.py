@@ -628,3 +628,175 @@ def test_attention_decode_scratch_reuse():
         fresh = run_decode(q, kc, vc, lens, W, True)
         again = run_decode(q, kc, vc, lens, W, True, scr=shared)
         assert np.array_equal(fresh[0], again[0]) and np.array_equal(fresh[1], again[1])
+
+
+# ------------------------------------------------------ FP8 (tensor-wise)
+FP8_FMT = {G.FP8_E4M3: "e4m3", G.FP8_E5M2: "e5m2"}
+
+
+def _fp8_input(rows, cols, seed, spread=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    if spread:   # magnitudes over many binades: exercises subnormals and the top
+        x *= np.exp2(rng.integers(-12, 4, (rows, cols))).astype(np.float32)
+    return x
+
+
+def run_fp8_cast(x, dt, fmt, want_q=True, want_t=False):
+    rows, cols = x.shape
+    tx = dev(x, tdtype(dt))
+    q = torch.empty(rows, cols, dtype=torch.uint8, device=DEV) if want_q else None
+    qt = torch.empty(cols, rows, dtype=torch.uint8, device=DEV) if want_t else None
+    sc = torch.empty(4, dtype=torch.float32, device=DEV)
+    scr = torch.empty(G.k_fp8_cast_scratch_bytes(), dtype=torch.uint8, device=DEV)
+    G.k_fp8_cast(tx, rows, cols, dt, fmt, q, qt, sc, scr)
+    torch.cuda.synchronize()
+    return (q.cpu().numpy() if want_q else None, qt.cpu().numpy() if want_t else None,
+            sc.cpu().numpy())
+
+
+@pytest.mark.parametrize("fmt", [G.FP8_E4M3, G.FP8_E5M2])
+@pytest.mark.parametrize("dt", [G.BF16, G.F32])
+@pytest.mark.parametrize("shape,trans", [((64, 64), True), ((130, 48), False), ((144, 80), True),
+                                         ((1008, 768), True), ((1000, 768), False), ((16, 3072), True)])
+def test_fp8_cast(shape, trans, dt, fmt):
+    """Codes bit-exact against the oracle's cast (same fp32 scale, same fp32
+    product, nearest-even rounding); the transposed copy is the transpose;
+    s and 1/s exact."""
+    from oracle import fp8
+    say("fp8 cast", shape, trans, dt, fmt)
+    x = _fp8_input(*shape, seed=70 + shape[0])
+    if dt == G.BF16:
+        x = O.round_bf16(x)
+    codes, _, s, inv = fp8.quantize(x, FP8_FMT[fmt])
+    q, qt, sc = run_fp8_cast(x, dt, fmt, True, trans)
+    assert sc[0] == s and sc[1] == inv
+    np.testing.assert_array_equal(q, codes)
+    if trans:
+        np.testing.assert_array_equal(qt, codes.T)
+
+
+def test_fp8_cast_zero_and_saturation():
+    """An all-zero tensor casts to zero codes with s = 448 / 1e-12; a tensor
+    whose amax times s lands above 448 in fp32 keeps its largest element at
+    the format's maximum (code 0x7E), never NaN."""
+    from oracle import fp8
+    z = np.zeros((32, 32), np.float32)
+    q, qt, sc = run_fp8_cast(z, G.F32, G.FP8_E4M3, True, True)
+    assert np.all(q == 0) and np.all(qt == 0)
+    assert sc[0] == np.float32(np.float32(448) / np.float32(1e-12))
+    x = _fp8_input(32, 32, 5, spread=False) * 0.1
+    x[3, 3] = np.float32(12.5159)
+    q, _, _ = run_fp8_cast(x, G.F32, G.FP8_E4M3)
+    assert q[3, 3] == 0x7E
+    np.testing.assert_array_equal(q, fp8.quantize(x, "e4m3")[0])
+
+
+def fp8_mm_bound(va, ia, vb, ib):
+    """Elementwise error bound of an fp32-output FP8 product: the matrix
+    cores form each 128-long block dot product of 8-bit values with about 16
+    significant bits before adding it to the fp32 accumulator (measured:
+    |error| / sum |a b| <= 2e-5 for one block, falling with K as blocks
+    add), so the bound is 2^-13 sum_k |a_k b_k| (1/sa) (1/sb)."""
+    mag = np.abs(np.asarray(va, np.float64)) @ np.abs(np.asarray(vb, np.float64)).T
+    return 2.0 ** -13 * mag * np.float64(ia) * np.float64(ib)
+
+
+def _gemm_fp8_case(M, N, K, fa, fb, seed):
+    from oracle import fp8
+    ca, va, _, ia = fp8.quantize(_fp8_input(M, K, seed, spread=False), FP8_FMT[fa])
+    cb, vb, _, ib = fp8.quantize(_fp8_input(N, K, seed + 1, spread=False), FP8_FMT[fb])
+    return ca, va, ia, cb, vb, ib
+
+
+@pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 200, 384), (512, 768, 768),
+                                   (1000, 260, 256), (64, 3072, 1024)])
+def test_gemm_fp8(M, N, K, fa, fb):
+    """The FP8 product on the oracle's own codes and inverse scales: bf16
+    output normwise within 1e-2 of the fp64 product (one bf16 step, 2^-7 of
+    an element, when the accumulation error moves a value across a rounding
+    boundary), fp32 output (+= onto a random C) elementwise within the
+    matrix cores' FP8 accumulation bound."""
+    from oracle import fp8
+    say("gemm fp8", M, N, K, fa, fb)
+    ca, va, ia, cb, vb, ib = _gemm_fp8_case(M, N, K, fa, fb, seed=M + N)
+    ref = fp8.scaled_mm(va, ia, vb, ib)
+    tA, tB = dev(ca, torch.uint8), dev(cb, torch.uint8)
+    tia = torch.tensor([ia], dtype=torch.float32, device=DEV)
+    tib = torch.tensor([ib], dtype=torch.float32, device=DEV)
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    G.k_gemm_fp8(M, N, K, tA, K, fa, tB, K, fb, tia, tib, out, N, G.EPI_STORE)
+    c0 = np.random.default_rng(3).standard_normal((M, N)).astype(np.float32)
+    acc = dev(c0, torch.float32)
+    G.k_gemm_fp8(M, N, K, tA, K, fa, tB, K, fb, tia, tib, acc, N, G.EPI_F32_ACC)
+    torch.cuda.synchronize()
+    assert rel_err(to_np(out), ref) < 1e-2
+    err = np.abs(to_np(acc) - (ref + c0))
+    assert np.all(err <= fp8_mm_bound(va, ia, vb, ib) + 1e-6 * np.abs(ref + c0))
+
+
+def test_gemm_fp8_split_k_and_strides():
+    """fp32 output with the K split over scratch partials (fixed-order sum),
+    and operands with leading dimensions above K."""
+    from oracle import fp8
+    M, N, K, lda, ldb = 256, 192, 8192, 8192 + 64, 8192 + 128
+    ca, va, ia, cb, vb, ib = _gemm_fp8_case(M, N, K, 0, 1, seed=11)
+    A = np.zeros((M, lda), np.uint8)
+    A[:, :K] = ca
+    B = np.full((N, ldb), 0x7F, np.uint8)     # NaN codes past K must never be read
+    B[:, :K] = cb
+    tA, tB = dev(A, torch.uint8), dev(B, torch.uint8)
+    tia = torch.tensor([ia], dtype=torch.float32, device=DEV)
+    tib = torch.tensor([ib], dtype=torch.float32, device=DEV)
+    nb = G.k_gemm_fp8_scratch_bytes(M, N, K)
+    assert nb > 0
+    scr = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    out = torch.empty(M, N, dtype=torch.float32, device=DEV)
+    G.k_gemm_fp8(M, N, K, tA, lda, 0, tB, ldb, 1, tia, tib, out, N, G.EPI_F32, scr)
+    torch.cuda.synchronize()
+    ref = fp8.scaled_mm(va, ia, vb, ib)
+    err = np.abs(to_np(out) - ref)
+    assert np.all(err <= fp8_mm_bound(va, ia, vb, ib) + 1e-6 * np.abs(ref))
+
+
+def test_fp8_linear_forward_and_backward_chain():
+    """Float8Linear end to end on the GPU (cast kernels feeding the product)
+    against the oracle: y = x W^T (e4m3 x e4m3), dX = dY W (e5m2 dY against
+    the transposed e4m3 weight copy) and dW = dY^T X (transposed copies of
+    both), at a d12 MLP shape."""
+    from oracle import fp8
+    M, K, N = 2048, 768, 3072           # tokens, in, out
+    x = O.round_bf16(_fp8_input(M, K, 1, spread=False))
+    w = O.round_bf16(_fp8_input(N, K, 2, spread=False) * 0.02)
+    dy = O.round_bf16(_fp8_input(M, N, 3, spread=False) * 1e-3)
+    tx, tw, tdy = dev(x, torch.bfloat16), dev(w, torch.bfloat16), dev(dy, torch.bfloat16)
+    scr = torch.empty(G.k_fp8_cast_scratch_bytes(), dtype=torch.uint8, device=DEV)
+
+    def cast(t, rows, cols, fmt):
+        q = torch.empty(rows, cols, dtype=torch.uint8, device=DEV)
+        qt = torch.empty(cols, rows, dtype=torch.uint8, device=DEV)
+        sc = torch.empty(2, dtype=torch.float32, device=DEV)
+        G.k_fp8_cast(t, rows, cols, G.BF16, fmt, q, qt, sc, scr)
+        return q, qt, sc
+
+    qx, qxt, sx = cast(tx, M, K, G.FP8_E4M3)
+    qw, qwt, sw = cast(tw, N, K, G.FP8_E4M3)
+    qd, qdt, sd = cast(tdy, M, N, G.FP8_E5M2)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    G.k_gemm_fp8(M, N, K, qx, K, 0, qw, K, 0, sx[1:], sw[1:], y, N, G.EPI_STORE)
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device=DEV)
+    G.k_gemm_fp8(M, K, N, qd, N, 1, qwt, N, 0, sd[1:], sw[1:], dx, K, G.EPI_STORE)
+    dw = torch.empty(N, K, dtype=torch.float32, device=DEV)
+    G.k_gemm_fp8(N, K, M, qdt, M, 1, qxt, M, 0, sd[1:], sx[1:], dw, K, G.EPI_F32)
+    torch.cuda.synchronize()
+    _, vx, _, ix = fp8.quantize(x, "e4m3")
+    _, vw, _, iw = fp8.quantize(w, "e4m3")
+    _, vd, _, idy = fp8.quantize(dy, "e5m2")
+    assert rel_err(to_np(y), fp8.fp8_linear(x, w)) < 1e-2
+    assert rel_err(to_np(dx), fp8.scaled_mm(vd, idy, vw.T, iw)) < 1e-2
+    dw_ref = fp8.scaled_mm(vd.T, idy, vx.T, ix)
+    assert np.all(np.abs(to_np(dw) - dw_ref) <= fp8_mm_bound(vd.T, idy, vx.T, ix)
+                  + 1e-6 * np.abs(dw_ref))
+    # and FP8 stays close to the bf16 product it stands in for
+    assert rel_err(to_np(y), x.astype(np.float64) @ w.astype(np.float64).T) < 0.1
