@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d12]
     python bench.py --workload decode [--config d12gqa] [--decode-batch 64]
+    python bench.py --workload fp8 [--config d24]
 
 Times K forward+backward steps of the d12 model (12 layers, width 768, 6
 heads of 128, vocab 32768, 16 rows of 2048 tokens, 'SSSL' windows 1024/2048,
@@ -20,6 +21,9 @@ With --workload decode it instead times the attention of one generation
 step: one new token for each of --decode-batch sequences whose caches hold
 seq_len positions, every layer over its own cache with that layer's window;
 the line reports new tokens/s and the KV-cache bytes read per second.
+With --workload fp8 it times the step's linear layers (forward and both
+backward products) as FP8 linear layers with tensor-wise scales, casts
+included, beside the same products in bf16.
 """
 from __future__ import annotations
 
@@ -195,12 +199,12 @@ def kernel_profile(step, n_steps, torch, G):
     return rows
 
 
-def roofline_of(row, step_ms):
+def roofline_of(row, step_ms, peak_flops=PEAK_BF16):
     """Roofline object of one kernel row of kernel_profile."""
     from rocprof_summary import load_traffic
     sec = row["avg_launch_ms"] / 1e3
     if row["flops_per_launch"] > 0:
-        ach, peak, unit, bound = row["flops_per_launch"] / sec / 1e12, PEAK_BF16 / 1e12, "TFLOP/s", "mfma"
+        ach, peak, unit, bound = row["flops_per_launch"] / sec / 1e12, peak_flops / 1e12, "TFLOP/s", "mfma"
     else:
         ach, peak, unit, bound = row["bytes_per_launch"] / sec / 1e9, PEAK_HBM / 1e9, "GB/s", "hbm"
     tr = load_traffic(row["kernel"])
@@ -351,20 +355,156 @@ def bench_decode(a, torch, G):
     print(json.dumps(out), flush=True)
 
 
+FP8_METRIC = "FP8 (tensor-wise) linear layers fwd+bwd of a training step: tokens/s; % fp8 MFMA peak"
+PEAK_FP8 = 5.0e15         # MI355X dense fp8 MFMA, FLOP/s
+
+
+def linear_shapes(cfg):
+    """(in, out) of the four linear layers of one block."""
+    D, H, Hkv, hd = cfg["d_model"], cfg["n_head"], cfg["n_kv_head"], cfg["head_dim"]
+    F = cfg["mlp_mult"] * D
+    return [(D, (H + 2 * Hkv) * hd), (H * hd, D), (D, F), (F, D)]
+
+
+def bench_fp8(a, torch, G):
+    """The linear layers of one d12 step as FP8 linear layers with tensor-wise
+    scales, forward and backward: per layer and linear, cast x (e4m3, with
+    its transpose), cast W (e4m3, with its transpose), y = x W^T; cast dY
+    (e5m2, with its transpose), dX = dY W, dW = dY^T X (fp32).  The same
+    products in bf16 are timed beside it."""
+    import gptinputs as gi
+    cfg = gi.preset(a.config)
+    N = cfg["batch"] * cfg["seq_len"]
+    shapes = linear_shapes(cfg)
+    L = cfg["n_layer"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg["seed"])
+    dev = "cuda"
+
+    def rnd(shape, scale):
+        return (torch.randn(shape, generator=g, device=dev) * scale).bfloat16()
+
+    log(f"fp8 inputs: {L} layers x {len(shapes)} linears, {N} tokens")
+    lay = []
+    for _ in range(L):
+        for (fi, fo) in shapes:
+            lay.append(dict(fi=fi, fo=fo, x=rnd((N, fi), 1.0), w=rnd((fo, fi), 0.02),
+                            dy=rnd((N, fo), 1e-3)))
+    u8 = torch.uint8
+    mx_in = max(fi for fi, _ in shapes)
+    mx_out = max(fo for _, fo in shapes)
+    qx, qxt = torch.empty(N * mx_in, dtype=u8, device=dev), torch.empty(N * mx_in, dtype=u8,
+                                                                          device=dev)
+    qw, qwt = (torch.empty(mx_in * mx_out, dtype=u8, device=dev) for _ in range(2))
+    qd, qdt = torch.empty(N * mx_out, dtype=u8, device=dev), torch.empty(N * mx_out, dtype=u8,
+                                                                           device=dev)
+    sc = torch.empty(12, dtype=torch.float32, device=dev)
+    cscr = torch.empty(G.k_fp8_cast_scratch_bytes(), dtype=u8, device=dev)
+    y = torch.empty(N * mx_out, dtype=torch.bfloat16, device=dev)
+    dx = torch.empty(N * mx_in, dtype=torch.bfloat16, device=dev)
+    dw = torch.empty(mx_in * mx_out, dtype=torch.float32, device=dev)
+    gs = max(max(G.k_gemm_fp8_scratch_bytes(fo, fi, N), G.k_gemm_scratch_bytes(fo, fi, N))
+             for fi, fo in shapes)
+    gscr = torch.empty(max(16, gs), dtype=u8, device=dev)
+    E4, E5 = G.FP8_E4M3, G.FP8_E5M2
+
+    def step_fp8():
+        for d in lay:
+            fi, fo = d["fi"], d["fo"]
+            G.k_fp8_cast(d["x"], N, fi, G.BF16, E4, qx, qxt, sc[0:2], cscr)
+            G.k_fp8_cast(d["w"], fo, fi, G.BF16, E4, qw, qwt, sc[4:6], cscr)
+            G.k_gemm_fp8(N, fo, fi, qx, fi, E4, qw, fi, E4, sc[1:2], sc[5:6], y, fo, G.EPI_STORE)
+            G.k_fp8_cast(d["dy"], N, fo, G.BF16, E5, qd, qdt, sc[8:10], cscr)
+            G.k_gemm_fp8(N, fi, fo, qd, fo, E5, qwt, fo, E4, sc[9:10], sc[5:6], dx, fi,
+                         G.EPI_STORE)
+            G.k_gemm_fp8(fo, fi, N, qdt, N, E5, qxt, N, E4, sc[9:10], sc[1:2], dw, fi, G.EPI_F32,
+                         gscr)
+
+    def step_bf16():
+        for d in lay:
+            fi, fo = d["fi"], d["fo"]
+            G.k_gemm(G.GEMM_NT, N, fo, fi, d["x"], fi, d["w"], fi, y, fo, G.EPI_STORE, None, G.BF16)
+            G.k_gemm(G.GEMM_NN, N, fi, fo, d["dy"], fo, d["w"], fi, dx, fi, G.EPI_STORE, None,
+                     G.BF16)
+            G.k_gemm(G.GEMM_TN, fo, fi, N, d["dy"], fo, d["x"], fi, dw, fi, G.EPI_F32, None,
+                     G.BF16, scratch=gscr)
+
+    for _ in range(a.warmup):
+        step_fp8()
+        step_bf16()
+    torch.cuda.synchronize()
+    assert torch.isfinite(y[:N * shapes[-1][1]].float()).all()
+    ms8 = time_events(step_fp8, a.steps, torch) * 1e3
+    ms16 = time_events(step_bf16, a.steps, torch) * 1e3
+    flops = 6.0 * N * sum(fi * fo for fi, fo in shapes) * L
+    log(f"fp8 linears {ms8:.3f} ms ({flops / ms8 / 1e9:,.0f} TFLOP/s incl. casts)  "
+        f"bf16 {ms16:.3f} ms ({flops / ms16 / 1e9:,.0f} TFLOP/s)")
+    prof = kernel_profile(step_fp8, a.prof_steps, torch, G) if a.prof_steps > 0 else []
+    for r in prof:
+        rate = (f"{r['tflops']:7.1f} TFLOP/s" if r["tflops"] else
+                f"{r['gbps']:7.0f} GB/s" if r["gbps"] else "")
+        log(f"  {r['ms_per_step']:7.3f} ms/step {r['launches_per_step']:5.0f} x "
+            f"{r['avg_launch_ms'] * 1e3:8.1f} us  {rate:>16}  {r['kernel']}")
+    roof = roofline_of(prof[0], ms8, peak_flops=PEAK_FP8) if prof else None
+    out = {
+        "metric": FP8_METRIC, "value": round(N / (ms8 / 1e3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms8, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, N(0,1e-3) "
+                "output gradients)",
+        "config": {"workload": f"{a.config} linear layers fwd+bwd in FP8: {L} layers x "
+                               f"{len(shapes)} linears {shapes} (in, out), {N} tokens; "
+                               "e4m3 x and W, e5m2 dY, tensor-wise scales, casts included",
+                   "global_batch": cfg["batch"], "seq_len": cfg["seq_len"],
+                   "parallelism": "single GPU"},
+        "bf16_ms_per_step": round(ms16, 4), "speedup_vs_bf16": round(ms16 / ms8, 3),
+        "linear_flops_per_step": flops,
+        "roofline": roof, "cpu_baseline": None if a.no_cpu else cpu_fp8_baseline(cfg),
+        "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
+                    for r in prof],
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_fp8_baseline(cfg, rows=256):
+    """The oracle's FP8 linear (cast both operands, fp64 product) over every
+    linear of one block for `rows` tokens, forward only: tokens/s."""
+    import numpy as np
+    from oracle import fp8
+    rng = np.random.default_rng(1)
+    dt = 0.0
+    for fi, fo in linear_shapes(cfg):
+        x = rng.standard_normal((rows, fi), dtype=np.float32)
+        w = rng.standard_normal((fo, fi), dtype=np.float32) * 0.02
+        t0 = time.perf_counter()
+        fp8.fp8_linear(x, w)
+        dt += time.perf_counter() - t0
+    scale = cfg["n_layer"] * 3        # all layers, and the two backward products
+    threads = os.environ.get("OMP_NUM_THREADS")
+    cores = int(threads) if threads else len(os.sched_getaffinity(0))
+    return {"value": round(rows / (dt * scale), 2), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{rows} tokens through the 4 linears of one block (forward: casts and "
+                      f"fp64 product, numpy, {dt:.2f} s measured), time scaled x{scale} for "
+                      f"{cfg['n_layer']} layers x 3 products of equal size"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default=None, help="preset (train: d12, decode: d12gqa)")
+    ap.add_argument("--config", default=None,
+                    help="preset (train: d12, decode: d12gqa, fp8: d24)")
     ap.add_argument("--eval-rows", type=int, default=64)
     ap.add_argument("--prof-steps", type=int, default=2,
                     help="steps run with launch recording for the per-kernel split (0: none)")
     ap.add_argument("--shapes", action="store_true",
                     help="also time every product / attention shape alone")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--workload", choices=("train", "decode"), default="train",
-                    help="train: the fwd+bwd step; decode: KV-cache decode attention")
+    ap.add_argument("--workload", choices=("train", "decode", "fp8"), default="train",
+                    help="train: the fwd+bwd step; decode: KV-cache decode attention; fp8: the "
+                         "step's linear layers as FP8 linear layers")
     ap.add_argument("--decode-batch", type=int, default=64,
                     help="sequences sampled in parallel (decode workload)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -389,6 +529,10 @@ def main():
     if a.workload == "decode":
         a.config = a.config or "d12gqa"
         bench_decode(a, torch, G)
+        return
+    if a.workload == "fp8":
+        a.config = a.config or "d24"
+        bench_fp8(a, torch, G)
         return
     a.config = a.config or "d12"
     cfg = gi.preset(a.config)

@@ -648,7 +648,9 @@ int gpt_k_fp8_cast(const void* x, int64_t rows, int64_t cols, int32_t dtype, int
                    void* q, void* q_t, float* scales, void* scratch, size_t scratch_bytes,
                    hipStream_t s) {
   int st;
-  if ((st = dtype_ok(dtype)) || (st = check_ptrs({x, scales, scratch}))) return st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({x, scratch}))) return st;
+  if (!scales || ((uintptr_t)scales & 3u))
+    return fail(GPT_ERR_INVALID_ARG, "scales null or not 4-byte aligned");
   if (fp8_format != GPT_FP8_E4M3 && fp8_format != GPT_FP8_E5M2)
     return fail(GPT_ERR_INVALID_ARG, "unknown fp8 format");
   if (!q && !q_t) return fail(GPT_ERR_INVALID_ARG, "no output requested");

@@ -77,13 +77,25 @@ __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
 
 }  // namespace
 
-// per-block max |x| over 8-element runs, grid-stride
+// per-block max |x| over 8-element runs, grid-stride, four runs in flight
+// per thread
 template <typename T>
 __global__ __launch_bounds__(256) void k_fp8_amax(const T* __restrict__ x, int64_t n8,
                                                   float* __restrict__ part) {
   __shared__ float red[4];
   float m = 0.f;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n8; i += 4 * stride) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8(x, 8 * (i + u * stride), v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = absmax(m, v[u][e]);
+  }
+  for (; i < n8; i += stride) {
     float v[8];
     load8(x, 8 * i, v);
 #pragma unroll
@@ -147,7 +159,8 @@ size_t fp8_cast_scratch_bytes() { return kMaxParts * sizeof(float); }
 hipError_t fp8_cast(const void* x, int64_t rows, int64_t cols, DType dt, int fmt, void* q,
                     void* qt, float* scales, void* scratch, hipStream_t s) {
   const int64_t n8 = rows * cols / 8;
-  const int parts = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxParts, cdiv(n8, 2048)));
+  // about 8 runs of 8 per thread (two rounds of four loads in flight)
+  const int parts = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxParts, cdiv(n8, 8 * 256)));
   float* part = (float*)scratch;
   const double in_bytes = (double)rows * cols * (dt == BF16 ? 2 : 4);
   if (dt == BF16)

@@ -235,7 +235,8 @@ enum { GPT_FP8_E4M3 = 0, GPT_FP8_E5M2 = 1 };
  * rounded to nearest even (NaN stays NaN).  Outputs (device, 16-byte
  * aligned, either may be null but not both): q [rows, cols] row-major and
  * q_t [cols, rows] (its transpose, for the products that contract over
- * rows); scales[0] = s, scales[1] = 1/s (device fp32).  Needs cols a
+ * rows); scales[0] = s, scales[1] = 1/s (device fp32, 4-byte aligned).
+ * Needs cols a
  * multiple of 16, and rows too when q_t is given.  scratch: device, >=
  * gpt_k_fp8_cast_scratch_bytes() bytes (per-block maxima). */
 size_t gpt_k_fp8_cast_scratch_bytes(void);
