@@ -11,8 +11,9 @@ seeded input generator (``gptinputs``), which holds no model arithmetic.
 Sources (pages, cited by title and section):
   [nanochat]  "5만원으로 나만의 ChatGPT 훈련하는 방법" (apidog.com blog, nanochat
               walkthrough): "1. GPT model (nanochat/gpt.py)" architecture list,
-              value-embedding snippet; "3. precision management" (also the
-              FP8 linear layers, `oracle.fp8`); "5. flash
+              value-embedding snippet; "2. Muon optimizer" (the Newton-
+              Schulz orthogonalization, `oracle.muon`); "3. precision
+              management" (also the FP8 linear layers, `oracle.fp8`); "5. flash
               attention integration" (causal + window_size call); "6.
               inference engine" (KV-cache attention of new tokens).
   [microgpt]  "microgpt" (news.hada.io): "model architecture" (RMSNorm, ReLU,
@@ -33,3 +34,4 @@ from .gpt import (  # noqa: F401
     forward, backward, step, eval_bpb, round_bf16,
 )
 from . import fp8  # noqa: F401  (FP8 linear layers with tensor-wise scaling)
+from . import muon  # noqa: F401  (Muon's Newton-Schulz orthogonalization)

@@ -613,3 +613,46 @@ def test_fp8_linear_exact_when_operands_are_representable():
     _, qx, sx, ix = fp8.quantize(x, "e4m3")
     assert sx == 128 and ix == np.float32(1 / 128)
     np.testing.assert_array_equal(qx, x * 128)
+
+
+# ------------------------------------------------------- Muon Newton-Schulz
+PAGE_NS = [(8.156, -22.483, 15.879), (4.043, -2.809, 0.500)]
+
+
+def test_polar_express_acts_on_singular_values():
+    """Each step maps every singular value s of X to a s + b s^3 + c s^5 and
+    keeps the singular vectors (X = U S V^T => a X + X (b X^T X + c (X^T
+    X)^2) = U p(S) V^T), starting from s / ||G||_F: checked against numpy's
+    SVD for a tall matrix, one and two steps."""
+    from oracle import muon
+    rng = np.random.default_rng(0)
+    G = rng.standard_normal((40, 24))
+    U, S, Vt = np.linalg.svd(G, full_matrices=False)
+    s = S / (np.linalg.norm(G) + muon.NS_EPS)
+    for k in (1, 2):
+        want = s.copy()
+        for a, b, c in PAGE_NS[:k]:
+            want = a * want + b * want ** 3 + c * want ** 5
+        X = muon.polar_express(G, PAGE_NS[:k])
+        np.testing.assert_allclose(X, (U * want) @ Vt, atol=1e-10)
+
+
+def test_polar_express_orientation_scale_and_bf16():
+    """A wide matrix is the transpose of its transpose's result; scaling G
+    by a positive constant changes nothing but the eps term (the start
+    divides by the norm);
+    the bf16 mode stays within bf16 rounding of the exact iteration; the
+    classic quintic Muon tuple iterated five times sends every singular
+    value into a band around 1."""
+    from oracle import muon
+    rng = np.random.default_rng(1)
+    G = rng.standard_normal((24, 56))
+    X = muon.polar_express(G, PAGE_NS)
+    np.testing.assert_allclose(X, muon.polar_express(G.T, PAGE_NS).T, atol=1e-12)
+    np.testing.assert_allclose(muon.polar_express(7.5 * G, PAGE_NS), X, atol=1e-6)
+    Xb = muon.polar_express(G, PAGE_NS, bf16=True)
+    assert np.abs(Xb - X).max() / np.abs(X).max() < 3e-2
+    classic = [(3.4445, -4.7750, 2.0315)] * 5
+    sv = np.linalg.svd(muon.polar_express(rng.standard_normal((64, 32)), classic),
+                       compute_uv=False)
+    assert sv.min() > 0.6 and sv.max() < 1.25
