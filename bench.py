@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d12]
     python bench.py --workload decode [--config d12gqa] [--decode-batch 64]
     python bench.py --workload fp8 [--config d24]
+    python bench.py --workload muon [--config d12]
 
 Times K forward+backward steps of the d12 model (12 layers, width 768, 6
 heads of 128, vocab 32768, 16 rows of 2048 tokens, 'SSSL' windows 1024/2048,
@@ -23,7 +24,8 @@ seq_len positions, every layer over its own cache with that layer's window;
 the line reports new tokens/s and the KV-cache bytes read per second.
 With --workload fp8 it times the step's linear layers (forward and both
 backward products) as FP8 linear layers with tensor-wise scales, casts
-included, beside the same products in bf16.
+included, beside the same products in bf16.  With --workload muon it times
+Muon's Newton-Schulz orthogonalization of an update for every block matrix.
 """
 from __future__ import annotations
 
@@ -489,6 +491,82 @@ def cpu_fp8_baseline(cfg, rows=256):
                       f"{cfg['n_layer']} layers x 3 products of equal size"}
 
 
+MUON_METRIC = "Muon orthogonalization of every matrix update of a step: ms/step; TFLOP/s"
+NS_TUPLE = (3.4445, -4.7750, 2.0315)   # the classic quintic tuple, five steps
+
+
+def matrix_shapes(cfg):
+    """[out, in] of the matrices Muon updates: the four linears of every block."""
+    return [(fo, fi) for fi, fo in linear_shapes(cfg)] * cfg["n_layer"]
+
+
+def bench_muon(a, torch, G):
+    """Newton-Schulz orthogonalization (5 quintic steps) of a random fp32
+    update for every block matrix of the model: one batched call per
+    parameter shape (that parameter of every layer)."""
+    import gptinputs as gi
+    from oracle.muon import ns_flops
+    cfg = gi.preset(a.config)
+    shapes = matrix_shapes(cfg)
+    groups = sorted(set(shapes))
+    L = cfg["n_layer"]
+    steps = 5
+    coeffs = [NS_TUPLE] * steps
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg["seed"])
+    grads = [torch.randn(L, m, n, generator=g, device="cuda") for m, n in groups]
+    outs = [torch.empty(L, m, n, dtype=torch.bfloat16, device="cuda") for m, n in groups]
+    ws = torch.empty(max(G.k_polar_express_ws_bytes(m, n, L) for m, n in groups),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        for (m, n), gr, o in zip(groups, grads, outs):
+            G.k_polar_express(gr, m, n, G.F32, coeffs, 1e-7, o, ws, batch=L)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(o.float()).all() for o in outs)
+    ms = time_events(step, a.steps, torch) * 1e3
+    flops = sum(ns_flops(m, n, steps) for m, n in shapes)
+    log(f"muon: {len(shapes)} matrices, {ms:.3f} ms per step, {flops / ms / 1e9:,.0f} TFLOP/s")
+    prof = kernel_profile(step, a.prof_steps, torch, G) if a.prof_steps > 0 else []
+    for r in prof[:10]:
+        rate = (f"{r['tflops']:7.1f} TFLOP/s" if r["tflops"] else
+                f"{r['gbps']:7.0f} GB/s" if r["gbps"] else "")
+        log(f"  {r['ms_per_step']:7.3f} ms/step {r['launches_per_step']:5.0f} x "
+            f"{r['avg_launch_ms'] * 1e3:8.1f} us  {rate:>16}  {r['kernel']}")
+    roof = roofline_of(prof[0], ms) if prof else None
+    cpu = None
+    if not a.no_cpu:
+        import numpy as np
+        from oracle import muon
+        rng = np.random.default_rng(2)
+        t0 = time.perf_counter()
+        for m, n in shapes[:4]:
+            muon.polar_express(rng.standard_normal((m, n)), coeffs)
+        dt = (time.perf_counter() - t0) * (len(shapes) / 4)
+        threads = os.environ.get("OMP_NUM_THREADS")
+        cores = int(threads) if threads else len(os.sched_getaffinity(0))
+        cpu = {"value": round(dt * 1e3, 1), "unit": "ms/step", "cores": cores, "kind": "oracle",
+               "sample": f"one block's 4 matrices (numpy fp64, {dt / (len(shapes) / 4):.2f} s "
+                         f"measured), time scaled x{len(shapes) // 4}"}
+    out = {
+        "metric": MUON_METRIC, "value": round(ms, 4), "unit": "ms/step", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) fp32 updates)",
+        "config": {"workload": f"{a.config} Muon orthogonalization: {len(shapes)} matrices, "
+                               f"{L} of each of {groups} batched per call, {steps} quintic "
+                               f"Newton-Schulz steps {NS_TUPLE}", "parallelism": "single GPU"},
+        "tflops": round(flops / ms / 1e9, 1), "ns_flops_per_step": flops,
+        "roofline": roof, "cpu_baseline": cpu,
+        "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
+                    for r in prof],
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -502,9 +580,10 @@ def main():
     ap.add_argument("--shapes", action="store_true",
                     help="also time every product / attention shape alone")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--workload", choices=("train", "decode", "fp8"), default="train",
+    ap.add_argument("--workload", choices=("train", "decode", "fp8", "muon"), default="train",
                     help="train: the fwd+bwd step; decode: KV-cache decode attention; fp8: the "
-                         "step's linear layers as FP8 linear layers")
+                         "step's linear layers as FP8 linear layers; muon: Muon's "
+                         "orthogonalization of every matrix update")
     ap.add_argument("--decode-batch", type=int, default=64,
                     help="sequences sampled in parallel (decode workload)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -529,6 +608,10 @@ def main():
     if a.workload == "decode":
         a.config = a.config or "d12gqa"
         bench_decode(a, torch, G)
+        return
+    if a.workload == "muon":
+        a.config = a.config or "d12"
+        bench_muon(a, torch, G)
         return
     if a.workload == "fp8":
         a.config = a.config or "d24"

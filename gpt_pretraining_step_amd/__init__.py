@@ -91,9 +91,9 @@ _SIGS = {
     "gpt_k_gemm_fp8_scratch_bytes": (_sz, [_i64, _i64, _i64]),
     "gpt_k_gemm_fp8": (C.c_int, [_i64, _i64, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _vp, _vp,
                                  _vp, _i64, _i32, _vp, _sz, _vp]),
-    "gpt_k_polar_express_ws_bytes": (_sz, [_i64, _i64]),
-    "gpt_k_polar_express": (C.c_int, [_vp, _i64, _i64, _i32, _vp, _i32, _f32, _vp, _vp, _sz,
-                                      _vp]),
+    "gpt_k_polar_express_ws_bytes": (_sz, [_i32, _i64, _i64]),
+    "gpt_k_polar_express": (C.c_int, [_vp, _i32, _i64, _i64, _i32, _vp, _i32, _f32, _vp, _vp,
+                                      _sz, _vp]),
     "gpt_k_ce": (C.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp]),
     "gpt_k_lm_ce_scratch_bytes": (_sz, [_i64, _i32]),
     "gpt_k_embed_fwd": (C.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp]),
@@ -286,17 +286,17 @@ def k_gemm_fp8(M, N, K, A, lda, fmt_a, B, ldb, fmt_b, a_inv, b_inv, C, ldc, epil
                                 _stream(stream)))
 
 
-def k_polar_express_ws_bytes(m, n):
-    return int(lib().gpt_k_polar_express_ws_bytes(m, n))
+def k_polar_express_ws_bytes(m, n, batch=1):
+    return int(lib().gpt_k_polar_express_ws_bytes(batch, m, n))
 
 
-def k_polar_express(g, m, n, dtype, coeffs, eps, x_out, ws, stream=None):
+def k_polar_express(g, m, n, dtype, coeffs, eps, x_out, ws, batch=1, stream=None):
     """coeffs: a sequence of (a, b, c) tuples (host)."""
     flat = [float(v) for t in coeffs for v in t]
     arr = (C.c_float * max(1, len(flat)))(*flat)
-    _check(lib().gpt_k_polar_express(_ptr(g), m, n, dtype, C.cast(arr, C.c_void_p), len(coeffs),
-                                     eps, _ptr(x_out), _ptr(ws), ws.numel() * ws.element_size(),
-                                     _stream(stream)))
+    _check(lib().gpt_k_polar_express(_ptr(g), batch, m, n, dtype, C.cast(arr, C.c_void_p),
+                                     len(coeffs), eps, _ptr(x_out), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def k_embed_fwd(tokens, B, T, wte, V, D, x, dtype, stream=None):

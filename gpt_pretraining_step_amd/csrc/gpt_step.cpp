@@ -693,26 +693,28 @@ int gpt_k_gemm_fp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, 
   return GPT_OK;
 }
 
-size_t gpt_k_polar_express_ws_bytes(int64_t m, int64_t n) {
-  if (m < 8 || n < 8 || m % 8 || n % 8) return 0;
-  return gk::polar_express_ws_bytes(m, n);
+size_t gpt_k_polar_express_ws_bytes(int32_t batch, int64_t m, int64_t n) {
+  if (batch < 1 || batch > 65535 || m < 8 || n < 8 || m % 8 || n % 8) return 0;
+  return gk::polar_express_ws_bytes(batch, m, n);
 }
 
-int gpt_k_polar_express(const void* g, int64_t m, int64_t n, int32_t dtype, const float* coeffs,
-                        int32_t steps, float eps, void* x_out, void* ws, size_t ws_bytes,
-                        hipStream_t s) {
+int gpt_k_polar_express(const void* g, int32_t batch, int64_t m, int64_t n, int32_t dtype,
+                        const float* coeffs, int32_t steps, float eps, void* x_out, void* ws,
+                        size_t ws_bytes, hipStream_t s) {
   int st;
   if ((st = dtype_ok(dtype)) || (st = check_ptrs({g, x_out, ws}))) return st;
+  if (batch < 1 || batch > 65535) return fail(GPT_ERR_INVALID_ARG, "batch outside [1, 65535]");
   if (m < 8 || n < 8 || m % 8 || n % 8)
     return fail(GPT_ERR_INVALID_ARG, "m and n must be multiples of 8");
   if (steps < 0 || steps > 64 || (steps > 0 && !coeffs))
     return fail(GPT_ERR_INVALID_ARG, "steps outside [0, 64] or coeffs null");
   if (!(eps >= 0.f)) return fail(GPT_ERR_INVALID_ARG, "eps must be >= 0");
-  if ((double)m * n * 2 >= 4294967295.0)
-    return fail(GPT_ERR_INVALID_ARG, "matrix too large");
-  if (ws_bytes < gk::polar_express_ws_bytes(m, n))
-    return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "ws needs %zu bytes", gk::polar_express_ws_bytes(m, n));
-  KERNEL_TRY(gk::polar_express(g, m, n, (gk::DType)dtype, coeffs, steps, eps, x_out, ws, s));
+  if ((double)batch * m * n * 4 >= 4294967295.0 * 64)
+    return fail(GPT_ERR_INVALID_ARG, "batch too large");
+  const size_t need = gk::polar_express_ws_bytes(batch, m, n);
+  if (ws_bytes < need) return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "ws needs %zu bytes", need);
+  KERNEL_TRY(gk::polar_express(g, batch, m, n, (gk::DType)dtype, coeffs, steps, eps, x_out, ws,
+                               s));
   return GPT_OK;
 }
 

@@ -279,6 +279,9 @@ __device__ __forceinline__ void mma_slice(const bf16* As, const bf16* Bs, int wm
 struct TileMap {
   int tiles_m, tiles_n, splits;
   int64_t k_per_split;     // multiple of BK
+  // batched products (k_gemm_mfma only, blockIdx.y = batch index): element
+  // strides between the batch's A, B and C matrices
+  int64_t bs_a = 0, bs_b = 0, bs_c = 0;
   // E_CE only: per-(row, column tile) stats, target logits, token rows
   float* ce_stats = nullptr;
   float* ce_zt = nullptr;
@@ -317,6 +320,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(int64_t M, int64_t N, int6
   constexpr int TMI = WM / 16, TNJ = WN / 16;
   __shared__ __attribute__((aligned(16))) bf16 As[BM * LDK];
   __shared__ __attribute__((aligned(16))) bf16 Bs[BN * LDK];
+  if (blockIdx.y) {
+    constexpr int ce = (EPI == E_F32 || EPI == E_F32_ACC) ? 4 : 2;
+    A += blockIdx.y * tm.bs_a;
+    B += blockIdx.y * tm.bs_b;
+    C = (char*)C + blockIdx.y * tm.bs_c * ce;
+  }
 
   // ---- which tile: XCD-contiguous numbering, then grouped column-major
   const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
@@ -663,6 +672,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
   constexpr int TMI = WM / 16, TNJ = WN / 16;
   __shared__ __attribute__((aligned(1024))) bf16 st0[(BM + BN) * 64];
   __shared__ __attribute__((aligned(1024))) bf16 st1[(BM + BN) * 64];
+  if (blockIdx.y) {
+    constexpr int ce = (EPI == E_F32 || EPI == E_F32_ACC) ? 4 : 2;
+    A += blockIdx.y * tm.bs_a;
+    B += blockIdx.y * tm.bs_b;
+    C = (char*)C + blockIdx.y * tm.bs_c * ce;
+  }
 
   const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
   const int per_xcd = (nb + 7) / 8;
@@ -1465,6 +1480,94 @@ hipError_t gemm_fp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
   const Work rw(0.0, 4.0 * MN * (tm.splits + 1 + (epi == E_F32_ACC ? 1 : 0)));
   GK_LAUNCH(rw, k_splitk_reduce, dim3((unsigned)cdiv(MN / 4, 256)), dim3(256), 0, s, partial,
             tm.splits, M, N, (float*)C, ldc, epi == E_F32_ACC ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace gk
+
+namespace gk {
+
+template <int BM, int BN, bool TA, bool TB, int EPI>
+static void launch_batched_t(const GemmDesc& g, const TileMap& tm, int batch, hipStream_t s) {
+  const int nb = tm.tiles_m * tm.tiles_n;
+  const int grid = ((nb + 7) / 8) * 8;
+  Work w = gemm_work(g);
+  w.flops *= batch;
+  w.bytes *= batch;
+  GK_LAUNCH(w, (k_gemm_mfma<BM, BN, TA, TB, EPI>), dim3(grid, batch), dim3(256), 0, s, g.M, g.N,
+            g.K, (const bf16*)g.A, g.lda, (const bf16*)g.B, g.ldb, g.C, g.ldc, nullptr, tm,
+            nullptr);
+}
+
+template <int BM, int BN, int EPI>
+static void launch_batched_op(const GemmDesc& g, const TileMap& tm, int batch, hipStream_t s) {
+  if (g.op == OP_NT) launch_batched_t<BM, BN, false, false, EPI>(g, tm, batch, s);
+  else if (g.op == OP_NN) launch_batched_t<BM, BN, false, true, EPI>(g, tm, batch, s);
+  else launch_batched_t<BM, BN, true, true, EPI>(g, tm, batch, s);
+}
+
+// `batch` products of one shape with A, B, C advanced by sa, sb, sc elements
+// per product (bf16 operands, E_STORE or E_F32, no K split): the direct-to-
+// LDS kernel when the product suits it (K a multiple of 64, at least 2^32
+// multiply-adds and a round of 256 x 256 tiles over the batch), else the
+// 4-wave kernel, 256 x 128 tiles
+// when the batch gives two rounds of them, else 128 x 128.
+hipError_t gemm_batched(const GemmDesc& g, int batch, int64_t sa, int64_t sb, int64_t sc,
+                        hipStream_t s) {
+  if (batch < 1 || batch > 65535 || !mfma_gemm_supported(g) ||
+      (g.epi != E_STORE && g.epi != E_F32))
+    return hipErrorInvalidValue;
+  const bool TA = g.op == OP_TN, TB = g.op != OP_NT;
+  const double a_bytes = 2.0 * (TA ? g.K * g.lda : g.M * g.lda);
+  const double b_bytes = 2.0 * (TB ? g.K * g.ldb : g.N * g.ldb);
+  if (g.K % BK == 0 && a_bytes < 4294967295.0 && b_bytes < 4294967295.0 &&
+      (double)g.M * g.N * g.K * batch >= 4294967296.0 &&
+      cdiv(g.M, 256) * cdiv(g.N, 256) * batch >= 256) {
+    // the direct-to-LDS kernel, 256 x 256 tiles
+    TileMap tm;
+    tm.tiles_m = (int)cdiv(g.M, 256);
+    tm.tiles_n = (int)cdiv(g.N, 256);
+    tm.splits = 1;
+    tm.k_per_split = g.K;
+    tm.bs_a = sa;
+    tm.bs_b = sb;
+    tm.bs_c = sc;
+    const int nb = tm.tiles_m * tm.tiles_n;
+    const dim3 grid(((nb + 7) / 8) * 8, batch);
+    Work w = gemm_work(g);
+    w.flops *= batch;
+    w.bytes *= batch;
+#define GK_DMA_B(TA, TB, EPI)                                                                   \
+  GK_LAUNCH(w, (k_gemm_dma<256, 256, TA, TB, EPI>), grid, dim3(512), 0, s, g.M, g.N, g.K,       \
+            (const bf16*)g.A, g.lda, (const bf16*)g.B, g.ldb, g.C, g.ldc, nullptr, tm, nullptr)
+    if (g.epi == E_STORE) {
+      if (g.op == OP_NT) GK_DMA_B(false, false, E_STORE);
+      else if (g.op == OP_NN) GK_DMA_B(false, true, E_STORE);
+      else GK_DMA_B(true, true, E_STORE);
+    } else {
+      if (g.op == OP_NT) GK_DMA_B(false, false, E_F32);
+      else if (g.op == OP_NN) GK_DMA_B(false, true, E_F32);
+      else GK_DMA_B(true, true, E_F32);
+    }
+#undef GK_DMA_B
+    return hipGetLastError();
+  }
+  const bool big = cdiv(g.M, 256) * cdiv(g.N, 128) * batch >= 2 * 256;
+  TileMap tm;
+  tm.tiles_m = (int)cdiv(g.M, big ? 256 : 128);
+  tm.tiles_n = (int)cdiv(g.N, 128);
+  tm.splits = 1;
+  tm.k_per_split = cdiv(g.K, BK) * BK;
+  tm.bs_a = sa;
+  tm.bs_b = sb;
+  tm.bs_c = sc;
+  if (big) {
+    if (g.epi == E_STORE) launch_batched_op<256, 128, E_STORE>(g, tm, batch, s);
+    else launch_batched_op<256, 128, E_F32>(g, tm, batch, s);
+  } else {
+    if (g.epi == E_STORE) launch_batched_op<128, 128, E_STORE>(g, tm, batch, s);
+    else launch_batched_op<128, 128, E_F32>(g, tm, batch, s);
+  }
   return hipGetLastError();
 }
 

@@ -40,11 +40,15 @@ struct GemmDesc {
   const void* B; int64_t ldb;
   void* C; int64_t ldc;
   int epi;           // Epi
-  void* aux;         // RELU2: output a; DRELU2: input u   (ldc, dtype)
+  void* aux;         // DRELU2: input a = relu(u)^2 (ldc, dtype)
   void* scratch;     // optional fp32 split-K partials (fp32 epilogues only)
   size_t scratch_bytes;
 };
 hipError_t gemm(const GemmDesc& g, DType dt, hipStream_t s);
+// `batch` bf16 products of g's shape, A, B, C advanced by sa, sb, sc
+// elements per product; E_STORE or E_F32, no aux, no K split.
+hipError_t gemm_batched(const GemmDesc& g, int batch, int64_t sa, int64_t sb, int64_t sc,
+                        hipStream_t s);
 // scratch bytes gemm() would use for this bf16 product with an fp32 epilogue
 size_t gemm_scratch_bytes(int64_t M, int64_t N, int64_t K);
 
@@ -174,13 +178,15 @@ hipError_t gemm_fp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                     const void* B, int64_t ldb, int fb, const float* a_inv, const float* b_inv,
                     void* C, int64_t ldc, int epi, void* scratch, size_t scratch_bytes,
                     hipStream_t s);
-// Muon's Newton-Schulz orthogonalization of G [m, n] (dtype): X =
+// Muon's Newton-Schulz orthogonalization of `batch` matrices G [m, n]
+// (dtype, contiguous): X =
 // G / (||G||_F + eps), then per tuple (a, b, c) of coeffs (host, 3 steps
 // floats) X <- a X + X (b A + c A A), A = X^T X (tall) or the transposed
 // form (wide); result bf16 in x_out [m, n]; ws: polar_express_ws_bytes.
-size_t polar_express_ws_bytes(int64_t m, int64_t n);
-hipError_t polar_express(const void* g, int64_t m, int64_t n, DType dt, const float* coeffs,
-                         int steps, float eps, void* x_out, void* ws, hipStream_t s);
+size_t polar_express_ws_bytes(int batch, int64_t m, int64_t n);
+hipError_t polar_express(const void* g, int batch, int64_t m, int64_t n, DType dt,
+                         const float* coeffs, int steps, float eps, void* x_out, void* ws,
+                         hipStream_t s);
 hipError_t loss_reduce(const float* ell, int64_t N, float* loss_ws,
                        float* loss_out, int* flag, hipStream_t s);
 // acc[0] += sum ell, acc[1] += sum bytes[tgt]; if final, acc[2] = bpb

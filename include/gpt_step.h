@@ -262,22 +262,25 @@ int gpt_k_gemm_fp8(int64_t M, int64_t N, int64_t K, const void* A,
                    int32_t epilogue, void* scratch, size_t scratch_bytes,
                    hipStream_t s);
 
-/* Muon's orthogonalization of a matrix update (the nanochat walkthrough,
+/* Muon's orthogonalization of matrix updates (the nanochat walkthrough,
  * section "2. Muon optimizer": quintic Newton-Schulz, "Polar Express").
- *   g [m, n] (dtype, device): the update (momentum-averaged gradient).
+ *   g [batch, m, n] (dtype, device, contiguous): `batch` updates of one
+ *   shape (e.g. the same parameter of every layer), each orthogonalized on
+ *   its own; they share the launches.
  *   coeffs (host): steps tuples (a, b, c), 3 * steps floats; the page
  *   prints the first two of its five tuples, so the caller supplies them.
  *   X = g / (||g||_F + eps); per tuple A = X^T X, B = b A + c A A,
  *   X <- a X + X B (a matrix with fewer rows than columns is iterated in
  *   the transposed form A = X X^T, X <- a X + B X).  X, A and B are bf16
  *   between the products (fp32 accumulation).
- *   x_out [m, n] bf16 (device): the orthogonalized update.  ws: device,
- *   >= gpt_k_polar_express_ws_bytes(m, n).  Needs m and n multiples of 8,
- *   0 <= steps <= 64.  Deterministic. */
-size_t gpt_k_polar_express_ws_bytes(int64_t m, int64_t n);
-int gpt_k_polar_express(const void* g, int64_t m, int64_t n, int32_t dtype,
-                        const float* coeffs, int32_t steps, float eps,
-                        void* x_out, void* ws, size_t ws_bytes, hipStream_t s);
+ *   x_out [batch, m, n] bf16 (device).  ws: device, >=
+ *   gpt_k_polar_express_ws_bytes(batch, m, n).  Needs m and n multiples of
+ *   8, 1 <= batch <= 65535, 0 <= steps <= 64.  Deterministic. */
+size_t gpt_k_polar_express_ws_bytes(int32_t batch, int64_t m, int64_t n);
+int gpt_k_polar_express(const void* g, int32_t batch, int64_t m, int64_t n,
+                        int32_t dtype, const float* coeffs, int32_t steps,
+                        float eps, void* x_out, void* ws, size_t ws_bytes,
+                        hipStream_t s);
 
 /* cos/sin table, float2 [T, hd/2]: (cos, sin) of t * base^(-2j/hd),
  * evaluated in double precision. */

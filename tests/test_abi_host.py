@@ -138,15 +138,17 @@ def test_entry_points_reject_bad_pointers_before_launch():
     assert g8(64, 62, 128, A, 128, 0, A, 128, 0, A, A, A, 64, 0, None, 0, None) == -1
     assert L.gpt_k_gemm_fp8_scratch_bytes(256, 256, 8192) > 0
     assert L.gpt_k_gemm_fp8_scratch_bytes(256, 256, 100) == 0
-    # Newton-Schulz: g, m, n, dtype, coeffs, steps, eps, x_out, ws, ws_bytes
+    # Newton-Schulz: g, batch, m, n, dtype, coeffs, steps, eps, x_out, ws, ws_bytes
     ns = L.gpt_k_polar_express
-    wb = L.gpt_k_polar_express_ws_bytes(768, 768)
-    assert wb > 0 and L.gpt_k_polar_express_ws_bytes(770, 768) == 0
-    assert ns(A, 770, 768, 1, A, 5, 1e-7, A, A, wb, None) == -1
-    assert ns(A, 768, 768, 1, None, 5, 1e-7, A, A, wb, None) == -1
-    assert ns(A, 768, 768, 1, A, 65, 1e-7, A, A, wb, None) == -1
-    assert ns(A, 768, 768, 1, A, 5, -1.0, A, A, wb, None) == -1
-    assert ns(A, 768, 768, 1, A, 5, 1e-7, A, A, wb - 1, None) == -3
+    wb = L.gpt_k_polar_express_ws_bytes(12, 768, 768)
+    assert wb > L.gpt_k_polar_express_ws_bytes(1, 768, 768) > 0
+    assert L.gpt_k_polar_express_ws_bytes(1, 770, 768) == 0
+    assert ns(A, 12, 770, 768, 1, A, 5, 1e-7, A, A, wb, None) == -1
+    assert ns(A, 0, 768, 768, 1, A, 5, 1e-7, A, A, wb, None) == -1
+    assert ns(A, 12, 768, 768, 1, None, 5, 1e-7, A, A, wb, None) == -1
+    assert ns(A, 12, 768, 768, 1, A, 65, 1e-7, A, A, wb, None) == -1
+    assert ns(A, 12, 768, 768, 1, A, 5, -1.0, A, A, wb, None) == -1
+    assert ns(A, 12, 768, 768, 1, A, 5, 1e-7, A, A, wb - 1, None) == -3
     # decode attention: q, kc, vc, lens, o, lse, B, Tq, Tmax, H, Hkv, hd, W, bound,
     # scratch, scratch_bytes, dtype
     dec = L.gpt_k_attn_decode

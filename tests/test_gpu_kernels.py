@@ -808,34 +808,38 @@ NS_CLASSIC = (3.4445, -4.7750, 2.0315)
 
 
 @pytest.mark.parametrize("dt", [G.F32, G.BF16])
-@pytest.mark.parametrize("m,n,steps", [(64, 32, 2), (32, 96, 2), (768, 768, 5), (2304, 768, 5),
-                                       (768, 3072, 5), (136, 72, 0), (72, 136, 1)])
-def test_polar_express(m, n, steps, dt):
-    """The orthogonalized update against the oracle's bf16 iteration (the
-    page's form a X + X B; the kernels run X B' with B' = a I + b A + c A A,
-    same matrix, other rounding points) and against the exact iteration.
-    Tuples: the page's two, or the classic
-    quintic tuple five times (a convergent schedule: the page's two tuples
-    expect the three elided ones after them)."""
+@pytest.mark.parametrize("m,n,steps,batch", [(64, 32, 2, 1), (32, 96, 2, 3), (768, 768, 5, 2),
+                                             (2304, 768, 5, 1), (768, 3072, 5, 2),
+                                             (136, 72, 0, 2), (72, 136, 1, 1)])
+def test_polar_express(m, n, steps, batch, dt):
+    """The orthogonalized updates of a batch of matrices against the
+    oracle's bf16 iteration (the page's form a X + X B; the kernels run
+    X B' with B' = a I + b A + c A A, same matrix, other rounding points)
+    and against the exact iteration, each matrix on its own.  Tuples: the
+    page's two, or the classic quintic tuple five times (a convergent
+    schedule: the page's two tuples expect the three elided ones after
+    them)."""
     from oracle import muon
-    say("polar express", m, n, steps, dt)
+    say("polar express", m, n, steps, batch, dt)
     coeffs = NS_PAGE[:steps] if steps <= 2 else [NS_CLASSIC] * steps
-    g = np.random.default_rng(m * 7 + n).standard_normal((m, n)).astype(np.float32)
+    g = np.random.default_rng(m * 7 + n).standard_normal((batch, m, n)).astype(np.float32)
+    g[-1] *= 40.0                       # matrices of different norms share the launches
     if dt == G.BF16:
         g = O.round_bf16(g)
     tg = dev(g, tdtype(dt))
-    x = torch.empty(m, n, dtype=torch.bfloat16, device=DEV)
-    ws = torch.empty(G.k_polar_express_ws_bytes(m, n), dtype=torch.uint8, device=DEV)
-    G.k_polar_express(tg, m, n, dt, coeffs, muon.NS_EPS, x, ws)
+    x = torch.empty(batch, m, n, dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(G.k_polar_express_ws_bytes(m, n, batch), dtype=torch.uint8, device=DEV)
+    G.k_polar_express(tg, m, n, dt, coeffs, muon.NS_EPS, x, ws, batch=batch)
     torch.cuda.synchronize()
-    got = to_np(x)
-    ref_b = muon.polar_express(g, coeffs, bf16=True)
-    ref = muon.polar_express(g, coeffs)
-    say("  err vs bf16 oracle", rel_err(got, ref_b), "vs exact", rel_err(got, ref))
-    # against the exact iteration: the 2e-2 bar of bf16 results; against the
-    # bf16 emulation, whose own roundings are independent of the kernels',
-    # the sum of both deviations
-    assert rel_err(got, ref) < 2e-2
-    assert rel_err(got, ref_b) < 3e-2
-    if steps == 0:   # the normalised start only: one bf16 rounding
-        assert rel_err(got, ref) < 4e-3
+    for i in range(batch):
+        got = to_np(x[i])
+        ref_b = muon.polar_express(g[i], coeffs, bf16=True)
+        ref = muon.polar_express(g[i], coeffs)
+        say("  err vs bf16 oracle", rel_err(got, ref_b), "vs exact", rel_err(got, ref))
+        # against the exact iteration: the 2e-2 bar of bf16 results; against
+        # the bf16 emulation, whose own roundings are independent of the
+        # kernels', the sum of both deviations
+        assert rel_err(got, ref) < 2e-2
+        assert rel_err(got, ref_b) < 3e-2
+        if steps == 0:   # the normalised start only: one bf16 rounding
+            assert rel_err(got, ref) < 4e-3
