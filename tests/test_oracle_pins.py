@@ -656,3 +656,46 @@ def test_polar_express_orientation_scale_and_bf16():
     sv = np.linalg.svd(muon.polar_express(rng.standard_normal((64, 32)), classic),
                        compute_uv=False)
     assert sv.min() > 0.6 and sv.max() < 1.25
+
+
+def test_adamw_matches_torch():
+    """Three AdamW steps equal torch.optim.AdamW (CPU, float64) on the same
+    parameter and gradients, weights, moments and all."""
+    from oracle import muon
+    rng = np.random.default_rng(4)
+    w0 = rng.standard_normal((6, 5))
+    grads = [rng.standard_normal((6, 5)) for _ in range(3)]
+    hp = dict(lr=3e-3, beta1=0.8, beta2=0.95, eps=1e-10, wd=0.1)
+    p = torch.tensor(w0, requires_grad=True)
+    opt = torch.optim.AdamW([p], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                            weight_decay=hp["wd"])
+    w, m, v = w0, np.zeros_like(w0), np.zeros_like(w0)
+    for k, g in enumerate(grads, 1):
+        p.grad = torch.tensor(g)
+        opt.step()
+        w, m, v = muon.adamw(w, g, m, v, k, **hp)
+    np.testing.assert_allclose(w, p.detach().numpy(), rtol=1e-13, atol=1e-15)
+    st = opt.state[p]
+    np.testing.assert_allclose(m, st["exp_avg"].numpy(), rtol=1e-13)
+    np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-13)
+
+
+def test_muon_momentum_and_update_closed_forms():
+    """A constant gradient c gives momentum c (1 - beta^k) after k steps from
+    zero, and the Nesterov update c (1 - beta^(k+1)); without Nesterov the
+    update is the momentum.  The parameter step with no decay moves W by
+    exactly -lr X; with decay it first scales W by 1 - lr wd."""
+    from oracle import muon
+    c = np.full((3, 4), 2.5)
+    m = np.zeros_like(c)
+    beta = 0.9
+    for k in range(1, 6):
+        m, u = muon.muon_momentum(c, m, beta)
+        np.testing.assert_allclose(m, c * (1 - beta ** k), rtol=1e-14)
+        np.testing.assert_allclose(u, c * (1 - beta ** (k + 1)), rtol=1e-14)
+    m2, u2 = muon.muon_momentum(c, m, beta, nesterov=False)
+    np.testing.assert_array_equal(u2, m2)
+    w = np.arange(12.0).reshape(3, 4)
+    x = np.ones((3, 4))
+    np.testing.assert_allclose(muon.muon_update(w, x, 0.02, 0.0), w - 0.02, rtol=1e-15)
+    np.testing.assert_allclose(muon.muon_update(w, x, 0.02, 0.5), w * 0.99 - 0.02, rtol=1e-15)
