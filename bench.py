@@ -4,6 +4,7 @@
     python bench.py --workload decode [--config d12gqa] [--decode-batch 64]
     python bench.py --workload fp8 [--config d24]
     python bench.py --workload muon [--config d12]
+    python bench.py --workload optim [--config d12]
 
 Times K forward+backward steps of the d12 model (12 layers, width 768, 6
 heads of 128, vocab 32768, 16 rows of 2048 tokens, 'SSSL' windows 1024/2048,
@@ -500,12 +501,55 @@ def matrix_shapes(cfg):
     return [(fo, fi) for fi, fo in linear_shapes(cfg)] * cfg["n_layer"]
 
 
+def cpu_muon_baseline(shapes, coeffs):
+    """The oracle's Newton-Schulz iteration (numpy fp64) on one block's
+    matrices, scaled to all of them: ms per optimizer step."""
+    import numpy as np
+    from oracle import muon
+    rng = np.random.default_rng(2)
+    t0 = time.perf_counter()
+    for m, n in shapes[:4]:
+        muon.polar_express(rng.standard_normal((m, n)), coeffs)
+    t = time.perf_counter() - t0
+    threads = os.environ.get("OMP_NUM_THREADS")
+    cores = int(threads) if threads else len(os.sched_getaffinity(0))
+    return {"value": round(t * len(shapes) / 4 * 1e3, 1), "unit": "ms/step", "cores": cores,
+            "kind": "oracle",
+            "sample": f"one block's 4 matrices (numpy fp64, {t:.2f} s measured), time scaled "
+                      f"x{len(shapes) // 4}"}
+
+
+def cpu_optim_baseline(muon_shapes, adam_sizes, coeffs):
+    """The oracle's optimizer step (Muon momentum, Newton-Schulz and update
+    for one block's matrices; AdamW for 2^20 parameters), scaled to the
+    whole model: ms per step."""
+    import numpy as np
+    from oracle import muon
+    rng = np.random.default_rng(3)
+    t0 = time.perf_counter()
+    for m, n in muon_shapes[:4]:
+        g = rng.standard_normal((m, n))
+        _, u = muon.muon_momentum(g, np.zeros_like(g), 0.95)
+        muon.muon_update(np.zeros_like(g), muon.polar_express(u, coeffs), 0.02, 0.0)
+    t_muon = time.perf_counter() - t0
+    k = 1 << 20
+    g = rng.standard_normal(k)
+    t0 = time.perf_counter()
+    muon.adamw(np.zeros(k), g, np.zeros(k), np.zeros(k), 1, 3e-3, 0.8, 0.95, 1e-10, 0.0)
+    t_adam = time.perf_counter() - t0
+    total = t_muon * len(muon_shapes) / 4 + t_adam * sum(adam_sizes) / k
+    threads = os.environ.get("OMP_NUM_THREADS")
+    cores = int(threads) if threads else len(os.sched_getaffinity(0))
+    return {"value": round(total * 1e3, 1), "unit": "ms/step", "cores": cores, "kind": "oracle",
+            "sample": f"one block's 4 matrices through Muon ({t_muon:.2f} s) and 2^20 AdamW "
+                      f"parameters ({t_adam:.3f} s), times scaled to the model"}
+
+
 def bench_muon(a, torch, G):
     """Newton-Schulz orthogonalization (5 quintic steps) of a random fp32
     update for every block matrix of the model: one batched call per
     parameter shape (that parameter of every layer)."""
     import gptinputs as gi
-    from oracle.muon import ns_flops
     cfg = gi.preset(a.config)
     shapes = matrix_shapes(cfg)
     groups = sorted(set(shapes))
@@ -528,7 +572,9 @@ def bench_muon(a, torch, G):
     torch.cuda.synchronize()
     assert all(torch.isfinite(o.float()).all() for o in outs)
     ms = time_events(step, a.steps, torch) * 1e3
-    flops = sum(ns_flops(m, n, steps) for m, n in shapes)
+    # per step: X^T X and X B' (2 m n^2 each) and A A (2 n^3), n the smaller side
+    flops = sum(steps * (4.0 * max(m, n) * min(m, n) ** 2 + 2.0 * min(m, n) ** 3)
+                for m, n in shapes)
     log(f"muon: {len(shapes)} matrices, {ms:.3f} ms per step, {flops / ms / 1e9:,.0f} TFLOP/s")
     prof = kernel_profile(step, a.prof_steps, torch, G) if a.prof_steps > 0 else []
     for r in prof[:10]:
@@ -537,20 +583,7 @@ def bench_muon(a, torch, G):
         log(f"  {r['ms_per_step']:7.3f} ms/step {r['launches_per_step']:5.0f} x "
             f"{r['avg_launch_ms'] * 1e3:8.1f} us  {rate:>16}  {r['kernel']}")
     roof = roofline_of(prof[0], ms) if prof else None
-    cpu = None
-    if not a.no_cpu:
-        import numpy as np
-        from oracle import muon
-        rng = np.random.default_rng(2)
-        t0 = time.perf_counter()
-        for m, n in shapes[:4]:
-            muon.polar_express(rng.standard_normal((m, n)), coeffs)
-        dt = (time.perf_counter() - t0) * (len(shapes) / 4)
-        threads = os.environ.get("OMP_NUM_THREADS")
-        cores = int(threads) if threads else len(os.sched_getaffinity(0))
-        cpu = {"value": round(dt * 1e3, 1), "unit": "ms/step", "cores": cores, "kind": "oracle",
-               "sample": f"one block's 4 matrices (numpy fp64, {dt / (len(shapes) / 4):.2f} s "
-                         f"measured), time scaled x{len(shapes) // 4}"}
+    cpu = None if a.no_cpu else cpu_muon_baseline(shapes, coeffs)
     out = {
         "metric": MUON_METRIC, "value": round(ms, 4), "unit": "ms/step", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
@@ -561,6 +594,96 @@ def bench_muon(a, torch, G):
                                f"Newton-Schulz steps {NS_TUPLE}", "parallelism": "single GPU"},
         "tflops": round(flops / ms / 1e9, 1), "ns_flops_per_step": flops,
         "roofline": roof, "cpu_baseline": cpu,
+        "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
+                    for r in prof],
+    }
+    print(json.dumps(out), flush=True)
+
+
+OPTIM_METRIC = "optimizer step (Muon for block matrices, AdamW for the rest): ms/step"
+
+
+def bench_optim(a, torch, G):
+    """One optimizer step over every parameter of the model: Muon (momentum,
+    batched Newton-Schulz per parameter shape, update with a bf16 copy) for
+    the block matrices, AdamW for the embeddings, lm_head, value embeddings
+    and gates; fp32 masters, gradients and states resident in HBM."""
+    import gptinputs as gi
+    cfg = gi.preset(a.config)
+    gc = G.make_config(cfg)
+    L = cfg["n_layer"]
+    n_total = G.param_count(gc)
+    D, F, V = cfg["d_model"], cfg["mlp_mult"] * cfg["d_model"], cfg["vocab"]
+    H, Hkv, hd, C = cfg["n_head"], cfg["n_kv_head"], cfg["head_dim"], cfg["ve_gate_channels"]
+    shape_of = {G.P_WQKV: ((H + 2 * Hkv) * hd, D), G.P_WO: (D, H * hd), G.P_WFC: (F, D),
+                G.P_WPROJ: (D, F), G.P_VE: (V, Hkv * hd), G.P_WG: (Hkv, C)}
+    groups = {}
+    adam = [(G.param_offset(gc, G.P_WTE), (V, D)), (G.param_offset(gc, G.P_WLM), (V, D))]
+    for l in range(L):
+        for p in (G.P_WQKV, G.P_WO, G.P_WFC, G.P_WPROJ):
+            groups.setdefault(p, []).append((G.param_offset(gc, p, l), shape_of[p]))
+        for p in (G.P_VE, G.P_WG):
+            off = G.param_offset(gc, p, l)
+            if off >= 0:
+                adam.append((off, shape_of[p]))
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg["seed"])
+    w = torch.randn(n_total, generator=g, device=dev) * 0.02
+    w16 = w.bfloat16()
+    grad = torch.randn(n_total, generator=g, device=dev) * 1e-3
+    mom = torch.zeros(n_total, device=dev)
+    m1, m2 = torch.zeros(n_total, device=dev), torch.zeros(n_total, device=dev)
+    stage = {k: torch.empty(len(v), *v[0][1], device=dev) for k, v in groups.items()}
+    xs = {k: torch.empty(len(v), *v[0][1], dtype=torch.bfloat16, device=dev)
+          for k, v in groups.items()}
+    ws = torch.empty(max(G.k_polar_express_ws_bytes(v[0][1][0], v[0][1][1], len(v))
+                         for v in groups.values()), dtype=torch.uint8, device=dev)
+    coeffs = [NS_TUPLE] * 5
+
+    def numel(shape):
+        return int(math.prod(shape))
+
+    def step():
+        for k, v in groups.items():
+            m, n = v[0][1]
+            for i, (off, shape) in enumerate(v):
+                G.k_muon_momentum(grad[off:], mom[off:], stage[k][i], m * n, 0.95, True, G.F32)
+            G.k_polar_express(stage[k], m, n, G.F32, coeffs, 1e-7, xs[k], ws, batch=len(v))
+            lr = 0.02 * max(1.0, m / n) ** 0.5
+            for i, (off, shape) in enumerate(v):
+                G.k_muon_update(w[off:], xs[k][i], m * n, lr, 0.0, w16[off:])
+        for off, shape in adam:
+            G.k_adamw(w[off:], grad[off:], m1[off:], m2[off:], numel(shape), 1, 3e-3, 0.8, 0.95,
+                      1e-10, 0.0, w16[off:])
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert torch.isfinite(w).all()
+    ms = time_events(step, a.steps, torch) * 1e3
+    n_muon = sum(numel(s) for v in groups.values() for _, s in v)
+    log(f"optimizer step {ms:.3f} ms: {n_muon:,} Muon + {n_total - n_muon:,} AdamW parameters")
+    prof = kernel_profile(step, a.prof_steps, torch, G) if a.prof_steps > 0 else []
+    for r in prof[:10]:
+        rate = (f"{r['tflops']:7.1f} TFLOP/s" if r["tflops"] else
+                f"{r['gbps']:7.0f} GB/s" if r["gbps"] else "")
+        log(f"  {r['ms_per_step']:7.3f} ms/step {r['launches_per_step']:5.0f} x "
+            f"{r['avg_launch_ms'] * 1e3:8.1f} us  {rate:>16}  {r['kernel']}")
+    roof = roofline_of(prof[0], ms) if prof else None
+    out = {
+        "metric": OPTIM_METRIC, "value": round(ms, 4), "unit": "ms/step", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "fp32+bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1e-3) gradients)",
+        "config": {"workload": f"{a.config} optimizer step: {n_muon} Muon parameters in "
+                               f"{len(groups)} shape groups of {L} (momentum 0.95 Nesterov, 5 "
+                               f"quintic Newton-Schulz steps), {n_total - n_muon} AdamW "
+                               "parameters", "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": None if a.no_cpu else cpu_optim_baseline(
+            [s for v in groups.values() for _, s in v[:1]] * L,
+            [numel(s) for _, s in adam], coeffs),
         "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
                     for r in prof],
     }
@@ -580,10 +703,12 @@ def main():
     ap.add_argument("--shapes", action="store_true",
                     help="also time every product / attention shape alone")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--workload", choices=("train", "decode", "fp8", "muon"), default="train",
+    ap.add_argument("--workload", choices=("train", "decode", "fp8", "muon", "optim"),
+                    default="train",
                     help="train: the fwd+bwd step; decode: KV-cache decode attention; fp8: the "
                          "step's linear layers as FP8 linear layers; muon: Muon's "
-                         "orthogonalization of every matrix update")
+                         "orthogonalization of every matrix update; optim: the whole optimizer "
+                         "step")
     ap.add_argument("--decode-batch", type=int, default=64,
                     help="sequences sampled in parallel (decode workload)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -608,6 +733,10 @@ def main():
     if a.workload == "decode":
         a.config = a.config or "d12gqa"
         bench_decode(a, torch, G)
+        return
+    if a.workload == "optim":
+        a.config = a.config or "d12"
+        bench_optim(a, torch, G)
         return
     if a.workload == "muon":
         a.config = a.config or "d12"

@@ -94,6 +94,10 @@ _SIGS = {
     "gpt_k_polar_express_ws_bytes": (_sz, [_i32, _i64, _i64]),
     "gpt_k_polar_express": (C.c_int, [_vp, _i32, _i64, _i64, _i32, _vp, _i32, _f32, _vp, _vp,
                                       _sz, _vp]),
+    "gpt_k_muon_momentum": (C.c_int, [_vp, _vp, _vp, _i64, _f32, _i32, _i32, _vp]),
+    "gpt_k_muon_update": (C.c_int, [_vp, _vp, _i64, _f32, _f32, _vp, _vp]),
+    "gpt_k_adamw": (C.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _f32, _f32, _f32, _f32, _f32, _vp,
+                              _vp]),
     "gpt_k_ce": (C.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp]),
     "gpt_k_lm_ce_scratch_bytes": (_sz, [_i64, _i32]),
     "gpt_k_embed_fwd": (C.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp]),
@@ -297,6 +301,20 @@ def k_polar_express(g, m, n, dtype, coeffs, eps, x_out, ws, batch=1, stream=None
     _check(lib().gpt_k_polar_express(_ptr(g), batch, m, n, dtype, C.cast(arr, C.c_void_p),
                                      len(coeffs), eps, _ptr(x_out), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def k_muon_momentum(grad, mom, u, n, beta, nesterov, u_dtype, stream=None):
+    _check(lib().gpt_k_muon_momentum(_ptr(grad), _ptr(mom), _ptr(u), n, beta, int(nesterov),
+                                     u_dtype, _stream(stream)))
+
+
+def k_muon_update(w, x, n, lr, wd, w_bf16=None, stream=None):
+    _check(lib().gpt_k_muon_update(_ptr(w), _ptr(x), n, lr, wd, _ptr(w_bf16), _stream(stream)))
+
+
+def k_adamw(w, grad, m, v, n, step, lr, beta1, beta2, eps, wd, w_bf16=None, stream=None):
+    _check(lib().gpt_k_adamw(_ptr(w), _ptr(grad), _ptr(m), _ptr(v), n, step, lr, beta1, beta2,
+                             eps, wd, _ptr(w_bf16), _stream(stream)))
 
 
 def k_embed_fwd(tokens, B, T, wte, V, D, x, dtype, stream=None):

@@ -718,6 +718,44 @@ int gpt_k_polar_express(const void* g, int32_t batch, int64_t m, int64_t n, int3
   return GPT_OK;
 }
 
+static int optim_ptrs(std::initializer_list<const void*> ps, int64_t n) {
+  int st;
+  if ((st = check_ptrs(ps))) return st;
+  if (n < 4 || n % 4) return fail(GPT_ERR_INVALID_ARG, "n must be a positive multiple of 4");
+  return GPT_OK;
+}
+
+int gpt_k_muon_momentum(const float* grad, float* mom, void* u, int64_t n, float beta,
+                        int32_t nesterov, int32_t u_dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(u_dtype)) || (st = optim_ptrs({grad, mom, u}, n))) return st;
+  if (!(beta >= 0.f && beta < 1.f)) return fail(GPT_ERR_INVALID_ARG, "beta outside [0, 1)");
+  KERNEL_TRY(gk::muon_momentum(grad, mom, u, n, beta, nesterov ? 1 : 0, (gk::DType)u_dtype, s));
+  return GPT_OK;
+}
+
+int gpt_k_muon_update(float* w, const void* x, int64_t n, float lr, float wd, void* w_bf16,
+                      hipStream_t s) {
+  int st;
+  if ((st = optim_ptrs({w, x}, n))) return st;
+  if (w_bf16 && !aligned16(w_bf16)) return fail(GPT_ERR_MISALIGNED, "w_bf16 misaligned");
+  KERNEL_TRY(gk::muon_update(w, x, n, lr, wd, w_bf16, s));
+  return GPT_OK;
+}
+
+int gpt_k_adamw(float* w, const float* grad, float* m, float* v, int64_t n, int32_t step,
+                float lr, float beta1, float beta2, float eps, float wd, void* w_bf16,
+                hipStream_t s) {
+  int st;
+  if ((st = optim_ptrs({w, grad, m, v}, n))) return st;
+  if (w_bf16 && !aligned16(w_bf16)) return fail(GPT_ERR_MISALIGNED, "w_bf16 misaligned");
+  if (step < 1) return fail(GPT_ERR_INVALID_ARG, "step counts from 1");
+  if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f))
+    return fail(GPT_ERR_INVALID_ARG, "betas outside [0, 1)");
+  KERNEL_TRY(gk::adamw(w, grad, m, v, n, step, lr, beta1, beta2, eps, wd, w_bf16, s));
+  return GPT_OK;
+}
+
 int gpt_k_rope_table(float* cs, int32_t T, int32_t hd, float base, hipStream_t s) {
   int st;
   if ((st = check_ptrs({cs}))) return st;

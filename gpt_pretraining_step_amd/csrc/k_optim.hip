@@ -1,0 +1,143 @@
+// The elementwise parts of the optimizer step (the nanochat walkthrough, "2.
+// Muon optimizer": Muon for the block matrices, AdamW for embeddings,
+// lm_head and value embeddings).  Muon: momentum with the Nesterov
+// look-ahead feeding the orthogonalization, then W <- W (1 - lr wd) - lr X;
+// AdamW with bias correction.  fp32 master weights, optionally written back
+// as the bf16 copy the step reads.  HBM-bound streams of 4-float vectors.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace gk {
+
+namespace {
+__device__ __forceinline__ void store4(float* p, float4 v) { *(float4*)p = v; }
+__device__ __forceinline__ void store4(bf16* p, float4 v) {
+  uint2 o;
+  o.x = pack2bf(v.x, v.y);
+  o.y = pack2bf(v.z, v.w);
+  *(uint2*)p = o;
+}
+__device__ __forceinline__ float4 load4(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ float4 load4(const bf16* p) {
+  const uint2 u = *(const uint2*)p;
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+}
+}  // namespace
+
+// M <- beta M + (1 - beta) G; U = (1 - beta) G + beta M (Nesterov) or M
+template <typename TU>
+__global__ __launch_bounds__(256) void k_muon_momentum(const float* __restrict__ g,
+                                                       float* __restrict__ mom,
+                                                       TU* __restrict__ u, int64_t n4, float beta,
+                                                       int nesterov) {
+  const float omb = 1.f - beta;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    const float4 gv = load4(g + 4 * i);
+    float4 m = load4(mom + 4 * i);
+    m.x = fmaf(beta, m.x, omb * gv.x);
+    m.y = fmaf(beta, m.y, omb * gv.y);
+    m.z = fmaf(beta, m.z, omb * gv.z);
+    m.w = fmaf(beta, m.w, omb * gv.w);
+    store4(mom + 4 * i, m);
+    float4 o = m;
+    if (nesterov) {
+      o.x = fmaf(beta, m.x, omb * gv.x);
+      o.y = fmaf(beta, m.y, omb * gv.y);
+      o.z = fmaf(beta, m.z, omb * gv.z);
+      o.w = fmaf(beta, m.w, omb * gv.w);
+    }
+    store4(u + 4 * i, o);
+  }
+}
+
+// W <- W (1 - lr wd) - lr X; optional bf16 copy
+__global__ __launch_bounds__(256) void k_muon_update(float* __restrict__ w,
+                                                     const bf16* __restrict__ x, int64_t n4,
+                                                     float lr, float decay,
+                                                     bf16* __restrict__ w16) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    float4 v = load4(w + 4 * i);
+    const float4 xv = load4(x + 4 * i);
+    v.x = fmaf(-lr, xv.x, v.x * decay);
+    v.y = fmaf(-lr, xv.y, v.y * decay);
+    v.z = fmaf(-lr, xv.z, v.z * decay);
+    v.w = fmaf(-lr, xv.w, v.w * decay);
+    store4(w + 4 * i, v);
+    if (w16) store4(w16 + 4 * i, v);
+  }
+}
+
+// AdamW: m, v moments; bc1 = 1 - beta1^t, bc2 = 1 - beta2^t
+__global__ __launch_bounds__(256) void k_adamw(float* __restrict__ w, const float* __restrict__ g,
+                                               float* __restrict__ m, float* __restrict__ v,
+                                               int64_t n4, float lr, float b1, float b2,
+                                               float eps, float decay, float bc1, float bc2,
+                                               bf16* __restrict__ w16) {
+  const float r1 = 1.f / bc1, r2 = 1.f / bc2;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    const float4 gv = load4(g + 4 * i);
+    float4 mv = load4(m + 4 * i), vv = load4(v + 4 * i), wv = load4(w + 4 * i);
+    float* mp = &mv.x;
+    float* vp = &vv.x;
+    float* wp = &wv.x;
+    const float* gp = &gv.x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mp[e] = fmaf(b1, mp[e], (1.f - b1) * gp[e]);
+      vp[e] = fmaf(b2, vp[e], (1.f - b2) * gp[e] * gp[e]);
+      const float den = sqrtf(vp[e] * r2) + eps;
+      wp[e] = fmaf(-lr, (mp[e] * r1) / den, wp[e] * decay);
+    }
+    store4(m + 4 * i, mv);
+    store4(v + 4 * i, vv);
+    store4(w + 4 * i, wv);
+    if (w16) store4(w16 + 4 * i, wv);
+  }
+}
+
+namespace {
+unsigned blocks_for(int64_t n4) {
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(2048, cdiv(n4, 256)));
+}
+}
+
+hipError_t muon_momentum(const float* g, float* mom, void* u, int64_t n, float beta, int nesterov,
+                         DType u_dt, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  const Work w(0.0, n * (4.0 + 8.0 + (u_dt == BF16 ? 2.0 : 4.0)));
+  if (u_dt == BF16)
+    GK_LAUNCH(w, k_muon_momentum<bf16>, dim3(blocks_for(n4)), dim3(256), 0, s, g, mom, (bf16*)u,
+              n4, beta, nesterov);
+  else
+    GK_LAUNCH(w, k_muon_momentum<float>, dim3(blocks_for(n4)), dim3(256), 0, s, g, mom,
+              (float*)u, n4, beta, nesterov);
+  return hipGetLastError();
+}
+
+hipError_t muon_update(float* w, const void* x, int64_t n, float lr, float wd, void* w16,
+                       hipStream_t s) {
+  const int64_t n4 = n / 4;
+  const Work wk(0.0, n * (8.0 + 2.0 + (w16 ? 2.0 : 0.0)));
+  GK_LAUNCH(wk, k_muon_update, dim3(blocks_for(n4)), dim3(256), 0, s, w, (const bf16*)x, n4, lr,
+            1.f - lr * wd, (bf16*)w16);
+  return hipGetLastError();
+}
+
+hipError_t adamw(float* w, const float* g, float* m, float* v, int64_t n, int step, float lr,
+                 float b1, float b2, float eps, float wd, void* w16, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  const float bc1 = (float)(1.0 - pow((double)b1, step));
+  const float bc2 = (float)(1.0 - pow((double)b2, step));
+  const Work wk(0.0, n * (4.0 + 3 * 8.0 + (w16 ? 2.0 : 0.0)));
+  GK_LAUNCH(wk, k_adamw, dim3(blocks_for(n4)), dim3(256), 0, s, w, g, m, v, n4, lr, b1, b2, eps,
+            1.f - lr * wd, bc1, bc2, (bf16*)w16);
+  return hipGetLastError();
+}
+
+}  // namespace gk

@@ -187,6 +187,16 @@ size_t polar_express_ws_bytes(int batch, int64_t m, int64_t n);
 hipError_t polar_express(const void* g, int batch, int64_t m, int64_t n, DType dt,
                          const float* coeffs, int steps, float eps, void* x_out, void* ws,
                          hipStream_t s);
+// Optimizer elementwise steps (n a multiple of 4, 16-byte aligned):
+// Muon momentum M <- beta M + (1 - beta) G, U = Nesterov look-ahead or M;
+// Muon step W <- W (1 - lr wd) - lr X (X bf16); AdamW (step counts from 1).
+// w16: optional bf16 copy of the updated weights.
+hipError_t muon_momentum(const float* g, float* mom, void* u, int64_t n, float beta, int nesterov,
+                         DType u_dt, hipStream_t s);
+hipError_t muon_update(float* w, const void* x, int64_t n, float lr, float wd, void* w16,
+                       hipStream_t s);
+hipError_t adamw(float* w, const float* g, float* m, float* v, int64_t n, int step, float lr,
+                 float b1, float b2, float eps, float wd, void* w16, hipStream_t s);
 hipError_t loss_reduce(const float* ell, int64_t N, float* loss_ws,
                        float* loss_out, int* flag, hipStream_t s);
 // acc[0] += sum ell, acc[1] += sum bytes[tgt]; if final, acc[2] = bpb

@@ -282,6 +282,28 @@ int gpt_k_polar_express(const void* g, int32_t batch, int64_t m, int64_t n,
                         float eps, void* x_out, void* ws, size_t ws_bytes,
                         hipStream_t s);
 
+/* The elementwise parts of the optimizer step (the nanochat walkthrough,
+ * section "2. Muon optimizer": Muon for the block matrices, AdamW for
+ * embeddings, lm_head and value embeddings).  All buffers device, 16-byte
+ * aligned, n elements (a multiple of 4); fp32 master weights, w_bf16 an
+ * optional bf16 copy of the updated weights (the step's parameters).
+ *   gpt_k_muon_momentum: mom <- beta mom + (1 - beta) grad, then
+ *     u = (1 - beta) grad + beta mom (Nesterov) or mom, as u_dtype (the
+ *     input of gpt_k_polar_express).
+ *   gpt_k_muon_update: w <- w (1 - lr wd) - lr x, x the orthogonalized
+ *     update (bf16); lr carries any shape factor.
+ *   gpt_k_adamw: m <- b1 m + (1 - b1) g, v <- b2 v + (1 - b2) g^2,
+ *     w <- w (1 - lr wd) - lr (m / (1 - b1^step)) / (sqrt(v / (1 - b2^step))
+ *     + eps); step counts from 1. */
+int gpt_k_muon_momentum(const float* grad, float* mom, void* u, int64_t n,
+                        float beta, int32_t nesterov, int32_t u_dtype,
+                        hipStream_t s);
+int gpt_k_muon_update(float* w, const void* x, int64_t n, float lr, float wd,
+                      void* w_bf16, hipStream_t s);
+int gpt_k_adamw(float* w, const float* grad, float* m, float* v, int64_t n,
+                int32_t step, float lr, float beta1, float beta2, float eps,
+                float wd, void* w_bf16, hipStream_t s);
+
 /* cos/sin table, float2 [T, hd/2]: (cos, sin) of t * base^(-2j/hd),
  * evaluated in double precision. */
 int gpt_k_rope_table(float* cs, int32_t T, int32_t hd, float base,

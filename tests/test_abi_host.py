@@ -149,6 +149,14 @@ def test_entry_points_reject_bad_pointers_before_launch():
     assert ns(A, 12, 768, 768, 1, A, 65, 1e-7, A, A, wb, None) == -1
     assert ns(A, 12, 768, 768, 1, A, 5, -1.0, A, A, wb, None) == -1
     assert ns(A, 12, 768, 768, 1, A, 5, 1e-7, A, A, wb - 1, None) == -3
+    # optimizer elementwise steps
+    assert L.gpt_k_muon_momentum(A, A, A, 6, 0.9, 1, 0, None) == -1
+    assert L.gpt_k_muon_momentum(A, A, A, 8, 1.0, 1, 0, None) == -1
+    assert L.gpt_k_muon_momentum(A, A, A, 8, 0.9, 1, 7, None) == -1
+    assert L.gpt_k_muon_update(A, None, 8, 0.1, 0.0, None, None) == -1
+    assert L.gpt_k_muon_update(A, A, 8, 0.1, 0.0, C.c_void_p(0x1004), None) == -4
+    assert L.gpt_k_adamw(A, A, A, A, 8, 0, 1e-3, 0.9, 0.95, 1e-8, 0.0, None, None) == -1
+    assert L.gpt_k_adamw(A, A, A, A, 8, 1, 1e-3, 1.5, 0.95, 1e-8, 0.0, None, None) == -1
     # decode attention: q, kc, vc, lens, o, lse, B, Tq, Tmax, H, Hkv, hd, W, bound,
     # scratch, scratch_bytes, dtype
     dec = L.gpt_k_attn_decode

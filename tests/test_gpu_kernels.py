@@ -843,3 +843,47 @@ def test_polar_express(m, n, steps, batch, dt):
         assert rel_err(got, ref_b) < 3e-2
         if steps == 0:   # the normalised start only: one bf16 rounding
             assert rel_err(got, ref) < 4e-3
+
+
+# ------------------------------------------------------ optimizer step
+@pytest.mark.parametrize("n", [4096, 1_000_004])
+def test_optimizer_elementwise(n):
+    """Muon momentum (Nesterov and plain), the Muon parameter step and AdamW
+    against the oracle over three steps (fp32 arithmetic against fp64:
+    1e-5 relative), bf16 copies equal to the rounded fp32 weights."""
+    from oracle import muon
+    say("optim", n)
+    rng = np.random.default_rng(n % 97)
+    w0 = rng.standard_normal(n).astype(np.float32)
+    grads = [rng.standard_normal(n).astype(np.float32) for _ in range(3)]
+    xs = [O.round_bf16(rng.standard_normal(n).astype(np.float32) * 0.02) for _ in range(3)]
+    tw = dev(w0, torch.float32)
+    tw16 = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    tmom = torch.zeros(n, dtype=torch.float32, device=DEV)
+    tu = torch.empty(n, dtype=torch.float32, device=DEV)
+    tu16 = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    aw, am, av = dev(w0, torch.float32), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+    w, mom = w0.astype(np.float64), np.zeros(n)
+    a_w, a_m, a_v = w0.astype(np.float64), np.zeros(n), np.zeros(n)
+    hp = dict(lr=3e-3, beta1=0.8, beta2=0.95, eps=1e-10, wd=0.01)
+    for k in range(3):
+        tg = dev(grads[k], torch.float32)
+        G.k_muon_momentum(tg, tmom, tu, n, 0.95, True, G.F32)
+        mom, u = muon.muon_momentum(grads[k], mom, 0.95)
+        torch.cuda.synchronize()
+        assert rel_err(to_np(tu), u) < 1e-6
+        # the plain form on a copy of the updated momentum M gives beta M +
+        # (1 - beta) G: the Nesterov value above, here rounded to bf16
+        G.k_muon_momentum(tg, tmom.clone(), tu16, n, 0.95, False, G.BF16)
+        G.k_muon_update(tw, dev(xs[k], torch.bfloat16), n, 0.02, 0.1, tw16)
+        w = muon.muon_update(w, xs[k], 0.02, 0.1)
+        G.k_adamw(aw, tg, am, av, n, k + 1, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                  hp["wd"])
+        a_w, a_m, a_v = muon.adamw(a_w, grads[k], a_m, a_v, k + 1, **hp)
+        torch.cuda.synchronize()
+        assert rel_err(to_np(tu16), O.round_bf16(u.astype(np.float32))) < 8e-3
+        assert rel_err(to_np(tw), w) < 1e-5
+        np.testing.assert_array_equal(to_np(tw16), O.round_bf16(tw.cpu().numpy()))
+        assert rel_err(to_np(aw), a_w) < 1e-5
+        assert rel_err(to_np(am), a_m) < 1e-5 and rel_err(to_np(av), a_v) < 1e-5
+        assert rel_err(to_np(tmom), mom) < 1e-6
