@@ -208,8 +208,11 @@ Plan make_plan(const Model& m, int mode) {
     size_t gs = 0;
     const int64_t HD = (int64_t)m.H * m.hd;
     const int64_t shapes[5][2] = {{m.V, m.D}, {m.D, m.F}, {m.F, m.D}, {m.D, HD}, {m.QKV, m.D}};
-    if (m.dt == gk::BF16)
+    if (m.dt == gk::BF16) {
       for (auto& sh : shapes) gs = std::max(gs, gk::gemm_scratch_bytes(sh[0], sh[1], N));
+      // also holds the transposed copy of W_proj for the MLP backward
+      gs = std::max(gs, (size_t)m.F * m.D * 2);
+    }
     p.gemm_scr_bytes = gs;
     p.gemm_scr = take(gs);
   } else {
@@ -380,8 +383,17 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
     g = gk::GemmDesc{gk::OP_TN, m.D, m.F, N, dx, m.D, a, m.F, grads + pl.wproj[l], m.F, wepi,
                      nullptr, gscr, gscr_bytes};
     HIP_TRY(gk::gemm(g, dt, s));
-    g = gk::GemmDesc{gk::OP_NN, N, m.F, m.D, dx, m.D, elem(params, pl.wproj[l], es), m.F, du,
-                     m.F, gk::E_DRELU2, const_cast<void*>(a)};
+    if (dt == gk::BF16 && m.F % 8 == 0 && m.D % 8 == 0) {
+      // du = (dx W_proj) * 2 sqrt(a) as an NT product against W_proj^T (in
+      // the GEMM scratch, free between the weight-gradient products): the
+      // K-contiguous operand reads run faster than the transposing ones
+      HIP_TRY(gk::transpose_bf16(elem(params, pl.wproj[l], es), m.D, m.F, gscr, s));
+      g = gk::GemmDesc{gk::OP_NT, N, m.F, m.D, dx, m.D, gscr, m.D, du, m.F, gk::E_DRELU2,
+                       const_cast<void*>(a)};
+    } else {
+      g = gk::GemmDesc{gk::OP_NN, N, m.F, m.D, dx, m.D, elem(params, pl.wproj[l], es), m.F, du,
+                       m.F, gk::E_DRELU2, const_cast<void*>(a)};
+    }
     HIP_TRY(gk::gemm(g, dt, s));
     g = gk::GemmDesc{gk::OP_TN, m.F, m.D, N, du, m.F, h2, m.D, grads + pl.wfc[l], m.D, wepi,
                      nullptr, gscr, gscr_bytes};

@@ -34,6 +34,41 @@ hipError_t fill_zero(void* p, int64_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------- transpose
+// out[c, r] = in[r, c] for a [rows, cols] bf16 matrix (rows, cols multiples
+// of 8): 64 x 64 tiles through LDS, 16-byte loads and stores.  grid
+// (cdiv(cols, 64), cdiv(rows, 64)), 512 threads: thread t moves 8 values.
+__global__ __launch_bounds__(512) void k_transpose16(const bf16* __restrict__ in, int64_t rows,
+                                                     int64_t cols, bf16* __restrict__ out) {
+  __shared__ bf16 tile[64][64 + 2];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tr = threadIdx.x >> 3, tc = 8 * (threadIdx.x & 7);
+  if (r0 + tr < rows && c0 + tc < cols) {
+    const uint4 v = *(const uint4*)(in + (r0 + tr) * cols + c0 + tc);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[tc + e][tr] = (bf16)(w[e >> 1] >> (16 * (e & 1)));
+  }
+  __syncthreads();
+  // thread t writes out row c0 + t / 8, columns (= in rows) r0 + 8 (t % 8) ..
+  const int64_t oc = c0 + tr, orr = r0 + tc;
+  if (oc < cols && orr < rows) {
+    uint4 o;
+    uint32_t* ow = (uint32_t*)&o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      ow[e] = (uint32_t)tile[tr][tc + 2 * e] | ((uint32_t)tile[tr][tc + 2 * e + 1] << 16);
+    *(uint4*)(out + oc * rows + orr) = o;
+  }
+}
+
+hipError_t transpose_bf16(const void* in, int64_t rows, int64_t cols, void* out, hipStream_t s) {
+  const dim3 grid((unsigned)cdiv(cols, 64), (unsigned)cdiv(rows, 64));
+  GK_LAUNCH(Work(0.0, 4.0 * rows * cols), k_transpose16, grid, dim3(512), 0, s, (const bf16*)in,
+            rows, cols, (bf16*)out);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------- rope table
 // (cos, sin) of theta_{t,j} = t * base^(-2j/hd), in double precision.
 __global__ void k_rope_table(float2* cs, int T, int hd, double base) {

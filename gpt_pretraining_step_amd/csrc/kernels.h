@@ -17,6 +17,9 @@ hipError_t fill_zero(void* p, int64_t bytes, hipStream_t s);
 
 hipError_t rope_table(float* cs, int T, int hd, float base, hipStream_t s);
 
+// out [cols, rows] = in [rows, cols]^T, bf16, rows and cols multiples of 8
+hipError_t transpose_bf16(const void* in, int64_t rows, int64_t cols, void* out, hipStream_t s);
+
 // x[n, :] = wte[tok[b, t], :], n = b*T + t, tok rows of length T+1
 hipError_t embed_fwd(const int32_t* tok, int B, int T, const void* wte,
                      void* x, int D, DType dt, hipStream_t s);
