@@ -10,7 +10,8 @@ seeded input generator (``gptinputs``), which holds no model arithmetic.
 
 Sources (pages, cited by title and section):
   [nanochat]  "5만원으로 나만의 ChatGPT 훈련하는 방법" (apidog.com blog, nanochat
-              walkthrough): "1. GPT model (nanochat/gpt.py)" architecture list,
+              walkthrough): "1. GPT model (nanochat/gpt.py)" architecture list
+              and efficiency tricks (`oracle.extras`),
               value-embedding snippet; "2. Muon optimizer" (the Newton-
               Schulz orthogonalization, `oracle.muon`); "3. precision
               management" (also the FP8 linear layers, `oracle.fp8`); "5. flash
@@ -35,3 +36,4 @@ from .gpt import (  # noqa: F401
 )
 from . import fp8  # noqa: F401  (FP8 linear layers with tensor-wise scaling)
 from . import muon  # noqa: F401  (Muon's Newton-Schulz orthogonalization)
+from . import extras  # noqa: F401  (residual lambdas, smear, backout)

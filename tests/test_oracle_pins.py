@@ -699,3 +699,68 @@ def test_muon_momentum_and_update_closed_forms():
     x = np.ones((3, 4))
     np.testing.assert_allclose(muon.muon_update(w, x, 0.02, 0.0), w - 0.02, rtol=1e-15)
     np.testing.assert_allclose(muon.muon_update(w, x, 0.02, 0.5), w * 0.99 - 0.02, rtol=1e-15)
+
+
+# ------------------------------------------------------- model extras
+def _fd(f, x, eps=1e-6):
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        xp, xm = x.copy(), x.copy()
+        xp[i] += eps
+        xm[i] -= eps
+        g[i] = (f(xp) - f(xm)) / (2 * eps)
+    return g
+
+
+def test_extras_backward_by_finite_differences():
+    """Every gradient of residual mixing, smear and backout equals central
+    differences of a random linear functional of the output (fp64)."""
+    from oracle import extras as X
+    rng = np.random.default_rng(8)
+    B, T, D = 2, 5, 28
+    x, x0, xm = (rng.standard_normal((B * T, D)) for _ in range(3))
+    c = rng.standard_normal((B * T, D))
+    w = rng.standard_normal(24) * 0.3
+    lr, l0, ls, lb = 0.9, 0.3, 0.7, 0.4
+    dx, dx0, dlr, dl0 = X.resid_mix_bwd(c, x, x0, lr, l0)
+    np.testing.assert_allclose(dx, _fd(lambda v: np.sum(c * X.resid_mix(v, x0, lr, l0)), x),
+                               atol=1e-7)
+    np.testing.assert_allclose(dx0, _fd(lambda v: np.sum(c * X.resid_mix(x, v, lr, l0)), x0),
+                               atol=1e-7)
+    assert dlr == pytest.approx(np.sum(c * x)) and dl0 == pytest.approx(np.sum(c * x0))
+    sx, sw, sl = X.smear_bwd(c, x, w, ls, T)
+    np.testing.assert_allclose(sx, _fd(lambda v: np.sum(c * X.smear(v, w, ls, T)[0]), x),
+                               atol=1e-7)
+    np.testing.assert_allclose(sw, _fd(lambda v: np.sum(c * X.smear(x, v, ls, T)[0]), w),
+                               atol=1e-7)
+    fl = _fd(lambda v: np.sum(c * X.smear(x, w, float(v[0]), T)[0]), np.array([ls]))
+    assert sl == pytest.approx(fl[0], abs=1e-7)
+    bx, bm, bl = X.backout_bwd(c, xm, lb)
+    np.testing.assert_allclose(bm, _fd(lambda v: np.sum(c * X.backout(x, v, lb)), xm),
+                               atol=1e-7)
+    np.testing.assert_array_equal(bx, c)
+    assert bl == pytest.approx(-np.sum(c * xm))
+
+
+def test_extras_closed_forms():
+    """lambda = 0 leaves the stream alone (smear, backout) or keeps only one
+    input (mix); a zero gate weight gives g = lambda / 2, so y_t = x_t +
+    (lambda / 2) x_(t-1) with the first position of every row untouched;
+    backing out the stream itself with lambda 1 gives zero."""
+    from oracle import extras as X
+    rng = np.random.default_rng(9)
+    T, D = 4, 30
+    x, x0 = rng.standard_normal((2 * T, D)), rng.standard_normal((2 * T, D))
+    np.testing.assert_array_equal(X.resid_mix(x, x0, 1.0, 0.0), x)
+    np.testing.assert_array_equal(X.resid_mix(x, x0, 0.0, 1.0), x0)
+    np.testing.assert_array_equal(X.smear(x, np.ones(24), 0.0, T)[0], x)
+    y, g = X.smear(x, np.zeros(24), 0.8, T)
+    for r in range(2):
+        np.testing.assert_array_equal(y[r * T], x[r * T])
+        for t in range(1, T):
+            np.testing.assert_allclose(y[r * T + t], x[r * T + t] + 0.4 * x[r * T + t - 1],
+                                       atol=1e-15)
+    np.testing.assert_array_equal(X.backout(x, x, 1.0), np.zeros_like(x))
+    np.testing.assert_array_equal(X.backout(x, x0, 0.0), x)
