@@ -5,6 +5,7 @@
     python bench.py --workload fp8 [--config d24]
     python bench.py --workload muon [--config d12]
     python bench.py --workload optim [--config d12]
+    python bench.py --workload extras [--config d12]
 
 Times K forward+backward steps of the d12 model (12 layers, width 768, 6
 heads of 128, vocab 32768, 16 rows of 2048 tokens, 'SSSL' windows 1024/2048,
@@ -690,6 +691,77 @@ def bench_optim(a, torch, G):
     print(json.dumps(out), flush=True)
 
 
+EXTRAS_METRIC = "model extras (smear, residual lambdas, backout) fwd+bwd of a step: GB/s"
+
+
+def bench_extras(a, torch, G):
+    """The model extras of one training step at the workload's token count:
+    smear once after the embedding, residual mixing before every block,
+    backout once after the last; forward and backward of each."""
+    import gptinputs as gi
+    cfg = gi.preset(a.config)
+    B, T, D, L = cfg["batch"], cfg["seq_len"], cfg["d_model"], cfg["n_layer"]
+    N = B * T
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg["seed"])
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=g, device=dev).bfloat16()
+
+    x0, xs, dy = rnd(N, D), [rnd(N, D) for _ in range(L)], rnd(N, D)
+    xm = rnd(N, D)
+    y, dx, dx0 = (torch.empty(N, D, dtype=torch.bfloat16, device=dev) for _ in range(3))
+    lam = torch.tensor([0.9, 0.1], device=dev).bfloat16()
+    bo = torch.tensor([1.0, -0.3], device=dev).bfloat16()
+    w = rnd(24)
+    sl = torch.tensor([0.5], device=dev).bfloat16()
+    gate = torch.empty(N, device=dev)
+    dl = torch.empty(32, device=dev)
+    mscr = torch.empty(G.lib().gpt_k_resid_mix_bwd_scratch_bytes(), dtype=torch.uint8, device=dev)
+    sscr = torch.empty(G.lib().gpt_k_smear_bwd_scratch_bytes(), dtype=torch.uint8, device=dev)
+    n = N * D
+
+    def step():
+        G.k_smear_fwd(x0, B, T, D, w, sl, y, gate, G.BF16)
+        for x in xs:
+            G.k_resid_mix_fwd(x, x0, y, n, lam, G.BF16)
+        G.k_resid_mix_fwd(y, xm, dx, n, bo, G.BF16)
+        G.k_resid_mix_bwd(dy, y, xm, None, dx0, False, n, bo, dl[0:], mscr, G.BF16)
+        for x in xs:
+            G.k_resid_mix_bwd(dy, x, x0, dx, dx0, True, n, lam, dl[2:], mscr, G.BF16)
+        G.k_smear_bwd(dy, x0, B, T, D, w, sl, gate, dx, dl[4:], sscr, G.BF16)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = time_events(step, a.steps, torch) * 1e3
+    # bytes: smear fwd 3 nD (x, x_prev, y) + bwd 4 nD; mix fwd 3 nD, bwd 5 nD (dy, x, x0, dx,
+    # dx0 read and written: 6); backout fwd 3, bwd 4 -- bf16, 2 bytes each
+    per = 2.0 * n
+    nbytes = per * (3 + 4 + L * (3 + 6) + 3 + 4)
+    gbs = nbytes / ms / 1e6
+    log(f"extras {ms:.3f} ms per step, {gbs:,.0f} GB/s")
+    prof = kernel_profile(step, a.prof_steps, torch, G) if a.prof_steps > 0 else []
+    for r in prof[:8]:
+        log(f"  {r['ms_per_step']:7.3f} ms/step {r['launches_per_step']:5.0f} x "
+            f"{r['avg_launch_ms'] * 1e3:8.1f} us  {r['gbps'] or 0:7.0f} GB/s  {r['kernel']}")
+    roof = roofline_of(prof[0], ms) if prof else None
+    out = {
+        "metric": EXTRAS_METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations and gradients)",
+        "config": {"workload": f"{a.config} model extras: smear + backout once, residual "
+                               f"mixing x {L}, forward and backward, {N} tokens x {D}",
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": None,
+        "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
+                    for r in prof],
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -703,12 +775,12 @@ def main():
     ap.add_argument("--shapes", action="store_true",
                     help="also time every product / attention shape alone")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--workload", choices=("train", "decode", "fp8", "muon", "optim"),
+    ap.add_argument("--workload", choices=("train", "decode", "fp8", "muon", "optim", "extras"),
                     default="train",
                     help="train: the fwd+bwd step; decode: KV-cache decode attention; fp8: the "
                          "step's linear layers as FP8 linear layers; muon: Muon's "
                          "orthogonalization of every matrix update; optim: the whole optimizer "
-                         "step")
+                         "step; extras: smear, residual lambdas and backout")
     ap.add_argument("--decode-batch", type=int, default=64,
                     help="sequences sampled in parallel (decode workload)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -733,6 +805,10 @@ def main():
     if a.workload == "decode":
         a.config = a.config or "d12gqa"
         bench_decode(a, torch, G)
+        return
+    if a.workload == "extras":
+        a.config = a.config or "d12"
+        bench_extras(a, torch, G)
         return
     if a.workload == "optim":
         a.config = a.config or "d12"

@@ -98,6 +98,14 @@ _SIGS = {
     "gpt_k_muon_update": (C.c_int, [_vp, _vp, _i64, _f32, _f32, _vp, _vp]),
     "gpt_k_adamw": (C.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _f32, _f32, _f32, _f32, _f32, _vp,
                               _vp]),
+    "gpt_k_resid_mix_fwd": (C.c_int, [_vp, _vp, _vp, _i64, _vp, _i32, _vp]),
+    "gpt_k_resid_mix_bwd_scratch_bytes": (_sz, []),
+    "gpt_k_resid_mix_bwd": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _sz,
+                                      _i32, _vp]),
+    "gpt_k_smear_fwd": (C.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp]),
+    "gpt_k_smear_bwd_scratch_bytes": (_sz, []),
+    "gpt_k_smear_bwd": (C.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                  _i32, _vp]),
     "gpt_k_ce": (C.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp]),
     "gpt_k_lm_ce_scratch_bytes": (_sz, [_i64, _i32]),
     "gpt_k_embed_fwd": (C.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp]),
@@ -315,6 +323,31 @@ def k_muon_update(w, x, n, lr, wd, w_bf16=None, stream=None):
 def k_adamw(w, grad, m, v, n, step, lr, beta1, beta2, eps, wd, w_bf16=None, stream=None):
     _check(lib().gpt_k_adamw(_ptr(w), _ptr(grad), _ptr(m), _ptr(v), n, step, lr, beta1, beta2,
                              eps, wd, _ptr(w_bf16), _stream(stream)))
+
+
+def k_resid_mix_fwd(x, x0, y, n, lambdas, dtype, stream=None):
+    _check(lib().gpt_k_resid_mix_fwd(_ptr(x), _ptr(x0), _ptr(y), n, _ptr(lambdas), dtype,
+                                     _stream(stream)))
+
+
+def k_resid_mix_bwd(dy, x, x0, dx, dx0, accumulate, n, lambdas, dlambdas, scratch, dtype,
+                    stream=None):
+    _check(lib().gpt_k_resid_mix_bwd(_ptr(dy), _ptr(x), _ptr(x0), _ptr(dx), _ptr(dx0),
+                                     int(accumulate), n, _ptr(lambdas), _ptr(dlambdas),
+                                     _ptr(scratch), scratch.numel() * scratch.element_size(),
+                                     dtype, _stream(stream)))
+
+
+def k_smear_fwd(x, B, T, D, w, lam, y, gate, dtype, stream=None):
+    _check(lib().gpt_k_smear_fwd(_ptr(x), B, T, D, _ptr(w), _ptr(lam), _ptr(y), _ptr(gate),
+                                 dtype, _stream(stream)))
+
+
+def k_smear_bwd(dy, x, B, T, D, w, lam, gate, dx, dw_dlam, scratch, dtype, stream=None):
+    _check(lib().gpt_k_smear_bwd(_ptr(dy), _ptr(x), B, T, D, _ptr(w), _ptr(lam), _ptr(gate),
+                                 _ptr(dx), _ptr(dw_dlam), _ptr(scratch),
+                                 scratch.numel() * scratch.element_size(), dtype,
+                                 _stream(stream)))
 
 
 def k_embed_fwd(tokens, B, T, wte, V, D, x, dtype, stream=None):

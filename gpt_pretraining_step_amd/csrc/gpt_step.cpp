@@ -768,6 +768,62 @@ int gpt_k_adamw(float* w, const float* grad, float* m, float* v, int64_t n, int3
   return GPT_OK;
 }
 
+int gpt_k_resid_mix_fwd(const void* x, const void* x0, void* y, int64_t n, const void* lambdas,
+                        int32_t dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({x, x0, y}))) return st;
+  if (!lambdas) return fail(GPT_ERR_INVALID_ARG, "lambdas is null");
+  if (n < 8 || n % 8) return fail(GPT_ERR_INVALID_ARG, "n must be a positive multiple of 8");
+  KERNEL_TRY(gk::resid_mix_fwd(x, x0, y, n, lambdas, (gk::DType)dtype, s));
+  return GPT_OK;
+}
+
+size_t gpt_k_resid_mix_bwd_scratch_bytes(void) { return gk::resid_mix_bwd_scratch_bytes(); }
+
+int gpt_k_resid_mix_bwd(const void* dy, const void* x, const void* x0, void* dx, void* dx0,
+                        int32_t accumulate, int64_t n, const void* lambdas, float* dlambdas,
+                        void* scratch, size_t scratch_bytes, int32_t dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({dy, x, x0, dx0, scratch}))) return st;
+  if (dx && !aligned16(dx)) return fail(GPT_ERR_MISALIGNED, "dx misaligned");
+  if (!lambdas || !dlambdas) return fail(GPT_ERR_INVALID_ARG, "lambdas or dlambdas is null");
+  if (n < 8 || n % 8) return fail(GPT_ERR_INVALID_ARG, "n must be a positive multiple of 8");
+  if (scratch_bytes < gk::resid_mix_bwd_scratch_bytes())
+    return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "scratch too small");
+  KERNEL_TRY(gk::resid_mix_bwd(dy, x, x0, dx, dx0, accumulate ? 1 : 0, n, lambdas, dlambdas,
+                               scratch, (gk::DType)dtype, s));
+  return GPT_OK;
+}
+
+int gpt_k_smear_fwd(const void* x, int32_t B, int32_t T, int32_t D, const void* w,
+                    const void* lambda, void* y, float* gate, int32_t dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({x, y}))) return st;
+  if (!w || !lambda || !gate) return fail(GPT_ERR_INVALID_ARG, "w, lambda or gate is null");
+  if (B < 1 || T < 1 || D < 24 || D % 8) return fail(GPT_ERR_INVALID_ARG, "bad sizes");
+  if (x == y) return fail(GPT_ERR_INVALID_ARG, "smear cannot run in place");
+  KERNEL_TRY(gk::smear_fwd(x, (int64_t)B * T, T, D, w, lambda, y, gate, (gk::DType)dtype, s));
+  return GPT_OK;
+}
+
+size_t gpt_k_smear_bwd_scratch_bytes(void) { return gk::smear_bwd_scratch_bytes(); }
+
+int gpt_k_smear_bwd(const void* dy, const void* x, int32_t B, int32_t T, int32_t D, const void* w,
+                    const void* lambda, const float* gate, void* dx, float* dw_dlambda,
+                    void* scratch, size_t scratch_bytes, int32_t dtype, hipStream_t s) {
+  int st;
+  if ((st = dtype_ok(dtype)) || (st = check_ptrs({dy, x, dx, scratch}))) return st;
+  if (!w || !lambda || !gate || !dw_dlambda)
+    return fail(GPT_ERR_INVALID_ARG, "w, lambda, gate or dw_dlambda is null");
+  if (B < 1 || T < 1 || D < 24 || D % 8) return fail(GPT_ERR_INVALID_ARG, "bad sizes");
+  if (dx == dy || dx == x) return fail(GPT_ERR_INVALID_ARG, "smear backward cannot run in place");
+  if (scratch_bytes < gk::smear_bwd_scratch_bytes())
+    return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "scratch too small");
+  KERNEL_TRY(gk::smear_bwd(dy, x, (int64_t)B * T, T, D, w, lambda, gate, dx, dw_dlambda, scratch,
+                           (gk::DType)dtype, s));
+  return GPT_OK;
+}
+
 int gpt_k_rope_table(float* cs, int32_t T, int32_t hd, float base, hipStream_t s) {
   int st;
   if ((st = check_ptrs({cs}))) return st;

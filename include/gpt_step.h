@@ -304,6 +304,40 @@ int gpt_k_adamw(float* w, const float* grad, float* m, float* v, int64_t n,
                 int32_t step, float lr, float beta1, float beta2, float eps,
                 float wd, void* w_bf16, hipStream_t s);
 
+/* Model extras (the nanochat walkthrough, section "1. GPT model
+ * (nanochat/gpt.py)", efficiency tricks).  Token-major rows [N, D] of
+ * `dtype`, device, 16-byte aligned; scalar parameters are device values of
+ * `dtype`, their gradients device fp32; reductions in a fixed order.
+ *   Residual mixing before each block: y = lambdas[0] x + lambdas[1] x0
+ *   (x0 the embedding output; n = N D elements, a multiple of 8).  Backout
+ *   of a mid-layer residual x_mid after the last block is the same call
+ *   with lambdas = (1, -backout_lambda) and x0 = x_mid.  Backward: dx =
+ *   lambdas[0] dy (dx may be null; may alias dy), dx0 = (or +=, with
+ *   accumulate) lambdas[1] dy, dlambdas[0] = sum dy x, dlambdas[1] = sum dy
+ *   x0.  scratch: gpt_k_resid_mix_bwd_scratch_bytes().
+ *   Smear after the embedding, rows of T tokens: y_t = x_t + g_t x_(t-1),
+ *   g_t = lambda sigmoid(w . x_t[0:24]) (w: 24 values), g_t = 0 at each
+ *   row's first position; gate[N] (fp32) keeps g for the backward.
+ *   Backward: dx (not aliasing dy or x), dw_dlambda[0:24] = dw,
+ *   dw_dlambda[24] = dlambda.  scratch: gpt_k_smear_bwd_scratch_bytes().
+ *   D a multiple of 8 and >= 24. */
+int gpt_k_resid_mix_fwd(const void* x, const void* x0, void* y, int64_t n,
+                        const void* lambdas, int32_t dtype, hipStream_t s);
+size_t gpt_k_resid_mix_bwd_scratch_bytes(void);
+int gpt_k_resid_mix_bwd(const void* dy, const void* x, const void* x0,
+                        void* dx, void* dx0, int32_t accumulate, int64_t n,
+                        const void* lambdas, float* dlambdas, void* scratch,
+                        size_t scratch_bytes, int32_t dtype, hipStream_t s);
+int gpt_k_smear_fwd(const void* x, int32_t B, int32_t T, int32_t D,
+                    const void* w, const void* lambda, void* y, float* gate,
+                    int32_t dtype, hipStream_t s);
+size_t gpt_k_smear_bwd_scratch_bytes(void);
+int gpt_k_smear_bwd(const void* dy, const void* x, int32_t B, int32_t T,
+                    int32_t D, const void* w, const void* lambda,
+                    const float* gate, void* dx, float* dw_dlambda,
+                    void* scratch, size_t scratch_bytes, int32_t dtype,
+                    hipStream_t s);
+
 /* cos/sin table, float2 [T, hd/2]: (cos, sin) of t * base^(-2j/hd),
  * evaluated in double precision. */
 int gpt_k_rope_table(float* cs, int32_t T, int32_t hd, float base,

@@ -157,6 +157,17 @@ def test_entry_points_reject_bad_pointers_before_launch():
     assert L.gpt_k_muon_update(A, A, 8, 0.1, 0.0, C.c_void_p(0x1004), None) == -4
     assert L.gpt_k_adamw(A, A, A, A, 8, 0, 1e-3, 0.9, 0.95, 1e-8, 0.0, None, None) == -1
     assert L.gpt_k_adamw(A, A, A, A, 8, 1, 1e-3, 1.5, 0.95, 1e-8, 0.0, None, None) == -1
+    # model extras
+    assert L.gpt_k_resid_mix_fwd(A, A, A, 12, A, 1, None) == -1
+    assert L.gpt_k_resid_mix_fwd(A, A, A, 16, None, 1, None) == -1
+    ms_ = L.gpt_k_resid_mix_bwd_scratch_bytes()
+    assert L.gpt_k_resid_mix_bwd(A, A, A, None, A, 1, 16, A, A, A, ms_ - 1, 1, None) == -3
+    assert L.gpt_k_resid_mix_bwd(A, A, A, None, A, 1, 16, A, None, A, ms_, 1, None) == -1
+    assert L.gpt_k_smear_fwd(A, 2, 8, 20, A, A, C.c_void_p(0x2000), A, 1, None) == -1
+    assert L.gpt_k_smear_fwd(A, 2, 8, 32, A, A, A, A, 1, None) == -1          # in place
+    ss_ = L.gpt_k_smear_bwd_scratch_bytes()
+    assert L.gpt_k_smear_bwd(A, C.c_void_p(0x2000), 2, 8, 32, A, A, A, C.c_void_p(0x3000), A,
+                             A, ss_ - 1, 1, None) == -3
     # decode attention: q, kc, vc, lens, o, lse, B, Tq, Tmax, H, Hkv, hd, W, bound,
     # scratch, scratch_bytes, dtype
     dec = L.gpt_k_attn_decode

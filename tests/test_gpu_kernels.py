@@ -887,3 +887,76 @@ def test_optimizer_elementwise(n):
         assert rel_err(to_np(aw), a_w) < 1e-5
         assert rel_err(to_np(am), a_m) < 1e-5 and rel_err(to_np(av), a_v) < 1e-5
         assert rel_err(to_np(tmom), mom) < 1e-6
+
+
+# ------------------------------------------------------ model extras
+@pytest.mark.parametrize("dt", [G.BF16, G.F32])
+@pytest.mark.parametrize("lams", [(0.9, 0.3), (1.0, -0.45)])   # mixing; backout
+def test_resid_mix(lams, dt):
+    """Residual mixing y = lr x + l0 x0 (and backout as lr = 1, l0 = -lambda)
+    with its backward (dx, dx0 accumulated onto a running value, the two
+    scalar gradients) against the oracle."""
+    from oracle import extras as X
+    say("resid mix", lams, dt)
+    bf = dt == G.BF16
+    N, D = 4096 + 16, 768
+    x, x0, dy, acc0 = (rnd_in((N, D), 90 + i, 1.0, bf) for i in range(4))
+    lam = np.array(lams, np.float32)
+    if bf:
+        lam = O.round_bf16(lam)
+    lr, l0 = float(lam[0]), float(lam[1])
+    tl = dev(lam, tdtype(dt))
+    tx, tx0, tdy = dev(x, tdtype(dt)), dev(x0, tdtype(dt)), dev(dy, tdtype(dt))
+    y = torch.empty_like(tx)
+    G.k_resid_mix_fwd(tx, tx0, y, N * D, tl, dt)
+    dx = torch.empty_like(tx)
+    dx0 = dev(acc0, tdtype(dt))
+    dl = torch.empty(2, dtype=torch.float32, device=DEV)
+    scr = torch.empty(G.lib().gpt_k_resid_mix_bwd_scratch_bytes(), dtype=torch.uint8, device=DEV)
+    G.k_resid_mix_bwd(tdy, tx, tx0, dx, dx0, True, N * D, tl, dl, scr, dt)
+    torch.cuda.synchronize()
+    tol = 1e-2 if bf else 1e-6
+    assert rel_err(to_np(y), X.resid_mix(x, x0, lr, l0)) < tol
+    rdx, rdx0, rlr, rl0 = X.resid_mix_bwd(dy, x, x0, lr, l0)
+    assert rel_err(to_np(dx), rdx) < tol
+    assert rel_err(to_np(dx0), rdx0 + acc0) < tol
+    np.testing.assert_allclose(to_np(dl), [rlr, rl0], rtol=1e-4)
+
+
+@pytest.mark.parametrize("dt", [G.BF16, G.F32])
+@pytest.mark.parametrize("B,T,D", [(2, 64, 768), (3, 5, 24), (1, 1, 256)])
+def test_smear(B, T, D, dt):
+    """Smear forward (y, the saved gates) and backward (dx, dw, dlambda)
+    against the oracle; a row of one token is never mixed."""
+    from oracle import extras as X
+    say("smear", B, T, D, dt)
+    bf = dt == G.BF16
+    N = B * T
+    x, dy = rnd_in((N, D), 95, 1.0, bf), rnd_in((N, D), 96, 1.0, bf)
+    w = rnd_in((24,), 97, 0.3, bf)
+    lam = np.array([0.7], np.float32)
+    if bf:
+        lam = O.round_bf16(lam)
+    lv = float(lam[0])
+    tx, tdy = dev(x, tdtype(dt)), dev(dy, tdtype(dt))
+    tw, tl = dev(w, tdtype(dt)), dev(lam, tdtype(dt))
+    y = torch.empty_like(tx)
+    gate = torch.empty(N, dtype=torch.float32, device=DEV)
+    G.k_smear_fwd(tx, B, T, D, tw, tl, y, gate, dt)
+    dx = torch.empty_like(tx)
+    dwl = torch.empty(25, dtype=torch.float32, device=DEV)
+    scr = torch.empty(G.lib().gpt_k_smear_bwd_scratch_bytes(), dtype=torch.uint8, device=DEV)
+    G.k_smear_bwd(tdy, tx, B, T, D, tw, tl, gate, dx, dwl, scr, dt)
+    torch.cuda.synchronize()
+    ry, rg = X.smear(x, w, lv, T)
+    rdx, rdw, rdl = X.smear_bwd(dy, x, w, lv, T)
+    tol = 1e-2 if bf else 1e-5
+    assert rel_err(to_np(y), ry) < tol
+    np.testing.assert_allclose(to_np(gate), rg, rtol=1e-5, atol=1e-6)
+    assert rel_err(to_np(dx), rdx) < tol
+    got = to_np(dwl)
+    if T > 1:
+        assert rel_err(got[:24], rdw) < 1e-4
+        assert got[24] == pytest.approx(rdl, rel=1e-4)
+    else:
+        assert np.all(got == 0.0)
