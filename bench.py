@@ -605,10 +605,11 @@ OPTIM_METRIC = "optimizer step (Muon for block matrices, AdamW for the rest): ms
 
 
 def bench_optim(a, torch, G):
-    """One optimizer step over every parameter of the model: Muon (momentum,
-    batched Newton-Schulz per parameter shape, update with a bf16 copy) for
-    the block matrices, AdamW for the embeddings, lm_head, value embeddings
-    and gates; fp32 masters, gradients and states resident in HBM."""
+    """One optimizer step over every parameter of the model (gpt_optim_step):
+    Muon (momentum, batched Newton-Schulz per parameter shape, update with a
+    bf16 copy) for the block matrices, AdamW for the embeddings, lm_head,
+    value embeddings and gates; fp32 masters, gradients and states resident
+    in HBM."""
     import gptinputs as gi
     cfg = gi.preset(a.config)
     gc = G.make_config(cfg)
@@ -633,30 +634,16 @@ def bench_optim(a, torch, G):
     w = torch.randn(n_total, generator=g, device=dev) * 0.02
     w16 = w.bfloat16()
     grad = torch.randn(n_total, generator=g, device=dev) * 1e-3
-    mom = torch.zeros(n_total, device=dev)
-    m1, m2 = torch.zeros(n_total, device=dev), torch.zeros(n_total, device=dev)
-    stage = {k: torch.empty(len(v), *v[0][1], device=dev) for k, v in groups.items()}
-    xs = {k: torch.empty(len(v), *v[0][1], dtype=torch.bfloat16, device=dev)
-          for k, v in groups.items()}
-    ws = torch.empty(max(G.k_polar_express_ws_bytes(v[0][1][0], v[0][1][1], len(v))
-                         for v in groups.values()), dtype=torch.uint8, device=dev)
+    mom, m2 = torch.zeros(n_total, device=dev), torch.zeros(n_total, device=dev)
+    hp = G.make_optim_hparams([NS_TUPLE] * 5)
+    ows = torch.empty(G.optim_ws_bytes(gc), dtype=torch.uint8, device=dev)
     coeffs = [NS_TUPLE] * 5
 
     def numel(shape):
         return int(math.prod(shape))
 
     def step():
-        for k, v in groups.items():
-            m, n = v[0][1]
-            for i, (off, shape) in enumerate(v):
-                G.k_muon_momentum(grad[off:], mom[off:], stage[k][i], m * n, 0.95, True, G.F32)
-            G.k_polar_express(stage[k], m, n, G.F32, coeffs, 1e-7, xs[k], ws, batch=len(v))
-            lr = 0.02 * max(1.0, m / n) ** 0.5
-            for i, (off, shape) in enumerate(v):
-                G.k_muon_update(w[off:], xs[k][i], m * n, lr, 0.0, w16[off:])
-        for off, shape in adam:
-            G.k_adamw(w[off:], grad[off:], m1[off:], m2[off:], numel(shape), 1, 3e-3, 0.8, 0.95,
-                      1e-10, 0.0, w16[off:])
+        G.optim_step(gc, hp, 1, w, w16, grad, mom, m2, ows)
 
     for _ in range(a.warmup):
         step()
@@ -859,6 +846,21 @@ def main():
     mfu = tok_s * train_fpt / PEAK_BF16
     log(f"step {ms:.2f} ms  {tok_s:,.0f} tok/s  mfu {mfu:.3f}  (wall {wall:.2f} s)")
 
+    # the optimizer step on the same model (fp32 masters and states), timed
+    # on its own: reported beside the fwd+bwd rate, not folded into it
+    hp = G.make_optim_hparams([NS_TUPLE] * 5)
+    master = s.params.float()
+    st1, st2 = torch.zeros_like(master), torch.zeros_like(master)
+    ows = torch.empty(G.optim_ws_bytes(s.cfg), dtype=torch.uint8, device="cuda")
+    opt_params = s.params.clone()
+    G.optim_step(s.cfg, hp, 1, master, opt_params, s.grads, st1, st2, ows)
+    torch.cuda.synchronize()
+    opt_ms = time_events(lambda: G.optim_step(s.cfg, hp, 2, master, opt_params, s.grads, st1,
+                                              st2, ows), 5, torch) * 1e3
+    del master, st1, st2, ows, opt_params
+    log(f"optimizer step {opt_ms:.2f} ms; fwd+bwd+optimizer "
+        f"{tokens_per_step / ((ms + opt_ms) / 1e3):,.0f} tok/s")
+
     # evaluation throughput (forward + CE + bytes reduction)
     ev_rows = a.eval_rows
     ev_tok = s.upload(gi.make_eval_tokens(cfg, ev_rows))
@@ -906,6 +908,8 @@ def main():
                                f"{cfg['window_long']}, value embeddings on odd layers",
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "mfu_bf16": round(mfu, 4), "train_flop_per_token": train_fpt,
+        "optimizer_ms_per_step": round(opt_ms, 3),
+        "tokens_per_s_with_optimizer": round(tokens_per_step / ((ms + opt_ms) / 1e3), 1),
         "eval_tokens_per_s": round(eval_tok_s, 1), "eval_rows": ev_rows, "eval_bpb": bpb[2],
         "roofline": roof, "cpu_baseline": cpu,
         "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}

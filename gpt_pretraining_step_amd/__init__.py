@@ -42,6 +42,31 @@ class GptConfig(C.Structure):
     ]
 
 
+class OptimHparams(C.Structure):
+    _fields_ = [
+        ("muon_lr", C.c_float), ("muon_momentum", C.c_float), ("muon_wd", C.c_float),
+        ("muon_nesterov", C.c_int32), ("ns_steps", C.c_int32), ("ns_coeffs", C.c_float * 48),
+        ("ns_eps", C.c_float), ("adam_lr_embed", C.c_float), ("adam_lr_head", C.c_float),
+        ("adam_lr_gate", C.c_float), ("adam_beta1", C.c_float), ("adam_beta2", C.c_float),
+        ("adam_eps", C.c_float), ("adam_wd", C.c_float),
+    ]
+
+
+def make_optim_hparams(coeffs, muon_lr=0.02, muon_momentum=0.95, muon_wd=0.0, nesterov=True,
+                       ns_eps=1e-7, adam_lr_embed=0.2, adam_lr_head=0.004, adam_lr_gate=0.02,
+                       beta1=0.8, beta2=0.95, eps=1e-10, adam_wd=0.0) -> OptimHparams:
+    h = OptimHparams()
+    h.muon_lr, h.muon_momentum, h.muon_wd = muon_lr, muon_momentum, muon_wd
+    h.muon_nesterov, h.ns_steps = int(nesterov), len(coeffs)
+    flat = [float(v) for t in coeffs for v in t]
+    for i, v in enumerate(flat):
+        h.ns_coeffs[i] = v
+    h.ns_eps = ns_eps
+    h.adam_lr_embed, h.adam_lr_head, h.adam_lr_gate = adam_lr_embed, adam_lr_head, adam_lr_gate
+    h.adam_beta1, h.adam_beta2, h.adam_eps, h.adam_wd = beta1, beta2, eps, adam_wd
+    return h
+
+
 def make_config(d: dict) -> GptConfig:
     """A GptConfig from a dict with the struct's field names."""
     c = GptConfig()
@@ -106,6 +131,8 @@ _SIGS = {
     "gpt_k_smear_bwd_scratch_bytes": (_sz, []),
     "gpt_k_smear_bwd": (C.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                   _i32, _vp]),
+    "gpt_optim_ws_bytes": (_sz, [_vp]),
+    "gpt_optim_step": (C.c_int, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "gpt_k_ce": (C.c_int, [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _f32, _i32, _vp]),
     "gpt_k_lm_ce_scratch_bytes": (_sz, [_i64, _i32]),
     "gpt_k_embed_fwd": (C.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp]),
@@ -348,6 +375,17 @@ def k_smear_bwd(dy, x, B, T, D, w, lam, gate, dx, dw_dlam, scratch, dtype, strea
                                  _ptr(dx), _ptr(dw_dlam), _ptr(scratch),
                                  scratch.numel() * scratch.element_size(), dtype,
                                  _stream(stream)))
+
+
+def optim_ws_bytes(cfg: GptConfig) -> int:
+    return int(lib().gpt_optim_ws_bytes(C.byref(cfg)))
+
+
+def optim_step(cfg: GptConfig, hp: OptimHparams, step, master, params, grads, state1, state2,
+               ws, stream=None):
+    _check(lib().gpt_optim_step(C.byref(cfg), C.byref(hp), step, _ptr(master), _ptr(params),
+                                _ptr(grads), _ptr(state1), _ptr(state2), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def k_embed_fwd(tokens, B, T, wte, V, D, x, dtype, stream=None):

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -580,6 +581,103 @@ int gpt_eval_bpb(const gpt_config* cfg, const void* params, const int32_t* token
   }
   hipError_t e = gk::eval_finish(acc, out_dev, stream);
   if (e != hipSuccess) return fail(GPT_ERR_HIP, "eval_finish: %s", hipGetErrorString(e));
+  return GPT_OK;
+}
+
+// ------------------------------------------------------- optimizer step
+namespace {
+struct MuonGroup {
+  const std::vector<int64_t>* offs;
+  int64_t rows, cols;
+};
+std::vector<MuonGroup> muon_groups(const Model& m, const ParamLayout& pl) {
+  return {{&pl.wqkv, m.QKV, m.D}, {&pl.wo, m.D, (int64_t)m.H * m.hd},
+          {&pl.wfc, m.F, m.D}, {&pl.wproj, m.D, m.F}};
+}
+size_t optim_ws(const Model& m, const ParamLayout& pl) {
+  size_t b = 0;
+  for (const MuonGroup& g : muon_groups(m, pl)) {
+    const size_t n = (size_t)m.L * g.rows * g.cols;
+    const size_t stage = (n * 4 + 255) / 256 * 256, xb = (n * 2 + 255) / 256 * 256;
+    b = std::max(b, stage + xb + gk::polar_express_ws_bytes(m.L, g.rows, g.cols));
+  }
+  return b;
+}
+}  // namespace
+
+size_t gpt_optim_ws_bytes(const gpt_config* cfg) {
+  Model m;
+  if (validate(cfg, &m)) return 0;
+  return optim_ws(m, param_layout(m));
+}
+
+int gpt_optim_step(const gpt_config* cfg, const gpt_optim_hparams* hp, int32_t step,
+                   float* master, void* params, const float* grads, float* state1,
+                   float* state2, void* ws, size_t ws_bytes, hipStream_t s) {
+  Model m;
+  int st = validate(cfg, &m);
+  if (st) return st;
+  if (!hp) return fail(GPT_ERR_INVALID_ARG, "hparams is null");
+  if ((st = check_ptrs({master, grads, state1, state2, ws}))) return st;
+  if (params && !aligned16(params)) return fail(GPT_ERR_MISALIGNED, "params misaligned");
+  if (m.dt == gk::BF16 && !params)
+    return fail(GPT_ERR_INVALID_ARG, "bf16 configs need the params copy to update");
+  if (step < 1) return fail(GPT_ERR_INVALID_ARG, "step counts from 1");
+  if (hp->ns_steps < 0 || hp->ns_steps > 16)
+    return fail(GPT_ERR_INVALID_ARG, "ns_steps outside [0, 16]");
+  if (!(hp->muon_momentum >= 0.f && hp->muon_momentum < 1.f) ||
+      !(hp->adam_beta1 >= 0.f && hp->adam_beta1 < 1.f) ||
+      !(hp->adam_beta2 >= 0.f && hp->adam_beta2 < 1.f))
+    return fail(GPT_ERR_INVALID_ARG, "momentum or betas outside [0, 1)");
+  const ParamLayout pl = param_layout(m);
+  const size_t need = optim_ws(m, pl);
+  if (ws_bytes < need) return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "ws needs %zu bytes", need);
+  // every tensor starts on a 16-byte boundary in both copies
+  auto ok_off = [&](int64_t off) { return off < 0 || off % 8 == 0; };
+  bool aligned = ok_off(pl.wte) && ok_off(pl.wlm);
+  for (int l = 0; l < m.L; ++l)
+    aligned = aligned && ok_off(pl.wqkv[l]) && ok_off(pl.wo[l]) && ok_off(pl.wfc[l]) &&
+              ok_off(pl.wproj[l]) && ok_off(pl.ve[l]) && ok_off(pl.wg[l]);
+  if (!aligned || m.D % 8 || m.F % 8 || m.QKV % 8 || (m.H * m.hd) % 8)
+    return fail(GPT_ERR_UNSUPPORTED_CONFIG, "parameter tensors not 8-element aligned");
+  const bool copy16 = m.dt == gk::BF16;
+  auto p16 = [&](int64_t off) { return copy16 ? (void*)((char*)params + off * 2) : nullptr; };
+  char* w = (char*)ws;
+  // Muon: momentum into a [L, rows, cols] staging copy, the batched
+  // orthogonalization, then the step with lr max(1, rows / cols)^0.5
+  for (const MuonGroup& g : muon_groups(m, pl)) {
+    const int64_t n = g.rows * g.cols;
+    const size_t stage = ((size_t)m.L * n * 4 + 255) / 256 * 256;
+    const size_t xb = ((size_t)m.L * n * 2 + 255) / 256 * 256;
+    float* u = (float*)w;
+    uint16_t* x = (uint16_t*)(w + stage);
+    void* nsws = w + stage + xb;
+    for (int l = 0; l < m.L; ++l) {
+      const int64_t off = (*g.offs)[l];
+      HIP_TRY(gk::muon_momentum(grads + off, state1 + off, u + l * n, n, hp->muon_momentum,
+                                hp->muon_nesterov ? 1 : 0, gk::F32, s));
+    }
+    HIP_TRY(gk::polar_express(u, m.L, g.rows, g.cols, gk::F32, hp->ns_coeffs, hp->ns_steps,
+                              hp->ns_eps, x, nsws, s));
+    const float lr = hp->muon_lr * std::sqrt(std::max(1.0f, (float)g.rows / (float)g.cols));
+    for (int l = 0; l < m.L; ++l) {
+      const int64_t off = (*g.offs)[l];
+      HIP_TRY(gk::muon_update(master + off, x + l * n, n, lr, hp->muon_wd, p16(off), s));
+    }
+  }
+  // AdamW: embeddings and value-embedding tables, lm_head, gates
+  auto adam = [&](int64_t off, int64_t n, float lr) -> int {
+    HIP_TRY(gk::adamw(master + off, grads + off, state1 + off, state2 + off, n, step, lr,
+                      hp->adam_beta1, hp->adam_beta2, hp->adam_eps, hp->adam_wd, p16(off), s));
+    return GPT_OK;
+  };
+  if ((st = adam(pl.wte, (int64_t)m.V * m.D, hp->adam_lr_embed))) return st;
+  if ((st = adam(pl.wlm, (int64_t)m.V * m.D, hp->adam_lr_head))) return st;
+  for (int l = 0; l < m.L; ++l) {
+    if (pl.ve[l] < 0) continue;
+    if ((st = adam(pl.ve[l], (int64_t)m.V * m.Hkv * m.hd, hp->adam_lr_embed))) return st;
+    if ((st = adam(pl.wg[l], (int64_t)m.Hkv * m.C, hp->adam_lr_gate))) return st;
+  }
   return GPT_OK;
 }
 

@@ -155,6 +155,40 @@ int gpt_eval_bpb(const gpt_config* cfg, const void* params,
                  const int32_t* token_bytes, void* ws, size_t ws_bytes,
                  double* out_dev, hipStream_t stream);
 
+/* ------------------------------------------------------ optimizer step */
+/*
+ * One optimizer step over the flat parameter layout (the nanochat
+ * walkthrough, section "2. Muon optimizer": Muon for the block matrices,
+ * AdamW for embeddings, lm_head and value embeddings).
+ *   Muon, per block matrix [rows, cols] (Wqkv, Wo, Wfc, Wproj): momentum
+ *   (state1) M <- mu M + (1 - mu) G, update U = (1 - mu) G + mu M
+ *   (Nesterov) or M; X = the Newton-Schulz orthogonalization of U (ns_steps
+ *   tuples from ns_coeffs, the same matrix of every layer batched);
+ *   W <- W (1 - lr wd) - lr X with lr = muon_lr max(1, rows / cols)^0.5.
+ *   AdamW (state1 = m, state2 = v, step counts from 1): wte and the value-
+ *   embedding tables at adam_lr_embed, Wlm at adam_lr_head, the value-
+ *   embedding gates at adam_lr_gate.
+ *   master, grads, state1, state2: device fp32 in the flat layout (states
+ *   zero before step 1).  params: the dtype copy the step reads, written
+ *   from the updated master (bf16 configs; may be null for fp32 configs,
+ *   whose master is the parameter buffer).  ws: gpt_optim_ws_bytes(cfg).
+ *   Tensor offsets must be multiples of 8 elements (true when D, F, the
+ *   qkv width and H hd are). */
+typedef struct gpt_optim_hparams {
+  float muon_lr, muon_momentum, muon_wd;
+  int32_t muon_nesterov, ns_steps;  /* ns_steps <= 16 */
+  float ns_coeffs[48];              /* (a, b, c) per step */
+  float ns_eps;
+  float adam_lr_embed, adam_lr_head, adam_lr_gate;
+  float adam_beta1, adam_beta2, adam_eps, adam_wd;
+} gpt_optim_hparams;
+
+size_t gpt_optim_ws_bytes(const gpt_config* cfg);
+int gpt_optim_step(const gpt_config* cfg, const gpt_optim_hparams* hp,
+                   int32_t step, float* master, void* params,
+                   const float* grads, float* state1, float* state2, void* ws,
+                   size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------- workspace inspection */
 /* Byte offset into a TRAIN workspace of a saved tensor, for tests and
  * debugging; -1 when absent.  Layer-wise items take `layer`. */

@@ -157,6 +157,19 @@ def test_entry_points_reject_bad_pointers_before_launch():
     assert L.gpt_k_muon_update(A, A, 8, 0.1, 0.0, C.c_void_p(0x1004), None) == -4
     assert L.gpt_k_adamw(A, A, A, A, 8, 0, 1e-3, 0.9, 0.95, 1e-8, 0.0, None, None) == -1
     assert L.gpt_k_adamw(A, A, A, A, 8, 1, 1e-3, 1.5, 0.95, 1e-8, 0.0, None, None) == -1
+    # optimizer step
+    tc = G.make_config(gi.preset("tiny"))
+    wsb = G.optim_ws_bytes(tc)
+    hp = G.make_optim_hparams([(3.4445, -4.775, 2.0315)] * 5)
+    assert wsb > 0
+    assert L.gpt_optim_step(C.byref(tc), None, 1, A, None, A, A, A, A, wsb, None) == -1
+    assert L.gpt_optim_step(C.byref(tc), C.byref(hp), 0, A, None, A, A, A, A, wsb, None) == -1
+    assert L.gpt_optim_step(C.byref(tc), C.byref(hp), 1, A, None, A, A, A, A, wsb - 1, None) == -3
+    bad_hp = G.make_optim_hparams([(3.4445, -4.775, 2.0315)] * 5, muon_momentum=1.0)
+    assert L.gpt_optim_step(C.byref(tc), C.byref(bad_hp), 1, A, None, A, A, A, A, wsb, None) == -1
+    bc = G.make_config(gi.preset("d4"))
+    assert L.gpt_optim_step(C.byref(bc), C.byref(hp), 1, A, None, A, A, A, A,
+                            G.optim_ws_bytes(bc), None) == -1      # bf16 needs params
     # model extras
     assert L.gpt_k_resid_mix_fwd(A, A, A, 12, A, 1, None) == -1
     assert L.gpt_k_resid_mix_fwd(A, A, A, 16, None, 1, None) == -1

@@ -960,3 +960,65 @@ def test_smear(B, T, D, dt):
         assert got[24] == pytest.approx(rdl, rel=1e-4)
     else:
         assert np.all(got == 0.0)
+
+
+# ------------------------------------------------------ whole optimizer step
+@pytest.mark.parametrize("which", ["small_bf16", "tiny"])
+def test_optim_step(which):
+    """gpt_optim_step over every tensor of a model, two steps, against the
+    oracle's Muon (momentum, exact Newton-Schulz, lr max(1, rows/cols)^0.5
+    step) and AdamW per tensor: Muon tensors' changes within 2e-2 normwise
+    (the kernels' bf16 iteration), AdamW tensors to 1e-5; the bf16 copy is
+    the rounded master."""
+    from oracle import muon
+    from tests.gpu_util import small_bf16, tiny_plus
+    import gptinputs as gi
+    cfgd = small_bf16() if which == "small_bf16" else tiny_plus()
+    say("optim step", which)
+    cfg = G.make_config(cfgd)
+    n = O.param_count(cfgd)
+    rng = np.random.default_rng(21)
+    w0 = (rng.standard_normal(n) * 0.05).astype(np.float32)
+    grads = [rng.standard_normal(n).astype(np.float32) * 1e-2 for _ in range(2)]
+    coeffs = [NS_CLASSIC] * 5
+    hpd = dict(muon_lr=0.02, muon_momentum=0.9, muon_wd=0.01, adam_lr_embed=0.05,
+               adam_lr_head=0.004, adam_lr_gate=0.01, beta1=0.8, beta2=0.95, eps=1e-10,
+               adam_wd=0.001)
+    hp = G.make_optim_hparams(coeffs, **hpd)
+    master = dev(w0, torch.float32)
+    bf = cfgd["dtype"] == G.BF16
+    params = torch.empty(n, dtype=torch.bfloat16, device=DEV) if bf else None
+    s1, s2 = torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+    ws = torch.empty(G.optim_ws_bytes(cfg), dtype=torch.uint8, device=DEV)
+    for k in range(2):
+        G.optim_step(cfg, hp, k + 1, master, params, dev(grads[k], torch.float32), s1, s2, ws)
+    torch.cuda.synchronize()
+    got = to_np(master)
+    # oracle, tensor by tensor
+    off = 0
+    ref = w0.astype(np.float64).copy()
+    for name, shape in O.param_layout(cfgd):
+        size = int(np.prod(shape))
+        sl = slice(off, off + size)
+        base = name.split(".")[-1]
+        w = w0[sl].astype(np.float64).reshape(shape)
+        if base in ("wqkv", "wo", "wfc", "wproj"):
+            mom = np.zeros(shape)
+            lr = hpd["muon_lr"] * max(1.0, shape[0] / shape[1]) ** 0.5
+            for k in range(2):
+                mom, u = muon.muon_momentum(grads[k][sl].reshape(shape), mom, 0.9)
+                w = muon.muon_update(w, muon.polar_express(u, coeffs), lr, hpd["muon_wd"])
+            d_ref, d_got = w - w0[sl].reshape(shape), got[sl].reshape(shape) - w0[sl].reshape(shape)
+            assert rel_err(d_got, d_ref) < 2e-2, name
+        else:
+            lr = {"wte": hpd["adam_lr_embed"], "ve": hpd["adam_lr_embed"],
+                  "wlm": hpd["adam_lr_head"], "wg": hpd["adam_lr_gate"]}[base]
+            m = v = np.zeros(shape)
+            for k in range(2):
+                w, m, v = muon.adamw(w, grads[k][sl].reshape(shape), m, v, k + 1, lr,
+                                     hpd["beta1"], hpd["beta2"], hpd["eps"], hpd["adam_wd"])
+            assert rel_err(got[sl], w.reshape(-1)) < 1e-5, name
+        off += size
+    assert off == n
+    if bf:
+        np.testing.assert_array_equal(to_np(params), O.round_bf16(got.astype(np.float32)))
