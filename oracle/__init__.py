@@ -32,7 +32,7 @@ from .gpt import (  # noqa: F401
     rmsnorm_bwd, attention, attention_bwd, attention_tiled, decode_attention,
     cross_entropy,
     embedding, embedding_bwd, value_embedding, value_embedding_bwd,
-    forward, backward, step, eval_bpb, round_bf16,
+    forward, backward, step, eval_bpb, round_bf16, extras_on, extras_slots,
 )
 from . import fp8  # noqa: F401  (FP8 linear layers with tensor-wise scaling)
 from . import muon  # noqa: F401  (Muon's Newton-Schulz orthogonalization)

@@ -27,11 +27,25 @@ are marked READING):
     h2 = rms(x);  u = h2 Wfc^T;  a = relu(u)^2;  x = x + a Wproj^T
   hf = rms(x);  z = hf Wlm^T                        untied head
   loss = mean_n [ logsumexp(z_n) - z_n[tgt_n] ]     [microgpt] cross-entropy
+
+Optional model extras ([nanochat] "1. GPT model", efficiency tricks; each
+off unless the config turns it on; the arithmetic is in oracle/extras.py):
+  smear=1          x = x + g x_prev right after the embedding, g = lambda_s
+                   sigmoid(w_s . x[:24]) (zero at a row's first position)
+  resid_lambdas=1  before block l: x = lr_l x + l0_l x0, x0 the stream the
+                   blocks start from (after smear)
+  backout_layer=j  the stream after block j is kept as x_mid; after the last
+                   block x = x - lambda_b x_mid
+The scalars and w_s live in one extra tensor "extras" after Wlm (READING: a
+flat vector; its slots are listed at extras_slots).  In bf16emu every
+extra's output is rounded once, like the residual adds.
 """
 from __future__ import annotations
 
 import math
 import numpy as np
+
+from . import extras as _ex
 
 PRECISIONS = ("fp64", "fp32", "bf16emu")
 
@@ -72,6 +86,20 @@ def is_ve_layer(cfg: dict, layer: int) -> bool:
     return bool(cfg.get("ve_every_odd", 0)) and layer % 2 == 1
 
 
+def extras_on(cfg: dict) -> bool:
+    return bool(cfg.get("resid_lambdas", 0) or cfg.get("smear", 0)
+                or cfg.get("backout_layer", -1) >= 0)
+
+
+def extras_slots(cfg: dict) -> dict:
+    """Slots of the "extras" vector: (lr_l, l0_l) at 2l, 2l+1; the smear
+    weights w_s at 2L..2L+24, lambda_s at 2L+24, lambda_b at 2L+25; the
+    length is padded to a multiple of 8."""
+    L = cfg["n_layer"]
+    return dict(smear_w=2 * L, smear_lambda=2 * L + 24, backout=2 * L + 25,
+                size=8 * ((2 * L + 26 + 7) // 8))
+
+
 def param_layout(cfg: dict):
     D, H, Hkv, hd = cfg["d_model"], cfg["n_head"], cfg["n_kv_head"], cfg["head_dim"]
     V, F, C = cfg["vocab"], cfg["mlp_mult"] * cfg["d_model"], cfg["ve_gate_channels"]
@@ -84,6 +112,8 @@ def param_layout(cfg: dict):
         if is_ve_layer(cfg, l):
             out += [(f"l{l}.ve", (V, Hkv * hd)), (f"l{l}.wg", (Hkv, C))]
     out.append(("wlm", (V, D)))
+    if extras_on(cfg):
+        out.append(("extras", (extras_slots(cfg)["size"],)))
     return out
 
 
@@ -444,9 +474,26 @@ def forward(cfg: dict, flat_params, tokens, precision: str = "fp32",
     cos, sin = rope_tables(T, hd, cfg["rope_base"])
 
     x = embedding(P["wte"], inp, num)                            # [B,T,D]
+    D = x.shape[-1]
+    ex = P.get("extras")
+    sl = extras_slots(cfg)
+    resid = bool(cfg.get("resid_lambdas", 0))
+    bo = int(cfg.get("backout_layer", -1))
+    if bo >= cfg["n_layer"] or (cfg.get("smear", 0) and D < _ex.SMEAR_CH):
+        raise ValueError("backout_layer past the last block, or smear with d_model < 24")
+    extra = {}
+    if cfg.get("smear", 0):
+        extra["x_emb"] = x
+        y, _ = _ex.smear(x.reshape(-1, D), ex[sl["smear_w"]:sl["smear_w"] + _ex.SMEAR_CH],
+                         ex[sl["smear_lambda"]], T)
+        x = num.rnd(y.reshape(B, T, D))
+    x0 = x
     layers = []
     for l in range(cfg["n_layer"]):
         c = {}
+        if resid:
+            c["x_pre"] = x
+            x = num.rnd(_ex.resid_mix(x, x0, ex[2 * l], ex[2 * l + 1]))
         h, r = rmsnorm(x, eps, num)
         qkv = num.rnd(h @ P[f"l{l}.wqkv"].T)
         q, k, v = _split_qkv(qkv, cfg)
@@ -463,10 +510,14 @@ def forward(cfg: dict, flat_params, tokens, precision: str = "fp32",
         u = num.rnd(h2 @ P[f"l{l}.wfc"].T)
         a = num.rnd(np.maximum(u, 0) ** 2)
         x = num.rnd(x + a @ P[f"l{l}.wproj"].T)
+        if l == bo:
+            extra["x_mid"] = x
         if keep:
             c.update(h=h, r=r, q=q, k=k, v=v, rq=rq, rk=rk, o=o2, lse=lse,
                      W=W, h2=h2, r2=r2, u=u, a=a)
             layers.append(c)
+    if bo >= 0:
+        x = num.rnd(_ex.backout(x, extra["x_mid"], ex[sl["backout"]]))
     hf, rf = rmsnorm(x, eps, num)
     z = hf.reshape(B * T, -1) @ P["wlm"].T
     ell, lse_z, dz = cross_entropy(z, tgt.reshape(-1), num)
@@ -474,7 +525,7 @@ def forward(cfg: dict, flat_params, tokens, precision: str = "fp32",
     cache = dict(num=num, P=P, inp=inp, tgt=tgt, B=B, T=T, cos=cos, sin=sin,
                  ell=ell, lse_z=lse_z, loss=loss)
     if keep:
-        cache.update(layers=layers, hf=hf, rf=rf, dz=num.rnd(dz), z=z)
+        cache.update(layers=layers, hf=hf, rf=rf, dz=num.rnd(dz), z=z, x0=x0, **extra)
     return loss, cache
 
 
@@ -496,9 +547,22 @@ def backward(cfg: dict, cache: dict) -> dict:
     grads["wlm"] = (dz.T @ hf).astype(dt)
     dhf = num.rnd(dz @ P["wlm"]).reshape(B, T, D)
     dx = num.rnd(rmsnorm_bwd(dhf, cache["hf"], cache["rf"], num))
+    ex = P.get("extras")
+    sl = extras_slots(cfg)
+    resid = bool(cfg.get("resid_lambdas", 0))
+    bo = int(cfg.get("backout_layer", -1))
+    if ex is not None:
+        gex = np.zeros(ex.shape, dtype=np.float64)
+    if bo >= 0:
+        # x_out = x - lambda_b x_mid: dx passes through, x_mid gets -lambda_b dx
+        _, dxm, gex[sl["backout"]] = _ex.backout_bwd(dx, cache["x_mid"], ex[sl["backout"]])
+        dxm = num.rnd(dxm)
+    dx0 = None
 
     for l in reversed(range(cfg["n_layer"])):
         c = cache["layers"][l]
+        if l == bo:
+            dx = num.rnd(dx + dxm)
         # MLP: x_out = x_mid + a Wproj^T,  a = relu(u)^2,  u = h2 Wfc^T
         grads[f"l{l}.wproj"] = (dx.reshape(-1, D).T
                                 @ c["a"].reshape(B * T, -1)).astype(dt)
@@ -532,8 +596,26 @@ def backward(cfg: dict, cache: dict) -> dict:
             dh = dh.astype(dt).copy()
             dh[..., :C] += dh_c
         dx = num.rnd(dx + rmsnorm_bwd(dh, c["h"], c["r"], num))
+        if resid:
+            # x = lr x_pre + l0 x0: x0's gradient gathers over the layers
+            dxp, dx0l, gex[2 * l], gex[2 * l + 1] = _ex.resid_mix_bwd(
+                dx, c["x_pre"], cache["x0"], ex[2 * l], ex[2 * l + 1])
+            dx0 = num.rnd(dx0l if dx0 is None else dx0 + dx0l)
+            dx = num.rnd(dxp)
 
+    if resid:
+        dx = num.rnd(dx + dx0)
+    if cfg.get("smear", 0):
+        D = dx.shape[-1]
+        w = ex[sl["smear_w"]:sl["smear_w"] + _ex.SMEAR_CH]
+        dxe, dw, dlam = _ex.smear_bwd(dx.reshape(-1, D), cache["x_emb"].reshape(-1, D), w,
+                                      ex[sl["smear_lambda"]], T)
+        gex[sl["smear_w"]:sl["smear_w"] + _ex.SMEAR_CH] = dw
+        gex[sl["smear_lambda"]] = dlam
+        dx = num.rnd(dxe).reshape(B, T, D)
     grads["wte"] = embedding_bwd(dx, inp, P["wte"].shape[0])
+    if ex is not None:
+        grads["extras"] = gex.astype(dt)
     return grads
 
 

@@ -6,7 +6,12 @@ an index, sign or transpose slip in either one shows up as a mismatch.  It
 follows the same readings: pre-norm RMSNorm without gain, half-split rotary
 pairs with theta = t * base^(-2j/hd), QK-norm after rotary, key j visible from
 query i iff 0 <= i-j <= W, KV head of query head h is h // (H/Hkv), value
-embeddings with gate 3*sigmoid(.) on odd layers, ReLU^2 MLP, untied head.
+embeddings with gate 3*sigmoid(.) on odd layers, ReLU^2 MLP, untied head;
+and, when the config turns them on, the model extras: smear of the previous
+position's embedding right after the lookup, per-block mixing with the
+post-smear stream before every block, and backout of the stream after block
+`backout_layer` once all blocks ran.  The extras vector follows Wlm: pairs
+(resid, x0) per layer, 24 smear weights, smear lambda, backout lambda.
 """
 import math
 
@@ -52,6 +57,13 @@ def brute_losses(cfg, flat, tokens):
             p["W"] = cfg["window_short"] if ch == "S" else cfg["window_long"]
         layers.append(p)
     wlm, off = _take(flat, off, V, D)
+    resid = bool(cfg.get("resid_lambdas", 0))
+    smear = bool(cfg.get("smear", 0))
+    bo = int(cfg.get("backout_layer", -1))
+    if resid or smear or bo >= 0:
+        n_ex = 8 * ((2 * L + 26 + 7) // 8)
+        ex = [float(v) for v in flat[off:off + n_ex]]
+        off += n_ex
     assert off == len(flat)
 
     out = []
@@ -59,7 +71,18 @@ def brute_losses(cfg, flat, tokens):
         row = [int(t) for t in row]
         T = len(row) - 1
         xs = [list(wte[row[t]]) for t in range(T)]
-        for p in layers:
+        if smear:
+            ws, lam = ex[2 * L:2 * L + 24], ex[2 * L + 24]
+            emb = [list(x) for x in xs]
+            for t in range(1, T):
+                z = sum(ws[c] * emb[t][c] for c in range(24))
+                gate = lam / (1.0 + math.exp(-z))
+                xs[t] = [emb[t][d] + gate * emb[t - 1][d] for d in range(D)]
+        x0s = [list(x) for x in xs]
+        for li, p in enumerate(layers):
+            if resid:
+                xs = [[ex[2 * li] * xs[t][d] + ex[2 * li + 1] * x0s[t][d] for d in range(D)]
+                      for t in range(T)]
             hs = [_rms(x, eps) for x in xs]
             qs, ks, vs = [], [], []
             for t in range(T):
@@ -106,6 +129,10 @@ def brute_losses(cfg, flat, tokens):
                 x = [x[d] + y for d, y in enumerate(_matvec(p["wproj"], a))]
                 new_x.append(x)
             xs = new_x
+            if li == bo:
+                mid = [list(x) for x in xs]
+        if bo >= 0:
+            xs = [[xs[t][d] - ex[2 * L + 25] * mid[t][d] for d in range(D)] for t in range(T)]
         losses = []
         for t in range(T):
             z = _matvec(wlm, _rms(xs[t], eps))

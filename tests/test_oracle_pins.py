@@ -27,12 +27,39 @@ def tiny_plus(**kw):
     return cfg
 
 
+def tiny_extras(**kw):
+    """tiny_plus widened to D = 32 (smear reads 24 channels) with residual
+    mixing, smear and backout after block 0 on."""
+    return dict(tiny_plus(), **dict(dict(d_model=32, resid_lambdas=1, smear=1, backout_layer=0),
+                                     **kw))
+
+
+def set_extras(cfg, w, seed=5):
+    """Put plausible values in the extras slots of a flat vector (in place):
+    resid lambdas near 1, x0 lambdas near 0.3, small smear weights, smear
+    lambda 0.6, backout lambda 0.35; padding zero."""
+    if not O.extras_on(cfg):
+        return w
+    sl = O.extras_slots(cfg)
+    off = O.param_count(cfg) - sl["size"]
+    rng = np.random.default_rng(seed)
+    ex = np.zeros(sl["size"])
+    L = cfg["n_layer"]
+    ex[0:2 * L:2] = 1.0 + 0.2 * rng.standard_normal(L)
+    ex[1:2 * L:2] = 0.3 + 0.1 * rng.standard_normal(L)
+    ex[sl["smear_w"]:sl["smear_w"] + 24] = 0.5 * rng.standard_normal(24)
+    ex[sl["smear_lambda"]] = 0.6
+    ex[sl["backout"]] = 0.35
+    w[off:off + sl["size"]] = ex
+    return w
+
+
 def inputs(cfg, rows=None, sigma=None):
     n = O.param_count(cfg)
     if sigma is not None:
         cfg = dict(cfg, sigma=sigma)
     w, _ = gi.make_params(cfg, n)
-    return w.astype(np.float64), gi.make_tokens(cfg, rows)
+    return set_extras(cfg, w.astype(np.float64)), gi.make_tokens(cfg, rows)
 
 
 # ---------------------------------------------------------------- P13, golden
@@ -71,9 +98,10 @@ def test_init_loss_matches_microgpt_start():
 
 
 # ------------------------------------------------------------ brute force fwd
-@pytest.mark.parametrize("which", ["tiny", "tiny_plus"])
+@pytest.mark.parametrize("which", ["tiny", "tiny_plus", "tiny_extras"])
 def test_forward_equals_scalar_brute_force(which):
-    cfg = gi.preset("tiny") if which == "tiny" else tiny_plus()
+    cfg = {"tiny": lambda: gi.preset("tiny"), "tiny_plus": tiny_plus,
+           "tiny_extras": tiny_extras}[which]()
     w, tok = inputs(cfg, rows=3)
     _, cache = O.forward(cfg, w, tok, "fp64", keep=False)
     ref = np.array(brute_losses(cfg, w, tok)).reshape(-1)
@@ -102,8 +130,10 @@ def test_finite_differences_tiny_all_params():
     assert err < 1e-6, err
 
 
-def test_finite_differences_tiny_plus_sampled():
-    cfg = tiny_plus()
+@pytest.mark.parametrize("which", ["tiny_plus", "tiny_extras", "extras_no_resid"])
+def test_finite_differences_tiny_plus_sampled(which):
+    cfg = {"tiny_plus": tiny_plus, "tiny_extras": tiny_extras,
+           "extras_no_resid": lambda: tiny_extras(resid_lambdas=0, backout_layer=1)}[which]()
     w, tok = inputs(cfg, rows=4)
     rng = np.random.default_rng(1)
     # a sample from every tensor, so no block's gradient goes unchecked
@@ -114,6 +144,27 @@ def test_finite_differences_tiny_plus_sampled():
         off += n
     err = _fd_check(cfg, w, tok, np.array(coords))
     assert err < 1e-6, err
+
+
+def test_neutral_extras_equal_the_plain_model():
+    """Mixing weights (1, 0), smear lambda 0 and backout lambda 0 leave the
+    stream as it is: the loss and every shared gradient equal those of the
+    same weights without the extras, and the extras' own gradients are the
+    sums their definitions give (d lambda_r = sum dx . x_pre is nonzero)."""
+    base = dict(tiny_plus(), d_model=32)
+    cfg = tiny_extras()
+    w, tok = inputs(base, rows=3)
+    sl = O.extras_slots(cfg)
+    ex = np.zeros(sl["size"])
+    ex[0:2 * cfg["n_layer"]:2] = 1.0
+    ex[sl["smear_w"]:sl["smear_w"] + 24] = 0.7
+    l0, g0, _ = O.step(base, w, tok, "fp64")
+    l1, g1, _ = O.step(cfg, np.concatenate([w, ex]), tok, "fp64")
+    assert l1 == pytest.approx(l0, rel=1e-14)
+    np.testing.assert_allclose(g1[:w.size], g0, rtol=1e-10, atol=1e-14)
+    gex = g1[w.size:]
+    assert np.all(gex[2 * cfg["n_layer"]:sl["smear_lambda"]] == 0.0)   # smear w: lambda 0
+    assert abs(gex[0]) > 1e-6 and gex[sl["smear_lambda"]] != 0.0
 
 
 # ------------------------------------------------------- P2 uniform logits
