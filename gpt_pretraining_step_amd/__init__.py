@@ -19,7 +19,7 @@ F32, BF16 = 0, 1
 MODE_TRAIN, MODE_EVAL = 0, 1
 GEMM_NT, GEMM_NN, GEMM_TN = 0, 1, 2
 EPI_STORE, EPI_RESADD, EPI_RELU2, EPI_DRELU2, EPI_F32, EPI_F32_ACC = range(6)
-P_WTE, P_WQKV, P_WO, P_WFC, P_WPROJ, P_VE, P_WG, P_WLM = range(8)
+P_WTE, P_WQKV, P_WO, P_WFC, P_WPROJ, P_VE, P_WG, P_WLM, P_EXTRAS = range(9)
 (WS_ELL, WS_LOSS, WS_NONFINITE, WS_X_H, WS_X_QKV, WS_X_O, WS_X_LSE, WS_X_H2,
  WS_X_A, WS_X_HF) = range(10)
 
@@ -39,6 +39,8 @@ class GptConfig(C.Structure):
         ("window_short", C.c_int32), ("window_long", C.c_int32),
         ("ve_every_odd", C.c_int32), ("rope_base", C.c_float),
         ("norm_eps", C.c_float), ("dtype", C.c_int32),
+        ("resid_lambdas", C.c_int32), ("smear", C.c_int32), ("backout", C.c_int32),
+        ("backout_layer", C.c_int32),
     ]
 
 
@@ -68,8 +70,14 @@ def make_optim_hparams(coeffs, muon_lr=0.02, muon_momentum=0.95, muon_wd=0.0, ne
 
 
 def make_config(d: dict) -> GptConfig:
-    """A GptConfig from a dict with the struct's field names."""
+    """A GptConfig from a dict with the struct's field names.  The model
+    extras default to off; backout_layer -1 (or absent) means no backout."""
     c = GptConfig()
+    d = dict(d)
+    d.setdefault("resid_lambdas", 0)
+    d.setdefault("smear", 0)
+    bl = int(d.get("backout_layer", -1))
+    d["backout"], d["backout_layer"] = (1, bl) if bl >= 0 else (0, 0)
     for name, _ in GptConfig._fields_:
         v = d[name]
         if name == "window_pattern":

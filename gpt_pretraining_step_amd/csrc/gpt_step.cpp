@@ -49,6 +49,12 @@ struct Model {
   int es;                     // element size of the storage dtype
   std::string pattern;
   int wS, wL;
+  // model extras: residual mixing, smear, backout after block `bo` (-1 off);
+  // slots of the extras vector
+  int resid, smear, bo;
+  int ex_n, ex_sw, ex_sl, ex_bo;
+
+  bool extras() const { return resid || smear || bo >= 0; }
 
   bool is_ve(int l) const { return ve_odd && (l % 2 == 1); }
   int window(int l) const {
@@ -89,6 +95,15 @@ int validate(const gpt_config* c, Model* m) {
   if (N > (1LL << 30) || (int64_t)c->mlp_mult * c->d_model > (1 << 30) || qkv > (1 << 30))
     return fail(GPT_ERR_UNSUPPORTED_CONFIG, "sizes too large");
   if (c->n_kv_head > 64) return fail(GPT_ERR_UNSUPPORTED_CONFIG, "n_kv_head > 64");
+  if ((c->resid_lambdas != 0 && c->resid_lambdas != 1) || (c->smear != 0 && c->smear != 1) ||
+      (c->backout != 0 && c->backout != 1))
+    return fail(GPT_ERR_INVALID_ARG, "resid_lambdas, smear and backout must be 0 or 1");
+  if (c->backout && (c->backout_layer < 0 || c->backout_layer >= c->n_layer))
+    return fail(GPT_ERR_INVALID_ARG, "backout_layer %d not in [0, n_layer)", c->backout_layer);
+  if ((c->resid_lambdas || c->smear || c->backout) && c->d_model % 8)
+    return fail(GPT_ERR_UNSUPPORTED_CONFIG, "model extras need d_model a multiple of 8");
+  if (c->smear && c->d_model < 24)
+    return fail(GPT_ERR_UNSUPPORTED_CONFIG, "smear reads 24 channels: d_model >= 24");
   if (m) {
     m->L = c->n_layer; m->D = c->d_model; m->H = c->n_head; m->Hkv = c->n_kv_head;
     m->hd = hd; m->V = c->vocab; m->T = c->seq_len; m->B = c->batch;
@@ -99,13 +114,19 @@ int validate(const gpt_config* c, Model* m) {
     m->es = c->dtype == GPT_BF16 ? 2 : 4;
     m->pattern.assign(c->window_pattern, plen);
     m->wS = c->window_short; m->wL = c->window_long;
+    m->resid = c->resid_lambdas; m->smear = c->smear;
+    m->bo = c->backout ? c->backout_layer : -1;
+    m->ex_sw = 2 * m->L;
+    m->ex_sl = 2 * m->L + 24;
+    m->ex_bo = 2 * m->L + 25;
+    m->ex_n = 8 * ((2 * m->L + 26 + 7) / 8);
   }
   return GPT_OK;
 }
 
 // element offsets of every tensor in the flat parameter buffer
 struct ParamLayout {
-  int64_t wte, wlm, total;
+  int64_t wte, wlm, extras, total;     // extras: -1 when no extra is on
   std::vector<int64_t> wqkv, wo, wfc, wproj, ve, wg;
 };
 
@@ -127,6 +148,8 @@ ParamLayout param_layout(const Model& m) {
     }
   }
   p.wlm = off; off += (int64_t)m.V * m.D;
+  p.extras = -1;
+  if (m.extras()) { p.extras = off; off += m.ex_n; }
   p.total = off;
   return p;
 }
@@ -142,6 +165,12 @@ struct Plan {
   bool fused_ce;         // lm_head + cross-entropy fused (no fp32 logits)
   size_t ce_stats, ce_zt;
   std::vector<LayerBufs> layers;     // train: one per layer; eval: one shared
+  // model extras: smear input and gates, the blocks' start x0, the stream
+  // before each block's mix (train, blocks >= 1), the kept backout stream;
+  // backward: x0's gradient, the kept stream's, the smear input's, and the
+  // scalar gradients' partials
+  size_t xe, sgate, x0, xmid, dx0, dxmid, dxe, ex_scr;
+  std::vector<size_t> xpre;
   // backward scratch
   size_t dx, dh, du, dout, dqkv, attn_scr, vez, vwg, sort, gemm_scr, gemm_scr_bytes;
   bool sorted_scatter;   // embedding-table gradients by the token sort (no atomics)
@@ -177,6 +206,21 @@ Plan make_plan(const Model& m, int mode) {
   p.ce_stats = p.fused_ce ? take(gk::lm_ce_stats_bytes(N, m.V)) : 0;
   p.ce_zt = p.fused_ce ? take(N * 4) : 0;
   p.dz = mode == GPT_MODE_TRAIN ? take((size_t)N * m.V * es) : 0;
+  const bool train = mode == GPT_MODE_TRAIN;
+  const size_t xbytes = (size_t)N * m.D * es;
+  p.xe = m.smear ? take(xbytes) : 0;
+  p.sgate = m.smear ? take(N * 4) : 0;
+  p.x0 = m.resid ? take(xbytes) : 0;
+  p.xmid = m.bo >= 0 ? take(xbytes) : 0;
+  p.xpre.assign(m.L, 0);
+  if (m.resid && train)
+    for (int l = 1; l < m.L; ++l) p.xpre[l] = take(xbytes);
+  p.dx0 = m.resid && train ? take(xbytes) : 0;
+  p.dxmid = m.bo >= 0 && train ? take(xbytes) : 0;
+  p.dxe = m.smear && train ? take(xbytes) : 0;
+  p.ex_scr = m.extras() && train ? take(std::max(gk::resid_mix_bwd_scratch_bytes(),
+                                                 gk::smear_bwd_scratch_bytes()))
+                                 : 0;
   const int nl = mode == GPT_MODE_TRAIN ? m.L : 1;
   for (int l = 0; l < nl; ++l) {
     LayerBufs b;
@@ -247,9 +291,28 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
   void* x = at<void>(ws, p.x);
   float* cs = at<float>(ws, p.cs);
   HIP_TRY(gk::rope_table(cs, m.T, m.hd, m.base, s));
-  HIP_TRY(gk::embed_fwd(tokens, rows, m.T, elem(params, pl.wte, es), x, m.D, dt, s));
+  // with the extras the embedding feeds smear, whose output is x0 (or the
+  // stream); mixing starts every block from the stream and x0
+  void* xe = m.smear ? at<void>(ws, p.xe) : nullptr;
+  void* x0 = m.resid ? at<void>(ws, p.x0) : nullptr;
+  void* xmid = m.bo >= 0 ? at<void>(ws, p.xmid) : nullptr;
+  const size_t xbytes = (size_t)N * m.D * es;
+  HIP_TRY(gk::embed_fwd(tokens, rows, m.T, elem(params, pl.wte, es), xe ? xe : (x0 ? x0 : x),
+                        m.D, dt, s));
+  if (m.smear)
+    HIP_TRY(gk::smear_fwd(xe, N, m.T, m.D, elem(params, pl.extras + m.ex_sw, es),
+                          elem(params, pl.extras + m.ex_sl, es), x0 ? x0 : x,
+                          at<float>(ws, p.sgate), dt, s));
   for (int l = 0; l < m.L; ++l) {
     const LayerBufs& b = p.layers[mode == GPT_MODE_TRAIN ? l : 0];
+    if (m.resid) {
+      // x = lr_l x + l0_l x0; the backward needs the stream before the mix
+      // (x0 itself for block 0)
+      void* save = mode == GPT_MODE_TRAIN && l > 0 ? at<void>(ws, p.xpre[l]) : nullptr;
+      HIP_TRY(gk::resid_mix_fwd(l == 0 ? x0 : x, x0, x, N * m.D,
+                                elem(params, pl.extras + 2 * l, es), dt, s, gk::MIX_LAMBDAS,
+                                save));
+    }
     void* h = at<void>(ws, b.h);
     void* qkv = at<void>(ws, b.qkv);
     void* o = at<void>(ws, b.o);
@@ -297,7 +360,11 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
     g = gk::GemmDesc{gk::OP_NT, N, m.D, m.F, a, m.F, elem(params, pl.wproj[l], es), m.F, x, m.D,
                      gk::E_RESADD, nullptr};
     HIP_TRY(gk::gemm(g, dt, s));
+    if (l == m.bo) HIP_TRY(hipMemcpyAsync(xmid, x, xbytes, hipMemcpyDeviceToDevice, s));
   }
+  if (m.bo >= 0)
+    HIP_TRY(gk::resid_mix_fwd(x, xmid, x, N * m.D, elem(params, pl.extras + m.ex_bo, es), dt, s,
+                              gk::MIX_BACKOUT));
   void* hf = at<void>(ws, p.hf);
   HIP_TRY(gk::rmsnorm_fwd(x, hf, at<float>(ws, p.rf), N, m.D, m.eps, dt, s));
   float* logits = at<float>(ws, p.logits);
@@ -364,6 +431,13 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
     for (int l = 0; l < m.L; ++l)
       if (m.is_ve(l)) HIP_TRY(gk::fill_zero(grads + pl.ve[l], (int64_t)m.V * m.Hkv * m.hd * 4, s));
   }
+  // the extras' scalar gradients are added up over their kernels
+  float* gex = m.extras() ? grads + pl.extras : nullptr;
+  void* exscr = at<void>(ws, p.ex_scr);
+  if (gex && !accumulate) HIP_TRY(gk::zero_f32(gex, m.ex_n, s));
+  void* x0 = m.resid ? at<void>(ws, p.x0) : nullptr;
+  void* dx0 = m.resid ? at<void>(ws, p.dx0) : nullptr;
+  void* dxmid = m.bo >= 0 ? at<void>(ws, p.dxmid) : nullptr;
   // lm_head
   gk::GemmDesc g{gk::OP_TN, m.V, m.D, N, dz, m.V, hf, m.D, grads + pl.wlm, m.D, wepi, nullptr};
   HIP_TRY(gk::gemm(g, dt, s));
@@ -372,8 +446,15 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
   HIP_TRY(gk::gemm(g, dt, s));
   HIP_TRY(gk::rmsnorm_bwd(dh, hf, at<float>(ws, p.rf), nullptr, dx, N, m.D, nullptr, nullptr, 0,
                           0, dt, s));
+  // backout x -= lambda_b x_kept: dx passes through, the kept stream's
+  // gradient is -lambda_b dx
+  if (m.bo >= 0)
+    HIP_TRY(gk::resid_mix_bwd(dx, nullptr, at<void>(ws, p.xmid), nullptr, dxmid, 0, N * m.D,
+                              elem(params, pl.extras + m.ex_bo, es), gex + m.ex_bo, exscr, dt, s,
+                              gk::MIX_BACKOUT, 1));
   for (int l = m.L - 1; l >= 0; --l) {
     const LayerBufs& b = p.layers[l];
+    if (l == m.bo) HIP_TRY(gk::resid_mix_fwd(dx, dxmid, dx, N * m.D, nullptr, dt, s, gk::MIX_ADD));
     const void* h = at<void>(ws, b.h);
     const void* qkv = at<void>(ws, b.qkv);
     const void* o = at<void>(ws, b.o);
@@ -446,12 +527,27 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
     HIP_TRY(gk::gemm(g, dt, s));
     HIP_TRY(gk::rmsnorm_bwd(dh, h, at<float>(ws, b.r), dx, dx, N, m.D, ve ? vez : nullptr,
                             ve ? elem(params, pl.wg[l], es) : nullptr, m.Hkv, m.C, dt, s));
+    // mix x = lr_l x_pre + l0_l x0: dx_pre = lr_l dx, x0's gradient gathers
+    // l0_l dx over the blocks
+    if (m.resid)
+      HIP_TRY(gk::resid_mix_bwd(dx, l == 0 ? x0 : at<void>(ws, p.xpre[l]), x0, dx, dx0,
+                                l < m.L - 1, N * m.D, elem(params, pl.extras + 2 * l, es),
+                                gex + 2 * l, exscr, dt, s, gk::MIX_LAMBDAS, 1));
+  }
+  if (m.resid) HIP_TRY(gk::resid_mix_fwd(dx, dx0, dx, N * m.D, nullptr, dt, s, gk::MIX_ADD));
+  void* demb = dx;
+  if (m.smear) {
+    demb = at<void>(ws, p.dxe);
+    HIP_TRY(gk::smear_bwd(dx, at<void>(ws, p.xe), N, m.T, m.D,
+                          elem(params, pl.extras + m.ex_sw, es),
+                          elem(params, pl.extras + m.ex_sl, es), at<float>(ws, p.sgate), demb,
+                          gex + m.ex_sw, exscr, dt, s, 1));
   }
   if (sorted)
-    HIP_TRY(gk::seg_scatter(sortws, N, m.V, maxW, dx, m.D, m.D, nullptr, 1, m.D, grads + pl.wte,
-                            accumulate, dt, s));
+    HIP_TRY(gk::seg_scatter(sortws, N, m.V, maxW, demb, m.D, m.D, nullptr, 1, m.D,
+                            grads + pl.wte, accumulate, dt, s));
   else
-    HIP_TRY(gk::embed_bwd(tokens, m.B, m.T, dx, m.D, grads + pl.wte, m.D, dt, s));
+    HIP_TRY(gk::embed_bwd(tokens, m.B, m.T, demb, m.D, grads + pl.wte, m.D, dt, s));
   return GPT_OK;
 }
 
@@ -484,6 +580,7 @@ int64_t gpt_param_offset(const gpt_config* cfg, int which, int layer) {
   ParamLayout p = param_layout(m);
   if (which == GPT_P_WTE) return p.wte;
   if (which == GPT_P_WLM) return p.wlm;
+  if (which == GPT_P_EXTRAS) return p.extras;
   if (layer < 0 || layer >= m.L) return fail(GPT_ERR_INVALID_ARG, "layer out of range");
   switch (which) {
     case GPT_P_WQKV: return p.wqkv[layer];
@@ -634,7 +731,7 @@ int gpt_optim_step(const gpt_config* cfg, const gpt_optim_hparams* hp, int32_t s
   if (ws_bytes < need) return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "ws needs %zu bytes", need);
   // every tensor starts on a 16-byte boundary in both copies
   auto ok_off = [&](int64_t off) { return off < 0 || off % 8 == 0; };
-  bool aligned = ok_off(pl.wte) && ok_off(pl.wlm);
+  bool aligned = ok_off(pl.wte) && ok_off(pl.wlm) && ok_off(pl.extras);
   for (int l = 0; l < m.L; ++l)
     aligned = aligned && ok_off(pl.wqkv[l]) && ok_off(pl.wo[l]) && ok_off(pl.wfc[l]) &&
               ok_off(pl.wproj[l]) && ok_off(pl.ve[l]) && ok_off(pl.wg[l]);
@@ -665,7 +762,7 @@ int gpt_optim_step(const gpt_config* cfg, const gpt_optim_hparams* hp, int32_t s
       HIP_TRY(gk::muon_update(master + off, x + l * n, n, lr, hp->muon_wd, p16(off), s));
     }
   }
-  // AdamW: embeddings and value-embedding tables, lm_head, gates
+  // AdamW: embeddings and value-embedding tables, lm_head, gates, extras
   auto adam = [&](int64_t off, int64_t n, float lr) -> int {
     HIP_TRY(gk::adamw(master + off, grads + off, state1 + off, state2 + off, n, step, lr,
                       hp->adam_beta1, hp->adam_beta2, hp->adam_eps, hp->adam_wd, p16(off), s));
@@ -678,6 +775,8 @@ int gpt_optim_step(const gpt_config* cfg, const gpt_optim_hparams* hp, int32_t s
     if ((st = adam(pl.ve[l], (int64_t)m.V * m.Hkv * m.hd, hp->adam_lr_embed))) return st;
     if ((st = adam(pl.wg[l], (int64_t)m.Hkv * m.C, hp->adam_lr_gate))) return st;
   }
+  // the model extras' scalars and smear weights, with the gates
+  if (pl.extras >= 0 && (st = adam(pl.extras, m.ex_n, hp->adam_lr_gate))) return st;
   return GPT_OK;
 }
 

@@ -5,7 +5,8 @@
 // g_t = lambda sigmoid(w . x_t[:24]) (no mix at a row's first position).
 // The scalars are device values of the storage type (parameters), their
 // gradients fp32 device values reduced in a fixed order (per-block partials,
-// then one block).  HBM-bound streams; smear takes one wave per token.
+// then one block), written or added to.  The mix kernels also serve as the
+// stream's plain add and its backout, and may work in place.  HBM-bound streams; smear takes one wave per token.
 #include <math.h>
 
 #include "common.h"
@@ -62,42 +63,63 @@ __device__ __forceinline__ double block_sum_d(double v, double* red) {
 }
 }  // namespace
 
-// y = lr x + l0 x0 (one rounding), runs of 8
+// the two weights of a mix: MIX_LAMBDAS (lam[0], lam[1]); MIX_BACKOUT (1,
+// -lam[0]); MIX_ADD (1, 1), lam unused
 template <typename T>
-__global__ __launch_bounds__(256) void k_resid_mix_fwd(const T* __restrict__ x,
-                                                       const T* __restrict__ x0,
-                                                       T* __restrict__ y, int64_t n8,
-                                                       const T* __restrict__ lam) {
-  const float lr = ld(lam, 0), l0 = ld(lam, 1);
+__device__ __forceinline__ void mix_weights(const T* lam, int mode, float& lr, float& l0) {
+  lr = 1.f;
+  l0 = 1.f;
+  if (mode == MIX_LAMBDAS) {
+    lr = ld(lam, 0);
+    l0 = ld(lam, 1);
+  } else if (mode == MIX_BACKOUT) {
+    l0 = -ld(lam, 0);
+  }
+}
+
+// y = lr x + l0 x0 (one rounding), runs of 8; y may be x (each thread reads
+// its run before writing it); `save`, if set, receives x
+template <typename T>
+__global__ __launch_bounds__(256) void k_resid_mix_fwd(const T* x, const T* __restrict__ x0,
+                                                       T* y, int64_t n8,
+                                                       const T* __restrict__ lam, int mode,
+                                                       T* __restrict__ save) {
+  float lr, l0;
+  mix_weights(lam, mode, lr, l0);
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
     float a[8], b[8];
     ld8(x, 8 * i, a);
     ld8(x0, 8 * i, b);
+    if (save) st8(save, 8 * i, a);
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[e] = fmaf(lr, a[e], l0 * b[e]);
     st8(y, 8 * i, a);
   }
 }
 
-// dx = lr dy; dx0 (+)= l0 dy; partials of sum dy x and sum dy x0
+// dx = lr dy (dx may be dy); dx0 (+)= l0 dy; per-block partials of the
+// scalars' gradients: MIX_LAMBDAS (sum dy x, sum dy x0); MIX_BACKOUT
+// (-sum dy x0, unused), x not read
 template <typename T>
 __global__ __launch_bounds__(256) void k_resid_mix_bwd(
-    const T* __restrict__ dy, const T* __restrict__ x, const T* __restrict__ x0,
-    T* __restrict__ dx, T* __restrict__ dx0, int accumulate, int64_t n8,
-    const T* __restrict__ lam, double* __restrict__ part) {
+    const T* dy, const T* __restrict__ x, const T* __restrict__ x0, T* dx,
+    T* __restrict__ dx0, int accumulate, int64_t n8, const T* __restrict__ lam, int mode,
+    double* __restrict__ part) {
   __shared__ double red[4];
-  const float lr = ld(lam, 0), l0 = ld(lam, 1);
+  float lr, l0;
+  mix_weights(lam, mode, lr, l0);
+  const bool want_x = mode == MIX_LAMBDAS;
   float sx = 0.f, s0 = 0.f;
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
     float g[8], a[8], b[8], o[8];
     ld8(dy, 8 * i, g);
-    ld8(x, 8 * i, a);
+    if (want_x) ld8(x, 8 * i, a);
     ld8(x0, 8 * i, b);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      sx = fmaf(g[e], a[e], sx);
+      if (want_x) sx = fmaf(g[e], a[e], sx);
       s0 = fmaf(g[e], b[e], s0);
       o[e] = lr * g[e];
     }
@@ -110,22 +132,24 @@ __global__ __launch_bounds__(256) void k_resid_mix_bwd(
   const double tx = block_sum_d(sx, red);
   const double t0 = block_sum_d(s0, red);
   if (threadIdx.x == 0) {
-    part[2 * blockIdx.x] = tx;
+    part[2 * blockIdx.x] = want_x ? tx : -t0;
     part[2 * blockIdx.x + 1] = t0;
   }
 }
 
-// out[k] (fp32) = sum over `nparts` partial records of width `width` (k <
-// width), fixed order: thread t sums records t, t + 256, ..., then a fixed
-// shuffle tree and the four waves in order; one block
+// out[k] (fp32) = (out[k] if accumulate) + sum over `nparts` partial records
+// spaced `stride` apart (k < width <= stride), fixed order: thread t sums
+// records t, t + 256, ..., then a fixed shuffle tree and the four waves in
+// order; one block
 __global__ __launch_bounds__(256) void k_sum_parts(const double* __restrict__ part, int nparts,
-                                                   int width, float* __restrict__ out) {
+                                                   int stride, int width, int accumulate,
+                                                   float* __restrict__ out) {
   __shared__ double red[4];
   for (int k = 0; k < width; ++k) {
     double v = 0.0;
-    for (int p = threadIdx.x; p < nparts; p += 256) v += part[(int64_t)p * width + k];
+    for (int p = threadIdx.x; p < nparts; p += 256) v += part[(int64_t)p * stride + k];
     v = block_sum_d(v, red);
-    if (threadIdx.x == 0) out[k] = (float)v;
+    if (threadIdx.x == 0) out[k] = accumulate ? out[k] + (float)v : (float)v;
   }
 }
 
@@ -219,43 +243,58 @@ __global__ __launch_bounds__(256) void k_smear_bwd(const T* __restrict__ dy,
   }
 }
 
+// p[0..n) = 0 with 4-byte stores (any float alignment)
+__global__ __launch_bounds__(256) void k_zero_f32(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0.f;
+}
+
+hipError_t zero_f32(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const unsigned nb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(1024, cdiv(n, 256)));
+  GK_LAUNCH(Work(0.0, 4.0 * n), k_zero_f32, dim3(nb), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 size_t resid_mix_bwd_scratch_bytes() { return kMixBlocks * 2 * sizeof(double); }
 size_t smear_bwd_scratch_bytes() { return kSmearBlocks * (kSmearCh + 1) * sizeof(double); }
 
 hipError_t resid_mix_fwd(const void* x, const void* x0, void* y, int64_t n, const void* lam,
-                         DType dt, hipStream_t s) {
+                         DType dt, hipStream_t s, int mode, void* save) {
   const int64_t n8 = n / 8;
   const unsigned nb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(4096, cdiv(n8, 256)));
-  const Work w(0.0, 3.0 * n * (dt == BF16 ? 2 : 4));
+  const Work w(0.0, (3.0 + (save ? 1.0 : 0.0)) * n * (dt == BF16 ? 2 : 4));
   if (dt == BF16)
     GK_LAUNCH(w, k_resid_mix_fwd<bf16>, dim3(nb), dim3(256), 0, s, (const bf16*)x,
-              (const bf16*)x0, (bf16*)y, n8, (const bf16*)lam);
+              (const bf16*)x0, (bf16*)y, n8, (const bf16*)lam, mode, (bf16*)save);
   else
     GK_LAUNCH(w, k_resid_mix_fwd<float>, dim3(nb), dim3(256), 0, s, (const float*)x,
-              (const float*)x0, (float*)y, n8, (const float*)lam);
+              (const float*)x0, (float*)y, n8, (const float*)lam, mode, (float*)save);
   return hipGetLastError();
 }
 
 hipError_t resid_mix_bwd(const void* dy, const void* x, const void* x0, void* dx, void* dx0,
                          int accumulate, int64_t n, const void* lam, float* dlam, void* scratch,
-                         DType dt, hipStream_t s) {
+                         DType dt, hipStream_t s, int mode, int accumulate_dlam) {
   const int64_t n8 = n / 8;
   const unsigned nb =
       (unsigned)std::max<int64_t>(1, std::min<int64_t>(kMixBlocks, cdiv(n8, 256 * 4)));
   double* part = (double*)scratch;
   const int es = dt == BF16 ? 2 : 4;
-  const Work w(0.0, (double)n * es * (3 + (dx ? 1 : 0) + 1 + (accumulate ? 1 : 0)));
+  const int reads = 2 + (mode == MIX_LAMBDAS ? 1 : 0) + (accumulate ? 1 : 0);
+  const Work w(0.0, (double)n * es * (reads + (dx ? 1 : 0) + 1));
   if (dt == BF16)
     GK_LAUNCH(w, k_resid_mix_bwd<bf16>, dim3(nb), dim3(256), 0, s, (const bf16*)dy,
               (const bf16*)x, (const bf16*)x0, (bf16*)dx, (bf16*)dx0, accumulate, n8,
-              (const bf16*)lam, part);
+              (const bf16*)lam, mode, part);
   else
     GK_LAUNCH(w, k_resid_mix_bwd<float>, dim3(nb), dim3(256), 0, s, (const float*)dy,
               (const float*)x, (const float*)x0, (float*)dx, (float*)dx0, accumulate, n8,
-              (const float*)lam, part);
+              (const float*)lam, mode, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  GK_LAUNCH(Work(), k_sum_parts, dim3(1), dim3(256), 0, s, (const double*)part, (int)nb, 2, dlam);
+  GK_LAUNCH(Work(), k_sum_parts, dim3(1), dim3(256), 0, s, (const double*)part, (int)nb, 2,
+            mode == MIX_LAMBDAS ? 2 : 1, accumulate_dlam, dlam);
   return hipGetLastError();
 }
 
@@ -274,7 +313,7 @@ hipError_t smear_fwd(const void* x, int64_t rows, int T, int D, const void* w, c
 
 hipError_t smear_bwd(const void* dy, const void* x, int64_t rows, int T, int D, const void* w,
                      const void* lam, const float* gate, void* dx, float* dw_dlam,
-                     void* scratch, DType dt, hipStream_t s) {
+                     void* scratch, DType dt, hipStream_t s, int accumulate_dw) {
   const unsigned nb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(kSmearBlocks,
                                                                          cdiv(rows, 16)));
   double* part = (double*)scratch;
@@ -291,7 +330,7 @@ hipError_t smear_bwd(const void* dy, const void* x, int64_t rows, int T, int D, 
   if (e != hipSuccess) return e;
   // dw[0..24) and dlambda at [24]
   GK_LAUNCH(Work(), k_sum_parts, dim3(1), dim3(256), 0, s, (const double*)part, (int)nb,
-            kSmearCh + 1, dw_dlam);
+            kSmearCh + 1, kSmearCh + 1, accumulate_dw, dw_dlam);
   return hipGetLastError();
 }
 

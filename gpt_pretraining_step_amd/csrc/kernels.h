@@ -200,24 +200,32 @@ hipError_t muon_update(float* w, const void* x, int64_t n, float lr, float wd, v
                        hipStream_t s);
 hipError_t adamw(float* w, const float* g, float* m, float* v, int64_t n, int step, float lr,
                  float b1, float b2, float eps, float wd, void* w16, hipStream_t s);
-// Model extras.  resid_mix: y = lam[0] x + lam[1] x0 (lam: 2 device values
-// of the storage type; backout is lam = (1, -lambda)); backward dx = lam[0]
-// dy (dx may be null), dx0 (+)= lam[1] dy, dlam[0..2) = sums of dy x, dy x0.
+// Model extras.  resid_mix: y = lr x + l0 x0 with (lr, l0) by `mode`:
+// MIX_LAMBDAS (lam[0], lam[1]), lam 2 device values of the storage type;
+// MIX_BACKOUT (1, -lam[0]); MIX_ADD (1, 1).  y may be x; `save` (optional)
+// receives x.  Backward dx = lr dy (dx may be null or dy), dx0 (+)= l0 dy,
+// dlam (=, or += with accumulate_dlam): MIX_LAMBDAS [0..2) = sums of dy x,
+// dy x0; MIX_BACKOUT [0] = -sum dy x0 (x unused).
 // smear: y_t = x_t + g_t x_(t-1), g_t = lam[0] sigmoid(w . x_t[:24]),
-// g_t = 0 at a row's first position (rows of T tokens); backward dx and
-// dw_dlam[0..24) = dw, [24] = dlambda.  n, D multiples of 8.
+// g_t = 0 at a row's first position (rows of T tokens); backward dx (not
+// dy) and dw_dlam[0..24) = dw, [24] = dlambda (= or +=).  n, D multiples
+// of 8.
+enum { MIX_LAMBDAS = 0, MIX_BACKOUT = 1, MIX_ADD = 2 };
+// p[0..n) = 0 for fp32 at any 4-byte alignment (a kernel, not a memset)
+hipError_t zero_f32(float* p, int64_t n, hipStream_t s);
 size_t resid_mix_bwd_scratch_bytes();
 size_t smear_bwd_scratch_bytes();
 hipError_t resid_mix_fwd(const void* x, const void* x0, void* y, int64_t n, const void* lam,
-                         DType dt, hipStream_t s);
+                         DType dt, hipStream_t s, int mode = MIX_LAMBDAS, void* save = nullptr);
 hipError_t resid_mix_bwd(const void* dy, const void* x, const void* x0, void* dx, void* dx0,
                          int accumulate, int64_t n, const void* lam, float* dlam, void* scratch,
-                         DType dt, hipStream_t s);
+                         DType dt, hipStream_t s, int mode = MIX_LAMBDAS,
+                         int accumulate_dlam = 0);
 hipError_t smear_fwd(const void* x, int64_t rows, int T, int D, const void* w, const void* lam,
                      void* y, float* gate, DType dt, hipStream_t s);
 hipError_t smear_bwd(const void* dy, const void* x, int64_t rows, int T, int D, const void* w,
                      const void* lam, const float* gate, void* dx, float* dw_dlam,
-                     void* scratch, DType dt, hipStream_t s);
+                     void* scratch, DType dt, hipStream_t s, int accumulate_dw = 0);
 hipError_t loss_reduce(const float* ell, int64_t N, float* loss_ws,
                        float* loss_out, int* flag, hipStream_t s);
 // acc[0] += sum ell, acc[1] += sum bytes[tgt]; if final, acc[2] = bpb

@@ -68,6 +68,16 @@ enum { GPT_MODE_TRAIN = 0, GPT_MODE_EVAL = 1 };
  *   norm_eps: added to the mean square inside every RMSNorm root.
  *   dtype: GPT_BF16 (bf16 storage, fp32 accumulation, fp32 softmax/CE) or
  *   GPT_F32 (fp32 storage).
+ *   Model extras (nanochat walkthrough, "1. GPT model", efficiency tricks),
+ *   each off when 0 (a zero-filled tail keeps the plain model):
+ *   resid_lambdas: 1 = before block l the stream becomes lr_l x + l0_l x0,
+ *     x0 the stream the blocks start from.
+ *   smear: 1 = right after the embedding, x_t += g_t x_(t-1) with g_t =
+ *     lambda_s sigmoid(w_s . x_t[:24]), g = 0 at a row's first position
+ *     (needs D >= 24).
+ *   backout: 1 = the stream after block backout_layer (0 <= it < n_layer)
+ *     is kept and, after the last block, x -= lambda_b x_kept.
+ *   With any extra on, D must be a multiple of 8.
  */
 typedef struct gpt_config {
   int32_t n_layer, d_model, n_head, n_kv_head, head_dim, vocab, seq_len, batch;
@@ -77,6 +87,7 @@ typedef struct gpt_config {
   int32_t ve_every_odd;
   float rope_base, norm_eps;
   int32_t dtype;
+  int32_t resid_lambdas, smear, backout, backout_layer;
 } gpt_config;
 
 /* ------------------------------------------------------- sizes and layout */
@@ -89,11 +100,15 @@ typedef struct gpt_config {
  *                Wo [D, H hd], Wfc [F, D], Wproj [D, F],
  *                and on value-embedding layers E_l [V, Hkv hd], Wg [Hkv, C]
  *   Wlm [V, D]
+ *   extras [8 ceil((2 L + 26) / 8)], only when a model extra is on: lr_l at
+ *     2 l, l0_l at 2 l + 1, w_s at 2 L .. 2 L + 23, lambda_s at 2 L + 24,
+ *     lambda_b at 2 L + 25, zero padding after (slots of extras that are
+ *     off are unused, their gradients zero)
  * Gradients use the same layout in fp32.
  */
 enum {
   GPT_P_WTE = 0, GPT_P_WQKV, GPT_P_WO, GPT_P_WFC, GPT_P_WPROJ, GPT_P_VE,
-  GPT_P_WG, GPT_P_WLM
+  GPT_P_WG, GPT_P_WLM, GPT_P_EXTRAS
 };
 
 /* Number of parameters (elements), or a negative status for a bad config. */
@@ -101,7 +116,8 @@ int64_t gpt_param_count(const gpt_config* cfg);
 
 /* Element offset of tensor `which` (GPT_P_*) of `layer` in the flat buffer;
  * -1 if that layer has no such tensor; a status < -1 for a bad argument.
- * `layer` is ignored for GPT_P_WTE and GPT_P_WLM. */
+ * `layer` is ignored for GPT_P_WTE, GPT_P_WLM and GPT_P_EXTRAS (-1 when no
+ * extra is on). */
 int64_t gpt_param_offset(const gpt_config* cfg, int which, int layer);
 
 /* Workspace bytes needed by gpt_step_fwd/bwd (GPT_MODE_TRAIN) or by
@@ -167,7 +183,8 @@ int gpt_eval_bpb(const gpt_config* cfg, const void* params,
  *   W <- W (1 - lr wd) - lr X with lr = muon_lr max(1, rows / cols)^0.5.
  *   AdamW (state1 = m, state2 = v, step counts from 1): wte and the value-
  *   embedding tables at adam_lr_embed, Wlm at adam_lr_head, the value-
- *   embedding gates at adam_lr_gate.
+ *   embedding gates and the extras vector (the model extras' scalars and
+ *   smear weights, when present) at adam_lr_gate.
  *   master, grads, state1, state2: device fp32 in the flat layout (states
  *   zero before step 1).  params: the dtype copy the step reads, written
  *   from the updated master (bf16 configs; may be null for fp32 configs,

@@ -36,6 +36,37 @@ def tiny_plus():
                      window_long=16, ve_every_odd=1, ve_gate_channels=8)
 
 
+def set_extras(cfg, w, seed=5):
+    """Put plausible values in the extras slots of a flat vector (in place):
+    resid lambdas near 1, x0 lambdas near 0.3, small smear weights, smear
+    lambda 0.6, backout lambda 0.35; padding zero."""
+    if not O.extras_on(cfg):
+        return w
+    sl = O.extras_slots(cfg)
+    off = O.param_count(cfg) - sl["size"]
+    rng = np.random.default_rng(seed)
+    ex = np.zeros(sl["size"])
+    L = cfg["n_layer"]
+    ex[0:2 * L:2] = 1.0 + 0.2 * rng.standard_normal(L)
+    ex[1:2 * L:2] = 0.3 + 0.1 * rng.standard_normal(L)
+    ex[sl["smear_w"]:sl["smear_w"] + 24] = 0.5 * rng.standard_normal(24)
+    ex[sl["smear_lambda"]] = 0.6
+    ex[sl["backout"]] = 0.35
+    w[off:off + sl["size"]] = ex
+    return w
+
+
+def with_extras(cfg, w, bits):
+    """(values, bf16 bits or None) of a flat vector whose extras slots hold
+    set_extras' values, rounded to bf16 for bf16 configs so both sides see
+    the same numbers."""
+    w = set_extras(cfg, np.asarray(w, np.float32).copy())
+    if bits is None:
+        return w, None
+    b = gi.bf16_bits_from_f32(w)
+    return gi.f32_from_bf16_bits(b), b
+
+
 def grads_by_tensor(cfg, flat):
     out, off = {}, 0
     for name, shape in O.param_layout(cfg):

@@ -36,9 +36,17 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(G.exported_symbols())
 
 
-@pytest.mark.parametrize("name", list(gi.PRESETS))
+_EXTRAS = dict(resid_lambdas=1, smear=1, backout_layer=2)
+
+
+@pytest.mark.parametrize("name", list(gi.PRESETS) + ["d4+extras", "d12+backout"])
 def test_param_layout_matches_oracle(name):
-    d = gi.preset(name)
+    if name == "d4+extras":
+        d = gi.preset("d4", **_EXTRAS)
+    elif name == "d12+backout":
+        d = gi.preset("d12", backout_layer=5)
+    else:
+        d = gi.preset(name)
     c = G.make_config(d)
     assert G.param_count(c) == O.param_count(d)
     off, layers = 0, {}
@@ -54,6 +62,11 @@ def test_param_layout_matches_oracle(name):
         assert G.param_offset(c, G.P_WPROJ, l) == layers[f"l{l}.wproj"]
         assert G.param_offset(c, G.P_VE, l) == layers.get(f"l{l}.ve", -1)
         assert G.param_offset(c, G.P_WG, l) == layers.get(f"l{l}.wg", -1)
+    assert G.param_offset(c, G.P_EXTRAS) == layers.get("extras", -1)
+    if "extras" in layers:
+        assert O.extras_slots(d) == dict(smear_w=2 * d["n_layer"], smear_lambda=2 * d["n_layer"] + 24,
+                                         backout=2 * d["n_layer"] + 25,
+                                         size=G.param_count(c) - layers["extras"])
 
 
 def test_workspace_sizes():
@@ -62,6 +75,14 @@ def test_workspace_sizes():
         tr, ev = G.workspace_bytes(c, G.MODE_TRAIN), G.workspace_bytes(c, G.MODE_EVAL)
         assert tr > ev > 0
         assert tr % 256 == 0
+        # the extras add the saved streams (x0, the kept stream, one per block
+        # after the first, their gradients, the smear input)
+        ce = G.make_config(gi.preset(name, **_EXTRAS, d_model=max(32, gi.preset(name)["d_model"])))
+        if gi.preset(name)["d_model"] >= 32:
+            d = gi.preset(name)
+            xb = d["batch"] * d["seq_len"] * d["d_model"] * (2 if d["dtype"] == G.BF16 else 4)
+            assert G.workspace_bytes(ce, G.MODE_TRAIN) - tr >= (d["n_layer"] + 5) * xb
+            assert G.workspace_bytes(ce, G.MODE_EVAL) - ev >= 3 * xb
     # d24 training state fits one 288 GB device with room to spare
     assert G.workspace_bytes(G.make_config(gi.preset("d24"))) < 64 << 30
 
@@ -82,6 +103,10 @@ def _bad(**kw):
     (dict(ve_gate_channels=0), -1),
     (dict(ve_gate_channels=4096), -1),
     (dict(window_short=-1), -1),
+    (dict(backout_layer=4), -1),
+    (dict(smear=2), -1),
+    (dict(resid_lambdas=1, d_model=252, n_head=2, head_dim=128), -2),
+    (dict(smear=1, d_model=16, n_head=2, head_dim=8, ve_gate_channels=8), -2),
 ])
 def test_invalid_configs_rejected(kw, status):
     c = _bad(**kw)

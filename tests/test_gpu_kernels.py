@@ -963,7 +963,7 @@ def test_smear(B, T, D, dt):
 
 
 # ------------------------------------------------------ whole optimizer step
-@pytest.mark.parametrize("which", ["small_bf16", "tiny"])
+@pytest.mark.parametrize("which", ["small_bf16", "tiny", "small_bf16_extras"])
 def test_optim_step(which):
     """gpt_optim_step over every tensor of a model, two steps, against the
     oracle's Muon (momentum, exact Newton-Schulz, lr max(1, rows/cols)^0.5
@@ -973,7 +973,9 @@ def test_optim_step(which):
     from oracle import muon
     from tests.gpu_util import small_bf16, tiny_plus
     import gptinputs as gi
-    cfgd = small_bf16() if which == "small_bf16" else tiny_plus()
+    cfgd = {"small_bf16": small_bf16, "tiny": tiny_plus,
+            "small_bf16_extras": lambda: small_bf16(resid_lambdas=1, smear=1,
+                                                    backout_layer=1)}[which]()
     say("optim step", which)
     cfg = G.make_config(cfgd)
     n = O.param_count(cfgd)
@@ -1012,7 +1014,8 @@ def test_optim_step(which):
             assert rel_err(d_got, d_ref) < 2e-2, name
         else:
             lr = {"wte": hpd["adam_lr_embed"], "ve": hpd["adam_lr_embed"],
-                  "wlm": hpd["adam_lr_head"], "wg": hpd["adam_lr_gate"]}[base]
+                  "wlm": hpd["adam_lr_head"], "wg": hpd["adam_lr_gate"],
+                  "extras": hpd["adam_lr_gate"]}[base]
             m = v = np.zeros(shape)
             for k in range(2):
                 w, m, v = muon.adamw(w, grads[k][sl].reshape(shape), m, v, k + 1, lr,

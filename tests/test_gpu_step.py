@@ -13,7 +13,7 @@ import pytest
 
 import gptinputs as gi
 import oracle as O
-from tests.gpu_util import grads_by_tensor, rel_err, small_bf16, tiny_plus, to_np
+from tests.gpu_util import grads_by_tensor, rel_err, small_bf16, tiny_plus, to_np, with_extras
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +38,7 @@ def _prec(cfg):
 
 def run_step(cfg, rows=None, accumulate_check=False):
     n = O.param_count(cfg)
-    w, bits = gi.make_params(cfg, n)
+    w, bits = with_extras(cfg, *gi.make_params(cfg, n))
     tok = gi.make_tokens(cfg, rows)
     if rows is not None:
         cfg = dict(cfg, batch=rows)
@@ -73,7 +73,8 @@ def compare(cfg, w, tok, loss, ell, grads, flag):
     ref = grads_by_tensor(cfg, ref_g)
     errs = {k: rel_err(got[k], ref[k]) for k in ref}
     say("grad errors", {k: f"{v:.2e}" for k, v in errs.items()})
-    bad = {k: v for k, v in errs.items() if not v < (TOL if prec == "bf16emu" else 1e-4)}
+    bad = {k: (v, int(np.argmax(np.abs(got[k] - ref[k]))))
+           for k, v in errs.items() if not v < (TOL if prec == "bf16emu" else 1e-4)}
     assert not bad, bad
 
 
@@ -98,13 +99,40 @@ def test_step_matches_oracle(name):
     compare(*out)
 
 
-@pytest.mark.parametrize("name,n_rows", [("tiny", 11), ("small_bf16", 7), ("d4", 20)])
+_EXTRAS = {
+    # residual mixing, smear and backout after block 0 (bf16, GQA, windows,
+    # value embeddings)
+    "small_bf16_extras": lambda: small_bf16(resid_lambdas=1, smear=1, backout_layer=0),
+    # smear and backout, no mixing, three layers (backing out the last
+    # block's own output only rescales the stream the final RMSNorm sees, so
+    # its lambda's gradient is a cancellation down to the norm's eps)
+    "small_bf16_smear_backout": lambda: small_bf16(n_layer=3, smear=1, backout_layer=1),
+    # mixing alone, four layers of fp32
+    "tiny_resid_f32": lambda: gi.preset("tiny", n_layer=4, d_model=32, resid_lambdas=1),
+    "tiny_extras_f32": lambda: dict(tiny_plus(), d_model=32, resid_lambdas=1, smear=1,
+                                    backout_layer=1),
+    "d4_extras": lambda: gi.preset("d4", resid_lambdas=1, smear=1, backout_layer=2),
+}
+
+
+@pytest.mark.parametrize("name", list(_EXTRAS))
+def test_step_with_extras_matches_oracle(name):
+    """The model extras inside the fused step (forward, backward, scalar
+    gradients) against the oracle; gradient accumulation adds."""
+    cfg = _EXTRAS[name]()
+    say("step extras", name)
+    out = run_step(cfg, accumulate_check=name in ("small_bf16_extras", "tiny_extras_f32"))
+    compare(*out)
+
+
+@pytest.mark.parametrize("name,n_rows", [("tiny", 11), ("small_bf16", 7), ("d4", 20),
+                                         ("small_bf16_extras", 7)])
 def test_eval_bpb_matches_oracle(name, n_rows):
     cfg = {"tiny": lambda: gi.preset("tiny"), "small_bf16": small_bf16,
-           "d4": lambda: gi.preset("d4")}[name]()
+           "d4": lambda: gi.preset("d4"), **_EXTRAS}[name]()
     say("eval", name, n_rows)
     n = O.param_count(cfg)
-    w, bits = gi.make_params(cfg, n)
+    w, bits = with_extras(cfg, *gi.make_params(cfg, n))
     tok = gi.make_eval_tokens(cfg, n_rows)          # ragged last batch
     tb = gi.make_token_bytes(cfg)
     s = Session(cfg, eval_ws=True, train_ws=False)
@@ -170,12 +198,16 @@ def test_deterministic_forward():
     assert torch.equal(a, s.ws_f32(G.WS_ELL, N))
 
 
-def test_deterministic_backward():
-    """Every gradient, the embedding tables' sorted scatter included, is a
-    fixed-order sum: two backward passes agree bit for bit."""
+@pytest.mark.parametrize("extras", [False, True])
+def test_deterministic_backward(extras):
+    """Every gradient, the embedding tables' sorted scatter and the extras'
+    scalar sums included, is a fixed-order sum: two backward passes agree
+    bit for bit."""
     cfg = small_bf16(batch=4, seq_len=256)
+    if extras:
+        cfg.update(resid_lambdas=1, smear=1, backout_layer=0)
     n = O.param_count(cfg)
-    w, bits = gi.make_params(cfg, n)
+    w, bits = with_extras(cfg, *gi.make_params(cfg, n))
     s = Session(cfg)
     s.set_params(w, bits)
     s.set_tokens(gi.make_tokens(cfg))

@@ -15,6 +15,7 @@ import gptinputs as gi
 import oracle as O
 from oracle.gpt import _Num
 from tests.brute_force import brute_losses
+from tests.gpu_util import set_extras
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -32,26 +33,6 @@ def tiny_extras(**kw):
     mixing, smear and backout after block 0 on."""
     return dict(tiny_plus(), **dict(dict(d_model=32, resid_lambdas=1, smear=1, backout_layer=0),
                                      **kw))
-
-
-def set_extras(cfg, w, seed=5):
-    """Put plausible values in the extras slots of a flat vector (in place):
-    resid lambdas near 1, x0 lambdas near 0.3, small smear weights, smear
-    lambda 0.6, backout lambda 0.35; padding zero."""
-    if not O.extras_on(cfg):
-        return w
-    sl = O.extras_slots(cfg)
-    off = O.param_count(cfg) - sl["size"]
-    rng = np.random.default_rng(seed)
-    ex = np.zeros(sl["size"])
-    L = cfg["n_layer"]
-    ex[0:2 * L:2] = 1.0 + 0.2 * rng.standard_normal(L)
-    ex[1:2 * L:2] = 0.3 + 0.1 * rng.standard_normal(L)
-    ex[sl["smear_w"]:sl["smear_w"] + 24] = 0.5 * rng.standard_normal(24)
-    ex[sl["smear_lambda"]] = 0.6
-    ex[sl["backout"]] = 0.35
-    w[off:off + sl["size"]] = ex
-    return w
 
 
 def inputs(cfg, rows=None, sigma=None):
@@ -165,6 +146,22 @@ def test_neutral_extras_equal_the_plain_model():
     gex = g1[w.size:]
     assert np.all(gex[2 * cfg["n_layer"]:sl["smear_lambda"]] == 0.0)   # smear w: lambda 0
     assert abs(gex[0]) > 1e-6 and gex[sl["smear_lambda"]] != 0.0
+
+
+def test_backout_of_the_last_block_only_rescales():
+    """Backing out the last block's own output gives x (1 - lambda_b) ahead
+    of the final RMSNorm: the loss equals the plain model's with the final
+    stream scaled, and d loss / d lambda_b vanishes but for the norm's eps
+    (here eps -> 1e-30 makes it exact to rounding)."""
+    cfg = tiny_extras(resid_lambdas=0, smear=0, backout_layer=1, norm_eps=1e-30)
+    w, tok = inputs(cfg, rows=3)
+    sl = O.extras_slots(cfg)
+    _, g, _ = O.step(cfg, w, tok, "fp64")
+    assert abs(g[-sl["size"] + sl["backout"]]) < 1e-12
+    base = dict(cfg, backout_layer=-1)
+    l0, _ = O.forward(base, w[:-sl["size"]], tok, "fp64", keep=False)
+    l1, _ = O.forward(cfg, w, tok, "fp64", keep=False)
+    assert l1 == pytest.approx(l0, rel=1e-12)
 
 
 # ------------------------------------------------------- P2 uniform logits
