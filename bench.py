@@ -768,6 +768,9 @@ def main():
                          "step's linear layers as FP8 linear layers; muon: Muon's "
                          "orthogonalization of every matrix update; optim: the whole optimizer "
                          "step; extras: smear, residual lambdas and backout")
+    ap.add_argument("--model-extras", action="store_true",
+                    help="train: turn on residual mixing, smear and backout (after the middle "
+                         "block) inside the step")
     ap.add_argument("--decode-batch", type=int, default=64,
                     help="sequences sampled in parallel (decode workload)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -811,6 +814,8 @@ def main():
         return
     a.config = a.config or "d12"
     cfg = gi.preset(a.config)
+    if a.model_extras:
+        cfg.update(resid_lambdas=1, smear=1, backout_layer=cfg["n_layer"] // 2)
     train_fpt, eval_fpt, mm = model_flops(cfg)
     B, T = cfg["batch"], cfg["seq_len"]
     tokens_per_step = B * T
@@ -818,6 +823,14 @@ def main():
     log("building inputs", a.config)
     s = Session(cfg, eval_ws=True)
     w, bits = gi.make_params(cfg, s.n_params)
+    if a.model_extras:
+        # the extras vector's slots (C ABI layout): mixing weights (1, 0.1)
+        # per block, smear lambda 0.5, backout lambda 0.2
+        L, off = cfg["n_layer"], G.param_offset(s.cfg, G.P_EXTRAS)
+        w[off:off + 2 * L:2], w[off + 1:off + 2 * L:2] = 1.0, 0.1
+        w[off + 2 * L + 24], w[off + 2 * L + 25] = 0.5, 0.2
+        bits = gi.bf16_bits_from_f32(w)
+        w = gi.f32_from_bf16_bits(bits)
     s.set_params(w, bits)
     s.set_tokens(gi.make_tokens(cfg))
     del w, bits
@@ -905,7 +918,9 @@ def main():
                                f"heads ({cfg['n_kv_head']} KV), vocab {cfg['vocab']}, "
                                f"{B} rows x T={T} ({tokens_per_step} tokens), windows "
                                f"'{cfg['window_pattern']}' {cfg['window_short']}/"
-                               f"{cfg['window_long']}, value embeddings on odd layers",
+                               f"{cfg['window_long']}, value embeddings on odd layers"
+                               + (f", model extras (residual mixing, smear, backout after "
+                                  f"block {cfg['backout_layer']})" if a.model_extras else ""),
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "mfu_bf16": round(mfu, 4), "train_flop_per_token": train_fpt,
         "optimizer_ms_per_step": round(opt_ms, 3),
