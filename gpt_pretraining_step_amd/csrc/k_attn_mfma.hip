@@ -26,7 +26,14 @@ using namespace attn;
 
 static constexpr int NW = 4;                   // waves per workgroup
 static constexpr int QW = 32;                  // queries per wave (2 blocks of 16)
-static constexpr int FWD_BQ = NW * QW;         // queries per workgroup
+// forward: 32 queries per wave at two waves per SIMD (48 or 64 queries at
+// one wave per SIMD halve the LDS reads per product but measured 6-25%
+// slower: the second wave hides the softmax and the tile waits)
+static constexpr int FWD_QW = 32;              // forward: queries per wave
+static constexpr int FQB = FWD_QW / 16;        // forward: 16-query blocks per wave
+static constexpr int FWD_OCC = 2;              // forward: workgroups per CU (launch bound)
+static constexpr int FWD_BQ = NW * FWD_QW;     // forward: queries per workgroup
+static constexpr int DQ_BQ = NW * QW;          // backward dQ: queries per workgroup
 static constexpr float kLog2e = 1.4426950408889634f;
 static constexpr float kLn2 = 0.6931471805599453f;
 static constexpr float kLazy = 8.0f;           // forward: offset lag allowed (log2 units)
@@ -37,6 +44,27 @@ __device__ __forceinline__ void key_range(int q_lo, int q_hi, int W, int& lo, in
   hi = q_hi;
 }
 
+// Block numbering of the attention grids: the dispatcher deals workgroups
+// round-robin over the 8 XCDs (each with its own L2), so a 1-D grid of
+// 8 ceil(nblk npair / 8) ids is renumbered to give each XCD a contiguous
+// run of whole (row, head) pairs, each pair's nblk blocks in the order
+// blk = nblk - 1, ..., 0.  The blocks of one pair then stream the same
+// tiles through one L2 at about the same time.  False for padding ids.
+__device__ __forceinline__ bool xcd_block(int nblk, int npair, int& pair, int& blk) {
+  const int nb = nblk * npair;
+  const int per_xcd = (nb + 7) / 8;
+  const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (logical >= nb) return false;
+  pair = logical / nblk;
+  blk = nblk - 1 - logical % nblk;
+  return true;
+}
+
+__host__ inline dim3 xcd_grid(int nblk, int npair) {
+  const int64_t nb = (int64_t)nblk * npair;
+  return dim3((unsigned)(8 * ((nb + 7) / 8)));
+}
+
 // BOUNDED: the caller guarantees |q . k| / sqrt(hd) <= bound for every pair
 // (true after QK-norm: RMS-normalised rows have norm <= sqrt(hd)), passed as
 // off2 = bound * log2(e).  Then p = 2^(s log2(e) / sqrt(hd) - off2) <= 1 for
@@ -45,24 +73,28 @@ __device__ __forceinline__ void key_range(int q_lo, int q_hi, int W, int& lo, in
 // of the unrounded P).  Without a bound the offset follows the running
 // maximum.
 template <bool BOUNDED>
-__global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict__ qkv,
+__global__ __launch_bounds__(256, FWD_OCC) void k_attn_fwd_mfma(const bf16* __restrict__ qkv,
                                                           bf16* __restrict__ o,
-                                                          float* __restrict__ lse, int T, int H,
-                                                          int Hkv, int W, float off2) {
+                                                          float* __restrict__ lse, int B, int T,
+                                                          int H, int Hkv, int W, float off2) {
   // two stages of (K tile, V tile), filled by buffer loads straight into LDS
   __shared__ __attribute__((aligned(16))) bf16 kv[2][2][TR * HD];
 
+  // which (row, head) and query block, longest first, XCD-contiguous
   const int nqb = (T + FWD_BQ - 1) / FWD_BQ;
-  const int qblk = nqb - 1 - (int)blockIdx.x;          // long rows first
-  const int h = blockIdx.y, b = blockIdx.z;
+  int pair, qblk;
+  if (!xcd_block(nqb, H * B, pair, qblk)) return;
+  const int h = pair % H, b = pair / H;
   const int kvh = h / (H / Hkv);
   const int64_t ldq = (int64_t)(H + 2 * Hkv) * HD;
   const bf16* rowbase = qkv + (int64_t)b * T * ldq;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform: said so, the per-wave tile tests below are
+  // scalar branches rather than per-lane selects
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = lane >> 4, lr = lane & 15;
   const int q0 = qblk * FWD_BQ;
-  const int qw = q0 + wave * QW;                       // this wave's first query
+  const int qw = q0 + wave * FWD_QW;                       // this wave's first query
   const float sl2 = kLog2e / sqrtf((float)HD);        // scores in log2 units
 
   const bf16* kbase = rowbase + (int64_t)(H + kvh) * HD;
@@ -77,9 +109,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
   td.issue(vbase, T, kt0 * TR, kv[0][1], wave);
 
   // this wave's queries as MFMA Y operands: qf[qb][ks]
-  bf16x8_t qf[2][4];
+  bf16x8_t qf[FQB][4];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < FQB; ++qb) {
     const int qi = qw + 16 * qb + lr;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -89,63 +121,55 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
     }
   }
   // running max (raw score units) and sum per query
-  float m[2], l[2];
-  f32x4_t oacc[8][2];
+  float m[FQB], l[FQB];
+  f32x4_t oacc[8][FQB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < FQB; ++qb) {
     m[qb] = -INFINITY;
     l[qb] = 0.f;
 #pragma unroll
     for (int hb = 0; hb < 8; ++hb) oacc[hb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // one key tile; the loop below is unrolled by two so every LDS address
-  // names its stage statically (fragment addresses become per-lane bases
-  // plus immediate offsets, no per-tile address arithmetic)
-  auto tile = [&](int kt, auto stc) {
-    const int k0 = kt * TR;
+  // S = K Q^T for one stage, softmax, O += V^T P; the causal / window mask
+  // unless every pair of the wave's tile is visible
+  auto tile_body = [&](int k0, auto stc, bool full) {
     constexpr int st = decltype(stc)::value;
-    dma_wait();
-    __syncthreads();                                   // stage st filled, stage st^1 free
-    if (kt < kt1) {
-      td.issue(kbase, T, k0 + TR, kv[st ^ 1][0], wave);
-      td.issue(vbase, T, k0 + TR, kv[st ^ 1][1], wave);
-    }
     const bf16* Ks = kv[st][0];
     const bf16* Vs = kv[st][1];
-    // pairs of this wave: queries [qw, qw+31], keys [k0, k0+63]
-    const bool any = (qw + QW - 1 >= k0) && (qw - (k0 + TR - 1) <= W) && qw < T;
-    const bool full = (qw >= k0 + TR - 1) && (qw + QW - 1 - k0 <= W);
-    if (!any) return;
-    f32x4_t s[4][2];
+    f32x4_t s[4][FQB];
+    // contraction step outermost: 4 FQB independent accumulators per step
+    // keep the matrix pipeline busy between dependent products
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const bf16x8_t kf0 = dfrag_row(Ks, 16 * kb + lr, 0, g);
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t kf[4];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma(kf0, qf[qb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+      for (int kb = 0; kb < 4; ++kb) kf[kb] = dfrag_row(Ks, 16 * kb + lr, ks, g);
 #pragma unroll
-      for (int ks = 1; ks < 4; ++ks) {
-        const bf16x8_t kf = dfrag_row(Ks, 16 * kb + lr, ks, g);
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma(kf, qf[qb][ks], s[kb][qb]);
-      }
+        for (int qb = 0; qb < FQB; ++qb)
+          s[kb][qb] = mfma(kf[kb], qf[qb][ks],
+                           ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : s[kb][qb]);
     }
     // mask (tiles on the diagonal or the window edge only: a wave-uniform
     // branch between two copies of the loop)
     if (!full) {
+      // d = query - key from one per-tile base
+      const int base = qw + lr - 4 * g - k0;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < FQB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int d = qw + 16 * qb + lr - (k0 + 16 * kb + 4 * g + r);
+            const int d = base + (16 * qb - 16 * kb - r);
             s[kb][qb][r] = (unsigned)d > (unsigned)W ? -INFINITY : s[kb][qb][r];
           }
     }
     if constexpr (BOUNDED) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < FQB; ++qb) {
         float ls = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -159,9 +183,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
       }
     } else {
     bool grew = false;
-    float alpha[2];
+    float alpha[FQB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < FQB; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -192,24 +216,43 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
     // rescale the output only when some running max of the wave moved
     if (__builtin_amdgcn_ballot_w64(grew)) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < FQB; ++qb)
 #pragma unroll
         for (int hb = 0; hb < 8; ++hb) oacc[hb][qb] *= alpha[qb];
     }
     }
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
-      bf16x8_t pf[2];
+      bf16x8_t pf[FQB];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) pf[qb] = pack8(s[2 * ch][qb], s[2 * ch + 1][qb]);
+      for (int qb = 0; qb < FQB; ++qb) pf[qb] = pack8(s[2 * ch][qb], s[2 * ch + 1][qb]);
 #pragma unroll
       for (int hb = 0; hb < 8; ++hb) {
         const bf16x8_t vf = dfrag_col(Vs, 16 * hb, 32 * ch + 4 * g, 32 * ch + 16 + 4 * g, lr);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) oacc[hb][qb] = mfma(vf, pf[qb], oacc[hb][qb]);
+        for (int qb = 0; qb < FQB; ++qb) oacc[hb][qb] = mfma(vf, pf[qb], oacc[hb][qb]);
       }
     }
-    };
+  };
+
+  // one key tile; the loop below is unrolled by two so every LDS address
+  // names its stage statically (fragment addresses become per-lane bases
+  // plus immediate offsets, no per-tile address arithmetic)
+  auto tile = [&](int kt, auto stc) {
+    const int k0 = kt * TR;
+    constexpr int st = decltype(stc)::value;
+    dma_wait();
+    __syncthreads();                                   // stage st filled, stage st^1 free
+    if (kt < kt1) {
+      td.issue(kbase, T, k0 + TR, kv[st ^ 1][0], wave);
+      td.issue(vbase, T, k0 + TR, kv[st ^ 1][1], wave);
+    }
+    // pairs of this wave: queries [qw, qw+31], keys [k0, k0+63]
+    const bool any = (qw + FWD_QW - 1 >= k0) && (qw - (k0 + TR - 1) <= W) && qw < T;
+    const bool full = (qw >= k0 + TR - 1) && (qw + FWD_QW - 1 - k0 <= W);
+    if (!any) return;
+    tile_body(k0, stc, full);
+  };
   int kt = kt0;
   for (; kt + 1 <= kt1; kt += 2) {
     tile(kt, std::integral_constant<int, 0>());
@@ -219,7 +262,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(const bf16* __restrict
 
   // normalise and store: lane holds O[query][16 hb + 4 g + r]
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < FQB; ++qb) {
     float lt = l[qb];
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
@@ -246,17 +289,17 @@ bool attn_mfma_supported(int T, int H, int Hkv, int hd) {
 hipError_t attn_mfma_fwd(const void* qkv, void* o, float* lse, int B, int T, int H, int Hkv,
                          int hd, int W, hipStream_t s, float score_bound) {
   (void)hd;
-  dim3 grid((T + FWD_BQ - 1) / FWD_BQ, H, B);
+  const dim3 grid = xcd_grid((T + FWD_BQ - 1) / FWD_BQ, H * B);
   // 2 hd flops per visible pair for each of S = Q K^T and O = P V; q, k, v
   // read once, o and lse written once
   const double pairs = (double)B * H * visible_pairs(T, W), tok = (double)B * T;
   const Work w(4.0 * HD * pairs, tok * HD * 2 * (2.0 * H + 2 * Hkv) + tok * H * 4);
   if (score_bound > 0.f)
     GK_LAUNCH(w, k_attn_fwd_mfma<true>, grid, dim3(NW * 64), 0, s, (const bf16*)qkv, (bf16*)o,
-              lse, T, H, Hkv, W, score_bound * kLog2e);
+              lse, B, T, H, Hkv, W, score_bound * kLog2e);
   else
     GK_LAUNCH(w, k_attn_fwd_mfma<false>, grid, dim3(NW * 64), 0, s, (const bf16*)qkv, (bf16*)o,
-              lse, T, H, Hkv, W, 0.f);
+              lse, B, T, H, Hkv, W, 0.f);
   return hipGetLastError();
 }
 
@@ -356,19 +399,22 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
                                                          const bf16* __restrict__ dout,
                                                          const float* __restrict__ lse,
                                                          const float* __restrict__ delta,
-                                                         bf16* __restrict__ dqkv, int T, int H,
-                                                         int Hkv, int W, NormBwdArgs nb) {
+                                                         bf16* __restrict__ dqkv, int B, int T,
+                                                         int H, int Hkv, int W, NormBwdArgs nb) {
   __shared__ __attribute__((aligned(16))) bf16 qd[2][2][TR * HD];   // stages of (Q, dO)
   __shared__ __attribute__((aligned(16))) float ldl[2][2][256];      // stages of (lse, delta)
 
   const int nkb = (T + KV_BK - 1) / KV_BK;
-  const int kblk = nkb - 1 - (int)blockIdx.x;
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  int pair, kblk;
+  if (!xcd_block(nkb, Hkv * B, pair, kblk)) return;
+  const int kvh = pair % Hkv, b = pair / Hkv;
   const int G = H / Hkv;
   const int64_t ldq = (int64_t)(H + 2 * Hkv) * HD, ldo = (int64_t)H * HD;
   const bf16* rowbase = qkv + (int64_t)b * T * ldq;
   const bf16* obase = dout + (int64_t)b * T * ldo;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform: said so, the per-wave tile tests below are
+  // scalar branches rather than per-lane selects
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = lane >> 4, lr = lane & 15;
   const int k0 = kblk * KV_BK;
   const int kw = k0 + 32 * wave;                      // this wave's first key
@@ -568,28 +614,31 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(const bf16* __restrict__
                                                         const bf16* __restrict__ dout,
                                                         const float* __restrict__ lse,
                                                         const float* __restrict__ delta,
-                                                        bf16* __restrict__ dqkv, int T, int H,
-                                                        int Hkv, int W, NormBwdArgs nb) {
+                                                        bf16* __restrict__ dqkv, int B, int T,
+                                                        int H, int Hkv, int W, NormBwdArgs nb) {
   __shared__ __attribute__((aligned(16))) bf16 kv[2][2][TR * HD];   // stages of (K, V)
 
-  const int nqb = (T + FWD_BQ - 1) / FWD_BQ;
-  const int qblk = nqb - 1 - (int)blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int nqb = (T + DQ_BQ - 1) / DQ_BQ;
+  int pair, qblk;
+  if (!xcd_block(nqb, H * B, pair, qblk)) return;
+  const int h = pair % H, b = pair / H;
   const int kvh = h / (H / Hkv);
   const int64_t ldq = (int64_t)(H + 2 * Hkv) * HD, ldo = (int64_t)H * HD;
   const bf16* rowbase = qkv + (int64_t)b * T * ldq;
   const bf16* kbase = rowbase + (int64_t)(H + kvh) * HD;
   const bf16* vbase = rowbase + (int64_t)(H + Hkv + kvh) * HD;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform: said so, the per-wave tile tests below are
+  // scalar branches rather than per-lane selects
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = lane >> 4, lr = lane & 15;
-  const int q0 = qblk * FWD_BQ;
+  const int q0 = qblk * DQ_BQ;
   const int qw = q0 + wave * QW;
   const float sl2 = kLog2e / sqrtf((float)HD);
 
   TileDma td;
   td.init(ldq, wave, lane);
   int klo, khi;
-  key_range(q0, min(q0 + FWD_BQ, T) - 1, W, klo, khi);
+  key_range(q0, min(q0 + DQ_BQ, T) - 1, W, klo, khi);
   const int kt0 = klo / TR, kt1 = khi / TR;
   td.issue(kbase, T, kt0 * TR, kv[0][0], wave);
   td.issue(vbase, T, kt0 * TR, kv[0][1], wave);
@@ -751,11 +800,11 @@ hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const
             (const bf16*)o, (const bf16*)dout, delta, T, H, rows);
   // dK and dV in two passes (two waves per SIMD each; measured faster than
   // the one-wave-per-SIMD combined pass despite recomputing S)
-  const dim3 gkv((T + KV_BK - 1) / KV_BK, Hkv, B);
+  const dim3 gkv = xcd_grid((T + KV_BK - 1) / KV_BK, Hkv * B);
   const Work wk(6.0 * HD * pairs, qkvo + stats + tok * Hkv * HD * 2);
   const Work wv(4.0 * HD * pairs, qkvo + stats / 2 + tok * Hkv * HD * 2);
-  const dim3 gq((T + FWD_BQ - 1) / FWD_BQ, H, B);
-#define DKV_ARGS (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, T, H, Hkv, W, nb
+  const dim3 gq = xcd_grid((T + DQ_BQ - 1) / DQ_BQ, H * B);
+#define DKV_ARGS (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, B, T, H, Hkv, W, nb
   if (fuse) {
     GK_LAUNCH(wk, (k_attn_bwd_dkv<2, 1, true>), gkv, dim3(NW * 64), 0, s, DKV_ARGS);
     GK_LAUNCH(wv, (k_attn_bwd_dkv<2, 2, false>), gkv, dim3(NW * 64), 0, s, DKV_ARGS);
