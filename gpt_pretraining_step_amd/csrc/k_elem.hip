@@ -994,24 +994,40 @@ __global__ __launch_bounds__(512) void k_ce_fix(const float2* __restrict__ stats
   const int tgt = direct ? tok[row] : tok[(row / T) * (T + 1) + row % T + 1];
   uint4* p = (uint4*)(dz + row * (int64_t)V);
   typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-  for (int k = threadIdx.x; k < V / 8; k += 512) {
-    const uint4 u = p[k];
-    const float c = ct[(8 * k) >> 8];
-    const uint32_t* wu = (const uint32_t*)&u;
-    float f[8];
+  // four 16-byte runs per thread in flight before the first store (the
+  // stores would otherwise hold every next load behind them)
+  constexpr int U = 4;
+  const int n8 = V / 8;
+  for (int k0 = threadIdx.x; k0 < n8; k0 += 512 * U) {
+    uint4 u[U];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const h2_t h = __builtin_bit_cast(h2_t, wu[e]);
-      f[2 * e] = (float)h[0] * c;
-      f[2 * e + 1] = (float)h[1] * c;
+    for (int i = 0; i < U; ++i)
+      if (k0 + 512 * i < n8) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)(p + k0 + 512 * i));
+        u[i] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int k = k0 + 512 * i;
+      if (k >= n8) break;
+      const float c = ct[(8 * k) >> 8];
+      const uint32_t* wu = (const uint32_t*)&u[i];
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const h2_t h = __builtin_bit_cast(h2_t, wu[e]);
+        f[2 * e] = (float)h[0] * c;
+        f[2 * e + 1] = (float)h[1] * c;
+      }
+      if ((tgt >> 3) == k) f[tgt & 7] -= scale;
+      uint4 o;
+      o.x = pack2bf(f[0], f[1]);
+      o.y = pack2bf(f[2], f[3]);
+      o.z = pack2bf(f[4], f[5]);
+      o.w = pack2bf(f[6], f[7]);
+      p[k] = o;
     }
-    if ((tgt >> 3) == k) f[tgt & 7] -= scale;
-    uint4 o;
-    o.x = pack2bf(f[0], f[1]);
-    o.y = pack2bf(f[2], f[3]);
-    o.z = pack2bf(f[4], f[5]);
-    o.w = pack2bf(f[6], f[7]);
-    p[k] = o;
   }
 }
 
