@@ -21,7 +21,7 @@ import pytest
 
 import gptinputs as gi
 import oracle as O
-from tests.gpu_util import grads_by_tensor, rel_err, to_np
+from tests.gpu_util import grads_by_tensor, rel_err, to_np, with_extras
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,7 @@ import gpt_pretraining_step_amd as G  # noqa: E402
 from gpt_pretraining_step_amd.session import Session  # noqa: E402
 
 TOL = 2e-2
-NAMES = ["d12", "d12gqa", "d24"]
+NAMES = ["d12", "d12gqa", "d24", "d12+extras"]
 
 
 def say(*a):
@@ -47,9 +47,14 @@ _cache = {}
 def model(name):
     """Preset, oracle-side fp32 weights and the bf16 bits, cached per preset."""
     if name not in _cache:
-        cfg = gi.preset(name)
+        if name == "d12+extras":
+            # the d12 step with residual mixing, smear and backout after
+            # the middle block
+            cfg = gi.preset("d12", resid_lambdas=1, smear=1, backout_layer=6)
+        else:
+            cfg = gi.preset(name)
         n = O.param_count(cfg)
-        w, bits = gi.make_params(cfg, n)
+        w, bits = with_extras(cfg, *gi.make_params(cfg, n))
         _cache.clear()
         _cache[name] = (cfg, w, bits)
     return _cache[name]
