@@ -407,6 +407,9 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
   const int nkb = (T + KV_BK - 1) / KV_BK;
   int pair, kblk;
   if (!xcd_block(nkb, Hkv * B, pair, kblk)) return;
+  // under the causal mask the first key blocks see the most queries: they
+  // go first
+  kblk = nkb - 1 - kblk;
   const int kvh = pair % Hkv, b = pair / Hkv;
   const int G = H / Hkv;
   const int64_t ldq = (int64_t)(H + 2 * Hkv) * HD, ldo = (int64_t)H * HD;
