@@ -288,7 +288,8 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
   const int64_t N = (int64_t)rows * m.T;
   const int es = m.es;
   const gk::DType dt = m.dt;
-  void* x = at<void>(ws, p.x);
+  void* x = at<void>(ws, p.x);            // the current block's stream
+  void* const xfinal = x;                  // the last block's stream
   float* cs = at<float>(ws, p.cs);
   HIP_TRY(gk::rope_table(cs, m.T, m.hd, m.base, s));
   // with the extras the embedding feeds smear, whose output is x0 (or the
@@ -305,20 +306,31 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
                           at<float>(ws, p.sgate), dt, s));
   for (int l = 0; l < m.L; ++l) {
     const LayerBufs& b = p.layers[mode == GPT_MODE_TRAIN ? l : 0];
-    if (m.resid) {
-      // x = lr_l x + l0_l x0; the backward needs the stream before the mix
-      // (x0 itself for block 0)
-      void* save = mode == GPT_MODE_TRAIN && l > 0 ? at<void>(ws, p.xpre[l]) : nullptr;
-      HIP_TRY(gk::resid_mix_fwd(l == 0 ? x0 : x, x0, x, N * m.D,
-                                elem(params, pl.extras + 2 * l, es), dt, s, gk::MIX_LAMBDAS,
-                                save));
-    }
     void* h = at<void>(ws, b.h);
     void* qkv = at<void>(ws, b.qkv);
     void* o = at<void>(ws, b.o);
     void* h2 = at<void>(ws, b.h2);
     void* a = at<void>(ws, b.a);
-    HIP_TRY(gk::rmsnorm_fwd(x, h, at<float>(ws, b.r), N, m.D, m.eps, dt, s));
+    if (m.resid) {
+      // stream = lr_l stream + l0_l x0 ahead of the block's norm (one pass
+      // where the kernel allows).  In training each block has its own
+      // stream buffer, so the stream before the mix (x0 for block 0) stays
+      // for the backward: block l writes block l+1's pre-mix buffer (the
+      // last block writes x); otherwise the mix works in place.
+      const void* xin = l == 0 ? x0 : x;
+      void* xo = mode == GPT_MODE_TRAIN && l < m.L - 1 ? at<void>(ws, p.xpre[l + 1]) : xfinal;
+      const void* lam = elem(params, pl.extras + 2 * l, es);
+      if (gk::rmsnorm_fwd_mix_ok(m.D, dt)) {
+        HIP_TRY(gk::rmsnorm_fwd_mix(xin, x0, lam, xo, h, at<float>(ws, b.r), N, m.D, m.eps, dt,
+                                    s));
+      } else {
+        HIP_TRY(gk::resid_mix_fwd(xin, x0, xo, N * m.D, lam, dt, s));
+        HIP_TRY(gk::rmsnorm_fwd(xo, h, at<float>(ws, b.r), N, m.D, m.eps, dt, s));
+      }
+      x = xo;
+    } else {
+      HIP_TRY(gk::rmsnorm_fwd(x, h, at<float>(ws, b.r), N, m.D, m.eps, dt, s));
+    }
     // RoPE then QK-norm touch only q and k, the value embedding only v: with
     // head_dim 128 the rotation and norm run in the QKV product's epilogue
     const bool qk_fused =

@@ -173,9 +173,14 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const Tv* x, Tv* y, float* 
 }
 
 // bf16 rows with D % 8 == 0: 16-byte vectors, the row kept in registers.
-template <int VPL>
+// MIX: the row is first mixed, x = bf16(lam[0] x + lam[1] x0) (the model
+// extras' residual mixing ahead of a block), stored to xout (may be x) and
+// normalised as rounded.
+template <int VPL, bool MIX = false>
 __global__ __launch_bounds__(256) void k_rmsnorm_fwd_v(const bf16* x, bf16* y, float* r,
-                                                       int64_t rows, int D, float eps) {
+                                                       int64_t rows, int D, float eps,
+                                                       const bf16* x0, const bf16* lam,
+                                                       bf16* xout) {
   int lane = threadIdx.x & 63;
   int64_t row = blockIdx.x * (int64_t)(blockDim.x >> 6) + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -183,10 +188,28 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd_v(const bf16* x, bf16* y, f
   int nv = D >> 3;
   uint4 buf[VPL];
   float ss = 0.f;
+  float lr = 0.f, l0 = 0.f;
+  if constexpr (MIX) {
+    lr = ld(lam, 0);
+    l0 = ld(lam, 1);
+  }
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
     int v = lane + 64 * k;
     buf[k] = v < nv ? xr[v] : make_uint4(0, 0, 0, 0);
+    if constexpr (MIX) {
+      if (v < nv) {
+        const uint4 u0 = ((const uint4*)(x0 + row * D))[v];
+        uint32_t* w = (uint32_t*)&buf[k];
+        const uint32_t* w0 = (const uint32_t*)&u0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = pack2bf(fmaf(lr, __uint_as_float(w[e] << 16), l0 * __uint_as_float(w0[e] << 16)),
+                         fmaf(lr, __uint_as_float(w[e] & 0xFFFF0000u),
+                              l0 * __uint_as_float(w0[e] & 0xFFFF0000u)));
+        ((uint4*)(xout + row * D))[v] = buf[k];
+      }
+    }
     const uint32_t* w = (const uint32_t*)&buf[k];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -221,18 +244,44 @@ hipError_t rmsnorm_fwd(const void* x, void* y, float* r, int64_t rows, int D,
   if (dt == BF16 && D % 8 == 0 && D <= 64 * 8 * 4) {
     int vpl = (int)cdiv(D / 8, 64);
     if (vpl == 1)
-      GK_LAUNCH(w, k_rmsnorm_fwd_v<1>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
+      GK_LAUNCH(w, k_rmsnorm_fwd_v<1>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps,
+                nullptr, nullptr, nullptr);
     else if (vpl == 2)
-      GK_LAUNCH(w, k_rmsnorm_fwd_v<2>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
+      GK_LAUNCH(w, k_rmsnorm_fwd_v<2>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps,
+                nullptr, nullptr, nullptr);
     else if (vpl == 3)
-      GK_LAUNCH(w, k_rmsnorm_fwd_v<3>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
+      GK_LAUNCH(w, k_rmsnorm_fwd_v<3>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps,
+                nullptr, nullptr, nullptr);
     else
-      GK_LAUNCH(w, k_rmsnorm_fwd_v<4>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
+      GK_LAUNCH(w, k_rmsnorm_fwd_v<4>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps,
+                nullptr, nullptr, nullptr);
   } else if (dt == BF16) {
     GK_LAUNCH(w, k_rmsnorm_fwd<bf16>, grid, block, 0, s, (const bf16*)x, (bf16*)y, r, rows, D, eps);
   } else {
     GK_LAUNCH(w, k_rmsnorm_fwd<float>, grid, block, 0, s, (const float*)x, (float*)y, r, rows, D, eps);
   }
+  return hipGetLastError();
+}
+
+bool rmsnorm_fwd_mix_ok(int D, DType dt) { return dt == BF16 && D % 8 == 0 && D <= 64 * 8 * 4; }
+
+hipError_t rmsnorm_fwd_mix(const void* x, const void* x0, const void* lam, void* xout, void* y,
+                           float* r, int64_t rows, int D, float eps, DType dt, hipStream_t s) {
+  if (!rmsnorm_fwd_mix_ok(D, dt)) return hipErrorInvalidValue;
+  dim3 grid((unsigned)cdiv(rows, 4)), block(256);
+  const Work w(0.0, (double)rows * D * 2 * 4 + rows * 4.0);   // x, x0 in; xout, y out; r
+  const int vpl = (int)cdiv(D / 8, 64);
+#define GK_MIX_ARGS (const bf16*)x, (bf16*)y, r, rows, D, eps, (const bf16*)x0, (const bf16*)lam, \
+                    (bf16*)xout
+  if (vpl == 1)
+    GK_LAUNCH(w, (k_rmsnorm_fwd_v<1, true>), grid, block, 0, s, GK_MIX_ARGS);
+  else if (vpl == 2)
+    GK_LAUNCH(w, (k_rmsnorm_fwd_v<2, true>), grid, block, 0, s, GK_MIX_ARGS);
+  else if (vpl == 3)
+    GK_LAUNCH(w, (k_rmsnorm_fwd_v<3, true>), grid, block, 0, s, GK_MIX_ARGS);
+  else
+    GK_LAUNCH(w, (k_rmsnorm_fwd_v<4, true>), grid, block, 0, s, GK_MIX_ARGS);
+#undef GK_MIX_ARGS
   return hipGetLastError();
 }
 

@@ -78,12 +78,11 @@ __device__ __forceinline__ void mix_weights(const T* lam, int mode, float& lr, f
 }
 
 // y = lr x + l0 x0 (one rounding), runs of 8; y may be x (each thread reads
-// its run before writing it); `save`, if set, receives x
+// its run before writing it)
 template <typename T>
 __global__ __launch_bounds__(256) void k_resid_mix_fwd(const T* x, const T* __restrict__ x0,
                                                        T* y, int64_t n8,
-                                                       const T* __restrict__ lam, int mode,
-                                                       T* __restrict__ save) {
+                                                       const T* __restrict__ lam, int mode) {
   float lr, l0;
   mix_weights(lam, mode, lr, l0);
   const int64_t stride = (int64_t)gridDim.x * 256;
@@ -91,7 +90,6 @@ __global__ __launch_bounds__(256) void k_resid_mix_fwd(const T* x, const T* __re
     float a[8], b[8];
     ld8(x, 8 * i, a);
     ld8(x0, 8 * i, b);
-    if (save) st8(save, 8 * i, a);
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[e] = fmaf(lr, a[e], l0 * b[e]);
     st8(y, 8 * i, a);
@@ -260,16 +258,16 @@ size_t resid_mix_bwd_scratch_bytes() { return kMixBlocks * 2 * sizeof(double); }
 size_t smear_bwd_scratch_bytes() { return kSmearBlocks * (kSmearCh + 1) * sizeof(double); }
 
 hipError_t resid_mix_fwd(const void* x, const void* x0, void* y, int64_t n, const void* lam,
-                         DType dt, hipStream_t s, int mode, void* save) {
+                         DType dt, hipStream_t s, int mode) {
   const int64_t n8 = n / 8;
   const unsigned nb = (unsigned)std::max<int64_t>(1, std::min<int64_t>(4096, cdiv(n8, 256)));
-  const Work w(0.0, (3.0 + (save ? 1.0 : 0.0)) * n * (dt == BF16 ? 2 : 4));
+  const Work w(0.0, 3.0 * n * (dt == BF16 ? 2 : 4));
   if (dt == BF16)
     GK_LAUNCH(w, k_resid_mix_fwd<bf16>, dim3(nb), dim3(256), 0, s, (const bf16*)x,
-              (const bf16*)x0, (bf16*)y, n8, (const bf16*)lam, mode, (bf16*)save);
+              (const bf16*)x0, (bf16*)y, n8, (const bf16*)lam, mode);
   else
     GK_LAUNCH(w, k_resid_mix_fwd<float>, dim3(nb), dim3(256), 0, s, (const float*)x,
-              (const float*)x0, (float*)y, n8, (const float*)lam, mode, (float*)save);
+              (const float*)x0, (float*)y, n8, (const float*)lam, mode);
   return hipGetLastError();
 }
 

@@ -29,6 +29,12 @@ hipError_t embed_bwd(const int32_t* tok, int B, int T, const void* dx,
 
 hipError_t rmsnorm_fwd(const void* x, void* y, float* r, int64_t rows, int D,
                        float eps, DType dt, hipStream_t s);
+// x <- bf16(lam[0] x + lam[1] x0) stored to xout (may be x), then y = rms(x)
+// (lam: 2 device bf16 values); bf16 rows, D % 8 == 0, D <= 2048 (else
+// hipErrorInvalidValue: mix and norm run as two launches instead)
+bool rmsnorm_fwd_mix_ok(int D, DType dt);
+hipError_t rmsnorm_fwd_mix(const void* x, const void* x0, const void* lam, void* xout, void* y,
+                           float* r, int64_t rows, int D, float eps, DType dt, hipStream_t s);
 // dx = dres + r (g - y mean(g y)),  g = dy (+ VE term on the first C cols:
 // sum_kv vez[n, kv] * wg[kv, c])
 hipError_t rmsnorm_bwd(const void* dy, const void* y, const float* r,
@@ -202,8 +208,7 @@ hipError_t adamw(float* w, const float* g, float* m, float* v, int64_t n, int st
                  float b1, float b2, float eps, float wd, void* w16, hipStream_t s);
 // Model extras.  resid_mix: y = lr x + l0 x0 with (lr, l0) by `mode`:
 // MIX_LAMBDAS (lam[0], lam[1]), lam 2 device values of the storage type;
-// MIX_BACKOUT (1, -lam[0]); MIX_ADD (1, 1).  y may be x; `save` (optional)
-// receives x.  Backward dx = lr dy (dx may be null or dy), dx0 (+)= l0 dy,
+// MIX_BACKOUT (1, -lam[0]); MIX_ADD (1, 1).  y may be x.  Backward dx = lr dy (dx may be null or dy), dx0 (+)= l0 dy,
 // dlam (=, or += with accumulate_dlam): MIX_LAMBDAS [0..2) = sums of dy x,
 // dy x0; MIX_BACKOUT [0] = -sum dy x0 (x unused).
 // smear: y_t = x_t + g_t x_(t-1), g_t = lam[0] sigmoid(w . x_t[:24]),
@@ -216,7 +221,7 @@ hipError_t zero_f32(float* p, int64_t n, hipStream_t s);
 size_t resid_mix_bwd_scratch_bytes();
 size_t smear_bwd_scratch_bytes();
 hipError_t resid_mix_fwd(const void* x, const void* x0, void* y, int64_t n, const void* lam,
-                         DType dt, hipStream_t s, int mode = MIX_LAMBDAS, void* save = nullptr);
+                         DType dt, hipStream_t s, int mode = MIX_LAMBDAS);
 hipError_t resid_mix_bwd(const void* dy, const void* x, const void* x0, void* dx, void* dx0,
                          int accumulate, int64_t n, const void* lam, float* dlam, void* scratch,
                          DType dt, hipStream_t s, int mode = MIX_LAMBDAS,
