@@ -79,7 +79,8 @@ def compare(cfg, w, tok, loss, ell, grads, flag):
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_plus", "small_bf16", "small_bf16_mha",
-                                  "small_bf16_wide_gate", "tiny_odd_gate", "d4"])
+                                  "small_bf16_wide_gate", "tiny_odd_gate", "d4", "tiny_T1",
+                                  "small_bf16_T1"])
 def test_step_matches_oracle(name):
     cfg = {"tiny": lambda: gi.preset("tiny"), "tiny_plus": tiny_plus,
            "small_bf16": small_bf16,
@@ -93,7 +94,10 @@ def test_step_matches_oracle(name):
            "tiny_odd_gate": lambda: gi.preset("tiny", n_layer=4, window_pattern="SL",
                                               window_short=4, window_long=16, ve_every_odd=1,
                                               ve_gate_channels=7),
-           "d4": lambda: gi.preset("d4")}[name]()
+           "d4": lambda: gi.preset("d4"),
+           # one-token rows (the degenerate sequence length)
+           "tiny_T1": lambda: gi.preset("tiny", seq_len=1),
+           "small_bf16_T1": lambda: small_bf16(seq_len=1, batch=5)}[name]()
     say("step", name)
     out = run_step(cfg, accumulate_check=(name == "tiny_plus"))
     compare(*out)
@@ -112,6 +116,12 @@ _EXTRAS = {
     "tiny_extras_f32": lambda: dict(tiny_plus(), d_model=32, resid_lambdas=1, smear=1,
                                     backout_layer=1),
     "d4_extras": lambda: gi.preset("d4", resid_lambdas=1, smear=1, backout_layer=2),
+    # one-token rows: every position starts its row (smear gates all zero,
+    # attention sees only itself)
+    "tiny_T1_extras_f32": lambda: dict(tiny_plus(), d_model=32, seq_len=1, resid_lambdas=1,
+                                       smear=1, backout_layer=0),
+    "small_bf16_T1_extras": lambda: small_bf16(seq_len=1, batch=5, resid_lambdas=1, smear=1,
+                                               backout_layer=0),
 }
 
 
