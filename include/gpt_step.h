@@ -159,7 +159,9 @@ int gpt_step_bwd(const gpt_config* cfg, const void* params,
 /*
  * Bits per byte over an evaluation set (forward only).
  *   tokens      : device int32 [n_rows, T+1]; rows are processed in batches
- *                 of cfg->batch rows (the last one may be shorter).
+ *                 of cfg->batch rows (the last one may be shorter); n_rows
+ *                 >= 1 (an empty set is GPT_ERR_INVALID_ARG, nothing is
+ *                 enqueued).
  *   token_bytes : device int32 [V], UTF-8 byte length of each vocabulary id,
  *                 indexed by the target id.
  *   ws          : ws_bytes >= gpt_workspace_bytes(EVAL).
