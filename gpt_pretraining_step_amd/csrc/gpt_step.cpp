@@ -761,17 +761,32 @@ int gpt_optim_step(const gpt_config* cfg, const gpt_optim_hparams* hp, int32_t s
     float* u = (float*)w;
     uint16_t* x = (uint16_t*)(w + stage);
     void* nsws = w + stage + xb;
-    for (int l = 0; l < m.L; ++l) {
-      const int64_t off = (*g.offs)[l];
-      HIP_TRY(gk::muon_momentum(grads + off, state1 + off, u + l * n, n, hp->muon_momentum,
-                                hp->muon_nesterov ? 1 : 0, gk::F32, s));
+    // momentum and update run over the group's L matrices in one launch each
+    // (per matrix for deeper models than the offset table holds)
+    const bool grouped = m.L <= gk::kMaxGroupLayers;
+    gk::LayerOffsets offs{};
+    for (int l = 0; grouped && l < m.L; ++l) offs.off[l] = (*g.offs)[l];
+    if (grouped) {
+      HIP_TRY(gk::muon_momentum_group(grads, state1, u, offs, m.L, n, hp->muon_momentum,
+                                      hp->muon_nesterov ? 1 : 0, gk::F32, s));
+    } else {
+      for (int l = 0; l < m.L; ++l) {
+        const int64_t off = (*g.offs)[l];
+        HIP_TRY(gk::muon_momentum(grads + off, state1 + off, u + l * n, n, hp->muon_momentum,
+                                  hp->muon_nesterov ? 1 : 0, gk::F32, s));
+      }
     }
     HIP_TRY(gk::polar_express(u, m.L, g.rows, g.cols, gk::F32, hp->ns_coeffs, hp->ns_steps,
                               hp->ns_eps, x, nsws, s));
     const float lr = hp->muon_lr * std::sqrt(std::max(1.0f, (float)g.rows / (float)g.cols));
-    for (int l = 0; l < m.L; ++l) {
-      const int64_t off = (*g.offs)[l];
-      HIP_TRY(gk::muon_update(master + off, x + l * n, n, lr, hp->muon_wd, p16(off), s));
+    if (grouped) {
+      HIP_TRY(gk::muon_update_group(master, x, offs, m.L, n, lr, hp->muon_wd,
+                                    copy16 ? params : nullptr, s));
+    } else {
+      for (int l = 0; l < m.L; ++l) {
+        const int64_t off = (*g.offs)[l];
+        HIP_TRY(gk::muon_update(master + off, x + l * n, n, lr, hp->muon_wd, p16(off), s));
+      }
     }
   }
   // AdamW: embeddings and value-embedding tables, lm_head, gates, extras

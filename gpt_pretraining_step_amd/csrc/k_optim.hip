@@ -101,6 +101,64 @@ __global__ __launch_bounds__(256) void k_adamw(float* __restrict__ w, const floa
   }
 }
 
+// The same two steps over the equally shaped matrices of one parameter group
+// (the same tensor of every layer) in one launch: blockIdx.y picks the
+// matrix, whose master / gradient / momentum sit at element offset
+// offs.off[y] of the flat layout and whose update u / orthogonalized x is
+// slot y of a contiguous [layers, n] staging buffer.
+template <typename TU>
+__global__ __launch_bounds__(256) void k_muon_momentum_group(const float* __restrict__ g,
+                                                             float* __restrict__ mom,
+                                                             TU* __restrict__ u, LayerOffsets offs,
+                                                             int64_t n4, float beta,
+                                                             int nesterov) {
+  const int64_t off = offs.off[blockIdx.y];
+  g += off;
+  mom += off;
+  u += (int64_t)blockIdx.y * n4 * 4;
+  const float omb = 1.f - beta;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    const float4 gv = load4(g + 4 * i);
+    float4 m = load4(mom + 4 * i);
+    m.x = fmaf(beta, m.x, omb * gv.x);
+    m.y = fmaf(beta, m.y, omb * gv.y);
+    m.z = fmaf(beta, m.z, omb * gv.z);
+    m.w = fmaf(beta, m.w, omb * gv.w);
+    store4(mom + 4 * i, m);
+    float4 o = m;
+    if (nesterov) {
+      o.x = fmaf(beta, m.x, omb * gv.x);
+      o.y = fmaf(beta, m.y, omb * gv.y);
+      o.z = fmaf(beta, m.z, omb * gv.z);
+      o.w = fmaf(beta, m.w, omb * gv.w);
+    }
+    store4(u + 4 * i, o);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_muon_update_group(float* __restrict__ w,
+                                                           const bf16* __restrict__ x,
+                                                           LayerOffsets offs, int64_t n4,
+                                                           float lr, float decay,
+                                                           bf16* __restrict__ w16) {
+  const int64_t off = offs.off[blockIdx.y];
+  w += off;
+  x += (int64_t)blockIdx.y * n4 * 4;
+  if (w16) w16 += off;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    float4 v = load4(w + 4 * i);
+    const float4 xv = load4(x + 4 * i);
+    v.x = fmaf(-lr, xv.x, v.x * decay);
+    v.y = fmaf(-lr, xv.y, v.y * decay);
+    v.z = fmaf(-lr, xv.z, v.z * decay);
+    v.w = fmaf(-lr, xv.w, v.w * decay);
+    store4(w + 4 * i, v);
+    if (w16) store4(w16 + 4 * i, v);
+  }
+}
+
 namespace {
 unsigned blocks_for(int64_t n4) {
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>(2048, cdiv(n4, 256)));
@@ -125,6 +183,40 @@ hipError_t muon_update(float* w, const void* x, int64_t n, float lr, float wd, v
   const int64_t n4 = n / 4;
   const Work wk(0.0, n * (8.0 + 2.0 + (w16 ? 2.0 : 0.0)));
   GK_LAUNCH(wk, k_muon_update, dim3(blocks_for(n4)), dim3(256), 0, s, w, (const bf16*)x, n4, lr,
+            1.f - lr * wd, (bf16*)w16);
+  return hipGetLastError();
+}
+
+// per matrix about 2048 / layers blocks, so a group fills the chip as one
+// large stream does
+static unsigned group_blocks(int64_t n4, int layers) {
+  const int64_t want = std::max<int64_t>(1, 2048 / std::max(layers, 1));
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(want, cdiv(n4, 256)));
+}
+
+hipError_t muon_momentum_group(const float* g, float* mom, void* u, const LayerOffsets& offs,
+                               int layers, int64_t n, float beta, int nesterov, DType u_dt,
+                               hipStream_t s) {
+  if (layers < 1 || layers > kMaxGroupLayers || n % 4) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  const dim3 grid(group_blocks(n4, layers), (unsigned)layers);
+  const Work w(0.0, (double)layers * n * (4.0 + 8.0 + (u_dt == BF16 ? 2.0 : 4.0)));
+  if (u_dt == BF16)
+    GK_LAUNCH(w, k_muon_momentum_group<bf16>, grid, dim3(256), 0, s, g, mom, (bf16*)u, offs, n4,
+              beta, nesterov);
+  else
+    GK_LAUNCH(w, k_muon_momentum_group<float>, grid, dim3(256), 0, s, g, mom, (float*)u, offs,
+              n4, beta, nesterov);
+  return hipGetLastError();
+}
+
+hipError_t muon_update_group(float* w, const void* x, const LayerOffsets& offs, int layers,
+                             int64_t n, float lr, float wd, void* w16, hipStream_t s) {
+  if (layers < 1 || layers > kMaxGroupLayers || n % 4) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  const dim3 grid(group_blocks(n4, layers), (unsigned)layers);
+  const Work wk(0.0, (double)layers * n * (8.0 + 2.0 + (w16 ? 2.0 : 0.0)));
+  GK_LAUNCH(wk, k_muon_update_group, grid, dim3(256), 0, s, w, (const bf16*)x, offs, n4, lr,
             1.f - lr * wd, (bf16*)w16);
   return hipGetLastError();
 }

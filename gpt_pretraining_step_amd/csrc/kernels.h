@@ -206,6 +206,17 @@ hipError_t muon_update(float* w, const void* x, int64_t n, float lr, float wd, v
                        hipStream_t s);
 hipError_t adamw(float* w, const float* g, float* m, float* v, int64_t n, int step, float lr,
                  float b1, float b2, float eps, float wd, void* w16, hipStream_t s);
+// muon_momentum / muon_update over the equally shaped matrices of a group
+// (1 <= layers <= kMaxGroupLayers) in one launch: matrix y's fp32 tensors at
+// element offset offs.off[y] of g / mom / w (and w16), its u / x at slot y
+// of a contiguous [layers, n] buffer; n a multiple of 4
+constexpr int kMaxGroupLayers = 64;
+struct LayerOffsets { int64_t off[kMaxGroupLayers]; };
+hipError_t muon_momentum_group(const float* g, float* mom, void* u, const LayerOffsets& offs,
+                               int layers, int64_t n, float beta, int nesterov, DType u_dt,
+                               hipStream_t s);
+hipError_t muon_update_group(float* w, const void* x, const LayerOffsets& offs, int layers,
+                             int64_t n, float lr, float wd, void* w16, hipStream_t s);
 // Model extras.  resid_mix: y = lr x + l0 x0 with (lr, l0) by `mode`:
 // MIX_LAMBDAS (lam[0], lam[1]), lam 2 device values of the storage type;
 // MIX_BACKOUT (1, -lam[0]); MIX_ADD (1, 1).  y may be x.  Backward dx = lr dy (dx may be null or dy), dx0 (+)= l0 dy,
