@@ -21,7 +21,7 @@ GEMM_NT, GEMM_NN, GEMM_TN = 0, 1, 2
 EPI_STORE, EPI_RESADD, EPI_RELU2, EPI_DRELU2, EPI_F32, EPI_F32_ACC = range(6)
 P_WTE, P_WQKV, P_WO, P_WFC, P_WPROJ, P_VE, P_WG, P_WLM, P_EXTRAS = range(9)
 (WS_ELL, WS_LOSS, WS_NONFINITE, WS_X_H, WS_X_QKV, WS_X_O, WS_X_LSE, WS_X_H2,
- WS_X_A, WS_X_HF) = range(10)
+ WS_X_A, WS_X_HF, WS_BAD_TOKENS) = range(11)
 
 
 class GptError(RuntimeError):
@@ -40,7 +40,7 @@ class GptConfig(C.Structure):
         ("ve_every_odd", C.c_int32), ("rope_base", C.c_float),
         ("norm_eps", C.c_float), ("dtype", C.c_int32),
         ("resid_lambdas", C.c_int32), ("smear", C.c_int32), ("backout", C.c_int32),
-        ("backout_layer", C.c_int32),
+        ("backout_layer", C.c_int32), ("check_tokens", C.c_int32),
     ]
 
 
@@ -51,12 +51,14 @@ class OptimHparams(C.Structure):
         ("ns_eps", C.c_float), ("adam_lr_embed", C.c_float), ("adam_lr_head", C.c_float),
         ("adam_lr_gate", C.c_float), ("adam_beta1", C.c_float), ("adam_beta2", C.c_float),
         ("adam_eps", C.c_float), ("adam_wd", C.c_float),
+        ("normuon", C.c_int32), ("normuon_beta2", C.c_float),
     ]
 
 
 def make_optim_hparams(coeffs, muon_lr=0.02, muon_momentum=0.95, muon_wd=0.0, nesterov=True,
                        ns_eps=1e-7, adam_lr_embed=0.2, adam_lr_head=0.004, adam_lr_gate=0.02,
-                       beta1=0.8, beta2=0.95, eps=1e-10, adam_wd=0.0) -> OptimHparams:
+                       beta1=0.8, beta2=0.95, eps=1e-10, adam_wd=0.0, normuon=False,
+                       normuon_beta2=0.95) -> OptimHparams:
     h = OptimHparams()
     h.muon_lr, h.muon_momentum, h.muon_wd = muon_lr, muon_momentum, muon_wd
     h.muon_nesterov, h.ns_steps = int(nesterov), len(coeffs)
@@ -66,6 +68,7 @@ def make_optim_hparams(coeffs, muon_lr=0.02, muon_momentum=0.95, muon_wd=0.0, ne
     h.ns_eps = ns_eps
     h.adam_lr_embed, h.adam_lr_head, h.adam_lr_gate = adam_lr_embed, adam_lr_head, adam_lr_gate
     h.adam_beta1, h.adam_beta2, h.adam_eps, h.adam_wd = beta1, beta2, eps, adam_wd
+    h.normuon, h.normuon_beta2 = int(normuon), normuon_beta2
     return h
 
 
@@ -76,6 +79,7 @@ def make_config(d: dict) -> GptConfig:
     d = dict(d)
     d.setdefault("resid_lambdas", 0)
     d.setdefault("smear", 0)
+    d.setdefault("check_tokens", 0)
     bl = int(d.get("backout_layer", -1))
     d["backout"], d["backout_layer"] = (1, bl) if bl >= 0 else (0, 0)
     for name, _ in GptConfig._fields_:
@@ -129,6 +133,9 @@ _SIGS = {
                                       _sz, _vp]),
     "gpt_k_muon_momentum": (C.c_int, [_vp, _vp, _vp, _i64, _f32, _i32, _i32, _vp]),
     "gpt_k_muon_update": (C.c_int, [_vp, _vp, _i64, _f32, _f32, _vp, _vp]),
+    "gpt_k_normuon_scratch_bytes": (_sz, [_i64]),
+    "gpt_k_normuon_update": (C.c_int, [_vp, _vp, _vp, _i64, _i64, _f32, _f32, _f32, _vp, _vp,
+                                       _sz, _vp]),
     "gpt_k_adamw": (C.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _f32, _f32, _f32, _f32, _f32, _vp,
                               _vp]),
     "gpt_k_resid_mix_fwd": (C.c_int, [_vp, _vp, _vp, _i64, _vp, _i32, _vp]),
@@ -358,6 +365,16 @@ def k_muon_update(w, x, n, lr, wd, w_bf16=None, stream=None):
 def k_adamw(w, grad, m, v, n, step, lr, beta1, beta2, eps, wd, w_bf16=None, stream=None):
     _check(lib().gpt_k_adamw(_ptr(w), _ptr(grad), _ptr(m), _ptr(v), n, step, lr, beta1, beta2,
                              eps, wd, _ptr(w_bf16), _stream(stream)))
+
+
+def k_normuon_scratch_bytes(rows) -> int:
+    return int(lib().gpt_k_normuon_scratch_bytes(rows))
+
+
+def k_normuon_update(w, x, v, rows, cols, beta2, lr, wd, scratch, w_bf16=None, stream=None):
+    _check(lib().gpt_k_normuon_update(_ptr(w), _ptr(x), _ptr(v), rows, cols, beta2, lr, wd,
+                                      _ptr(w_bf16), _ptr(scratch), scratch.numel(),
+                                      _stream(stream)))
 
 
 def k_resid_mix_fwd(x, x0, y, n, lambdas, dtype, stream=None):

@@ -15,6 +15,13 @@
 
 #include "kernels.h"
 
+// A debugging build (-DGPT_DEBUG_CHECKS) checks token ids on every call.
+#ifdef GPT_DEBUG_CHECKS
+static constexpr bool kDebugChecks = true;
+#else
+static constexpr bool kDebugChecks = false;
+#endif
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -53,6 +60,7 @@ struct Model {
   // slots of the extras vector
   int resid, smear, bo;
   int ex_n, ex_sw, ex_sl, ex_bo;
+  bool check_tokens;          // count out-of-range ids before any gather
 
   bool extras() const { return resid || smear || bo >= 0; }
 
@@ -98,6 +106,8 @@ int validate(const gpt_config* c, Model* m) {
   if ((c->resid_lambdas != 0 && c->resid_lambdas != 1) || (c->smear != 0 && c->smear != 1) ||
       (c->backout != 0 && c->backout != 1))
     return fail(GPT_ERR_INVALID_ARG, "resid_lambdas, smear and backout must be 0 or 1");
+  if (c->check_tokens != 0 && c->check_tokens != 1)
+    return fail(GPT_ERR_INVALID_ARG, "check_tokens must be 0 or 1");
   if (c->backout && (c->backout_layer < 0 || c->backout_layer >= c->n_layer))
     return fail(GPT_ERR_INVALID_ARG, "backout_layer %d not in [0, n_layer)", c->backout_layer);
   if ((c->resid_lambdas || c->smear || c->backout) && c->d_model % 8)
@@ -120,6 +130,7 @@ int validate(const gpt_config* c, Model* m) {
     m->ex_sl = 2 * m->L + 24;
     m->ex_bo = 2 * m->L + 25;
     m->ex_n = 8 * ((2 * m->L + 26 + 7) / 8);
+    m->check_tokens = c->check_tokens != 0 || kDebugChecks;
   }
   return GPT_OK;
 }
@@ -161,7 +172,7 @@ struct LayerBufs {
 
 struct Plan {
   int64_t N, chunk;
-  size_t cs, x, hf, rf, ell, lse_z, loss, flag, logits, dz, evacc;
+  size_t cs, x, hf, rf, ell, lse_z, loss, flag, badtok, logits, dz, evacc;
   bool fused_ce;         // lm_head + cross-entropy fused (no fp32 logits)
   size_t ce_stats, ce_zt;
   std::vector<LayerBufs> layers;     // train: one per layer; eval: one shared
@@ -200,6 +211,7 @@ Plan make_plan(const Model& m, int mode) {
   p.lse_z = take(N * 4);
   p.loss = take(4);
   p.flag = take(4);
+  p.badtok = take(4);
   p.evacc = take(3 * 8);
   p.fused_ce = m.dt == gk::BF16 && gk::lm_ce_fused_ok(N, m.V, m.D);
   p.logits = p.fused_ce ? 0 : take((size_t)p.chunk * m.V * 4);
@@ -625,6 +637,7 @@ int64_t gpt_ws_offset(const gpt_config* cfg, int which, int layer) {
     case GPT_WS_LOSS: return (int64_t)p.loss;
     case GPT_WS_NONFINITE: return (int64_t)p.flag;
     case GPT_WS_X_HF: return (int64_t)p.hf;
+    case GPT_WS_BAD_TOKENS: return (int64_t)p.badtok;
   }
   if (layer < 0 || layer >= m.L) return fail(GPT_ERR_INVALID_ARG, "layer out of range");
   const LayerBufs& b = p.layers[layer];
@@ -639,6 +652,21 @@ int64_t gpt_ws_offset(const gpt_config* cfg, int which, int layer) {
   return fail(GPT_ERR_INVALID_ARG, "unknown workspace item %d", which);
 }
 
+// With the token check on: count the ids outside [0, V) on the device,
+// wait for the count, and refuse the call before any gather is enqueued.
+static int check_token_ids(const Model& m, const Plan& p, const int32_t* tokens, int64_t n,
+                           void* ws, hipStream_t stream) {
+  if (!m.check_tokens) return GPT_OK;
+  int* dcount = at<int>(ws, p.badtok);
+  hipError_t e = gk::count_bad_ids(tokens, n, m.V, dcount, stream);
+  int bad = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&bad, dcount, 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(GPT_ERR_HIP, "token check: %s", hipGetErrorString(e));
+  if (bad) return fail(GPT_ERR_INVALID_ARG, "%d token ids outside [0, %d)", bad, m.V);
+  return GPT_OK;
+}
+
 int gpt_step_fwd(const gpt_config* cfg, const void* params, const int32_t* tokens, void* ws,
                  size_t ws_bytes, float* loss_dev, hipStream_t stream) {
   Model m;
@@ -648,6 +676,7 @@ int gpt_step_fwd(const gpt_config* cfg, const void* params, const int32_t* token
   Plan p = make_plan(m, GPT_MODE_TRAIN);
   if (ws_bytes < p.total)
     return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, p.total);
+  if ((st = check_token_ids(m, p, tokens, (int64_t)m.B * (m.T + 1), ws, stream))) return st;
   return run_forward(m, p, param_layout(m), params, tokens, m.B, ws, GPT_MODE_TRAIN, loss_dev,
                      stream);
 }
@@ -663,6 +692,7 @@ int gpt_step_bwd(const gpt_config* cfg, const void* params, const int32_t* token
   Plan p = make_plan(m, GPT_MODE_TRAIN);
   if (ws_bytes < p.total)
     return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, p.total);
+  if ((st = check_token_ids(m, p, tokens, (int64_t)m.B * (m.T + 1), ws, stream))) return st;
   return run_backward(m, p, param_layout(m), params, tokens, ws, grads, accumulate, stream);
 }
 
@@ -677,6 +707,7 @@ int gpt_eval_bpb(const gpt_config* cfg, const void* params, const int32_t* token
   Plan p = make_plan(m, GPT_MODE_EVAL);
   if (ws_bytes < p.total)
     return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, p.total);
+  if ((st = check_token_ids(m, p, tokens, n_rows * (m.T + 1), ws, stream))) return st;
   ParamLayout pl = param_layout(m);
   double* acc = at<double>(ws, p.evacc);
   for (int64_t r0 = 0; r0 < n_rows; r0 += m.B) {
@@ -708,7 +739,8 @@ size_t optim_ws(const Model& m, const ParamLayout& pl) {
   for (const MuonGroup& g : muon_groups(m, pl)) {
     const size_t n = (size_t)m.L * g.rows * g.cols;
     const size_t stage = (n * 4 + 255) / 256 * 256, xb = (n * 2 + 255) / 256 * 256;
-    b = std::max(b, stage + xb + gk::polar_express_ws_bytes(m.L, g.rows, g.cols));
+    b = std::max(b, stage + xb + std::max(gk::polar_express_ws_bytes(m.L, g.rows, g.cols),
+                                          gk::normuon_scratch_bytes(m.L, g.rows)));
   }
   return b;
 }
@@ -734,6 +766,8 @@ int gpt_optim_step(const gpt_config* cfg, const gpt_optim_hparams* hp, int32_t s
   if (step < 1) return fail(GPT_ERR_INVALID_ARG, "step counts from 1");
   if (hp->ns_steps < 0 || hp->ns_steps > 16)
     return fail(GPT_ERR_INVALID_ARG, "ns_steps outside [0, 16]");
+  if (hp->normuon && !(hp->normuon_beta2 >= 0.f && hp->normuon_beta2 < 1.f))
+    return fail(GPT_ERR_INVALID_ARG, "normuon_beta2 outside [0, 1)");
   if (!(hp->muon_momentum >= 0.f && hp->muon_momentum < 1.f) ||
       !(hp->adam_beta1 >= 0.f && hp->adam_beta1 < 1.f) ||
       !(hp->adam_beta2 >= 0.f && hp->adam_beta2 < 1.f))
@@ -779,7 +813,24 @@ int gpt_optim_step(const gpt_config* cfg, const gpt_optim_hparams* hp, int32_t s
     HIP_TRY(gk::polar_express(u, m.L, g.rows, g.cols, gk::F32, hp->ns_coeffs, hp->ns_steps,
                               hp->ns_eps, x, nsws, s));
     const float lr = hp->muon_lr * std::sqrt(std::max(1.0f, (float)g.rows / (float)g.cols));
-    if (grouped) {
+    if (hp->normuon) {
+      // NorMuon: per-row second moments in state2 (the first `rows` floats
+      // of each matrix's slot, unused by Muon otherwise); the statistics'
+      // scratch reuses the orthogonalization's workspace, done by now
+      if (grouped) {
+        HIP_TRY(gk::normuon_update_group(master, x, state2, offs, m.L, g.rows, g.cols,
+                                         hp->normuon_beta2, lr, hp->muon_wd,
+                                         copy16 ? params : nullptr, nsws, s));
+      } else {
+        for (int l = 0; l < m.L; ++l) {
+          gk::LayerOffsets one{};
+          one.off[0] = (*g.offs)[l];
+          HIP_TRY(gk::normuon_update_group(master, x + l * n, state2, one, 1, g.rows, g.cols,
+                                           hp->normuon_beta2, lr, hp->muon_wd,
+                                           copy16 ? params : nullptr, nsws, s));
+        }
+      }
+    } else if (grouped) {
       HIP_TRY(gk::muon_update_group(master, x, offs, m.L, n, lr, hp->muon_wd,
                                     copy16 ? params : nullptr, s));
     } else {
@@ -976,6 +1027,28 @@ int gpt_k_muon_update(float* w, const void* x, int64_t n, float lr, float wd, vo
   if ((st = optim_ptrs({w, x}, n))) return st;
   if (w_bf16 && !aligned16(w_bf16)) return fail(GPT_ERR_MISALIGNED, "w_bf16 misaligned");
   KERNEL_TRY(gk::muon_update(w, x, n, lr, wd, w_bf16, s));
+  return GPT_OK;
+}
+
+size_t gpt_k_normuon_scratch_bytes(int64_t rows) {
+  return rows < 1 ? 0 : gk::normuon_scratch_bytes(1, rows);
+}
+
+int gpt_k_normuon_update(float* w, const void* x, float* v, int64_t rows, int64_t cols,
+                         float beta2, float lr, float wd, void* w_bf16, void* scratch,
+                         size_t scratch_bytes, hipStream_t s) {
+  int st;
+  if ((st = check_ptrs({w, x, v, scratch}))) return st;
+  if (w_bf16 && !aligned16(w_bf16)) return fail(GPT_ERR_MISALIGNED, "w_bf16 misaligned");
+  if (rows < 1 || cols < 8 || cols % 8 || rows * cols >= ((int64_t)1 << 31))
+    return fail(GPT_ERR_INVALID_ARG, "rows >= 1, cols a multiple of 8, rows cols < 2^31");
+  if (!(beta2 >= 0.f && beta2 < 1.f)) return fail(GPT_ERR_INVALID_ARG, "beta2 outside [0, 1)");
+  const size_t need = gk::normuon_scratch_bytes(1, rows);
+  if (scratch_bytes < need)
+    return fail(GPT_ERR_WORKSPACE_TOO_SMALL, "scratch needs %zu bytes", need);
+  gk::LayerOffsets one{};
+  KERNEL_TRY(gk::normuon_update_group(w, x, v, one, 1, rows, cols, beta2, lr, wd, w_bf16,
+                                      scratch, s));
   return GPT_OK;
 }
 

@@ -288,9 +288,14 @@ __global__ __launch_bounds__(DW * 64, 1) void k_attn_decode(
   }
   const int64_t pair = ((int64_t)b * Hkv + kvh) * qgroups + qgrp;
   float* pbase = part + pair * nchunks * QS * PSTRIDE + tslot * PSTRIDE;
-  // Publish this chunk's record with agent-scope stores, wait until they
-  // have completed, then count the chunk; the last chunk to arrive merges
-  // all records (agent-scope loads) and sets the counter back to zero.
+  // Publish this chunk's record with agent-scope stores, then count the
+  // chunk with an acquire-release add at agent scope (one thread, after the
+  // workgroup barrier that orders every wave's stores before it): the
+  // release makes the record visible to whichever workgroup counts last,
+  // and that workgroup's acquire orders its merge loads (agent-scope) after
+  // every other chunk's release.  The last chunk to arrive merges all
+  // records and sets the counter back to zero (the next launch sees it
+  // through the kernel boundary).
   if (active) {
     const Merged r = merge_records<false>(red + tslot * PSTRIDE, QS * PSTRIDE, DW, tpart, sl2);
     float* rec = pbase + (int64_t)chunk * QS * PSTRIDE;
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(DW * 64, 1) void k_attn_decode(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0)
-    last_flag = __hip_atomic_fetch_add(cnt + pair, 1, __ATOMIC_RELAXED,
+    last_flag = __hip_atomic_fetch_add(cnt + pair, 1, __ATOMIC_ACQ_REL,
                                        __HIP_MEMORY_SCOPE_AGENT) == nchunks - 1;
   __syncthreads();
   if (!last_flag) return;

@@ -792,20 +792,23 @@ hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const
   const bool fuse = nrq && nrk && ncs;
   const NormBwdArgs nb{nrq, nrk, (const float2*)ncs};
   const int64_t rows = (int64_t)B * T * H;
-  // per kernel: 2 hd flops per visible pair and matrix product formed
-  // (dK pass: S, dP, dK; dV pass: S, dV; dQ pass: S, dP, dQ); operands read
-  // once, results written once
+  // Algorithmic work only: the backward's four products (dV = P^T dO,
+  // dP = dO V^T, dK = dS^T Q, dQ = dS K) at 2 hd flops per visible pair
+  // each, 8 hd in all, credited to the pass that produces each result (dK
+  // pass: dP and dK; dV pass: dV; dQ pass: dQ).  The recomputed S (all
+  // three passes) and the dQ pass's second dP are not counted.  Operands
+  // read once, results written once.
   const double pairs = (double)B * H * visible_pairs(T, W), tok = (double)B * T;
   const double qkvo = tok * HD * 2 * (2.0 * H + 2 * Hkv), stats = (double)rows * 8;
   const Work wd(0.0, tok * H * HD * 2 * 2 + rows * 4.0);
-  const Work wq(6.0 * HD * pairs, qkvo + stats + tok * H * HD * 2);
+  const Work wq(2.0 * HD * pairs, qkvo + stats + tok * H * HD * 2);
   GK_LAUNCH(wd, k_attn_delta, dim3((unsigned)cdiv(rows * 16, 256)), dim3(256), 0, s,
             (const bf16*)o, (const bf16*)dout, delta, T, H, rows);
   // dK and dV in two passes (two waves per SIMD each; measured faster than
   // the one-wave-per-SIMD combined pass despite recomputing S)
   const dim3 gkv = xcd_grid((T + KV_BK - 1) / KV_BK, Hkv * B);
-  const Work wk(6.0 * HD * pairs, qkvo + stats + tok * Hkv * HD * 2);
-  const Work wv(4.0 * HD * pairs, qkvo + stats / 2 + tok * Hkv * HD * 2);
+  const Work wk(4.0 * HD * pairs, qkvo + stats + tok * Hkv * HD * 2);
+  const Work wv(2.0 * HD * pairs, qkvo + stats / 2 + tok * Hkv * HD * 2);
   const dim3 gq = xcd_grid((T + DQ_BQ - 1) / DQ_BQ, H * B);
 #define DKV_ARGS (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, B, T, H, Hkv, W, nb
   if (fuse) {

@@ -1,13 +1,14 @@
 // Muon's orthogonalization of a matrix update (the nanochat walkthrough, "2.
 // Muon optimizer": a quintic Newton-Schulz iteration, "Polar Express").
 //
-// Per tuple (a, b, c) the page's step is A = X^T X, B = b A + c A A,
-// X <- a X + X B.  Here it runs as X <- X B' with B' = a I + b A + c A A
-// (the same matrix, the identity term folded in), so each step is three
-// products on the MFMA GEMM kernels plus one small elementwise pass over
-// the s x s Gram matrix (s = the smaller side).  A matrix with fewer rows
-// than columns is iterated in the transposed form of the same step: A =
-// X X^T, X <- B' X.  X is bf16 between steps (A, B' too), products
+// A step with coefficients (a, b, c) maps X to its odd quintic, a X +
+// b X (X^T X) + c X (X^T X)^2, i.e. moves every singular value s to
+// a s + b s^3 + c s^5 and keeps the singular vectors.  It is formed through
+// the Gram matrix A = X^T X as X <- X P with P = a I + b A + c A A, so each
+// step is three products on the MFMA GEMM kernels (A, A A, X P) plus one
+// small elementwise pass over the s x s Gram matrix (s = the smaller
+// side).  A matrix with fewer rows than columns takes the Gram matrix on
+// the row side: A = X X^T, X <- P X.  X is bf16 between steps (A, B' too), products
 // accumulate in fp32.  A batch of equally shaped matrices (the same
 // parameter of every layer) runs in the same launches, one batch index per
 // grid row, so the small products fill the chip.  The start divides G by

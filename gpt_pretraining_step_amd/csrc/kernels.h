@@ -190,7 +190,7 @@ hipError_t gemm_fp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 // Muon's Newton-Schulz orthogonalization of `batch` matrices G [m, n]
 // (dtype, contiguous): X =
 // G / (||G||_F + eps), then per tuple (a, b, c) of coeffs (host, 3 steps
-// floats) X <- a X + X (b A + c A A), A = X^T X (tall) or the transposed
+// floats) X <- X (a I + b A + c A A), A = X^T X (tall) or the transposed
 // form (wide); result bf16 in x_out [m, n]; ws: polar_express_ws_bytes.
 size_t polar_express_ws_bytes(int batch, int64_t m, int64_t n);
 hipError_t polar_express(const void* g, int batch, int64_t m, int64_t n, DType dt,
@@ -217,6 +217,18 @@ hipError_t muon_momentum_group(const float* g, float* mom, void* u, const LayerO
                                hipStream_t s);
 hipError_t muon_update_group(float* w, const void* x, const LayerOffsets& offs, int layers,
                              int64_t n, float lr, float wd, void* w16, hipStream_t s);
+// NorMuon variant of muon_update_group on matrices [rows, cols] (cols a
+// multiple of 8): per row the mean square of X's row updates the second
+// moment v (matrix y's at v + offs.off[y], `rows` floats), then W <- W (1 -
+// lr wd) - lr f_r X with f_r = v_r^(-1/2) ||X||_F / ||v^(-1/2) X||_F (the
+// floor 1e-10 under v and the norm); scratch: normuon_scratch_bytes.
+size_t normuon_scratch_bytes(int layers, int64_t rows);
+hipError_t normuon_update_group(float* w, const void* x, float* v, const LayerOffsets& offs,
+                                int layers, int64_t rows, int64_t cols, float b2, float lr,
+                                float wd, void* w16, void* scratch, hipStream_t s);
+// Number of ids outside [0, V) among tok[0 .. n) written to *count (one
+// workgroup, fixed order).
+hipError_t count_bad_ids(const int32_t* tok, int64_t n, int V, int* count, hipStream_t s);
 // Model extras.  resid_mix: y = lr x + l0 x0 with (lr, l0) by `mode`:
 // MIX_LAMBDAS (lam[0], lam[1]), lam 2 device values of the storage type;
 // MIX_BACKOUT (1, -lam[0]); MIX_ADD (1, 1).  y may be x.  Backward dx = lr dy (dx may be null or dy), dx0 (+)= l0 dy,

@@ -78,6 +78,13 @@ enum { GPT_MODE_TRAIN = 0, GPT_MODE_EVAL = 1 };
  *   backout: 1 = the stream after block backout_layer (0 <= it < n_layer)
  *     is kept and, after the last block, x -= lambda_b x_kept.
  *   With any extra on, D must be a multiple of 8.
+ *   check_tokens: 1 = gpt_step_fwd, gpt_step_bwd and gpt_eval_bpb first
+ *     count the token ids outside [0, V) on the device, wait for the count
+ *     (a stream synchronisation) and return GPT_ERR_INVALID_ARG, with the
+ *     count in gpt_last_error(), when it is not zero; nothing but that
+ *     check has been enqueued then.  0 = ids are a precondition (no check,
+ *     no synchronisation).  A library built for debugging
+ *     (`python -m gpt_pretraining_step_amd.build --debug`) checks always.
  */
 typedef struct gpt_config {
   int32_t n_layer, d_model, n_head, n_kv_head, head_dim, vocab, seq_len, batch;
@@ -88,6 +95,7 @@ typedef struct gpt_config {
   float rope_base, norm_eps;
   int32_t dtype;
   int32_t resid_lambdas, smear, backout, backout_layer;
+  int32_t check_tokens;
 } gpt_config;
 
 /* ------------------------------------------------------- sizes and layout */
@@ -133,7 +141,8 @@ int gpt_validate_config(const gpt_config* cfg);
  *   params : device, dtype per cfg->dtype, the flat layout above.
  *   tokens : device int32 [B, T+1] row-major; inputs are the first T ids of a
  *            row, targets the last T.  Ids outside [0, V) are a precondition
- *            violation (not checked on the device).
+ *            violation, checked only with cfg->check_tokens (or in a debug
+ *            build): then GPT_ERR_INVALID_ARG before any gather runs.
  *   ws     : device workspace of ws_bytes >= gpt_workspace_bytes(TRAIN).  The
  *            forward saves what the backward needs in it; ws[] also holds the
  *            per-token losses (gpt_ws_offset(GPT_WS_ELL)).
@@ -183,6 +192,12 @@ int gpt_eval_bpb(const gpt_config* cfg, const void* params,
  *   (Nesterov) or M; X = the Newton-Schulz orthogonalization of U (ns_steps
  *   tuples from ns_coeffs, the same matrix of every layer batched);
  *   W <- W (1 - lr wd) - lr X with lr = muon_lr max(1, rows / cols)^0.5.
+ *   NorMuon (normuon != 0; the same section's per-neuron normalisation):
+ *   X is rescaled per output row before the step, X_r <- X_r s_r
+ *   ||X||_F / ||diag(s) X||_F with s_r = 1 / sqrt(max(v_r, 1e-10)) and
+ *   v_r <- normuon_beta2 v_r + (1 - normuon_beta2) mean_c X[r, c]^2 kept
+ *   in state2 (its first `rows` floats in each Muon matrix's slot; zero
+ *   before step 1); the second norm is clamped below at 1e-10.
  *   AdamW (state1 = m, state2 = v, step counts from 1): wte and the value-
  *   embedding tables at adam_lr_embed, Wlm at adam_lr_head, the value-
  *   embedding gates and the extras vector (the model extras' scalars and
@@ -200,6 +215,8 @@ typedef struct gpt_optim_hparams {
   float ns_eps;
   float adam_lr_embed, adam_lr_head, adam_lr_gate;
   float adam_beta1, adam_beta2, adam_eps, adam_wd;
+  int32_t normuon;                  /* 0: plain Muon (a zeroed tail keeps it) */
+  float normuon_beta2;              /* second-moment decay, [0, 1) */
 } gpt_optim_hparams;
 
 size_t gpt_optim_ws_bytes(const gpt_config* cfg);
@@ -222,7 +239,8 @@ enum {
   GPT_WS_X_LSE,         /* fp32 [B, H, T] attention log-sum-exp      (layer)  */
   GPT_WS_X_H2,          /* dtype [N, D] normalised MLP input         (layer)  */
   GPT_WS_X_A,           /* dtype [N, F] relu(u)^2                    (layer)  */
-  GPT_WS_X_HF           /* dtype [N, D] final normalised features            */
+  GPT_WS_X_HF,          /* dtype [N, D] final normalised features            */
+  GPT_WS_BAD_TOKENS     /* int32, ids outside [0, V) at the last check       */
 };
 int64_t gpt_ws_offset(const gpt_config* cfg, int which, int layer);
 
@@ -322,10 +340,11 @@ int gpt_k_gemm_fp8(int64_t M, int64_t N, int64_t K, const void* A,
  *   its own; they share the launches.
  *   coeffs (host): steps tuples (a, b, c), 3 * steps floats; the page
  *   prints the first two of its five tuples, so the caller supplies them.
- *   X = g / (||g||_F + eps); per tuple A = X^T X, B = b A + c A A,
- *   X <- a X + X B (a matrix with fewer rows than columns is iterated in
- *   the transposed form A = X X^T, X <- a X + B X).  X, A and B are bf16
- *   between the products (fp32 accumulation).
+ *   X = g / (||g||_F + eps); each tuple (a, b, c) replaces X by its odd
+ *   quintic a X + b X (X^T X) + c X (X^T X)^2, formed as X (a I + b A +
+ *   c A A) with A = X^T X (a matrix with fewer rows than columns takes
+ *   A = X X^T and X <- (a I + b A + c A A) X).  X, A and the polynomial
+ *   matrix are bf16 between the products (fp32 accumulation).
  *   x_out [batch, m, n] bf16 (device).  ws: device, >=
  *   gpt_k_polar_express_ws_bytes(batch, m, n).  Needs m and n multiples of
  *   8, 1 <= batch <= 65535, 0 <= steps <= 64.  Deterministic. */
@@ -353,6 +372,21 @@ int gpt_k_muon_momentum(const float* grad, float* mom, void* u, int64_t n,
                         hipStream_t s);
 int gpt_k_muon_update(float* w, const void* x, int64_t n, float lr, float wd,
                       void* w_bf16, hipStream_t s);
+/* NorMuon's step on one matrix (the nanochat walkthrough, section "2. Muon
+ * optimizer", the per-neuron normalisation after the orthogonalization):
+ * x [rows, cols] bf16 the orthogonalized update, v [rows] fp32 the per-row
+ * second moment (in/out, zero before the first step), w [rows, cols] fp32
+ * (in/out), w_bf16 an optional bf16 copy.  m_r = mean_c x[r, c]^2,
+ * v_r <- beta2 v_r + (1 - beta2) m_r, s_r = 1 / sqrt(max(v_r, 1e-10)),
+ * f_r = s_r sqrt(sum_r m_r) / max(sqrt(sum_r m_r s_r^2), 1e-10), then
+ * w <- w (1 - lr wd) - lr f_r x.  cols a multiple of 8, rows cols < 2^31.
+ * scratch: device, >= gpt_k_normuon_scratch_bytes(rows).  Deterministic
+ * (fixed-order sums). */
+size_t gpt_k_normuon_scratch_bytes(int64_t rows);
+int gpt_k_normuon_update(float* w, const void* x, float* v, int64_t rows,
+                         int64_t cols, float beta2, float lr, float wd,
+                         void* w_bf16, void* scratch, size_t scratch_bytes,
+                         hipStream_t s);
 int gpt_k_adamw(float* w, const float* grad, float* m, float* v, int64_t n,
                 int32_t step, float lr, float beta1, float beta2, float eps,
                 float wd, void* w_bf16, hipStream_t s);

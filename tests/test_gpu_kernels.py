@@ -813,9 +813,8 @@ NS_CLASSIC = (3.4445, -4.7750, 2.0315)
                                              (136, 72, 0, 2), (72, 136, 1, 1)])
 def test_polar_express(m, n, steps, batch, dt):
     """The orthogonalized updates of a batch of matrices against the
-    oracle's bf16 iteration (the page's form a X + X B; the kernels run
-    X B' with B' = a I + b A + c A A, same matrix, other rounding points)
-    and against the exact iteration, each matrix on its own.  Tuples: the
+    oracle's bf16 Gram-matrix form and against the exact result (the SVD
+    definition), each matrix on its own.  Tuples: the
     page's two, or the classic quintic tuple five times (a convergent
     schedule: the page's two tuples expect the three elided ones after
     them)."""
@@ -887,6 +886,36 @@ def test_optimizer_elementwise(n):
         assert rel_err(to_np(aw), a_w) < 1e-5
         assert rel_err(to_np(am), a_m) < 1e-5 and rel_err(to_np(av), a_v) < 1e-5
         assert rel_err(to_np(tmom), mom) < 1e-6
+
+
+@pytest.mark.parametrize("rows,cols", [(768, 768), (3072, 768), (40, 3072), (5, 8)])
+def test_normuon_update(rows, cols):
+    """NorMuon's step on one matrix, three steps from a zero second moment,
+    against the oracle (fp32 kernels against fp64: 1e-5 relative on the
+    weights' change and on the state); rows of very different scales so
+    the per-row normalisation matters; the bf16 copy is the rounded
+    master."""
+    from oracle import muon
+    say("normuon", rows, cols)
+    rng = np.random.default_rng(rows + cols)
+    w0 = rng.standard_normal((rows, cols)).astype(np.float32)
+    tw = dev(w0, torch.float32)
+    tw16 = torch.empty(rows * cols, dtype=torch.bfloat16, device=DEV)
+    tv = torch.zeros(rows, dtype=torch.float32, device=DEV)
+    scr = torch.empty(G.k_normuon_scratch_bytes(rows), dtype=torch.uint8, device=DEV)
+    w, v = w0.astype(np.float64), np.zeros(rows)
+    for k in range(3):
+        x = O.round_bf16((rng.standard_normal((rows, cols)) *
+                          np.geomspace(0.05, 2.0, rows)[:, None] * 0.03).astype(np.float32))
+        G.k_normuon_update(tw, dev(x, torch.bfloat16), tv, rows, cols, 0.9, 0.02, 0.1, scr,
+                           w_bf16=tw16)
+        xs, v = muon.normuon(x, v, 0.9)
+        w = muon.muon_update(w, xs, 0.02, 0.1)
+        torch.cuda.synchronize()
+        got = to_np(tw).reshape(rows, cols)
+        assert rel_err(got - w0, w - w0) < 1e-5
+        assert rel_err(to_np(tv), v) < 1e-5
+        np.testing.assert_array_equal(to_np(tw16), O.round_bf16(tw.cpu().numpy()))
 
 
 # ------------------------------------------------------ model extras
@@ -963,20 +992,23 @@ def test_smear(B, T, D, dt):
 
 
 # ------------------------------------------------------ whole optimizer step
-@pytest.mark.parametrize("which", ["small_bf16", "tiny", "small_bf16_extras"])
-def test_optim_step(which):
+@pytest.mark.parametrize("which,normuon", [("small_bf16", False), ("tiny", False),
+                                           ("small_bf16_extras", False), ("small_bf16", True),
+                                           ("tiny", True)])
+def test_optim_step(which, normuon):
     """gpt_optim_step over every tensor of a model, two steps, against the
-    oracle's Muon (momentum, exact Newton-Schulz, lr max(1, rows/cols)^0.5
-    step) and AdamW per tensor: Muon tensors' changes within 2e-2 normwise
-    (the kernels' bf16 iteration), AdamW tensors to 1e-5; the bf16 copy is
-    the rounded master."""
+    oracle's Muon (momentum, exact Newton-Schulz, NorMuon's per-row
+    rescaling when on, lr max(1, rows/cols)^0.5 step) and AdamW per tensor:
+    Muon tensors' changes within 2e-2 normwise (the kernels' bf16
+    iteration), AdamW tensors to 1e-5; the bf16 copy is the rounded
+    master."""
     from oracle import muon
     from tests.gpu_util import small_bf16, tiny_plus
     import gptinputs as gi
     cfgd = {"small_bf16": small_bf16, "tiny": tiny_plus,
             "small_bf16_extras": lambda: small_bf16(resid_lambdas=1, smear=1,
                                                     backout_layer=1)}[which]()
-    say("optim step", which)
+    say("optim step", which, "normuon", normuon)
     cfg = G.make_config(cfgd)
     n = O.param_count(cfgd)
     rng = np.random.default_rng(21)
@@ -986,7 +1018,7 @@ def test_optim_step(which):
     hpd = dict(muon_lr=0.02, muon_momentum=0.9, muon_wd=0.01, adam_lr_embed=0.05,
                adam_lr_head=0.004, adam_lr_gate=0.01, beta1=0.8, beta2=0.95, eps=1e-10,
                adam_wd=0.001)
-    hp = G.make_optim_hparams(coeffs, **hpd)
+    hp = G.make_optim_hparams(coeffs, normuon=normuon, normuon_beta2=0.9, **hpd)
     master = dev(w0, torch.float32)
     bf = cfgd["dtype"] == G.BF16
     params = torch.empty(n, dtype=torch.bfloat16, device=DEV) if bf else None
@@ -1005,11 +1037,14 @@ def test_optim_step(which):
         base = name.split(".")[-1]
         w = w0[sl].astype(np.float64).reshape(shape)
         if base in ("wqkv", "wo", "wfc", "wproj"):
-            mom = np.zeros(shape)
+            mom, vrow = np.zeros(shape), np.zeros(shape[0])
             lr = hpd["muon_lr"] * max(1.0, shape[0] / shape[1]) ** 0.5
             for k in range(2):
                 mom, u = muon.muon_momentum(grads[k][sl].reshape(shape), mom, 0.9)
-                w = muon.muon_update(w, muon.polar_express(u, coeffs), lr, hpd["muon_wd"])
+                x = muon.polar_express(u, coeffs)
+                if normuon:
+                    x, vrow = muon.normuon(x, vrow, 0.9)
+                w = muon.muon_update(w, x, lr, hpd["muon_wd"])
             d_ref, d_got = w - w0[sl].reshape(shape), got[sl].reshape(shape) - w0[sl].reshape(shape)
             assert rel_err(d_got, d_ref) < 2e-2, name
         else:

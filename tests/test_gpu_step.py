@@ -229,3 +229,45 @@ def test_deterministic_backward(extras):
     s.bwd()
     torch.cuda.synchronize()
     assert torch.equal(a, s.grads)
+
+
+def test_token_check():
+    """With check_tokens on, in-range ids give the unchecked results bit
+    for bit (the check only reads the tokens), and ids outside [0, V) make
+    fwd, bwd and eval return GPT_ERR_INVALID_ARG before any gather runs
+    (the loss buffer keeps its sentinel, the count sits in the workspace)."""
+    cfg = small_bf16()
+    n = O.param_count(cfg)
+    w, bits = gi.make_params(cfg, n)
+    tok = gi.make_tokens(cfg)
+    ref = Session(cfg)
+    ref.set_params(w, bits)
+    ref.set_tokens(tok)
+    ref.fwd()
+    ref.bwd()
+    s = Session(dict(cfg, check_tokens=1), eval_ws=True)
+    s.set_params(w, bits)
+    s.set_tokens(tok)
+    s.fwd()
+    s.bwd()
+    torch.cuda.synchronize()
+    assert torch.equal(s.loss, ref.loss) and torch.equal(s.grads, ref.grads)
+    V = cfg["vocab"]
+    for bad_ids in ((-1,), (V,), (V, 2**31 - 1, -7)):
+        say("token check", bad_ids)
+        t = tok.copy()
+        for i, b in enumerate(bad_ids):
+            t[i % t.shape[0], 1 + 3 * i] = b
+        s.set_tokens(t)
+        s.loss.fill_(-123.0)
+        with pytest.raises(G.GptError) as e:
+            s.fwd()
+        assert e.value.status == -1 and f"{len(bad_ids)} token ids" in str(e.value)
+        with pytest.raises(G.GptError):
+            s.bwd()
+        with pytest.raises(G.GptError):
+            s.evaluate(s.tokens, s.upload(gi.make_token_bytes(cfg)))
+        torch.cuda.synchronize()
+        assert s.loss.item() == -123.0
+        off = G.ws_offset(s.cfg, G.WS_BAD_TOKENS)
+        assert int(s.ws[off:off + 4].view(torch.int32).item()) == len(bad_ids)

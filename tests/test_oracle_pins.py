@@ -667,22 +667,27 @@ def test_fp8_linear_exact_when_operands_are_representable():
 PAGE_NS = [(8.156, -22.483, 15.879), (4.043, -2.809, 0.500)]
 
 
-def test_polar_express_acts_on_singular_values():
-    """Each step maps every singular value s of X to a s + b s^3 + c s^5 and
-    keeps the singular vectors (X = U S V^T => a X + X (b X^T X + c (X^T
-    X)^2) = U p(S) V^T), starting from s / ||G||_F: checked against numpy's
-    SVD for a tall matrix, one and two steps."""
+def test_polar_express_equals_the_matrix_quintic():
+    """The oracle's SVD form equals the odd matrix quintic aX + bX(X^T X) +
+    cX(X^T X)^2 evaluated directly with matrix products (fp64), one and two
+    steps from X = G / ||G||_F, tall and wide; and on a diagonal matrix the
+    result is the diagonal of the composed scalar quintic of d / ||d||
+    (signs kept: the polynomials are odd)."""
     from oracle import muon
     rng = np.random.default_rng(0)
-    G = rng.standard_normal((40, 24))
-    U, S, Vt = np.linalg.svd(G, full_matrices=False)
-    s = S / (np.linalg.norm(G) + muon.NS_EPS)
-    for k in (1, 2):
-        want = s.copy()
-        for a, b, c in PAGE_NS[:k]:
-            want = a * want + b * want ** 3 + c * want ** 5
-        X = muon.polar_express(G, PAGE_NS[:k])
-        np.testing.assert_allclose(X, (U * want) @ Vt, atol=1e-10)
+    for shape in ((40, 24), (24, 56)):
+        G = rng.standard_normal(shape)
+        for k in (1, 2):
+            X = G / (np.linalg.norm(G) + muon.NS_EPS)
+            for a, b, c in PAGE_NS[:k]:
+                XtX = X.T @ X
+                X = a * X + b * (X @ XtX) + c * (X @ XtX @ XtX)
+            np.testing.assert_allclose(muon.polar_express(G, PAGE_NS[:k]), X, atol=1e-10)
+    d = np.array([3.0, -1.0, 0.5, 2.0, -0.25])
+    s = d / (np.linalg.norm(d) + muon.NS_EPS)
+    for a, b, c in PAGE_NS:
+        s = a * s + b * s ** 3 + c * s ** 5
+    np.testing.assert_allclose(muon.polar_express(np.diag(d), PAGE_NS), np.diag(s), atol=1e-12)
 
 
 def test_polar_express_orientation_scale_and_bf16():
@@ -704,6 +709,58 @@ def test_polar_express_orientation_scale_and_bf16():
     sv = np.linalg.svd(muon.polar_express(rng.standard_normal((64, 32)), classic),
                        compute_uv=False)
     assert sv.min() > 0.6 and sv.max() < 1.25
+
+
+def test_normuon_keeps_the_update_norm():
+    """NorMuon only redistributes the update across neurons: the Frobenius
+    norm of the scaled update equals the input's for any second-moment
+    state; the state moves as v <- b2 v + (1 - b2) mean_c X^2 per row."""
+    from oracle import muon
+    rng = np.random.default_rng(3)
+    for shape in ((48, 20), (16, 64)):
+        X = rng.standard_normal(shape) * rng.uniform(0.1, 3.0, (shape[0], 1))
+        v0 = rng.uniform(0.0, 2.0, shape[0])
+        Y, v = muon.normuon(X, v0, 0.95)
+        assert abs(np.linalg.norm(Y) - np.linalg.norm(X)) < 1e-12 * np.linalg.norm(X)
+        np.testing.assert_allclose(v, 0.95 * v0 + 0.05 * (X ** 2).sum(1) / shape[1],
+                                   rtol=1e-14)
+
+
+def test_normuon_equalises_neurons_on_a_constant_series():
+    """The same update t times from a zero state: the state is (1 - b2^t)
+    times each row's mean square, and every row of the output has the same
+    RMS, ||X||_F / sqrt(m n), whatever the rows' own scales (rows, not
+    columns, are the neurons of an [out, in] weight)."""
+    from oracle import muon
+    rng = np.random.default_rng(4)
+    m, n, b2 = 12, 40, 0.9
+    X = rng.standard_normal((m, n)) * np.geomspace(0.01, 10.0, m)[:, None]
+    v = np.zeros(m)
+    for t in range(1, 6):
+        Y, v = muon.normuon(X, v, b2)
+        np.testing.assert_allclose(v, (1 - b2 ** t) * (X ** 2).mean(1), rtol=1e-12)
+        row_rms = np.sqrt((Y ** 2).mean(1))
+        np.testing.assert_allclose(row_rms, np.linalg.norm(X) / np.sqrt(m * n), rtol=1e-12)
+        # each row keeps its direction
+        np.testing.assert_allclose(Y / row_rms[:, None],
+                                   X / np.sqrt((X ** 2).mean(1))[:, None], rtol=1e-12)
+
+
+def test_normuon_special_cases():
+    """Rows of equal RMS from a zero state come back unchanged (a +-1
+    matrix); a zero row stays zero; an all-zero update gives zeros, not
+    NaN (both norms clamp at 1e-10)."""
+    from oracle import muon
+    rng = np.random.default_rng(5)
+    X = rng.choice([-1.0, 1.0], (8, 16))
+    Y, _ = muon.normuon(X, np.zeros(8), 0.95)
+    np.testing.assert_allclose(Y, X, rtol=1e-13)
+    X[3] = 0.0
+    X[5] *= 4.0
+    Y, v = muon.normuon(X, np.zeros(8), 0.95)
+    assert np.all(Y[3] == 0.0) and np.all(np.isfinite(Y)) and v[3] == 0.0
+    Z, vz = muon.normuon(np.zeros((4, 8)), np.zeros(4), 0.95)
+    assert np.all(Z == 0.0) and np.all(vz == 0.0)
 
 
 def test_adamw_matches_torch():
