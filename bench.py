@@ -251,12 +251,91 @@ def cpu_baseline(cfg, seconds_hint=10.0, max_rows=8):
         O.step(c1, w, tok[rows:rows + 1], "fp32")
         dt += time.perf_counter() - t0
         rows += 1
-    threads = os.environ.get("OMP_NUM_THREADS")
-    cores = int(threads) if threads else len(os.sched_getaffinity(0))
-    return {"value": round(rows * cfg["seq_len"] / dt, 2), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
+    host = host_cpu_info()
+    return {"value": round(rows * cfg["seq_len"] / dt, 2), "unit": "tokens/s",
+            "cores": host["blas_threads"] or host["cores"], "kind": "oracle",
+            "cpu_model": host["cpu_model"], "host_cores": host["cores"],
+            "blas": host["blas"], "blas_threads": host["blas_threads"],
             "sample": f"{rows} one-row batches of {cfg['seq_len']} tokens from the "
-                      f"{cfg['name']} workload (fwd+bwd, numpy fp32, {dt:.1f} s)"}
+                      f"{cfg['name']} workload (fwd+bwd, numpy fp32, {dt:.1f} s; the "
+                      f"oracle's elementwise work is single-threaded, its products use "
+                      f"the BLAS threads)"}
+
+
+def host_cpu_info():
+    """CPU model, usable cores and numpy's BLAS library / thread count."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = None, None
+    try:
+        import numpy as np
+        import threadpoolctl
+        np.ones(4) @ np.ones(4)
+        for info in threadpoolctl.threadpool_info():
+            if info.get("user_api") == "blas":
+                blas = f"{info.get('internal_api')} {info.get('version')}"
+                threads = int(info.get("num_threads"))
+                break
+    except Exception:
+        pass
+    return {"cpu_model": model, "cores": len(os.sched_getaffinity(0)), "blas": blas,
+            "blas_threads": threads}
+
+
+def gpu_clock_mhz():
+    """Current shader clock of GPU 0 in MHz from rocm-smi, or None."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "-d", "0", "--showclocks"], capture_output=True,
+                             text=True, timeout=20).stdout
+    except Exception:
+        return None
+    return parse_sclk(out)
+
+
+def parse_sclk(text):
+    """The shader clock (MHz) in rocm-smi's --showclocks text, or None."""
+    import re
+    m = re.search(r"sclk[^\n]*?\((\d+)\s*Mhz\)", text, re.IGNORECASE)
+    return int(m.group(1)) if m else None
+
+
+class ClockSampler:
+    """Samples the shader clock every `period` seconds in a thread while
+    the timed steps run; reports the median of the samples."""
+
+    def __init__(self, period=0.5):
+        import threading
+        self.period, self.samples = period, []
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            c = gpu_clock_mhz()
+            if c:
+                self.samples.append(c)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join(timeout=30)
+
+    def median(self):
+        import statistics
+        return statistics.median(self.samples) if self.samples else None
 
 
 DECODE_METRIC = "decode attention: new tokens/s over KV caches (all layers), HBM GB/s"
@@ -753,6 +832,33 @@ def bench_extras(a, torch, G):
     print(json.dumps(out), flush=True)
 
 
+def eval_set_line(name, torch, G, gi, Session):
+    """Evaluation tokens/s and bpb of a preset over its whole evaluation set
+    (one gpt_eval_bpb call, timed with events; one warm-up call)."""
+    cfg = gi.preset(name)
+    _, eval_fpt, _ = model_flops(cfg)
+    s = Session(cfg, eval_ws=True, train_ws=False)
+    w, bits = gi.make_params(cfg, s.n_params)
+    s.set_params(w, bits)
+    del w, bits
+    n_rows = cfg["eval_rows"]
+    tok = s.upload(gi.make_eval_tokens(cfg, n_rows))
+    tb = s.upload(gi.make_token_bytes(cfg))
+    s.evaluate(tok, tb)
+    torch.cuda.synchronize()
+    t = time_events(lambda: s.evaluate(tok, tb), 2, torch)
+    targets = n_rows * cfg["seq_len"]
+    bpb = s.bpb.cpu().numpy().tolist()
+    log(f"{name} eval over {targets} targets: {targets / t:,.0f} tok/s, bpb {bpb[2]:.4f}")
+    out = {"workload": f"{name} evaluation set: {n_rows} rows x {cfg['seq_len']} "
+                       f"({targets} targets), batches of {cfg['batch']}",
+           "tokens_per_s": round(targets / t, 1), "seconds": round(t, 4), "bpb": bpb[2],
+           "mfu_bf16": round(targets / t * eval_fpt / PEAK_BF16, 4)}
+    del s, tok, tb
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -766,6 +872,8 @@ def main():
     ap.add_argument("--shapes", action="store_true",
                     help="also time every product / attention shape alone")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-gqa-eval", action="store_true",
+                    help="train: skip the d12-GQA 2^21-target evaluation line")
     ap.add_argument("--workload", choices=("train", "decode", "fp8", "muon", "optim", "extras"),
                     default="train",
                     help="train: the fwd+bwd step; decode: KV-cache decode attention; fp8: the "
@@ -849,33 +957,47 @@ def main():
     loss0 = s.loss.item()
     assert math.isfinite(loss0), loss0
     log(f"warmup done, loss {loss0:.4f}")
-    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event before each step and one after the last, on the stream the
+    # library's kernels run on: K per-step times, and the whole span
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    st.record()
-    for _ in range(a.steps):
-        step()
-    en.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = st.elapsed_time(en) / a.steps
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        evs[0].record()
+        for k in range(a.steps):
+            step()
+            evs[k + 1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    per_step = np.array([evs[k].elapsed_time(evs[k + 1]) for k in range(a.steps)])
+    ms_mean = evs[0].elapsed_time(evs[-1]) / a.steps
+    ms = float(np.median(per_step))
+    p10, p90 = (float(np.percentile(per_step, q)) for q in (10, 90))
     tok_s = tokens_per_step / (ms / 1e3)
     mfu = tok_s * train_fpt / PEAK_BF16
-    log(f"step {ms:.2f} ms  {tok_s:,.0f} tok/s  mfu {mfu:.3f}  (wall {wall:.2f} s)")
+    clock = clk.median()
+    max_clock = 2400
+    mfu_clk = mfu * max_clock / clock if clock else None
+    log(f"step median {ms:.2f} ms (p10 {p10:.2f}, p90 {p90:.2f}, mean {ms_mean:.2f})  "
+        f"{tok_s:,.0f} tok/s  mfu {mfu:.3f}  clock {clock} MHz  (wall {wall:.2f} s)")
 
     # the optimizer step on the same model (fp32 masters and states), timed
     # on its own: reported beside the fwd+bwd rate, not folded into it
-    hp = G.make_optim_hparams([NS_TUPLE] * 5)
-    master = s.params.float()
-    st1, st2 = torch.zeros_like(master), torch.zeros_like(master)
-    ows = torch.empty(G.optim_ws_bytes(s.cfg), dtype=torch.uint8, device="cuda")
-    opt_params = s.params.clone()
-    G.optim_step(s.cfg, hp, 1, master, opt_params, s.grads, st1, st2, ows)
-    torch.cuda.synchronize()
-    opt_ms = time_events(lambda: G.optim_step(s.cfg, hp, 2, master, opt_params, s.grads, st1,
-                                              st2, ows), 5, torch) * 1e3
-    del master, st1, st2, ows, opt_params
-    log(f"optimizer step {opt_ms:.2f} ms; fwd+bwd+optimizer "
+    opt = {}
+    for normuon in (False, True):
+        hp = G.make_optim_hparams([NS_TUPLE] * 5, normuon=normuon)
+        master = s.params.float()
+        st1, st2 = torch.zeros_like(master), torch.zeros_like(master)
+        ows = torch.empty(G.optim_ws_bytes(s.cfg), dtype=torch.uint8, device="cuda")
+        opt_params = s.params.clone()
+        G.optim_step(s.cfg, hp, 1, master, opt_params, s.grads, st1, st2, ows)
+        torch.cuda.synchronize()
+        opt[normuon] = time_events(lambda: G.optim_step(s.cfg, hp, 2, master, opt_params,
+                                                        s.grads, st1, st2, ows), 5, torch) * 1e3
+        del master, st1, st2, ows, opt_params
+        torch.cuda.empty_cache()
+    opt_ms = opt[False]
+    log(f"optimizer step {opt_ms:.2f} ms (NorMuon {opt[True]:.2f} ms); fwd+bwd+optimizer "
         f"{tokens_per_step / ((ms + opt_ms) / 1e3):,.0f} tok/s")
 
     # evaluation throughput (forward + CE + bytes reduction)
@@ -888,6 +1010,12 @@ def main():
     eval_tok_s = ev_rows * T / t_ev
     bpb = s.bpb.cpu().numpy().tolist()
     log(f"eval {eval_tok_s:,.0f} tok/s, bpb {bpb[2]:.4f}")
+    del ev_tok
+    # the long-context workload's evaluation: d12-GQA over its whole 2^21-
+    # target set (512 rows x 4096), a separate model of that shape
+    gqa = None
+    if not a.model_extras and a.config == "d12" and not a.no_gqa_eval:
+        gqa = eval_set_line("d12gqa", torch, G, gi, Session)
 
     # per-kernel split of the step with the library's launch recording
     prof = kernel_profile(step, a.prof_steps, torch, G) if a.prof_steps > 0 else []
@@ -915,6 +1043,9 @@ def main():
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 3),
+        "ms_per_step_stats": {"median": round(ms, 3), "p10": round(p10, 3),
+                              "p90": round(p90, 3), "mean": round(ms_mean, 3),
+                              "value_from": "median"},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded Zipf(1.1) tokens, N(0,0.02) random-init weights)",
         "config": {"workload": f"{a.config} fwd+bwd step: {cfg['n_layer']} layers, "
@@ -927,9 +1058,27 @@ def main():
                                   f"block {cfg['backout_layer']})" if a.model_extras else ""),
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "mfu_bf16": round(mfu, 4), "train_flop_per_token": train_fpt,
+        "gpu_clock_mhz": clock, "mfu_bf16_clock_adjusted": round(mfu_clk, 4) if mfu_clk else None,
+        "clock_note": f"median shader clock sampled by rocm-smi during the timed steps; "
+                      f"the adjusted MFU prices the peak at that clock instead of "
+                      f"{max_clock} MHz",
         "optimizer_ms_per_step": round(opt_ms, 3),
+        "optimizer_ms_per_step_normuon": round(opt[True], 3),
+        "optimizer_ns": f"Muon Newton-Schulz: {NS_TUPLE} x 5 (the classic quintic tuple; the "
+                        f"page prints two of its five tuples)",
         "tokens_per_s_with_optimizer": round(tokens_per_step / ((ms + opt_ms) / 1e3), 1),
         "eval_tokens_per_s": round(eval_tok_s, 1), "eval_rows": ev_rows, "eval_bpb": bpb[2],
+        "eval_mfu_bf16": round(eval_tok_s * eval_fpt / PEAK_BF16, 4),
+        "eval_d12gqa_2m": gqa,
+        "context": {
+            "autoresearch_5min_budget": {
+                "d12_steps_in_300s": int(300.0 / (ms / 1e3)),
+                "d12_tokens_in_300s": int(300.0 / (ms / 1e3)) * tokens_per_step,
+                "d12_steps_in_300s_with_optimizer": int(300.0 / ((ms + opt_ms) / 1e3)),
+                "note": "the autoresearch pages give each experiment 5 minutes of training "
+                        "on one GPU"},
+            "microgpt_cpu": "the microgpt page's pure-Python run: 1,000 steps of a "
+                            "4,192-parameter model in about a minute on a CPU"},
         "roofline": roof, "cpu_baseline": cpu,
         "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
                     for r in prof],

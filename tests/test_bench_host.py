@@ -38,3 +38,15 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_clock_parsing_and_host_info():
+    sys.path.insert(0, ROOT)
+    import bench
+    txt = ("============ ROCm System Management Interface ============\n"
+           "GPU[0]\t\t: fclk clock level: 0: (1600Mhz)\n"
+           "GPU[0]\t\t: sclk clock level: 1: (2400Mhz)\n")
+    assert bench.parse_sclk(txt) == 2400
+    assert bench.parse_sclk("no clocks here") is None
+    info = bench.host_cpu_info()
+    assert info["cores"] >= 1 and "blas_threads" in info

@@ -869,3 +869,25 @@ def test_extras_closed_forms():
                                        atol=1e-15)
     np.testing.assert_array_equal(X.backout(x, x, 1.0), np.zeros_like(x))
     np.testing.assert_array_equal(X.backout(x, x0, 0.0), x)
+
+
+def test_batch_gradient_is_mean_of_row_gradients_in_the_oracle():
+    """Rows never interact, so the oracle's gradient of a batch's mean loss
+    equals the mean of its one-row gradients, and its evaluation sums are
+    the sums of its rows' (fp64, tiny+ with windows, GQA and value
+    embeddings) -- computed through the worker pool the full-size GPU tests
+    use, so the pool's bookkeeping (row split, sums, order) is pinned too."""
+    from tests.gpu_util import tiny_plus
+    from tests import oracle_pool
+    cfg = dict(tiny_plus(), batch=5)
+    w, _ = gi.make_params(cfg, O.param_count(cfg))
+    tok = gi.make_tokens(cfg)
+    loss, g, _ = O.step(cfg, w, tok, "fp64")
+    gm, losses = oracle_pool.mean_row_gradients(cfg, w, tok, "fp64", workers=2, cores=2)
+    # the pool keeps fp32 partial sums
+    assert np.abs(gm - g).max() <= 1e-6 * np.abs(g).max()
+    assert abs(losses.mean() - loss) < 1e-12
+    tb = gi.make_token_bytes(cfg)
+    sums = oracle_pool.row_eval_sums(cfg, w, tok, tb, "fp64", workers=3, cores=3)
+    ref = O.eval_bpb(cfg, w, tok, tb, "fp64")
+    assert abs(sums[:, 0].sum() - ref[0]) < 1e-10 and sums[:, 1].sum() == ref[1]
