@@ -917,7 +917,7 @@ def test_normuon_update(rows, cols):
         got = to_np(tw).reshape(rows, cols)
         assert rel_err(got - w0, w - w0) < 1e-5
         assert rel_err(to_np(tv), v) < 1e-5
-        np.testing.assert_array_equal(to_np(tw16), O.round_bf16(tw.cpu().numpy()))
+        np.testing.assert_array_equal(to_np(tw16), O.round_bf16(tw.cpu().numpy()).reshape(-1))
 
 
 # ------------------------------------------------------ model extras
@@ -1048,7 +1048,10 @@ def test_optim_step(which, normuon):
                     x, vrow = muon.normuon(x, vrow, 0.9)
                 w = muon.muon_update(w, x, lr, hpd["muon_wd"])
             d_ref, d_got = w - w0[sl].reshape(shape), got[sl].reshape(shape) - w0[sl].reshape(shape)
-            assert rel_err(d_got, d_ref) < 2e-2, name
+            # NorMuon rescales each row by the bf16 iterate's own row
+            # statistics, which carry the iteration's error once more: the
+            # bar of the orthogonalization against its bf16 emulation
+            assert rel_err(d_got, d_ref) < (3e-2 if normuon else 2e-2), name
         else:
             lr = {"wte": hpd["adam_lr_embed"], "ve": hpd["adam_lr_embed"],
                   "wlm": hpd["adam_lr_head"], "wg": hpd["adam_lr_gate"],
