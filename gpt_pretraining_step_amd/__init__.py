@@ -123,6 +123,9 @@ _SIGS = {
     "gpt_k_attn_decode_scratch_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "gpt_k_attn_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _f32, _vp, _sz, _i32, _vp]),
+    "gpt_k_attn_decode_noalloc_max_scratch": (_sz, []),
+    "gpt_k_attn_decode_noalloc": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                            _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
     "gpt_k_fp8_cast_scratch_bytes": (_sz, []),
     "gpt_k_fp8_cast": (C.c_int, [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "gpt_k_gemm_fp8_scratch_bytes": (_sz, [_i64, _i64, _i64]),
@@ -313,6 +316,18 @@ def k_attn_decode(q, k_cache, v_cache, cache_lens, o, lse, B, Tq, Tmax, H, Hkv, 
     _check(lib().gpt_k_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens),
                                    _ptr(o), _ptr(lse), B, Tq, Tmax, H, Hkv, hd, window,
                                    score_bound, _ptr(scratch), nb, dtype, _stream(stream)))
+
+
+def k_attn_decode_noalloc_max_scratch():
+    return int(lib().gpt_k_attn_decode_noalloc_max_scratch())
+
+
+def k_attn_decode_noalloc(q, k_cache, v_cache, cache_lens, o, lse, B, Tq, Tmax, H, Hkv, hd,
+                          window, score_bound, dtype, stream=None):
+    _check(lib().gpt_k_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                           _ptr(cache_lens), _ptr(o), _ptr(lse), B, Tq, Tmax,
+                                           H, Hkv, hd, window, score_bound, dtype,
+                                           _stream(stream)))
 
 
 FP8_E4M3, FP8_E5M2 = 0, 1

@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -580,6 +581,40 @@ int check_ptrs(std::initializer_list<const void*> ps) {
     if (!q) return fail(GPT_ERR_INVALID_ARG, "a required pointer is null");
     if (!aligned16(q)) return fail(GPT_ERR_MISALIGNED, "a pointer is not 16-byte aligned");
   }
+  return GPT_OK;
+}
+
+// ------------------------------ decode attention without allocation
+// The split-key scratch of gpt_k_attn_decode (arrival counters, then the
+// chunks' partial records) in a fixed-size device array instead of a caller
+// buffer, for callers that cannot allocate (graph capture, serving loops).
+// Each GPU holds its own copy of the array; host code reaches it only
+// through the device address looked up below, once per device.  The decode
+// plan caps the records at 510 chunk records of 16 query slots x 130 floats
+// (plus 1 KB of counters): 4,244,224 bytes, so every size the regular entry
+// accepts fits.
+constexpr size_t kDecodeScratchMax = (size_t)8 << 20;      // bytes per GPU
+static __device__ __align__(256) unsigned char decode_scratch[kDecodeScratchMax];
+constexpr int kMaxDevices = 64;
+void* g_decode_scratch[kMaxDevices];
+std::mutex g_decode_scratch_mu;
+
+// The array's address on the current device (looked up with that device
+// current, the first time it is asked for there).
+int decode_scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GPT_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(GPT_ERR_HIP, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_decode_scratch_mu);
+  if (!g_decode_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(decode_scratch));
+    if (e != hipSuccess || !p)
+      return fail(GPT_ERR_HIP, "hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_decode_scratch[dev] = p;
+  }
+  *out = g_decode_scratch[dev];
   return GPT_OK;
 }
 
@@ -1229,6 +1264,31 @@ int gpt_k_attn_decode(const void* q, const void* k_cache, const void* v_cache,
   KERNEL_TRY(gk::attn_decode(q, k_cache, v_cache, cache_lens, o, lse, B, Tq, Tmax, H, Hkv,
                              window, score_bound, scratch, s));
   return GPT_OK;
+}
+
+size_t gpt_k_attn_decode_noalloc_max_scratch(void) { return kDecodeScratchMax; }
+
+int gpt_k_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* cache_lens, void* o, float* lse, int32_t B,
+                              int32_t Tq, int32_t Tmax, int32_t H, int32_t Hkv, int32_t hd,
+                              int32_t window, float score_bound, int32_t dtype, hipStream_t s) {
+  // sizes the regular entry rejects give 0 here and are rejected by it below
+  const size_t need = gpt_k_attn_decode_scratch_bytes(B, Tq, H, Hkv, Tmax, window);
+  if (need > kDecodeScratchMax)
+    return fail(GPT_ERR_INVALID_ARG,
+                "these sizes need %zu bytes of decode scratch; the no-allocation entry holds "
+                "%zu (use gpt_k_attn_decode with a caller buffer)", need, kDecodeScratchMax);
+  void* p = nullptr;
+  if (need) {
+    int st = decode_scratch_ptr(&p);
+    if (st) return st;
+    // the counters start at zero: cleared by a kernel (no memset node, so
+    // the call can be captured into a graph)
+    const size_t nc = gk::attn_decode_counter_bytes(B, Tq, H, Hkv, Tmax, window);
+    KERNEL_TRY(gk::fill_zero(p, (int64_t)nc, s));
+  }
+  return gpt_k_attn_decode(q, k_cache, v_cache, cache_lens, o, lse, B, Tq, Tmax, H, Hkv, hd,
+                           window, score_bound, p, need, dtype, s);
 }
 
 int gpt_k_ce(const float* z, const int32_t* tgt, int64_t rows, int32_t V, float* ell, float* lse,

@@ -342,6 +342,11 @@ DecodePlan decode_plan(int B, int Tq, int H, int Hkv, int Tmax, int W) {
 // query group), padded to 256 bytes), then the partial records
 size_t counter_bytes(const DecodePlan& d) { return (d.pairs * 4 + 255) / 256 * 256; }
 
+size_t attn_decode_counter_bytes(int B, int Tq, int H, int Hkv, int Tmax, int W) {
+  const DecodePlan d = decode_plan(B, Tq, H, Hkv, Tmax, W);
+  return d.nchunks == 1 ? 0 : counter_bytes(d);
+}
+
 size_t attn_decode_scratch_bytes(int B, int Tq, int H, int Hkv, int Tmax, int W) {
   const DecodePlan d = decode_plan(B, Tq, H, Hkv, Tmax, W);
   if (d.nchunks == 1) return 0;

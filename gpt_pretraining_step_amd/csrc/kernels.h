@@ -113,6 +113,9 @@ size_t attn_bwd_scratch_bytes(int B, int T, int H, int hd);
 // 128], lse [B, H, Tq].  Query t of sequence b at position lens[b] - Tq + t.
 // scratch: attn_decode_scratch_bytes (0: none needed).
 size_t attn_decode_scratch_bytes(int B, int Tq, int H, int Hkv, int Tmax, int W);
+// the leading part of that scratch that must be zero before a launch (the
+// arrival counters; the kernel returns them to zero)
+size_t attn_decode_counter_bytes(int B, int Tq, int H, int Hkv, int Tmax, int W);
 hipError_t attn_decode(const void* q, const void* kc, const void* vc, const int32_t* lens,
                        void* o, float* lse, int B, int Tq, int Tmax, int H, int Hkv, int W,
                        float score_bound, void* scratch, hipStream_t s);

@@ -498,6 +498,27 @@ int gpt_k_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                       float score_bound, void* scratch, size_t scratch_bytes,
                       int32_t dtype, hipStream_t s);
 
+/* gpt_k_attn_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results without the scratch buffer.
+ * Its scratch is a library-owned device array of
+ * gpt_k_attn_decode_noalloc_max_scratch() bytes (8 MiB) per GPU, held
+ * until the process ends.  Every size gpt_k_attn_decode accepts needs at
+ * most 4,244,224 bytes of scratch, so all of them fit; a size whose
+ * gpt_k_attn_decode_scratch_bytes() exceeded the array would return
+ * GPT_ERR_INVALID_ARG before anything is enqueued.  The
+ * call allocates nothing: it clears the array's counters with a kernel on
+ * `s` (no memset node) and runs the decode kernel on it.  All calls on one
+ * GPU share the array, so calls that overlap on one GPU (other streams, or
+ * other threads) race; serialise them. */
+size_t gpt_k_attn_decode_noalloc_max_scratch(void);
+int gpt_k_attn_decode_noalloc(const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* cache_lens,
+                              void* o, float* lse, int32_t B, int32_t Tq,
+                              int32_t Tmax, int32_t H, int32_t Hkv, int32_t hd,
+                              int32_t window, float score_bound, int32_t dtype,
+                              hipStream_t s);
+
 /* Token embedding (a1).  tokens [B, T+1] int32 (inputs are the first T of
  * each row), wte [V, D] dtype -> x [B*T, D] dtype: x[b*T + t] =
  * wte[tokens[b][t]] (bitwise copies of the rows). */

@@ -240,3 +240,23 @@ def test_no_cpu_fallback_in_product_path():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
+
+
+def test_decode_noalloc_array_covers_every_decode_size():
+    """The no-allocation decode entry's array holds the scratch of every
+    size the regular decode entry accepts: the plan caps the split-key
+    records (at most 510 chunk records), and a scan over batch, group
+    width, query count and cache length never needs more than the cap."""
+    cap = G.k_attn_decode_noalloc_max_scratch()
+    worst = 0
+    for B in (1, 2, 5, 17, 64, 85, 86, 128, 129, 255, 256, 1000):
+        for Hkv in (1, 2, 3):
+            for grp in (1, 3, 16, 33):
+                for Tq in (1, 2, 16, 31):
+                    if grp * Tq > 1024:
+                        continue
+                    for Tmax in (64, 4096, 100000):
+                        for W in (0, 1024, Tmax):
+                            worst = max(worst, G.k_attn_decode_scratch_bytes(
+                                B, Tq, Hkv * grp, Hkv, Tmax, W))
+    assert 0 < worst <= 4_244_224 <= cap
