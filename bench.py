@@ -433,7 +433,9 @@ def bench_decode(a, torch, G):
                                f"positions, 1 new token each, {n_layer} layers "
                                f"'{cfg['window_pattern']}' {cfg['window_short']}/"
                                f"{cfg['window_long']}, {H} heads on {Hkv} KV heads x 128",
-                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU",
+                   "streams": "one" if a.one_stream else
+                              "two (weight-gradient work of the backward on a second stream)"},
         "kv_bytes_per_step": kv_bytes, "kv_gbps": round(kv_bytes / ms / 1e6, 1),
         "roofline": roof, "cpu_baseline": cpu,
         "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
@@ -824,7 +826,9 @@ def bench_extras(a, torch, G):
         "data": "synthetic (seeded N(0,1) activations and gradients)",
         "config": {"workload": f"{a.config} model extras: smear + backout once, residual "
                                f"mixing x {L}, forward and backward, {N} tokens x {D}",
-                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU",
+                   "streams": "one" if a.one_stream else
+                              "two (weight-gradient work of the backward on a second stream)"},
         "roofline": roof, "cpu_baseline": None,
         "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
                     for r in prof],
@@ -874,6 +878,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-gqa-eval", action="store_true",
                     help="train: skip the d12-GQA 2^21-target evaluation line")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="train: the whole step on one stream (no second stream for the "
+                         "weight-gradient work)")
     ap.add_argument("--workload", choices=("train", "decode", "fp8", "muon", "optim", "extras"),
                     default="train",
                     help="train: the fwd+bwd step; decode: KV-cache decode attention; fp8: the "
@@ -928,6 +935,8 @@ def main():
     cfg = gi.preset(a.config)
     if a.model_extras:
         cfg.update(resid_lambdas=1, smear=1, backout_layer=cfg["n_layer"] // 2)
+    if a.one_stream:
+        cfg.update(one_stream=1)
     train_fpt, eval_fpt, mm = model_flops(cfg)
     B, T = cfg["batch"], cfg["seq_len"]
     tokens_per_step = B * T
@@ -1017,8 +1026,13 @@ def main():
     if not a.model_extras and a.config == "d12" and not a.no_gqa_eval:
         gqa = eval_set_line("d12gqa", torch, G, gi, Session)
 
-    # per-kernel split of the step with the library's launch recording
+    # per-kernel split of the step with the library's launch recording, the
+    # step on one stream (a kernel's time then carries no overlap with the
+    # backward's second stream)
+    step_cfg = s.cfg
+    s.cfg = G.make_config(dict(cfg, one_stream=1))
     prof = kernel_profile(step, a.prof_steps, torch, G) if a.prof_steps > 0 else []
+    s.cfg = step_cfg
     roof = roofline_of(prof[0], ms) if prof else None
     for r in prof[:14]:
         rate = (f"{r['tflops']:7.1f} TFLOP/s" if r["tflops"] else
@@ -1056,7 +1070,9 @@ def main():
                                f"{cfg['window_long']}, value embeddings on odd layers"
                                + (f", model extras (residual mixing, smear, backout after "
                                   f"block {cfg['backout_layer']})" if a.model_extras else ""),
-                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU",
+                   "streams": "one" if a.one_stream else
+                              "two (weight-gradient work of the backward on a second stream)"},
         "mfu_bf16": round(mfu, 4), "train_flop_per_token": train_fpt,
         "gpu_clock_mhz": clock, "mfu_bf16_clock_adjusted": round(mfu_clk, 4) if mfu_clk else None,
         "clock_note": f"median shader clock sampled by rocm-smi during the timed steps; "

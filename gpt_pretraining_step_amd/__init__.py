@@ -40,7 +40,7 @@ class GptConfig(C.Structure):
         ("ve_every_odd", C.c_int32), ("rope_base", C.c_float),
         ("norm_eps", C.c_float), ("dtype", C.c_int32),
         ("resid_lambdas", C.c_int32), ("smear", C.c_int32), ("backout", C.c_int32),
-        ("backout_layer", C.c_int32), ("check_tokens", C.c_int32),
+        ("backout_layer", C.c_int32), ("check_tokens", C.c_int32), ("one_stream", C.c_int32),
     ]
 
 
@@ -80,6 +80,7 @@ def make_config(d: dict) -> GptConfig:
     d.setdefault("resid_lambdas", 0)
     d.setdefault("smear", 0)
     d.setdefault("check_tokens", 0)
+    d.setdefault("one_stream", 0)
     bl = int(d.get("backout_layer", -1))
     d["backout"], d["backout_layer"] = (1, bl) if bl >= 0 else (0, 0)
     for name, _ in GptConfig._fields_:

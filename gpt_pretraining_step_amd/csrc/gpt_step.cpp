@@ -22,6 +22,7 @@ static constexpr bool kDebugChecks = true;
 #else
 static constexpr bool kDebugChecks = false;
 #endif
+static constexpr int kMaxSideDevices = 64;
 
 namespace {
 
@@ -62,6 +63,7 @@ struct Model {
   int resid, smear, bo;
   int ex_n, ex_sw, ex_sl, ex_bo;
   bool check_tokens;          // count out-of-range ids before any gather
+  bool one_stream;            // backward on the caller's stream only
 
   bool extras() const { return resid || smear || bo >= 0; }
 
@@ -109,6 +111,8 @@ int validate(const gpt_config* c, Model* m) {
     return fail(GPT_ERR_INVALID_ARG, "resid_lambdas, smear and backout must be 0 or 1");
   if (c->check_tokens != 0 && c->check_tokens != 1)
     return fail(GPT_ERR_INVALID_ARG, "check_tokens must be 0 or 1");
+  if (c->one_stream != 0 && c->one_stream != 1)
+    return fail(GPT_ERR_INVALID_ARG, "one_stream must be 0 or 1");
   if (c->backout && (c->backout_layer < 0 || c->backout_layer >= c->n_layer))
     return fail(GPT_ERR_INVALID_ARG, "backout_layer %d not in [0, n_layer)", c->backout_layer);
   if ((c->resid_lambdas || c->smear || c->backout) && c->d_model % 8)
@@ -132,6 +136,7 @@ int validate(const gpt_config* c, Model* m) {
     m->ex_bo = 2 * m->L + 25;
     m->ex_n = 8 * ((2 * m->L + 26 + 7) / 8);
     m->check_tokens = c->check_tokens != 0 || kDebugChecks;
+    m->one_stream = c->one_stream != 0;
   }
   return GPT_OK;
 }
@@ -184,7 +189,7 @@ struct Plan {
   size_t xe, sgate, x0, xmid, dx0, dxmid, dxe, ex_scr;
   std::vector<size_t> xpre;
   // backward scratch
-  size_t dx, dh, du, dout, dqkv, attn_scr, vez, vwg, sort, gemm_scr, gemm_scr_bytes;
+  size_t dx, dh, du, dout, dqkv, attn_scr, vez, vwg, sort, gemm_scr, gemm_scr_bytes, wtp;
   bool sorted_scatter;   // embedding-table gradients by the token sort (no atomics)
   size_t total;
 };
@@ -266,15 +271,17 @@ Plan make_plan(const Model& m, int mode) {
     size_t gs = 0;
     const int64_t HD = (int64_t)m.H * m.hd;
     const int64_t shapes[5][2] = {{m.V, m.D}, {m.D, m.F}, {m.F, m.D}, {m.D, HD}, {m.QKV, m.D}};
-    if (m.dt == gk::BF16) {
+    if (m.dt == gk::BF16)
       for (auto& sh : shapes) gs = std::max(gs, gk::gemm_scratch_bytes(sh[0], sh[1], N));
-      // also holds the transposed copy of W_proj for the MLP backward
-      gs = std::max(gs, (size_t)m.F * m.D * 2);
-    }
     p.gemm_scr_bytes = gs;
     p.gemm_scr = take(gs);
+    // the transposed copy of W_proj for the MLP backward (its own buffer:
+    // the weight-gradient products that use the split-K scratch may run at
+    // the same time)
+    p.wtp = m.dt == gk::BF16 ? take((size_t)m.F * m.D * 2) : 0;
   } else {
     p.dx = p.dh = p.du = p.dout = p.dqkv = p.attn_scr = p.vez = p.vwg = p.sort = p.gemm_scr = 0;
+    p.wtp = 0;
     p.sorted_scatter = false;
     p.gemm_scr_bytes = 0;
   }
@@ -422,6 +429,43 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
   return GPT_OK;
 }
 
+// The backward's second stream.  The weight-gradient products and the
+// embedding-table and gate gradients are off the backward's critical path
+// (nothing later reads them): they run on a library-owned stream, forked
+// from the caller's stream where their inputs are ready and joined back
+// before those inputs are overwritten and before the call returns, so they
+// fill the caller stream's memory-bound kernels and kernel tails.  One
+// stream and set of events per (host thread, device), created on first use
+// and kept; default priority.  Results are bit for bit those of one stream
+// (every kernel and its inputs are unchanged; only the overlap differs).
+enum { EV_START, EV_DX1, EV_DX1_FREE, EV_DU, EV_DU_FREE, EV_DX2, EV_DX2_FREE, EV_QKV,
+       EV_QKV_FREE, EV_END, EV_COUNT };
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t ev[EV_COUNT] = {};
+  bool ready = false, failed = false;
+};
+thread_local SideStream t_side[kMaxSideDevices];
+
+// the side stream of the current device, or null (one stream then)
+SideStream* side_stream() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
+  SideStream& ss = t_side[dev];
+  if (ss.ready) return &ss;
+  if (ss.failed) return nullptr;
+  bool ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess;
+  for (int i = 0; ok && i < EV_COUNT; ++i)
+    ok = hipEventCreateWithFlags(&ss.ev[i], hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    ss.failed = true;
+    return nullptr;
+  }
+  ss.ready = true;
+  return &ss;
+}
+
 int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const void* params,
                  const int32_t* tokens, void* ws, float* grads, int accumulate, hipStream_t s) {
   const int64_t N = p.N;
@@ -439,6 +483,25 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
   const float* cs = at<float>(ws, p.cs);
   const void* dz = at<void>(ws, p.dz);
   const void* hf = at<void>(ws, p.hf);
+  // w: the stream of the off-path gradient work (the caller's stream when
+  // the model is small or the side stream is unavailable)
+  SideStream* sd = m.dt == gk::BF16 && N >= 4096 && !m.one_stream ? side_stream() : nullptr;
+  const hipStream_t w = sd ? sd->s : s;
+  bool marked[EV_COUNT] = {};
+  auto fork = [&](int e) -> hipError_t {       // w waits for s's work so far
+    if (!sd) return hipSuccess;
+    hipError_t r = hipEventRecord(sd->ev[e], s);
+    return r == hipSuccess ? hipStreamWaitEvent(w, sd->ev[e], 0) : r;
+  };
+  auto mark = [&](int e) -> hipError_t {       // a point in w's work
+    if (!sd) return hipSuccess;
+    marked[e] = true;
+    return hipEventRecord(sd->ev[e], w);
+  };
+  auto need = [&](int e) -> hipError_t {       // s waits for w's work up to mark(e)
+    if (!sd || !marked[e]) return hipSuccess;
+    return hipStreamWaitEvent(s, sd->ev[e], 0);
+  };
 
   // embedding tables: the batch's token ids are sorted once and every table
   // row is summed in a fixed order (rows of absent ids cleared unless
@@ -463,9 +526,11 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
   void* x0 = m.resid ? at<void>(ws, p.x0) : nullptr;
   void* dx0 = m.resid ? at<void>(ws, p.dx0) : nullptr;
   void* dxmid = m.bo >= 0 ? at<void>(ws, p.dxmid) : nullptr;
+  // w starts after the token sort, the table clears and the forward
+  HIP_TRY(fork(EV_START));
   // lm_head
   gk::GemmDesc g{gk::OP_TN, m.V, m.D, N, dz, m.V, hf, m.D, grads + pl.wlm, m.D, wepi, nullptr};
-  HIP_TRY(gk::gemm(g, dt, s));
+  HIP_TRY(gk::gemm(g, dt, w));
   g = gk::GemmDesc{gk::OP_NN, N, m.D, m.V, dz, m.V, elem(params, pl.wlm, es), m.D, dh, m.D,
                    gk::E_STORE, nullptr};
   HIP_TRY(gk::gemm(g, dt, s));
@@ -487,35 +552,44 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
     const void* a = at<void>(ws, b.a);
     const int64_t HD = (int64_t)m.H * m.hd;
     // MLP
+    HIP_TRY(fork(EV_DX1));                      // dx (the block output's gradient) ready
     g = gk::GemmDesc{gk::OP_TN, m.D, m.F, N, dx, m.D, a, m.F, grads + pl.wproj[l], m.F, wepi,
                      nullptr, gscr, gscr_bytes};
-    HIP_TRY(gk::gemm(g, dt, s));
+    HIP_TRY(gk::gemm(g, dt, w));
+    HIP_TRY(mark(EV_DX1_FREE));
+    HIP_TRY(need(EV_DU_FREE));                  // the previous block's dW_fc has read du
     if (dt == gk::BF16 && m.F % 8 == 0 && m.D % 8 == 0) {
-      // du = (dx W_proj) * 2 sqrt(a) as an NT product against W_proj^T (in
-      // the GEMM scratch, free between the weight-gradient products): the
-      // K-contiguous operand reads run faster than the transposing ones
-      HIP_TRY(gk::transpose_bf16(elem(params, pl.wproj[l], es), m.D, m.F, gscr, s));
-      g = gk::GemmDesc{gk::OP_NT, N, m.F, m.D, dx, m.D, gscr, m.D, du, m.F, gk::E_DRELU2,
+      // du = (dx W_proj) * 2 sqrt(a) as an NT product against W_proj^T:
+      // the K-contiguous operand reads run faster than the transposing ones
+      void* wtp = at<void>(ws, p.wtp);
+      HIP_TRY(gk::transpose_bf16(elem(params, pl.wproj[l], es), m.D, m.F, wtp, s));
+      g = gk::GemmDesc{gk::OP_NT, N, m.F, m.D, dx, m.D, wtp, m.D, du, m.F, gk::E_DRELU2,
                        const_cast<void*>(a)};
     } else {
       g = gk::GemmDesc{gk::OP_NN, N, m.F, m.D, dx, m.D, elem(params, pl.wproj[l], es), m.F, du,
                        m.F, gk::E_DRELU2, const_cast<void*>(a)};
     }
     HIP_TRY(gk::gemm(g, dt, s));
+    HIP_TRY(fork(EV_DU));
     g = gk::GemmDesc{gk::OP_TN, m.F, m.D, N, du, m.F, h2, m.D, grads + pl.wfc[l], m.D, wepi,
                      nullptr, gscr, gscr_bytes};
-    HIP_TRY(gk::gemm(g, dt, s));
+    HIP_TRY(gk::gemm(g, dt, w));
+    HIP_TRY(mark(EV_DU_FREE));
     g = gk::GemmDesc{gk::OP_NN, N, m.D, m.F, du, m.F, elem(params, pl.wfc[l], es), m.D, dh, m.D,
                      gk::E_STORE, nullptr};
     HIP_TRY(gk::gemm(g, dt, s));
+    HIP_TRY(need(EV_DX1_FREE));                 // dW_proj has read dx
     HIP_TRY(gk::rmsnorm_bwd(dh, h2, at<float>(ws, b.r2), dx, dx, N, m.D, nullptr, nullptr, 0, 0,
                             dt, s));
     // attention
+    HIP_TRY(fork(EV_DX2));
     g = gk::GemmDesc{gk::OP_TN, m.D, HD, N, dx, m.D, o, HD, grads + pl.wo[l], HD, wepi, nullptr, gscr, gscr_bytes};
-    HIP_TRY(gk::gemm(g, dt, s));
+    HIP_TRY(gk::gemm(g, dt, w));
+    HIP_TRY(mark(EV_DX2_FREE));
     g = gk::GemmDesc{gk::OP_NN, N, HD, m.D, dx, m.D, elem(params, pl.wo[l], es), HD, dout, HD,
                      gk::E_STORE, nullptr};
     HIP_TRY(gk::gemm(g, dt, s));
+    HIP_TRY(need(EV_QKV_FREE));                 // the previous block's users of dqkv, vez are done
     // attention backward; where the kernels can, they also apply the
     // backward of RoPE-then-QK-norm in their epilogues
     if (gk::attn_bwd_fuses_norm(m.T, m.H, m.Hkv, m.hd, dt)) {
@@ -534,22 +608,28 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
       if (sorted) {
         HIP_TRY(gk::ve_vez(tokens, m.B, m.T, dqkv, m.QKV, voff, elem(params, pl.ve[l], es),
                            at<float>(ws, b.g), vez, m.Hkv, m.hd, dt, s));
+        HIP_TRY(fork(EV_QKV));
         HIP_TRY(gk::seg_scatter(sortws, N, m.V, maxW, elem(dqkv, voff, es), m.QKV,
                                 m.Hkv * m.hd, at<float>(ws, b.g), m.Hkv, m.hd, grads + pl.ve[l],
-                                accumulate, dt, s));
+                                accumulate, dt, w));
       } else {
         HIP_TRY(gk::ve_bwd(tokens, m.B, m.T, dqkv, m.QKV, voff, elem(params, pl.ve[l], es),
                            at<float>(ws, b.g), vez, grads + pl.ve[l], m.Hkv, m.hd, dt, s));
+        HIP_TRY(fork(EV_QKV));
       }
       HIP_TRY(gk::ve_wgrad(vez, h, m.D, N, m.Hkv, m.C, grads + pl.wg[l], accumulate,
-                           at<float>(ws, p.vwg), dt, s));
+                           at<float>(ws, p.vwg), dt, w));
+    } else {
+      HIP_TRY(fork(EV_QKV));
     }
     g = gk::GemmDesc{gk::OP_TN, m.QKV, m.D, N, dqkv, m.QKV, h, m.D, grads + pl.wqkv[l], m.D,
                      wepi, nullptr, gscr, gscr_bytes};
-    HIP_TRY(gk::gemm(g, dt, s));
+    HIP_TRY(gk::gemm(g, dt, w));
+    HIP_TRY(mark(EV_QKV_FREE));
     g = gk::GemmDesc{gk::OP_NN, N, m.D, m.QKV, dqkv, m.QKV, elem(params, pl.wqkv[l], es), m.D,
                      dh, m.D, gk::E_STORE, nullptr};
     HIP_TRY(gk::gemm(g, dt, s));
+    HIP_TRY(need(EV_DX2_FREE));                 // dW_o has read dx
     HIP_TRY(gk::rmsnorm_bwd(dh, h, at<float>(ws, b.r), dx, dx, N, m.D, ve ? vez : nullptr,
                             ve ? elem(params, pl.wg[l], es) : nullptr, m.Hkv, m.C, dt, s));
     // mix x = lr_l x_pre + l0_l x0: dx_pre = lr_l dx, x0's gradient gathers
@@ -573,6 +653,9 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
                             grads + pl.wte, accumulate, dt, s));
   else
     HIP_TRY(gk::embed_bwd(tokens, m.B, m.T, demb, m.D, grads + pl.wte, m.D, dt, s));
+  // everything on w is done before the caller's stream moves on
+  HIP_TRY(mark(EV_END));
+  HIP_TRY(need(EV_END));
   return GPT_OK;
 }
 

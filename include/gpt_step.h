@@ -85,6 +85,13 @@ enum { GPT_MODE_TRAIN = 0, GPT_MODE_EVAL = 1 };
  *     check has been enqueued then.  0 = ids are a precondition (no check,
  *     no synchronisation).  A library built for debugging
  *     (`python -m gpt_pretraining_step_amd.build --debug`) checks always.
+ *   one_stream: 1 = gpt_step_bwd runs everything on the caller's stream.
+ *     0 = for bf16 models of at least 4096 tokens the weight-gradient
+ *     products and the embedding and gate gradients run on a second,
+ *     library-owned stream (one per host thread and device, default
+ *     priority), forked from and joined back into the caller's stream with
+ *     events, so the call still completes in the caller's stream order (and
+ *     can be captured into a graph); results are bit for bit the same.
  */
 typedef struct gpt_config {
   int32_t n_layer, d_model, n_head, n_kv_head, head_dim, vocab, seq_len, batch;
@@ -96,6 +103,7 @@ typedef struct gpt_config {
   int32_t dtype;
   int32_t resid_lambdas, smear, backout, backout_layer;
   int32_t check_tokens;
+  int32_t one_stream;
 } gpt_config;
 
 /* ------------------------------------------------------- sizes and layout */

@@ -106,6 +106,7 @@ def _bad(**kw):
     (dict(backout_layer=4), -1),
     (dict(smear=2), -1),
     (dict(check_tokens=2), -1),
+    (dict(one_stream=3), -1),
     (dict(resid_lambdas=1, d_model=252, n_head=2, head_dim=128), -2),
     (dict(smear=1, d_model=16, n_head=2, head_dim=8, ve_gate_channels=8), -2),
 ])

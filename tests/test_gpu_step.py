@@ -271,3 +271,29 @@ def test_token_check():
         assert s.loss.item() == -123.0
         off = G.ws_offset(s.cfg, G.WS_BAD_TOKENS)
         assert int(s.ws[off:off + 4].view(torch.int32).item()) == len(bad_ids)
+
+
+@pytest.mark.parametrize("extras", [False, True])
+def test_two_stream_backward_equals_one_stream(extras):
+    """At 4096 tokens the backward runs its weight-gradient products and
+    table gradients on a second stream; every gradient equals, bit for bit,
+    the same backward on the caller's stream alone, over two steps (the
+    second accumulating)."""
+    cfg = small_bf16(batch=16, seq_len=256)
+    if extras:
+        cfg.update(resid_lambdas=1, smear=1, backout_layer=0)
+    n = O.param_count(cfg)
+    w, bits = with_extras(cfg, *gi.make_params(cfg, n))
+    tok = gi.make_tokens(cfg)
+    out = []
+    for one in (0, 1):
+        s = Session(dict(cfg, one_stream=one))
+        s.set_params(w, bits)
+        s.set_tokens(tok)
+        s.fwd()
+        s.bwd()
+        s.fwd()
+        s.bwd(accumulate=True)
+        torch.cuda.synchronize()
+        out.append(s.grads.clone())
+    assert torch.equal(out[0], out[1])
