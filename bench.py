@@ -290,22 +290,42 @@ def host_cpu_info():
 
 
 def gpu_clock_mhz():
-    """Current shader clock of GPU 0 in MHz from rocm-smi, or None."""
-    import re
-    import subprocess
-    try:
-        out = subprocess.run(["rocm-smi", "-d", "0", "--showclocks"], capture_output=True,
-                             text=True, timeout=20).stdout
-    except Exception:
-        return None
-    return parse_sclk(out)
+    """Current shader clock (MHz) of the first AMD GPU, read from sysfs (the
+    files rocm-smi reads; no child process is started), or None."""
+    import glob
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            with open(os.path.join(dev, "vendor")) as f:
+                if f.read().strip() != "0x1002":
+                    continue
+        except OSError:
+            continue
+        for hw in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*", "freq1_input"))):
+            try:
+                with open(hw) as f:
+                    return int(f.read().strip()) // 1000000
+            except (OSError, ValueError):
+                pass
+        try:
+            with open(os.path.join(dev, "pp_dpm_sclk")) as f:
+                c = parse_sclk(f.read())
+            if c:
+                return c
+        except OSError:
+            pass
+    return None
 
 
 def parse_sclk(text):
-    """The shader clock (MHz) in rocm-smi's --showclocks text, or None."""
+    """The active level (marked '*') of a pp_dpm_sclk listing, in MHz, or
+    None."""
     import re
-    m = re.search(r"sclk[^\n]*?\((\d+)\s*Mhz\)", text, re.IGNORECASE)
-    return int(m.group(1)) if m else None
+    for line in text.splitlines():
+        if "*" in line:
+            m = re.search(r"(\d+)\s*Mhz", line, re.IGNORECASE)
+            if m:
+                return int(m.group(1))
+    return None
 
 
 class ClockSampler:
@@ -1075,7 +1095,7 @@ def main():
                               "two (weight-gradient work of the backward on a second stream)"},
         "mfu_bf16": round(mfu, 4), "train_flop_per_token": train_fpt,
         "gpu_clock_mhz": clock, "mfu_bf16_clock_adjusted": round(mfu_clk, 4) if mfu_clk else None,
-        "clock_note": f"median shader clock sampled by rocm-smi during the timed steps; "
+        "clock_note": f"median shader clock read from sysfs during the timed steps; "
                       f"the adjusted MFU prices the peak at that clock instead of "
                       f"{max_clock} MHz",
         "optimizer_ms_per_step": round(opt_ms, 3),

@@ -301,7 +301,33 @@ struct TileMap {
   const bf16* ve_E = nullptr;
   float* ve_g = nullptr;
   int ve_D = 0, ve_C = 0;
+  // tile order inside one K split: 0 = column-major groups of 8 tile rows;
+  // 1 = row by row (tile_m slow), 2 = column by column (tile_n slow)
+  int order = 0;
 };
+
+// (tile_m, tile_n) of tile t of a split, in the order the plan chose.  The
+// blocks of one split are dealt to consecutive XCDs; with split K the run of
+// a split's tiles usually crosses an XCD boundary, and each XCD then reads
+// every panel its part of the run touches.  Row by row (or column by
+// column) order cuts the run across the larger operand's panels only once,
+// so only the smaller operand's panels are read by both XCDs.
+__device__ __forceinline__ void tile_of(const TileMap& tm, int t, int& tile_m, int& tile_n) {
+  if (tm.order == 1) {
+    tile_m = t / tm.tiles_n;
+    tile_n = t % tm.tiles_n;
+  } else if (tm.order == 2) {
+    tile_n = t / tm.tiles_m;
+    tile_m = t % tm.tiles_m;
+  } else {
+    constexpr int GM = 8;
+    const int group = t / (GM * tm.tiles_n);
+    const int first_m = group * GM;
+    const int gsize = min(tm.tiles_m - first_m, GM);
+    tile_m = first_m + (t % (GM * tm.tiles_n)) % gsize;
+    tile_n = (t % (GM * tm.tiles_n)) / gsize;
+  }
+}
 
 // two floats as packed fp16 (round to nearest even)
 __device__ __forceinline__ uint32_t pack2h(float a, float b) {
@@ -335,12 +361,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(int64_t M, int64_t N, int6
   const int ntile = tm.tiles_m * tm.tiles_n;
   const int split = logical / ntile;
   const int t = logical % ntile;
-  constexpr int GM = 8;
-  const int group = t / (GM * tm.tiles_n);
-  const int first_m = group * GM;
-  const int gsize = min(tm.tiles_m - first_m, GM);
-  const int tile_m = first_m + (t % (GM * tm.tiles_n)) % gsize;
-  const int tile_n = (t % (GM * tm.tiles_n)) / gsize;
+  int tile_m, tile_n;
+  tile_of(tm, t, tile_m, tile_n);
   const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
   const int64_t kbeg = (int64_t)split * tm.k_per_split;
   const int64_t kend = min(K, kbeg + tm.k_per_split);
@@ -426,12 +448,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mfma_db(int64_t M, int64_t N, i
   const int ntile = tm.tiles_m * tm.tiles_n;
   const int split = logical / ntile;
   const int t = logical % ntile;
-  constexpr int GM = 8;
-  const int group = t / (GM * tm.tiles_n);
-  const int first_m = group * GM;
-  const int gsize = min(tm.tiles_m - first_m, GM);
-  const int tile_m = first_m + (t % (GM * tm.tiles_n)) % gsize;
-  const int tile_n = (t % (GM * tm.tiles_n)) / gsize;
+  int tile_m, tile_n;
+  tile_of(tm, t, tile_m, tile_n);
   const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
   const int64_t kbeg = (int64_t)split * tm.k_per_split;
   const int64_t kend = min(K, kbeg + tm.k_per_split);
@@ -686,12 +704,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
   const int ntile = tm.tiles_m * tm.tiles_n;
   const int split = logical / ntile;
   const int t = logical % ntile;
-  constexpr int GM = 8;
-  const int group = t / (GM * tm.tiles_n);
-  const int first_m = group * GM;
-  const int gsize = min(tm.tiles_m - first_m, GM);
-  const int tile_m = first_m + (t % (GM * tm.tiles_n)) % gsize;
-  const int tile_n = (t % (GM * tm.tiles_n)) / gsize;
+  int tile_m, tile_n;
+  tile_of(tm, t, tile_m, tile_n);
   const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
   const int64_t kbeg = (int64_t)split * tm.k_per_split;
   const int64_t kend = min(K, kbeg + tm.k_per_split);
@@ -996,12 +1010,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(int64_t M, int64_t N, int64
   const int ntile = tm.tiles_m * tm.tiles_n;
   const int split = logical / ntile;
   const int t = logical % ntile;
-  constexpr int GM = 8;
-  const int group = t / (GM * tm.tiles_n);
-  const int first_m = group * GM;
-  const int gsize = min(tm.tiles_m - first_m, GM);
-  const int tile_m = first_m + (t % (GM * tm.tiles_n)) % gsize;
-  const int tile_n = (t % (GM * tm.tiles_n)) / gsize;
+  int tile_m, tile_n;
+  tile_of(tm, t, tile_m, tile_n);
   const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
   const int64_t kbeg = (int64_t)split * tm.k_per_split;
   const int64_t kend = min(Ku, kbeg + tm.k_per_split);
@@ -1283,6 +1293,9 @@ static TileMap plan_dma(int64_t M, int64_t N, int64_t K, bool f32out, size_t scr
   if (best > 1) {
     tm.k_per_split = cdiv(ksl, best) * BK;
     tm.splits = (int)cdiv(K, tm.k_per_split);
+    // a split's run of tiles crosses XCDs: keep the larger operand's
+    // panels (A's rows ~ M, B's ~ N) on one side of the cut
+    tm.order = M >= N ? 1 : 2;
   }
   return tm;
 }

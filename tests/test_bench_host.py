@@ -43,10 +43,8 @@ def test_bench_refuses_more_than_one_gpu():
 def test_clock_parsing_and_host_info():
     sys.path.insert(0, ROOT)
     import bench
-    txt = ("============ ROCm System Management Interface ============\n"
-           "GPU[0]\t\t: fclk clock level: 0: (1600Mhz)\n"
-           "GPU[0]\t\t: sclk clock level: 1: (2400Mhz)\n")
+    txt = "0: 500Mhz\n1: 1900Mhz\n2: 2400Mhz *\n"
     assert bench.parse_sclk(txt) == 2400
-    assert bench.parse_sclk("no clocks here") is None
+    assert bench.parse_sclk("0: 500Mhz\n1: 2400Mhz\n") is None
     info = bench.host_cpu_info()
     assert info["cores"] >= 1 and "blas_threads" in info
