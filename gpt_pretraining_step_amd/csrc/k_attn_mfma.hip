@@ -787,7 +787,7 @@ size_t attn_mfma_bwd_scratch_bytes(int, int, int, int) { return 0; }
 hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const void* dout,
                          void* dqkv, float* delta, void*, int B, int T, int H, int Hkv, int hd,
                          int W, hipStream_t s, const float* nrq, const float* nrk,
-                         const float* ncs) {
+                         const float* ncs, hipStream_t s2, hipEvent_t fork, hipEvent_t join) {
   (void)hd;
   const bool fuse = nrq && nrk && ncs;
   const NormBwdArgs nb{nrq, nrk, (const float2*)ncs};
@@ -804,6 +804,15 @@ hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const
   const Work wq(2.0 * HD * pairs, qkvo + stats + tok * H * HD * 2);
   GK_LAUNCH(wd, k_attn_delta, dim3((unsigned)cdiv(rows * 16, 256)), dim3(256), 0, s,
             (const bf16*)o, (const bf16*)dout, delta, T, H, rows);
+  // the dQ pass beside the dK and dV passes: the three write disjoint parts
+  // of dqkv and read only what Delta's pass and the forward left
+  const bool two = s2 && fork && join;
+  const hipStream_t sq = two ? s2 : s;
+  if (two) {
+    hipError_t e = hipEventRecord(fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s2, fork, 0);
+    if (e != hipSuccess) return e;
+  }
   // dK and dV in two passes (two waves per SIMD each; measured faster than
   // the one-wave-per-SIMD combined pass despite recomputing S)
   const dim3 gkv = xcd_grid((T + KV_BK - 1) / KV_BK, Hkv * B);
@@ -812,15 +821,20 @@ hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const
   const dim3 gq = xcd_grid((T + DQ_BQ - 1) / DQ_BQ, H * B);
 #define DKV_ARGS (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, B, T, H, Hkv, W, nb
   if (fuse) {
+    GK_LAUNCH(wq, k_attn_bwd_dq<true>, gq, dim3(NW * 64), 0, sq, DKV_ARGS);
     GK_LAUNCH(wk, (k_attn_bwd_dkv<2, 1, true>), gkv, dim3(NW * 64), 0, s, DKV_ARGS);
     GK_LAUNCH(wv, (k_attn_bwd_dkv<2, 2, false>), gkv, dim3(NW * 64), 0, s, DKV_ARGS);
-    GK_LAUNCH(wq, k_attn_bwd_dq<true>, gq, dim3(NW * 64), 0, s, DKV_ARGS);
   } else {
+    GK_LAUNCH(wq, k_attn_bwd_dq<false>, gq, dim3(NW * 64), 0, sq, DKV_ARGS);
     GK_LAUNCH(wk, (k_attn_bwd_dkv<2, 1, false>), gkv, dim3(NW * 64), 0, s, DKV_ARGS);
     GK_LAUNCH(wv, (k_attn_bwd_dkv<2, 2, false>), gkv, dim3(NW * 64), 0, s, DKV_ARGS);
-    GK_LAUNCH(wq, k_attn_bwd_dq<false>, gq, dim3(NW * 64), 0, s, DKV_ARGS);
   }
 #undef DKV_ARGS
+  if (two) {
+    hipError_t e = hipEventRecord(join, s2);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, join, 0);
+    if (e != hipSuccess) return e;
+  }
   return hipGetLastError();
 }
 

@@ -123,11 +123,18 @@ hipError_t attn_decode(const void* q, const void* kc, const void* vc, const int3
 // and attn_bwd_fuses_norm() true, the backward of RoPE-then-QK-norm is
 // applied too (dq, dk w.r.t. the raw q, k); otherwise they are ignored.
 bool attn_bwd_fuses_norm(int T, int H, int Hkv, int hd, DType dt);
+// A second stream for work that may run beside s, with two events: `fork`
+// (recorded on s, waited for by s2) and `join` (recorded on s2, waited for
+// by s).  A null s2 means one stream.
+struct Beside {
+  hipStream_t s2 = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
 hipError_t attn_bwd(const void* qkv, const void* o, const float* lse,
                     const void* dout, void* dqkv, void* scratch, int B, int T,
                     int H, int Hkv, int hd, int W, DType dt, hipStream_t s,
                     const float* nrq = nullptr, const float* nrk = nullptr,
-                    const float* ncs = nullptr);
+                    const float* ncs = nullptr, const Beside& beside = Beside());
 
 // cross-entropy over fp32 logits; tgt given by a token-row pointer:
 // target of row n = tok[(n / T) * (T+1) + n % T + 1]  (T = tgt_T)

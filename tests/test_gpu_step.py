@@ -273,14 +273,18 @@ def test_token_check():
         assert int(s.ws[off:off + 4].view(torch.int32).item()) == len(bad_ids)
 
 
-@pytest.mark.parametrize("extras", [False, True])
-def test_two_stream_backward_equals_one_stream(extras):
-    """At 4096 tokens the backward runs its weight-gradient products and
-    table gradients on a second stream; every gradient equals, bit for bit,
-    the same backward on the caller's stream alone, over two steps (the
-    second accumulating)."""
-    cfg = small_bf16(batch=16, seq_len=256)
-    if extras:
+@pytest.mark.parametrize("name", ["small", "small_extras", "d4"])
+def test_two_stream_backward_equals_one_stream(name):
+    """From 4096 tokens the backward runs its weight-gradient products and
+    table gradients on a second stream (and, at head_dim 128, the attention
+    dQ pass on a third); every gradient equals, bit for bit, the same
+    backward on the caller's stream alone, over two steps (the second
+    accumulating)."""
+    if name == "d4":
+        cfg = gi.preset("d4")
+    else:
+        cfg = small_bf16(batch=16, seq_len=256)
+    if name == "small_extras":
         cfg.update(resid_lambdas=1, smear=1, backout_layer=0)
     n = O.param_count(cfg)
     w, bits = with_extras(cfg, *gi.make_params(cfg, n))
