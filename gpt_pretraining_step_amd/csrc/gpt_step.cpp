@@ -180,7 +180,11 @@ struct Plan {
   int64_t N, chunk;
   size_t cs, x, hf, rf, ell, lse_z, loss, flag, badtok, logits, dz, evacc;
   bool fused_ce;         // lm_head + cross-entropy fused (no fp32 logits)
-  size_t ce_stats, ce_zt;
+  // train, fused: the lm_head's input gradient is taken from e directly and
+  // the softmax gradient for its weight gradient formed off the critical
+  // path (into dzs); otherwise it is formed in place over e in the forward
+  bool ce_bwd;
+  size_t ce_stats, ce_zt, dzs;
   std::vector<LayerBufs> layers;     // train: one per layer; eval: one shared
   // model extras: smear input and gates, the blocks' start x0, the stream
   // before each block's mix (train, blocks >= 1), the kept backout stream;
@@ -224,6 +228,8 @@ Plan make_plan(const Model& m, int mode) {
   p.ce_stats = p.fused_ce ? take(gk::lm_ce_stats_bytes(N, m.V)) : 0;
   p.ce_zt = p.fused_ce ? take(N * 4) : 0;
   p.dz = mode == GPT_MODE_TRAIN ? take((size_t)N * m.V * es) : 0;
+  p.ce_bwd = p.fused_ce && mode == GPT_MODE_TRAIN && gk::lm_ce_bwd_ok(N, m.V, m.D);
+  p.dzs = p.ce_bwd ? take((size_t)N * m.V * 2) : 0;
   const bool train = mode == GPT_MODE_TRAIN;
   const size_t xbytes = (size_t)N * m.D * es;
   p.xe = m.smear ? take(xbytes) : 0;
@@ -402,15 +408,16 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
   float* logits = at<float>(ws, p.logits);
   const float inv_n = 1.0f / (float)N;
   if (p.fused_ce) {
-    // e = exp(logit - tile max) lands where the softmax gradient goes and
-    // is rescaled there in place; EVAL keeps only the per-tile statistics
-    void* dz = mode == GPT_MODE_TRAIN ? at<void>(ws, p.dz) : nullptr;
+    // TRAIN keeps e = exp(logit - tile max) for the backward (rescaled in
+    // place into the softmax gradient here only when the backward cannot
+    // take e as it is); EVAL keeps only the per-tile statistics
+    void* e = mode == GPT_MODE_TRAIN ? at<void>(ws, p.dz) : nullptr;
     float* stats = at<float>(ws, p.ce_stats);
     float* zt = at<float>(ws, p.ce_zt);
-    HIP_TRY(gk::lm_ce_gemm(hf, N, m.D, elem(params, pl.wlm, es), m.V, dz, stats, zt, tokens, m.T,
+    HIP_TRY(gk::lm_ce_gemm(hf, N, m.D, elem(params, pl.wlm, es), m.V, e, stats, zt, tokens, m.T,
                            0, s));
     HIP_TRY(gk::ce_fix(stats, zt, N, m.V, tokens, m.T, 0, at<float>(ws, p.ell),
-                       at<float>(ws, p.lse_z), dz, inv_n, s));
+                       at<float>(ws, p.lse_z), e, p.ce_bwd ? nullptr : e, inv_n, s));
   } else {
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
     const int64_t nr = N - r0 < p.chunk ? N - r0 : p.chunk;
@@ -530,12 +537,28 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
   void* dxmid = m.bo >= 0 ? at<void>(ws, p.dxmid) : nullptr;
   // w starts after the token sort, the table clears and the forward
   HIP_TRY(fork(EV_START));
-  // lm_head
-  gk::GemmDesc g{gk::OP_TN, m.V, m.D, N, dz, m.V, hf, m.D, grads + pl.wlm, m.D, wepi, nullptr};
+  // lm_head.  With ce_bwd, dz holds e = exp(logit - m_t): the softmax
+  // gradient for the weight gradient is formed from it on w, while the
+  // input gradient's product reads e itself on s
+  const float inv_n = 1.0f / (float)N;
+  const void* dzw = dz;
+  if (p.ce_bwd) {
+    void* dzs = at<void>(ws, p.dzs);
+    HIP_TRY(gk::ce_fix(at<float>(ws, p.ce_stats), nullptr, N, m.V, tokens, m.T, 0, nullptr,
+                       nullptr, dz, dzs, inv_n, w));
+    dzw = dzs;
+  }
+  gk::GemmDesc g{gk::OP_TN, m.V, m.D, N, dzw, m.V, hf, m.D, grads + pl.wlm, m.D, wepi, nullptr};
   HIP_TRY(gk::gemm(g, dt, w));
-  g = gk::GemmDesc{gk::OP_NN, N, m.D, m.V, dz, m.V, elem(params, pl.wlm, es), m.D, dh, m.D,
-                   gk::E_STORE, nullptr};
-  HIP_TRY(gk::gemm(g, dt, s));
+  if (p.ce_bwd) {
+    HIP_TRY(gk::lm_ce_bwd_gemm(dz, N, m.V, elem(params, pl.wlm, es), m.D, dh,
+                               at<float>(ws, p.ce_stats), at<float>(ws, p.lse_z), tokens, m.T, 0,
+                               inv_n, s));
+  } else {
+    g = gk::GemmDesc{gk::OP_NN, N, m.D, m.V, dz, m.V, elem(params, pl.wlm, es), m.D, dh, m.D,
+                     gk::E_STORE, nullptr};
+    HIP_TRY(gk::gemm(g, dt, s));
+  }
   HIP_TRY(gk::rmsnorm_bwd(dh, hf, at<float>(ws, p.rf), nullptr, dx, N, m.D, nullptr, nullptr, 0,
                           0, dt, s));
   // backout x -= lambda_b x_kept: dx passes through, the kept stream's
@@ -1501,7 +1524,7 @@ int gpt_k_lm_ce(const void* h, const void* w, const int32_t* tgt, int64_t rows, 
   float* stats = (float*)scratch;
   float* zt = (float*)((char*)scratch + pad256(gk::lm_ce_stats_bytes(rows, V)));
   KERNEL_TRY(gk::lm_ce_gemm(h, rows, D, w, V, dz, stats, zt, tgt, 1, 1, s));
-  KERNEL_TRY(gk::ce_fix(stats, zt, rows, V, tgt, 1, 1, ell, lse, dz, grad_scale, s));
+  KERNEL_TRY(gk::ce_fix(stats, zt, rows, V, tgt, 1, 1, ell, lse, dz, dz, grad_scale, s));
   return GPT_OK;
 }
 

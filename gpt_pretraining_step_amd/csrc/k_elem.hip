@@ -998,15 +998,16 @@ generic:
 }
 
 // Fused lm_head + cross-entropy, second half: one 512-thread block per row.
-// lse from the row's per-tile (m_t, s_t) in a fixed order, the loss, then
-// the softmax gradient from the stored fp16 e = exp(logit - m_t), rescaled
-// by exp(m_t - lse) and written back as bf16 over the same bytes.
+// lse from the row's per-tile (m_t, s_t) in a fixed order, the loss, and
+// (with dz) the softmax gradient from the stored bf16 e = exp(logit - m_t),
+// rescaled by exp(m_t - lse) into dz (which may be e itself: every thread
+// reads its runs before writing them).
 __global__ __launch_bounds__(512) void k_ce_fix(const float2* __restrict__ stats, int ntn,
                                                 const float* __restrict__ zt, int V,
                                                 const int32_t* __restrict__ tok, int T,
                                                 int direct, float* __restrict__ ell,
-                                                float* __restrict__ lse, uint16_t* dz,
-                                                float scale) {
+                                                float* __restrict__ lse, const uint16_t* e,
+                                                uint16_t* dz, float scale) {
   __shared__ float ct[1024];
   __shared__ float red[8];
   const int64_t row = blockIdx.x;
@@ -1033,7 +1034,7 @@ __global__ __launch_bounds__(512) void k_ce_fix(const float2* __restrict__ stats
 #pragma unroll
   for (int k = 0; k < 8; ++k) S += red[k];
   const float L = M + logf(S);
-  if (threadIdx.x == 0) {
+  if (ell && threadIdx.x == 0) {
     ell[row] = L - zt[row];
     lse[row] = L;
   }
@@ -1041,8 +1042,8 @@ __global__ __launch_bounds__(512) void k_ce_fix(const float2* __restrict__ stats
   for (int t = threadIdx.x; t < ntn; t += 512) ct[t] = expf(st[t].x - L) * scale;
   __syncthreads();
   const int tgt = direct ? tok[row] : tok[(row / T) * (T + 1) + row % T + 1];
+  const uint4* pe = (const uint4*)(e + row * (int64_t)V);
   uint4* p = (uint4*)(dz + row * (int64_t)V);
-  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
   // four 16-byte runs per thread in flight before the first store (the
   // stores would otherwise hold every next load behind them)
   constexpr int U = 4;
@@ -1053,7 +1054,7 @@ __global__ __launch_bounds__(512) void k_ce_fix(const float2* __restrict__ stats
     for (int i = 0; i < U; ++i)
       if (k0 + 512 * i < n8) {
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 v = __builtin_nontemporal_load((const u32x4*)(p + k0 + 512 * i));
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)(pe + k0 + 512 * i));
         u[i] = make_uint4(v[0], v[1], v[2], v[3]);
       }
 #pragma unroll
@@ -1064,10 +1065,9 @@ __global__ __launch_bounds__(512) void k_ce_fix(const float2* __restrict__ stats
       const uint32_t* wu = (const uint32_t*)&u[i];
       float f[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const h2_t h = __builtin_bit_cast(h2_t, wu[e]);
-        f[2 * e] = (float)h[0] * c;
-        f[2 * e + 1] = (float)h[1] * c;
+      for (int q = 0; q < 4; ++q) {
+        f[2 * q] = __uint_as_float(wu[q] << 16) * c;
+        f[2 * q + 1] = __uint_as_float(wu[q] & 0xFFFF0000u) * c;
       }
       if ((tgt >> 3) == k) f[tgt & 7] -= scale;
       uint4 o;
@@ -1081,15 +1081,19 @@ __global__ __launch_bounds__(512) void k_ce_fix(const float2* __restrict__ stats
 }
 
 hipError_t ce_fix(const float* stats, const float* zt, int64_t rows, int V, const int32_t* tok,
-                  int tgt_T, int tgt_direct, float* ell, float* lse, void* dz, float grad_scale,
-                  hipStream_t s) {
+                  int tgt_T, int tgt_direct, float* ell, float* lse, const void* e, void* dz,
+                  float grad_scale, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (V % 256 || V / 256 > 1024) return hipErrorInvalidValue;
+  if (dz && !e) return hipErrorInvalidValue;
+  if ((ell == nullptr) != (lse == nullptr)) return hipErrorInvalidValue;
   const int ntn = V / 256;
-  // stats and target logits read once; e read and the gradient written once
-  const Work w(0.0, (double)rows * (8.0 * ntn + 12.0) + (dz ? 4.0 * (double)rows * V : 0.0));
+  // stats read once (target logits with ell); e read and the gradient
+  // written once
+  const Work w(0.0, (double)rows * (8.0 * ntn + (ell ? 12.0 : 0.0)) +
+                        (dz ? 4.0 * (double)rows * V : 0.0));
   GK_LAUNCH(w, k_ce_fix, dim3((unsigned)rows), dim3(512), 0, s, (const float2*)stats, ntn, zt, V,
-            tok, tgt_T, tgt_direct, ell, lse, (uint16_t*)dz, grad_scale);
+            tok, tgt_T, tgt_direct, ell, lse, (const uint16_t*)e, (uint16_t*)dz, grad_scale);
   return hipGetLastError();
 }
 

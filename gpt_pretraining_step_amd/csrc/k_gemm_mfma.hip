@@ -288,6 +288,9 @@ struct TileMap {
   const int32_t* ce_tok = nullptr;
   int ce_T = 1;
   int ce_direct = 0;
+  // E_CEB only: per-row lse, and the gradient's scale (1 / tokens)
+  const float* ce_lse = nullptr;
+  float ce_scale = 0.f;
   // E_QKNORM only
   const float2* qk_cs = nullptr;
   float* qk_rq = nullptr;
@@ -327,13 +330,6 @@ __device__ __forceinline__ void tile_of(const TileMap& tm, int t, int& tile_m, i
     tile_m = first_m + (t % (GM * tm.tiles_n)) % gsize;
     tile_n = (t % (GM * tm.tiles_n)) / gsize;
   }
-}
-
-// two floats as packed fp16 (round to nearest even)
-__device__ __forceinline__ uint32_t pack2h(float a, float b) {
-  typedef float f2_t __attribute__((ext_vector_type(2)));
-  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, h2_t));
 }
 
 template <int BM, int BN, bool TA, bool TB, int EPI>
@@ -724,7 +720,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
 #pragma unroll
     for (int j = 0; j < TNJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const bf16* st) {
+  // E_CEB: per-row factors applied to the accumulator just before its first
+  // MFMA of a slice (scaled = true), so the multiplies interleave with the
+  // matrix work instead of draining it
+  float cb_f[TMI];
+  auto compute = [&](const bf16* st, auto scaled) {
     const bf16* As = st;
     const bf16* Bs = st + BM * 64;
 #pragma unroll
@@ -735,38 +735,95 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
 #pragma unroll
       for (int i = 0; i < TMI; ++i) a[i] = frag<BM, TA>(As, wm + 16 * i, kk, lane);
 #pragma unroll
-      for (int i = 0; i < TMI; ++i)
+      for (int i = 0; i < TMI; ++i) {
+        if constexpr (decltype(scaled)::value) {
+          if (kk == 0) {
+            // row group i in place, then its MFMAs: the order is pinned so
+            // the scaled copies never coexist with the originals
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < TNJ; ++j) acc[i][j] *= cb_f[i];
+          }
+        }
 #pragma unroll
         for (int j = 0; j < TNJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+      }
     }
   };
+  const std::false_type plain;
 
-  // two stages in two arrays, visited in a loop unrolled by two so that
-  // every LDS access names its stage statically (the loads in flight into
-  // one stage then never hold up reads of the other)
+  // E_CEB (A = e = exp(logit - m_t), K = the vocabulary): the accumulator
+  // of each row is kept in units of exp(m'_t) for the 256-column tile t
+  // being summed, m'_t = max(m_t, lse - 40), and multiplied by exp(m'_(t-1)
+  // - m'_t) when a tile starts.  Every m' lies in [lse - 40, lse], so the
+  // factors stay within e^(+-40); a tile whose max is more than 40 below
+  // lse counts as if it were 40 below, a change far under bf16 resolution
+  // (its true weight is below e^-40).  The next tile's m_t is fetched a
+  // tile ahead.
+  float cb_lse[TMI], cb_m[TMI], cb_next[TMI];
+  const int ntv = (int)(K >> 8);
+  const int64_t mrow = m0 + wm + (lane & 15);
+  auto cb_stat = [&](int i, int t) {       // m_t of row i's tile t
+    return tm.ce_stats[2 * (min(mrow + 16 * i, M - 1) * ntv + t)];
+  };
+  if constexpr (EPI == E_CEB) {
+#pragma unroll
+    for (int i = 0; i < TMI; ++i) {
+      cb_lse[i] = tm.ce_lse[min(mrow + 16 * i, M - 1)];
+      cb_next[i] = cb_stat(i, 0);
+      cb_m[i] = fmaxf(cb_next[i], cb_lse[i] - 40.f);   // the first factor is 1
+    }
+  }
+
+  // two stages in two arrays, visited in a loop unrolled by two (by four
+  // for E_CEB, one 256-wide vocabulary tile per trip) so that every LDS
+  // access names its stage statically (the loads in flight into one stage
+  // then never hold up reads of the other)
   const int nsl = (int)((kend - kbeg) / BK);
   pa.issue(kbeg, st0, wave);
   pb.issue(kbeg, st0 + BM * 64, wave);
-  int it = 0;
-  for (; it + 2 <= nsl; it += 2) {
+  auto next = [&](int it, bf16* st) {      // wait for slice it - 1, fetch slice it
     dma_wait();
     __syncthreads();
-    pa.issue(kbeg + (int64_t)(it + 1) * BK, st1, wave);
-    pb.issue(kbeg + (int64_t)(it + 1) * BK, st1 + BM * 64, wave);
-    compute(st0);
-    dma_wait();
-    __syncthreads();
-    if (it + 2 < nsl) {
-      pa.issue(kbeg + (int64_t)(it + 2) * BK, st0, wave);
-      pb.issue(kbeg + (int64_t)(it + 2) * BK, st0 + BM * 64, wave);
+    if (it < nsl) {
+      pa.issue(kbeg + (int64_t)it * BK, st, wave);
+      pb.issue(kbeg + (int64_t)it * BK, st + BM * 64, wave);
     }
-    compute(st1);
-  }
-  if (it < nsl) {
-    dma_wait();
-    __syncthreads();
-    compute(st0);
+  };
+  int it = 0;
+  if constexpr (EPI == E_CEB) {
+    // K = V, a multiple of 256: nsl is a multiple of 4
+    for (; it < nsl; it += 4) {
+      next(it + 1, st1);
+      const int t = it >> 2;
+#pragma unroll
+      for (int i = 0; i < TMI; ++i) {
+        const float mt = fmaxf(cb_next[i], cb_lse[i] - 40.f);
+        cb_f[i] = __builtin_amdgcn_exp2f((cb_m[i] - mt) * 1.4426950408889634f);
+        cb_m[i] = mt;
+        if (t + 1 < ntv) cb_next[i] = cb_stat(i, t + 1);
+      }
+      compute(st0, std::true_type());
+      next(it + 2, st0);
+      compute(st1, plain);
+      next(it + 3, st1);
+      compute(st0, plain);
+      next(it + 4, st0);
+      compute(st1, plain);
+    }
+  } else {
+    for (; it + 2 <= nsl; it += 2) {
+      next(it + 1, st1);
+      compute(st0, plain);
+      next(it + 2, st0);
+      compute(st1, plain);
+    }
+    if (it < nsl) {
+      dma_wait();
+      __syncthreads();
+      compute(st0, plain);
+    }
   }
 
   const int cq = (lane >> 4) * 4, lr = lane & 15;
@@ -774,7 +831,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
     // Fused lm_head + cross-entropy, first half (the tile is 256 x 256 and
     // every column is a valid vocabulary entry): per row of the tile, the
     // max m of its 256 logits and s = sum exp(logit - m) in fp32, e = exp(
-    // logit - m) as fp16 (when C is given), and the target's logit.  The
+    // logit - m) as bf16 (when C is given), and the target's logit.  The
     // two waves sharing a row combine through LDS (the stages are free).
     const int ntn = tm.tiles_n;
     int tg[TMI];
@@ -849,10 +906,38 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
         for (int j = 0; j < TNJ; ++j) {
           const int64_t n = n0 + wn + 16 * j + cq;
           uint2 u;
-          u.x = pack2h(acc[i][j][0], acc[i][j][1]);
-          u.y = pack2h(acc[i][j][2], acc[i][j][3]);
+          u.x = pack2bf(acc[i][j][0], acc[i][j][1]);
+          u.y = pack2bf(acc[i][j][2], acc[i][j][3]);
           *(uint2*)((uint16_t*)C + m * ldc + n) = u;
         }
+      }
+    }
+    return;
+  }
+  if constexpr (EPI == E_CEB) {
+    // dh = (softmax - onehot(target)) grad_scale times Wlm: the accumulator
+    // (units exp(m'_last)) times exp(m'_last - lse) grad_scale, minus the
+    // target's row of Wlm (B) times grad_scale
+    const float sc = tm.ce_scale;
+#pragma unroll
+    for (int i = 0; i < TMI; ++i) {
+      const int64_t m = m0 + wm + 16 * i + lr;
+      if (m >= M) continue;
+      const float f = __builtin_amdgcn_exp2f((cb_m[i] - cb_lse[i]) * 1.4426950408889634f) * sc;
+      const int tg = tm.ce_direct ? tm.ce_tok[m]
+                                  : tm.ce_tok[(m / tm.ce_T) * (tm.ce_T + 1) + m % tm.ce_T + 1];
+      const bf16* wrow = B + (int64_t)tg * ldb;
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j) {
+        const int64_t n = n0 + wn + 16 * j + cq;
+        if (n >= N) continue;
+        const uint2 wv = *(const uint2*)(wrow + n);
+        uint2 o;
+        o.x = pack2bf(fmaf(acc[i][j][0], f, -sc * __uint_as_float(wv.x << 16)),
+                      fmaf(acc[i][j][1], f, -sc * __uint_as_float(wv.x & 0xFFFF0000u)));
+        o.y = pack2bf(fmaf(acc[i][j][2], f, -sc * __uint_as_float(wv.y << 16)),
+                      fmaf(acc[i][j][3], f, -sc * __uint_as_float(wv.y & 0xFFFF0000u)));
+        *(uint2*)((bf16*)C + m * ldc + n) = o;
       }
     }
     return;
@@ -1349,9 +1434,14 @@ bool lm_ce_fused_ok(int64_t rows, int V, int D) {
          2.0 * rows * D < 4294967295.0 && 2.0 * V * D < 4294967295.0;
 }
 
+// e [rows, V] addressable with 32-bit buffer offsets
+bool lm_ce_bwd_ok(int64_t rows, int V, int D) {
+  return lm_ce_fused_ok(rows, V, D) && 2.0 * rows * V < 4294967295.0;
+}
+
 size_t lm_ce_stats_bytes(int64_t rows, int V) { return (size_t)rows * (V / 256) * 8; }
 
-hipError_t lm_ce_gemm(const void* hf, int64_t rows, int D, const void* wlm, int V, void* e16,
+hipError_t lm_ce_gemm(const void* hf, int64_t rows, int D, const void* wlm, int V, void* e,
                       float* stats, float* zt, const int32_t* tok, int tgt_T, int tgt_direct,
                       hipStream_t s) {
   if (!lm_ce_fused_ok(rows, V, D)) return hipErrorInvalidValue;
@@ -1370,11 +1460,40 @@ hipError_t lm_ce_gemm(const void* hf, int64_t rows, int D, const void* wlm, int 
   // 2 rows V D flops; hf and Wlm read once, e written (2 bytes), stats and
   // target logits written
   const double mn = (double)rows * V;
-  const Work w(2.0 * mn * D, 2.0 * ((double)rows * D + (double)V * D) + (e16 ? 2.0 * mn : 0.0) +
+  const Work w(2.0 * mn * D, 2.0 * ((double)rows * D + (double)V * D) + (e ? 2.0 * mn : 0.0) +
                                  8.0 * rows * (V / 256) + 4.0 * rows);
   GK_LAUNCH(w, (k_gemm_dma<256, 256, false, false, E_CE>), dim3(grid), dim3(512), 0, s, rows,
             (int64_t)V, (int64_t)D, (const bf16*)hf, (int64_t)D, (const bf16*)wlm, (int64_t)D,
-            e16, (int64_t)V, nullptr, tm, nullptr);
+            e, (int64_t)V, nullptr, tm, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t lm_ce_bwd_gemm(const void* e, int64_t rows, int V, const void* wlm, int D, void* dh,
+                          const float* stats, const float* lse, const int32_t* tok, int tgt_T,
+                          int tgt_direct, float grad_scale, hipStream_t s) {
+  if (!lm_ce_bwd_ok(rows, V, D)) return hipErrorInvalidValue;
+  // 256 x 192 tiles whatever D is (the 256-wide tile's extra per-row state
+  // would not fit its registers); columns past D are dropped
+  TileMap tm;
+  tm.tiles_m = (int)cdiv(rows, 256);
+  tm.tiles_n = (int)cdiv(D, 192);
+  tm.splits = 1;
+  tm.k_per_split = V;
+  tm.ce_stats = (float*)stats;
+  tm.ce_tok = tok;
+  tm.ce_T = tgt_T;
+  tm.ce_direct = tgt_direct;
+  tm.ce_lse = lse;
+  tm.ce_scale = grad_scale;
+  const int nb = tm.tiles_m * tm.tiles_n;
+  const int grid = ((nb + 7) / 8) * 8;
+  // 2 rows D V flops; e and Wlm read once, dh written, the stats' maxima,
+  // lse, the targets and their Wlm rows read
+  const Work w(2.0 * rows * D * V, 2.0 * ((double)rows * V + (double)V * D + 2.0 * rows * D) +
+                                       4.0 * rows * (V / 256 + 2));
+  GK_LAUNCH(w, (k_gemm_dma<256, 192, false, true, E_CEB>), dim3(grid), dim3(512), 0, s, rows,
+            (int64_t)D, (int64_t)V, (const bf16*)e, (int64_t)V, (const bf16*)wlm, (int64_t)D, dh,
+            (int64_t)D, nullptr, tm, nullptr);
   return hipGetLastError();
 }
 

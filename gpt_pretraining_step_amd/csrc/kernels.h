@@ -10,7 +10,8 @@ enum DType { F32 = 0, BF16 = 1 };
 enum GemmOp { OP_NT = 0, OP_NN = 1, OP_TN = 2 };
 enum Epi { E_STORE = 0, E_RESADD, E_RELU2, E_DRELU2, E_F32, E_F32_ACC,
            E_CE,       // lm_ce_gemm only
-           E_QKNORM }; // qkv_gemm_rope_norm only
+           E_QKNORM,   // qkv_gemm_rope_norm only
+           E_CEB };    // lm_ce_bwd_gemm only
 
 // ---- elementwise / reductions -------------------------------------------
 hipError_t fill_zero(void* p, int64_t bytes, hipStream_t s);
@@ -167,19 +168,30 @@ hipError_t qkv_gemm_rope_norm(const void* h, int64_t rows, int D, const void* wq
 // direct-to-LDS GEMM takes).  lm_ce_gemm: logits = hf[rows, D] Wlm[V, D]^T,
 // never stored as such; per row and 256-column tile t the max m_t of the
 // logits and s_t = sum exp(logit - m_t) go to stats[row * (V / 256) + t],
-// the target's logit to zt[row], and (if e16) e = exp(logit - m_t) as fp16
-// to e16[row * V + col].  ce_fix: lse = max_t m_t + log(sum_t s_t
-// exp(m_t - max)), ell = lse - zt, and (if dz) dz = (e exp(m_t - lse) -
-// onehot) * grad_scale as bf16, in place over e16.  Targets as in ce_rows.
+// the target's logit to zt[row], and (if e) e = exp(logit - m_t) as bf16 to
+// e[row * V + col].  ce_fix: lse = max_t m_t + log(sum_t s_t exp(m_t -
+// max)); if ell, ell = lse - zt and lse go out; if dz, dz = (e exp(m_t -
+// lse) - onehot) * grad_scale as bf16 (dz may be e itself).  Targets as in
+// ce_rows.
 bool lm_ce_fused_ok(int64_t rows, int V, int D);
 size_t lm_ce_stats_bytes(int64_t rows, int V);
 // (tgt_direct: the target of row n is tok[n] instead)
-hipError_t lm_ce_gemm(const void* hf, int64_t rows, int D, const void* wlm, int V, void* e16,
+hipError_t lm_ce_gemm(const void* hf, int64_t rows, int D, const void* wlm, int V, void* e,
                       float* stats, float* zt, const int32_t* tok, int tgt_T, int tgt_direct,
                       hipStream_t s);
 hipError_t ce_fix(const float* stats, const float* zt, int64_t rows, int V, const int32_t* tok,
-                  int tgt_T, int tgt_direct, float* ell, float* lse, void* dz, float grad_scale,
-                  hipStream_t s);
+                  int tgt_T, int tgt_direct, float* ell, float* lse, const void* e, void* dz,
+                  float grad_scale, hipStream_t s);
+// The lm_head's input gradient straight from lm_ce_gemm's e:
+// dh[rows, D] = dz Wlm with dz = (e exp(m_t - lse) - onehot) * grad_scale,
+// without forming dz.  The product runs over the vocabulary in 256-column
+// tiles with the accumulator kept in units of the current tile's exp(m_t)
+// (rescaled at each tile boundary), the final scale and the target's row of
+// Wlm applied in the epilogue.
+bool lm_ce_bwd_ok(int64_t rows, int V, int D);
+hipError_t lm_ce_bwd_gemm(const void* e, int64_t rows, int V, const void* wlm, int D, void* dh,
+                          const float* stats, const float* lse, const int32_t* tok, int tgt_T,
+                          int tgt_direct, float grad_scale, hipStream_t s);
 // FP8 linear layers with tensor-wise scaling.  fp8_cast: q = fp8(clamp(x s,
 // +-fmax)), s = fmax / max(max|x|, 1e-12), x [rows, cols] (cols % 16 == 0;
 // rows % 16 == 0 when qt is given), row-major into q and/or transposed into

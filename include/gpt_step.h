@@ -155,9 +155,12 @@ int gpt_validate_config(const gpt_config* cfg);
  *            forward saves what the backward needs in it; ws[] also holds the
  *            per-token losses (gpt_ws_offset(GPT_WS_ELL)).
  *   loss_dev : device float, receives mean loss over the B*T targets.
- * Softmax and cross-entropy are fp32; logits are fp32.  The softmax gradient
- * (softmax - onehot)/(B T) is formed here too and kept in ws for the
- * backward.  A non-finite loss sets the int32 flag at GPT_WS_NONFINITE.
+ * Softmax and cross-entropy are fp32; logits are fp32.  What the backward
+ * needs of the softmax gradient (softmax - onehot)/(B T) stays in ws: for
+ * bf16 models with V a multiple of 256, exp(logit - max) per 256-column
+ * tile (bf16) with each tile's max and the row's lse, from which the
+ * backward forms the gradient itself; otherwise the gradient (dtype).  A
+ * non-finite loss sets the int32 flag at GPT_WS_NONFINITE.
  */
 int gpt_step_fwd(const gpt_config* cfg, const void* params,
                  const int32_t* tokens, void* ws, size_t ws_bytes,
@@ -572,7 +575,7 @@ int gpt_k_ve_bwd(const int32_t* tokens, int32_t B, int32_t T,
 /* Fused lm_head + softmax cross-entropy (bf16): logits = h [rows, D] times
  * w [V, D]^T are formed in fp32 inside the product and never stored; per
  * row and 256-column tile the product keeps the max and sum of exp(logit -
- * max) and writes exp(logit - max) as fp16 into dz, which a second pass
+ * max) and writes exp(logit - max) as bf16 into dz, which a second pass
  * rescales in place (the same steps as the training step's loss).
  *   tgt[rows]: target ids in [0, V).  ell[row] = lse - logit[tgt[row]],
  *   lse[row] (fp32).  dz (may be null): [rows, V] bf16, receives

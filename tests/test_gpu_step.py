@@ -156,10 +156,56 @@ def test_eval_bpb_matches_oracle(name, n_rows):
     assert abs(got[0] - nats) / nats < 1e-3
 
 
-def test_uniform_logits_on_gpu():
+def _wlm_offset(cfg):
+    off = 0
+    for name, shape in O.param_layout(cfg):
+        if name == "wlm":
+            return off
+        off += int(np.prod(shape))
+    raise KeyError("wlm")
+
+
+def test_step_far_apart_vocab_tiles():
+    """lm_head rows of the first 256-entry vocabulary tile near +u and of the
+    second near -u, |u| = 30: in about half the rows one tile's logits lie
+    more than 40 below the other's, where the fused lm_head backward weighs
+    the low tile at e^-40 instead of its (smaller) true weight.  Loss, losses
+    and every gradient still match the oracle."""
+    cfg = small_bf16(vocab=512)
+    n = O.param_count(cfg)
+    w, _ = with_extras(cfg, *gi.make_params(cfg, n))
+    V, D = cfg["vocab"], cfg["d_model"]
+    rng = np.random.default_rng(11)
+    u = rng.standard_normal(D)
+    u *= 30.0 / np.linalg.norm(u)
+    wl = 0.02 * rng.standard_normal((V, D))
+    wl[:256] += u
+    wl[256:] -= u
+    off = _wlm_offset(cfg)
+    w = w.copy()
+    w[off:off + V * D] = wl.reshape(-1)
+    w, bits = with_extras(cfg, w, gi.bf16_bits_from_f32(w))
+    tok = gi.make_tokens(cfg)
+    s = Session(cfg)
+    s.set_params(w, bits)
+    s.set_tokens(tok)
+    s.fwd()
+    s.bwd()
+    torch.cuda.synchronize()
+    N = tok.shape[0] * (tok.shape[1] - 1)
+    ell = to_np(s.ws_f32(G.WS_ELL, N))
+    say("far-apart tiles: loss", float(s.loss.item()), "max loss", ell.max())
+    assert ell.max() > 40.0          # some targets sit in the suppressed tile
+    flag = int(s.ws[G.ws_offset(s.cfg, G.WS_NONFINITE):][:4].view(torch.int32).item())
+    compare(cfg, w, tok, float(s.loss.item()), ell, to_np(s.grads), flag)
+
+
+@pytest.mark.parametrize("vocab", [500, 512])
+def test_uniform_logits_on_gpu(vocab):
     """With W_lm = 0 the loss is ln V exactly and every gradient but the
-    lm_head's is exactly zero (closed form)."""
-    cfg = small_bf16()
+    lm_head's is exactly zero (closed form); V = 512 takes the fused
+    lm_head / cross-entropy path, V = 500 the fp32-logits one."""
+    cfg = small_bf16(vocab=vocab)
     n = O.param_count(cfg)
     w, bits = gi.make_params(cfg, n)
     off = O.param_count(cfg) - cfg["vocab"] * cfg["d_model"]
@@ -176,8 +222,9 @@ def test_uniform_logits_on_gpu():
     assert np.abs(g[off:]).max() > 0
 
 
-def test_nonfinite_flag():
-    cfg = small_bf16()
+@pytest.mark.parametrize("vocab", [500, 512])
+def test_nonfinite_flag(vocab):
+    cfg = small_bf16(vocab=vocab)
     n = O.param_count(cfg)
     w, bits = gi.make_params(cfg, n)
     bits = bits.copy()
