@@ -53,4 +53,14 @@ __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t lds, uint32_t voff)
 // by the compiler); follow with a barrier before other waves read the data.
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait until at most N of this wave's vector memory loads are outstanding:
+// loads complete in issue order, so everything but the N issued last has
+// landed.  Only for loops whose VMEM instructions are all buffer-to-LDS
+// loads this code issues (any other load or store in flight would be
+// counted too).
+template <int N>
+__device__ __forceinline__ void dma_wait_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 }  // namespace gk

@@ -684,8 +684,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
                                                      TileMap tm, float* partial) {
   constexpr int WM = BM / 4, WN = BN / 2;
   constexpr int TMI = WM / 16, TNJ = WN / 16;
-  __shared__ __attribute__((aligned(1024))) bf16 st0[(BM + BN) * 64];
-  __shared__ __attribute__((aligned(1024))) bf16 st1[(BM + BN) * 64];
+  // LDS: E_CEB keeps two stages of (A, B) tiles; every other product a
+  // ring of three A tiles and two B tiles (below)
+  constexpr int S0 = EPI == E_CEB ? (BM + BN) * 64 : (3 * BM + 2 * BN) * 64;
+  constexpr int S1 = EPI == E_CEB ? (BM + BN) * 64 : 512;
+  __shared__ __attribute__((aligned(1024))) bf16 st0[S0];
+  __shared__ __attribute__((aligned(1024))) bf16 st1[S1];
+  bf16* const lds = st0;
   if (blockIdx.y) {
     constexpr int ce = (EPI == E_F32 || EPI == E_F32_ACC) ? 4 : 2;
     A += blockIdx.y * tm.bs_a;
@@ -752,6 +757,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
     }
   };
   const std::false_type plain;
+  auto compute2 = [&](const bf16* As, const bf16* Bs) {
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      bf16x8_t a[TMI], b[TNJ];
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j) b[j] = frag<BN, TB>(Bs, wn + 16 * j, kk, lane);
+#pragma unroll
+      for (int i = 0; i < TMI; ++i) a[i] = frag<BM, TA>(As, wm + 16 * i, kk, lane);
+#pragma unroll
+      for (int i = 0; i < TMI; ++i)
+#pragma unroll
+        for (int j = 0; j < TNJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    }
+  };
 
   // E_CEB (A = e = exp(logit - m_t), K = the vocabulary): the accumulator
   // of each row is kept in units of exp(m'_t) for the 256-column tile t
@@ -776,24 +796,22 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
     }
   }
 
-  // two stages in two arrays, visited in a loop unrolled by two (by four
-  // for E_CEB, one 256-wide vocabulary tile per trip) so that every LDS
-  // access names its stage statically (the loads in flight into one stage
-  // then never hold up reads of the other)
   const int nsl = (int)((kend - kbeg) / BK);
-  pa.issue(kbeg, st0, wave);
-  pb.issue(kbeg, st0 + BM * 64, wave);
-  auto next = [&](int it, bf16* st) {      // wait for slice it - 1, fetch slice it
-    dma_wait();
-    __syncthreads();
-    if (it < nsl) {
-      pa.issue(kbeg + (int64_t)it * BK, st, wave);
-      pb.issue(kbeg + (int64_t)it * BK, st + BM * 64, wave);
-    }
-  };
   int it = 0;
   if constexpr (EPI == E_CEB) {
-    // K = V, a multiple of 256: nsl is a multiple of 4
+    // two stages in two arrays, visited in a loop unrolled by four (one
+    // 256-wide vocabulary tile per trip) so that every LDS access names its
+    // stage statically; K = V, a multiple of 256: nsl is a multiple of 4
+    pa.issue(kbeg, st0, wave);
+    pb.issue(kbeg, st0 + BM * 64, wave);
+    auto next = [&](int it, bf16* st) {    // wait for slice it - 1, fetch slice it
+      dma_wait();
+      __syncthreads();
+      if (it < nsl) {
+        pa.issue(kbeg + (int64_t)it * BK, st, wave);
+        pb.issue(kbeg + (int64_t)it * BK, st + BM * 64, wave);
+      }
+    };
     for (; it < nsl; it += 4) {
       next(it + 1, st1);
       const int t = it >> 2;
@@ -813,16 +831,29 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
       compute(st1, plain);
     }
   } else {
-    for (; it + 2 <= nsl; it += 2) {
-      next(it + 1, st1);
-      compute(st0, plain);
-      next(it + 2, st0);
-      compute(st1, plain);
-    }
-    if (it < nsl) {
-      dma_wait();
+    // A ring of three, B ring of two: A (the activations or gradients, the
+    // operand that streams from HBM) is fetched two slices ahead, B one.
+    // Per slice: wait until only A(s + 1) is in flight (loads land in issue
+    // order and A(s + 1) went out after B(s)), barrier (every wave is done
+    // with slice s - 1, whose A and B stages the next loads reuse), issue
+    // B(s + 1) then A(s + 2), multiply slice s.
+    bf16* const ra = lds;                    // A stages: ra + j BM 64
+    bf16* const rb = lds + 3 * BM * 64;      // B stages: rb + j BN 64
+    constexpr int NA = DmaPlan<BM, TA>::NB;  // A loads per wave and slice
+    pa.issue(kbeg, ra, wave);
+    pb.issue(kbeg, rb, wave);
+    if (nsl > 1) pa.issue(kbeg + BK, ra + BM * 64, wave);
+    int sa = 0, sb = 0;                      // stages of slice `it`
+    for (; it < nsl; ++it) {
+      if (it + 1 < nsl) dma_wait_n<NA>();
+      else dma_wait();
       __syncthreads();
-      compute(st0, plain);
+      const int sa2 = sa == 0 ? 2 : sa - 1;  // (it + 2) % 3
+      if (it + 1 < nsl) pb.issue(kbeg + (int64_t)(it + 1) * BK, rb + (sb ^ 1) * BN * 64, wave);
+      if (it + 2 < nsl) pa.issue(kbeg + (int64_t)(it + 2) * BK, ra + sa2 * BM * 64, wave);
+      compute2(ra + sa * BM * 64, rb + sb * BN * 64);
+      sa = sa == 2 ? 0 : sa + 1;
+      sb ^= 1;
     }
   }
 
@@ -843,7 +874,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
                              : tm.ce_tok[(m / tm.ce_T) * (tm.ce_T + 1) + m % tm.ce_T + 1];
     }
     __syncthreads();
-    float* red = (float*)st0;              // [0, 512): maxima, [512, 1024): sums
+    float* red = (float*)lds;              // [0, 512): maxima, [512, 1024): sums
     float mx[TMI];
 #pragma unroll
     for (int i = 0; i < TMI; ++i) {
