@@ -505,12 +505,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mfma_db(int64_t M, int64_t N, i
 }
 
 // ------------------------------------------------- direct-to-LDS variant
-// 8 waves (4 x 2, each (BM/4) x (BN/2)), two LDS stages filled straight from
-// global memory by global_load_lds_dwordx4: every load instruction moves one
-// contiguous 1 KB LDS block (lane i -> bytes 16i..16i+15), so the layout is
-// chosen through which global 16-byte chunk each lane fetches.  No staging
-// registers, no LDS store instructions, and the loads of slice s+1 stay in
-// flight while slice s is multiplied.
+// 8 waves (4 x 2, each (BM/4) x (BN/2)), LDS stages filled straight from
+// global memory by buffer_load_dwordx4 ... lds: every load instruction moves
+// one contiguous 1 KB LDS block (lane i -> bytes 16i..16i+15), so the layout
+// is chosen through which global 16-byte chunk each lane fetches.  No
+// staging registers and no LDS store instructions; A is fetched two K-slices
+// ahead (a ring of three stages), B one slice ahead (a ring of two), so the
+// loads of slices s+1 and s+2 stay in flight while slice s is multiplied.
 //
 // K-contiguous operand: LDS rows of 64 k (128 B, no padding), 16-byte chunk c
 // of row r stored at position c ^ ((r >> 1) & 7); a fragment read (16 rows,
