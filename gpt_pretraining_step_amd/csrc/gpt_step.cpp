@@ -496,6 +496,14 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
   // the model is small or the side stream is unavailable)
   SideStream* sd = m.dt == gk::BF16 && N >= 4096 && !m.one_stream ? side_stream() : nullptr;
   const hipStream_t w = sd ? sd->s : s;
+  // split-K scratch of a weight-gradient product [M_, N_].  Beside the main
+  // stream these products need not fill the chip alone, and every split adds
+  // partial-tile traffic: at most 4 splits there (d12 step: 33.56 ms against
+  // 33.75 ms with the standalone plan's 7-28; 2 splits 38.1, 3 33.8, 5 33.6,
+  // 6 33.9 ms, one box)
+  auto wsb = [&](int64_t M_, int64_t N_) {
+    return sd ? std::min(gscr_bytes, (size_t)4 * M_ * N_ * 4) : gscr_bytes;
+  };
   bool marked[EV_COUNT] = {};
   auto fork = [&](int e) -> hipError_t {       // w waits for s's work so far
     if (!sd) return hipSuccess;
@@ -579,7 +587,7 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
     // MLP
     HIP_TRY(fork(EV_DX1));                      // dx (the block output's gradient) ready
     g = gk::GemmDesc{gk::OP_TN, m.D, m.F, N, dx, m.D, a, m.F, grads + pl.wproj[l], m.F, wepi,
-                     nullptr, gscr, gscr_bytes};
+                     nullptr, gscr, wsb(m.D, m.F)};
     HIP_TRY(gk::gemm(g, dt, w));
     HIP_TRY(mark(EV_DX1_FREE));
     HIP_TRY(need(EV_DU_FREE));                  // the previous block's dW_fc has read du
@@ -597,7 +605,7 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
     HIP_TRY(gk::gemm(g, dt, s));
     HIP_TRY(fork(EV_DU));
     g = gk::GemmDesc{gk::OP_TN, m.F, m.D, N, du, m.F, h2, m.D, grads + pl.wfc[l], m.D, wepi,
-                     nullptr, gscr, gscr_bytes};
+                     nullptr, gscr, wsb(m.F, m.D)};
     HIP_TRY(gk::gemm(g, dt, w));
     HIP_TRY(mark(EV_DU_FREE));
     g = gk::GemmDesc{gk::OP_NN, N, m.D, m.F, du, m.F, elem(params, pl.wfc[l], es), m.D, dh, m.D,
@@ -608,7 +616,7 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
                             dt, s));
     // attention
     HIP_TRY(fork(EV_DX2));
-    g = gk::GemmDesc{gk::OP_TN, m.D, HD, N, dx, m.D, o, HD, grads + pl.wo[l], HD, wepi, nullptr, gscr, gscr_bytes};
+    g = gk::GemmDesc{gk::OP_TN, m.D, HD, N, dx, m.D, o, HD, grads + pl.wo[l], HD, wepi, nullptr, gscr, wsb(m.D, HD)};
     HIP_TRY(gk::gemm(g, dt, w));
     HIP_TRY(mark(EV_DX2_FREE));
     g = gk::GemmDesc{gk::OP_NN, N, HD, m.D, dx, m.D, elem(params, pl.wo[l], es), HD, dout, HD,
@@ -650,7 +658,7 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
       HIP_TRY(fork(EV_QKV));
     }
     g = gk::GemmDesc{gk::OP_TN, m.QKV, m.D, N, dqkv, m.QKV, h, m.D, grads + pl.wqkv[l], m.D,
-                     wepi, nullptr, gscr, gscr_bytes};
+                     wepi, nullptr, gscr, wsb(m.QKV, m.D)};
     HIP_TRY(gk::gemm(g, dt, w));
     HIP_TRY(mark(EV_QKV_FREE));
     g = gk::GemmDesc{gk::OP_NN, N, m.D, m.QKV, dqkv, m.QKV, elem(params, pl.wqkv[l], es), m.D,

@@ -91,7 +91,11 @@ enum { GPT_MODE_TRAIN = 0, GPT_MODE_EVAL = 1 };
  *     library-owned stream (one per host thread and device, default
  *     priority), forked from and joined back into the caller's stream with
  *     events, so the call still completes in the caller's stream order (and
- *     can be captured into a graph); results are bit for bit the same.
+ *     can be captured into a graph).  Beside the caller's stream the linear
+ *     layers' weight-gradient products split K at most 4 ways, so those
+ *     four gradients differ from the one-stream results by fp32 summation
+ *     order; every other result is bit for bit the same, and each mode is
+ *     deterministic.
  */
 typedef struct gpt_config {
   int32_t n_layer, d_model, n_head, n_kv_head, head_dim, vocab, seq_len, batch;

@@ -324,9 +324,11 @@ def test_token_check():
 def test_two_stream_backward_equals_one_stream(name):
     """From 4096 tokens the backward runs its weight-gradient products and
     table gradients on a second stream (and, at head_dim 128, the attention
-    dQ pass on a third); every gradient equals, bit for bit, the same
-    backward on the caller's stream alone, over two steps (the second
-    accumulating)."""
+    dQ pass on a third).  Over two steps (the second accumulating), every
+    gradient equals, bit for bit, the same backward on the caller's stream
+    alone, except the linear layers' weight gradients: beside the main
+    stream those products split K at most 4 ways (alone, as far as the plan
+    likes), so they agree up to the fp32 summation order of the splits."""
     if name == "d4":
         cfg = gi.preset("d4")
     else:
@@ -346,5 +348,10 @@ def test_two_stream_backward_equals_one_stream(name):
         s.fwd()
         s.bwd(accumulate=True)
         torch.cuda.synchronize()
-        out.append(s.grads.clone())
-    assert torch.equal(out[0], out[1])
+        out.append(to_np(s.grads))
+    a, b = grads_by_tensor(cfg, out[0]), grads_by_tensor(cfg, out[1])
+    for k in a:
+        if k.split(".")[-1] in ("wqkv", "wo", "wfc", "wproj"):
+            assert rel_err(a[k], b[k]) < 1e-6, k
+        else:
+            assert np.array_equal(a[k], b[k]), k
