@@ -445,10 +445,11 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
 // and kept; default priority.  Results are bit for bit those of one stream
 // (every kernel and its inputs are unchanged; only the overlap differs).
 enum { EV_START, EV_DX1, EV_DX1_FREE, EV_DU, EV_DU_FREE, EV_DX2, EV_DX2_FREE, EV_QKV,
-       EV_QKV_FREE, EV_END, EV_ATT_FORK, EV_ATT_JOIN, EV_COUNT };
+       EV_QKV_FREE, EV_END, EV_ATT_FORK, EV_ATT_JOIN, EV_ATT_JOIN4, EV_COUNT };
 struct SideStream {
   hipStream_t s = nullptr;
   hipStream_t s3 = nullptr;     // the attention backward's dQ pass
+  hipStream_t s4 = nullptr;     // and its dV pass
   hipEvent_t ev[EV_COUNT] = {};
   bool ready = false, failed = false;
 };
@@ -462,7 +463,8 @@ SideStream* side_stream() {
   if (ss.ready) return &ss;
   if (ss.failed) return nullptr;
   bool ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
-            hipStreamCreateWithFlags(&ss.s3, hipStreamNonBlocking) == hipSuccess;
+            hipStreamCreateWithFlags(&ss.s3, hipStreamNonBlocking) == hipSuccess &&
+            hipStreamCreateWithFlags(&ss.s4, hipStreamNonBlocking) == hipSuccess;
   for (int i = 0; ok && i < EV_COUNT; ++i)
     ok = hipEventCreateWithFlags(&ss.ev[i], hipEventDisableTiming) == hipSuccess;
   if (!ok) {
@@ -629,7 +631,9 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
     // backward of RoPE-then-QK-norm in their epilogues
     if (gk::attn_bwd_fuses_norm(m.T, m.H, m.Hkv, m.hd, dt)) {
       gk::Beside bes;
-      if (sd) bes = gk::Beside{sd->s3, sd->ev[EV_ATT_FORK], sd->ev[EV_ATT_JOIN]};
+      if (sd)
+        bes = gk::Beside{sd->s3, sd->ev[EV_ATT_FORK], sd->ev[EV_ATT_JOIN], sd->s4,
+                         sd->ev[EV_ATT_JOIN4]};
       HIP_TRY(gk::attn_bwd(qkv, o, at<float>(ws, b.lse), dout, dqkv, at<void>(ws, p.attn_scr),
                            m.B, m.T, m.H, m.Hkv, m.hd, m.window(l), dt, s, at<float>(ws, b.rq),
                            at<float>(ws, b.rk), cs, bes));

@@ -175,7 +175,8 @@ hipError_t attn_bwd(const void* qkv, const void* o, const float* lse, const void
   if (dt == BF16 && attn_mfma_bwd_supported(T, H, Hkv, hd)) {
     size_t dbytes = (((size_t)B * H * T * sizeof(float) + 255) / 256) * 256;
     return attn_mfma_bwd(qkv, o, lse, dout, dqkv, delta, (char*)scratch + dbytes, B, T, H, Hkv,
-                         hd, W, s, nrq, nrk, ncs, beside.s2, beside.fork, beside.join);
+                         hd, W, s, nrq, nrk, ncs, beside.s2, beside.fork, beside.join,
+                         beside.s4, beside.join4);
   }
   const int64_t rows = (int64_t)B * H * T;
   const int64_t krows = (int64_t)B * Hkv * T;

@@ -787,7 +787,8 @@ size_t attn_mfma_bwd_scratch_bytes(int, int, int, int) { return 0; }
 hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const void* dout,
                          void* dqkv, float* delta, void*, int B, int T, int H, int Hkv, int hd,
                          int W, hipStream_t s, const float* nrq, const float* nrk,
-                         const float* ncs, hipStream_t s2, hipEvent_t fork, hipEvent_t join) {
+                         const float* ncs, hipStream_t s2, hipEvent_t fork, hipEvent_t join,
+                         hipStream_t s4, hipEvent_t join4) {
   (void)hd;
   const bool fuse = nrq && nrk && ncs;
   const NormBwdArgs nb{nrq, nrk, (const float2*)ncs};
@@ -808,9 +809,12 @@ hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const
   // of dqkv and read only what Delta's pass and the forward left
   const bool two = s2 && fork && join;
   const hipStream_t sq = two ? s2 : s;
+  const bool four = two && s4 && join4;
+  const hipStream_t sv = four ? s4 : sq;
   if (two) {
     hipError_t e = hipEventRecord(fork, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(s2, fork, 0);
+    if (e == hipSuccess && four) e = hipStreamWaitEvent(s4, fork, 0);
     if (e != hipSuccess) return e;
   }
   // dK and dV in two passes (two waves per SIMD each; measured faster than
@@ -820,21 +824,24 @@ hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const
   const Work wv(2.0 * HD * pairs, qkvo + stats / 2 + tok * Hkv * HD * 2);
   const dim3 gq = xcd_grid((T + DQ_BQ - 1) / DQ_BQ, H * B);
 #define DKV_ARGS (const bf16*)qkv, (const bf16*)dout, lse, (const float*)delta, (bf16*)dqkv, B, T, H, Hkv, W, nb
-  // dQ then dV on the second stream, dK (the longest pass) on the caller's:
-  // 0.1 ms per d12 step against dK then dV on the caller's stream
+  // dK (the longest pass) on the caller's stream, dQ and dV beside it on
+  // streams of their own (or dV after dQ): 0.1 ms per d12 step each against
+  // dV after dK on the caller's stream, and against dV after dQ
   if (fuse) {
     GK_LAUNCH(wq, k_attn_bwd_dq<true>, gq, dim3(NW * 64), 0, sq, DKV_ARGS);
-    GK_LAUNCH(wv, (k_attn_bwd_dkv<2, 2, false>), gkv, dim3(NW * 64), 0, sq, DKV_ARGS);
+    GK_LAUNCH(wv, (k_attn_bwd_dkv<2, 2, false>), gkv, dim3(NW * 64), 0, sv, DKV_ARGS);
     GK_LAUNCH(wk, (k_attn_bwd_dkv<2, 1, true>), gkv, dim3(NW * 64), 0, s, DKV_ARGS);
   } else {
     GK_LAUNCH(wq, k_attn_bwd_dq<false>, gq, dim3(NW * 64), 0, sq, DKV_ARGS);
-    GK_LAUNCH(wv, (k_attn_bwd_dkv<2, 2, false>), gkv, dim3(NW * 64), 0, sq, DKV_ARGS);
+    GK_LAUNCH(wv, (k_attn_bwd_dkv<2, 2, false>), gkv, dim3(NW * 64), 0, sv, DKV_ARGS);
     GK_LAUNCH(wk, (k_attn_bwd_dkv<2, 1, false>), gkv, dim3(NW * 64), 0, s, DKV_ARGS);
   }
 #undef DKV_ARGS
   if (two) {
     hipError_t e = hipEventRecord(join, s2);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, join, 0);
+    if (e == hipSuccess && four) e = hipEventRecord(join4, s4);
+    if (e == hipSuccess && four) e = hipStreamWaitEvent(s, join4, 0);
     if (e != hipSuccess) return e;
   }
   return hipGetLastError();

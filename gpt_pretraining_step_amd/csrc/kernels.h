@@ -130,6 +130,8 @@ bool attn_bwd_fuses_norm(int T, int H, int Hkv, int hd, DType dt);
 struct Beside {
   hipStream_t s2 = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  hipStream_t s4 = nullptr;                    // optional: the dV pass there (else on s2)
+  hipEvent_t join4 = nullptr;
 };
 hipError_t attn_bwd(const void* qkv, const void* o, const float* lse,
                     const void* dout, void* dqkv, void* scratch, int B, int T,

@@ -88,7 +88,8 @@ enum { GPT_MODE_TRAIN = 0, GPT_MODE_EVAL = 1 };
  *   one_stream: 1 = gpt_step_bwd runs everything on the caller's stream.
  *     0 = for bf16 models of at least 4096 tokens the weight-gradient
  *     products and the embedding and gate gradients run on a second,
- *     library-owned stream (one per host thread and device, default
+ *     library-owned stream, and (head_dim 128) the attention backward's dQ
+ *     and dV passes on two more (all per host thread and device, default
  *     priority), forked from and joined back into the caller's stream with
  *     events, so the call still completes in the caller's stream order (and
  *     can be captured into a graph).  Beside the caller's stream the linear
