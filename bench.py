@@ -856,16 +856,28 @@ def bench_extras(a, torch, G):
     print(json.dumps(out), flush=True)
 
 
+EVAL_BATCH_TOKENS = 131072
+
+
+def eval_batch_rows(cfg, n_rows):
+    """Rows per gpt_eval_bpb batch: up to 131,072 tokens (64 d12 rows, 32
+    d12-GQA rows), at least the training batch.  Larger batches fill the
+    GEMMs' rounds of 256 tiles better (d12, 64 rows: 3.41M tokens/s against
+    3.25M in batches of 16); the result does not depend on the batching."""
+    return max(cfg["batch"], min(n_rows, EVAL_BATCH_TOKENS // cfg["seq_len"]))
+
+
 def eval_set_line(name, torch, G, gi, Session):
     """Evaluation tokens/s and bpb of a preset over its whole evaluation set
     (one gpt_eval_bpb call, timed with events; one warm-up call)."""
     cfg = gi.preset(name)
     _, eval_fpt, _ = model_flops(cfg)
+    n_rows = cfg["eval_rows"]
+    cfg["batch"] = eval_batch_rows(cfg, n_rows)
     s = Session(cfg, eval_ws=True, train_ws=False)
     w, bits = gi.make_params(cfg, s.n_params)
     s.set_params(w, bits)
     del w, bits
-    n_rows = cfg["eval_rows"]
     tok = s.upload(gi.make_eval_tokens(cfg, n_rows))
     tb = s.upload(gi.make_token_bytes(cfg))
     s.evaluate(tok, tb)
@@ -962,7 +974,7 @@ def main():
     tokens_per_step = B * T
 
     log("building inputs", a.config)
-    s = Session(cfg, eval_ws=True)
+    s = Session(cfg)
     w, bits = gi.make_params(cfg, s.n_params)
     if a.model_extras:
         # the extras vector's slots (C ABI layout): mixing weights (1, 0.1)
@@ -1029,17 +1041,22 @@ def main():
     log(f"optimizer step {opt_ms:.2f} ms (NorMuon {opt[True]:.2f} ms); fwd+bwd+optimizer "
         f"{tokens_per_step / ((ms + opt_ms) / 1e3):,.0f} tok/s")
 
-    # evaluation throughput (forward + CE + bytes reduction)
+    # evaluation throughput (forward + CE + bytes reduction), in batches of
+    # eval_batch_rows rows (a session of that batch sharing the parameters)
     ev_rows = a.eval_rows
-    ev_tok = s.upload(gi.make_eval_tokens(cfg, ev_rows))
-    tb = s.upload(gi.make_token_bytes(cfg))
-    s.evaluate(ev_tok, tb)
+    ev_batch = eval_batch_rows(cfg, ev_rows)
+    se = Session(dict(cfg, batch=ev_batch), eval_ws=True, train_ws=False)
+    se.params = s.params
+    ev_tok = se.upload(gi.make_eval_tokens(cfg, ev_rows))
+    tb = se.upload(gi.make_token_bytes(cfg))
+    se.evaluate(ev_tok, tb)
     torch.cuda.synchronize()
-    t_ev = time_events(lambda: s.evaluate(ev_tok, tb), 2, torch)
+    t_ev = time_events(lambda: se.evaluate(ev_tok, tb), 2, torch)
     eval_tok_s = ev_rows * T / t_ev
-    bpb = s.bpb.cpu().numpy().tolist()
-    log(f"eval {eval_tok_s:,.0f} tok/s, bpb {bpb[2]:.4f}")
-    del ev_tok
+    bpb = se.bpb.cpu().numpy().tolist()
+    log(f"eval {eval_tok_s:,.0f} tok/s (batches of {ev_batch} rows), bpb {bpb[2]:.4f}")
+    del ev_tok, se
+    torch.cuda.empty_cache()
     # the long-context workload's evaluation: d12-GQA over its whole 2^21-
     # target set (512 rows x 4096), a separate model of that shape
     gqa = None
@@ -1103,7 +1120,8 @@ def main():
         "optimizer_ns": f"Muon Newton-Schulz: {NS_TUPLE} x 5 (the classic quintic tuple; the "
                         f"page prints two of its five tuples)",
         "tokens_per_s_with_optimizer": round(tokens_per_step / ((ms + opt_ms) / 1e3), 1),
-        "eval_tokens_per_s": round(eval_tok_s, 1), "eval_rows": ev_rows, "eval_bpb": bpb[2],
+        "eval_tokens_per_s": round(eval_tok_s, 1), "eval_rows": ev_rows,
+        "eval_batch_rows": ev_batch, "eval_bpb": bpb[2],
         "eval_mfu_bf16": round(eval_tok_s * eval_fpt / PEAK_BF16, 4),
         "eval_d12gqa_2m": gqa,
         "context": {
