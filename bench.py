@@ -757,7 +757,14 @@ def bench_optim(a, torch, G):
     ms = time_events(step, a.steps, torch) * 1e3
     n_muon = sum(numel(s) for v in groups.values() for _, s in v)
     log(f"optimizer step {ms:.3f} ms: {n_muon:,} Muon + {n_total - n_muon:,} AdamW parameters")
-    prof = kernel_profile(step, a.prof_steps, torch, G) if a.prof_steps > 0 else []
+    # per-kernel split with every group on one stream (a kernel's time then
+    # carries no overlap with the groups on the library's side streams)
+    gc_one = G.make_config(dict(cfg, one_stream=1))
+
+    def step_one():
+        G.optim_step(gc_one, hp, 1, w, w16, grad, mom, m2, ows)
+
+    prof = kernel_profile(step_one, a.prof_steps, torch, G) if a.prof_steps > 0 else []
     for r in prof[:10]:
         rate = (f"{r['tflops']:7.1f} TFLOP/s" if r["tflops"] else
                 f"{r['gbps']:7.0f} GB/s" if r["gbps"] else "")

@@ -445,7 +445,8 @@ int run_forward(const Model& m0, const Plan& p, const ParamLayout& pl, const voi
 // and kept; default priority.  Results are bit for bit those of one stream
 // (every kernel and its inputs are unchanged; only the overlap differs).
 enum { EV_START, EV_DX1, EV_DX1_FREE, EV_DU, EV_DU_FREE, EV_DX2, EV_DX2_FREE, EV_QKV,
-       EV_QKV_FREE, EV_END, EV_ATT_FORK, EV_ATT_JOIN, EV_ATT_JOIN4, EV_COUNT };
+       EV_QKV_FREE, EV_END, EV_ATT_FORK, EV_ATT_JOIN, EV_ATT_JOIN4, EV_OPT_FORK, EV_OPT_J1,
+       EV_OPT_J2, EV_OPT_J3, EV_COUNT };
 struct SideStream {
   hipStream_t s = nullptr;
   hipStream_t s3 = nullptr;     // the attention backward's dQ pass
@@ -893,14 +894,20 @@ std::vector<MuonGroup> muon_groups(const Model& m, const ParamLayout& pl) {
   return {{&pl.wqkv, m.QKV, m.D}, {&pl.wo, m.D, (int64_t)m.H * m.hd},
           {&pl.wfc, m.F, m.D}, {&pl.wproj, m.D, m.F}};
 }
+// the optimizer workspace of one Muon group (staging copy, orthogonalized
+// update, orthogonalization / NorMuon scratch); the groups get disjoint
+// regions so they can run side by side
+size_t muon_group_ws(const Model& m, const MuonGroup& g) {
+  const size_t n = (size_t)m.L * g.rows * g.cols;
+  const size_t stage = (n * 4 + 255) / 256 * 256, xb = (n * 2 + 255) / 256 * 256;
+  const size_t scr = std::max(gk::polar_express_ws_bytes(m.L, g.rows, g.cols),
+                              gk::normuon_scratch_bytes(m.L, g.rows));
+  return stage + xb + (scr + 255) / 256 * 256;
+}
+
 size_t optim_ws(const Model& m, const ParamLayout& pl) {
   size_t b = 0;
-  for (const MuonGroup& g : muon_groups(m, pl)) {
-    const size_t n = (size_t)m.L * g.rows * g.cols;
-    const size_t stage = (n * 4 + 255) / 256 * 256, xb = (n * 2 + 255) / 256 * 256;
-    b = std::max(b, stage + xb + std::max(gk::polar_express_ws_bytes(m.L, g.rows, g.cols),
-                                          gk::normuon_scratch_bytes(m.L, g.rows)));
-  }
+  for (const MuonGroup& g : muon_groups(m, pl)) b += muon_group_ws(m, g);
   return b;
 }
 }  // namespace
@@ -945,15 +952,31 @@ int gpt_optim_step(const gpt_config* cfg, const gpt_optim_hparams* hp, int32_t s
   const bool copy16 = m.dt == gk::BF16;
   auto p16 = [&](int64_t off) { return copy16 ? (void*)((char*)params + off * 2) : nullptr; };
   char* w = (char*)ws;
-  // Muon: momentum into a [L, rows, cols] staging copy, the batched
-  // orthogonalization, then the step with lr max(1, rows / cols)^0.5
-  for (const MuonGroup& g : muon_groups(m, pl)) {
+  // The Muon groups (one per weight shape) are independent: beside the
+  // caller's stream they run on the library's side streams, forked from and
+  // joined back into it with events, each in its own workspace region (the
+  // small Newton-Schulz products of one group leave most CUs idle)
+  SideStream* sd = m.dt == gk::BF16 && !m.one_stream ? side_stream() : nullptr;
+  const std::vector<MuonGroup> groups = muon_groups(m, pl);
+  hipStream_t gs[4] = {s, s, s, s};
+  if (sd && groups.size() <= 4) {
+    HIP_TRY(hipEventRecord(sd->ev[EV_OPT_FORK], s));
+    const hipStream_t side[3] = {sd->s, sd->s3, sd->s4};
+    for (size_t i = 1; i < groups.size(); ++i) {
+      gs[i] = side[i - 1];
+      HIP_TRY(hipStreamWaitEvent(gs[i], sd->ev[EV_OPT_FORK], 0));
+    }
+  }
+  for (size_t gi = 0; gi < groups.size(); ++gi) {
+    const MuonGroup& g = groups[gi];
+    const hipStream_t s = gs[gi];
     const int64_t n = g.rows * g.cols;
     const size_t stage = ((size_t)m.L * n * 4 + 255) / 256 * 256;
     const size_t xb = ((size_t)m.L * n * 2 + 255) / 256 * 256;
     float* u = (float*)w;
     uint16_t* x = (uint16_t*)(w + stage);
     void* nsws = w + stage + xb;
+    w += muon_group_ws(m, g);
     // momentum and update run over the group's L matrices in one launch each
     // (per matrix for deeper models than the offset table holds)
     const bool grouped = m.L <= gk::kMaxGroupLayers;
@@ -999,7 +1022,8 @@ int gpt_optim_step(const gpt_config* cfg, const gpt_optim_hparams* hp, int32_t s
       }
     }
   }
-  // AdamW: embeddings and value-embedding tables, lm_head, gates, extras
+  // AdamW (on the caller's stream, beside the side streams' groups):
+  // embeddings and value-embedding tables, lm_head, gates, extras
   auto adam = [&](int64_t off, int64_t n, float lr) -> int {
     HIP_TRY(gk::adamw(master + off, grads + off, state1 + off, state2 + off, n, step, lr,
                       hp->adam_beta1, hp->adam_beta2, hp->adam_eps, hp->adam_wd, p16(off), s));
@@ -1014,6 +1038,13 @@ int gpt_optim_step(const gpt_config* cfg, const gpt_optim_hparams* hp, int32_t s
   }
   // the model extras' scalars and smear weights, with the gates
   if (pl.extras >= 0 && (st = adam(pl.extras, m.ex_n, hp->adam_lr_gate))) return st;
+  // the caller's stream waits for the side streams' groups
+  const int joins[3] = {EV_OPT_J1, EV_OPT_J2, EV_OPT_J3};
+  for (size_t i = 1; i < groups.size(); ++i) {
+    if (gs[i] == s) continue;
+    HIP_TRY(hipEventRecord(sd->ev[joins[i - 1]], gs[i]));
+    HIP_TRY(hipStreamWaitEvent(s, sd->ev[joins[i - 1]], 0));
+  }
   return GPT_OK;
 }
 

@@ -221,7 +221,11 @@ int gpt_eval_bpb(const gpt_config* cfg, const void* params,
  *   master, grads, state1, state2: device fp32 in the flat layout (states
  *   zero before step 1).  params: the dtype copy the step reads, written
  *   from the updated master (bf16 configs; may be null for fp32 configs,
- *   whose master is the parameter buffer).  ws: gpt_optim_ws_bytes(cfg).
+ *   whose master is the parameter buffer).  ws: gpt_optim_ws_bytes(cfg)
+ *   (one region per Muon group).  For bf16 configs without one_stream, the
+ *   Muon groups other than the first run on the library's side streams,
+ *   forked from and joined back into `stream` with events, so the call
+ *   completes in `stream` order; results do not depend on it.
  *   Tensor offsets must be multiples of 8 elements (true when D, F, the
  *   qkv width and H hd are). */
 typedef struct gpt_optim_hparams {

@@ -1065,3 +1065,34 @@ def test_optim_step(which, normuon):
     assert off == n
     if bf:
         np.testing.assert_array_equal(to_np(params), O.round_bf16(got.astype(np.float32)))
+
+
+@pytest.mark.parametrize("normuon", [False, True])
+def test_optim_step_streams_bitwise(normuon):
+    """The Muon groups on the library's side streams (the default for bf16)
+    leave masters, bf16 copies and both states bit for bit as on one
+    stream: each group's kernels and inputs are the same, only the overlap
+    differs.  Three steps, so the second and third read the states the
+    concurrent groups wrote."""
+    from tests.gpu_util import small_bf16
+    cfgd = small_bf16(resid_lambdas=1, smear=1, backout_layer=1)
+    say("optim streams", "normuon", normuon)
+    n = O.param_count(cfgd)
+    rng = np.random.default_rng(23)
+    w0 = (rng.standard_normal(n) * 0.05).astype(np.float32)
+    grads = [dev(rng.standard_normal(n).astype(np.float32) * 1e-2, torch.float32)
+             for _ in range(3)]
+    hp = G.make_optim_hparams([NS_CLASSIC] * 5, normuon=normuon, normuon_beta2=0.9)
+    out = []
+    for one in (0, 1):
+        cfg = G.make_config(dict(cfgd, one_stream=one))
+        master = dev(w0, torch.float32)
+        params = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+        s1, s2 = torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+        ws = torch.empty(G.optim_ws_bytes(cfg), dtype=torch.uint8, device=DEV)
+        for k in range(3):
+            G.optim_step(cfg, hp, k + 1, master, params, grads[k], s1, s2, ws)
+        torch.cuda.synchronize()
+        out.append([to_np(t) for t in (master, params.float(), s1, s2)])
+    for a, b in zip(*out):
+        np.testing.assert_array_equal(a, b)
