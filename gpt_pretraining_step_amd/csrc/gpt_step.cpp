@@ -560,7 +560,7 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
                                at<float>(ws, p.ce_stats), at<float>(ws, p.lse_z), tokens, m.T, 0,
                                inv_n, s));
     HIP_TRY(gk::ce_fix(at<float>(ws, p.ce_stats), nullptr, N, m.V, tokens, m.T, 0, nullptr,
-                       nullptr, dz, const_cast<void*>(dz), inv_n, s));
+                       at<float>(ws, p.lse_z), dz, const_cast<void*>(dz), inv_n, s));
     HIP_TRY(fork(EV_START));
     g = gk::GemmDesc{gk::OP_TN, m.V, m.D, N, dz, m.V, hf, m.D, grads + pl.wlm, m.D, wepi, nullptr};
     HIP_TRY(gk::gemm(g, dt, w));

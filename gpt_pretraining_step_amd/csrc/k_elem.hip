@@ -997,56 +997,54 @@ generic:
   return hipGetLastError();
 }
 
-// Fused lm_head + cross-entropy, second half: one 512-thread block per row.
-// lse from the row's per-tile (m_t, s_t) in a fixed order, the loss, and
-// (with dz) the softmax gradient from the stored bf16 e = exp(logit - m_t),
-// rescaled by exp(m_t - lse) into dz (which may be e itself: every thread
-// reads its runs before writing them).
-__global__ __launch_bounds__(512) void k_ce_fix(const float2* __restrict__ stats, int ntn,
-                                                const float* __restrict__ zt, int V,
-                                                const int32_t* __restrict__ tok, int T,
-                                                int direct, float* __restrict__ ell,
-                                                float* __restrict__ lse, const uint16_t* e,
-                                                uint16_t* dz, float scale) {
-  __shared__ float ct[1024];
-  __shared__ float red[8];
-  const int64_t row = blockIdx.x;
+// Fused lm_head + cross-entropy, second half.  k_ce_stats: one wave per row,
+// lse = M + log(sum_t s_t exp(m_t - M)) with M = max_t m_t over the row's
+// per-tile (m_t, s_t), summed per lane then across the wave in a fixed
+// order; ell = lse - the target's logit.
+__global__ __launch_bounds__(256) void k_ce_stats(const float2* __restrict__ stats, int ntn,
+                                                  const float* __restrict__ zt, int64_t rows,
+                                                  float* __restrict__ ell,
+                                                  float* __restrict__ lse) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
   const float2* st = stats + row * ntn;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float m = -INFINITY;
-  for (int t = threadIdx.x; t < ntn; t += 512) m = fmaxf(m, st[t].x);
-  m = wave_max(m);
-  if (lane == 0) red[w] = m;
-  __syncthreads();
-  float M = red[0];
-#pragma unroll
-  for (int k = 1; k < 8; ++k) M = fmaxf(M, red[k]);
-  __syncthreads();
+  for (int t = lane; t < ntn; t += 64) m = fmaxf(m, st[t].x);
+  const float M = wave_max(m);
   float sacc = 0.f;
-  for (int t = threadIdx.x; t < ntn; t += 512) {
+  for (int t = lane; t < ntn; t += 64) {
     const float2 v = st[t];
     sacc += v.y * expf(v.x - M);
   }
-  sacc = wave_sum(sacc);
-  if (lane == 0) red[w] = sacc;
-  __syncthreads();
-  float S = 0.f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) S += red[k];
-  const float L = M + logf(S);
-  if (ell && threadIdx.x == 0) {
+  const float L = M + logf(wave_sum(sacc));
+  if (lane == 0) {
     ell[row] = L - zt[row];
     lse[row] = L;
   }
-  if (!dz) return;
+}
+
+// k_ce_grad: one 512-thread block per row; the softmax gradient from the
+// stored bf16 e = exp(logit - m_t) and the row's lse, rescaled per tile by
+// exp(m_t - lse) grad_scale into dz (which may be e itself: every thread
+// reads its runs before writing them), minus grad_scale at the target.
+__global__ __launch_bounds__(512) void k_ce_grad(const float2* __restrict__ stats, int ntn,
+                                                 const float* __restrict__ lse_in, int V,
+                                                 const int32_t* __restrict__ tok, int T,
+                                                 int direct, const uint16_t* e, uint16_t* dz,
+                                                 float scale) {
+  __shared__ float ct[1024];
+  const int64_t row = blockIdx.x;
+  const float2* st = stats + row * ntn;
+  const float L = lse_in[row];
   for (int t = threadIdx.x; t < ntn; t += 512) ct[t] = expf(st[t].x - L) * scale;
   __syncthreads();
   const int tgt = direct ? tok[row] : tok[(row / T) * (T + 1) + row % T + 1];
   const uint4* pe = (const uint4*)(e + row * (int64_t)V);
   uint4* p = (uint4*)(dz + row * (int64_t)V);
-  // four 16-byte runs per thread in flight before the first store (the
+  // eight 16-byte runs per thread in flight before the first store (the
   // stores would otherwise hold every next load behind them)
-  constexpr int U = 4;
+  constexpr int U = 8;
   const int n8 = V / 8;
   for (int k0 = threadIdx.x; k0 < n8; k0 += 512 * U) {
     uint4 u[U];
@@ -1075,7 +1073,10 @@ __global__ __launch_bounds__(512) void k_ce_fix(const float2* __restrict__ stats
       o.y = pack2bf(f[2], f[3]);
       o.z = pack2bf(f[4], f[5]);
       o.w = pack2bf(f[6], f[7]);
-      p[k] = o;
+      // streaming stores: the 2 bytes per logit leave for HBM at once (the
+      // weight-gradient product that reads them runs later)
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(u32x4{o.x, o.y, o.z, o.w}, (u32x4*)(p + k));
     }
   }
 }
@@ -1086,14 +1087,20 @@ hipError_t ce_fix(const float* stats, const float* zt, int64_t rows, int V, cons
   if (rows <= 0) return hipSuccess;
   if (V % 256 || V / 256 > 1024) return hipErrorInvalidValue;
   if (dz && !e) return hipErrorInvalidValue;
-  if ((ell == nullptr) != (lse == nullptr)) return hipErrorInvalidValue;
+  if (!lse || (ell && !zt)) return hipErrorInvalidValue;
   const int ntn = V / 256;
-  // stats read once (target logits with ell); e read and the gradient
-  // written once
-  const Work w(0.0, (double)rows * (8.0 * ntn + (ell ? 12.0 : 0.0)) +
-                        (dz ? 4.0 * (double)rows * V : 0.0));
-  GK_LAUNCH(w, k_ce_fix, dim3((unsigned)rows), dim3(512), 0, s, (const float2*)stats, ntn, zt, V,
-            tok, tgt_T, tgt_direct, ell, lse, (const uint16_t*)e, (uint16_t*)dz, grad_scale);
+  if (ell) {
+    // stats read once, ell and lse written
+    const Work w(0.0, (double)rows * (8.0 * ntn + 12.0));
+    GK_LAUNCH(w, k_ce_stats, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+              (const float2*)stats, ntn, zt, rows, ell, lse);
+  }
+  if (dz) {
+    // e read and the gradient written once
+    const Work w(0.0, (double)rows * (8.0 * ntn + 4.0) + 4.0 * (double)rows * V);
+    GK_LAUNCH(w, k_ce_grad, dim3((unsigned)rows), dim3(512), 0, s, (const float2*)stats, ntn,
+              lse, V, tok, tgt_T, tgt_direct, (const uint16_t*)e, (uint16_t*)dz, grad_scale);
+  }
   return hipGetLastError();
 }
 

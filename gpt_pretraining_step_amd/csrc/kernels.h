@@ -171,10 +171,11 @@ hipError_t qkv_gemm_rope_norm(const void* h, int64_t rows, int D, const void* wq
 // never stored as such; per row and 256-column tile t the max m_t of the
 // logits and s_t = sum exp(logit - m_t) go to stats[row * (V / 256) + t],
 // the target's logit to zt[row], and (if e) e = exp(logit - m_t) as bf16 to
-// e[row * V + col].  ce_fix: lse = max_t m_t + log(sum_t s_t exp(m_t -
-// max)); if ell, ell = lse - zt and lse go out; if dz, dz = (e exp(m_t -
-// lse) - onehot) * grad_scale as bf16 (dz may be e itself).  Targets as in
-// ce_rows.
+// e[row * V + col].  ce_fix: with ell (and zt), lse = max_t m_t +
+// log(sum_t s_t exp(m_t - max)) and ell = lse - zt go out; with dz, dz =
+// (e exp(m_t - lse) - onehot) * grad_scale as bf16 (dz may be e itself),
+// from the lse just formed or, without ell, the one lse holds.  Targets as
+// in ce_rows.
 bool lm_ce_fused_ok(int64_t rows, int V, int D);
 size_t lm_ce_stats_bytes(int64_t rows, int V);
 // (tgt_direct: the target of row n is tok[n] instead)
