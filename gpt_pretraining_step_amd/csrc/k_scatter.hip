@@ -202,13 +202,17 @@ __device__ __forceinline__ void rows_sum(const uint64_t* ck, int i0, int i1, con
   }
 }
 
-// One block (4 waves) per chunk of 64 sorted positions.  Runs of equal ids
+// One block (8 waves) per chunk of 64 sorted positions.  Runs of equal ids
 // shorter than kLongRun go to the waves round-robin, each summed by one wave
-// in sorted order; longer runs are split into 4 consecutive quarters, one per
-// wave, added in quarter order through LDS.  A run that is its id's whole
+// in sorted order; longer runs are split into 8 consecutive parts, one per
+// wave, added pairwise in a fixed order through LDS.  (Eight waves: a run
+// costs its wave a load round trip however short, and most runs of a Zipf
+// batch are a row or two; 39 us per d12 table against 58 for four waves and
+// 51 for sixteen.)  A run that is its id's whole
 // segment is written as the final row; a run cut by the chunk's edge leaves a
 // partial row (slot 0 if it starts the chunk, 1 if it ends it).
 static constexpr int kLongRun = 16;
+static constexpr int kSegWaves = 8;
 
 template <int NP>
 __device__ __forceinline__ void put_row(float* out, int W, int lane, bool add,
@@ -228,14 +232,14 @@ __device__ __forceinline__ void put_row(float* out, int W, int lane, bool add,
 }
 
 template <typename Tv, int NP>
-__global__ __launch_bounds__(256) void k_seg_rows(const uint64_t* keys, int64_t N,
+__global__ __launch_bounds__(64 * kSegWaves) void k_seg_rows(const uint64_t* keys, int64_t N,
                                                   const int32_t* first1, const int32_t* last1,
                                                   const Tv* src, int64_t ld, int W,
                                                   const float* gate, int Hkv, int hd,
                                                   float* dst, float* part, int accumulate) {
   static_assert(kChunk == 64, "one lane per chunk position");
   __shared__ uint64_t ck[kChunk];
-  __shared__ float red[4][NP * 256];
+  __shared__ float red[kSegWaves][NP * 256];
   const int64_t c0 = (int64_t)blockIdx.x * kChunk, c1 = std::min(N, c0 + kChunk);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int len = (int)(c1 - c0);
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(256) void k_seg_rows(const uint64_t* keys, int64_t 
     const int rs = __builtin_ctzll(m);
     m &= m - 1;
     const int re = m ? __builtin_ctzll(m) : len;
-    if (re - rs >= kLongRun || (r & 3) != w) continue;
+    if (re - rs >= kLongRun || (r & (kSegWaves - 1)) != w) continue;
     const uint32_t id = (uint32_t)(ck[rs] >> 32);
     rows_sum<Tv, NP>(ck, rs, re, src, ld, W, gate, Hkv, hd, lane, acc);
     bool whole;
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(256) void k_seg_rows(const uint64_t* keys, int64_t 
     m &= m - 1;
     const int re = m ? __builtin_ctzll(m) : len;
     if (re - rs < kLongRun) continue;
-    const int q = (re - rs + 3) / 4;
+    const int q = (re - rs + kSegWaves - 1) / kSegWaves;
     const int a = std::min(re, rs + w * q), b = std::min(re, a + q);
     rows_sum<Tv, NP>(ck, a, b, src, ld, W, gate, Hkv, hd, lane, acc);
 #pragma unroll
@@ -291,7 +295,14 @@ __global__ __launch_bounds__(256) void k_seg_rows(const uint64_t* keys, int64_t 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int c = 256 * p + 4 * lane + e;
-          acc[p][e] = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+          float t[kSegWaves];                       // pairwise, fixed tree
+#pragma unroll
+          for (int k = 0; k < kSegWaves; ++k) t[k] = red[k][c];
+#pragma unroll
+          for (int n = kSegWaves / 2; n >= 1; n /= 2)
+#pragma unroll
+            for (int k = 0; k < n; ++k) t[k] = t[2 * k] + t[2 * k + 1];
+          acc[p][e] = t[0];
         }
       const uint32_t id = (uint32_t)(ck[rs] >> 32);
       bool whole;
@@ -358,8 +369,8 @@ hipError_t seg_scatter(const void* scratch, int64_t N, int V, int maxW, const vo
   const int es = dt == BF16 ? 2 : 4;
   const Work w(0.0, (double)N * (W * es + 12) + (double)V * W * 4 * (accumulate ? 2 : 1));
 #define SEG_ROWS(TV, NPV)                                                                      \
-  GK_LAUNCH(w, (k_seg_rows<TV, NPV>), dim3(chunks), dim3(256), 0, s, keys, N, first1, last1,   \
-            (const TV*)src, ld, W, gate, Hkv, hd, dst, part, accumulate)
+  GK_LAUNCH(w, (k_seg_rows<TV, NPV>), dim3(chunks), dim3(64 * kSegWaves), 0, s, keys, N,       \
+            first1, last1, (const TV*)src, ld, W, gate, Hkv, hd, dst, part, accumulate)
 #define SEG_NP(TV)                                                                             \
   switch (np) {                                                                                \
     case 1: SEG_ROWS(TV, 1); break;                                                            \
