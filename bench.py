@@ -717,6 +717,8 @@ def bench_optim(a, torch, G):
     in HBM."""
     import gptinputs as gi
     cfg = gi.preset(a.config)
+    if a.one_stream:
+        cfg["one_stream"] = 1
     gc = G.make_config(cfg)
     L = cfg["n_layer"]
     n_total = G.param_count(gc)
@@ -779,7 +781,9 @@ def bench_optim(a, torch, G):
         "config": {"workload": f"{a.config} optimizer step: {n_muon} Muon parameters in "
                                f"{len(groups)} shape groups of {L} (momentum 0.95 Nesterov, 5 "
                                f"quintic Newton-Schulz steps), {n_total - n_muon} AdamW "
-                               "parameters", "parallelism": "single GPU"},
+                               "parameters", "parallelism": "single GPU",
+                   "streams": "one" if a.one_stream else
+                              "four (Muon groups beside each other and AdamW)"},
         "roofline": roof,
         "cpu_baseline": None if a.no_cpu else cpu_optim_baseline(
             [s for v in groups.values() for _, s in v[:1]] * L,
@@ -919,7 +923,7 @@ def main():
                     help="train: skip the d12-GQA 2^21-target evaluation line")
     ap.add_argument("--one-stream", action="store_true",
                     help="train: the whole step on one stream (no second stream for the "
-                         "weight-gradient work)")
+                         "weight-gradient work); optim: every Muon group on one stream")
     ap.add_argument("--workload", choices=("train", "decode", "fp8", "muon", "optim", "extras"),
                     default="train",
                     help="train: the fwd+bwd step; decode: KV-cache decode attention; fp8: the "
