@@ -844,6 +844,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
     pa.issue(kbeg, ra, wave);
     pb.issue(kbeg, rb, wave);
     if (nsl > 1) pa.issue(kbeg + BK, ra + BM * 64, wave);
+    // The second half slice's products are carried over the next barrier:
+    // its fragments are read before it, and its MFMAs cover the latency of
+    // the next slice's first reads (every wave reads at the same moment,
+    // right after the barrier).
+    auto rd = [&](bf16x8_t (&a)[TMI], bf16x8_t (&b)[TNJ], const bf16* As, const bf16* Bs,
+                  int kk) {
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j) b[j] = frag<BN, TB>(Bs, wn + 16 * j, kk, lane);
+#pragma unroll
+      for (int i = 0; i < TMI; ++i) a[i] = frag<BM, TA>(As, wm + 16 * i, kk, lane);
+    };
+    auto mm = [&](const bf16x8_t (&a)[TMI], const bf16x8_t (&b)[TNJ]) {
+#pragma unroll
+      for (int i = 0; i < TMI; ++i)
+#pragma unroll
+        for (int j = 0; j < TNJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    };
+    bf16x8_t fa[TMI], fb[TNJ], ga[TMI], gb[TNJ];   // first / second half slice
     int sa = 0, sb = 0;                      // stages of slice `it`
     for (; it < nsl; ++it) {
       if (it + 1 < nsl) dma_wait_n<NA>();
@@ -852,10 +871,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
       const int sa2 = sa == 0 ? 2 : sa - 1;  // (it + 2) % 3
       if (it + 1 < nsl) pb.issue(kbeg + (int64_t)(it + 1) * BK, rb + (sb ^ 1) * BN * 64, wave);
       if (it + 2 < nsl) pa.issue(kbeg + (int64_t)(it + 2) * BK, ra + sa2 * BM * 64, wave);
-      compute2(ra + sa * BM * 64, rb + sb * BN * 64);
+      const bf16* As = ra + sa * BM * 64;
+      const bf16* Bs = rb + sb * BN * 64;
+      rd(fa, fb, As, Bs, 0);
+      if (it > 0) mm(ga, gb);                // slice it - 1, second half
+      mm(fa, fb);
+      rd(ga, gb, As, Bs, 32);
       sa = sa == 2 ? 0 : sa + 1;
       sb ^= 1;
     }
+    if (nsl > 0) mm(ga, gb);
   }
 
   const int cq = (lane >> 4) * 4, lr = lane & 15;
