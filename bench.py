@@ -204,23 +204,34 @@ def kernel_profile(step, n_steps, torch, G):
 
 
 def roofline_of(row, step_ms, peak_flops=PEAK_BF16):
-    """Roofline object of one kernel row of kernel_profile."""
-    from rocprof_summary import load_traffic
+    """Roofline object of one kernel row of kernel_profile (its measured
+    HBM traffic is attached by emit(), which knows the workload)."""
     sec = row["avg_launch_ms"] / 1e3
     if row["flops_per_launch"] > 0:
         ach, peak, unit, bound = row["flops_per_launch"] / sec / 1e12, peak_flops / 1e12, "TFLOP/s", "mfma"
     else:
         ach, peak, unit, bound = row["bytes_per_launch"] / sec / 1e9, PEAK_HBM / 1e9, "GB/s", "hbm"
-    tr = load_traffic(row["kernel"])
     return {"bound": bound, "kernel": row["kernel"], "achieved": round(ach, 2), "peak": peak,
             "unit": unit, "frac": round(ach / peak, 4),
-            "traffic": tr["traffic_bytes"] if tr else None,
-            "traffic_source": tr["summary"] if tr else None,
+            "traffic": None, "traffic_source": None,
             "algorithmic_flops_per_launch": row["flops_per_launch"],
             "algorithmic_bytes_per_launch": row["bytes_per_launch"],
             "avg_launch_ms": round(row["avg_launch_ms"], 4),
             "launches_per_step": row["launches_per_step"],
             "share_of_step": round(row["ms_per_step"] / step_ms, 3)}
+
+
+def emit(out):
+    """Print the JSON line, with the roofline kernel's HBM traffic per
+    launch from the committed rocprofv3 summary of the same kernel sources
+    and the same workload (null when there is none)."""
+    from rocprof_summary import load_traffic
+    rf = out.get("roofline")
+    if rf:
+        tr = load_traffic(rf["kernel"], out.get("config", {}).get("workload"))
+        rf["traffic"] = tr["traffic_bytes"] if tr else None
+        rf["traffic_source"] = tr["summary"] if tr else None
+    print(json.dumps(out), flush=True)
 
 
 def copy_calibration(torch):
@@ -461,7 +472,7 @@ def bench_decode(a, torch, G):
         "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
                     for r in prof],
     }
-    print(json.dumps(out), flush=True)
+    emit(out)
 
 
 FP8_METRIC = "FP8 (tensor-wise) linear layers fwd+bwd of a training step: tokens/s; % fp8 MFMA peak"
@@ -572,7 +583,7 @@ def bench_fp8(a, torch, G):
         "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
                     for r in prof],
     }
-    print(json.dumps(out), flush=True)
+    emit(out)
 
 
 def cpu_fp8_baseline(cfg, rows=256):
@@ -703,7 +714,7 @@ def bench_muon(a, torch, G):
         "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
                     for r in prof],
     }
-    print(json.dumps(out), flush=True)
+    emit(out)
 
 
 OPTIM_METRIC = "optimizer step (Muon for block matrices, AdamW for the rest): ms/step"
@@ -791,7 +802,7 @@ def bench_optim(a, torch, G):
         "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
                     for r in prof],
     }
-    print(json.dumps(out), flush=True)
+    emit(out)
 
 
 EXTRAS_METRIC = "model extras (smear, residual lambdas, backout) fwd+bwd of a step: GB/s"
@@ -864,7 +875,7 @@ def bench_extras(a, torch, G):
         "kernels": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
                     for r in prof],
     }
-    print(json.dumps(out), flush=True)
+    emit(out)
 
 
 EVAL_BATCH_TOKENS = 131072
@@ -1150,7 +1161,7 @@ def main():
         "shapes": [{k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
                    for r in table],
     }
-    print(json.dumps(out), flush=True)
+    emit(out)
 
 
 if __name__ == "__main__":

@@ -69,16 +69,18 @@ def kernel_sources_sha256(kernel: str) -> str:
     return h.hexdigest()
 
 
-def load_traffic(kernel: str):
+def load_traffic(kernel: str, workload: str | None = None):
     """Calibrated HBM bytes per launch of `kernel` from profiles/, or None
-    when no summary covers it or its sources changed since."""
+    when no summary covers it, its sources changed since, or (with a
+    workload) the summary was taken on another workload."""
     want = kernel_sources_sha256(kernel)
     for f in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
         with open(f, encoding="utf-8") as fh:
             for line in fh:
                 if line.startswith("traffic-json:"):
                     d = json.loads(line[len("traffic-json:"):])
-                    if d.get("kernel") == kernel and d.get("sources_sha256") == want:
+                    if d.get("kernel") == kernel and d.get("sources_sha256") == want and \
+                            (workload is None or d.get("workload") == workload):
                         d["summary"] = os.path.relpath(f, ROOT)
                         return d
     return None
@@ -187,6 +189,8 @@ def main():
                    traffic_bytes=round(fetch_b + write_b), fetch_factor=round(ff, 5),
                    write_factor=round(wf, 5), dispatches=len(fv),
                    sources_sha256=kernel_sources_sha256(a.kernel))
+        if bench and isinstance(bench.get("config"), dict):
+            rec["workload"] = bench["config"].get("workload")
         L.append("traffic-json: " + json.dumps(rec))
         L.append("")
     os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)

@@ -33,6 +33,22 @@ def test_load_traffic_unknown_kernel_is_none():
     assert R.load_traffic("k_no_such_kernel") is None
 
 
+def test_load_traffic_matches_workload(tmp_path, monkeypatch):
+    """A summary's traffic is reported only for the workload it was taken
+    on: the same kernel on another model shape gets none."""
+    k = "k_gemm_dma<256, 256, true, true, 4>"
+    rec = {"kernel": k, "traffic_bytes": 123, "sources_sha256": R.kernel_sources_sha256(k),
+           "workload": "shape A"}
+    (tmp_path / "p.md").write_text("# t\n\ntraffic-json: " + __import__("json").dumps(rec) + "\n")
+    monkeypatch.setattr(R, "PROFILES", str(tmp_path))
+    assert R.load_traffic(k, "shape A")["traffic_bytes"] == 123
+    assert R.load_traffic(k, "shape B") is None
+    assert R.load_traffic(k)["traffic_bytes"] == 123
+    rec["sources_sha256"] = "0" * 64                   # sources changed since
+    (tmp_path / "p.md").write_text("traffic-json: " + __import__("json").dumps(rec) + "\n")
+    assert R.load_traffic(k, "shape A") is None
+
+
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
