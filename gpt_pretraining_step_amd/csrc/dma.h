@@ -49,6 +49,16 @@ __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t lds, uint32_t voff)
                : "memory", "m0");
 }
 
+// One 4-byte-per-lane buffer load into LDS at `lds` + 4 lane: a gather, each
+// lane with its own byte offset `voff` (range-checked like dma16's).  Same
+// tracking as dma16: waited for by the explicit waits below.
+__device__ __forceinline__ void dma4(i32x4_t rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
 // Wait for every buffer-to-LDS load this wave issued (they are not tracked
 // by the compiler); follow with a barrier before other waves read the data.
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

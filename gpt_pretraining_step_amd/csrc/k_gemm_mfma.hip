@@ -685,13 +685,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
                                                      TileMap tm, float* partial) {
   constexpr int WM = BM / 4, WN = BN / 2;
   constexpr int TMI = WM / 16, TNJ = WN / 16;
-  // LDS: E_CEB keeps two stages of (A, B) tiles; every other product a
-  // ring of three A tiles and two B tiles (below)
-  constexpr int S0 = EPI == E_CEB ? (BM + BN) * 64 : (3 * BM + 2 * BN) * 64;
-  constexpr int S1 = EPI == E_CEB ? (BM + BN) * 64 : 512;
-  __shared__ __attribute__((aligned(1024))) bf16 st0[S0];
-  __shared__ __attribute__((aligned(1024))) bf16 st1[S1];
-  bf16* const lds = st0;
+  // LDS: a ring of three A tiles and two B tiles (below); E_CEB also keeps
+  // the tile's 256 rows' lse and two slots of their vocabulary-tile maxima
+  constexpr int SX = EPI == E_CEB ? 3 * 256 * 2 : 0;
+  __shared__ __attribute__((aligned(1024))) bf16 lds[(3 * BM + 2 * BN) * 64 + SX];
   if (blockIdx.y) {
     constexpr int ce = (EPI == E_F32 || EPI == E_F32_ACC) ? 4 : 2;
     A += blockIdx.y * tm.bs_a;
@@ -726,54 +723,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
 #pragma unroll
     for (int j = 0; j < TNJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // E_CEB: per-row factors applied to the accumulator just before its first
-  // MFMA of a slice (scaled = true), so the multiplies interleave with the
-  // matrix work instead of draining it
-  float cb_f[TMI];
-  auto compute = [&](const bf16* st, auto scaled) {
-    const bf16* As = st;
-    const bf16* Bs = st + BM * 64;
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      bf16x8_t a[TMI], b[TNJ];
-#pragma unroll
-      for (int j = 0; j < TNJ; ++j) b[j] = frag<BN, TB>(Bs, wn + 16 * j, kk, lane);
-#pragma unroll
-      for (int i = 0; i < TMI; ++i) a[i] = frag<BM, TA>(As, wm + 16 * i, kk, lane);
-#pragma unroll
-      for (int i = 0; i < TMI; ++i) {
-        if constexpr (decltype(scaled)::value) {
-          if (kk == 0) {
-            // row group i in place, then its MFMAs: the order is pinned so
-            // the scaled copies never coexist with the originals
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < TNJ; ++j) acc[i][j] *= cb_f[i];
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < TNJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-      }
-    }
-  };
-  const std::false_type plain;
-  auto compute2 = [&](const bf16* As, const bf16* Bs) {
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      bf16x8_t a[TMI], b[TNJ];
-#pragma unroll
-      for (int j = 0; j < TNJ; ++j) b[j] = frag<BN, TB>(Bs, wn + 16 * j, kk, lane);
-#pragma unroll
-      for (int i = 0; i < TMI; ++i) a[i] = frag<BM, TA>(As, wm + 16 * i, kk, lane);
-#pragma unroll
-      for (int i = 0; i < TMI; ++i)
-#pragma unroll
-        for (int j = 0; j < TNJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-    }
-  };
-
   // E_CEB (A = e = exp(logit - m_t), K = the vocabulary): the accumulator
   // of each row is kept in units of exp(m'_t) for the 256-column tile t
   // being summed, m'_t = max(m_t, lse - 40), and multiplied by exp(m'_(t-1)
@@ -781,108 +730,111 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
   // factors stay within e^(+-40); a tile whose max is more than 40 below
   // lse counts as if it were 40 below, a change far under bf16 resolution
   // (its true weight is below e^-40).  The next tile's m_t is fetched a
-  // tile ahead.
-  float cb_lse[TMI], cb_m[TMI], cb_next[TMI];
+  // tile ahead.  The factors of a tile are applied after the carried
+  // products of the previous tile's last slice and before the tile's own
+  // first products.
+  // The lse of the block's rows and each tile's maxima reach LDS by buffer
+  // loads issued ahead of a slice's operand loads (waves 0-3, one row a
+  // lane), so the per-slice waits cover them and no other load is in flight
+  // in the main loop: the maxima of tile t + 1 are fetched when tile t
+  // starts, into slot (t + 1) % 2.
+  float cb_lse[TMI], cb_m[TMI];
   const int ntv = (int)(K >> 8);
-  const int64_t mrow = m0 + wm + (lane & 15);
-  auto cb_stat = [&](int i, int t) {       // m_t of row i's tile t
-    return tm.ce_stats[2 * (min(mrow + 16 * i, M - 1) * ntv + t)];
+  float* const cb_lds = (float*)(lds + (3 * BM + 2 * BN) * 64);   // lse, slot 0, slot 1
+  // descriptors and the wave test are uniform (scalar registers, branch)
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const i32x4_t cb_rs = make_rsrc(EPI == E_CEB ? tm.ce_stats : nullptr, M * ntv * 8);
+  const uint32_t cb_off = (uint32_t)(min(m0 + 64 * (wave & 3) + lane, M - 1) * ntv * 8);
+  auto cb_issue = [&](int t) {             // maxima of tile t
+    if (wv < 4) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(lds_void_t*)(cb_lds + 256 * (1 + (t & 1)) + 64 * wv));
+      dma4(cb_rs, dst, cb_off + 8u * (uint32_t)t);
+    }
   };
   if constexpr (EPI == E_CEB) {
-#pragma unroll
-    for (int i = 0; i < TMI; ++i) {
-      cb_lse[i] = tm.ce_lse[min(mrow + 16 * i, M - 1)];
-      cb_next[i] = cb_stat(i, 0);
-      cb_m[i] = fmaxf(cb_next[i], cb_lse[i] - 40.f);   // the first factor is 1
+    const i32x4_t cb_rl = make_rsrc(tm.ce_lse, M * 4);
+    if (wv < 4) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(lds_void_t*)(cb_lds + 64 * wv));
+      dma4(cb_rl, dst, (uint32_t)(min(m0 + 64 * wv + lane, M - 1) * 4));
     }
+    cb_issue(0);
   }
 
   const int nsl = (int)((kend - kbeg) / BK);
   int it = 0;
-  if constexpr (EPI == E_CEB) {
-    // two stages in two arrays, visited in a loop unrolled by four (one
-    // 256-wide vocabulary tile per trip) so that every LDS access names its
-    // stage statically; K = V, a multiple of 256: nsl is a multiple of 4
-    pa.issue(kbeg, st0, wave);
-    pb.issue(kbeg, st0 + BM * 64, wave);
-    auto next = [&](int it, bf16* st) {    // wait for slice it - 1, fetch slice it
-      dma_wait();
-      __syncthreads();
-      if (it < nsl) {
-        pa.issue(kbeg + (int64_t)it * BK, st, wave);
-        pb.issue(kbeg + (int64_t)it * BK, st + BM * 64, wave);
+  // A ring of three, B ring of two: A (the activations or gradients, the
+  // operand that streams from HBM) is fetched two slices ahead, B one.
+  // Per slice: wait until only A(s + 1) is in flight (loads land in issue
+  // order and A(s + 1) went out after B(s)), barrier (every wave is done
+  // with slice s - 1, whose A and B stages the next loads reuse), issue
+  // B(s + 1) then A(s + 2), multiply slice s.
+  bf16* const ra = lds;                    // A stages: ra + j BM 64
+  bf16* const rb = lds + 3 * BM * 64;      // B stages: rb + j BN 64
+  constexpr int NA = DmaPlan<BM, TA>::NB;  // A loads per wave and slice
+  pa.issue(kbeg, ra, wave);
+  pb.issue(kbeg, rb, wave);
+  if (nsl > 1) pa.issue(kbeg + BK, ra + BM * 64, wave);
+  // The second half slice's products are carried over the next barrier:
+  // its fragments are read before it, and its MFMAs cover the latency of
+  // the next slice's first reads (every wave reads at the same moment,
+  // right after the barrier).
+  auto rd = [&](bf16x8_t (&a)[TMI], bf16x8_t (&b)[TNJ], const bf16* As, const bf16* Bs,
+                int kk) {
+#pragma unroll
+    for (int j = 0; j < TNJ; ++j) b[j] = frag<BN, TB>(Bs, wn + 16 * j, kk, lane);
+#pragma unroll
+    for (int i = 0; i < TMI; ++i) a[i] = frag<BM, TA>(As, wm + 16 * i, kk, lane);
+  };
+  auto mm = [&](const bf16x8_t (&a)[TMI], const bf16x8_t (&b)[TNJ]) {
+#pragma unroll
+    for (int i = 0; i < TMI; ++i)
+#pragma unroll
+      for (int j = 0; j < TNJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+  };
+  bf16x8_t fa[TMI], fb[TNJ], ga[TMI], gb[TNJ];   // first / second half slice
+  int sa = 0, sb = 0;                      // stages of slice `it`
+  for (; it < nsl; ++it) {
+    if (it + 1 < nsl) dma_wait_n<NA>();
+    else dma_wait();
+    __syncthreads();
+    if constexpr (EPI == E_CEB)
+      if ((it & 3) == 0 && (it >> 2) + 1 < ntv) cb_issue((it >> 2) + 1);
+    const int sa2 = sa == 0 ? 2 : sa - 1;  // (it + 2) % 3
+    if (it + 1 < nsl) pb.issue(kbeg + (int64_t)(it + 1) * BK, rb + (sb ^ 1) * BN * 64, wave);
+    if (it + 2 < nsl) pa.issue(kbeg + (int64_t)(it + 2) * BK, ra + sa2 * BM * 64, wave);
+    const bf16* As = ra + sa * BM * 64;
+    const bf16* Bs = rb + sb * BN * 64;
+    rd(fa, fb, As, Bs, 0);
+    if (it > 0) mm(ga, gb);                // slice it - 1, second half
+    if constexpr (EPI == E_CEB) {
+      if ((it & 3) == 0) {                 // a 256-wide vocabulary tile starts
+        const int t = it >> 2;
+        const float* mx = cb_lds + 256 * (1 + (t & 1)) + wm + (lane & 15);
+        if (t == 0) {
+#pragma unroll
+          for (int i = 0; i < TMI; ++i) cb_lse[i] = cb_lds[wm + 16 * i + (lane & 15)];
+        }
+#pragma unroll
+        for (int i = 0; i < TMI; ++i) {
+          const float mt = fmaxf(mx[16 * i], cb_lse[i] - 40.f);
+          if (t > 0) {                       // the accumulator is zero at t = 0
+            const float f = __builtin_amdgcn_exp2f((cb_m[i] - mt) * 1.4426950408889634f);
+#pragma unroll
+            for (int j = 0; j < TNJ; ++j) acc[i][j] *= f;
+          }
+          cb_m[i] = mt;
+        }
       }
-    };
-    for (; it < nsl; it += 4) {
-      next(it + 1, st1);
-      const int t = it >> 2;
-#pragma unroll
-      for (int i = 0; i < TMI; ++i) {
-        const float mt = fmaxf(cb_next[i], cb_lse[i] - 40.f);
-        cb_f[i] = __builtin_amdgcn_exp2f((cb_m[i] - mt) * 1.4426950408889634f);
-        cb_m[i] = mt;
-        if (t + 1 < ntv) cb_next[i] = cb_stat(i, t + 1);
-      }
-      compute(st0, std::true_type());
-      next(it + 2, st0);
-      compute(st1, plain);
-      next(it + 3, st1);
-      compute(st0, plain);
-      next(it + 4, st0);
-      compute(st1, plain);
     }
-  } else {
-    // A ring of three, B ring of two: A (the activations or gradients, the
-    // operand that streams from HBM) is fetched two slices ahead, B one.
-    // Per slice: wait until only A(s + 1) is in flight (loads land in issue
-    // order and A(s + 1) went out after B(s)), barrier (every wave is done
-    // with slice s - 1, whose A and B stages the next loads reuse), issue
-    // B(s + 1) then A(s + 2), multiply slice s.
-    bf16* const ra = lds;                    // A stages: ra + j BM 64
-    bf16* const rb = lds + 3 * BM * 64;      // B stages: rb + j BN 64
-    constexpr int NA = DmaPlan<BM, TA>::NB;  // A loads per wave and slice
-    pa.issue(kbeg, ra, wave);
-    pb.issue(kbeg, rb, wave);
-    if (nsl > 1) pa.issue(kbeg + BK, ra + BM * 64, wave);
-    // The second half slice's products are carried over the next barrier:
-    // its fragments are read before it, and its MFMAs cover the latency of
-    // the next slice's first reads (every wave reads at the same moment,
-    // right after the barrier).
-    auto rd = [&](bf16x8_t (&a)[TMI], bf16x8_t (&b)[TNJ], const bf16* As, const bf16* Bs,
-                  int kk) {
-#pragma unroll
-      for (int j = 0; j < TNJ; ++j) b[j] = frag<BN, TB>(Bs, wn + 16 * j, kk, lane);
-#pragma unroll
-      for (int i = 0; i < TMI; ++i) a[i] = frag<BM, TA>(As, wm + 16 * i, kk, lane);
-    };
-    auto mm = [&](const bf16x8_t (&a)[TMI], const bf16x8_t (&b)[TNJ]) {
-#pragma unroll
-      for (int i = 0; i < TMI; ++i)
-#pragma unroll
-        for (int j = 0; j < TNJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-    };
-    bf16x8_t fa[TMI], fb[TNJ], ga[TMI], gb[TNJ];   // first / second half slice
-    int sa = 0, sb = 0;                      // stages of slice `it`
-    for (; it < nsl; ++it) {
-      if (it + 1 < nsl) dma_wait_n<NA>();
-      else dma_wait();
-      __syncthreads();
-      const int sa2 = sa == 0 ? 2 : sa - 1;  // (it + 2) % 3
-      if (it + 1 < nsl) pb.issue(kbeg + (int64_t)(it + 1) * BK, rb + (sb ^ 1) * BN * 64, wave);
-      if (it + 2 < nsl) pa.issue(kbeg + (int64_t)(it + 2) * BK, ra + sa2 * BM * 64, wave);
-      const bf16* As = ra + sa * BM * 64;
-      const bf16* Bs = rb + sb * BN * 64;
-      rd(fa, fb, As, Bs, 0);
-      if (it > 0) mm(ga, gb);                // slice it - 1, second half
-      mm(fa, fb);
-      rd(ga, gb, As, Bs, 32);
-      sa = sa == 2 ? 0 : sa + 1;
-      sb ^= 1;
-    }
-    if (nsl > 0) mm(ga, gb);
+    mm(fa, fb);
+    rd(ga, gb, As, Bs, 32);
+    sa = sa == 2 ? 0 : sa + 1;
+    sb ^= 1;
   }
-
+  if (nsl > 0) mm(ga, gb);
   const int cq = (lane >> 4) * 4, lr = lane & 15;
   if constexpr (EPI == E_CE) {
     // Fused lm_head + cross-entropy, first half (the tile is 256 x 256 and
@@ -1116,7 +1068,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
 // of its row (the 16-byte chunks g and g + 4, the same k positions for
 // both operands, so their products pair up whatever order the instruction
 // sums them in).  FA / FB: 0 = e4m3, 1 = e5m2.  Twice the bf16 rate per
-// instruction and half the bytes per k.
+// instruction and half the bytes per k.  The stages form the bf16 kernel's
+// rings: three A stages fetched two slices ahead, two B stages one ahead.
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 template <int R>
@@ -1142,8 +1095,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(int64_t M, int64_t N, int64
   constexpr int BM = 256;
   constexpr int WM = BM / 4, WN = BN / 2;
   constexpr int TMI = WM / 16, TNJ = WN / 16;
-  __shared__ __attribute__((aligned(1024))) bf16 st0[(BM + BN) * 64];
-  __shared__ __attribute__((aligned(1024))) bf16 st1[(BM + BN) * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 lds[(3 * BM + 2 * BN) * 64];
 
   const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
   const int per_xcd = (nb + 7) / 8;
@@ -1172,9 +1124,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(int64_t M, int64_t N, int64
 #pragma unroll
     for (int j = 0; j < TNJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const bf16* st) {
-    const bf16* As = st;
-    const bf16* Bs = st + BM * 64;
+  auto compute = [&](const bf16* As, const bf16* Bs) {
     i32x8_t a[TMI], b[TNJ];
 #pragma unroll
     for (int j = 0; j < TNJ; ++j) b[j] = frag_f8<BN>(Bs, wn + 16 * j, lane);
@@ -1188,28 +1138,27 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8(int64_t M, int64_t N, int64
                                                                      0, 0, 0, 0);
   };
 
+  // per slice: wait until only A(s + 1) is in flight (loads land in issue
+  // order), barrier (every wave is done with slice s - 1, whose stages the
+  // next loads reuse), issue B(s + 1) then A(s + 2), multiply slice s
   const int nsl = (int)((kend - kbeg) / BK);
-  pa.issue(kbeg, st0, wave);
-  pb.issue(kbeg, st0 + BM * 64, wave);
-  int it = 0;
-  for (; it + 2 <= nsl; it += 2) {
-    dma_wait();
+  bf16* const ra = lds;                    // A stages: ra + j BM 64
+  bf16* const rb = lds + 3 * BM * 64;      // B stages: rb + j BN 64
+  constexpr int NA = DmaPlan<BM, false>::NB;
+  pa.issue(kbeg, ra, wave);
+  pb.issue(kbeg, rb, wave);
+  if (nsl > 1) pa.issue(kbeg + BK, ra + BM * 64, wave);
+  int sa = 0, sb = 0;
+  for (int it = 0; it < nsl; ++it) {
+    if (it + 1 < nsl) dma_wait_n<NA>();
+    else dma_wait();
     __syncthreads();
-    pa.issue(kbeg + (int64_t)(it + 1) * BK, st1, wave);
-    pb.issue(kbeg + (int64_t)(it + 1) * BK, st1 + BM * 64, wave);
-    compute(st0);
-    dma_wait();
-    __syncthreads();
-    if (it + 2 < nsl) {
-      pa.issue(kbeg + (int64_t)(it + 2) * BK, st0, wave);
-      pb.issue(kbeg + (int64_t)(it + 2) * BK, st0 + BM * 64, wave);
-    }
-    compute(st1);
-  }
-  if (it < nsl) {
-    dma_wait();
-    __syncthreads();
-    compute(st0);
+    const int sa2 = sa == 0 ? 2 : sa - 1;  // (it + 2) % 3
+    if (it + 1 < nsl) pb.issue(kbeg + (int64_t)(it + 1) * BK, rb + (sb ^ 1) * BN * 64, wave);
+    if (it + 2 < nsl) pa.issue(kbeg + (int64_t)(it + 2) * BK, ra + sa2 * BM * 64, wave);
+    compute(ra + sa * BM * 64, rb + sb * BN * 64);
+    sa = sa == 2 ? 0 : sa + 1;
+    sb ^= 1;
   }
   const float sc = a_inv[0] * b_inv[0];
 #pragma unroll
