@@ -13,6 +13,18 @@ unit stands for on this part.  The summary gives the per-kernel time table,
 the kernel's counters per dispatch and, on a line starting `traffic-json:`,
 its calibrated HBM bytes per launch with a hash of the kernel's sources;
 bench.py reports that traffic only while the sources still hash the same.
+
+    python rocprof_summary.py --table --bench-json FILE --fetch DIR --write DIR
+        --cal-fetch DIR --cal-write DIR --mfma DIR [--mops COUNTER]
+        [--marker KERNEL] [--peak TFLOPS] --out profiles/<file>.md
+
+--table writes one row per kernel of the bench line's `kernels` list (launch
+times from the library's HIP events): its measured HBM bytes per launch and
+the rate they give against 8 TB/s, and from a `rocprofv3 --pmc MfmaUtil
+<mops counter>` run the fraction of SIMD cycles its matrix cores were busy
+and the MFMA rate the op counter gives (512 flops per unit) against the
+dtype's peak.  With --marker only the dispatches between the second and the
+third launch of that kernel (one timed step) are counted.
 """
 from __future__ import annotations
 
@@ -114,6 +126,74 @@ def read_counter(d: str, counter: str):
     return out
 
 
+def read_dispatches(d: str, marker: str | None):
+    """[(short kernel name, {counter: value})] in dispatch order; with a
+    marker, only the dispatches from its second launch up to its third."""
+    by_id = {}
+    with open(_one(d, "*counter_collection.csv")) as fh:
+        for r in csv.DictReader(fh):
+            e = by_id.setdefault(int(r["Dispatch_Id"]), (short_name(r["Kernel_Name"]), {}))
+            e[1][r["Counter_Name"]] = float(r["Counter_Value"])
+    seq = [by_id[i] for i in sorted(by_id)]
+    if marker:
+        at = [i for i, (n, _) in enumerate(seq) if n == marker]
+        if len(at) < 3:
+            raise SystemExit(f"{marker} launched {len(at)} times in {d}")
+        seq = seq[at[1]:at[2]]
+    return seq
+
+
+def per_kernel_mean(seq, counter: str):
+    acc = {}
+    for n, c in seq:
+        if counter in c:
+            acc.setdefault(n, []).append(c[counter])
+    return {n: sum(v) / len(v) for n, v in acc.items()}
+
+
+def step_table(a):
+    with open(a.bench_json) as fh:
+        bench = json.loads([l for l in fh if l.startswith("{")][-1])
+    ff = copy_factor(a.cal_fetch, "FETCH_SIZE")[0]
+    wf = copy_factor(a.cal_write, "WRITE_SIZE")[0]
+    fetch = per_kernel_mean(read_dispatches(a.fetch, a.marker), "FETCH_SIZE")
+    write = per_kernel_mean(read_dispatches(a.write, a.marker), "WRITE_SIZE")
+    mseq = read_dispatches(a.mfma, a.marker)
+    util = per_kernel_mean(mseq, "MfmaUtil")
+    mops = per_kernel_mean(mseq, a.mops)
+    L = [f"# {a.title}", ""]
+    if a.cmd:
+        L += ["Commands (run from the repository root; rocprofv3 after "
+              "`cd /tmp && export TMPDIR=/tmp`, paths shortened):", ""]
+        L += [f"    {c}" for c in a.cmd] + [""]
+    L += [f"Launch times: the library's HIP events over the bench line's profiled steps "
+          f"({bench['config'].get('workload')}). HBM: calibrated FETCH_SIZE + WRITE_SIZE per "
+          f"dispatch (factors {ff:.4f} and {wf:.4f} bytes per counted byte) over the launch "
+          f"time, against 8 TB/s. MFMA busy: `MfmaUtil`, the matrix cores' busy cycles over "
+          f"the SIMD cycles of the dispatch. MFMA rate: `{a.mops}` x 512 flops over the launch "
+          f"time, against {a.peak:.0f} TFLOP/s; it counts every MFMA issued, recomputed "
+          f"products included, while the algorithmic rate counts each result once.", "",
+          "| kernel | launches / step | us / launch | algorithmic rate | HBM MB / launch "
+          "| HBM GB/s (of 8 TB/s) | MFMA busy | MFMA TFLOP/s (of peak) |",
+          "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for k in bench["kernels"][:a.top]:
+        n, t = k["kernel"], k["avg_launch_ms"] / 1e3
+        alg = (f"{k['tflops']:.0f} TFLOP/s" if k.get("tflops") else
+               f"{k['gbps']:.0f} GB/s" if k.get("gbps") else "")
+        hbm = ((fetch[n] * ff + write[n] * wf) * 1024 if n in fetch and n in write else None)
+        hb = f"{hbm / 1e6:.1f}" if hbm is not None else ""
+        hr = f"{hbm / t / 1e9:.0f} ({hbm / t / 8e12:.0%})" if hbm is not None else ""
+        mu = f"{util[n]:.1f}%" if n in util else ""
+        mr = (f"{mops[n] * 512 / t / 1e12:.0f} ({mops[n] * 512 / t / 1e12 / a.peak:.0%})"
+              if mops.get(n) else "")
+        L.append(f"| `{n}` | {k['launches_per_step']:.0f} | {t * 1e6:.1f} | {alg} | {hb} | {hr} "
+                 f"| {mu} | {mr} |")
+    L.append("")
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(L))
+    print(a.out)
+
+
 def copy_factor(d: str, counter: str):
     """Bytes per counter KiB unit, from the 1 GiB copy: the largest dispatch
     of the calibration run is the copy."""
@@ -124,8 +204,13 @@ def copy_factor(d: str, counter: str):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--kernel", required=True)
-    ap.add_argument("--stats", required=True)
+    ap.add_argument("--table", action="store_true")
+    ap.add_argument("--mfma")
+    ap.add_argument("--mops", default="SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    ap.add_argument("--marker")
+    ap.add_argument("--peak", type=float, default=2500.0)
+    ap.add_argument("--kernel")
+    ap.add_argument("--stats")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--cal-fetch")
@@ -136,6 +221,10 @@ def main():
     ap.add_argument("--top", type=int, default=25)
     ap.add_argument("--out", required=True)
     a = ap.parse_args()
+    if a.table:
+        return step_table(a)
+    if not (a.kernel and a.stats):
+        ap.error("--kernel and --stats are required without --table")
 
     stats = read_stats(a.stats)
     tot = sum(r["total_ns"] for r in stats)

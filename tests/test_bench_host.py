@@ -64,3 +64,27 @@ def test_clock_parsing_and_host_info():
     assert bench.parse_sclk("0: 500Mhz\n1: 2400Mhz\n") is None
     info = bench.host_cpu_info()
     assert info["cores"] >= 1 and "blas_threads" in info
+
+
+def test_counter_table_takes_one_step_between_markers(tmp_path):
+    """--table counts the dispatches from the marker kernel's second launch
+    up to its third (one timed step), one value per dispatch and counter,
+    averaged per kernel."""
+    import csv
+    d = tmp_path / "run"
+    d.mkdir()
+    seq = [("k_embed", 1.0), ("k_a", 10.0), ("k_b", 5.0),      # warm-up step
+           ("k_embed", 2.0), ("k_a", 20.0), ("k_a", 40.0), ("k_b", 7.0),   # timed step
+           ("k_embed", 3.0), ("k_a", 99.0)]                   # next step
+    with open(d / "p_counter_collection.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, (k, v) in enumerate(seq, start=1):
+            name = f"void gk::{k}(int)"
+            w.writerow([i, name, "MfmaUtil", v])
+            w.writerow([i, name, "FETCH_SIZE", 2 * v])
+    steps = R.read_dispatches(str(d), "k_embed")
+    assert [n for n, _ in steps] == ["k_embed", "k_a", "k_a", "k_b"]
+    assert R.per_kernel_mean(steps, "MfmaUtil") == {"k_embed": 2.0, "k_a": 30.0, "k_b": 7.0}
+    assert R.per_kernel_mean(steps, "FETCH_SIZE")["k_a"] == 60.0
+    assert len(R.read_dispatches(str(d), None)) == len(seq)
