@@ -279,9 +279,13 @@ __device__ __forceinline__ void mma_slice(const bf16* As, const bf16* Bs, int wm
 struct TileMap {
   int tiles_m, tiles_n, splits;
   int64_t k_per_split;     // multiple of BK
-  // batched products (k_gemm_mfma only, blockIdx.y = batch index): element
-  // strides between the batch's A, B and C matrices
+  // batched products: element strides between the batch's A, B and C
+  // matrices.  k_gemm_mfma takes the batch index from blockIdx.y;
+  // k_gemm_dma, when batch > 1, from a 1-D grid over batch x tiles numbered
+  // like its tiles (each XCD a contiguous run, so the tiles of one matrix
+  // share at most two L2s)
   int64_t bs_a = 0, bs_b = 0, bs_c = 0;
+  int batch = 0;
   // E_CE only: per-(row, column tile) stats, target logits, token rows
   float* ce_stats = nullptr;
   float* ce_zt = nullptr;
@@ -689,17 +693,22 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
   // the tile's 256 rows' lse and two slots of their vocabulary-tile maxima
   constexpr int SX = EPI == E_CEB ? 3 * 256 * 2 : 0;
   __shared__ __attribute__((aligned(1024))) bf16 lds[(3 * BM + 2 * BN) * 64 + SX];
-  if (blockIdx.y) {
-    constexpr int ce = (EPI == E_F32 || EPI == E_F32_ACC) ? 4 : 2;
-    A += blockIdx.y * tm.bs_a;
-    B += blockIdx.y * tm.bs_b;
-    C = (char*)C + blockIdx.y * tm.bs_c * ce;
-  }
-
-  const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
+  const int nb1 = tm.tiles_m * tm.tiles_n * tm.splits;
+  const int nb = tm.batch > 1 ? nb1 * tm.batch : nb1;
   const int per_xcd = (nb + 7) / 8;
-  const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
   if (logical >= nb) return;
+  int bz = (int)blockIdx.y;
+  if (tm.batch > 1) {
+    bz = logical / nb1;
+    logical -= bz * nb1;
+  }
+  if (bz) {
+    constexpr int ce = (EPI == E_F32 || EPI == E_F32_ACC) ? 4 : 2;
+    A += bz * tm.bs_a;
+    B += bz * tm.bs_b;
+    C = (char*)C + bz * tm.bs_c * ce;
+  }
   const int ntile = tm.tiles_m * tm.tiles_n;
   const int split = logical / ntile;
   const int t = logical % ntile;
@@ -1670,8 +1679,9 @@ hipError_t gemm_batched(const GemmDesc& g, int batch, int64_t sa, int64_t sb, in
     tm.bs_a = sa;
     tm.bs_b = sb;
     tm.bs_c = sc;
-    const int nb = tm.tiles_m * tm.tiles_n;
-    const dim3 grid(((nb + 7) / 8) * 8, batch);
+    tm.batch = batch;
+    const int64_t nb = (int64_t)tm.tiles_m * tm.tiles_n * batch;
+    const dim3 grid((unsigned)(((nb + 7) / 8) * 8));
     Work w = gemm_work(g);
     w.flops *= batch;
     w.bytes *= batch;

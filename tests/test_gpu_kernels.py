@@ -810,11 +810,14 @@ NS_CLASSIC = (3.4445, -4.7750, 2.0315)
 @pytest.mark.parametrize("dt", [G.F32, G.BF16])
 @pytest.mark.parametrize("m,n,steps,batch", [(64, 32, 2, 1), (32, 96, 2, 3), (768, 768, 5, 2),
                                              (2304, 768, 5, 1), (768, 3072, 5, 2),
-                                             (136, 72, 0, 2), (72, 136, 1, 1)])
+                                             (136, 72, 0, 2), (72, 136, 1, 1),
+                                             (2304, 768, 5, 12), (768, 3072, 5, 12)])
 def test_polar_express(m, n, steps, batch, dt):
     """The orthogonalized updates of a batch of matrices against the
     oracle's bf16 Gram-matrix form and against the exact result (the SVD
-    definition), each matrix on its own.  Tuples: the
+    definition), each matrix on its own.  The batches of 12 d12 matrices
+    run the polynomial products on the direct-to-LDS kernel, whose grid
+    numbers (matrix, tile) pairs per XCD.  Tuples: the
     page's two, or the classic quintic tuple five times (a convergent
     schedule: the page's two tuples expect the three elided ones after
     them)."""
