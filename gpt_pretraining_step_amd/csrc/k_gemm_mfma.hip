@@ -280,10 +280,10 @@ struct TileMap {
   int tiles_m, tiles_n, splits;
   int64_t k_per_split;     // multiple of BK
   // batched products: element strides between the batch's A, B and C
-  // matrices.  k_gemm_mfma takes the batch index from blockIdx.y;
-  // k_gemm_dma, when batch > 1, from a 1-D grid over batch x tiles numbered
-  // like its tiles (each XCD a contiguous run, so the tiles of one matrix
-  // share at most two L2s)
+  // matrices; when batch > 1 the batch index comes from a 1-D grid over
+  // batch x tiles numbered like a product's tiles (each XCD a contiguous
+  // run, so the tiles of one matrix share at most two L2s), else from
+  // blockIdx.y
   int64_t bs_a = 0, bs_b = 0, bs_c = 0;
   int batch = 0;
   // E_CE only: per-(row, column tile) stats, target logits, token rows
@@ -346,18 +346,24 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(int64_t M, int64_t N, int6
   constexpr int TMI = WM / 16, TNJ = WN / 16;
   __shared__ __attribute__((aligned(16))) bf16 As[BM * LDK];
   __shared__ __attribute__((aligned(16))) bf16 Bs[BN * LDK];
-  if (blockIdx.y) {
-    constexpr int ce = (EPI == E_F32 || EPI == E_F32_ACC) ? 4 : 2;
-    A += blockIdx.y * tm.bs_a;
-    B += blockIdx.y * tm.bs_b;
-    C = (char*)C + blockIdx.y * tm.bs_c * ce;
-  }
-
-  // ---- which tile: XCD-contiguous numbering, then grouped column-major
-  const int nb = tm.tiles_m * tm.tiles_n * tm.splits;
+  // ---- which tile: XCD-contiguous numbering (of (matrix, tile) pairs when
+  // batched), then grouped column-major
+  const int nb1 = tm.tiles_m * tm.tiles_n * tm.splits;
+  const int nb = tm.batch > 1 ? nb1 * tm.batch : nb1;
   const int per_xcd = (nb + 7) / 8;
-  const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
   if (logical >= nb) return;
+  int bz = (int)blockIdx.y;
+  if (tm.batch > 1) {
+    bz = logical / nb1;
+    logical -= bz * nb1;
+  }
+  if (bz) {
+    constexpr int ce = (EPI == E_F32 || EPI == E_F32_ACC) ? 4 : 2;
+    A += bz * tm.bs_a;
+    B += bz * tm.bs_b;
+    C = (char*)C + bz * tm.bs_c * ce;
+  }
   const int ntile = tm.tiles_m * tm.tiles_n;
   const int split = logical / ntile;
   const int t = logical % ntile;
@@ -1635,15 +1641,15 @@ hipError_t gemm_fp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 namespace gk {
 
 template <int BM, int BN, bool TA, bool TB, int EPI>
-static void launch_batched_t(const GemmDesc& g, const TileMap& tm, int batch, hipStream_t s) {
-  const int nb = tm.tiles_m * tm.tiles_n;
-  const int grid = ((nb + 7) / 8) * 8;
+static void launch_batched_t(const GemmDesc& g, TileMap tm, int batch, hipStream_t s) {
+  tm.batch = batch;
+  const int64_t nb = (int64_t)tm.tiles_m * tm.tiles_n * batch;
+  const int grid = (int)(((nb + 7) / 8) * 8);
   Work w = gemm_work(g);
   w.flops *= batch;
   w.bytes *= batch;
-  GK_LAUNCH(w, (k_gemm_mfma<BM, BN, TA, TB, EPI>), dim3(grid, batch), dim3(256), 0, s, g.M, g.N,
-            g.K, (const bf16*)g.A, g.lda, (const bf16*)g.B, g.ldb, g.C, g.ldc, nullptr, tm,
-            nullptr);
+  GK_LAUNCH(w, (k_gemm_mfma<BM, BN, TA, TB, EPI>), dim3(grid), dim3(256), 0, s, g.M, g.N, g.K,
+            (const bf16*)g.A, g.lda, (const bf16*)g.B, g.ldb, g.C, g.ldc, nullptr, tm, nullptr);
 }
 
 template <int BM, int BN, int EPI>
