@@ -889,9 +889,10 @@ def eval_batch_rows(cfg, n_rows):
     return max(cfg["batch"], min(n_rows, EVAL_BATCH_TOKENS // cfg["seq_len"]))
 
 
-def eval_set_line(name, torch, G, gi, Session):
+def eval_set_line(name, torch, G, gi, Session, iters=2):
     """Evaluation tokens/s and bpb of a preset over its whole evaluation set
-    (one gpt_eval_bpb call, timed with events; one warm-up call)."""
+    (gpt_eval_bpb calls over the set, `iters` of them timed with events
+    after one warm-up call)."""
     cfg = gi.preset(name)
     _, eval_fpt, _ = model_flops(cfg)
     n_rows = cfg["eval_rows"]
@@ -904,7 +905,7 @@ def eval_set_line(name, torch, G, gi, Session):
     tb = s.upload(gi.make_token_bytes(cfg))
     s.evaluate(tok, tb)
     torch.cuda.synchronize()
-    t = time_events(lambda: s.evaluate(tok, tb), 2, torch)
+    t = time_events(lambda: s.evaluate(tok, tb), iters, torch)
     targets = n_rows * cfg["seq_len"]
     bpb = s.bpb.cpu().numpy().tolist()
     log(f"{name} eval over {targets} targets: {targets / t:,.0f} tok/s, bpb {bpb[2]:.4f}")
@@ -931,7 +932,8 @@ def main():
                     help="also time every product / attention shape alone")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-gqa-eval", action="store_true",
-                    help="train: skip the d12-GQA 2^21-target evaluation line")
+                    help="train: skip the evaluation-set lines (d12-GQA over 2^21 targets, "
+                         "d24 over 2^22)")
     ap.add_argument("--one-stream", action="store_true",
                     help="train: the whole step on one stream (no second stream for the "
                          "weight-gradient work); optim: every Muon group on one stream")
@@ -1081,9 +1083,11 @@ def main():
     torch.cuda.empty_cache()
     # the long-context workload's evaluation: d12-GQA over its whole 2^21-
     # target set (512 rows x 4096), a separate model of that shape
-    gqa = None
+    gqa = d24 = None
     if not a.model_extras and a.config == "d12" and not a.no_gqa_eval:
         gqa = eval_set_line("d12gqa", torch, G, gi, Session)
+        # and d24's 2^22-target set (about 7 s a pass: one timed pass)
+        d24 = eval_set_line("d24", torch, G, gi, Session, iters=1)
 
     # per-kernel split of the step with the library's launch recording, the
     # step on one stream (a kernel's time then carries no overlap with the
@@ -1145,7 +1149,7 @@ def main():
         "eval_tokens_per_s": round(eval_tok_s, 1), "eval_rows": ev_rows,
         "eval_batch_rows": ev_batch, "eval_bpb": bpb[2],
         "eval_mfu_bf16": round(eval_tok_s * eval_fpt / PEAK_BF16, 4),
-        "eval_d12gqa_2m": gqa,
+        "eval_d12gqa_2m": gqa, "eval_d24_4m": d24,
         "context": {
             "autoresearch_5min_budget": {
                 "d12_steps_in_300s": int(300.0 / (ms / 1e3)),
