@@ -15,7 +15,7 @@ its calibrated HBM bytes per launch with a hash of the kernel's sources;
 bench.py reports that traffic only while the sources still hash the same.
 
     python rocprof_summary.py --table --bench-json FILE --fetch DIR --write DIR
-        --cal-fetch DIR --cal-write DIR --mfma DIR [--mops COUNTER]
+        --cal-fetch DIR --cal-write DIR --mfma DIR [--mops COUNTER] [--waits DIR]
         [--marker KERNEL] [--peak TFLOPS] --out profiles/<file>.md
 
 --table writes one row per kernel of the bench line's `kernels` list (launch
@@ -23,8 +23,10 @@ times from the library's HIP events): its measured HBM bytes per launch and
 the rate they give against 8 TB/s, and from a `rocprofv3 --pmc MfmaUtil
 <mops counter>` run the fraction of SIMD cycles its matrix cores were busy
 and the MFMA rate the op counter gives (512 flops per unit) against the
-dtype's peak.  With --marker only the dispatches between the second and the
-third launch of that kernel (one timed step) are counted.
+dtype's peak; with --waits, from a run of the SQ wait counters, the share of
+the waves' cycles spent waiting for data or barriers, for an issue slot and
+for an LDS issue slot.  With --marker only the dispatches between the second
+and the third launch of that kernel (one timed step) are counted.
 """
 from __future__ import annotations
 
@@ -161,6 +163,12 @@ def step_table(a):
     mseq = read_dispatches(a.mfma, a.marker)
     util = per_kernel_mean(mseq, "MfmaUtil")
     mops = per_kernel_mean(mseq, a.mops)
+    waits = None
+    if a.waits:
+        wseq = read_dispatches(a.waits, a.marker)
+        waits = {c: per_kernel_mean(wseq, c) for c in
+                 ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS",
+                  "SQ_LDS_BANK_CONFLICT")}
     L = [f"# {a.title}", ""]
     if a.cmd:
         L += ["Commands (run from the repository root; rocprofv3 after "
@@ -174,8 +182,15 @@ def step_table(a):
           f"time, against {a.peak:.0f} TFLOP/s; it counts every MFMA issued, recomputed "
           f"products included, while the algorithmic rate counts each result once.", "",
           "| kernel | launches / step | us / launch | algorithmic rate | HBM MB / launch "
-          "| HBM GB/s (of 8 TB/s) | MFMA busy | MFMA TFLOP/s (of peak) |",
-          "|---|---:|---:|---:|---:|---:|---:|---:|"]
+          "| HBM GB/s (of 8 TB/s) | MFMA busy | MFMA TFLOP/s (of peak) |"
+          + (" wait: data / issue / LDS issue | LDS bank conflicts |" if waits else ""),
+          "|---|---:|---:|---:|---:|---:|---:|---:|" + ("---:|---:|" if waits else "")]
+    if waits:
+        L[-3:-3] = [f"Waits (a run of `rocprofv3 --pmc SQ_WAVE_CYCLES SQ_WAIT_ANY "
+                    f"SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT ...`): the "
+                    f"fractions of the waves' cycles spent waiting for anything (data, "
+                    f"barriers), for an instruction issue slot, and for an LDS issue slot; "
+                    f"bank conflicts in cycles per dispatch.", ""]
     for k in bench["kernels"][:a.top]:
         n, t = k["kernel"], k["avg_launch_ms"] / 1e3
         alg = (f"{k['tflops']:.0f} TFLOP/s" if k.get("tflops") else
@@ -186,8 +201,17 @@ def step_table(a):
         mu = f"{util[n]:.1f}%" if n in util else ""
         mr = (f"{mops[n] * 512 / t / 1e12:.0f} ({mops[n] * 512 / t / 1e12 / a.peak:.0%})"
               if mops.get(n) else "")
-        L.append(f"| `{n}` | {k['launches_per_step']:.0f} | {t * 1e6:.1f} | {alg} | {hb} | {hr} "
-                 f"| {mu} | {mr} |")
+        row = (f"| `{n}` | {k['launches_per_step']:.0f} | {t * 1e6:.1f} | {alg} | {hb} | {hr} "
+               f"| {mu} | {mr} |")
+        if waits:
+            wc = waits["SQ_WAVE_CYCLES"].get(n)
+            if wc:
+                f = lambda c: waits[c].get(n, 0.0) / wc
+                row += (f" {f('SQ_WAIT_ANY'):.0%} / {f('SQ_WAIT_INST_ANY'):.0%} / "
+                        f"{f('SQ_WAIT_INST_LDS'):.1%} | {waits['SQ_LDS_BANK_CONFLICT'].get(n, 0):.0f} |")
+            else:
+                row += " | |"
+        L.append(row)
     L.append("")
     with open(a.out, "w") as fh:
         fh.write("\n".join(L))
@@ -206,6 +230,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--table", action="store_true")
     ap.add_argument("--mfma")
+    ap.add_argument("--waits")
     ap.add_argument("--mops", default="SQ_INSTS_VALU_MFMA_MOPS_BF16")
     ap.add_argument("--marker")
     ap.add_argument("--peak", type=float, default=2500.0)
