@@ -744,18 +744,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_dma(int64_t M, int64_t N, int64
   // - m'_t) when a tile starts.  Every m' lies in [lse - 40, lse], so the
   // factors stay within e^(+-40); a tile whose max is more than 40 below
   // lse counts as if it were 40 below, a change far under bf16 resolution
-  // (its true weight is below e^-40).  The next tile's m_t is fetched a
-  // tile ahead.  The factors of a tile are applied after the carried
-  // products of the previous tile's last slice and before the tile's own
-  // first products.
-  // The lse of the block's rows and each tile's maxima reach LDS by buffer
-  // loads issued ahead of a slice's operand loads (waves 0-3, one row a
-  // lane), so the per-slice waits cover them and no other load is in flight
-  // in the main loop: the maxima of tile t + 1 are fetched when tile t
-  // starts, into slot (t + 1) % 2.
+  // (its true weight is below e^-40).  The factors of a tile are applied
+  // after the carried products of the previous tile's last slice and
+  // before the tile's own first products.  The lse of the block's rows and
+  // each tile's maxima reach LDS by buffer loads (waves 0-3, one row a
+  // lane) issued ahead of a slice's operand loads, so the per-slice waits
+  // cover them and no other load is in flight in the main loop; the maxima
+  // of tile t + 1 are fetched when tile t starts.
   float cb_lse[TMI], cb_m[TMI];
   const int ntv = (int)(K >> 8);
-  float* const cb_lds = (float*)(lds + (3 * BM + 2 * BN) * 64);   // lse, slot 0, slot 1
+  // floats [0, 256): lse; [256, 512) and [512, 768): maxima of the even and
+  // the odd tiles
+  float* const cb_lds = (float*)(lds + (3 * BM + 2 * BN) * 64);
   // descriptors and the wave test are uniform (scalar registers, branch)
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const i32x4_t cb_rs = make_rsrc(EPI == E_CEB ? tm.ce_stats : nullptr, M * ntv * 8);
