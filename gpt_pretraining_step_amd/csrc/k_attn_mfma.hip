@@ -34,6 +34,7 @@ static constexpr int FQB = FWD_QW / 16;        // forward: 16-query blocks per w
 static constexpr int FWD_OCC = 2;              // forward: workgroups per CU (launch bound)
 static constexpr int FWD_BQ = NW * FWD_QW;     // forward: queries per workgroup
 static constexpr int DQ_BQ = NW * QW;          // backward dQ: queries per workgroup
+static constexpr bool kJointDKV = true;        // dK and dV in one pass (16 keys a wave)
 static constexpr float kLog2e = 1.4426950408889634f;
 static constexpr float kLn2 = 0.6931471805599453f;
 static constexpr float kLazy = 8.0f;           // forward: offset lag allowed (log2 units)
@@ -381,7 +382,7 @@ __device__ __forceinline__ void norm_rope_bwd_row(float (&x)[8][4], const bf16* 
   }
 }
 
-// dK, dV of 128 keys of one KV head (4 waves x 32 keys), summed over the G
+// dK, dV of 4 KPW keys of one KV head (4 waves x KPW keys), summed over the G
 // query heads of the group and every 64-query tile that sees these keys.
 // Scores are formed queries x keys (X = Q tile rows, Y = K in registers), so
 // each lane owns one key; a 64-query tile is taken in halves of 16 NQB
@@ -389,13 +390,13 @@ __device__ __forceinline__ void norm_rope_bwd_row(float (&x)[8][4], const bf16* 
 // and P and dS of a half feed dV^T += dO^T P and dK^T += Q^T dS from
 // registers, with the dO^T and Q^T fragments gathered by transposing LDS
 // reads.
-static constexpr int KV_BK = NW * 32;          // keys per workgroup
-
-// MODE: 0 = dK and dV together (one wave per SIMD: both accumulators and the
-// K and V fragments do not fit two), 1 = dK only, 2 = dV only (each fits two
-// waves per SIMD; dV needs no dP, Delta or Q^T, dK no dO^T).
-template <int NQB, int MODE, bool FUSE>
-__global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const bf16* __restrict__ qkv,
+// MODE: 0 = dK and dV together, 1 = dK only, 2 = dV only (dV needs no dP,
+// Delta or Q^T, dK no dO^T).  KPW: keys per wave, a multiple of 16.  At 32
+// keys a wave the joint pass needs one wave per SIMD (both accumulators
+// and the K and V fragments); at 16 it fits two, and S and P are formed
+// once for both results.
+template <int NQB, int MODE, bool FUSE, int KPW = 32>
+__global__ __launch_bounds__(256, (MODE == 0 && KPW > 16) ? 1 : 2) void k_attn_bwd_dkv(const bf16* __restrict__ qkv,
                                                          const bf16* __restrict__ dout,
                                                          const float* __restrict__ lse,
                                                          const float* __restrict__ delta,
@@ -404,6 +405,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
   __shared__ __attribute__((aligned(16))) bf16 qd[2][2][TR * HD];   // stages of (Q, dO)
   __shared__ __attribute__((aligned(16))) float ldl[2][2][256];      // stages of (lse, delta)
 
+  constexpr int KBN = KPW / 16, KV_BK = NW * KPW;   // key blocks per wave, keys per workgroup
   const int nkb = (T + KV_BK - 1) / KV_BK;
   int pair, kblk;
   if (!xcd_block(nkb, Hkv * B, pair, kblk)) return;
@@ -420,11 +422,11 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = lane >> 4, lr = lane & 15;
   const int k0 = kblk * KV_BK;
-  const int kw = k0 + 32 * wave;                      // this wave's first key
+  const int kw = k0 + KPW * wave;                     // this wave's first key
   const float sl2 = kLog2e / sqrtf((float)HD);
   constexpr bool DO_K = MODE != 2, DO_V = MODE != 1;
 
-  // queries that see keys [k0, k0+127]: [k0, k0 + 127 + W]
+  // queries that see keys [k0, k0 + KV_BK - 1]: [k0, k0 + KV_BK - 1 + W]
   const int qhi = (int)min((int64_t)T - 1, (int64_t)k0 + KV_BK - 1 + W);
   const int qt0 = k0 / TR, nqt = qhi / TR - qt0 + 1;
   const int iters = G * nqt;
@@ -445,9 +447,9 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
   };
   issue(0, 0);
 
-  bf16x8_t kf[2][4], vf[2][4];
+  bf16x8_t kf[KBN][4], vf[KBN][4];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < KBN; ++kb) {
     const int key = kw + 16 * kb + lr;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -460,11 +462,11 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
       }
     }
   }
-  f32x4_t dk[8][2], dv[8][2];
+  f32x4_t dk[8][KBN], dv[8][KBN];
 #pragma unroll
   for (int hb = 0; hb < 8; ++hb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KBN; ++kb) {
       dk[hb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       dv[hb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -483,19 +485,20 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
     const float* Dl = ldl[st][1];
 #pragma unroll
     for (int hq = 0; hq < 4 / NQB; ++hq) {
-      // pairs of this wave: queries [qa, qa + 16 NQB), keys [kw, kw+31]
+      // pairs of this wave: queries [qa, qa + 16 NQB), keys [kw, kw + KPW)
       const int qa = q0 + 16 * NQB * hq;
-      const bool any = (qa + 16 * NQB - 1 >= kw) && (qa - (kw + 31) <= W) && kw < T && qa < T;
-      const bool full = (qa >= kw + 31) && (qa + 16 * NQB - 1 - kw <= W);
+      const bool any =
+          (qa + 16 * NQB - 1 >= kw) && (qa - (kw + KPW - 1) <= W) && kw < T && qa < T;
+      const bool full = (qa >= kw + KPW - 1) && (qa + 16 * NQB - 1 - kw <= W);
       if (!any) continue;
-      f32x4_t s[NQB][2], dp[NQB][2];
+      f32x4_t s[NQB][KBN], dp[NQB][KBN];
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         const int row = 16 * NQB * hq + 16 * qb + lr;
         const bf16x8_t qx0 = dfrag_row(Qs, row, 0, g);
         const bf16x8_t dx0 = DO_K ? dfrag_row(Ds, row, 0, g) : qx0;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KBN; ++kb) {
           s[qb][kb] = mfma(qx0, kf[kb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
           if constexpr (DO_K) dp[qb][kb] = mfma(dx0, vf[kb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
         }
@@ -503,11 +506,11 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
         for (int ks = 1; ks < 4; ++ks) {
           const bf16x8_t qx = dfrag_row(Qs, row, ks, g);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) s[qb][kb] = mfma(qx, kf[kb][ks], s[qb][kb]);
+          for (int kb = 0; kb < KBN; ++kb) s[qb][kb] = mfma(qx, kf[kb][ks], s[qb][kb]);
           if constexpr (DO_K) {
             const bf16x8_t dx = dfrag_row(Ds, row, ks, g);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) dp[qb][kb] = mfma(dx, vf[kb][ks], dp[qb][kb]);
+            for (int kb = 0; kb < KBN; ++kb) dp[qb][kb] = mfma(dx, vf[kb][ks], dp[qb][kb]);
           }
         }
       }
@@ -516,7 +519,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < KBN; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int d = qa + 16 * qb + 4 * g + r - (kw + 16 * kb + lr);
@@ -531,7 +534,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
+          for (int kb = 0; kb < KBN; ++kb) {
             const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], sl2, -L2[r]));
             s[qb][kb][r] = p;
             if constexpr (DO_K) dp[qb][kb][r] = p * (dp[qb][kb][r] - Dq[r]);
@@ -543,7 +546,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
         const int ch = (NQB / 2) * hq + c;                 // 32-query chunk of the tile
         const int ka = 32 * ch + 4 * g, kb2 = 32 * ch + 16 + 4 * g;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KBN; ++kb) {
           if constexpr (DO_V) {
             const bf16x8_t pp = pack8(s[2 * c][kb], s[2 * c + 1][kb]);
 #pragma unroll
@@ -569,7 +572,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void k_attn_bwd_dkv(const b
   // lane holds dK^T / dV^T [16hb + 4g + r][key 16kb + lr]
   const float scale = 1.0f / sqrtf((float)HD);
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < KBN; ++kb) {
     const int key = kw + 16 * kb + lr;
     const bool ok = key < T;
     if constexpr (DO_K && FUSE) {          // every lane of the row takes part
@@ -819,7 +822,8 @@ hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const
   }
   // dK and dV in two passes (two waves per SIMD each; measured faster than
   // the one-wave-per-SIMD combined pass despite recomputing S)
-  const dim3 gkv = xcd_grid((T + KV_BK - 1) / KV_BK, Hkv * B);
+  const dim3 gkv = xcd_grid((T + NW * 32 - 1) / (NW * 32), Hkv * B);       // 32 keys a wave
+  const dim3 g16 = xcd_grid((T + NW * 16 - 1) / (NW * 16), Hkv * B);       // 16 keys a wave
   const Work wk(4.0 * HD * pairs, qkvo + stats + tok * Hkv * HD * 2);
   const Work wv(2.0 * HD * pairs, qkvo + stats / 2 + tok * Hkv * HD * 2);
   const dim3 gq = xcd_grid((T + DQ_BQ - 1) / DQ_BQ, H * B);
@@ -827,7 +831,11 @@ hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const
   // dK (the longest pass) on the caller's stream, dQ and dV beside it on
   // streams of their own (or dV after dQ): 0.1 ms per d12 step each against
   // dV after dK on the caller's stream, and against dV after dQ
-  if (fuse) {
+  const Work wkv(6.0 * HD * pairs, qkvo + stats + tok * Hkv * HD * 4);
+  if (fuse && kJointDKV) {
+    GK_LAUNCH(wq, k_attn_bwd_dq<true>, gq, dim3(NW * 64), 0, sq, DKV_ARGS);
+    GK_LAUNCH(wkv, (k_attn_bwd_dkv<2, 0, true, 16>), g16, dim3(NW * 64), 0, s, DKV_ARGS);
+  } else if (fuse) {
     GK_LAUNCH(wq, k_attn_bwd_dq<true>, gq, dim3(NW * 64), 0, sq, DKV_ARGS);
     GK_LAUNCH(wv, (k_attn_bwd_dkv<2, 2, false>), gkv, dim3(NW * 64), 0, sv, DKV_ARGS);
     GK_LAUNCH(wk, (k_attn_bwd_dkv<2, 1, true>), gkv, dim3(NW * 64), 0, s, DKV_ARGS);
