@@ -834,7 +834,7 @@ hipError_t attn_mfma_bwd(const void* qkv, const void* o, const float* lse, const
   const Work wkv(6.0 * HD * pairs, qkvo + stats + tok * Hkv * HD * 4);
   if (fuse && kJointDKV) {
     GK_LAUNCH(wq, k_attn_bwd_dq<true>, gq, dim3(NW * 64), 0, sq, DKV_ARGS);
-    GK_LAUNCH(wkv, (k_attn_bwd_dkv<2, 0, true, 16>), g16, dim3(NW * 64), 0, s, DKV_ARGS);
+    GK_LAUNCH(wkv, (k_attn_bwd_dkv<4, 0, true, 16>), g16, dim3(NW * 64), 0, s, DKV_ARGS);
   } else if (fuse) {
     GK_LAUNCH(wq, k_attn_bwd_dq<true>, gq, dim3(NW * 64), 0, sq, DKV_ARGS);
     GK_LAUNCH(wv, (k_attn_bwd_dkv<2, 2, false>), gkv, dim3(NW * 64), 0, sv, DKV_ARGS);
