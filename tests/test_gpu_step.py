@@ -79,14 +79,19 @@ def compare(cfg, w, tok, loss, ell, grads, flag):
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_plus", "small_bf16", "small_bf16_mha",
-                                  "small_bf16_wide_gate", "tiny_odd_gate", "d4", "tiny_T1",
-                                  "small_bf16_T1"])
+                                  "small_bf16_gqa_hd128", "small_bf16_wide_gate",
+                                  "tiny_odd_gate", "d4", "tiny_T1", "small_bf16_T1"])
 def test_step_matches_oracle(name):
     cfg = {"tiny": lambda: gi.preset("tiny"), "tiny_plus": tiny_plus,
            "small_bf16": small_bf16,
            "small_bf16_mha": lambda: small_bf16(n_kv_head=2, batch=2, seq_len=160,
                                                 window_short=40, window_long=160,
                                                 head_dim=128, n_head=2),
+           # head dim 128 (the MFMA attention and its joint dK/dV pass) with two
+           # query heads on one KV head and a ragged last 64-key block
+           "small_bf16_gqa_hd128": lambda: small_bf16(n_kv_head=1, batch=2, seq_len=200,
+                                                      window_short=72, window_long=200,
+                                                      head_dim=128, n_head=2),
            # gate reading more channels than the fast gate-gradient path covers
            "small_bf16_wide_gate": lambda: small_bf16(ve_gate_channels=100),
            # a gate of 7 channels leaves later value-embedding tables off 16-byte
