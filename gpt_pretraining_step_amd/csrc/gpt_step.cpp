@@ -457,6 +457,12 @@ struct SideStream {
 thread_local SideStream t_side[kMaxSideDevices];
 
 // the side stream of the current device, or null (one stream then)
+// split-K cap beside the main stream for weight-gradient products of fewer
+// than 16 output tiles (W_o at d12: 9 tiles), whose partials are small:
+// d12 step 33.84-33.90 ms against 33.94-34.02 with the common cap of 4
+// (8: 33.93-33.97, 16: 33.92-33.95; one box)
+static constexpr size_t kSmallSplitCap = 12;
+
 SideStream* side_stream() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
@@ -504,7 +510,9 @@ int run_backward(const Model& m, const Plan& p, const ParamLayout& pl, const voi
   // 33.75 ms with the standalone plan's 7-28; 2 splits 38.1, 3 33.8, 5 33.6,
   // 6 33.9 ms, one box)
   auto wsb = [&](int64_t M_, int64_t N_) {
-    return sd ? std::min(gscr_bytes, (size_t)4 * M_ * N_ * 4) : gscr_bytes;
+    const int64_t tiles = ((M_ + 255) / 256) * ((N_ + 255) / 256);
+    const size_t cap = tiles < 16 ? kSmallSplitCap : 4;
+    return sd ? std::min(gscr_bytes, cap * M_ * N_ * 4) : gscr_bytes;
   };
   bool marked[EV_COUNT] = {};
   auto fork = [&](int e) -> hipError_t {       // w waits for s's work so far
